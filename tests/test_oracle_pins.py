@@ -1,0 +1,419 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than itself.
+
+Hand-worked examples (tests/golden/*.json, each citing its source), closed forms, invariants,
+special cases that reduce to a library routine (torch's scaled_dot_product_attention in float64,
+torch's float32 -> bfloat16 rounding) and brute-force properties on small inputs.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from synth import gen as G
+from synth.workloads import get
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------------- formats
+
+
+def test_bf16_rounding_matches_torch_on_float32_values():
+    rng = np.random.default_rng(1)
+    x32 = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(5000) * 1e-30).astype(np.float32),
+        (rng.standard_normal(5000) * 1e30).astype(np.float32),
+        # exact halfway cases: 1 + odd multiples of 2**-8
+        (1.0 + (2 * np.arange(64) + 1) * 2.0 ** -8).astype(np.float32),
+    ])
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x32.astype(np.float64)), ref)
+
+
+def test_bf16_round_ties_to_even_by_hand():
+    # 1 + 2**-8 lies halfway between 1 and 1 + 2**-7: the even mantissa (1.0) wins.
+    assert O.round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    # 1 + 3*2**-8 lies halfway between 1 + 2**-7 (odd) and 1 + 2**-6 (even).
+    assert O.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    # just above the halfway point rounds up
+    assert O.round_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1 + 2.0 ** -7
+
+
+def test_bf16_generator_bits_decode_to_their_value():
+    x = G.normal_f32(3, "t", (4096,))
+    bits = G.f32_to_bf16_bits(x)
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(bits), O.round_bf16(x.astype(np.float64)))
+
+
+def test_mxfp4_table_from_spec():
+    g = _gold("mxfp4_e2m1.json")
+    for code, val in g["e2m1_code_to_value"].items():
+        got = O.e2m1_decode(np.array([int(code)]))[0]
+        assert got == val and np.signbit(got) == np.signbit(val), (code, got, val)
+    for E, s in g["e8m0_scale"].items():
+        codes = np.zeros(16, dtype=np.uint8)
+        codes[0] = 0x02                        # element 0 = +1.0, element 1 = 0
+        codes[1] = 0x70                        # element 2 = 0,    element 3 = +6.0
+        vals = O.mxfp4_decode(codes[None], np.array([[int(E)]], dtype=np.uint8))[0]
+        assert vals[0] == 1.0 * s and vals[1] == 0.0 and vals[2] == 0.0 and vals[3] == 6.0 * s
+
+
+def test_mxfp4_each_block_has_its_own_scale():
+    codes = np.full((1, 64), 0x22, dtype=np.uint8)        # every element +1.0
+    scales = np.array([[127, 128, 126, 130]], dtype=np.uint8)
+    v = O.mxfp4_decode(codes, scales)[0]
+    np.testing.assert_array_equal(v, np.repeat([1.0, 2.0, 0.5, 8.0], 32))
+
+
+def test_mxfp4_encoder_roundtrip_error_bound():
+    x = G.normal_f32(5, "q", (64, 128))
+    codes, scales = G.mxfp4_encode(x)
+    y = O.mxfp4_decode(codes, scales)
+    # The scale puts max|x| / scale in [4, 8): below 6 the error is at most half an e2m1 step
+    # (steps are at most 2 scales wide); above 6 saturation costs at most 8 - 6 = 2 scales.
+    scale = np.repeat(np.ldexp(1.0, scales.astype(int) - 127), 32, axis=-1)
+    err = np.abs(y - x) / scale
+    assert np.all(err <= 2.0)
+    assert np.all(err[np.abs(x) <= 6 * scale] <= 1.0)
+
+
+# ---------------------------------------------------------------------------------- compressor
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def test_compress_hand_example():
+    g = _gold("compress_hand.json")
+    e = O.compress(g["ca"], g["za"], g["cb"], g["zb"], g["bias_a"], g["bias_b"], g["m"], 0)
+    np.testing.assert_allclose(e, g["expected_entries"], rtol=0, atol=1e-12)
+
+
+def test_compress_weights_sum_to_one_and_entry0_pools_own_block_only():
+    rng = np.random.default_rng(0)
+    T, c, m = 40, 7, 4
+    ca, za, cb, zb = (_rand(rng, T, c) * 3 for _ in range(4))
+    ba, bb = _rand(rng, m, c), _rand(rng, m, c)
+    e, p = O.compress(ca, za, cb, zb, ba, bb, m, 0, return_weights=True)
+    assert e.shape == (T // m, c)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(p[0, m:] == 0.0)            # entry 0: no previous block
+    assert np.all(p[1:, m:] > 0.0)            # later entries: both blocks take part
+
+
+def test_compress_zero_logits_give_plain_mean():
+    rng = np.random.default_rng(1)
+    T, c, m = 24, 5, 4
+    ca, cb = _rand(rng, T, c), _rand(rng, T, c)
+    z = np.zeros((T, c))
+    b0 = np.zeros((m, c))
+    e = O.compress(ca, z, cb, z, b0, b0, m, 0)
+    np.testing.assert_allclose(e[0], ca[0:4].mean(axis=0), atol=1e-12)
+    for i in range(1, T // m):
+        want = (ca[i * m:(i + 1) * m].sum(axis=0) + cb[(i - 1) * m:i * m].sum(axis=0)) / (2 * m)
+        np.testing.assert_allclose(e[i], want, atol=1e-12)
+
+
+@pytest.mark.parametrize("series,r", [("a", 0), ("a", 3), ("b", 1), ("b", 2)])
+def test_compress_one_hot_bias_selects_that_token(series, r):
+    rng = np.random.default_rng(2)
+    T, c, m = 20, 3, 4
+    ca, za, cb, zb = (_rand(rng, T, c) for _ in range(4))
+    ba, bb = np.zeros((m, c)), np.zeros((m, c))
+    (ba if series == "a" else bb)[r, :] = 1e4
+    e = O.compress(ca, za, cb, zb, ba, bb, m, 0)
+    for i in range(1, T // m):
+        want = ca[i * m + r] if series == "a" else cb[(i - 1) * m + r]
+        np.testing.assert_allclose(e[i], want, atol=1e-9)
+
+
+def test_compress_constant_values():
+    rng = np.random.default_rng(3)
+    T, c, m = 16, 4, 4
+    za, zb = _rand(rng, T, c), _rand(rng, T, c)
+    ba, bb = _rand(rng, m, c), _rand(rng, m, c)
+    const = np.tile(np.array([1.5, -2.0, 0.25, 7.0]), (T, 1))
+    e = O.compress(const, za, const, zb, ba, bb, m, 0)
+    np.testing.assert_allclose(e, const[: T // m], atol=1e-12)
+
+
+def test_compress_with_halo_equals_compress_of_whole_sequence():
+    rng = np.random.default_rng(4)
+    T, c, m, split = 32, 6, 4, 12
+    ca, za, cb, zb = (_rand(rng, T, c) for _ in range(4))
+    ba, bb = _rand(rng, m, c), _rand(rng, m, c)
+    whole = O.compress(ca, za, cb, zb, ba, bb, m, 0)
+    tail = O.compress(ca[split:], za[split:], cb[split:], zb[split:], ba, bb, m, split // m,
+                      halo_cb=cb[split - m:split], halo_zb=zb[split - m:split])
+    np.testing.assert_allclose(tail, whole[split // m:], atol=1e-12)
+
+
+def test_compress_drops_incomplete_trailing_block():
+    rng = np.random.default_rng(5)
+    ca, za, cb, zb = (_rand(rng, 10, 2) for _ in range(4))
+    e = O.compress(ca, za, cb, zb, np.zeros((4, 2)), np.zeros((4, 2)), 4, 0)
+    assert e.shape == (2, 2)
+
+
+def test_compress_single_series_special_case():
+    # With identical series and biases the two readings coincide: entry i is a softmax over the
+    # 8 consecutive tokens [(i-1)m, (i+1)m) of z + bias[token mod m].
+    rng = np.random.default_rng(6)
+    T, c, m = 24, 3, 4
+    cc, zz = _rand(rng, T, c), _rand(rng, T, c)
+    bias = _rand(rng, m, c)
+    e = O.compress(cc, zz, cc, zz, bias, bias, m, 0)
+    for i in range(1, T // m):
+        rows = np.arange((i - 1) * m, (i + 1) * m)
+        lg = zz[rows] + bias[rows % m]
+        w = np.exp(lg - lg.max(axis=0))
+        w /= w.sum(axis=0)
+        np.testing.assert_allclose(e[i], (w * cc[rows]).sum(axis=0), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------- indexer
+
+
+def test_index_hand_example():
+    g = _gold("index_hand.json")
+    s = O.index_scores(g["q_idx"], g["keys"], g["w"], np.array(g["n_vis"]))
+    np.testing.assert_allclose(s, g["expected_scores"], atol=1e-12)
+
+
+def test_index_single_head_is_relu_dot():
+    rng = np.random.default_rng(7)
+    q, k = _rand(rng, 5, 1, 8), _rand(rng, 9, 8)
+    s = O.index_scores(q, k, np.array([1.0]), np.full(5, 9))
+    for t in range(5):
+        for i in range(9):
+            assert s[t, i] == pytest.approx(max(0.0, float(np.dot(q[t, 0], k[i]))), abs=1e-12)
+
+
+def test_index_nonnegative_and_invisible_masked():
+    rng = np.random.default_rng(8)
+    q, k = _rand(rng, 6, 3, 4), _rand(rng, 10, 4)
+    w = np.abs(_rand(rng, 3))
+    nv = np.array([0, 1, 3, 5, 10, 12])
+    s = O.index_scores(q, k, w, nv)
+    for t in range(6):
+        v = min(nv[t], 10)
+        assert np.all(s[t, :v] >= 0)
+        assert np.all(np.isneginf(s[t, v:]))
+
+
+def test_index_per_query_weights():
+    rng = np.random.default_rng(9)
+    q, k = _rand(rng, 3, 2, 4), _rand(rng, 5, 4)
+    w = np.abs(_rand(rng, 3, 2))
+    s = O.index_scores(q, k, w, np.full(3, 5))
+    for t in range(3):
+        s1 = O.index_scores(q[t:t + 1], k, w[t], np.array([5]))
+        np.testing.assert_allclose(s[t], s1[0], atol=1e-12)
+
+
+def test_n_visible_matches_block_completion_by_enumeration():
+    m = 4
+    for p in range(0, 50):
+        complete = sum(1 for i in range(100) if (i + 1) * m - 1 <= p)
+        assert O.n_visible(p, m) == complete
+    assert O.n_visible(2, 4) == 0 and O.n_visible(3, 4) == 1 and O.n_visible(131072, 4) == 32768
+
+
+# ---------------------------------------------------------------------------------- top-k
+
+
+def test_topk_hand_cases():
+    for c in _gold("topk_hand.json")["cases"]:
+        got = O.topk_select(np.array(c["scores"]), c["n_vis"], c["k"])
+        assert got.tolist() == c["expected"], c
+
+
+def _check_topk_properties(s, nv, k, idx):
+    sel = idx[idx >= 0]
+    assert sel.size == min(k, nv)
+    assert np.all(np.diff(sel) > 0)                       # ascending, distinct
+    assert np.all(idx[sel.size:] == -1)
+    assert np.all(sel < nv)                               # causal: nothing invisible
+    rest = np.setdiff1d(np.arange(nv), sel)
+    if sel.size and rest.size:
+        kth = s[sel].min()
+        assert np.all(s[rest] <= kth)                     # everything kept beats everything left
+        ties = rest[s[rest] == kth]
+        tied_sel = sel[s[sel] == kth]
+        assert ties.size == 0 or tied_sel.max() < ties.min()   # ties go to smaller indices
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_properties_random_and_tied(seed):
+    rng = np.random.default_rng(seed)
+    N = 300
+    s = rng.standard_normal(N) if seed % 2 else np.round(rng.standard_normal(N) * 2) / 2
+    if seed == 4:
+        s[:] = 0.0
+        s[::7] = -0.0
+    for nv in (0, 1, 17, 150, 300):
+        for k in (1, 16, 64, 400):
+            _check_topk_properties(s, nv, k, O.topk_select(s, nv, k))
+
+
+def test_topk_all_equal_takes_first_k():
+    assert O.topk_select(np.zeros(50), 50, 8).tolist() == list(range(8))
+
+
+# ---------------------------------------------------------------------------------- attention
+
+
+def test_attention_hand_example():
+    g = _gold("attention_hand.json")
+    q = np.array(g["q"])
+    o = O.sparse_attention(q, np.array(g["entries"]), np.array(g["idx"]), np.array(g["raw"]), 0,
+                           [g["p"]], g["W"])
+    np.testing.assert_allclose(o, g["expected_out"], atol=1e-12)
+    o = O.sparse_attention(q, np.array(g["entries"]), np.array(g["idx"]), np.array(g["raw"]), 0,
+                           [g["p"]], g["W"], sink=np.array(g["sink"]))
+    np.testing.assert_allclose(o, g["expected_out_sink"], atol=1e-12)
+
+
+def test_attention_dense_equivalence_with_sdpa():
+    # With k >= N and W >= T the layer is masked dense attention over [entries ; raw tokens].
+    rng = np.random.default_rng(10)
+    T, H, D, m = 37, 3, 8, 4
+    N = T // m
+    q = _rand(rng, T, H, D)
+    ent = _rand(rng, N, D)
+    raw = _rand(rng, T, D)
+    q_pos = np.arange(T)
+    nv = O.n_visible(q_pos, m)
+    idx = np.stack([O.topk_select(rng.standard_normal(N), nv[t], N) for t in range(T)])
+    o = O.sparse_attention(q, ent, idx, raw, 0, q_pos, W=T)
+    keys = torch.from_numpy(np.concatenate([ent, raw], axis=0))        # [N + T, D]
+    mask = torch.zeros(T, N + T, dtype=torch.bool)
+    for t in range(T):
+        mask[t, :nv[t]] = True
+        mask[t, N:N + t + 1] = True
+    qq = torch.from_numpy(q).permute(1, 0, 2)                          # [H, T, D]
+    kk = keys.unsqueeze(0).expand(H, -1, -1).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, kk, attn_mask=mask)
+    np.testing.assert_allclose(o, ref.permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def test_attention_window_only_returns_own_raw_row():
+    rng = np.random.default_rng(11)
+    T, H, D = 3, 2, 5                    # p < m - 1: no entries are visible yet
+    q, raw = _rand(rng, T, H, D), _rand(rng, T, D)
+    idx = np.full((T, 4), -1)
+    o = O.sparse_attention(q, np.zeros((0, D)), idx, raw, 0, np.arange(T), W=1)
+    for t in range(T):
+        np.testing.assert_allclose(o[t], np.tile(raw[t], (H, 1)), atol=1e-15)
+
+
+def test_attention_zero_query_is_uniform_mean():
+    rng = np.random.default_rng(12)
+    T, H, D = 1, 2, 6
+    ent, raw = _rand(rng, 10, D), _rand(rng, 20, D)
+    idx = np.array([[1, 4, 7, -1]])
+    o = O.sparse_attention(np.zeros((T, H, D)), ent, idx, raw, 0, [15], W=5)
+    want = np.concatenate([ent[[1, 4, 7]], raw[11:16]]).mean(axis=0)
+    np.testing.assert_allclose(o[0], np.tile(want, (H, 1)), atol=1e-12)
+
+
+def test_attention_sink_limits():
+    rng = np.random.default_rng(13)
+    q, ent, raw = _rand(rng, 2, 3, 4), _rand(rng, 8, 4), _rand(rng, 12, 4)
+    idx = np.array([[0, 2, 5], [1, 3, -1]])
+    base = O.sparse_attention(q, ent, idx, raw, 0, [9, 11], W=4)
+    none = O.sparse_attention(q, ent, idx, raw, 0, [9, 11], W=4, sink=np.full(3, -np.inf))
+    np.testing.assert_allclose(none, base, atol=1e-15)
+    huge = O.sparse_attention(q, ent, idx, raw, 0, [9, 11], W=4, sink=np.full(3, 60.0))
+    assert np.abs(huge).max() < 1e-20
+
+
+# ---------------------------------------------------------------------------------- whole layer
+
+
+def _tiny(**kw):
+    return get("tiny").with_(**kw)
+
+
+def test_prefill_dense_equivalence_end_to_end():
+    wl = _tiny(T=64, k=64, W=64)
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    T, H, D, N = wl.T, wl.H, wl.D, r["entries"].shape[0]
+    keys = torch.from_numpy(np.concatenate([r["entries"], r["raw"]], axis=0))
+    mask = torch.zeros(T, N + T, dtype=torch.bool)
+    for t in range(T):
+        mask[t, :r["n_vis"][t]] = True
+        mask[t, N:N + t + 1] = True
+    qq = torch.from_numpy(r["q"]).permute(1, 0, 2)
+    kk = keys.unsqueeze(0).expand(H, -1, -1).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, kk, attn_mask=mask)
+    np.testing.assert_allclose(r["out"], ref.permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def _prefix_inputs_from_full(inp_full, wl_full, r_full, L):
+    """Build chunked-prefill inputs whose context is the first L tokens of a full run."""
+    wl = wl_full.with_(L=L, T=wl_full.T - L)
+    m, D, DI = wl.m, wl.D, wl.D_I
+    cols, _ = O.projection_columns(D, DI, wl.H, wl.H_I)
+    p = r_full["parts"]
+    inp = dict(inp_full)
+    inp["x"] = inp_full["x"][:, L:]
+    inp["entries_prefix"] = r_full["entries"][None, : L // m]
+    inp["keys_prefix"] = r_full["keys"][None, : L // m]
+    inp["win_prefix"] = p["kv"][None, L - (wl.W - 1):L]
+    hb = slice(L - m, L)
+    inp["halo"] = np.concatenate([p["cb"][hb], p["zb"][hb], p["icb"][hb], p["izb"][hb]], axis=1)[None]
+    return wl, inp
+
+
+def test_chunked_prefill_equals_one_shot():
+    wl_full = _tiny(T=96)
+    inp = G.make_inputs(wl_full)
+    full = O.prefill(inp, wl_full)
+    wl, inp2 = _prefix_inputs_from_full(inp, wl_full, full, L=48)
+    part = O.prefill(inp2, wl)
+    np.testing.assert_allclose(part["entries"], full["entries"], atol=1e-12)
+    np.testing.assert_allclose(part["out"], full["out"][48:], atol=1e-12)
+    np.testing.assert_array_equal(part["idx"], full["idx"][48:])
+
+
+def test_decode_equals_prefill_of_the_last_token():
+    wl_full = _tiny(T=97)                       # the last token sits at p = 96 = L
+    inp = G.make_inputs(wl_full)
+    full = O.prefill(inp, wl_full)
+    L = 96
+    wl = wl_full.with_(kind="decode", L=L, T=1, d=0)
+    dec = {
+        "entries": full["entries"][None, : L // 4],
+        "keys": full["keys"][None, : L // 4],
+        "kv_raw": full["parts"]["kv"][None, L - wl.W + 1:L + 1],
+        "q": full["q"][None, L:L + 1],
+        "q_idx": full["q_idx"][None, L:L + 1],
+        "w_head": inp["w_head"],
+    }
+    wl = wl.with_(dtype="f32", idx_dtype="f32")
+    r = O.decode(dec, wl, 0)
+    np.testing.assert_array_equal(r["idx"][0], full["idx"][L])
+    np.testing.assert_allclose(r["out"][0], full["out"][L], atol=1e-12)
+
+
+def test_prefill_invariants_bf16_tiny():
+    wl = _tiny(dtype="bf16", idx_dtype="bf16")
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    # stored tensors sit on the bf16 grid
+    for a in (r["entries"], r["keys"], r["q"], r["raw"]):
+        np.testing.assert_array_equal(O.round_bf16(a), a)
+    for t in range(wl.T):
+        _check_topk_properties(r["scores"][t], r["n_vis"][t], wl.k, r["idx"][t])
