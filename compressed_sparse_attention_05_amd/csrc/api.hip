@@ -1,0 +1,448 @@
+// The C ABI: argument validation (host only, before any HIP call), workspace carving and dispatch
+// to the kernels. Declarations and the meaning of every argument are in include/csa.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "kernels.h"
+
+namespace csa {
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err.clear();
+    return CSA_OK;
+  }
+  return fail(CSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int esize(int dt) { return dt == CSA_F32 ? 4 : 2; }
+
+bool is_act_dtype(int dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+
+constexpr int kMaxTopK = 4096;
+
+__global__ void copy_rows_kernel(int rows, int cols, int esz, const uint8_t* src, int64_t src_ld, int64_t src_seq,
+                                 uint8_t* dst, int64_t dst_ld, int64_t dst_seq) {
+  const int b = blockIdx.y;
+  const int64_t nbytes = (int64_t)rows * cols * esz;
+  const int64_t rowb = (int64_t)cols * esz;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nbytes; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / rowb, c = i % rowb;
+    dst[(b * dst_seq + r * dst_ld) * esz + c] = src[(b * src_seq + r * src_ld) * esz + c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy_rows(int B, int rows, int cols, int esz, const void* src, int64_t src_ld, int64_t src_seq,
+                            void* dst, int64_t dst_ld, int64_t dst_seq, hipStream_t s) {
+  if (B == 0 || rows == 0 || cols == 0) return hipSuccess;
+  const int64_t nbytes = (int64_t)rows * cols * esz;
+  unsigned gx = (unsigned)ceil_div(nbytes, 256);
+  if (gx > 4096) gx = 4096;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(gx, (unsigned)B), dim3(256), 0, s, rows, cols, esz,
+                     static_cast<const uint8_t*>(src), src_ld, src_seq, static_cast<uint8_t*>(dst), dst_ld, dst_seq);
+  return hipGetLastError();
+}
+
+hipError_t allow_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = done.find(key);
+  if (it != done.end() && it->second >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done[key] = bytes;
+  return e;
+}
+
+}  // namespace csa
+
+using namespace csa;
+
+namespace {
+
+int check_dims(const csa_dims* d) {
+  if (!d) return fail(CSA_ERR_ARG, "dims is NULL");
+  if (d->m < 1 || d->m > compress_max_m()) return fail(CSA_ERR_ARG, "m=%d out of [1, %d]", d->m, compress_max_m());
+  if (d->D < 1 || d->H < 1 || d->H_I < 1 || d->D_I < 1) return fail(CSA_ERR_ARG, "dims must be positive");
+  if (d->top_k < 1 || d->top_k > kMaxTopK) return fail(CSA_ERR_ARG, "top_k=%d out of [1, %d]", d->top_k, kMaxTopK);
+  if (d->window < 1) return fail(CSA_ERR_ARG, "window=%d must be >= 1", d->window);
+  if (!(d->sm_scale >= 0.f) || std::isinf(d->sm_scale)) return fail(CSA_ERR_ARG, "sm_scale must be finite and >= 0");
+  return CSA_OK;
+}
+
+float scale_of(const csa_dims* d) { return d->sm_scale > 0.f ? d->sm_scale : 1.0f / std::sqrt((float)d->D); }
+
+IndexArgs make_index_args(const csa_dims* d, int B, int T, int64_t q_pos0, int idx_dtype, const void* q_idx,
+                          int64_t q_ld, int64_t q_seq_stride, const void* q_scale, const float* w, int64_t w_ld,
+                          const void* keys, int64_t keys_seq_stride, const void* k_scale, int64_t n_cap,
+                          int32_t* out_idx, float* out_score) {
+  IndexArgs a{};
+  a.B = B;
+  a.T = T;
+  a.q_pos0 = q_pos0;
+  a.m = d->m;
+  a.H_I = d->H_I;
+  a.D_I = d->D_I;
+  a.k = d->top_k;
+  a.idx_dtype = idx_dtype;
+  a.q = q_idx;
+  a.q_ld = q_ld;
+  a.q_seq_stride = q_seq_stride;
+  a.q_scale = static_cast<const uint8_t*>(q_scale);
+  a.w = w;
+  a.w_ld = w_ld;
+  a.keys = keys;
+  a.keys_seq_stride = keys_seq_stride;
+  a.k_scale = static_cast<const uint8_t*>(k_scale);
+  a.n_cap = n_cap;
+  a.out_idx = out_idx;
+  a.out_score = out_score;
+  if (idx_dtype == CSA_MXFP4) {  // contiguous MXFP4 tensors, strides in code bytes
+    a.q_ld = (int64_t)d->H_I * d->D_I / 2;
+    a.q_seq_stride = (int64_t)T * a.q_ld;
+    a.keys_seq_stride = n_cap * d->D_I / 2;
+  }
+  return a;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return CSA_OK;
+  if (!ws) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (!aligned(ws, 256)) return fail(CSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return CSA_OK;
+}
+
+int64_t n_tot_of(const csa_dims* d) {
+  return 4LL * d->D + 4LL * d->D_I + (int64_t)d->H * d->D + (int64_t)d->H_I * d->D_I + d->D;
+}
+
+int validate_index(const csa_dims* d, int B, int T, int64_t q_pos0, int idx_dtype, const void* q_idx, int64_t q_ld,
+                   int64_t q_seq_stride, const void* q_scale, const float* w, int64_t w_ld, const void* keys,
+                   int64_t keys_seq_stride, const void* k_scale, int64_t n_cap, const int32_t* out_idx) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
+  if (q_pos0 < 0) return fail(CSA_ERR_ARG, "q_pos0 must be >= 0");
+  if (n_cap < 0 || n_cap > 0x7FFFFFFFLL) return fail(CSA_ERR_ARG, "n_cap out of range");
+  if (idx_dtype != CSA_F32 && idx_dtype != CSA_BF16 && idx_dtype != CSA_MXFP4)
+    return fail(CSA_ERR_ARG, "unknown idx_dtype %d", idx_dtype);
+  if ((int64_t)B * T == 0) return CSA_OK;
+  if (!q_idx || !w || !out_idx || (!keys && n_cap > 0)) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  if (w_ld < 0) return fail(CSA_ERR_ARG, "w_ld must be >= 0");
+  if (w_ld > 0 && w_ld < d->H_I) return fail(CSA_ERR_ARG, "w_ld must be 0 or >= H_I");
+  if (idx_dtype == CSA_MXFP4) {
+    if (d->D_I % 32) return fail(CSA_ERR_ARG, "MXFP4 needs D_I %% 32 == 0");
+    if (!q_scale || (!k_scale && n_cap > 0)) return fail(CSA_ERR_ARG, "MXFP4 needs q_scale and k_scale");
+    if (q_ld != 0 || q_seq_stride != 0) return fail(CSA_ERR_ARG, "MXFP4 q must be contiguous (q_ld = q_seq_stride = 0)");
+    if (keys_seq_stride != 0 && keys_seq_stride != n_cap * d->D_I / 2)
+      return fail(CSA_ERR_ARG, "MXFP4 keys must be contiguous");
+    if (!aligned(q_idx, 16) || (keys && !aligned(keys, 16))) return fail(CSA_ERR_ARG, "MXFP4 codes must be 16-byte aligned");
+  } else {
+    if (q_ld < (int64_t)d->H_I * d->D_I) return fail(CSA_ERR_ARG, "q_ld < H_I*D_I");
+    if (B > 1 && q_seq_stride < (int64_t)T * q_ld) return fail(CSA_ERR_ARG, "q_seq_stride too small");
+    if (B > 1 && keys_seq_stride < n_cap * d->D_I) return fail(CSA_ERR_ARG, "keys_seq_stride too small");
+    const size_t a = esize(idx_dtype) == 2 ? 16 : 4;
+    if (!aligned(q_idx, a) || (keys && !aligned(keys, a))) return fail(CSA_ERR_ARG, "misaligned q_idx/keys");
+    if (idx_dtype == CSA_BF16 && d->H_I == 64 && d->D_I == 128 &&
+        ((q_ld % 8) || (q_seq_stride % 8) || (keys_seq_stride % 8)))
+      return fail(CSA_ERR_ARG, "bf16 indexer strides must be multiples of 8 elements");
+  }
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_version(void) { return 1; }
+
+const char* csa_last_error(void) { return g_err.c_str(); }
+
+int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap, int d_model, int idx_dtype,
+                       int64_t* bytes) {
+  if (!bytes) return fail(CSA_ERR_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (B < 0 || T < 0 || n_cap < 0 || d_model < 0) return fail(CSA_ERR_ARG, "negative size");
+  switch (op) {
+    case CSA_OP_COMPRESS:
+    case CSA_OP_SPARSE_ATTN:
+      return CSA_OK;
+    case CSA_OP_TOPK_FROM_SCORES: {
+      if (!dims) return fail(CSA_ERR_ARG, "dims is NULL");
+      *bytes = (int64_t)topk_workspace(B, n_cap, dims->top_k);
+      return CSA_OK;
+    }
+    case CSA_OP_INDEX_TOPK:
+    case CSA_OP_FORWARD: {
+      int rc = check_dims(dims);
+      if (rc) return rc;
+      IndexArgs a = make_index_args(dims, B, T, 0, idx_dtype, nullptr, 0, 0, nullptr, nullptr, 0, nullptr, 0,
+                                    nullptr, n_cap, nullptr, nullptr);
+      size_t need = index_topk_workspace(a);
+      if (op == CSA_OP_FORWARD) {
+        const int es = idx_dtype == CSA_F32 ? 4 : 2;
+        need = align256((size_t)B * T * n_tot_of(dims) * es) + align256((size_t)B * T * dims->top_k * 4) + align256(need);
+      }
+      *bytes = (int64_t)need;
+      return CSA_OK;
+    }
+    default:
+      return fail(CSA_ERR_ARG, "unknown op %d", op);
+  }
+}
+
+int csa_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype, const void* ca, const void* za,
+                 const void* cb, const void* zb, int64_t ld, int64_t seq_stride, const void* halo_cb,
+                 const void* halo_zb, int64_t halo_ld, int64_t halo_seq_stride, const float* bias_a,
+                 const float* bias_b, void* entries, int64_t entries_seq_stride, int64_t n_cap, int out_dtype,
+                 void* stream) {
+  if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
+  if (m < 1 || m > compress_max_m()) return fail(CSA_ERR_ARG, "m=%d out of [1, %d]", m, compress_max_m());
+  if (c < 1) return fail(CSA_ERR_ARG, "c must be >= 1");
+  if (!is_act_dtype(in_dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
+  if (pos0 < 0 || pos0 % m) return fail(CSA_ERR_ARG, "pos0=%lld must be a non-negative multiple of m", (long long)pos0);
+  const int n_new = T / m;
+  if (B == 0 || n_new == 0) return CSA_OK;
+  const int64_t first = pos0 / m;
+  if (first + n_new > n_cap) return fail(CSA_ERR_ARG, "entries rows %lld..%lld exceed n_cap=%lld", (long long)first,
+                                         (long long)(first + n_new - 1), (long long)n_cap);
+  if (!ca || !za || !cb || !zb || !bias_a || !bias_b || !entries) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  if (ld < c) return fail(CSA_ERR_ARG, "ld=%lld < c=%d", (long long)ld, c);
+  if (B > 1 && seq_stride < (int64_t)T * ld) return fail(CSA_ERR_ARG, "seq_stride too small");
+  if (B > 1 && entries_seq_stride < n_cap * c) return fail(CSA_ERR_ARG, "entries_seq_stride too small");
+  if (first > 0) {
+    if (!halo_cb || !halo_zb) return fail(CSA_ERR_ARG, "pos0 > 0 needs the previous block (halo_cb, halo_zb)");
+    if (halo_ld < c) return fail(CSA_ERR_ARG, "halo_ld < c");
+    if (B > 1 && halo_seq_stride < (int64_t)m * halo_ld) return fail(CSA_ERR_ARG, "halo_seq_stride too small");
+  }
+  CompressArgs a{};
+  a.B = B;
+  a.n_new = n_new;
+  a.m = m;
+  a.c = c;
+  a.first_entry = first;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.ca = ca;
+  a.za = za;
+  a.cb = cb;
+  a.zb = zb;
+  a.ld = ld;
+  a.seq_stride = seq_stride;
+  a.halo_cb = first > 0 ? halo_cb : ca;
+  a.halo_zb = first > 0 ? halo_zb : za;
+  a.halo_ld = first > 0 ? halo_ld : ld;
+  a.halo_seq_stride = first > 0 ? halo_seq_stride : seq_stride;
+  a.bias_a = bias_a;
+  a.bias_b = bias_b;
+  a.entries = entries;
+  a.entries_seq_stride = entries_seq_stride;
+  a.aligned16 = aligned(ca, 16) && aligned(za, 16) && aligned(cb, 16) && aligned(zb, 16) && aligned(a.halo_cb, 16) &&
+                aligned(a.halo_zb, 16) && aligned(entries, 16);
+  return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)), "csa_compress");
+}
+
+int csa_index_topk(const csa_dims* dims, int B, int T, int64_t q_pos0, int idx_dtype, const void* q_idx, int64_t q_ld,
+                   int64_t q_seq_stride, const void* q_scale, const float* w, int64_t w_ld, const void* keys,
+                   int64_t keys_seq_stride, const void* k_scale, int64_t n_cap, int32_t* out_idx, float* out_score,
+                   void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate_index(dims, B, T, q_pos0, idx_dtype, q_idx, q_ld, q_seq_stride, q_scale, w, w_ld, keys,
+                          keys_seq_stride, k_scale, n_cap, out_idx);
+  if (rc) return rc;
+  if ((int64_t)B * T == 0) return CSA_OK;
+  IndexArgs a = make_index_args(dims, B, T, q_pos0, idx_dtype, q_idx, q_ld, q_seq_stride, q_scale, w, w_ld, keys,
+                                keys_seq_stride, k_scale, n_cap, out_idx, out_score);
+  rc = check_ws(ws, ws_bytes, index_topk_workspace(a));
+  if (rc) return rc;
+  return hip_status(launch_index_topk(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), "csa_index_topk");
+}
+
+int csa_topk_from_scores(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
+                         float* out_score, void* ws, size_t ws_bytes, void* stream) {
+  if (R < 0 || ld < 0) return fail(CSA_ERR_ARG, "R and ld must be >= 0");
+  if (k < 1 || k > kMaxTopK) return fail(CSA_ERR_ARG, "k=%d out of [1, %d]", k, kMaxTopK);
+  if (ld > 0x7FFFFFFFLL) return fail(CSA_ERR_ARG, "ld too large");
+  if (R == 0) return CSA_OK;
+  if (!scores || !n_valid || !out_idx) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  int rc = check_ws(ws, ws_bytes, topk_workspace(R, ld, k));
+  if (rc) return rc;
+  TopkArgs a{scores, ld, n_valid, R, k, out_idx, out_score};
+  return hip_status(launch_topk_from_scores(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), "csa_topk_from_scores");
+}
+
+int csa_sparse_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype, const void* q, int64_t q_ld,
+                    int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride, int64_t n_cap,
+                    const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
+                    int64_t raw_len, const float* sink, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
+  if (!is_act_dtype(in_dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
+  if (q_pos0 < 0 || n_cap < 0 || raw_len < 0) return fail(CSA_ERR_ARG, "negative position or size");
+  if (dims->D > 1024) return fail(CSA_ERR_UNSUPPORTED, "D > 1024");
+  if ((int64_t)B * T == 0) return CSA_OK;
+  if (!q || !idx || !kv_raw || !out || (!entries && n_cap > 0)) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  const int64_t H = dims->H, D = dims->D;
+  if (q_ld < H * D) return fail(CSA_ERR_ARG, "q_ld < H*D");
+  if (B > 1 && q_seq_stride < (int64_t)T * q_ld) return fail(CSA_ERR_ARG, "q_seq_stride too small");
+  if (B > 1 && entries_seq_stride < n_cap * D) return fail(CSA_ERR_ARG, "entries_seq_stride too small");
+  if (raw_ld < D) return fail(CSA_ERR_ARG, "raw_ld < D");
+  if (B > 1 && raw_seq_stride < raw_len * raw_ld) return fail(CSA_ERR_ARG, "raw_seq_stride too small");
+  const int64_t need_lo = q_pos0 - dims->window + 1 > 0 ? q_pos0 - dims->window + 1 : 0;
+  const int64_t need_hi = q_pos0 + T - 1;
+  if (raw_pos0 > need_lo || raw_pos0 + raw_len - 1 < need_hi)
+    return fail(CSA_ERR_ARG, "kv_raw rows [%lld, %lld] do not cover the windows [%lld, %lld]", (long long)raw_pos0,
+                (long long)(raw_pos0 + raw_len - 1), (long long)need_lo, (long long)need_hi);
+  const size_t al = esize(in_dtype) == 2 ? 16 : 4;
+  if (!aligned(q, al) || !aligned(kv_raw, al) || (entries && !aligned(entries, al)))
+    return fail(CSA_ERR_ARG, "misaligned q / entries / kv_raw");
+  AttnArgs a{};
+  a.B = B;
+  a.T = T;
+  a.q_pos0 = q_pos0;
+  a.H = dims->H;
+  a.D = dims->D;
+  a.k = dims->top_k;
+  a.W = dims->window;
+  a.scale = scale_of(dims);
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.q_ld = q_ld;
+  a.q_seq_stride = q_seq_stride;
+  a.entries = entries;
+  a.entries_seq_stride = entries_seq_stride;
+  a.n_cap = n_cap;
+  a.idx = idx;
+  a.raw = kv_raw;
+  a.raw_ld = raw_ld;
+  a.raw_seq_stride = raw_seq_stride;
+  a.raw_pos0 = raw_pos0;
+  a.raw_len = raw_len;
+  a.sink = sink;
+  a.out = out;
+  rc = check_ws(ws, ws_bytes, attn_workspace(a));
+  if (rc) return rc;
+  return hip_status(launch_attn(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), "csa_sparse_attn");
+}
+
+int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_t pos0, int d_model, int dtype,
+                const void* x, const csa_cache* cache, void* out, int out_dtype, int32_t* out_idx, void* ws,
+                size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!w || !cache) return fail(CSA_ERR_ARG, "weights or cache is NULL");
+  if (B < 0 || T < 0 || d_model < 1) return fail(CSA_ERR_ARG, "bad B/T/d_model");
+  if (!is_act_dtype(dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
+  const int m = dims->m, D = dims->D, DI = dims->D_I, H = dims->H, HI = dims->H_I, W = dims->window, k = dims->top_k;
+  if (pos0 < 0 || pos0 % m) return fail(CSA_ERR_ARG, "pos0 must be a non-negative multiple of m");
+  if ((int64_t)B * T == 0) return CSA_OK;
+  if (!x || !out || !w->w_proj || !w->bias_a || !w->bias_b || !w->ibias_a || !w->ibias_b || !w->w_head)
+    return fail(CSA_ERR_ARG, "NULL weight/input pointer");
+  if (!cache->entries || !cache->keys || !cache->win) return fail(CSA_ERR_ARG, "NULL cache pointer");
+  if ((pos0 + T) / m > cache->n_cap) return fail(CSA_ERR_ARG, "(pos0+T)/m exceeds n_cap");
+  if ((int64_t)W - 1 + T > cache->win_cap) return fail(CSA_ERR_ARG, "window - 1 + T exceeds win_cap");
+  if (pos0 > 0 && !cache->halo) return fail(CSA_ERR_ARG, "pos0 > 0 needs cache->halo");
+  if (cache->halo_out && T % m) return fail(CSA_ERR_ARG, "halo_out needs T %% m == 0");
+  const int64_t ntot = n_tot_of(dims);
+  const int es = esize(dtype);
+  // workspace: P [B*T, ntot] | idx [B*T, k] | index scratch
+  IndexArgs probe = make_index_args(dims, B, T, pos0, dtype, nullptr, 0, 0, nullptr, nullptr, 0, nullptr, 0, nullptr,
+                                    cache->n_cap, nullptr, nullptr);
+  const size_t p_bytes = align256((size_t)B * T * ntot * es);
+  const size_t i_bytes = align256((size_t)B * T * k * 4);
+  const size_t x_bytes = align256(index_topk_workspace(probe));
+  rc = check_ws(ws, ws_bytes, p_bytes + i_bytes + x_bytes);
+  if (rc) return rc;
+  if (!aligned(x, 16) || !aligned(w->w_proj, 16)) return fail(CSA_ERR_ARG, "x and w_proj must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* P = static_cast<uint8_t*>(ws);
+  int32_t* idx = out_idx ? out_idx : reinterpret_cast<int32_t*>(P + p_bytes);
+  void* xws = P + p_bytes + i_bytes;
+  auto col = [&](int64_t c) { return static_cast<void*>(P + c * es); };
+  const int64_t c_ca = 0, c_za = D, c_cb = 2LL * D, c_zb = 3LL * D;
+  const int64_t c_ica = 4LL * D, c_iza = c_ica + DI, c_icb = c_ica + 2LL * DI, c_izb = c_ica + 3LL * DI;
+  const int64_t c_q = 4LL * D + 4LL * DI, c_qi = c_q + (int64_t)H * D, c_kv = c_qi + (int64_t)HI * DI;
+  const int64_t halo_ld = 2LL * D + 2LL * DI;
+  const uint8_t* halo = static_cast<const uint8_t*>(cache->halo);
+
+  GemmArgs g{};
+  g.M = B * T;
+  g.N = (int)ntot;
+  g.K = d_model;
+  g.dtype = dtype;
+  g.out_dtype = dtype;
+  g.A = x;
+  g.lda = d_model;
+  g.Bm = w->w_proj;
+  g.ldb = d_model;
+  g.C = P;
+  g.ldc = ntot;
+  hipError_t e = launch_gemm(g, s);
+  if (e != hipSuccess) return hip_status(e, "csa_forward: projection");
+
+  rc = csa_compress(B, T, pos0, m, D, dtype, col(c_ca), col(c_za), col(c_cb), col(c_zb), ntot, (int64_t)T * ntot,
+                    halo ? halo : nullptr, halo ? halo + (size_t)D * es : nullptr, halo_ld, (int64_t)m * halo_ld,
+                    w->bias_a, w->bias_b, cache->entries, cache->n_cap * D, cache->n_cap, dtype, stream);
+  if (rc) return rc;
+  rc = csa_compress(B, T, pos0, m, DI, dtype, col(c_ica), col(c_iza), col(c_icb), col(c_izb), ntot, (int64_t)T * ntot,
+                    halo ? halo + (size_t)2 * D * es : nullptr, halo ? halo + (size_t)(2 * D + DI) * es : nullptr,
+                    halo_ld, (int64_t)m * halo_ld, w->ibias_a, w->ibias_b, cache->keys, cache->n_cap * DI,
+                    cache->n_cap, dtype, stream);
+  if (rc) return rc;
+  // the chunk's raw KV goes to window rows [W-1, W-1+T)
+  e = launch_copy_rows(B, T, D, es, col(c_kv), ntot, (int64_t)T * ntot,
+                       static_cast<uint8_t*>(cache->win) + (size_t)(W - 1) * D * es, D, cache->win_cap * D, s);
+  if (e != hipSuccess) return hip_status(e, "csa_forward: window copy");
+  rc = csa_index_topk(dims, B, T, pos0, dtype, col(c_qi), ntot, (int64_t)T * ntot, nullptr, w->w_head, 0, cache->keys,
+                      cache->n_cap * DI, nullptr, cache->n_cap, idx, nullptr, xws, x_bytes, stream);
+  if (rc) return rc;
+  rc = csa_sparse_attn(dims, B, T, pos0, dtype, col(c_q), ntot, (int64_t)T * ntot, cache->entries, cache->n_cap * D,
+                       cache->n_cap, idx, cache->win, D, cache->win_cap * D, pos0 - (W - 1), (int64_t)W - 1 + T,
+                       w->sink, out, out_dtype, nullptr, 0, stream);
+  if (rc) return rc;
+  if (cache->halo_out) {
+    uint8_t* ho = static_cast<uint8_t*>(cache->halo_out);
+    e = launch_copy_rows(B, m, 2 * D, es, col(c_cb + (int64_t)(T - m) * ntot), ntot, (int64_t)T * ntot, ho, halo_ld,
+                         (int64_t)m * halo_ld, s);
+    if (e == hipSuccess)
+      e = launch_copy_rows(B, m, 2 * DI, es, col(c_icb + (int64_t)(T - m) * ntot), ntot, (int64_t)T * ntot,
+                           ho + (size_t)2 * D * es, halo_ld, (int64_t)m * halo_ld, s);
+    if (e != hipSuccess) return hip_status(e, "csa_forward: halo copy");
+  }
+  g_err.clear();
+  return CSA_OK;
+}
+
+}  // extern "C"

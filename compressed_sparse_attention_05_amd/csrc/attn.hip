@@ -1,0 +1,325 @@
+// Step 4: sparse single-KV-head attention over the selected entries plus the raw-token window,
+// one softmax over both ("Anatomy of a Frontier Model", "The skeleton, and what's kept": one KV
+// head for every query head, the entry is key and value; bullet "A sliding window in every
+// layer"; bullet "An attention sink": an extra exp(sink_h) in the denominator).
+//
+// Paths:
+//  * attn_mfma (bf16, D = 512, 64-head groups): one workgroup per (query row, 64-head group); the
+//    four waves split the 512 dims into quarters. For each tile of 32 gathered keys a wave loads its
+//    quarter of every key straight from HBM/L2 into MFMA B-fragments, computes the partial logits of
+//    all 64 heads (QK^T over its 128 dims, q resident in VGPRs), and stores the partials plus a
+//    transposed copy of its key quarter (the V operand) in LDS. After a barrier each wave finishes
+//    the online softmax of 16 heads (sum of the four partials, running max and sum, P in bf16);
+//    after a second barrier each wave accumulates O[64 heads x its 128 dims] += P V with MFMA.
+//    Key bytes cross the L2->CU path once per head group; the entry is both K and V.
+//  * attn_generic (any H, D, fp32 or bf16): one wave per (row, head), lanes over dims, one key at
+//    a time with a wave reduction; used for fp32 layers and odd shapes.
+#include "kernels.h"
+
+namespace csa {
+
+namespace {
+
+__device__ __forceinline__ int64_t window_lo(const AttnArgs& a, int64_t p) {
+  int64_t lo = p - a.W + 1;
+  if (lo < 0) lo = 0;
+  if (lo < a.raw_pos0) lo = a.raw_pos0;
+  return lo;
+}
+__device__ __forceinline__ int64_t window_hi(const AttnArgs& a, int64_t p) {
+  int64_t hi = p;
+  if (hi > a.raw_pos0 + a.raw_len - 1) hi = a.raw_pos0 + a.raw_len - 1;
+  return hi;
+}
+
+// ---------------------------------------------------------------- generic
+
+constexpr int kGenWaves = 4;
+
+template <int DT, int OT>
+__global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int64_t row = blockIdx.x;
+  const int b = (int)(row / a.T), t = (int)(row % a.T);
+  const int64_t p = a.q_pos0 + t;
+  const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
+  const int32_t* idx = a.idx + row * a.k;
+  constexpr int kMaxPer = 16;  // dims per lane (D <= 1024)
+  const int per = (a.D + 63) / 64;
+  for (int h = wave; h < a.H; h += kGenWaves) {
+    const int64_t qoff = (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld + (int64_t)h * a.D;
+    float qv[kMaxPer], ov[kMaxPer];
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int d = lane + 64 * j;
+      qv[j] = (j < per && d < a.D) ? load_elem<DT>(a.q, qoff + d) * a.scale : 0.f;
+      ov[j] = 0.f;
+    }
+    float mx = -INFINITY, den = 0.f;
+    if (a.sink) {
+      mx = a.sink[h];
+      den = 1.f;
+    }
+    const int64_t nsel = a.k;
+    const int64_t nwin = whi >= wlo ? whi - wlo + 1 : 0;
+    for (int64_t j = 0; j < nsel + nwin; ++j) {
+      int64_t off;
+      const void* src;
+      if (j < nsel) {
+        const int32_t e = idx[j];
+        if (e < 0 || e >= a.n_cap) continue;
+        src = a.entries;
+        off = (int64_t)b * a.entries_seq_stride + (int64_t)e * a.D;
+      } else {
+        src = a.raw;
+        off = (int64_t)b * a.raw_seq_stride + (wlo + (j - nsel) - a.raw_pos0) * a.raw_ld;
+      }
+      float kv[kMaxPer];
+      float part = 0.f;
+      for (int jj = 0; jj < kMaxPer; ++jj) {
+        const int d = lane + 64 * jj;
+        kv[jj] = (jj < per && d < a.D) ? load_elem<DT>(src, off + d) : 0.f;
+        part = fmaf(qv[jj], kv[jj], part);
+      }
+      const float l = wave_sum(part);
+      const float nm = fmaxf(mx, l);
+      const float sc = expf(mx - nm);
+      const float pe = expf(l - nm);
+      den = den * sc + pe;
+      for (int jj = 0; jj < kMaxPer; ++jj) ov[jj] = fmaf(ov[jj], sc, pe * kv[jj]);
+      mx = nm;
+    }
+    const float inv = 1.f / den;
+    const int64_t ooff = (row * a.H + h) * (int64_t)a.D;
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int d = lane + 64 * j;
+      if (j < per && d < a.D) store_elem<OT>(a.out, ooff + d, ov[j] * inv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MFMA (bf16, D = 512)
+
+constexpr int kHG = 64;        // heads per workgroup
+constexpr int kNK = 32;        // keys per tile
+constexpr int kVT = 40;        // LDS row stride (bf16) of the transposed key quarter and of P
+constexpr int kDQ = 128;       // dims per wave
+
+struct AttnSmem {
+  float sred[4][kHG][kNK];         // partial logits per wave          32 KiB
+  uint16_t vt[4][kDQ][kVT];        // key quarters, dim-major          40 KiB
+  uint16_t pl[kHG][kVT];           // probabilities, bf16              5 KiB
+  float alpha[kHG];                // per-head rescale of O this tile
+  float lsum[kHG];                 // per-head running denominators
+  int32_t keys[1];                 // gathered key list (entry ids >= 0, window rows as -(r+1))
+};
+
+template <int OT>
+__global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int64_t row = blockIdx.x / n_groups;
+  const int hg = (int)(blockIdx.x % n_groups);
+  const int b = (int)(row / a.T), t = (int)(row % a.T);
+  const int64_t p = a.q_pos0 + t;
+  const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
+
+  // ---- key list: valid selected entries, then the window rows
+  int nsel = 0;
+  if (wave == 0) {
+    const int32_t* idx = a.idx + row * a.k;
+    for (int base = 0; base < a.k; base += 64) {
+      const int j = base + lane;
+      const int32_t e = j < a.k ? idx[j] : -1;
+      const bool ok = e >= 0 && e < a.n_cap;
+      const uint64_t bm = __ballot(ok);
+      if (ok) sm.keys[nsel + __popcll(bm & lanemask_lt())] = e;
+      nsel += __popcll(bm);
+    }
+    const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
+    for (int j = lane; j < nwin; j += 64) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
+    if (lane == 0) sm.keys[a.k + a.W] = nsel + nwin;
+  }
+  __syncthreads();
+  const int nkeys = sm.keys[a.k + a.W];
+
+  // ---- q quarter as A-fragments: head hg*64 + mt*32 + lane%32, dims wave*128 + s*16 + (lane/32)*8
+  const float scale = a.scale * 1.4426950408889634f;  // logits in log2 units
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld +
+                         (int64_t)hg * kHG * 512 + wave * kDQ;
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[mt][s] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)(mt * 32 + (lane & 31)) * 512 + s * 16 + (lane >> 5) * 8);
+
+  f32x16 o[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x16{};
+
+  // softmax ownership: wave w handles heads w*16 + lane/4, keys (lane%4)*8 .. +7
+  const int sh = wave * 16 + (lane >> 2);
+  const int sk0 = (lane & 3) * 8;
+  float m_run = -INFINITY, l_run = 0.f;
+  if (a.sink) {
+    m_run = a.sink[hg * kHG + sh] * 1.4426950408889634f;
+    l_run = 1.f;
+  }
+
+  const uint16_t* ent = static_cast<const uint16_t*>(a.entries) + (int64_t)b * a.entries_seq_stride;
+  const uint16_t* raw = static_cast<const uint16_t*>(a.raw) + (int64_t)b * a.raw_seq_stride;
+  const int ntiles = (nkeys + kNK - 1) / kNK;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    // ---- this wave's quarter of 32 keys as B-fragments: key lane%32, dims s*16 + (lane/32)*8
+    const int kj = tile * kNK + (lane & 31);
+    const bool kok = kj < nkeys;
+    const uint16_t* krow = nullptr;
+    if (kok) {
+      const int32_t id = sm.keys[kj];
+      krow = id >= 0 ? ent + (int64_t)id * 512 : raw + (int64_t)(-id - 1) * a.raw_ld;
+    }
+    uint4 ku[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      ku[s] = kok ? *reinterpret_cast<const uint4*>(krow + wave * kDQ + s * 16 + (lane >> 5) * 8) : make_uint4(0, 0, 0, 0);
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, ku[s]);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, sacc[1], 0, 0, 0);
+    }
+    // partial logits -> LDS: head mt*32 + (r/4)*8 + (lane/32)*4 + r%4, key lane%32
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sm.sred[wave][mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)][lane & 31] = sacc[mt][r];
+    // key quarter, transposed: vt[dim][key]
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t w4[4] = {ku[s].x, ku[s].y, ku[s].z, ku[s].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        sm.vt[wave][s * 16 + (lane >> 5) * 8 + j][lane & 31] = (uint16_t)(w4[j >> 1] >> ((j & 1) * 16));
+    }
+    __syncthreads();
+
+    // ---- online softmax of 16 heads x 32 keys per wave
+    {
+      float sv[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = sk0 + j;
+        float v = sm.sred[0][sh][key] + sm.sred[1][sh][key] + sm.sred[2][sh][key] + sm.sred[3][sh][key];
+        v = (tile * kNK + key < nkeys) ? v * scale : -INFINITY;
+        sv[j] = v;
+        tmax = fmaxf(tmax, v);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      const float al = exp2f(m_run - m_new);
+      float psum = 0.f;
+      uint16_t pb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pe = exp2f(sv[j] - m_new);
+        const uint16_t h16 = f2bf(pe);
+        pb[j] = h16;
+        psum += bf2f(h16);  // the denominator sums the same rounded weights P V uses
+      }
+      psum += __shfl_xor(psum, 1, 64);
+      psum += __shfl_xor(psum, 2, 64);
+      l_run = l_run * al + psum;
+      m_run = m_new;
+      *reinterpret_cast<uint4*>(&sm.pl[sh][sk0]) =
+          make_uint4(pb[0] | ((uint32_t)pb[1] << 16), pb[2] | ((uint32_t)pb[3] << 16), pb[4] | ((uint32_t)pb[5] << 16),
+                     pb[6] | ((uint32_t)pb[7] << 16));
+      if ((lane & 3) == 0) {
+        sm.alpha[sh] = al;
+        sm.lsum[sh] = l_run;
+      }
+    }
+    __syncthreads();
+
+    // ---- O = alpha * O + P V over this wave's 128 dims
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      float al[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) al[r] = sm.alpha[mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
+      bf16x8 pf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pf[ks] = *reinterpret_cast<const bf16x8*>(&sm.pl[mt * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mt][nt][r] *= al[r];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sm.vt[wave][nt * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8]);
+          o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[ks], vf, o[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // ---- normalise and store: head hg*64 + row index, dim wave*128 + nt*32 + lane%32
+  const int64_t obase = (row * a.H + (int64_t)hg * kHG) * 512 + wave * kDQ;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const float inv = 1.f / sm.lsum[h];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) store_elem<OT>(a.out, obase + (int64_t)h * 512 + nt * 32 + (lane & 31), o[mt][nt][r] * inv);
+    }
+}
+
+int attn_mfma_lds(const AttnArgs& a) { return (int)(sizeof(AttnSmem) + (size_t)(a.k + a.W + 1) * 4); }
+
+bool use_attn_mfma(const AttnArgs& a) {
+  return a.in_dtype == CSA_BF16 && a.D == 512 && a.H % kHG == 0 && a.raw_ld % 8 == 0 && a.q_ld % 8 == 0 &&
+         a.q_seq_stride % 8 == 0 && a.entries_seq_stride % 8 == 0 && a.raw_seq_stride % 8 == 0;
+}
+
+}  // namespace
+
+size_t attn_workspace(const AttnArgs&) { return 0; }
+
+hipError_t launch_attn(const AttnArgs& a, void*, size_t, hipStream_t s) {
+  const int64_t R = (int64_t)a.B * a.T;
+  if (R == 0) return hipSuccess;
+  hipError_t e;
+  if (use_attn_mfma(a)) {
+    const int ng = a.H / kHG;
+    const int lds = attn_mfma_lds(a);
+    if (a.out_dtype == CSA_BF16) {
+      if ((e = allow_lds((const void*)attn_mfma<CSA_BF16>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(attn_mfma<CSA_BF16>, dim3((unsigned)(R * ng)), dim3(256), lds, s, a, ng);
+    } else {
+      if ((e = allow_lds((const void*)attn_mfma<CSA_F32>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(attn_mfma<CSA_F32>, dim3((unsigned)(R * ng)), dim3(256), lds, s, a, ng);
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)R), block(kGenWaves * 64);
+  if (a.in_dtype == CSA_F32 && a.out_dtype == CSA_F32)
+    hipLaunchKernelGGL((attn_generic<CSA_F32, CSA_F32>), grid, block, 0, s, a);
+  else if (a.in_dtype == CSA_F32)
+    hipLaunchKernelGGL((attn_generic<CSA_F32, CSA_BF16>), grid, block, 0, s, a);
+  else if (a.out_dtype == CSA_F32)
+    hipLaunchKernelGGL((attn_generic<CSA_BF16, CSA_F32>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_generic<CSA_BF16, CSA_BF16>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,112 @@
+// Shared device helpers of the CSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+// ------------------------------------------------------------------ vector types for MFMA
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ bf16 <-> f32
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<CSA_F32>(const void* p, int64_t i) {
+  return static_cast<const float*>(p)[i];
+}
+template <>
+__device__ __forceinline__ float load_elem<CSA_BF16>(const void* p, int64_t i) {
+  return bf2f(static_cast<const uint16_t*>(p)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_elem<CSA_F32>(void* p, int64_t i, float v) {
+  static_cast<float*>(p)[i] = v;
+}
+template <>
+__device__ __forceinline__ void store_elem<CSA_BF16>(void* p, int64_t i, float v) {
+  static_cast<uint16_t*>(p)[i] = f2bf(v);
+}
+
+// ------------------------------------------------------------------ wave helpers
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Orders this wave's LDS traffic around the call (the wave executes in lockstep; the fence keeps
+// the compiler from moving LDS accesses across it).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int l = lane_id();
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, 64);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = __shfl((uint32_t)v, src, 64);
+  uint32_t hi = __shfl((uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w < v ? w : v;
+  }
+  return v;
+}
+
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// n_vis(p) = min(floor((p+1)/m), n_cap): entries whose block is complete at position p.
+__device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t n_cap) {
+  int64_t v = (p + 1) / m;
+  if (v < 0) v = 0;
+  return v < n_cap ? v : n_cap;
+}
+
+}  // namespace csa

@@ -1,0 +1,424 @@
+// Steps 2+3: the lightning indexer fused with top-k selection.
+//
+//   s[t, i] = sum_h w[h] * max(0, q_I[t, h, :] . k_I[i, :]),  i < n_vis(p_t)
+// ("The Exchange Rates of a Million Tokens", section 3: ReLU-gated dot products; "Anatomy of a
+// Frontier Model", bullet "Compressed Sparse Attention (CSA)": 64 heads x 128 dims, FP4 q/k.)
+//
+// Three paths:
+//  * index_prefill_mfma (bf16, H_I = 64, D_I = 128, many query rows per sequence): a workgroup
+//    holds QW consecutive query rows of one sequence, one per wave, with each wave's q_I (64 heads x
+//    128 dims) resident in VGPRs as MFMA A-fragments. Key tiles of 64 entries stream through
+//    double-buffered LDS and are shared by the QW waves. Per tile a wave runs 32
+//    v_mfma_f32_32x32x16_bf16 (heads along the accumulator rows, entries along its columns),
+//    reduces w_h * ReLU over the 32 heads it holds in registers plus one cross-half shuffle, and
+//    offers the 64 scores to its query's streaming top-k buffer in LDS. The T x N score matrix is
+//    never written.
+//  * decode (few query rows, long contexts): scores of every (row, entry) are written to the
+//    workspace by a key-streaming MFMA kernel (bf16, or MXFP4 through the scaled
+//    v_mfma_scale_f32_16x16x128_f8f6f4 with e8m0 block scales), then selected by the top-k pass.
+//  * index_generic (any dims, fp32 / bf16 / MXFP4): one wave per query row, scalar FMA scores,
+//    same streaming selection.
+#include "kernels.h"
+#include "topk_wave.h"
+
+namespace csa {
+
+namespace {
+
+// ---------------------------------------------------------------- element access
+
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  const float v = mag[code & 7u];
+  return (code & 8u) ? -v : v;
+}
+
+// Element d of an indexer row; for MXFP4 `row` addresses the code bytes and `sc` its scales.
+template <int DT>
+__device__ __forceinline__ float idx_elem(const void* row, const uint8_t* sc, int d);
+template <>
+__device__ __forceinline__ float idx_elem<CSA_F32>(const void* row, const uint8_t*, int d) {
+  return static_cast<const float*>(row)[d];
+}
+template <>
+__device__ __forceinline__ float idx_elem<CSA_BF16>(const void* row, const uint8_t*, int d) {
+  return bf2f(static_cast<const uint16_t*>(row)[d]);
+}
+template <>
+__device__ __forceinline__ float idx_elem<CSA_MXFP4>(const void* row, const uint8_t* sc, int d) {
+  const uint8_t byte = static_cast<const uint8_t*>(row)[d >> 1];
+  const uint32_t code = (d & 1) ? (byte >> 4) : (byte & 15u);
+  return ldexpf(e2m1_value(code), (int)sc[d >> 5] - 127);
+}
+
+template <int DT>
+__device__ __forceinline__ int64_t row_units(int D_I) {
+  return DT == CSA_MXFP4 ? D_I / 2 : D_I;  // elements, or code bytes for MXFP4
+}
+
+template <int DT>
+__device__ __forceinline__ const void* advance(const void* p, int64_t units) {
+  if (DT == CSA_F32) return static_cast<const float*>(p) + units;
+  if (DT == CSA_BF16) return static_cast<const uint16_t*>(p) + units;
+  return static_cast<const uint8_t*>(p) + units;
+}
+
+__device__ __forceinline__ const float* head_weights(const IndexArgs& a, int64_t row) {
+  return a.w_ld ? a.w + row * a.w_ld : a.w;
+}
+
+// ---------------------------------------------------------------- generic fused path
+
+constexpr int kGenWaves = 4;
+
+template <int DT>
+__global__ void __launch_bounds__(kGenWaves * 64) index_generic(IndexArgs a, int cap) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int64_t row = (int64_t)blockIdx.x * kGenWaves + wave;
+  if (row >= (int64_t)a.B * a.T) return;
+  const int b = (int)(row / a.T), t = (int)(row % a.T);
+  uint64_t* buf = reinterpret_cast<uint64_t*>(smem) + (int64_t)wave * cap;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<uint64_t*>(smem) + kGenWaves * cap) + wave * 256;
+  const int64_t nv = n_visible(a.q_pos0 + t, a.m, a.n_cap);
+  const int64_t ru = row_units<DT>(a.D_I);
+  const int nsb = a.D_I / 32;
+  const void* q = advance<DT>(a.q, (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld);
+  const uint8_t* qs = DT == CSA_MXFP4 ? a.q_scale + row * a.H_I * nsb : nullptr;
+  const float* w = head_weights(a, row);
+  WaveTopK tk;
+  tk.init(buf, hist, cap, a.k);
+  for (int64_t base = 0; base < nv; base += 64) {
+    const int64_t i = base + lane;
+    const bool valid = i < nv;
+    float s = 0.f;
+    if (valid) {
+      const void* krow = advance<DT>(a.keys, (int64_t)b * a.keys_seq_stride + i * ru);
+      const uint8_t* ks = DT == CSA_MXFP4 ? a.k_scale + ((int64_t)b * a.n_cap + i) * nsb : nullptr;
+      for (int h = 0; h < a.H_I; ++h) {
+        const void* qh = advance<DT>(q, (int64_t)h * ru);
+        const uint8_t* qhs = DT == CSA_MXFP4 ? qs + h * nsb : nullptr;
+        float dot = 0.f;
+        for (int d = 0; d < a.D_I; ++d) dot = fmaf(idx_elem<DT>(qh, qhs, d), idx_elem<DT>(krow, ks, d), dot);
+        s = fmaf(w[h], fmaxf(dot, 0.f), s);
+      }
+    }
+    tk.offer(make_cand(s, (uint32_t)i), valid);
+  }
+  tk.finish(a.out_idx + row * a.k, a.out_score ? a.out_score + row * a.k : nullptr);
+}
+
+// ---------------------------------------------------------------- fused MFMA prefill path
+
+constexpr int kNE = 64;     // entries per key tile
+constexpr int kLDK = 136;   // LDS row stride of a key row in bf16 (128 + 8: conflict-free b128 reads)
+constexpr int kTileBytes = kNE * kLDK * 2;
+
+template <int QW>
+__global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int cap, int t_blocks) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* ktile = reinterpret_cast<uint16_t*>(smem);
+  uint64_t* bufs = reinterpret_cast<uint64_t*>(smem + 2 * kTileBytes);
+  uint32_t* hists = reinterpret_cast<uint32_t*>(bufs + (int64_t)QW * cap);
+
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int b = blockIdx.x / t_blocks;
+  const int tb = t_blocks - 1 - (int)(blockIdx.x % t_blocks);  // heaviest (latest) rows first
+  const int t0 = tb * QW;
+  const int t = t0 + wave;
+  const bool active = t < a.T;
+  const int tq = active ? t : t0;
+  const int64_t row = (int64_t)b * a.T + tq;
+  const int64_t nv = active ? n_visible(a.q_pos0 + t, a.m, a.n_cap) : 0;
+  const int t_last = (t0 + QW < a.T ? t0 + QW : a.T) - 1;
+  const int64_t nv_max = n_visible(a.q_pos0 + t_last, a.m, a.n_cap);
+
+  // q_I of this wave's row as A-fragments: heads mt*32 + lane%32, dims s*16 + (lane/32)*8 .. +7
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)tq * a.q_ld;
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[mt][s] = *reinterpret_cast<const bf16x8*>(qrow + (mt * 32 + (lane & 31)) * 128 + s * 16 + (lane >> 5) * 8);
+  // head weights of the accumulator rows this lane holds: head = mt*32 + (r/4)*8 + (lane/32)*4 + r%4
+  const float* w = head_weights(a, row);
+  float wr[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[mt][r] = w[mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
+
+  WaveTopK tk;
+  tk.init(bufs + (int64_t)wave * cap, hists + wave * 256, cap, a.k);
+
+  const uint16_t* kseq = static_cast<const uint16_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
+  const int ntiles = (int)ceil_div(nv_max, kNE);
+  constexpr int kChunks = kNE * 16;               // 16-byte chunks per tile
+  constexpr int kPer = kChunks / (QW * 64);       // chunks per thread
+  uint4 stage[kPer];
+
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = threadIdx.x + j * QW * 64;
+      const int r = c >> 4, c16 = c & 15;
+      const int64_t e = (int64_t)tile * kNE + r;
+      stage[j] = e < nv_max ? *reinterpret_cast<const uint4*>(kseq + e * 128 + c16 * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = threadIdx.x + j * QW * 64;
+      const int r = c >> 4, c16 = c & 15;
+      *reinterpret_cast<uint4*>(ktile + buf * (kNE * kLDK) + r * kLDK + c16 * 8) = stage[j];
+    }
+  };
+
+  if (ntiles > 0) {
+    fetch(0);
+    put(0);
+  }
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int cur = tile & 1;
+    if (tile + 1 < ntiles) fetch(tile + 1);
+    if (active && (int64_t)tile * kNE < nv) {
+      const uint16_t* kt = ktile + cur * (kNE * kLDK);
+      float sc[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + (nt * 32 + (lane & 31)) * kLDK + s * 16 + (lane >> 5) * 8);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, acc1, 0, 0, 0);
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p = fmaf(wr[0][r], fmaxf(acc0[r], 0.f), p);
+          p = fmaf(wr[1][r], fmaxf(acc1[r], 0.f), p);
+        }
+        p += __shfl_xor(p, 32, 64);
+        sc[nt] = p;
+      }
+      // lane < 32 takes entry tile*64 + lane (first column tile), lane >= 32 the second tile's
+      const float s = lane < 32 ? sc[0] : sc[1];
+      const int64_t i = (int64_t)tile * kNE + lane;
+      tk.offer(make_cand(s, (uint32_t)i), i < nv);
+    }
+    if (tile + 1 < ntiles) put(cur ^ 1);
+    __syncthreads();
+  }
+  if (active) tk.finish(a.out_idx + row * a.k, a.out_score ? a.out_score + row * a.k : nullptr);
+}
+
+constexpr int kPrefillQW = 8;
+
+int prefill_lds(int cap) { return 2 * kTileBytes + kPrefillQW * (cap * 8 + 256 * 4); }
+
+// ---------------------------------------------------------------- decode scores
+
+constexpr int kScoreWaves = 4;
+constexpr int kScoreTiles = 4;   // 64-entry tiles per wave
+constexpr int kScoreChunk = kScoreWaves * kScoreTiles * 64;
+
+// scores[row, i] for i < n_vis(row); n_valid[row] = n_vis(row).
+__global__ void __launch_bounds__(kScoreWaves * 64) score_bf16_mfma(IndexArgs a, float* scores, int32_t* n_valid) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int64_t row = blockIdx.y;
+  const int b = (int)(row / a.T), t = (int)(row % a.T);
+  const int64_t nv = n_visible(a.q_pos0 + t, a.m, a.n_cap);
+  if (blockIdx.x == 0 && threadIdx.x == 0) n_valid[row] = (int32_t)nv;
+  const int64_t base0 = (int64_t)blockIdx.x * kScoreChunk + (int64_t)wave * kScoreTiles * 64;
+  if (base0 >= nv) return;
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld;
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[mt][s] = *reinterpret_cast<const bf16x8*>(qrow + (mt * 32 + (lane & 31)) * 128 + s * 16 + (lane >> 5) * 8);
+  const float* w = head_weights(a, row);
+  float wr[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[mt][r] = w[mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
+  const uint16_t* kseq = static_cast<const uint16_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
+  float* srow = scores + row * a.n_cap;
+  for (int tl = 0; tl < kScoreTiles; ++tl) {
+    const int64_t base = base0 + (int64_t)tl * 64;
+    if (base >= nv) break;
+    float sc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t e = base + nt * 32 + (lane & 31);
+      const bool ok = e < nv;
+      bf16x8 kf[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if (ok) {
+          kf[s] = *reinterpret_cast<const bf16x8*>(kseq + e * 128 + s * 16 + (lane >> 5) * 8);
+        } else {
+          kf[s] = bf16x8{};
+        }
+      }
+      f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf[s], acc1, 0, 0, 0);
+      }
+      float p = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p = fmaf(wr[0][r], fmaxf(acc0[r], 0.f), p);
+        p = fmaf(wr[1][r], fmaxf(acc1[r], 0.f), p);
+      }
+      p += __shfl_xor(p, 32, 64);
+      sc[nt] = p;
+    }
+    const int64_t i = base + lane;
+    if (i < nv) srow[i] = lane < 32 ? sc[0] : sc[1];
+  }
+}
+
+// MXFP4 q/k: A = q (16 heads x 128 dims per M-tile), B = keys (128 dims x 16 entries); lane l holds
+// row/column l%16 and the 32-element block l/16 (16 code bytes) plus that block's e8m0 scale.
+__global__ void __launch_bounds__(kScoreWaves * 64) score_fp4_mfma(IndexArgs a, float* scores, int32_t* n_valid) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int64_t row = blockIdx.y;
+  const int b = (int)(row / a.T), t = (int)(row % a.T);
+  const int64_t nv = n_visible(a.q_pos0 + t, a.m, a.n_cap);
+  if (blockIdx.x == 0 && threadIdx.x == 0) n_valid[row] = (int32_t)nv;
+  const int64_t base0 = (int64_t)blockIdx.x * kScoreChunk + (int64_t)wave * kScoreTiles * 64;
+  if (base0 >= nv) return;
+  const int g = lane >> 4, c = lane & 15;
+  const uint8_t* qcodes = static_cast<const uint8_t*>(a.q) + row * (64 * 64);
+  const uint8_t* qsc = a.q_scale + row * (64 * 4);
+  i32x8 qa[4];
+  int qs[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(qcodes + (mt * 16 + c) * 64 + g * 16);
+    qa[mt] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    qs[mt] = qsc[(mt * 16 + c) * 4 + g];
+  }
+  const float* w = head_weights(a, row);
+  float wr[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wr[mt][r] = w[mt * 16 + g * 4 + r];
+  const uint8_t* kcodes = static_cast<const uint8_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
+  const uint8_t* ksc = a.k_scale + (int64_t)b * a.n_cap * 4;
+  float* srow = scores + row * a.n_cap;
+  for (int tl = 0; tl < kScoreTiles; ++tl) {
+    const int64_t base = base0 + (int64_t)tl * 64;
+    if (base >= nv) break;
+    float mine = 0.f;
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int64_t e = base + grp * 16 + c;
+      i32x8 kb = {};
+      int ks = 127;
+      if (e < nv) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(kcodes + e * 64 + g * 16);
+        kb = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        ks = ksc[e * 4 + g];
+      }
+      float p = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 acc = {};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb, acc, 4, 4, 0, qs[mt], 0, ks);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p = fmaf(wr[mt][r], fmaxf(acc[r], 0.f), p);
+      }
+      p += __shfl_xor(p, 16, 64);
+      p += __shfl_xor(p, 32, 64);
+      if (g == grp) mine = p;
+    }
+    const int64_t i = base + lane;
+    if (i < nv) srow[i] = mine;
+  }
+}
+
+constexpr int kMaxLds = 160 * 1024;
+
+bool use_prefill_mfma(const IndexArgs& a) {
+  return a.idx_dtype == CSA_BF16 && a.H_I == 64 && a.D_I == 128 && a.T >= kPrefillQW &&
+         prefill_lds(topk_cap_for(a.k, 512)) <= kMaxLds;
+}
+bool use_decode_scores(const IndexArgs& a) {
+  if (a.H_I != 64 || a.D_I != 128) return false;
+  if (a.idx_dtype == CSA_MXFP4) return true;
+  return a.idx_dtype == CSA_BF16 && a.T < kPrefillQW;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t index_topk_workspace(const IndexArgs& a) {
+  if (!use_decode_scores(a)) return 0;
+  const int64_t R = (int64_t)a.B * a.T;
+  return align256((size_t)R * a.n_cap * 4) + align256((size_t)R * 4) + topk_workspace((int)R, a.n_cap, a.k);
+}
+
+hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
+  const int64_t R = (int64_t)a.B * a.T;
+  if (R == 0) return hipSuccess;
+  hipError_t e;
+  if (use_prefill_mfma(a)) {
+    const int cap = topk_cap_for(a.k, 512);
+    const int lds = prefill_lds(cap);
+    if ((e = allow_lds((const void*)index_prefill_mfma<kPrefillQW>, lds)) != hipSuccess) return e;
+    const int t_blocks = (int)ceil_div(a.T, kPrefillQW);
+    hipLaunchKernelGGL(index_prefill_mfma<kPrefillQW>, dim3((unsigned)(a.B * t_blocks)), dim3(kPrefillQW * 64),
+                       lds, s, a, cap, t_blocks);
+    return hipGetLastError();
+  }
+  if (use_decode_scores(a)) {
+    if (ws == nullptr || ws_bytes < index_topk_workspace(a)) return hipErrorInvalidValue;
+    uint8_t* p = static_cast<uint8_t*>(ws);
+    float* scores = reinterpret_cast<float*>(p);
+    p += align256((size_t)R * a.n_cap * 4);
+    int32_t* nvalid = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)R * 4);
+    dim3 grid((unsigned)ceil_div(a.n_cap, kScoreChunk) > 0 ? (unsigned)ceil_div(a.n_cap, kScoreChunk) : 1u,
+              (unsigned)R);
+    if (a.idx_dtype == CSA_MXFP4) {
+      hipLaunchKernelGGL(score_fp4_mfma, grid, dim3(kScoreWaves * 64), 0, s, a, scores, nvalid);
+    } else {
+      hipLaunchKernelGGL(score_bf16_mfma, grid, dim3(kScoreWaves * 64), 0, s, a, scores, nvalid);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    TopkArgs t{scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score};
+    return launch_topk_from_scores(t, p, ws_bytes - (size_t)(p - static_cast<uint8_t*>(ws)), s);
+  }
+  const int cap = topk_cap_for(a.k, 256);
+  const int lds = kGenWaves * (cap * 8 + 256 * 4);
+  const dim3 grid((unsigned)ceil_div(R, kGenWaves));
+  switch (a.idx_dtype) {
+    case CSA_F32:
+      if ((e = allow_lds((const void*)index_generic<CSA_F32>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(index_generic<CSA_F32>, grid, dim3(kGenWaves * 64), lds, s, a, cap);
+      break;
+    case CSA_BF16:
+      if ((e = allow_lds((const void*)index_generic<CSA_BF16>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(index_generic<CSA_BF16>, grid, dim3(kGenWaves * 64), lds, s, a, cap);
+      break;
+    default:
+      if ((e = allow_lds((const void*)index_generic<CSA_MXFP4>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(index_generic<CSA_MXFP4>, grid, dim3(kGenWaves * 64), lds, s, a, cap);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

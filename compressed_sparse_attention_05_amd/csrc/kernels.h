@@ -1,0 +1,95 @@
+// Internal launch interface between the C ABI (api.hip) and the kernel translation units.
+#pragma once
+
+#include "common.h"
+
+namespace csa {
+
+struct CompressArgs {
+  int B, n_new, m, c;
+  int64_t first_entry;
+  int in_dtype, out_dtype;
+  const void *ca, *za, *cb, *zb;
+  int64_t ld, seq_stride;
+  const void *halo_cb, *halo_zb;
+  int64_t halo_ld, halo_seq_stride;
+  const float *bias_a, *bias_b;
+  void* entries;
+  int64_t entries_seq_stride;
+  bool aligned16;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+int compress_max_m();
+
+// C[M, N] (row stride ldc) = A[M, K] (row stride lda) . Bm[N, K]^T (row stride ldb)
+struct GemmArgs {
+  int M, N, K;
+  int dtype, out_dtype;
+  const void* A;
+  int64_t lda;
+  const void* Bm;
+  int64_t ldb;
+  void* C;
+  int64_t ldc;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+struct IndexArgs {
+  int B, T;
+  int64_t q_pos0;
+  int m, H_I, D_I, k;
+  int idx_dtype;
+  const void* q;
+  int64_t q_ld, q_seq_stride;  // elements (bf16/f32) or bytes of codes (MXFP4)
+  const uint8_t* q_scale;      // MXFP4: [B, T, H_I, D_I/32]
+  const float* w;
+  int64_t w_ld;
+  const void* keys;
+  int64_t keys_seq_stride;     // elements (bf16/f32) or bytes of codes (MXFP4)
+  const uint8_t* k_scale;      // MXFP4: [B, n_cap, D_I/32]
+  int64_t n_cap;
+  int32_t* out_idx;
+  float* out_score;
+};
+size_t index_topk_workspace(const IndexArgs& a);
+hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+
+struct TopkArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* n_valid;  // device [R]
+  int R, k;
+  int32_t* out_idx;
+  float* out_score;
+};
+size_t topk_workspace(int R, int64_t n, int k);
+hipError_t launch_topk_from_scores(const TopkArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+
+struct AttnArgs {
+  int B, T;
+  int64_t q_pos0;
+  int H, D, k, W;
+  float scale;
+  int in_dtype, out_dtype;
+  const void* q;
+  int64_t q_ld, q_seq_stride;
+  const void* entries;
+  int64_t entries_seq_stride, n_cap;
+  const int32_t* idx;
+  const void* raw;
+  int64_t raw_ld, raw_seq_stride, raw_pos0, raw_len;
+  const float* sink;
+  void* out;
+};
+size_t attn_workspace(const AttnArgs& a);
+hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+
+// Copies rows: dst[b, r, :] = src[b, r, :] for r < rows, `cols` elements of `esize` bytes.
+hipError_t launch_copy_rows(int B, int rows, int cols, int esize, const void* src, int64_t src_ld,
+                            int64_t src_seq, void* dst, int64_t dst_ld, int64_t dst_seq,
+                            hipStream_t s);
+
+// Sets the dynamic-LDS ceiling of a kernel once (needed above 64 KiB).
+hipError_t allow_lds(const void* kernel, int bytes);
+
+}  // namespace csa

@@ -1,0 +1,200 @@
+// Wave-level streaming top-k selection in LDS.
+//
+// Each candidate (score s, entry i) is packed into one 64-bit key that orders candidates exactly as
+// the layer's selection does: larger score first, equal scores toward the smaller entry index.
+//   high 32 bits: order-preserving map of the float32 score (-0 mapped to +0)
+//   low  32 bits: ~i
+// All keys of one query are distinct, so "the k largest keys" is a unique set and a threshold on
+// the key selects it exactly.
+//
+// One wave owns one query's candidate buffer (capacity `cap` >= k + 64). Candidates above the
+// running threshold are appended (ballot + prefix popcount, no atomics). When a batch would
+// overflow the buffer, a radix select (8-bit digits, most significant first, histogram in LDS)
+// finds the k-th largest key, the buffer is compacted to the k keys at or above it, and that key
+// becomes the new threshold. At the end the kept entries are sorted ascending by entry index with
+// a bitonic network and written out, padded with -1.
+//
+// Every function must be called by all 64 lanes of the wave with uniform arguments.
+#pragma once
+
+#include "common.h"
+
+namespace csa {
+
+__device__ __forceinline__ uint32_t score_to_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;  // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t make_cand(float s, uint32_t idx) {
+  return ((uint64_t)score_to_key(s) << 32) | (uint32_t)(~idx);
+}
+
+struct WaveTopK {
+  uint64_t* buf;   // LDS, cap entries
+  uint32_t* hist;  // LDS, 256 counters
+  int cap;
+  int k;
+  int cnt;         // wave-uniform
+  uint64_t thr;    // wave-uniform: a candidate enters iff key > thr
+
+  __device__ void init(uint64_t* b, uint32_t* h, int capacity, int kk) {
+    buf = b;
+    hist = h;
+    cap = capacity;
+    k = kk;
+    cnt = 0;
+    thr = 0;
+  }
+
+  // Threshold T with exactly k keys >= T among buf[0, cnt) (requires cnt >= k >= 1).
+  __device__ uint64_t kth_threshold() {
+    const int lane = lane_id();
+    uint64_t prefix = 0, pmask = 0;
+    uint32_t krem = (uint32_t)k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int b = lane; b < 256; b += 64) hist[b] = 0;
+      wave_sync();
+      for (int i = lane; i < cnt; i += 64) {
+        const uint64_t key = buf[i];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+      }
+      wave_sync();
+      // lane l owns digits 255-4l .. 252-4l, scanned from the top digit down
+      uint32_t c[4];
+      uint32_t local = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[255 - 4 * lane - j];
+        local += c[j];
+      }
+      const uint32_t incl = wave_incl_scan(local);
+      const uint32_t excl = incl - local;
+      const bool mine = (excl < krem) && (krem <= incl);
+      const uint64_t who = __ballot(mine);
+      const int src = __ffsll((unsigned long long)who) - 1;
+      uint32_t digit = 0, above = excl, inbin = 0;
+      if (mine) {
+        uint32_t run = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (run + c[j] >= krem) {
+            digit = 255u - 4u * lane - j;
+            above = run;
+            inbin = c[j];
+            break;
+          }
+          run += c[j];
+        }
+      }
+      digit = __shfl(digit, src, 64);
+      above = __shfl(above, src, 64);
+      inbin = __shfl(inbin, src, 64);
+      wave_sync();
+      prefix |= (uint64_t)digit << shift;
+      pmask |= 255ull << shift;
+      krem -= above;
+      if (inbin == krem) break;  // every key with this prefix is in: prefix (low bits 0) works
+    }
+    return prefix;
+  }
+
+  // Keep the keys >= T (exactly k of them) at the front; the smallest kept becomes thr.
+  __device__ void compact_to(uint64_t T) {
+    const int lane = lane_id();
+    int out = 0;
+    uint64_t mn = ~0ull;
+    for (int base = 0; base < cnt; base += 64) {
+      const int i = base + lane;
+      const uint64_t key = i < cnt ? buf[i] : 0ull;
+      const bool keep = (i < cnt) && (key >= T);
+      const uint64_t bm = __ballot(keep);
+      wave_sync();
+      if (keep) {
+        buf[out + __popcll(bm & lanemask_lt())] = key;
+        mn = key < mn ? key : mn;
+      }
+      out += __popcll(bm);
+      wave_sync();
+    }
+    cnt = out;
+    thr = wave_min_u64(mn);
+  }
+
+  __device__ void shrink() { compact_to(kth_threshold()); }
+
+  // Offer one candidate per lane (valid lanes only).
+  __device__ void offer(uint64_t key, bool valid) {
+    bool pass = valid && key > thr;
+    uint64_t bm = __ballot(pass);
+    int n = __popcll(bm);
+    if (n == 0) return;
+    if (cnt + n > cap) {
+      shrink();
+      pass = valid && key > thr;
+      bm = __ballot(pass);
+      n = __popcll(bm);
+    }
+    if (pass) buf[cnt + __popcll(bm & lanemask_lt())] = key;
+    cnt += n;
+    wave_sync();
+  }
+
+  // Final top-k, sorted by entry index ascending; out_idx[j] (and out_score[j]) for j < k.
+  __device__ void finish(int32_t* out_idx, float* out_score) {
+    const int lane = lane_id();
+    if (cnt > k) shrink();
+    // re-key as (index << 32 | score key) so that sorting orders by entry index
+    int P = 1;
+    while (P < k) P <<= 1;
+    for (int i = lane; i < P; i += 64) {
+      uint64_t v = ~0ull;
+      if (i < cnt) {
+        const uint64_t key = buf[i];
+        v = ((uint64_t)(~(uint32_t)key) << 32) | (key >> 32);
+      }
+      buf[i] = v;  // each lane rewrites only slots it read itself
+    }
+    wave_sync();
+    for (int size = 2; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = lane; t < (P >> 1); t += 64) {
+          const int i = (t / stride) * stride * 2 + (t % stride);
+          const int j = i + stride;
+          const bool up = (i & size) == 0;
+          const uint64_t a = buf[i], b = buf[j];
+          if ((a > b) == up) {
+            buf[i] = b;
+            buf[j] = a;
+          }
+        }
+        wave_sync();
+      }
+    }
+    for (int j = lane; j < k; j += 64) {
+      const uint64_t v = buf[j];
+      const uint32_t idx = (uint32_t)(v >> 32);
+      out_idx[j] = idx == 0xFFFFFFFFu ? -1 : (int32_t)idx;
+      if (out_score) out_score[j] = idx == 0xFFFFFFFFu ? -INFINITY : key_to_score((uint32_t)v);
+    }
+    wave_sync();
+  }
+};
+
+// LDS bytes one wave needs for a k-selection with capacity cap.
+__host__ __device__ inline int topk_cap_for(int k, int slack) {
+  int P = 1;
+  while (P < k) P <<= 1;
+  int cap = k + slack;
+  if (cap < k + 64) cap = k + 64;
+  if (cap < P) cap = P;
+  return (cap + 63) & ~63;
+}
+
+}  // namespace csa

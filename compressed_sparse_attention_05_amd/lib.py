@@ -1,0 +1,246 @@
+"""Thin ctypes binding of libcsa.so (include/csa.h) over torch tensors.
+
+Argument marshalling only: every step runs in the HIP kernels of libcsa.so. torch supplies device
+memory (tensors, workspaces) and the current HIP stream. There is no CPU fallback: if the library
+is missing, importing the entry points fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa.so")
+
+CSA_F32, CSA_BF16, CSA_MXFP4 = 0, 1, 2
+CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD = range(5)
+EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
+           "csa_topk_from_scores", "csa_sparse_attn", "csa_forward")
+
+
+class CsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"csa error {code}: {msg}")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("D", ctypes.c_int32), ("H", ctypes.c_int32), ("H_I", ctypes.c_int32),
+                ("D_I", ctypes.c_int32), ("top_k", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("w_proj", ctypes.c_void_p), ("bias_a", ctypes.c_void_p), ("bias_b", ctypes.c_void_p),
+                ("ibias_a", ctypes.c_void_p), ("ibias_b", ctypes.c_void_p), ("w_head", ctypes.c_void_p),
+                ("sink", ctypes.c_void_p)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("entries", ctypes.c_void_p), ("keys", ctypes.c_void_p), ("n_cap", ctypes.c_int64),
+                ("win", ctypes.c_void_p), ("win_cap", ctypes.c_int64), ("halo", ctypes.c_void_p),
+                ("halo_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libcsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m compressed_sparse_attention_05_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.csa_version.restype = i32
+    lib.csa_last_error.restype = ctypes.c_char_p
+    lib.csa_workspace_size.argtypes = [i32, ctypes.POINTER(Dims), i32, i32, i64, i32, i32, ctypes.POINTER(i64)]
+    lib.csa_compress.argtypes = [i32, i32, i64, i32, i32, i32, vp, vp, vp, vp, i64, i64, vp, vp, i64, i64, vp, vp,
+                                 vp, i64, i64, i32, vp]
+    lib.csa_index_topk.argtypes = [ctypes.POINTER(Dims), i32, i32, i64, i32, vp, i64, i64, vp, vp, i64, vp, i64, vp,
+                                   i64, vp, vp, vp, sz, vp]
+    lib.csa_topk_from_scores.argtypes = [vp, i64, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.csa_sparse_attn.argtypes = [ctypes.POINTER(Dims), i32, i32, i64, i32, vp, i64, i64, vp, i64, i64, vp, vp,
+                                    i64, i64, i64, i64, vp, vp, i32, vp, sz, vp]
+    lib.csa_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i32, i64, i32, i32, vp,
+                                ctypes.POINTER(Cache), vp, i32, vp, vp, sz, vp]
+    for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
+              "csa_forward"):
+        getattr(lib, f).restype = i32
+    _lib = lib
+    return lib
+
+
+def make_dims(m, D, H, H_I, D_I, top_k, window, sm_scale=0.0) -> Dims:
+    return Dims(m, D, H, H_I, D_I, top_k, window, sm_scale)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise CsaError(rc, load().csa_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dt(t) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    if t.dtype == torch.uint8:
+        return CSA_MXFP4
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
+    """A byte tensor large enough for an nbytes workspace at a 256-byte aligned address."""
+    return _workspace(nbytes, device)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned_ptr(ws):
+    if ws is None:
+        return None, 0
+    p = ws.data_ptr()
+    off = (-p) % 256
+    return p + off, ws.numel() - off
+
+
+def csa_version() -> int:
+    return load().csa_version()
+
+
+def csa_workspace_size(op: int, dims: Dims, B: int, T: int, n_cap: int, d_model: int = 0,
+                       idx_dtype: int = CSA_BF16) -> int:
+    out = ctypes.c_int64(0)
+    _check(load().csa_workspace_size(op, ctypes.byref(dims), B, T, n_cap, d_model, idx_dtype, ctypes.byref(out)))
+    return out.value
+
+
+def csa_compress(ca, za, cb, zb, bias_a, bias_b, entries, *, pos0: int, m: int, halo_cb=None, halo_zb=None):
+    """Step 1. ca/za/cb/zb: [B, T, c] views sharing strides; entries: [B, n_cap, c] (rows contiguous)."""
+    _require_cuda(ca, za, cb, zb, bias_a, bias_b, entries, halo_cb, halo_zb)
+    B, T, c = ca.shape
+    for v in (za, cb, zb):
+        if v.shape != ca.shape or v.stride() != ca.stride():
+            raise ValueError("ca, za, cb, zb must share shape and strides")
+    if ca.stride(2) != 1 or entries.stride(2) != 1 or entries.stride(1) != c:
+        raise ValueError("channel axes must be contiguous")
+    hl = hs = 0
+    if halo_cb is not None:
+        if halo_cb.stride() != halo_zb.stride() or halo_cb.stride(2) != 1:
+            raise ValueError("halo views must share strides with unit channel stride")
+        hl, hs = halo_cb.stride(1), halo_cb.stride(0)
+    _check(load().csa_compress(B, T, pos0, m, c, _dt(ca), _p(ca), _p(za), _p(cb), _p(zb), ca.stride(1), ca.stride(0),
+                               _p(halo_cb), _p(halo_zb), hl, hs, _p(bias_a), _p(bias_b), _p(entries),
+                               entries.stride(0), entries.shape[1], _dt(entries), _stream()))
+    return entries
+
+
+def csa_index_topk(dims: Dims, q_idx, w, keys, out_idx, *, q_pos0: int, q_scale=None, k_scale=None,
+                   out_score=None, ws=None):
+    """Steps 2+3. q_idx [B, T, H_I, D_I] (MXFP4: uint8 codes [B, T, H_I, D_I/2] + q_scale);
+    keys [B, n_cap, D_I] (MXFP4: uint8 [B, n_cap, D_I/2] + k_scale); w [H_I] or per row [B, T, H_I];
+    out_idx int32 [B, T, k]."""
+    _require_cuda(q_idx, w, keys, out_idx, q_scale, k_scale, out_score)
+    B, T = q_idx.shape[0], q_idx.shape[1]
+    n_cap = keys.shape[1]
+    dt = _dt(q_idx)
+    if dt == CSA_MXFP4:
+        q_ld = q_ss = 0
+        k_ss = 0
+    else:
+        if q_idx.stride(3) != 1 or q_idx.stride(2) != dims.D_I or keys.stride(2) != 1 or keys.stride(1) != dims.D_I:
+            raise ValueError("indexer rows must be contiguous")
+        q_ld, q_ss, k_ss = q_idx.stride(1), q_idx.stride(0), keys.stride(0)
+    w_ld = 0 if w.dim() == 1 else w.stride(-2)
+    if out_idx.shape != (B, T, dims.top_k) or out_idx.dtype != torch.int32 or not out_idx.is_contiguous():
+        raise ValueError("out_idx must be a contiguous int32 [B, T, top_k] tensor")
+    need = csa_workspace_size(CSA_OP_INDEX_TOPK, dims, B, T, n_cap, 0, dt)
+    if ws is None or ws.numel() < need + 256:
+        ws = _workspace(need, q_idx.device)
+    wp, wn = _aligned_ptr(ws)
+    _check(load().csa_index_topk(ctypes.byref(dims), B, T, q_pos0, dt, _p(q_idx), q_ld, q_ss, _p(q_scale), _p(w),
+                                 w_ld, _p(keys), k_ss, _p(k_scale), n_cap, _p(out_idx), _p(out_score), wp, wn,
+                                 _stream()))
+    return out_idx
+
+
+def csa_topk_from_scores(scores, n_valid, k: int, out_idx, out_score=None):
+    """Step 3 alone on float32 scores [R, n] with n_valid int32 [R]; out_idx int32 [R, k]."""
+    _require_cuda(scores, n_valid, out_idx, out_score)
+    R, n = scores.shape
+    if scores.stride(1) != 1:
+        raise ValueError("score rows must be contiguous")
+    d = make_dims(1, 1, 1, 1, 1, k, 1)
+    need = csa_workspace_size(CSA_OP_TOPK_FROM_SCORES, d, R, 1, scores.stride(0))
+    ws = _workspace(need, scores.device)
+    wp, wn = _aligned_ptr(ws)
+    _check(load().csa_topk_from_scores(_p(scores), scores.stride(0), _p(n_valid), R, k, _p(out_idx), _p(out_score),
+                                       wp, wn, _stream()))
+    return out_idx
+
+
+def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, raw_pos0: int, sink=None):
+    """Step 4. q [B, T, H, D]; entries [B, n_cap, D]; idx int32 [B, T, k]; kv_raw [B, R, D] whose row r is
+    position raw_pos0 + r; out [B, T, H, D] (float32 or bfloat16)."""
+    _require_cuda(q, entries, idx, kv_raw, out, sink)
+    B, T = q.shape[0], q.shape[1]
+    if q.stride(3) != 1 or q.stride(2) != dims.D or entries.stride(2) != 1 or entries.stride(1) != dims.D:
+        raise ValueError("q heads and entry rows must be contiguous")
+    if kv_raw.stride(2) != 1 or not out.is_contiguous() or not idx.is_contiguous():
+        raise ValueError("kv_raw rows, idx and out must be contiguous")
+    _check(load().csa_sparse_attn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
+                                  _p(entries), entries.stride(0), entries.shape[1], _p(idx), _p(kv_raw),
+                                  kv_raw.stride(1), kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out),
+                                  _dt(out), None, 0, _stream()))
+    return out
+
+
+class Forward:
+    """csa_forward with a reusable workspace (allocated once per shape, outside the timed call)."""
+
+    def __init__(self, dims: Dims, B: int, T: int, d_model: int, n_cap: int, dtype: int, device):
+        self.dims, self.B, self.T, self.d_model, self.dtype = dims, B, T, d_model, dtype
+        need = csa_workspace_size(CSA_OP_FORWARD, dims, B, T, n_cap, d_model, dtype)
+        self._ws = _workspace(need, device)
+        self._wp, self._wn = _aligned_ptr(self._ws)
+
+    def __call__(self, weights: dict, x, cache: dict, out, *, pos0: int, out_idx=None):
+        w = Weights(_p(weights["w_proj"]), _p(weights["bias_a"]), _p(weights["bias_b"]), _p(weights["ibias_a"]),
+                    _p(weights["ibias_b"]), _p(weights["w_head"]), _p(weights.get("sink")))
+        c = Cache(_p(cache["entries"]), _p(cache["keys"]), cache["entries"].shape[1], _p(cache["win"]),
+                  cache["win"].shape[1], _p(cache.get("halo")), _p(cache.get("halo_out")))
+        _check(load().csa_forward(ctypes.byref(self.dims), ctypes.byref(w), self.B, self.T, pos0, self.d_model,
+                                  self.dtype, _p(x), ctypes.byref(c), _p(out), _dt(out), _p(out_idx), self._wp,
+                                  self._wn, _stream()))
+        return out
+
+
+def csa_forward(dims: Dims, weights: dict, x, cache: dict, out, *, pos0: int, out_idx=None):
+    """The whole layer on x [B, T, d_model]; see include/csa.h for the cache layout."""
+    _require_cuda(x, out)
+    B, T, d = x.shape
+    f = Forward(dims, B, T, d, cache["entries"].shape[1], _dt(x), x.device)
+    return f(weights, x, cache, out, pos0=pos0, out_idx=out_idx)

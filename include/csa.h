@@ -1,0 +1,219 @@
+/*
+ * csa.h — C ABI of the Compressed Sparse Attention (CSA) forward pass on AMD Instinct MI355X
+ * (gfx950). Hand-written HIP kernels; no torch types cross this boundary.
+ *
+ * The layer (DeepSeek-V4's CSA, as described on the pages "Anatomy of a Frontier Model: Reading
+ * DeepSeek-V4 Through Part V", section "The attention: compress, then select", and "The Exchange
+ * Rates of a Million Tokens", section 3) runs four steps:
+ *   1. compress   every m tokens into one K=V entry by per-channel softmax pooling with learned
+ *                 position biases, each entry pooling its own block and the previous one;
+ *   2. index      score each query against every causally visible entry:
+ *                 s[t,i] = sum_h w_h * ReLU(q_I[t,h] . k_I[i]);
+ *   3. top-k      keep the k best entries per query;
+ *   4. attend     single-KV-head attention over the selected entries plus the last W raw tokens.
+ *
+ * Conventions (every entry point):
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major. Strides are in elements
+ *     of the tensor's dtype unless stated otherwise. The library never frees or keeps them.
+ *   - Scalars and the small structs below live in HOST memory and are read during the call only.
+ *   - Every call validates its arguments on the host before any HIP call. On failure nothing is
+ *     launched and an error code is returned; csa_last_error() then describes it (thread-local).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - No device memory is allocated by a compute call: scratch comes from the caller's workspace
+ *     `ws` of `ws_bytes` bytes (256-byte aligned), sized by csa_workspace_size().
+ *   - Results are deterministic: no floating-point atomics, fixed reduction orders, and top-k ties
+ *     broken toward the smaller entry index.
+ *   - Positions: a batch shares one absolute position for its first query (`q_pos0`); query row t
+ *     of every sequence sits at position q_pos0 + t.
+ *   - Visibility: entry i (tokens [i*m, (i+1)*m)) is visible to position p iff its block is
+ *     complete, (i+1)*m - 1 <= p; so n_vis(p) = min(floor((p+1)/m), n_cap).
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_OK 0
+#define CSA_ERR_ARG (-1)          /* invalid argument (shape, stride, pointer, value)          */
+#define CSA_ERR_UNSUPPORTED (-2)  /* valid but not implemented (dtype/shape combination)         */
+#define CSA_ERR_WORKSPACE (-3)    /* workspace missing, misaligned or too small                  */
+#define CSA_ERR_HIP (-4)          /* a HIP runtime call failed (launch error, no device)         */
+
+/* Storage types. */
+#define CSA_F32 0
+#define CSA_BF16 1
+#define CSA_MXFP4 2  /* indexer q/k only: e2m1 codes, 2 per byte (even element in the low nibble),
+                        plus one e8m0 scale byte per 32 elements (OCP Microscaling v1.0). */
+
+/* Operations, for csa_workspace_size. */
+#define CSA_OP_COMPRESS 0
+#define CSA_OP_INDEX_TOPK 1
+#define CSA_OP_TOPK_FROM_SCORES 2
+#define CSA_OP_SPARSE_ATTN 3
+#define CSA_OP_FORWARD 4
+
+/* Layer dimensions. */
+typedef struct csa_dims {
+  int32_t m;        /* tokens per compressed entry (4 in DeepSeek-V4's CSA layers)              */
+  int32_t D;        /* entry dim = query head dim; the entry is both key and value (512)         */
+  int32_t H;        /* query heads, all sharing the one KV head (64 / 128)                       */
+  int32_t H_I;      /* indexer heads (64)                                                        */
+  int32_t D_I;      /* indexer head dim (128)                                                    */
+  int32_t top_k;    /* entries kept per query (512 / 1024)                                       */
+  int32_t window;   /* raw tokens attended directly, including the query's own (128)             */
+  float sm_scale;   /* softmax scale; 0 selects 1/sqrt(D)                                       */
+} csa_dims;
+
+int csa_version(void);
+const char* csa_last_error(void);
+
+/*
+ * Bytes of workspace an operation needs (written to *bytes). `T` is query rows per sequence,
+ * `n_cap` the entry capacity per sequence, `d_model` the width of x (CSA_OP_FORWARD only),
+ * `idx_dtype` the indexer storage type (CSA_OP_INDEX_TOPK / CSA_OP_FORWARD).
+ * For CSA_OP_TOPK_FROM_SCORES pass R (rows) as B, T = 1 and the row length as n_cap.
+ * Errors: CSA_ERR_ARG for an unknown op or negative sizes.
+ */
+int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap, int d_model,
+                       int idx_dtype, int64_t* bytes);
+
+/*
+ * Step 1 — compressor ("The Exchange Rates of a Million Tokens", section 3; "Anatomy of a
+ * Frontier Model", bullet "Compressed Sparse Attention (CSA)").
+ * For each complete block of this call (entry i = pos0/m + e, e < floor(T/m)) and channel j:
+ *   logits = { za[i*m+r, j] + bias_a[r, j] }_{r<m}  U  { zb[(i-1)*m+r, j] + bias_b[r, j] }_{r<m}
+ *   entries[i, j] = softmax(logits) . [ca[i*m+r, j] ; cb[(i-1)*m+r, j]]
+ * Entry 0 pools its own block only. Tokens of an incomplete trailing block produce nothing.
+ *   ca, za, cb, zb  [B, T, c] views: token stride `ld`, sequence stride `seq_stride` (elements,
+ *                   shared by the four), channel stride 1; dtype `in_dtype` (F32 or BF16).
+ *   halo_cb/zb      the previous block's cb/zb rows [B, m, c] (stride halo_ld / halo_seq_stride),
+ *                   required iff pos0 > 0, ignored (may be NULL) when pos0 == 0.
+ *   bias_a/b        [m, c] float32.
+ *   entries         [B, n_cap, c] (row stride c, sequence stride entries_seq_stride), dtype
+ *                   out_dtype; rows pos0/m .. pos0/m + floor(T/m) - 1 are written.
+ * Requires pos0 % m == 0 and pos0/m + floor(T/m) <= n_cap. B == 0 or T < m is a no-op.
+ */
+int csa_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype,
+                 const void* ca, const void* za, const void* cb, const void* zb,
+                 int64_t ld, int64_t seq_stride,
+                 const void* halo_cb, const void* halo_zb, int64_t halo_ld, int64_t halo_seq_stride,
+                 const float* bias_a, const float* bias_b,
+                 void* entries, int64_t entries_seq_stride, int64_t n_cap, int out_dtype,
+                 void* stream);
+
+/*
+ * Steps 2+3 — lightning indexer fused with top-k ("Anatomy of a Frontier Model", bullet
+ * "Compressed Sparse Attention (CSA)": 64 heads x 128 dims, top 1,024 / 512; "The Exchange Rates
+ * of a Million Tokens", section 3: ReLU-gated dot products, top-k).
+ *   s[t, i] = sum_h w[h] * max(0, q_idx[t, h, :] . keys[i, :])   for i < n_vis(q_pos0 + t)
+ *   out_idx[t] = the top_k entries by (s descending, i ascending), stored ascending and padded
+ *   with -1 when fewer than top_k are visible.
+ *   q_idx    [B, T, H_I, D_I]: token stride q_ld, sequence stride q_seq_stride, heads D_I apart.
+ *            MXFP4: codes [B, T, H_I, D_I/2] bytes and q_scale [B, T, H_I, D_I/32], both
+ *            contiguous (q_ld / q_seq_stride must be 0).
+ *   w        float32 head weights: [H_I] shared when w_ld == 0, else row (b*T + t) at w + row*w_ld.
+ *   keys     [B, n_cap, D_I] (row stride D_I, sequence stride keys_seq_stride); MXFP4: codes
+ *            [B, n_cap, D_I/2] contiguous plus k_scale [B, n_cap, D_I/32].
+ *   out_idx  [B, T, top_k] int32.  out_score (nullable) [B, T, top_k] the scores of out_idx.
+ * The T x n_cap score matrix is not stored for large T (fused streaming selection); for few
+ * query rows the scores go through the workspace.
+ */
+int csa_index_topk(const csa_dims* dims, int B, int T, int64_t q_pos0, int idx_dtype,
+                   const void* q_idx, int64_t q_ld, int64_t q_seq_stride, const void* q_scale,
+                   const float* w, int64_t w_ld,
+                   const void* keys, int64_t keys_seq_stride, const void* k_scale, int64_t n_cap,
+                   int32_t* out_idx, float* out_score,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 3 on its own, on caller-provided float32 scores (the selection routine of
+ * csa_index_topk, exposed so that it can be checked bit for bit).
+ *   scores   [R, ld] float32; row r's candidates are columns 0 .. n_valid[r]-1 (clamped to ld).
+ *   n_valid  device int32 [R].
+ *   out_idx  [R, k] int32, ascending, -1 padded; out_score (nullable) [R, k].
+ * Order: score descending (-0 == +0), then column ascending. NaN scores are not supported.
+ */
+int csa_topk_from_scores(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
+                         int32_t* out_idx, float* out_score,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 4 — sparse single-KV-head attention ("Anatomy of a Frontier Model", sections "The
+ * skeleton, and what's kept" and "The attention: compress, then select", bullets "A sliding
+ * window in every layer" and "An attention sink").
+ * For query row t at p = q_pos0 + t and head h, over the key set
+ *   S_t = { entries[idx[t, j]] : idx[t, j] >= 0 }  ++  { raw row of position u : u in
+ *         [max(0, p - window + 1), p] }
+ *   o[t, h] = sum_{v in S_t} exp(l_v - mu) v / (sum_v exp(l_v - mu) [+ exp(sink[h] - mu)]),
+ *   l_v = sm_scale * q[t, h] . v,  mu = the largest logit (and sink[h] when given).
+ *   q        [B, T, H, D]: token stride q_ld, sequence stride q_seq_stride, heads D apart.
+ *   entries  [B, n_cap, D] (row stride D); idx [B, T, top_k] int32 (values outside [0, n_cap)
+ *            are skipped).
+ *   kv_raw   [B, raw_len, D]: row stride raw_ld, sequence stride raw_seq_stride; row r holds
+ *            position raw_pos0 + r and must cover every query's window.
+ *   sink     nullable float32 [H].
+ *   out      [B, T, H, D] contiguous, out_dtype F32 or BF16.
+ */
+int csa_sparse_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+                    const void* q, int64_t q_ld, int64_t q_seq_stride,
+                    const void* entries, int64_t entries_seq_stride, int64_t n_cap,
+                    const int32_t* idx,
+                    const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
+                    int64_t raw_len,
+                    const float* sink,
+                    void* out, int out_dtype,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Weights of one CSA layer (device pointers). */
+typedef struct csa_weights {
+  /* Fused projection, [n_tot, d_model] row-major (one output column per row), dtype of x, with
+     n_tot = 4D + 4D_I + H*D + H_I*D_I + D and rows in this order:
+     ca | za | cb | zb (D each) | ica | iza | icb | izb (D_I each) | q (H*D) | q_I (H_I*D_I) | kv (D). */
+  const void* w_proj;
+  const float* bias_a;   /* [m, D]   */
+  const float* bias_b;   /* [m, D]   */
+  const float* ibias_a;  /* [m, D_I] */
+  const float* ibias_b;  /* [m, D_I] */
+  const float* w_head;   /* [H_I]    */
+  const float* sink;     /* nullable [H] */
+} csa_weights;
+
+/* Caches the layer reads and extends (device pointers, all of the activation dtype). */
+typedef struct csa_cache {
+  void* entries;         /* [B, n_cap, D]: rows < pos0/m are the context; new rows appended     */
+  void* keys;            /* [B, n_cap, D_I] indexer keys, same row numbering                     */
+  int64_t n_cap;
+  void* win;             /* [B, win_cap, D] raw KV: row r = position pos0 - (window-1) + r. Rows
+                            [0, window-1) hold the context's last raw tokens (only those at
+                            positions >= 0 are read); rows [window-1, window-1+T) are written.  */
+  int64_t win_cap;
+  const void* halo;      /* [B, m, 2D + 2D_I] cb | zb | icb | izb of block pos0/m - 1; NULL iff
+                            pos0 == 0                                                            */
+  void* halo_out;        /* nullable [B, m, 2D + 2D_I]: receives this chunk's last block (needs
+                            T % m == 0), i.e. the next chunk's halo                               */
+} csa_cache;
+
+/*
+ * The whole layer for a chunk of T tokens per sequence at positions pos0 .. pos0+T-1:
+ * projection (x @ w_proj^T), both compressors, indexer + top-k, sparse attention.
+ *   x        [B, T, d_model] contiguous, dtype F32 or BF16 (also the cache/projection dtype).
+ *   out      [B, T, H, D] contiguous, out_dtype F32 or BF16.
+ *   out_idx  nullable [B, T, top_k]: receives the selected entries.
+ * Requires pos0 % m == 0 and (pos0 + T)/m <= n_cap, window - 1 + T <= win_cap.
+ */
+int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_t pos0,
+                int d_model, int dtype, const void* x, const csa_cache* cache,
+                void* out, int out_dtype, int32_t* out_idx,
+                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

@@ -24,3 +24,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    """Names the case before it touches the GPU, so a run that dies mid-test still says which."""
+    if "gpu" in request.node.keywords:
+        print(f"\n[case] {request.node.nodeid}", flush=True)
+    yield

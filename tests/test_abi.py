@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry point, sizes its
+workspaces and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_sparse_attention_05_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "csa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_steps_and_helpers():
+    names = _declared()
+    for n in ("csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn", "csa_forward",
+              "csa_workspace_size", "csa_last_error", "csa_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib.load()
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert set(lib.EXPORTS) == set(_declared())
+    assert lib.csa_version() == 1
+
+
+def _d(**kw):
+    base = dict(m=4, D=512, H=64, H_I=64, D_I=128, top_k=512, window=128)
+    base.update(kw)
+    return lib.make_dims(**base)
+
+
+def test_workspace_sizes():
+    d = _d()
+    assert lib.csa_workspace_size(lib.CSA_OP_COMPRESS, d, 1, 8192, 2048) == 0
+    assert lib.csa_workspace_size(lib.CSA_OP_SPARSE_ATTN, d, 1, 8192, 2048) == 0
+    # prefill (many rows per sequence): fused streaming selection, no score matrix
+    assert lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, d, 1, 8192, 2048) == 0
+    # decode: scores of every (row, entry) pass through the workspace
+    nb = lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, _d(top_k=1024), 64, 1, 32768)
+    assert nb >= 64 * 32768 * 4
+    fw = lib.csa_workspace_size(lib.CSA_OP_FORWARD, d, 1, 8192, 2048, 4096)
+    n_tot = 4 * 512 + 4 * 128 + 64 * 512 + 64 * 128 + 512
+    assert fw >= 8192 * n_tot * 2 + 8192 * 512 * 4
+
+
+def _err(rc):
+    return rc, lib.load().csa_last_error().decode()
+
+
+def test_compress_rejects_bad_arguments():
+    L = lib.load()
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    # pos0 not a multiple of m
+    rc, msg = _err(L.csa_compress(1, 8, 2, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p,
+                                  64, 8, lib.CSA_BF16, None))
+    assert rc == -1 and "multiple of m" in msg
+    # pos0 > 0 without the previous block
+    rc, msg = _err(L.csa_compress(1, 8, 4, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p,
+                                  64, 8, lib.CSA_BF16, None))
+    assert rc == -1 and "halo" in msg
+    # entries beyond capacity
+    rc, msg = _err(L.csa_compress(1, 64, 0, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 1024, None, None, 0, 0, p, p, p,
+                                  64, 8, lib.CSA_BF16, None))
+    assert rc == -1 and "n_cap" in msg
+    # bad dtype
+    rc, _ = _err(L.csa_compress(1, 8, 0, 4, 16, 7, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p, 64, 8,
+                                lib.CSA_BF16, None))
+    assert rc == -1
+    # nothing to do is fine
+    assert L.csa_compress(1, 3, 0, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p, 64, 8,
+                          lib.CSA_BF16, None) == 0
+
+
+def test_index_topk_rejects_bad_arguments():
+    L = lib.load()
+    p = ctypes.c_void_p(256)
+    d = _d()
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(_d(top_k=0)), 1, 8, 0, lib.CSA_BF16, p, 8192, 65536, None, p, 0,
+                                    p, 262144, None, 2048, p, None, None, 0, None))
+    assert rc == -1 and "top_k" in msg
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, 0, lib.CSA_MXFP4, p, 0, 0, None, p, 0, p, 0, None,
+                                    2048, p, None, None, 0, None))
+    assert rc == -1 and "scale" in msg
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, 0, lib.CSA_BF16, p, 100, 800, None, p, 0, p, 262144,
+                                    None, 2048, p, None, None, 0, None))
+    assert rc == -1 and "q_ld" in msg
+    # decode shape needs a workspace
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 64, 1, 131072, lib.CSA_BF16, ctypes.c_void_p(4096), 8192,
+                                    8192, None, p, 0, ctypes.c_void_p(4096), 32768 * 128, None, 32768, p, None,
+                                    None, 0, None))
+    assert rc == -3 and "workspace" in msg
+
+
+def test_sparse_attn_checks_window_coverage():
+    L = lib.load()
+    p = ctypes.c_void_p(4096)
+    d = _d()
+    # raw rows start after the first query's window start
+    rc, msg = _err(L.csa_sparse_attn(ctypes.byref(d), 1, 16, 1000, lib.CSA_BF16, p, 32768, 0, p, 0, 256, p, p, 512,
+                                     0, 900, 200, None, p, lib.CSA_F32, None, 0, None))
+    assert rc == -1 and "cover" in msg
+
+
+def test_topk_from_scores_rejects_bad_k():
+    L = lib.load()
+    p = ctypes.c_void_p(256)
+    rc, _ = _err(L.csa_topk_from_scores(p, 100, p, 4, 0, p, None, None, 0, None))
+    assert rc == -1
+    rc, _ = _err(L.csa_topk_from_scores(p, 100, p, 4, 5000, p, None, None, 0, None))
+    assert rc == -1
+    assert L.csa_topk_from_scores(p, 100, p, 0, 4, p, None, None, 0, None) == 0
+
+
+def test_forward_rejects_capacity_overflow():
+    L = lib.load()
+    p = ctypes.c_void_p(4096)
+    d = _d()
+    w = lib.Weights(4096, 4096, 4096, 4096, 4096, 4096, None)
+    c = lib.Cache(4096, 4096, 100, 4096, 1000, None, None)
+    rc, msg = _err(L.csa_forward(ctypes.byref(d), ctypes.byref(w), 1, 8192, 0, 4096, lib.CSA_BF16, p, ctypes.byref(c),
+                                 p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "n_cap" in msg

@@ -1,0 +1,292 @@
+"""GPU parity: every step of the HIP path against the CPU oracle on the same seeded inputs.
+
+Small cases are compared element by element; the named full-size workloads are run in the launch
+configuration the benchmark times and compared on sampled rows / sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_05_amd import lib
+from synth.torch_io import act, to_device
+from synth.workloads import get
+from tests.csa_testlib import (O, G, TOL, check_idx_rows, decode_tensors, dims_of, max_err, run_decode, run_prefill,
+                               tensor_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------------------------ selection
+
+
+def _oracle_topk_rows(s32, nv, k):
+    return np.stack([O.topk_select(s32[r].astype(np.float64), nv[r], k) for r in range(s32.shape[0])])
+
+
+@pytest.mark.parametrize("R,n,k,tie", [(7, 100, 16, False), (5, 3000, 512, True), (3, 5000, 1024, False),
+                                       (2, 40000, 1024, True), (4, 70000, 100, False), (6, 64, 64, True)])
+def test_topk_from_scores_bit_exact(R, n, k, tie):
+    rng = np.random.default_rng(R * 1000 + n)
+    s = rng.standard_normal((R, n)).astype(np.float32)
+    if tie:
+        s = (np.round(s * 4) / 4).astype(np.float32)
+        s[:, ::3] = 0.0
+        s[:, 1::7] = -0.0
+    nv = np.array([n, n // 2, 0, 1, min(n, k - 1), n - 1, 5][:R], dtype=np.int32)
+    idx = torch.empty(R, k, dtype=torch.int32, device="cuda")
+    sc = torch.empty(R, k, dtype=torch.float32, device="cuda")
+    lib.csa_topk_from_scores(to_device(s, "f32"), to_device(nv, "i32"), k, idx, out_score=sc)
+    got = idx.cpu().numpy()
+    want = _oracle_topk_rows(s, nv, k)
+    np.testing.assert_array_equal(got, want)
+    gs = sc.cpu().numpy()
+    for r in range(R):
+        v = want[r] >= 0
+        np.testing.assert_array_equal(gs[r][v], s[r][want[r][v]])
+
+
+# ------------------------------------------------------------------------------------ tiny fp32
+
+
+def test_tiny_forward_fp32_end_to_end():
+    wl = get("tiny")
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    st = run_prefill(wl, inp)
+    np.testing.assert_allclose(tensor_f64(st.entries[0]), r["entries"], atol=TOL["f32"], rtol=0)
+    np.testing.assert_allclose(tensor_f64(st.keys[0]), r["keys"], atol=TOL["f32"], rtol=0)
+    gidx = st.idx[0].cpu().numpy()
+    differ = check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
+    ref = r["out"].copy()
+    for t in differ:
+        ref[t] = O.sparse_attention(r["q"][t:t + 1], r["entries"], gidx[t:t + 1], r["raw"], r["raw_pos0"],
+                                    r["q_pos"][t:t + 1], wl.W)[0]
+    assert max_err(tensor_f64(st.out[0]), ref) <= TOL["f32"]
+
+
+def test_tiny_steps_fp32_on_oracle_inputs():
+    wl = get("tiny")
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    d = dims_of(wl)
+    p = r["parts"]
+    f = lambda a: to_device(a.astype(np.float32), "f32")
+    # step 1
+    ent = torch.zeros(1, wl.n_cap, wl.D, device="cuda")
+    lib.csa_compress(f(p["ca"])[None], f(p["za"])[None], f(p["cb"])[None], f(p["zb"])[None],
+                     f(inp["bias_a"]), f(inp["bias_b"]), ent, pos0=0, m=wl.m)
+    assert max_err(tensor_f64(ent[0]), r["entries"]) <= TOL["f32"]
+    # steps 2+3
+    idx = torch.empty(1, wl.T, wl.k, dtype=torch.int32, device="cuda")
+    lib.csa_index_topk(d, f(r["q_idx"])[None], f(inp["w_head"]), f(r["keys"])[None], idx, q_pos0=0)
+    check_idx_rows(idx[0].cpu().numpy(), r["idx"], r["scores"], r["n_vis"])
+    # step 4 with the oracle's selection
+    out = torch.empty(1, wl.T, wl.H, wl.D, device="cuda")
+    lib.csa_sparse_attn(d, f(r["q"])[None], f(r["entries"])[None], to_device(r["idx"], "i32")[None],
+                        f(r["raw"])[None], out, q_pos0=0, raw_pos0=0)
+    assert max_err(tensor_f64(out[0]), r["out"]) <= TOL["f32"]
+
+
+def test_attention_sink_fp32():
+    wl = get("tiny")
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    sink = np.linspace(-1.0, 2.0, wl.H)
+    want = O.sparse_attention(r["q"], r["entries"], r["idx"], r["raw"], 0, r["q_pos"], wl.W, sink=sink)
+    f = lambda a: to_device(np.asarray(a, dtype=np.float32), "f32")
+    out = torch.empty(1, wl.T, wl.H, wl.D, device="cuda")
+    lib.csa_sparse_attn(dims_of(wl), f(r["q"])[None], f(r["entries"])[None], to_device(r["idx"], "i32")[None],
+                        f(r["raw"])[None], out, q_pos0=0, raw_pos0=0, sink=f(sink))
+    assert max_err(tensor_f64(out[0]), want) <= TOL["f32"]
+
+
+# ------------------------------------------------------------------------------------ bf16 prefill
+
+
+def _bf16_small(**kw):
+    base = dict(T=1000, d=1024)   # ragged T: not a multiple of 8 (rows per workgroup) or 64 (key tile)
+    base.update(kw)
+    return get("prefill8k").with_(**base)
+
+
+def _assert_bf16_close(got, want, frac_exact=0.99):
+    assert max_err(got, want) <= TOL["bf16"]
+    assert np.mean(got == want) >= frac_exact
+
+
+def test_bf16_prefill_end_to_end_small():
+    wl = _bf16_small()
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    st = run_prefill(wl, inp)
+    _assert_bf16_close(tensor_f64(st.entries[0]), r["entries"])
+    _assert_bf16_close(tensor_f64(st.keys[0]), r["keys"])
+    gidx = st.idx[0].cpu().numpy()
+    differ = check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
+    assert len(differ) <= wl.T // 20
+    ref = r["out"].copy()
+    for t in differ:
+        ref[t] = O.sparse_attention(r["q"][t:t + 1], r["entries"], gidx[t:t + 1], r["raw"], 0, r["q_pos"][t:t + 1],
+                                    wl.W)[0]
+    assert max_err(tensor_f64(st.out[0]), ref) <= TOL["bf16"]
+
+
+def test_bf16_steps_on_oracle_inputs():
+    wl = _bf16_small(T=520)
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    d = dims_of(wl)
+    bits = lambda a: to_device(G.f32_to_bf16_bits(np.asarray(a, dtype=np.float32)), "bf16")  # exact: on bf16 grid
+    p = r["parts"]
+    ent = torch.zeros(1, wl.n_cap, wl.D, dtype=torch.bfloat16, device="cuda")
+    lib.csa_compress(bits(p["ca"])[None], bits(p["za"])[None], bits(p["cb"])[None], bits(p["zb"])[None],
+                     to_device(inp["bias_a"], "f32"), to_device(inp["bias_b"], "f32"), ent, pos0=0, m=wl.m)
+    _assert_bf16_close(tensor_f64(ent[0]), r["entries"])
+    idx = torch.empty(1, wl.T, wl.k, dtype=torch.int32, device="cuda")
+    lib.csa_index_topk(d, bits(r["q_idx"])[None], to_device(inp["w_head"], "f32"), bits(r["keys"])[None], idx,
+                       q_pos0=0)
+    check_idx_rows(idx[0].cpu().numpy(), r["idx"], r["scores"], r["n_vis"])
+    out = torch.empty(1, wl.T, wl.H, wl.D, device="cuda")
+    lib.csa_sparse_attn(d, bits(r["q"])[None], bits(r["entries"])[None], to_device(r["idx"], "i32")[None],
+                        bits(r["raw"])[None], out, q_pos0=0, raw_pos0=0)
+    assert max_err(tensor_f64(out[0]), r["out"]) <= TOL["bf16"]
+
+
+def test_bf16_selection_bit_exact_on_oracle_scores():
+    wl = _bf16_small(T=300, d=512)
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    s32 = np.where(np.isfinite(r["scores"]), r["scores"], 0).astype(np.float32)
+    nv = r["n_vis"].astype(np.int32)
+    idx = torch.empty(wl.T, wl.k, dtype=torch.int32, device="cuda")
+    lib.csa_topk_from_scores(to_device(s32, "f32"), to_device(nv, "i32"), wl.k, idx)
+    np.testing.assert_array_equal(idx.cpu().numpy(), _oracle_topk_rows(s32, nv, wl.k))
+
+
+def test_bf16_chunked_prefill_with_context():
+    # a chunk after L tokens of context: prefix entries/keys, window rows and halo come from the cache
+    wl = get("chunk1m").with_(L=2048, T=264, d=512)
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    st = run_prefill(wl, inp)
+    _assert_bf16_close(tensor_f64(st.entries[0]), r["entries"])
+    gidx = st.idx[0].cpu().numpy()
+    differ = check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
+    ref = r["out"].copy()
+    for t in differ:
+        ref[t] = O.sparse_attention(r["q"][t:t + 1], r["entries"], gidx[t:t + 1], r["raw"], r["raw_pos0"],
+                                    r["q_pos"][t:t + 1], wl.W)[0]
+    assert max_err(tensor_f64(st.out[0]), ref) <= TOL["bf16"]
+
+
+def test_bf16_short_sequence_window_only():
+    # T < k and the first m-1 rows see no entry at all: padding and the window-only path
+    wl = _bf16_small(T=40, d=512)
+    inp = G.make_inputs(wl)
+    r = O.prefill(inp, wl)
+    st = run_prefill(wl, inp)
+    gidx = st.idx[0].cpu().numpy()
+    assert np.all(gidx[:3] == -1)
+    check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
+    assert max_err(tensor_f64(st.out[0]), r["out"]) <= TOL["bf16"]
+
+
+def test_bf16_forward_is_deterministic():
+    wl = _bf16_small(T=256, d=512)
+    inp = G.make_inputs(wl)
+    a = run_prefill(wl, inp)
+    o1, i1 = a.out.clone(), a.idx.clone()
+    b = run_prefill(wl, inp)
+    assert torch.equal(o1, b.out) and torch.equal(i1, b.idx)
+
+
+# ------------------------------------------------------------------------------------ decode
+
+
+def _decode_check(wl, inp, st, seqs):
+    gidx = st.idx.cpu().numpy()
+    gout = st.out.float().cpu().numpy()
+    for b in seqs:
+        r = O.decode(inp, wl, b)
+        differ = check_idx_rows(gidx[b], r["idx"], r["scores"], r["n_vis"])
+        ref = r["out"]
+        if differ:
+            ref = O.sparse_attention(r["q"], r["entries"], gidx[b], r["raw"], wl.L - wl.W + 1, [wl.L], wl.W)
+        assert max_err(gout[b], ref) <= TOL["bf16"], f"sequence {b}"
+
+
+def test_decode_bf16_small():
+    wl = get("decode128k").with_(B=3, L=4096 + 2048)
+    inp = G.make_inputs(wl)
+    st = run_decode(wl, decode_tensors(wl, inp))
+    _decode_check(wl, inp, st, range(wl.B))
+
+
+def test_decode_fewer_entries_than_k():
+    wl = get("decode128k").with_(B=2, L=1000)        # 250 entries < k = 1024: all kept, padded
+    inp = G.make_inputs(wl)
+    st = run_decode(wl, decode_tensors(wl, inp))
+    assert np.all(st.idx.cpu().numpy()[:, 0, 250:] == -1)
+    _decode_check(wl, inp, st, range(wl.B))
+
+
+def test_decode_mxfp4_small():
+    wl = get("decode1m_fp4").with_(B=2, L=4 * 20000)
+    inp = G.make_inputs(wl)
+    st = run_decode(wl, decode_tensors(wl, inp))
+    _decode_check(wl, inp, st, range(wl.B))
+
+
+def test_decode_batch_invariance():
+    wl = get("decode128k").with_(B=8, L=4 * 9000)
+    inp = G.make_inputs(wl)
+    t = decode_tensors(wl, inp)
+    full = run_decode(wl, t)
+    o_full, i_full = full.out.clone(), full.idx.clone()
+    b = 5
+    one = {k: (v[b:b + 1] if (v is not None and k != "w_head") else v) for k, v in t.items()}
+    solo = run_decode(wl.with_(B=1), one)
+    assert torch.equal(solo.out[0], o_full[b]) and torch.equal(solo.idx[0], i_full[b])
+
+
+# ------------------------------------------------------------------------------------ full-size workloads
+
+
+def _sampled_prefill(name, rows):
+    wl = get(name)
+    inp = G.make_inputs(wl)
+    st = run_prefill(wl, inp)
+    r = O.prefill(inp, wl, query_rows=rows)
+    n_new = wl.T // wl.m
+    first = wl.L // wl.m
+    _assert_bf16_close(tensor_f64(st.entries[0, first:first + n_new]), r["entries_new"])
+    _assert_bf16_close(tensor_f64(st.keys[0, first:first + n_new]), r["keys_new"])
+    gidx = st.idx[0].cpu().numpy()[rows]
+    differ = check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
+    ref = r["out"].copy()
+    for j in differ:
+        ref[j] = O.sparse_attention(r["q"][j:j + 1], r["entries"], gidx[j:j + 1], r["raw"], r["raw_pos0"],
+                                    r["q_pos"][j:j + 1], wl.W)[0]
+    assert max_err(tensor_f64(st.out[0, rows]), ref) <= TOL["bf16"]
+
+
+def test_full_prefill8k_sampled():
+    _sampled_prefill("prefill8k", np.array([0, 3, 4, 127, 128, 1000, 4095, 4096, 6001, 8190, 8191]))
+
+
+def test_full_chunk1m_sampled():
+    _sampled_prefill("chunk1m", np.array([0, 1, 2, 3, 777, 2048, 4094, 4095]))
+
+
+def test_full_decode128k_sampled():
+    wl = get("decode128k")
+    inp = G.make_inputs(wl)
+    st = run_decode(wl, decode_tensors(wl, inp))
+    _decode_check(wl, inp, st, [0, 17, 63])
+
+
+def test_full_decode1m_fp4():
+    wl = get("decode1m_fp4")
+    inp = G.make_inputs(wl)
+    st = run_decode(wl, decode_tensors(wl, inp))
+    _decode_check(wl, inp, st, [0, 3])
