@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA forward on one MI355X.
+
+Headline: prefill tokens/s of a 4096-token chunk at the end of a 1,048,576-token context (all
+steps of the layer: projection, both compressors, indexer + top-k, sparse attention), plus decode
+step latency at 128K context (64 sequences) and at 1M context with the MXFP4 indexer (4 sequences).
+Inputs are seeded synthetic tensors with the workloads' shapes; they are resident in HBM before the
+timed region starts. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload chunk1m] [--no-decode] [--no-cpu-baseline]
+    python bench.py --copy-probe      # a plain 1 GiB device copy, for counter calibration
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA prefill tok/s & decode step µs at 128K/1M ctx; % of HBM/MFMA roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+MALL_FLUSH_BYTES = 512 << 20  # larger than the 256 MB Infinity Cache
+KERNEL_SOURCES = ("csrc/index.hip", "csrc/topk_wave.h", "csrc/common.h")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "compressed_sparse_attention_05_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def index_pairs(wl) -> int:
+    """Sum over the chunk's queries of the entries each can see: (q, entry) pairs the indexer scores."""
+    p = wl.L + np.arange(wl.T, dtype=np.int64)
+    nv = np.minimum((p + 1) // wl.m, wl.n_cap)
+    return int(nv.sum()) * wl.B
+
+
+def attn_pairs(wl) -> int:
+    p = wl.L + np.arange(wl.T, dtype=np.int64)
+    nv = np.minimum((p + 1) // wl.m, wl.n_cap)
+    return int((np.minimum(nv, wl.k) + np.minimum(p + 1, wl.W)).sum()) * wl.B
+
+
+def timed_events(fn, n, stream_sync):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    for i in range(n):
+        evs[2 * i].record()
+        fn()
+        evs[2 * i + 1].record()
+    stream_sync()
+    return [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n)]
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+
+
+def load_traffic(name: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except Exception:
+        return None
+    if d.get("kernel_sources_sha256_16") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp):
+    """The oracle, as it stands, on a bounded sample of the workload: the per-chunk work (projection
+    of the compressor and window columns, both compressors) plus 4 and then 12 query rows; per-row
+    and per-chunk times are separated from the two runs and scaled to the whole chunk."""
+    from oracle import csa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    rows_a = np.linspace(0, wl.T - 1, 4).astype(int)
+    rows_b = np.linspace(0, wl.T - 1, 12).astype(int)
+    t0 = time.perf_counter()
+    O.prefill(inp, wl, query_rows=rows_a)
+    t1 = time.perf_counter()
+    O.prefill(inp, wl, query_rows=rows_b)
+    t2 = time.perf_counter()
+    per_row = max((t2 - t1) - (t1 - t0), 1e-9) / (len(rows_b) - len(rows_a))
+    fixed = max((t1 - t0) - len(rows_a) * per_row, 0.0)
+    est = fixed + wl.T * per_row
+    return {"value": wl.B * wl.T / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{wl.name}: oracle prefill with 4 and with 12 of the {wl.T} query rows "
+                      f"({t1 - t0:.1f} s + {t2 - t1:.1f} s); per-row {per_row * 1e3:.1f} ms and per-chunk "
+                      f"{fixed:.1f} s scaled to all {wl.T} rows = {est:.0f} s per chunk"}
+
+
+def bench_prefill(wl, steps, warmup):
+    import torch
+    from compressed_sparse_attention_05_amd import layer, lib
+    from synth import gen as G
+    from synth.torch_io import act, to_device
+
+    log(f"generating {wl.name} inputs")
+    inp = G.make_inputs(wl)
+    d = layer.dims(wl.m, wl.D, wl.H, wl.H_I, wl.D_I, wl.k, wl.W)
+    weights = {"w_proj": act(inp["W"], wl), "bias_a": to_device(inp["bias_a"], "f32"),
+               "bias_b": to_device(inp["bias_b"], "f32"), "ibias_a": to_device(inp["ibias_a"], "f32"),
+               "ibias_b": to_device(inp["ibias_b"], "f32"), "w_head": to_device(inp["w_head"], "f32")}
+    st = layer.CSAPrefill(d, wl.B, wl.T, wl.d, wl.n_cap, dtype=torch.bfloat16, out_dtype=torch.float32)
+    if wl.L > 0:
+        n0 = wl.L // wl.m
+        st.entries[:, :n0] = act(inp["entries_prefix"], wl)
+        st.keys[:, :n0] = act(inp["keys_prefix"], wl)
+        st.win[:, : wl.W - 1] = act(inp["win_prefix"], wl)
+        st.halo.copy_(act(inp["halo"], wl))
+    x = act(inp["x"], wl)
+    torch.cuda.synchronize()
+    log(f"warmup {warmup}")
+    for _ in range(warmup):
+        st(weights, x, wl.L)
+    torch.cuda.synchronize()
+    log(f"timing {steps} steps")
+    t0 = time.perf_counter()
+    step_ms = timed_events(lambda: st(weights, x, wl.L), steps, torch.cuda.synchronize)
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+
+    # the dominant kernel alone, same arguments and launch configuration as inside the step
+    P = st.fwd.projection()
+    c_qi = 4 * wl.D + 4 * wl.D_I + wl.H * wl.D
+    q_idx = P[:, c_qi:c_qi + wl.H_I * wl.D_I].view(wl.B, wl.T, wl.H_I, wl.D_I)
+    idx = torch.empty_like(st.idx)
+    w_head = weights["w_head"]
+    run_idx = lambda: lib.csa_index_topk(d, q_idx, w_head, st.keys, idx, q_pos0=wl.L)
+    run_idx()
+    torch.cuda.synchronize()
+    idx_ms = timed_events(run_idx, steps, torch.cuda.synchronize)
+    assert torch.equal(idx, st.idx), "index kernel alone disagrees with the step"
+    c_q = 4 * wl.D + 4 * wl.D_I
+    q = P[:, c_q:c_q + wl.H * wl.D].view(wl.B, wl.T, wl.H, wl.D)
+    out = torch.empty_like(st.out)
+    run_attn = lambda: lib.csa_sparse_attn(d, q, st.entries, st.idx, st.win, out, q_pos0=wl.L,
+                                           raw_pos0=wl.L - (wl.W - 1))
+    run_attn()
+    torch.cuda.synchronize()
+    attn_ms = timed_events(run_attn, steps, torch.cuda.synchronize)
+    return dict(inp=inp, ms_per_step=ms_per_step, step_ms=step_ms, idx_ms=idx_ms, attn_ms=attn_ms)
+
+
+def bench_decode(name, steps, warmup):
+    import torch
+    from compressed_sparse_attention_05_amd import layer, lib
+    from synth import gen as G
+    from synth.torch_io import act, to_device
+    from synth.workloads import get
+
+    wl = get(name)
+    log(f"generating {name} inputs")
+    inp = G.make_inputs(wl)
+    t = {"entries": act(inp["entries"], wl), "kv_raw": act(inp["kv_raw"], wl), "q": act(inp["q"], wl),
+         "w_head": to_device(inp["w_head"], "f32")}
+    fp4 = wl.idx_dtype == "mxfp4"
+    if fp4:
+        t["keys"], t["k_scale"] = to_device(inp["keys_codes"], "u8"), to_device(inp["keys_scales"], "u8")
+        t["q_idx"], t["q_scale"] = to_device(inp["q_idx_codes"], "u8"), to_device(inp["q_idx_scales"], "u8")
+    else:
+        t["keys"], t["q_idx"] = act(inp["keys"], wl), act(inp["q_idx"], wl)
+        t["k_scale"] = t["q_scale"] = None
+    del inp
+    d = layer.dims(wl.m, wl.D, wl.H, wl.H_I, wl.D_I, wl.k, wl.W)
+    N = wl.L // wl.m
+    st = layer.CSADecode(d, wl.B, N, idx_dtype=lib.CSA_MXFP4 if fp4 else lib.CSA_BF16)
+    flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    step = lambda: st(wl.L, t["q_idx"], t["w_head"], t["keys"], t["q"], t["entries"], t["kv_raw"],
+                      q_scale=t["q_scale"], k_scale=t["k_scale"])
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        flush.fill_(1)  # evict the caches from the Infinity Cache (outside the timed events)
+        ms += timed_events(step, 1, torch.cuda.synchronize)
+    key_bytes = wl.B * N * (wl.D_I // 2 + wl.D_I // 32 if fp4 else wl.D_I * 2)
+    gather = wl.B * (min(N, wl.k) + wl.W) * wl.D * 2
+    qb = wl.B * wl.H * wl.D * 2 + wl.B * wl.H_I * (wl.D_I // 2 + wl.D_I // 32 if fp4 else wl.D_I * 2)
+    outb = wl.B * wl.H * wl.D * 4 + wl.B * wl.k * 4
+    nbytes = key_bytes + gather + qb + outb
+    us = float(np.median(ms)) * 1e3
+    return {"us_per_step": round(us, 2), "us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+            "us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2), "algorithmic_bytes": int(nbytes),
+            "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "B": wl.B, "context_tokens": wl.L, "top_k": wl.k, "indexer": "mxfp4" if fp4 else "bf16",
+            "mall": "512 MiB written between steps, outside the timed events"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="chunk1m")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py runs on one GPU only: the CSA layer here is a single-GPU build (asked for "
+              f"--gpus {args.gpus}, WORLD_SIZE={world}); multi-GPU sharding is a design, not code.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
+    from synth.workloads import get
+    wl = get(args.workload)
+    if wl.kind != "prefill":
+        raise SystemExit("--workload must be a prefill workload (tiny, prefill8k, chunk1m)")
+    r = bench_prefill(wl, args.steps, args.warmup)
+    ms = r["ms_per_step"]
+    flops_idx = index_pairs(wl) * wl.H_I * wl.D_I * 2
+    flops_attn = attn_pairs(wl) * wl.H * wl.D * 4
+    flops_proj = 2 * wl.B * wl.T * wl.d * wl.n_tot
+    idx_ms = float(np.mean(r["idx_ms"]))
+    attn_ms = float(np.mean(r["attn_ms"]))
+    ach = flops_idx / (idx_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(wl.B * wl.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.T}-token chunk after {wl.L} context tokens",
+                   "B": wl.B, "context_tokens": wl.L, "chunk_tokens": wl.T, "d_model": wl.d, "heads": wl.H,
+                   "head_dim": wl.D, "indexer": f"{wl.H_I}x{wl.D_I}", "top_k": wl.k, "window": wl.W,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "index_prefill_mfma (fused indexer scores + top-k)", "bound": "mfma",
+                     "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(f"index_prefill_mfma_{wl.name}_pmc.json"),
+                     "avg_launch_ms": round(idx_ms, 3), "algorithmic_flops": flops_idx},
+        "kernels": {
+            "sparse_attn_mfma": {"avg_launch_ms": round(attn_ms, 3), "algorithmic_flops": flops_attn,
+                                 "tflops": round(flops_attn / (attn_ms * 1e-3) / 1e12, 1),
+                                 "frac_bf16_peak": round(flops_attn / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "step": {"ms_events_median": round(float(np.median(r["step_ms"])), 3),
+                     "layer_flops": flops_idx + flops_attn + flops_proj,
+                     "layer_tflops": round((flops_idx + flops_attn + flops_proj) / (ms * 1e-3) / 1e12, 1)},
+        },
+    }
+    if not args.no_decode:
+        res["decode"] = {n: bench_decode(n, max(args.steps, 10), 3) for n in ("decode128k", "decode1m_fp4")}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(wl, r["inp"])
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

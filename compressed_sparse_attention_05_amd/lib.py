@@ -227,6 +227,15 @@ class Forward:
         self._ws = _workspace(need, device)
         self._wp, self._wn = _aligned_ptr(self._ws)
 
+    def projection(self) -> torch.Tensor:
+        """The projection x @ w_proj^T of the last call, [B*T, n_tot], as a view of the workspace."""
+        d = self.dims
+        n_tot = 4 * d.D + 4 * d.D_I + d.H * d.D + d.H_I * d.D_I + d.D
+        es = 4 if self.dtype == CSA_F32 else 2
+        off = self._wp - self._ws.data_ptr()
+        raw = self._ws[off:off + self.B * self.T * n_tot * es]
+        return raw.view(torch.float32 if es == 4 else torch.bfloat16).view(self.B * self.T, n_tot)
+
     def __call__(self, weights: dict, x, cache: dict, out, *, pos0: int, out_idx=None):
         w = Weights(_p(weights["w_proj"]), _p(weights["bias_a"]), _p(weights["bias_b"]), _p(weights["ibias_a"]),
                     _p(weights["ibias_b"]), _p(weights["w_head"]), _p(weights.get("sink")))
