@@ -134,6 +134,25 @@ IndexArgs make_index_args(const csa_dims* d, int B, int T, int64_t q_pos0, int i
   return a;
 }
 
+// AttnArgs with contiguous strides, for workspace sizing (the real call may need less).
+AttnArgs sizing_attn(const csa_dims* d, int B, int T, int dtype) {
+  AttnArgs a{};
+  a.B = B;
+  a.T = T;
+  a.H = d->H;
+  a.D = d->D;
+  a.k = d->top_k;
+  a.W = d->window;
+  a.in_dtype = dtype;
+  a.out_dtype = CSA_F32;
+  a.q_ld = (int64_t)d->H * d->D;
+  a.q_seq_stride = (int64_t)T * a.q_ld;
+  a.entries_seq_stride = 0;
+  a.raw_ld = d->D;
+  a.raw_seq_stride = 0;
+  return a;
+}
+
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return CSA_OK;
   if (!ws) return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
@@ -195,8 +214,13 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
   if (B < 0 || T < 0 || n_cap < 0 || d_model < 0) return fail(CSA_ERR_ARG, "negative size");
   switch (op) {
     case CSA_OP_COMPRESS:
-    case CSA_OP_SPARSE_ATTN:
       return CSA_OK;
+    case CSA_OP_SPARSE_ATTN: {
+      int rc = check_dims(dims);
+      if (rc) return rc;
+      *bytes = (int64_t)attn_workspace(sizing_attn(dims, B, T, idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16));
+      return CSA_OK;
+    }
     case CSA_OP_TOPK_FROM_SCORES: {
       if (!dims) return fail(CSA_ERR_ARG, "dims is NULL");
       *bytes = (int64_t)topk_workspace(B, n_cap, dims->top_k);
@@ -211,7 +235,9 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
       size_t need = index_topk_workspace(a);
       if (op == CSA_OP_FORWARD) {
         const int es = idx_dtype == CSA_F32 ? 4 : 2;
-        need = align256((size_t)B * T * n_tot_of(dims) * es) + align256((size_t)B * T * dims->top_k * 4) + align256(need);
+        const size_t at = attn_workspace(sizing_attn(dims, B, T, idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16));
+        need = align256((size_t)B * T * n_tot_of(dims) * es) + align256((size_t)B * T * dims->top_k * 4) +
+               align256(need > at ? need : at);
       }
       *bytes = (int64_t)need;
       return CSA_OK;
@@ -382,7 +408,9 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
                                     cache->n_cap, nullptr, nullptr);
   const size_t p_bytes = align256((size_t)B * T * ntot * es);
   const size_t i_bytes = align256((size_t)B * T * k * 4);
-  const size_t x_bytes = align256(index_topk_workspace(probe));
+  const size_t i_ws = index_topk_workspace(probe);
+  const size_t a_ws = attn_workspace(sizing_attn(dims, B, T, dtype));
+  const size_t x_bytes = align256(i_ws > a_ws ? i_ws : a_ws);
   rc = check_ws(ws, ws_bytes, p_bytes + i_bytes + x_bytes);
   if (rc) return rc;
   if (!aligned(x, 16) || !aligned(w->w_proj, 16)) return fail(CSA_ERR_ARG, "x and w_proj must be 16-byte aligned");
@@ -430,7 +458,7 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
   if (rc) return rc;
   rc = csa_sparse_attn(dims, B, T, pos0, dtype, col(c_q), ntot, (int64_t)T * ntot, cache->entries, cache->n_cap * D,
                        cache->n_cap, idx, cache->win, D, cache->win_cap * D, pos0 - (W - 1), (int64_t)W - 1 + T,
-                       w->sink, out, out_dtype, nullptr, 0, stream);
+                       w->sink, out, out_dtype, xws, x_bytes, stream);
   if (rc) return rc;
   if (cache->halo_out) {
     uint8_t* ho = static_cast<uint8_t*>(cache->halo_out);

@@ -103,6 +103,7 @@ constexpr int kHG = 64;        // heads per workgroup
 constexpr int kNK = 32;        // keys per tile
 constexpr int kVT = 40;        // LDS row stride (bf16) of the transposed key quarter and of P
 constexpr int kDQ = 128;       // dims per wave
+constexpr float kRescaleLog2 = 8.f;  // reference-max slack before O is rescaled
 
 struct AttnSmem {
   float sred[4][kHG][kNK];         // partial logits per wave          32 KiB
@@ -110,16 +111,45 @@ struct AttnSmem {
   uint16_t pl[kHG][kVT];           // probabilities, bf16              5 KiB
   float alpha[kHG];                // per-head rescale of O this tile
   float lsum[kHG];                 // per-head running denominators
+  float mrun[kHG];                 // per-head running maxima (log2 units)
+  int32_t rescale[2];              // some head rescaled O in this tile (by tile parity)
   int32_t keys[1];                 // gathered key list (entry ids >= 0, window rows as -(r+1))
 };
 
+// Split-KV bookkeeping: in the decode regime (fewer than 8 query rows per sequence) the key list
+// of a row is cut into fixed ranges of split_keys keys, one workgroup each; every workgroup leaves
+// (running max in log2 units, running sum, O / sum in bf16) and attn_combine merges the splits in a
+// fixed order. The plan depends only on T, k and the window, never on the batch size, so a row's
+// result is the same alone or inside any batch.
+struct AttnSplit {
+  int n_splits, split_keys;
+  uint16_t* part_o;  // [R*G*S, 64, 512] bf16, each split's output normalised by its own sum
+  float* part_ml;    // [R*G*S, 64, 2]: running max (log2 units), running sum
+};
+
+__device__ __forceinline__ void load_quarter(uint4 (&ku)[8], const int32_t* keys, int kj, int kend,
+                                             const uint16_t* ent, const uint16_t* raw, int64_t raw_ld, int wave,
+                                             int lane) {
+  const bool kok = kj < kend;
+  const uint16_t* krow = nullptr;
+  if (kok) {
+    const int32_t id = keys[kj];
+    krow = id >= 0 ? ent + (int64_t)id * 512 : raw + (int64_t)(-id - 1) * raw_ld;
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    ku[s] = kok ? *reinterpret_cast<const uint4*>(krow + wave * kDQ + s * 16 + (lane >> 5) * 8) : make_uint4(0, 0, 0, 0);
+}
+
 template <int OT>
-__global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups) {
+__global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnSplit sp) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int64_t row = blockIdx.x / n_groups;
-  const int hg = (int)(blockIdx.x % n_groups);
+  const int split = (int)(blockIdx.x % sp.n_splits);
+  const int64_t rg = blockIdx.x / sp.n_splits;
+  const int64_t row = rg / n_groups;
+  const int hg = (int)(rg % n_groups);
   const int b = (int)(row / a.T), t = (int)(row % a.T);
   const int64_t p = a.q_pos0 + t;
   const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
@@ -139,9 +169,12 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups) {
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
     for (int j = lane; j < nwin; j += 64) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
     if (lane == 0) sm.keys[a.k + a.W] = nsel + nwin;
+    if (lane == 0) sm.rescale[0] = 0;
   }
   __syncthreads();
   const int nkeys = sm.keys[a.k + a.W];
+  const int kbeg = split * sp.split_keys;
+  const int kend = kbeg + sp.split_keys < nkeys ? kbeg + sp.split_keys : nkeys;
 
   // ---- q quarter as A-fragments: head hg*64 + mt*32 + lane%32, dims wave*128 + s*16 + (lane/32)*8
   const float scale = a.scale * 1.4426950408889634f;  // logits in log2 units
@@ -164,27 +197,18 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups) {
   const int sh = wave * 16 + (lane >> 2);
   const int sk0 = (lane & 3) * 8;
   float m_run = -INFINITY, l_run = 0.f;
-  if (a.sink) {
+  if (a.sink && sp.n_splits == 1) {
     m_run = a.sink[hg * kHG + sh] * 1.4426950408889634f;
     l_run = 1.f;
   }
 
   const uint16_t* ent = static_cast<const uint16_t*>(a.entries) + (int64_t)b * a.entries_seq_stride;
   const uint16_t* raw = static_cast<const uint16_t*>(a.raw) + (int64_t)b * a.raw_seq_stride;
-  const int ntiles = (nkeys + kNK - 1) / kNK;
+  const int ntiles = kend > kbeg ? (kend - kbeg + kNK - 1) / kNK : 0;
+  uint4 ku[8];
   for (int tile = 0; tile < ntiles; ++tile) {
-    // ---- this wave's quarter of 32 keys as B-fragments: key lane%32, dims s*16 + (lane/32)*8
-    const int kj = tile * kNK + (lane & 31);
-    const bool kok = kj < nkeys;
-    const uint16_t* krow = nullptr;
-    if (kok) {
-      const int32_t id = sm.keys[kj];
-      krow = id >= 0 ? ent + (int64_t)id * 512 : raw + (int64_t)(-id - 1) * a.raw_ld;
-    }
-    uint4 ku[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      ku[s] = kok ? *reinterpret_cast<const uint4*>(krow + wave * kDQ + s * 16 + (lane >> 5) * 8) : make_uint4(0, 0, 0, 0);
+    const int k0 = kbeg + tile * kNK;
+    load_quarter(ku, sm.keys, k0 + (lane & 31), kend, ent, raw, a.raw_ld, wave, lane);
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -216,14 +240,16 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups) {
       for (int j = 0; j < 8; ++j) {
         const int key = sk0 + j;
         float v = sm.sred[0][sh][key] + sm.sred[1][sh][key] + sm.sred[2][sh][key] + sm.sred[3][sh][key];
-        v = (tile * kNK + key < nkeys) ? v * scale : -INFINITY;
+        v = (k0 + key < kend) ? v * scale : -INFINITY;
         sv[j] = v;
         tmax = fmaxf(tmax, v);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float al = exp2f(m_run - m_new);
+      // lazy rescaling: the reference max moves only when a logit exceeds it by more than 2^8, so
+      // weights stay below 256 and O is rescaled in few tiles
+      const float m_new = tmax > m_run + kRescaleLog2 ? tmax : m_run;
+      const float al = m_new == m_run ? 1.f : exp2f(m_run - m_new);
       float psum = 0.f;
       uint16_t pb[8];
 #pragma unroll
@@ -243,24 +269,33 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups) {
       if ((lane & 3) == 0) {
         sm.alpha[sh] = al;
         sm.lsum[sh] = l_run;
+        sm.mrun[sh] = m_run;
       }
+      // the flag of this tile's parity was cleared a tile ago; clear the other one for the next tile
+      if (al != 1.f) sm.rescale[tile & 1] = 1;
+      if (threadIdx.x == 0) sm.rescale[(tile + 1) & 1] = 0;
     }
     __syncthreads();
 
     // ---- O = alpha * O + P V over this wave's 128 dims
+    if (sm.rescale[tile & 1]) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float al = sm.alpha[mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) o[mt][nt][r] *= al;
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      float al[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) al[r] = sm.alpha[mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
       bf16x8 pf[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         pf[ks] = *reinterpret_cast<const bf16x8*>(&sm.pl[mt * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mt][nt][r] *= al[r];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sm.vt[wave][nt * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8]);
@@ -269,18 +304,85 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups) {
       }
     }
   }
+  if (ntiles == 0 && (lane & 3) == 0) {
+    sm.lsum[sh] = l_run;
+    sm.mrun[sh] = m_run;
+  }
   __syncthreads();
-  // ---- normalise and store: head hg*64 + row index, dim wave*128 + nt*32 + lane%32
-  const int64_t obase = (row * a.H + (int64_t)hg * kHG) * 512 + wave * kDQ;
+  if (sp.n_splits == 1) {
+    // ---- normalise and store: head hg*64 + row index, dim wave*128 + nt*32 + lane%32
+    const int64_t obase = (row * a.H + (int64_t)hg * kHG) * 512 + wave * kDQ;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int h = mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      const float inv = 1.f / sm.lsum[h];
+      for (int r = 0; r < 16; ++r) {
+        const int h = mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const float inv = 1.f / sm.lsum[h];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) store_elem<OT>(a.out, obase + (int64_t)h * 512 + nt * 32 + (lane & 31), o[mt][nt][r] * inv);
+        for (int nt = 0; nt < 4; ++nt)
+          store_elem<OT>(a.out, obase + (int64_t)h * 512 + nt * 32 + (lane & 31), o[mt][nt][r] * inv);
+      }
+  } else {
+    // ---- this split's partial for attn_combine: O / l in bf16, (m, l) in fp32
+    const int64_t pidx = rg * sp.n_splits + split;
+    uint16_t* po = sp.part_o + pidx * (kHG * 512) + wave * kDQ;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int h = mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const float l = sm.lsum[h];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) po[h * 512 + nt * 32 + (lane & 31)] = f2bf(o[mt][nt][r] * inv);
+      }
+    if (threadIdx.x < kHG) {
+      sp.part_ml[(pidx * kHG + threadIdx.x) * 2] = sm.mrun[threadIdx.x];
+      sp.part_ml[(pidx * kHG + threadIdx.x) * 2 + 1] = sm.lsum[threadIdx.x];
     }
+  }
+}
+
+// Merges the n_splits partials of every (row, head): M = max m_s, L = sum l_s 2^(m_s - M) (plus the
+// sink), O = sum l_s 2^(m_s - M) (O_s / l_s) / L, splits taken in order. One workgroup per
+// (row, 4 heads).
+template <int OT>
+__global__ void __launch_bounds__(256) attn_combine(AttnArgs a, int n_groups, AttnSplit sp) {
+  const int64_t R = (int64_t)a.B * a.T;
+  const int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
+  if (gid >= R * a.H) return;
+  const int64_t row = gid / a.H;
+  const int h = (int)(gid % a.H);
+  const int hg = h / kHG, hl = h % kHG;
+  const int64_t rg = row * n_groups + hg;
+  const int lane = lane_id();
+  float M = -INFINITY;
+  for (int s = 0; s < sp.n_splits; ++s) {
+    const float* ml = sp.part_ml + ((rg * sp.n_splits + s) * kHG + hl) * 2;
+    if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+  }
+  float sink2 = -INFINITY;
+  if (a.sink) {
+    sink2 = a.sink[h] * 1.4426950408889634f;
+    M = fmaxf(M, sink2);
+  }
+  float L = a.sink ? exp2f(sink2 - M) : 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < sp.n_splits; ++s) {
+    const int64_t pidx = rg * sp.n_splits + s;
+    const float* ml = sp.part_ml + (pidx * kHG + hl) * 2;
+    if (!(ml[1] > 0.f)) continue;
+    const float wgt = ml[1] * exp2f(ml[0] - M);
+    L += wgt;
+    const uint4 u = *reinterpret_cast<const uint4*>(sp.part_o + pidx * (kHG * 512) + hl * 512 + lane * 8);
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = fmaf(__uint_as_float((w4[j >> 1] >> ((j & 1) * 16)) << 16), wgt, acc[j]);
+  }
+  const float inv = 1.f / L;
+  const int64_t ob = (row * a.H + h) * 512 + lane * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) store_elem<OT>(a.out, ob + j, acc[j] * inv);
 }
 
 int attn_mfma_lds(const AttnArgs& a) { return (int)(sizeof(AttnSmem) + (size_t)(a.k + a.W + 1) * 4); }
@@ -290,25 +392,64 @@ bool use_attn_mfma(const AttnArgs& a) {
          a.q_seq_stride % 8 == 0 && a.entries_seq_stride % 8 == 0 && a.raw_seq_stride % 8 == 0;
 }
 
+
+constexpr int kDecodeRows = 8;     // fewer query rows per sequence than this: decode regime
+constexpr int kSplitKeys = 256;    // keys per split in the decode regime
+
+AttnSplit plan_split(const AttnArgs& a) {
+  AttnSplit sp{1, a.k + a.W, nullptr, nullptr};
+  if (!use_attn_mfma(a) || a.T >= kDecodeRows) return sp;
+  const int maxkeys = a.k + a.W;
+  const int S = (int)ceil_div(maxkeys, kSplitKeys);
+  if (S <= 1) return sp;
+  sp.n_splits = S;
+  sp.split_keys = kSplitKeys;
+  return sp;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
-size_t attn_workspace(const AttnArgs&) { return 0; }
+size_t attn_workspace(const AttnArgs& a) {
+  const AttnSplit sp = plan_split(a);
+  if (sp.n_splits <= 1) return 0;
+  const int64_t parts = (int64_t)a.B * a.T * (a.H / kHG) * sp.n_splits;
+  return align256((size_t)parts * kHG * 512 * 2) + align256((size_t)parts * kHG * 2 * 4);
+}
 
-hipError_t launch_attn(const AttnArgs& a, void*, size_t, hipStream_t s) {
+hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
   const int64_t R = (int64_t)a.B * a.T;
   if (R == 0) return hipSuccess;
   hipError_t e;
   if (use_attn_mfma(a)) {
     const int ng = a.H / kHG;
     const int lds = attn_mfma_lds(a);
+    AttnSplit sp = plan_split(a);
+    if (sp.n_splits > 1) {
+      if (ws == nullptr || ws_bytes < attn_workspace(a)) return hipErrorInvalidValue;
+      const int64_t parts = R * ng * sp.n_splits;
+      sp.part_o = static_cast<uint16_t*>(ws);
+      sp.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256((size_t)parts * kHG * 512 * 2));
+    }
+    const dim3 grid((unsigned)(R * ng * sp.n_splits));
     if (a.out_dtype == CSA_BF16) {
       if ((e = allow_lds((const void*)attn_mfma<CSA_BF16>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(attn_mfma<CSA_BF16>, dim3((unsigned)(R * ng)), dim3(256), lds, s, a, ng);
+      hipLaunchKernelGGL(attn_mfma<CSA_BF16>, grid, dim3(256), lds, s, a, ng, sp);
     } else {
       if ((e = allow_lds((const void*)attn_mfma<CSA_F32>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(attn_mfma<CSA_F32>, dim3((unsigned)(R * ng)), dim3(256), lds, s, a, ng);
+      hipLaunchKernelGGL(attn_mfma<CSA_F32>, grid, dim3(256), lds, s, a, ng, sp);
     }
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (sp.n_splits > 1) {
+      const dim3 cg((unsigned)ceil_div(R * a.H, 4));
+      if (a.out_dtype == CSA_BF16)
+        hipLaunchKernelGGL(attn_combine<CSA_BF16>, cg, dim3(256), 0, s, a, ng, sp);
+      else
+        hipLaunchKernelGGL(attn_combine<CSA_F32>, cg, dim3(256), 0, s, a, ng, sp);
+      return hipGetLastError();
+    }
+    return hipSuccess;
   }
   const dim3 grid((unsigned)R), block(kGenWaves * 64);
   if (a.in_dtype == CSA_F32 && a.out_dtype == CSA_F32)

@@ -49,6 +49,9 @@ __device__ __forceinline__ void store_elem<CSA_BF16>(void* p, int64_t i, float v
   static_cast<uint16_t*>(p)[i] = f2bf(v);
 }
 
+// max(v, 0) in one v_med3_f32 (fmaxf adds a NaN-quieting max in IEEE mode); inputs are finite.
+__device__ __forceinline__ float relu(float v) { return __builtin_amdgcn_fmed3f(v, 0.f, 3.0e38f); }
+
 // ------------------------------------------------------------------ wave helpers
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -19,6 +19,7 @@
 //  * index_generic (any dims, fp32 / bf16 / MXFP4): one wave per query row, scalar FMA scores,
 //    same streaming selection.
 #include "kernels.h"
+#include "select_radix.h"
 #include "topk_wave.h"
 
 namespace csa {
@@ -100,7 +101,7 @@ __global__ void __launch_bounds__(kGenWaves * 64) index_generic(IndexArgs a, int
         const uint8_t* qhs = DT == CSA_MXFP4 ? qs + h * nsb : nullptr;
         float dot = 0.f;
         for (int d = 0; d < a.D_I; ++d) dot = fmaf(idx_elem<DT>(qh, qhs, d), idx_elem<DT>(krow, ks, d), dot);
-        s = fmaf(w[h], fmaxf(dot, 0.f), s);
+        s = fmaf(w[h], relu(dot), s);
       }
     }
     tk.offer(make_cand(s, (uint32_t)i), valid);
@@ -186,22 +187,28 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
     if (tile + 1 < ntiles) fetch(tile + 1);
     if (active && (int64_t)tile * kNE < nv) {
       const uint16_t* kt = ktile + cur * (kNE * kLDK);
+      // both 32-entry column tiles at once: four independent MFMA chains
+      f32x16 acc[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + (nt * 32 + (lane & 31)) * kLDK + s * 16 + (lane >> 5) * 8);
+          acc[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, acc[nt][0], 0, 0, 0);
+          acc[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, acc[nt][1], 0, 0, 0);
+        }
+      }
       float sc[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + (nt * 32 + (lane & 31)) * kLDK + s * 16 + (lane >> 5) * 8);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, acc1, 0, 0, 0);
-        }
-        float p = 0.f;
+        // sum_h w_h * ReLU over the 32 heads held in registers, in four partial sums
+        float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p = fmaf(wr[0][r], fmaxf(acc0[r], 0.f), p);
-          p = fmaf(wr[1][r], fmaxf(acc1[r], 0.f), p);
+          p4[r & 3] = fmaf(wr[0][r], relu(acc[nt][0][r]), p4[r & 3]);
+          p4[r & 3] = fmaf(wr[1][r], relu(acc[nt][1][r]), p4[r & 3]);
         }
+        float p = (p4[0] + p4[1]) + (p4[2] + p4[3]);
         p += __shfl_xor(p, 32, 64);
         sc[nt] = p;
       }
@@ -227,14 +234,18 @@ constexpr int kScoreTiles = 4;   // 64-entry tiles per wave
 constexpr int kScoreChunk = kScoreWaves * kScoreTiles * 64;
 
 // scores[row, i] for i < n_vis(row); n_valid[row] = n_vis(row).
-__global__ void __launch_bounds__(kScoreWaves * 64) score_bf16_mfma(IndexArgs a, float* scores, int32_t* n_valid) {
+__global__ void __launch_bounds__(kScoreWaves * 64) score_bf16_mfma(IndexArgs a, float* scores, int32_t* n_valid,
+                                                                     uint32_t* hist) {
+  __shared__ uint32_t lh[kSelBins];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int64_t row = blockIdx.y;
   const int b = (int)(row / a.T), t = (int)(row % a.T);
   const int64_t nv = n_visible(a.q_pos0 + t, a.m, a.n_cap);
   if (blockIdx.x == 0 && threadIdx.x == 0) n_valid[row] = (int32_t)nv;
+  if ((int64_t)blockIdx.x * kScoreChunk >= nv) return;
+  sel_zero_lds_hist(lh);
+  __syncthreads();
   const int64_t base0 = (int64_t)blockIdx.x * kScoreChunk + (int64_t)wave * kScoreTiles * 64;
-  if (base0 >= nv) return;
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld;
   bf16x8 qf[2][8];
 #pragma unroll
@@ -273,30 +284,41 @@ __global__ void __launch_bounds__(kScoreWaves * 64) score_bf16_mfma(IndexArgs a,
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf[s], acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf[s], acc1, 0, 0, 0);
       }
-      float p = 0.f;
+      float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p = fmaf(wr[0][r], fmaxf(acc0[r], 0.f), p);
-        p = fmaf(wr[1][r], fmaxf(acc1[r], 0.f), p);
+        p4[r & 3] = fmaf(wr[0][r], relu(acc0[r]), p4[r & 3]);
+        p4[r & 3] = fmaf(wr[1][r], relu(acc1[r]), p4[r & 3]);
       }
+      float p = (p4[0] + p4[1]) + (p4[2] + p4[3]);
       p += __shfl_xor(p, 32, 64);
       sc[nt] = p;
     }
     const int64_t i = base + lane;
-    if (i < nv) srow[i] = lane < 32 ? sc[0] : sc[1];
+    if (i < nv) {
+      const float v = lane < 32 ? sc[0] : sc[1];
+      srow[i] = v;
+      atomicAdd(&lh[score_to_key(v) >> kSelShift], 1u);
+    }
   }
+  __syncthreads();
+  sel_flush_hist(lh, hist + row * kSelBins);
 }
 
 // MXFP4 q/k: A = q (16 heads x 128 dims per M-tile), B = keys (128 dims x 16 entries); lane l holds
 // row/column l%16 and the 32-element block l/16 (16 code bytes) plus that block's e8m0 scale.
-__global__ void __launch_bounds__(kScoreWaves * 64) score_fp4_mfma(IndexArgs a, float* scores, int32_t* n_valid) {
+__global__ void __launch_bounds__(kScoreWaves * 64) score_fp4_mfma(IndexArgs a, float* scores, int32_t* n_valid,
+                                                                    uint32_t* hist) {
+  __shared__ uint32_t lh[kSelBins];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int64_t row = blockIdx.y;
   const int b = (int)(row / a.T), t = (int)(row % a.T);
   const int64_t nv = n_visible(a.q_pos0 + t, a.m, a.n_cap);
   if (blockIdx.x == 0 && threadIdx.x == 0) n_valid[row] = (int32_t)nv;
+  if ((int64_t)blockIdx.x * kScoreChunk >= nv) return;
+  sel_zero_lds_hist(lh);
+  __syncthreads();
   const int64_t base0 = (int64_t)blockIdx.x * kScoreChunk + (int64_t)wave * kScoreTiles * 64;
-  if (base0 >= nv) return;
   const int g = lane >> 4, c = lane & 15;
   const uint8_t* qcodes = static_cast<const uint8_t*>(a.q) + row * (64 * 64);
   const uint8_t* qsc = a.q_scale + row * (64 * 4);
@@ -337,15 +359,20 @@ __global__ void __launch_bounds__(kScoreWaves * 64) score_fp4_mfma(IndexArgs a, 
         f32x4 acc = {};
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb, acc, 4, 4, 0, qs[mt], 0, ks);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p = fmaf(wr[mt][r], fmaxf(acc[r], 0.f), p);
+        for (int r = 0; r < 4; ++r) p = fmaf(wr[mt][r], relu(acc[r]), p);
       }
       p += __shfl_xor(p, 16, 64);
       p += __shfl_xor(p, 32, 64);
       if (g == grp) mine = p;
     }
     const int64_t i = base + lane;
-    if (i < nv) srow[i] = mine;
+    if (i < nv) {
+      srow[i] = mine;
+      atomicAdd(&lh[score_to_key(mine) >> kSelShift], 1u);
+    }
   }
+  __syncthreads();
+  sel_flush_hist(lh, hist + row * kSelBins);
 }
 
 constexpr int kMaxLds = 160 * 1024;
@@ -367,7 +394,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t index_topk_workspace(const IndexArgs& a) {
   if (!use_decode_scores(a)) return 0;
   const int64_t R = (int64_t)a.B * a.T;
-  return align256((size_t)R * a.n_cap * 4) + align256((size_t)R * 4) + topk_workspace((int)R, a.n_cap, a.k);
+  return align256((size_t)R * a.n_cap * 4) + align256((size_t)R * 4) + select_workspace((int)R, a.n_cap, a.k);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -392,14 +419,15 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
     p += align256((size_t)R * 4);
     dim3 grid((unsigned)ceil_div(a.n_cap, kScoreChunk) > 0 ? (unsigned)ceil_div(a.n_cap, kScoreChunk) : 1u,
               (unsigned)R);
+    if ((e = launch_select_zero(p, (int)R, a.n_cap, a.k, s)) != hipSuccess) return e;
+    uint32_t* hist = select_hist(p);
     if (a.idx_dtype == CSA_MXFP4) {
-      hipLaunchKernelGGL(score_fp4_mfma, grid, dim3(kScoreWaves * 64), 0, s, a, scores, nvalid);
+      hipLaunchKernelGGL(score_fp4_mfma, grid, dim3(kScoreWaves * 64), 0, s, a, scores, nvalid, hist);
     } else {
-      hipLaunchKernelGGL(score_bf16_mfma, grid, dim3(kScoreWaves * 64), 0, s, a, scores, nvalid);
+      hipLaunchKernelGGL(score_bf16_mfma, grid, dim3(kScoreWaves * 64), 0, s, a, scores, nvalid, hist);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    TopkArgs t{scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score};
-    return launch_topk_from_scores(t, p, ws_bytes - (size_t)(p - static_cast<uint8_t*>(ws)), s);
+    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s);
   }
   const int cap = topk_cap_for(a.k, 256);
   const int lds = kGenWaves * (cap * 8 + 256 * 4);

@@ -47,10 +47,12 @@ class CSADecode:
         self.idx = torch.empty(B, 1, d.top_k, dtype=torch.int32, device=device)
         self.out = torch.empty(B, 1, d.H, d.D, dtype=out_dtype, device=device)
         self.ws = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, d, B, 1, n_cap, 0, idx_dtype), device)
+        self.ws_attn = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_SPARSE_ATTN, d, B, 1, n_cap, 0, lib.CSA_BF16),
+                                     device)
 
     def __call__(self, L: int, q_idx, w_head, keys, q, entries, kv_raw, q_scale=None, k_scale=None, sink=None):
         lib.csa_index_topk(self.d, q_idx, w_head, keys, self.idx, q_pos0=L, q_scale=q_scale, k_scale=k_scale,
                            ws=self.ws)
         lib.csa_sparse_attn(self.d, q, entries, self.idx, kv_raw, self.out, q_pos0=L,
-                            raw_pos0=L - (self.d.window - 1), sink=sink)
+                            raw_pos0=L - (self.d.window - 1), sink=sink, ws=self.ws_attn)
         return self.out

@@ -202,7 +202,7 @@ def csa_topk_from_scores(scores, n_valid, k: int, out_idx, out_score=None):
     return out_idx
 
 
-def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, raw_pos0: int, sink=None):
+def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, raw_pos0: int, sink=None, ws=None):
     """Step 4. q [B, T, H, D]; entries [B, n_cap, D]; idx int32 [B, T, k]; kv_raw [B, R, D] whose row r is
     position raw_pos0 + r; out [B, T, H, D] (float32 or bfloat16)."""
     _require_cuda(q, entries, idx, kv_raw, out, sink)
@@ -211,10 +211,14 @@ def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, ra
         raise ValueError("q heads and entry rows must be contiguous")
     if kv_raw.stride(2) != 1 or not out.is_contiguous() or not idx.is_contiguous():
         raise ValueError("kv_raw rows, idx and out must be contiguous")
+    need = csa_workspace_size(CSA_OP_SPARSE_ATTN, dims, B, T, entries.shape[1], 0, _dt(q))
+    if ws is None or ws.numel() < need + 256:
+        ws = _workspace(need, q.device)
+    wp, wn = _aligned_ptr(ws)
     _check(load().csa_sparse_attn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
                                   _p(entries), entries.stride(0), entries.shape[1], _p(idx), _p(kv_raw),
                                   kv_raw.stride(1), kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out),
-                                  _dt(out), None, 0, _stream()))
+                                  _dt(out), wp, wn, _stream()))
     return out
 
 

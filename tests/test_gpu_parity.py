@@ -290,3 +290,25 @@ def test_full_decode1m_fp4():
     inp = G.make_inputs(wl)
     st = run_decode(wl, decode_tensors(wl, inp))
     _decode_check(wl, inp, st, [0, 3])
+
+
+def test_decode_sink_split_kv():
+    # few (row, head group) pairs: the key list is split across workgroups and merged; the sink
+    # enters once, in the merge
+    wl = get("decode128k").with_(B=2, L=4 * 3000)
+    inp = G.make_inputs(wl)
+    t = decode_tensors(wl, inp)
+    sink = np.linspace(-2.0, 3.0, wl.H)
+    from compressed_sparse_attention_05_amd import layer
+    code = lib.CSA_BF16
+    st = layer.CSADecode(dims_of(wl), wl.B, wl.L // wl.m, idx_dtype=code)
+    st(wl.L, t["q_idx"], t["w_head"], t["keys"], t["q"], t["entries"], t["kv_raw"],
+       sink=to_device(sink.astype(np.float32), "f32"))
+    torch.cuda.synchronize()
+    gidx = st.idx.cpu().numpy()
+    gout = st.out.float().cpu().numpy()
+    for b in range(wl.B):
+        r = O.decode(inp, wl, b, sink=sink)
+        check_idx_rows(gidx[b], r["idx"], r["scores"], r["n_vis"])
+        ref = O.sparse_attention(r["q"], r["entries"], gidx[b], r["raw"], wl.L - wl.W + 1, [wl.L], wl.W, sink=sink)
+        assert max_err(gout[b], ref) <= TOL["bf16"]
