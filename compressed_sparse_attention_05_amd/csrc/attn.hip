@@ -99,15 +99,17 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
 
 // ---------------------------------------------------------------- MFMA (bf16, D = 512)
 
-constexpr int kHG = 64;        // heads per workgroup
-constexpr int kNK = 32;        // keys per tile
-constexpr int kVT = 40;        // LDS row stride (bf16) of the transposed key quarter and of P
-constexpr int kDQ = 128;       // dims per wave
-constexpr float kRescaleLog2 = 8.f;  // reference-max slack before O is rescaled
+constexpr int kHG = 64;                // heads per workgroup
+constexpr int kNW = 8;                 // waves per workgroup; each owns 512/kNW dims
+constexpr int kDW = 512 / kNW;         // dims per wave (64)
+constexpr int kNK = 32;                // keys per tile
+constexpr int kVT = 40;                // LDS row stride (bf16) of the transposed key slice and of P
+constexpr int kHW = kHG / kNW;         // heads whose softmax a wave finishes (8)
+constexpr float kRescaleLog2 = 8.f;    // reference-max slack before O is rescaled
 
 struct AttnSmem {
-  float sred[4][kHG][kNK];         // partial logits per wave          32 KiB
-  uint16_t vt[4][kDQ][kVT];        // key quarters, dim-major          40 KiB
+  float sred[kNW][kHG][kNK];       // partial logits per wave          64 KiB
+  uint16_t vt[kNW][kDW][kVT];      // key slices, dim-major            40 KiB
   uint16_t pl[kHG][kVT];           // probabilities, bf16              5 KiB
   float alpha[kHG];                // per-head rescale of O this tile
   float lsum[kHG];                 // per-head running denominators
@@ -127,9 +129,10 @@ struct AttnSplit {
   float* part_ml;    // [R*G*S, 64, 2]: running max (log2 units), running sum
 };
 
-__device__ __forceinline__ void load_quarter(uint4 (&ku)[8], const int32_t* keys, int kj, int kend,
-                                             const uint16_t* ent, const uint16_t* raw, int64_t raw_ld, int wave,
-                                             int lane) {
+// This wave's slice of one gathered key as B-fragments: key kj, dims wave*64 + s*16 + (lane/32)*8.
+__device__ __forceinline__ void load_slice(uint4 (&ku)[kDW / 16], const int32_t* keys, int kj, int kend,
+                                           const uint16_t* ent, const uint16_t* raw, int64_t raw_ld, int wave,
+                                           int lane) {
   const bool kok = kj < kend;
   const uint16_t* krow = nullptr;
   if (kok) {
@@ -137,12 +140,12 @@ __device__ __forceinline__ void load_quarter(uint4 (&ku)[8], const int32_t* keys
     krow = id >= 0 ? ent + (int64_t)id * 512 : raw + (int64_t)(-id - 1) * raw_ld;
   }
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    ku[s] = kok ? *reinterpret_cast<const uint4*>(krow + wave * kDQ + s * 16 + (lane >> 5) * 8) : make_uint4(0, 0, 0, 0);
+  for (int s = 0; s < kDW / 16; ++s)
+    ku[s] = kok ? *reinterpret_cast<const uint4*>(krow + wave * kDW + s * 16 + (lane >> 5) * 8) : make_uint4(0, 0, 0, 0);
 }
 
 template <int OT>
-__global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnSplit sp) {
+__global__ void __launch_bounds__(kNW * 64) attn_mfma(AttnArgs a, int n_groups, AttnSplit sp) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
   const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -155,8 +158,8 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
   const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
 
   // ---- key list: valid selected entries, then the window rows
-  int nsel = 0;
   if (wave == 0) {
+    int nsel = 0;
     const int32_t* idx = a.idx + row * a.k;
     for (int base = 0; base < a.k; base += 64) {
       const int j = base + lane;
@@ -168,34 +171,36 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
     }
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
     for (int j = lane; j < nwin; j += 64) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
-    if (lane == 0) sm.keys[a.k + a.W] = nsel + nwin;
-    if (lane == 0) sm.rescale[0] = 0;
+    if (lane == 0) {
+      sm.keys[a.k + a.W] = nsel + nwin;
+      sm.rescale[0] = 0;
+    }
   }
   __syncthreads();
   const int nkeys = sm.keys[a.k + a.W];
   const int kbeg = split * sp.split_keys;
   const int kend = kbeg + sp.split_keys < nkeys ? kbeg + sp.split_keys : nkeys;
 
-  // ---- q quarter as A-fragments: head hg*64 + mt*32 + lane%32, dims wave*128 + s*16 + (lane/32)*8
+  // ---- q slice as A-fragments: head hg*64 + mt*32 + lane%32, dims wave*64 + s*16 + (lane/32)*8
   const float scale = a.scale * 1.4426950408889634f;  // logits in log2 units
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld +
-                         (int64_t)hg * kHG * 512 + wave * kDQ;
-  bf16x8 qf[2][8];
+                         (int64_t)hg * kHG * 512 + wave * kDW;
+  bf16x8 qf[2][kDW / 16];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < kDW / 16; ++s)
       qf[mt][s] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)(mt * 32 + (lane & 31)) * 512 + s * 16 + (lane >> 5) * 8);
 
-  f32x16 o[2][4];
+  f32x16 o[2][kDW / 32];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = f32x16{};
+    for (int nt = 0; nt < kDW / 32; ++nt) o[mt][nt] = f32x16{};
 
-  // softmax ownership: wave w handles heads w*16 + lane/4, keys (lane%4)*8 .. +7
-  const int sh = wave * 16 + (lane >> 2);
-  const int sk0 = (lane & 3) * 8;
+  // softmax ownership: wave w finishes heads w*8 + lane/8, keys (lane%8)*4 .. +3
+  const int sh = wave * kHW + (lane >> 3);
+  const int sk0 = (lane & 7) * 4;
   float m_run = -INFINITY, l_run = 0.f;
   if (a.sink && sp.n_splits == 1) {
     m_run = a.sink[hg * kHG + sh] * 1.4426950408889634f;
@@ -205,13 +210,14 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
   const uint16_t* ent = static_cast<const uint16_t*>(a.entries) + (int64_t)b * a.entries_seq_stride;
   const uint16_t* raw = static_cast<const uint16_t*>(a.raw) + (int64_t)b * a.raw_seq_stride;
   const int ntiles = kend > kbeg ? (kend - kbeg + kNK - 1) / kNK : 0;
-  uint4 ku[8];
-  for (int tile = 0; tile < ntiles; ++tile) {
+  // Gathered key slices cycle through three register sets: the loads of tile i+3 are issued as soon
+  // as tile i has been consumed, so three tiles of HBM/L2 latency are in flight behind the math.
+  uint4 kbuf[3][kDW / 16];
+  auto tile_step = [&](uint4 (&ku)[kDW / 16], const int tile) {
     const int k0 = kbeg + tile * kNK;
-    load_quarter(ku, sm.keys, k0 + (lane & 31), kend, ent, raw, a.raw_ld, wave, lane);
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kDW / 16; ++s) {
       const bf16x8 kf = __builtin_bit_cast(bf16x8, ku[s]);
       sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, sacc[0], 0, 0, 0);
       sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, sacc[1], 0, 0, 0);
@@ -222,51 +228,55 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         sm.sred[wave][mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)][lane & 31] = sacc[mt][r];
-    // key quarter, transposed: vt[dim][key]
+    // key slice, transposed: vt[dim][key]
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kDW / 16; ++s) {
       const uint32_t w4[4] = {ku[s].x, ku[s].y, ku[s].z, ku[s].w};
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         sm.vt[wave][s * 16 + (lane >> 5) * 8 + j][lane & 31] = (uint16_t)(w4[j >> 1] >> ((j & 1) * 16));
     }
+    // this register set is free again: start gathering the tile three ahead into it
+    if (tile + 3 < ntiles) load_slice(ku, sm.keys, k0 + 3 * kNK + (lane & 31), kend, ent, raw, a.raw_ld, wave, lane);
     __syncthreads();
 
-    // ---- online softmax of 16 heads x 32 keys per wave
+    // ---- online softmax of kHW heads x 32 keys per wave
     {
-      float sv[8];
+      float sv[4];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         const int key = sk0 + j;
-        float v = sm.sred[0][sh][key] + sm.sred[1][sh][key] + sm.sred[2][sh][key] + sm.sred[3][sh][key];
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) v += sm.sred[w][sh][key];
         v = (k0 + key < kend) ? v * scale : -INFINITY;
         sv[j] = v;
         tmax = fmaxf(tmax, v);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 4, 64));
       // lazy rescaling: the reference max moves only when a logit exceeds it by more than 2^8, so
       // weights stay below 256 and O is rescaled in few tiles
       const float m_new = tmax > m_run + kRescaleLog2 ? tmax : m_run;
       const float al = m_new == m_run ? 1.f : exp2f(m_run - m_new);
       float psum = 0.f;
-      uint16_t pb[8];
+      uint16_t pb[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pe = exp2f(sv[j] - m_new);
-        const uint16_t h16 = f2bf(pe);
+      for (int j = 0; j < 4; ++j) {
+        const uint16_t h16 = f2bf(exp2f(sv[j] - m_new));
         pb[j] = h16;
         psum += bf2f(h16);  // the denominator sums the same rounded weights P V uses
       }
       psum += __shfl_xor(psum, 1, 64);
       psum += __shfl_xor(psum, 2, 64);
+      psum += __shfl_xor(psum, 4, 64);
       l_run = l_run * al + psum;
       m_run = m_new;
-      *reinterpret_cast<uint4*>(&sm.pl[sh][sk0]) =
-          make_uint4(pb[0] | ((uint32_t)pb[1] << 16), pb[2] | ((uint32_t)pb[3] << 16), pb[4] | ((uint32_t)pb[5] << 16),
-                     pb[6] | ((uint32_t)pb[7] << 16));
-      if ((lane & 3) == 0) {
+      *reinterpret_cast<uint2*>(&sm.pl[sh][sk0]) =
+          make_uint2(pb[0] | ((uint32_t)pb[1] << 16), pb[2] | ((uint32_t)pb[3] << 16));
+      if ((lane & 7) == 0) {
         sm.alpha[sh] = al;
         sm.lsum[sh] = l_run;
         sm.mrun[sh] = m_run;
@@ -277,7 +287,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
     }
     __syncthreads();
 
-    // ---- O = alpha * O + P V over this wave's 128 dims
+    // ---- O = alpha * O + P V over this wave's dims
     if (sm.rescale[tile & 1]) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -285,7 +295,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
         for (int r = 0; r < 16; ++r) {
           const float al = sm.alpha[mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) o[mt][nt][r] *= al;
+          for (int nt = 0; nt < kDW / 32; ++nt) o[mt][nt][r] *= al;
         }
     }
 #pragma unroll
@@ -295,7 +305,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
       for (int ks = 0; ks < 2; ++ks)
         pf[ks] = *reinterpret_cast<const bf16x8*>(&sm.pl[mt * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < kDW / 32; ++nt) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sm.vt[wave][nt * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8]);
@@ -303,15 +313,23 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
         }
       }
     }
+    };
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < ntiles) load_slice(kbuf[j], sm.keys, kbeg + j * kNK + (lane & 31), kend, ent, raw, a.raw_ld, wave, lane);
+  for (int tile = 0; tile < ntiles; tile += 3) {
+    tile_step(kbuf[0], tile);
+    if (tile + 1 < ntiles) tile_step(kbuf[1], tile + 1);
+    if (tile + 2 < ntiles) tile_step(kbuf[2], tile + 2);
   }
-  if (ntiles == 0 && (lane & 3) == 0) {
+  if (ntiles == 0 && (lane & 7) == 0) {
     sm.lsum[sh] = l_run;
     sm.mrun[sh] = m_run;
   }
   __syncthreads();
   if (sp.n_splits == 1) {
-    // ---- normalise and store: head hg*64 + row index, dim wave*128 + nt*32 + lane%32
-    const int64_t obase = (row * a.H + (int64_t)hg * kHG) * 512 + wave * kDQ;
+    // ---- normalise and store: head hg*64 + row index, dim wave*64 + nt*32 + lane%32
+    const int64_t obase = (row * a.H + (int64_t)hg * kHG) * 512 + wave * kDW;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -319,13 +337,13 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
         const int h = mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const float inv = 1.f / sm.lsum[h];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < kDW / 32; ++nt)
           store_elem<OT>(a.out, obase + (int64_t)h * 512 + nt * 32 + (lane & 31), o[mt][nt][r] * inv);
       }
   } else {
     // ---- this split's partial for attn_combine: O / l in bf16, (m, l) in fp32
     const int64_t pidx = rg * sp.n_splits + split;
-    uint16_t* po = sp.part_o + pidx * (kHG * 512) + wave * kDQ;
+    uint16_t* po = sp.part_o + pidx * (kHG * 512) + wave * kDW;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -334,7 +352,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int n_groups, AttnS
         const float l = sm.lsum[h];
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) po[h * 512 + nt * 32 + (lane & 31)] = f2bf(o[mt][nt][r] * inv);
+        for (int nt = 0; nt < kDW / 32; ++nt) po[h * 512 + nt * 32 + (lane & 31)] = f2bf(o[mt][nt][r] * inv);
       }
     if (threadIdx.x < kHG) {
       sp.part_ml[(pidx * kHG + threadIdx.x) * 2] = sm.mrun[threadIdx.x];
@@ -435,10 +453,10 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
     const dim3 grid((unsigned)(R * ng * sp.n_splits));
     if (a.out_dtype == CSA_BF16) {
       if ((e = allow_lds((const void*)attn_mfma<CSA_BF16>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(attn_mfma<CSA_BF16>, grid, dim3(256), lds, s, a, ng, sp);
+      hipLaunchKernelGGL(attn_mfma<CSA_BF16>, grid, dim3(kNW * 64), lds, s, a, ng, sp);
     } else {
       if ((e = allow_lds((const void*)attn_mfma<CSA_F32>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(attn_mfma<CSA_F32>, grid, dim3(256), lds, s, a, ng, sp);
+      hipLaunchKernelGGL(attn_mfma<CSA_F32>, grid, dim3(kNW * 64), lds, s, a, ng, sp);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (sp.n_splits > 1) {

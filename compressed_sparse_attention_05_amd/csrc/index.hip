@@ -229,135 +229,153 @@ int prefill_lds(int cap) { return 2 * kTileBytes + kPrefillQW * (cap * 8 + 256 *
 
 // ---------------------------------------------------------------- decode scores
 
-constexpr int kScoreWaves = 4;
-constexpr int kScoreTiles = 4;   // 64-entry tiles per wave
-constexpr int kScoreChunk = kScoreWaves * kScoreTiles * 64;
+// Loads one 64-entry tile of bf16 keys as B-fragments of v_mfma_f32_16x16x32_bf16: for column
+// group g and k-step s, lane l holds entry base + g*16 + l%16, dims s*32 + (l/16)*8 .. +7.
+__device__ __forceinline__ void load_keys16(uint4 (&kb)[16], const uint16_t* kseq, int64_t base, int64_t nv,
+                                            int lane) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int64_t e = base + g * 16 + (lane & 15);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      kb[g * 4 + s] = e < nv ? *reinterpret_cast<const uint4*>(kseq + e * 128 + s * 32 + (lane >> 4) * 8)
+                             : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------- decode scores, streamed
 
 // scores[row, i] for i < n_vis(row); n_valid[row] = n_vis(row).
-__global__ void __launch_bounds__(kScoreWaves * 64) score_bf16_mfma(IndexArgs a, float* scores, int32_t* n_valid,
-                                                                     uint32_t* hist) {
-  __shared__ uint32_t lh[kSelBins];
+// The (row, 512-entry unit) space is walked grid-stride by workgroups of 8 waves, so at every step
+// the whole chip reads adjacent 128 KiB units of the key arrays. The unit's row has its q_I staged
+// in LDS once (A-fragments are read from there), which keeps a wave at ~128 VGPRs and four waves
+// per SIMD in flight; each wave multiplies one 64-entry tile of the unit.
+// v_mfma_f32_16x16x32_bf16 with heads along the rows (4 M-tiles) and 16 entries along the columns:
+// lane l reads entry l%16, dims s*32 + (l/16)*8 .. +7 of k-step s (16 rows x 64 contiguous bytes per
+// load instruction).
+constexpr int kStreamWaves = 8;
+constexpr int kUnit = kStreamWaves * 64;
+constexpr int kQLd = 136;  // LDS row stride (bf16) of the staged q_I heads
+
+__global__ void __launch_bounds__(kStreamWaves * 64) score_bf16_stream(IndexArgs a, float* scores, int32_t* n_valid,
+                                                                        int64_t units_per_row) {
+  __shared__ __align__(16) uint16_t qs[64 * kQLd];
+  __shared__ float ws[64];
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int64_t row = blockIdx.y;
-  const int b = (int)(row / a.T), t = (int)(row % a.T);
-  const int64_t nv = n_visible(a.q_pos0 + t, a.m, a.n_cap);
-  if (blockIdx.x == 0 && threadIdx.x == 0) n_valid[row] = (int32_t)nv;
-  if ((int64_t)blockIdx.x * kScoreChunk >= nv) return;
-  sel_zero_lds_hist(lh);
-  __syncthreads();
-  const int64_t base0 = (int64_t)blockIdx.x * kScoreChunk + (int64_t)wave * kScoreTiles * 64;
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld;
-  bf16x8 qf[2][8];
+  const int64_t R = (int64_t)a.B * a.T;
+  const int64_t total = R * units_per_row;
+  int64_t cur_row = -1;
+  for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
+    const int64_t row = u / units_per_row;
+    const int64_t base = (u % units_per_row) * kUnit + wave * 64;
+    const int b = (int)(row / a.T), tq = (int)(row % a.T);
+    const int64_t nv = n_visible(a.q_pos0 + tq, a.m, a.n_cap);
+    if (row != cur_row) {  // uniform across the workgroup
+      __syncthreads();
+      cur_row = row;
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)tq * a.q_ld;
+      for (int c = threadIdx.x; c < 64 * 16; c += kStreamWaves * 64)
+        *reinterpret_cast<uint4*>(&qs[(c >> 4) * kQLd + (c & 15) * 8]) = *reinterpret_cast<const uint4*>(qrow + c * 8);
+      if (threadIdx.x < 64) ws[threadIdx.x] = head_weights(a, row)[threadIdx.x];
+      if (threadIdx.x == 0 && u % units_per_row == 0) n_valid[row] = (int32_t)nv;
+      __syncthreads();
+    }
+    if (base >= nv) continue;
+    const uint16_t* kseq = static_cast<const uint16_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
+    uint4 kb[16];
+    load_keys16(kb, kseq, base, nv, lane);
+    float wr[4][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qf[mt][s] = *reinterpret_cast<const bf16x8*>(qrow + (mt * 32 + (lane & 31)) * 128 + s * 16 + (lane >> 5) * 8);
-  const float* w = head_weights(a, row);
-  float wr[2][16];
+      for (int r = 0; r < 4; ++r) wr[mt][r] = ws[mt * 16 + (lane >> 4) * 4 + r];
+    float mine = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int g = 0; g < 4; ++g) {
+      // re-read the q_I fragments from LDS for every column group instead of holding all 64 VGPRs
+      asm volatile("" ::: "memory");
+      f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) wr[mt][r] = w[mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
-  const uint16_t* kseq = static_cast<const uint16_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
-  float* srow = scores + row * a.n_cap;
-  for (int tl = 0; tl < kScoreTiles; ++tl) {
-    const int64_t base = base0 + (int64_t)tl * 64;
-    if (base >= nv) break;
-    float sc[2];
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[g * 4 + s]);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t e = base + nt * 32 + (lane & 31);
-      const bool ok = e < nv;
-      bf16x8 kf[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (ok) {
-          kf[s] = *reinterpret_cast<const bf16x8*>(kseq + e * 128 + s * 16 + (lane >> 5) * 8);
-        } else {
-          kf[s] = bf16x8{};
+        for (int mt = 0; mt < 4; ++mt) {
+          // A-fragment: head mt*16 + lane%16, dims s*32 + (lane/16)*8 .. +7
+          const bf16x8 qf = *reinterpret_cast<const bf16x8*>(&qs[(mt * 16 + (lane & 15)) * kQLd + s * 32 + (lane >> 4) * 8]);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf, acc[mt], 0, 0, 0);
         }
-      }
-      f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf[s], acc1, 0, 0, 0);
       }
       float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p4[r & 3] = fmaf(wr[0][r], relu(acc0[r]), p4[r & 3]);
-        p4[r & 3] = fmaf(wr[1][r], relu(acc1[r]), p4[r & 3]);
-      }
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p4[r] = fmaf(wr[mt][r], relu(acc[mt][r]), p4[r]);
       float p = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      p += __shfl_xor(p, 16, 64);
       p += __shfl_xor(p, 32, 64);
-      sc[nt] = p;
+      if ((lane >> 4) == g) mine = p;  // lane l keeps entry base + l
     }
     const int64_t i = base + lane;
-    if (i < nv) {
-      const float v = lane < 32 ? sc[0] : sc[1];
-      srow[i] = v;
-      atomicAdd(&lh[score_to_key(v) >> kSelShift], 1u);
-    }
+    if (i < nv) scores[row * a.n_cap + i] = mine;
   }
-  __syncthreads();
-  sel_flush_hist(lh, hist + row * kSelBins);
 }
 
-// MXFP4 q/k: A = q (16 heads x 128 dims per M-tile), B = keys (128 dims x 16 entries); lane l holds
-// row/column l%16 and the 32-element block l/16 (16 code bytes) plus that block's e8m0 scale.
-__global__ void __launch_bounds__(kScoreWaves * 64) score_fp4_mfma(IndexArgs a, float* scores, int32_t* n_valid,
-                                                                    uint32_t* hist) {
-  __shared__ uint32_t lh[kSelBins];
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int64_t row = blockIdx.y;
-  const int b = (int)(row / a.T), t = (int)(row % a.T);
-  const int64_t nv = n_visible(a.q_pos0 + t, a.m, a.n_cap);
-  if (blockIdx.x == 0 && threadIdx.x == 0) n_valid[row] = (int32_t)nv;
-  if ((int64_t)blockIdx.x * kScoreChunk >= nv) return;
-  sel_zero_lds_hist(lh);
-  __syncthreads();
-  const int64_t base0 = (int64_t)blockIdx.x * kScoreChunk + (int64_t)wave * kScoreTiles * 64;
+// MXFP4 variant: a tile is 64 entries x (64 code bytes + 4 scale bytes).
+constexpr int kFp4Waves = 4;
+
+__global__ void __launch_bounds__(kFp4Waves * 64) score_fp4_stream(IndexArgs a, float* scores, int32_t* n_valid,
+                                                                     int64_t tiles_per_row) {
+  const int lane = lane_id();
   const int g = lane >> 4, c = lane & 15;
-  const uint8_t* qcodes = static_cast<const uint8_t*>(a.q) + row * (64 * 64);
-  const uint8_t* qsc = a.q_scale + row * (64 * 4);
+  const int64_t R = (int64_t)a.B * a.T;
+  const int64_t total = R * tiles_per_row;
+  const int64_t nwaves = (int64_t)gridDim.x * kFp4Waves;
+  int64_t cur_row = -1;
   i32x8 qa[4];
   int qs[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const i32x4 v = *reinterpret_cast<const i32x4*>(qcodes + (mt * 16 + c) * 64 + g * 16);
-    qa[mt] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-    qs[mt] = qsc[(mt * 16 + c) * 4 + g];
-  }
-  const float* w = head_weights(a, row);
   float wr[4][4];
+  for (int64_t t = (int64_t)blockIdx.x * kFp4Waves + (threadIdx.x >> 6); t < total; t += nwaves) {
+    const int64_t row = t / tiles_per_row;
+    const int64_t base = (t % tiles_per_row) * 64;
+    const int b = (int)(row / a.T), tq = (int)(row % a.T);
+    const int64_t nv = n_visible(a.q_pos0 + tq, a.m, a.n_cap);
+    if (base == 0 && lane == 0) n_valid[row] = (int32_t)nv;
+    if (base >= nv) continue;
+    if (row != cur_row) {
+      cur_row = row;
+      const uint8_t* qcodes = static_cast<const uint8_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)tq * a.q_ld;
+      const uint8_t* qsc = a.q_scale + row * (64 * 4);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(qcodes + (mt * 16 + c) * 64 + g * 16);
+        qa[mt] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        qs[mt] = qsc[(mt * 16 + c) * 4 + g];
+      }
+      const float* w = head_weights(a, row);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wr[mt][r] = w[mt * 16 + g * 4 + r];
-  const uint8_t* kcodes = static_cast<const uint8_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
-  const uint8_t* ksc = a.k_scale + (int64_t)b * a.n_cap * 4;
-  float* srow = scores + row * a.n_cap;
-  for (int tl = 0; tl < kScoreTiles; ++tl) {
-    const int64_t base = base0 + (int64_t)tl * 64;
-    if (base >= nv) break;
-    float mine = 0.f;
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wr[mt][r] = w[mt * 16 + g * 4 + r];
+    }
+    const uint8_t* kcodes = static_cast<const uint8_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
+    const uint8_t* ksc = a.k_scale + (int64_t)b * a.n_cap * 4;
+    i32x4 kv[4];
+    int ks[4];
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int64_t e = base + grp * 16 + c;
-      i32x8 kb = {};
-      int ks = 127;
-      if (e < nv) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(kcodes + e * 64 + g * 16);
-        kb = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        ks = ksc[e * 4 + g];
-      }
+      kv[grp] = e < nv ? *reinterpret_cast<const i32x4*>(kcodes + e * 64 + g * 16) : i32x4{0, 0, 0, 0};
+      ks[grp] = e < nv ? ksc[e * 4 + g] : 127;
+    }
+    float mine = 0.f;
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const i32x8 kb = i32x8{kv[grp][0], kv[grp][1], kv[grp][2], kv[grp][3], 0, 0, 0, 0};
       float p = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc = {};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb, acc, 4, 4, 0, qs[mt], 0, ks);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb, acc, 4, 4, 0, qs[mt], 0, ks[grp]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) p = fmaf(wr[mt][r], relu(acc[r]), p);
       }
@@ -366,13 +384,19 @@ __global__ void __launch_bounds__(kScoreWaves * 64) score_fp4_mfma(IndexArgs a, 
       if (g == grp) mine = p;
     }
     const int64_t i = base + lane;
-    if (i < nv) {
-      srow[i] = mine;
-      atomicAdd(&lh[score_to_key(mine) >> kSelShift], 1u);
-    }
+    if (i < nv) scores[row * a.n_cap + i] = mine;
   }
-  __syncthreads();
-  sel_flush_hist(lh, hist + row * kSelBins);
+}
+
+int stream_grid() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cus = n;
+    if (cus <= 0) cus = 256;
+  }
+  return 2 * cus;
 }
 
 constexpr int kMaxLds = 160 * 1024;
@@ -417,17 +441,19 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
     p += align256((size_t)R * a.n_cap * 4);
     int32_t* nvalid = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)R * 4);
-    dim3 grid((unsigned)ceil_div(a.n_cap, kScoreChunk) > 0 ? (unsigned)ceil_div(a.n_cap, kScoreChunk) : 1u,
-              (unsigned)R);
-    if ((e = launch_select_zero(p, (int)R, a.n_cap, a.k, s)) != hipSuccess) return e;
-    uint32_t* hist = select_hist(p);
     if (a.idx_dtype == CSA_MXFP4) {
-      hipLaunchKernelGGL(score_fp4_mfma, grid, dim3(kScoreWaves * 64), 0, s, a, scores, nvalid, hist);
+      const int64_t tpr = ceil_div(a.n_cap, 64) > 0 ? ceil_div(a.n_cap, 64) : 1;
+      int64_t g = ceil_div(R * tpr, kFp4Waves);
+      if (g > 2 * stream_grid()) g = 2 * stream_grid();
+      hipLaunchKernelGGL(score_fp4_stream, dim3((unsigned)g), dim3(kFp4Waves * 64), 0, s, a, scores, nvalid, tpr);
     } else {
-      hipLaunchKernelGGL(score_bf16_mfma, grid, dim3(kScoreWaves * 64), 0, s, a, scores, nvalid, hist);
+      const int64_t upr = ceil_div(a.n_cap, kUnit) > 0 ? ceil_div(a.n_cap, kUnit) : 1;
+      int64_t g = R * upr;
+      if (g > stream_grid()) g = stream_grid();
+      hipLaunchKernelGGL(score_bf16_stream, dim3((unsigned)g), dim3(kStreamWaves * 64), 0, s, a, scores, nvalid, upr);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s);
+    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, false, s);
   }
   const int cap = topk_cap_for(a.k, 256);
   const int lds = kGenWaves * (cap * 8 + 256 * 4);

@@ -159,9 +159,11 @@ __global__ void __launch_bounds__(kSelThreads) sel_final(const int32_t* n_valid,
   const uint64_t* Bl = cached ? sm.bc : Bg;
   uint64_t T = 0;
   if (krem > 0 && (uint32_t)krem < nb) {
-    uint64_t prefix = 0, pmask = 0;
+    // every boundary key shares the top 12 bits (the boundary digit): start below them
+    const uint64_t known = ~0ull << (32 + kSelShift);
+    uint64_t prefix = Bl[0] & known, pmask = known;
     uint32_t kr = (uint32_t)krem;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int shift = 32 + kSelShift - 8; shift >= 0; shift = shift >= 8 ? shift - 8 : (shift > 0 ? 0 : -1)) {
       sm.hist[tid] = 0u;
       __syncthreads();
       for (uint32_t i = tid; i < nb; i += kSelThreads) {
