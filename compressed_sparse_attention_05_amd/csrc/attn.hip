@@ -106,9 +106,11 @@ constexpr int kNK = 32;                // keys per tile
 constexpr int kVT = 40;                // LDS row stride (bf16) of the transposed key slice and of P
 constexpr int kHW = kHG / kNW;         // heads whose softmax a wave finishes (8)
 constexpr float kRescaleLog2 = 8.f;    // reference-max slack before O is rescaled
+constexpr int kSR = 40;                // row stride (floats) of the partial logits: the two lane halves,
+                                       // which write rows 4 apart, land on opposite bank halves
 
 struct AttnSmem {
-  float sred[kNW][kHG][kNK];       // partial logits per wave          64 KiB
+  float sred[kNW][kHG][kSR];       // partial logits per wave          80 KiB
   uint16_t vt[kNW][kDW][kVT];      // key slices, dim-major            40 KiB
   uint16_t pl[kHG][kVT];           // probabilities, bf16              5 KiB
   float alpha[kHG];                // per-head rescale of O this tile

@@ -177,48 +177,95 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
     }
   };
 
+  // Software pipeline over 32-entry column tiles: while the matrix cores run one column tile, the
+  // VALU reduces the heads of the previous one. The source order below is the issue order (each
+  // sched_barrier pins it): every MFMA is followed by the ReLU + weighted sums of two accumulator
+  // element pairs of the other column tile, which run while the MFMA is in flight.
+  //   phase A of tile t: MFMA column 0 of t  |  reduce column 1 of t-1
+  //   phase B of tile t: MFMA column 1 of t  |  reduce column 0 of t
+  //   then offer the 64 scores of tile t-1 (column 0 from phase B of t-1, column 1 from phase A)
+  f32x16 acc0[2], acc1[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) acc1[mt] = f32x16{};
+  float part0 = 0.f;
+  const int lrow = (lane & 31) * kLDK + (lane >> 5) * 8;
+
+  // p4[r & 3] += w_h * ReLU(acc[mt][r]) for both head tiles mt
+  auto reduce_r = [&](float (&p4)[4], const f32x16 (&acc)[2], int r) {
+    p4[r & 3] = fmaf(wr[0][r], relu(acc[0][r]), p4[r & 3]);
+    p4[r & 3] = fmaf(wr[1][r], relu(acc[1][r]), p4[r & 3]);
+  };
+
   if (ntiles > 0) {
     fetch(0);
     put(0);
   }
+  // Every prologue load (q_I, w, first tile) has landed: otherwise the waits for the loads of
+  // q_I / w that the first iteration needs stay in the loop body and stall each tile on the
+  // key fetch that is in flight.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int tile = 0; tile < ntiles; ++tile) {
-    const int cur = tile & 1;
+    const uint16_t* kt = ktile + (tile & 1) * (kNE * kLDK) + lrow;
     if (tile + 1 < ntiles) fetch(tile + 1);
-    if (active && (int64_t)tile * kNE < nv) {
-      const uint16_t* kt = ktile + cur * (kNE * kLDK);
-      // both 32-entry column tiles at once: four independent MFMA chains
-      f32x16 acc[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
+    float sc;
+    {
+      bf16x8 kf0[8], kf1[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kf0[s] = *reinterpret_cast<const bf16x8*>(kt + s * 16);
+      float p4[4] = {0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + (nt * 32 + (lane & 31)) * kLDK + s * 16 + (lane >> 5) * 8);
-          acc[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, acc[nt][0], 0, 0, 0);
-          acc[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, acc[nt][1], 0, 0, 0);
-        }
+        acc0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf0[s], s ? acc0[0] : f32x16{}, 0, 0, 0);
+        asm volatile("" ::"v"(acc0[0]));
+        reduce_r(p4, acc1, 2 * s);
+        __builtin_amdgcn_sched_barrier(0);
+        acc0[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf0[s], s ? acc0[1] : f32x16{}, 0, 0, 0);
+        asm volatile("" ::"v"(acc0[1]));
+        kf1[s] = *reinterpret_cast<const bf16x8*>(kt + 32 * kLDK + s * 16);
+        reduce_r(p4, acc1, 2 * s + 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      float sc[2];
+      const float part1 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      // lanes < 32 end with column 0 of t-1 (both head halves), lanes >= 32 with column 1
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part0), __float_as_uint(part1), false, false);
+      sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        // sum_h w_h * ReLU over the 32 heads held in registers, in four partial sums
-        float p4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) p4[j] = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p4[r & 3] = fmaf(wr[0][r], relu(acc[nt][0][r]), p4[r & 3]);
-          p4[r & 3] = fmaf(wr[1][r], relu(acc[nt][1][r]), p4[r & 3]);
-        }
-        float p = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-        p += __shfl_xor(p, 32, 64);
-        sc[nt] = p;
+      for (int s = 0; s < 8; ++s) {
+        acc1[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf1[s], s ? acc1[0] : f32x16{}, 0, 0, 0);
+        asm volatile("" ::"v"(acc1[0]));
+        reduce_r(p4, acc0, 2 * s);
+        __builtin_amdgcn_sched_barrier(0);
+        acc1[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf1[s], s ? acc1[1] : f32x16{}, 0, 0, 0);
+        asm volatile("" ::"v"(acc1[1]));
+        reduce_r(p4, acc0, 2 * s + 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // lane < 32 takes entry tile*64 + lane (first column tile), lane >= 32 the second tile's
-      const float s = lane < 32 ? sc[0] : sc[1];
-      const int64_t i = (int64_t)tile * kNE + lane;
-      tk.offer(make_cand(s, (uint32_t)i), i < nv);
+      part0 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      asm volatile("" ::"v"(part0));  // keeps the reduction inside phase B
     }
-    if (tile + 1 < ntiles) put(cur ^ 1);
+    if (active && tile > 0) {
+      const int64_t i = (int64_t)(tile - 1) * kNE + lane;
+      tk.offer(make_cand(sc, (uint32_t)i), i < nv);
+    }
+    if (tile + 1 < ntiles) put((tile & 1) ^ 1);
     __syncthreads();
+  }
+  if (ntiles > 0) {
+    float p4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) reduce_r(p4, acc1, r);
+    const float part1 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part0), __float_as_uint(part1), false, false);
+    const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (active) {
+      const int64_t i = (int64_t)(ntiles - 1) * kNE + lane;
+      tk.offer(make_cand(sc, (uint32_t)i), i < nv);
+    }
   }
   if (active) tk.finish(a.out_idx + row * a.k, a.out_score ? a.out_score + row * a.k : nullptr);
 }

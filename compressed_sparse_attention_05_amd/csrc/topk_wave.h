@@ -10,8 +10,9 @@
 // One wave owns one query's candidate buffer (capacity `cap` >= k + 64). Candidates above the
 // running threshold are appended (ballot + prefix popcount, no atomics). When a batch would
 // overflow the buffer, a radix select (8-bit digits, most significant first, histogram in LDS)
-// finds the k-th largest key, the buffer is compacted to the k keys at or above it, and that key
-// becomes the new threshold. At the end the kept entries are sorted ascending by entry index with
+// finds a key at or below the k-th largest that keeps at most cap - 64 keys, the buffer is
+// compacted to the keys at or above it, and the smallest kept key becomes the new threshold. The
+// final selection resolves the exact k-th largest key. At the end the kept entries are sorted ascending by entry index with
 // a bitonic network and written out, padded with -1.
 //
 // Every function must be called by all 64 lanes of the wave with uniform arguments.
@@ -53,17 +54,47 @@ struct WaveTopK {
     thr = 0;
   }
 
-  // Threshold T with exactly k keys >= T among buf[0, cnt) (requires cnt >= k >= 1).
-  __device__ uint64_t kth_threshold() {
+  // A threshold T such that the keys >= T among buf[0, cnt) are at least k and at most `limit`
+  // (limit >= k; limit == k gives the exact k-th largest key). Requires cnt >= k >= 1.
+  //
+  // Radix select over 8-bit digits, most significant first, starting at the highest bit in which
+  // the buffered keys differ (the bits above it are common to all of them). After each digit the
+  // bin holding the k-th key is known; if keeping that whole bin stays within `limit`, its lower
+  // bound is returned without resolving the remaining bits.
+  __device__ uint64_t kth_threshold(int limit) {
     const int lane = lane_id();
-    uint64_t prefix = 0, pmask = 0;
-    uint32_t krem = (uint32_t)k;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    uint64_t mn = ~0ull, mx = 0ull;
+    for (int i = lane; i < cnt; i += 64) {
+      const uint64_t key = buf[i];
+      mn = key < mn ? key : mn;
+      mx = key > mx ? key : mx;
+    }
+    mn = wave_min_u64(mn);
+    mx = wave_max_u64(mx);
+    const uint64_t diff = mn ^ mx;
+    if (diff == 0) return mx;  // a single key
+    int top = 63 - __clzll((long long)diff);
+    uint64_t pmask = top == 63 ? 0ull : ~((2ull << top) - 1ull);
+    uint64_t prefix = mx & pmask;
+    uint32_t krem = (uint32_t)k;       // keys still needed from those matching the prefix
+    uint32_t kept_above = 0;           // keys above the prefix range
+    while (true) {
+      const int shift = top >= 7 ? top - 7 : 0;
+      const uint32_t dmask = (uint32_t)((2ull << (top - shift)) - 1ull);
       for (int b = lane; b < 256; b += 64) hist[b] = 0;
       wave_sync();
-      for (int i = lane; i < cnt; i += 64) {
-        const uint64_t key = buf[i];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+      for (int base = 0; base < cnt; base += 256) {
+        uint64_t kk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = base + j * 64 + lane;
+          kk[j] = i < cnt ? buf[i] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = base + j * 64 + lane;
+          if (i < cnt && (kk[j] & pmask) == prefix) atomicAdd(&hist[(uint32_t)(kk[j] >> shift) & dmask], 1u);
+        }
       }
       wave_sync();
       // lane l owns digits 255-4l .. 252-4l, scanned from the top digit down
@@ -98,36 +129,47 @@ struct WaveTopK {
       inbin = __shfl(inbin, src, 64);
       wave_sync();
       prefix |= (uint64_t)digit << shift;
-      pmask |= 255ull << shift;
+      pmask |= (uint64_t)dmask << shift;
+      // keys >= prefix (its low bits zero): those above the range, above the bin, and the whole bin
+      if (inbin == krem - above || kept_above + above + inbin <= (uint32_t)limit || shift == 0) return prefix;
+      kept_above += above;
       krem -= above;
-      if (inbin == krem) break;  // every key with this prefix is in: prefix (low bits 0) works
+      top = shift - 1;
     }
-    return prefix;
   }
 
-  // Keep the keys >= T (exactly k of them) at the front; the smallest kept becomes thr.
+  // Keep the keys >= T at the front; the smallest kept becomes thr.
   __device__ void compact_to(uint64_t T) {
     const int lane = lane_id();
     int out = 0;
     uint64_t mn = ~0ull;
-    for (int base = 0; base < cnt; base += 64) {
-      const int i = base + lane;
-      const uint64_t key = i < cnt ? buf[i] : 0ull;
-      const bool keep = (i < cnt) && (key >= T);
-      const uint64_t bm = __ballot(keep);
-      wave_sync();
-      if (keep) {
-        buf[out + __popcll(bm & lanemask_lt())] = key;
-        mn = key < mn ? key : mn;
+    for (int base = 0; base < cnt; base += 256) {
+      uint64_t kk[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j * 64 + lane;
+        kk[j] = i < cnt ? buf[i] : 0ull;
       }
-      out += __popcll(bm);
+      wave_sync();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j * 64 + lane;
+        const bool keep = (i < cnt) && (kk[j] >= T);
+        const uint64_t bm = __ballot(keep);
+        if (keep) {
+          buf[out + __popcll(bm & lanemask_lt())] = kk[j];
+          mn = kk[j] < mn ? kk[j] : mn;
+        }
+        out += __popcll(bm);
+      }
       wave_sync();
     }
     cnt = out;
     thr = wave_min_u64(mn);
   }
 
-  __device__ void shrink() { compact_to(kth_threshold()); }
+  // Frees room while streaming: keeps at least k and at most cap - 64 keys.
+  __device__ void shrink() { compact_to(kth_threshold(cap - 64)); }
 
   // Offer one candidate per lane (valid lanes only).
   __device__ void offer(uint64_t key, bool valid) {
@@ -149,7 +191,7 @@ struct WaveTopK {
   // Final top-k, sorted by entry index ascending; out_idx[j] (and out_score[j]) for j < k.
   __device__ void finish(int32_t* out_idx, float* out_score) {
     const int lane = lane_id();
-    if (cnt > k) shrink();
+    if (cnt > k) compact_to(kth_threshold(k));
     // re-key as (index << 32 | score key) so that sorting orders by entry index
     int P = 1;
     while (P < k) P <<= 1;
