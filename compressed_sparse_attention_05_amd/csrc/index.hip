@@ -7,8 +7,9 @@
 // Three paths:
 //  * index_prefill_mfma (bf16, H_I = 64, D_I = 128, many query rows per sequence): a workgroup
 //    holds QW consecutive query rows of one sequence, one per wave, with each wave's q_I (64 heads x
-//    128 dims) resident in VGPRs as MFMA A-fragments. Key tiles of 64 entries stream through
-//    double-buffered LDS and are shared by the QW waves. Per tile a wave runs 32
+//    128 dims) resident in VGPRs as MFMA A-fragments. Key tiles of 64 entries stream through a
+//    three-deep LDS ring (direct global-to-LDS loads) and are shared by the QW waves. Per tile a
+//    wave runs 32
 //    v_mfma_f32_32x32x16_bf16 (heads along the accumulator rows, entries along its columns),
 //    reduces w_h * ReLU over the 32 heads it holds in registers plus one cross-half shuffle, and
 //    offers the 64 scores to its query's streaming top-k buffer in LDS. The T x N score matrix is
@@ -111,15 +112,52 @@ __global__ void __launch_bounds__(kGenWaves * 64) index_generic(IndexArgs a, int
 
 // ---------------------------------------------------------------- fused MFMA prefill path
 
-constexpr int kNE = 64;     // entries per key tile
-constexpr int kLDK = 136;   // LDS row stride of a key row in bf16 (128 + 8: conflict-free b128 reads)
-constexpr int kTileBytes = kNE * kLDK * 2;
+constexpr int kNE = 64;            // entries per key tile
+constexpr int kTileBytes = kNE * 256;  // one tile of bf16 keys (128 dims), no padding
+constexpr int kRing = 3;           // key tiles in flight: the one read and two being loaded
+
+// A key tile in LDS is 16 blocks of 1 KB; block q = (r/16)%2 + 2*(c/4) + 8*(r/32) holds rows
+// r = 32*nt + 16*(q%2) + 0..15 and 16-byte chunks c = 4*((q/2)%4) + 0..3 (dims 8c .. 8c+7) as
+// slot p = r%16 + 16*(c%4). This is the order in which v_mfma_f32_32x32x16_bf16 reads its B
+// fragments: at k-step s a lane l reads row 32*nt + l%32, chunk 2s + l/32, so a lane's 16 reads
+// sit at one per-lane base plus offsets fixed at compile time, and every 16 consecutive lanes hit
+// 16 distinct 16-byte bank groups. Each block is written by one direct-to-LDS load instruction
+// (64 lanes x 16 bytes, lane p to slot p): 16 rows x 64 contiguous bytes of the key array.
+__device__ __forceinline__ int key_block_row(int q, int p) { return 32 * (q >> 3) + 16 * (q & 1) + (p & 15); }
+__device__ __forceinline__ int key_block_chunk(int q, int p) { return 4 * ((q >> 1) & 3) + (p >> 4); }
+__device__ __forceinline__ int key_read_base(int lane) {  // bytes
+  return 16 * ((lane & 15) + 16 * (lane >> 5) + 64 * ((lane >> 4) & 1));
+}
+__device__ __forceinline__ constexpr int key_read_off(int s, int nt) {  // bytes
+  return 512 * (s & 1) + 2048 * (s >> 1) + 8192 * nt;
+}
+
+// Global -> LDS copy of 16 bytes per lane: lane p writes LDS bytes [lds + 16p, lds + 16p + 16).
+// Issued as inline asm so that the compiler does not make later LDS reads wait for it; the
+// caller waits on vmcnt before the barrier that publishes the tile. M0 (the LDS base of the
+// load) is saved and restored around it.
+__device__ __forceinline__ void copy_to_lds16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
+}
 
 template <int QW>
 __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int cap, int t_blocks) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* ktile = reinterpret_cast<uint16_t*>(smem);
-  uint64_t* bufs = reinterpret_cast<uint64_t*>(smem + 2 * kTileBytes);
+  uint64_t* bufs = reinterpret_cast<uint64_t*>(smem + kRing * kTileBytes);
   uint32_t* hists = reinterpret_cast<uint32_t*>(bufs + (int64_t)QW * cap);
 
   const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -154,27 +192,25 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
   tk.init(bufs + (int64_t)wave * cap, hists + wave * 256, cap, a.k);
 
   const uint16_t* kseq = static_cast<const uint16_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
-  const int ntiles = (int)ceil_div(nv_max, kNE);
-  constexpr int kChunks = kNE * 16;               // 16-byte chunks per tile
-  constexpr int kPer = kChunks / (QW * 64);       // chunks per thread
-  uint4 stage[kPer];
-
-  auto fetch = [&](int tile) {
+  const int ntiles = __builtin_amdgcn_readfirstlane((int)ceil_div(nv_max, kNE));  // uniform
+  static_assert(16 % QW == 0, "each wave loads 16 / QW blocks of a key tile");
+  const uint32_t ring_lds = lds_offset(smem);
+  // the 16 / QW blocks this wave loads of each tile: q = j*QW + wave
+  auto load_tile = [&](int tile, int buf) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int c = threadIdx.x + j * QW * 64;
-      const int r = c >> 4, c16 = c & 15;
-      const int64_t e = (int64_t)tile * kNE + r;
-      stage[j] = e < nv_max ? *reinterpret_cast<const uint4*>(kseq + e * 128 + c16 * 8) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 16 / QW; ++j) {
+      const int q = j * QW + wave;
+      int64_t e = (int64_t)tile * kNE + key_block_row(q, lane);
+      e = e < nv_max ? e : nv_max - 1;  // rows past the last visible entry are never offered
+      copy_to_lds16(kseq + e * 128 + key_block_chunk(q, lane) * 8,
+                    __builtin_amdgcn_readfirstlane(ring_lds + buf * kTileBytes + q * 1024));
     }
   };
-  auto put = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int c = threadIdx.x + j * QW * 64;
-      const int r = c >> 4, c16 = c & 15;
-      *reinterpret_cast<uint4*>(ktile + buf * (kNE * kLDK) + r * kLDK + c16 * 8) = stage[j];
-    }
+  // waits for this wave's copies of every tile but the newest `pending` ones (2 instructions each)
+  auto wait_tiles = [&](int pending) {
+    static_assert(16 / QW == 2, "vmcnt immediates assume two copies per wave and tile");
+    if (pending) __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
   };
 
   // Software pipeline over 32-entry column tiles: while the matrix cores run one column tile, the
@@ -188,7 +224,7 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) acc1[mt] = f32x16{};
   float part0 = 0.f;
-  const int lrow = (lane & 31) * kLDK + (lane >> 5) * 8;
+  const int lbase = key_read_base(lane);
 
   // p4[r & 3] += w_h * ReLU(acc[mt][r]) for both head tiles mt
   auto reduce_r = [&](float (&p4)[4], const f32x16 (&acc)[2], int r) {
@@ -196,23 +232,22 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
     p4[r & 3] = fmaf(wr[1][r], relu(acc[1][r]), p4[r & 3]);
   };
 
-  if (ntiles > 0) {
-    fetch(0);
-    put(0);
-  }
-  // Every prologue load (q_I, w, first tile) has landed: otherwise the waits for the loads of
-  // q_I / w that the first iteration needs stay in the loop body and stall each tile on the
-  // key fetch that is in flight.
+  // Every prologue load (q_I, w) has landed before the loop, so that no wait for them is left in
+  // the loop body.
   __builtin_amdgcn_s_waitcnt(0);
+  if (ntiles > 0) load_tile(0, 0);
+  if (ntiles > 1) load_tile(1, 1);
+  wait_tiles(ntiles > 1);
   __syncthreads();
+  int cur = 0;  // ring slot of the tile being read
   for (int tile = 0; tile < ntiles; ++tile) {
-    const uint16_t* kt = ktile + (tile & 1) * (kNE * kLDK) + lrow;
-    if (tile + 1 < ntiles) fetch(tile + 1);
+    const uint8_t* kt = smem + cur * kTileBytes + lbase;
+    if (tile + 2 < ntiles) load_tile(tile + 2, cur == 0 ? 2 : cur - 1);
     float sc;
     {
       bf16x8 kf0[8], kf1[8];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) kf0[s] = *reinterpret_cast<const bf16x8*>(kt + s * 16);
+      for (int s = 0; s < 8; ++s) kf0[s] = *reinterpret_cast<const bf16x8*>(kt + key_read_off(s, 0));
       float p4[4] = {0.f, 0.f, 0.f, 0.f};
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -223,7 +258,7 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
         __builtin_amdgcn_sched_barrier(0);
         acc0[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf0[s], s ? acc0[1] : f32x16{}, 0, 0, 0);
         asm volatile("" ::"v"(acc0[1]));
-        kf1[s] = *reinterpret_cast<const bf16x8*>(kt + 32 * kLDK + s * 16);
+        kf1[s] = *reinterpret_cast<const bf16x8*>(kt + key_read_off(s, 1));
         reduce_r(p4, acc1, 2 * s + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -252,8 +287,9 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
       const int64_t i = (int64_t)(tile - 1) * kNE + lane;
       tk.offer(make_cand(sc, (uint32_t)i), i < nv);
     }
-    if (tile + 1 < ntiles) put((tile & 1) ^ 1);
+    if (tile + 1 < ntiles) wait_tiles(tile + 2 < ntiles);  // tile + 1 has landed
     __syncthreads();
+    cur = cur == kRing - 1 ? 0 : cur + 1;
   }
   if (ntiles > 0) {
     float p4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -272,7 +308,7 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
 
 constexpr int kPrefillQW = 8;
 
-int prefill_lds(int cap) { return 2 * kTileBytes + kPrefillQW * (cap * 8 + 256 * 4); }
+int prefill_lds(int cap) { return kRing * kTileBytes + kPrefillQW * (cap * 8 + 256 * 4); }
 
 // ---------------------------------------------------------------- decode scores
 
