@@ -99,286 +99,290 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
 
 // ---------------------------------------------------------------- MFMA (bf16, D = 512)
 
-constexpr int kHG = 64;                // heads per workgroup
-constexpr int kNW = 8;                 // waves per workgroup; each owns 512/kNW dims
-constexpr int kDW = 512 / kNW;         // dims per wave (64)
-constexpr int kNK = 32;                // keys per tile
-constexpr int kVT = 40;                // LDS row stride (bf16) of the transposed key slice and of P
-constexpr int kHW = kHG / kNW;         // heads whose softmax a wave finishes (8)
-constexpr float kRescaleLog2 = 8.f;    // reference-max slack before O is rescaled
-constexpr int kSR = 40;                // row stride (floats) of the partial logits: the two lane halves,
-                                       // which write rows 4 apart, land on opposite bank halves
+constexpr int kHPW = 16;              // query heads per wave
+constexpr int kNK = 32;               // keys per tile
+constexpr int kKNS = 536;             // LDS row stride (bf16) of a key row, 1072 B: 16 consecutive
+                                      // rows start in 16 distinct 16-byte bank groups, and 4
+                                      // consecutive rows keep 32-byte reads apart
+constexpr int kRingA = 3;             // key tiles in LDS: the one read and two being loaded
+constexpr float kRescaleLog2 = 8.f;   // reference-max slack before O is rescaled
 
 struct AttnSmem {
-  float sred[kNW][kHG][kSR];       // partial logits per wave          80 KiB
-  uint16_t vt[kNW][kDW][kVT];      // key slices, dim-major            40 KiB
-  uint16_t pl[kHG][kVT];           // probabilities, bf16              5 KiB
-  float alpha[kHG];                // per-head rescale of O this tile
-  float lsum[kHG];                 // per-head running denominators
-  float mrun[kHG];                 // per-head running maxima (log2 units)
-  int32_t rescale[2];              // some head rescaled O in this tile (by tile parity)
-  int32_t keys[1];                 // gathered key list (entry ids >= 0, window rows as -(r+1))
+  uint16_t kn[kRingA][kNK][kKNS];   // 3 x 34304 B
+  int32_t wcnt[16];                 // per-wave counts while the key list is compacted
+  int32_t keys[1];                  // gathered key list (entry ids >= 0, window rows as -(r+1))
 };
 
-// Split-KV bookkeeping: in the decode regime (fewer than 8 query rows per sequence) the key list
-// of a row is cut into fixed ranges of split_keys keys, one workgroup each; every workgroup leaves
-// (running max in log2 units, running sum, O / sum in bf16) and attn_combine merges the splits in a
-// fixed order. The plan depends only on T, k and the window, never on the batch size, so a row's
-// result is the same alone or inside any batch.
+// Split-KV bookkeeping: with fewer than 8 query rows per sequence the key list of a row is cut into
+// fixed ranges of split_keys keys, one workgroup each; every workgroup leaves (running max in log2
+// units, running sum, O / sum in bf16) and attn_combine merges the splits in a fixed order. The plan
+// depends only on T, k and the window, never on the batch size, so a row's result is the same alone
+// or inside any batch.
 struct AttnSplit {
   int n_splits, split_keys;
-  uint16_t* part_o;  // [R*G*S, 64, 512] bf16, each split's output normalised by its own sum
-  float* part_ml;    // [R*G*S, 64, 2]: running max (log2 units), running sum
+  uint16_t* part_o;  // [R*S, H, 512] bf16, each split's output normalised by its own sum
+  float* part_ml;    // [R*S, H, 2]: running max (log2 units), running sum
 };
 
-// This wave's slice of one gathered key as B-fragments: key kj, dims wave*64 + s*16 + (lane/32)*8.
-__device__ __forceinline__ void load_slice(uint4 (&ku)[kDW / 16], const int32_t* keys, int kj, int kend,
-                                           const uint16_t* ent, const uint16_t* raw, int64_t raw_ld, int wave,
-                                           int lane) {
-  const bool kok = kj < kend;
-  const uint16_t* krow = nullptr;
-  if (kok) {
-    const int32_t id = keys[kj];
-    krow = id >= 0 ? ent + (int64_t)id * 512 : raw + (int64_t)(-id - 1) * raw_ld;
-  }
-#pragma unroll
-  for (int s = 0; s < kDW / 16; ++s)
-    ku[s] = kok ? *reinterpret_cast<const uint4*>(krow + wave * kDW + s * 16 + (lane >> 5) * 8) : make_uint4(0, 0, 0, 0);
-}
-
-template <int OT>
-__global__ void __launch_bounds__(kNW * 64) attn_mfma(AttnArgs a, int n_groups, AttnSplit sp) {
+// One workgroup per (query row, split) with all H = 16 * NW heads; wave w owns heads 16w .. 16w+15
+// whole, so logits, softmax and O of a head never leave its wave:
+//   S^T[32 keys x 16 heads] = K[32 x 512] Q_w^T   (v_mfma_f32_16x16x32_bf16, K rows from LDS, Q in
+//                                                   VGPRs)
+//   online softmax over the keys of each head: lane l holds head l%16 and keys 4g .. 4g+3,
+//   16+4g .. 16+4g+3 (g = l/16), two cross-lane steps
+//   O_w^T[512 x 16] += V^T[512 x 32] P^T          (V^T read from the same key rows with the
+//                                                   transposing ds_read_b64_tr_b16, P^T in VGPRs)
+// Key rows are gathered by direct global-to-LDS loads (one 1 KiB row per instruction) into a
+// three-deep ring, two tiles ahead of the math; one barrier per tile.
+template <int NW, int OT>
+__global__ void __launch_bounds__(NW * 64) attn_mfma(AttnArgs a, AttnSplit sp) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
+  constexpr int kThreads = NW * 64;
+  constexpr int kRowsPerWave = kNK / NW;  // key rows one wave loads per tile
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int split = (int)(blockIdx.x % sp.n_splits);
-  const int64_t rg = blockIdx.x / sp.n_splits;
-  const int64_t row = rg / n_groups;
-  const int hg = (int)(rg % n_groups);
+  const int64_t row = blockIdx.x / sp.n_splits;
   const int b = (int)(row / a.T), t = (int)(row % a.T);
   const int64_t p = a.q_pos0 + t;
   const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
 
-  // ---- key list: valid selected entries, then the window rows
-  if (wave == 0) {
-    int nsel = 0;
+  // ---- key list: valid selected entries, then the window rows. All threads load their indices in
+  // one burst (one memory latency, not one per 64 indices) and the waves compact them in order.
+  {
     const int32_t* idx = a.idx + row * a.k;
-    for (int base = 0; base < a.k; base += 64) {
-      const int j = base + lane;
-      const int32_t e = j < a.k ? idx[j] : -1;
-      const bool ok = e >= 0 && e < a.n_cap;
-      const uint64_t bm = __ballot(ok);
-      if (ok) sm.keys[nsel + __popcll(bm & lanemask_lt())] = e;
-      nsel += __popcll(bm);
+    int nsel = 0;
+    for (int base = 0; base < a.k; base += 4 * kThreads) {
+      int32_t e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = base + r * kThreads + (int)threadIdx.x;
+        e[r] = j < a.k ? idx[j] : -1;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (base + r * kThreads >= a.k) break;
+        const bool ok = e[r] >= 0 && e[r] < a.n_cap;
+        const uint64_t bm = __ballot(ok);
+        if (lane == 0) sm.wcnt[wave] = __popcll(bm);
+        __syncthreads();
+        int off = nsel, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int c = sm.wcnt[w];
+          off += w < wave ? c : 0;
+          tot += c;
+        }
+        if (ok) sm.keys[off + __popcll(bm & lanemask_lt())] = e[r];
+        nsel += tot;
+        __syncthreads();
+      }
     }
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
-    for (int j = lane; j < nwin; j += 64) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
-    if (lane == 0) {
-      sm.keys[a.k + a.W] = nsel + nwin;
-      sm.rescale[0] = 0;
-    }
+    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
+    if (threadIdx.x == 0) sm.keys[a.k + a.W] = nsel + nwin;
   }
   __syncthreads();
   const int nkeys = sm.keys[a.k + a.W];
   const int kbeg = split * sp.split_keys;
   const int kend = kbeg + sp.split_keys < nkeys ? kbeg + sp.split_keys : nkeys;
+  const int ntiles = __builtin_amdgcn_readfirstlane(kend > kbeg ? (kend - kbeg + kNK - 1) / kNK : 0);
 
-  // ---- q slice as A-fragments: head hg*64 + mt*32 + lane%32, dims wave*64 + s*16 + (lane/32)*8
-  const float scale = a.scale * 1.4426950408889634f;  // logits in log2 units
+  // ---- Q_w^T as B-fragments: head 16w + lane%16, dims s*32 + (lane/16)*8 .. +7
+  const int head = wave * kHPW + (lane & 15);
+  const int g = lane >> 4;
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld +
-                         (int64_t)hg * kHG * 512 + wave * kDW;
-  bf16x8 qf[2][kDW / 16];
+                         (int64_t)head * 512 + g * 8;
+  bf16x8 qf[16];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int s = 0; s < kDW / 16; ++s)
-      qf[mt][s] = *reinterpret_cast<const bf16x8*>(qrow + (int64_t)(mt * 32 + (lane & 31)) * 512 + s * 16 + (lane >> 5) * 8);
+  for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 32);
 
-  f32x16 o[2][kDW / 32];
+  f32x4 o[32];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < kDW / 32; ++nt) o[mt][nt] = f32x16{};
-
-  // softmax ownership: wave w finishes heads w*8 + lane/8, keys (lane%8)*4 .. +3
-  const int sh = wave * kHW + (lane >> 3);
-  const int sk0 = (lane & 7) * 4;
+  for (int db = 0; db < 32; ++db) o[db] = f32x4{};
+  const float scale = a.scale * 1.4426950408889634f;  // logits in log2 units
   float m_run = -INFINITY, l_run = 0.f;
   if (a.sink && sp.n_splits == 1) {
-    m_run = a.sink[hg * kHG + sh] * 1.4426950408889634f;
+    m_run = a.sink[head] * 1.4426950408889634f;
     l_run = 1.f;
   }
 
+  // ---- key rows: row r of tile `tile` into ring slot `buf`; keys past the split's end repeat its
+  // last key (finite values; their logits are masked)
   const uint16_t* ent = static_cast<const uint16_t*>(a.entries) + (int64_t)b * a.entries_seq_stride;
   const uint16_t* raw = static_cast<const uint16_t*>(a.raw) + (int64_t)b * a.raw_seq_stride;
-  const int ntiles = kend > kbeg ? (kend - kbeg + kNK - 1) / kNK : 0;
-  // Gathered key slices cycle through three register sets: the loads of tile i+3 are issued as soon
-  // as tile i has been consumed, so three tiles of HBM/L2 latency are in flight behind the math.
-  uint4 kbuf[3][kDW / 16];
-  auto tile_step = [&](uint4 (&ku)[kDW / 16], const int tile) {
-    const int k0 = kbeg + tile * kNK;
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  const uint32_t ring = lds_offset(&sm.kn[0][0][0]);
+  auto load_tile = [&](int tile, int buf) {
 #pragma unroll
-    for (int s = 0; s < kDW / 16; ++s) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, ku[s]);
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, sacc[1], 0, 0, 0);
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int r = j * NW + wave;
+      int kj = kbeg + tile * kNK + r;
+      kj = kj < kend ? kj : kend - 1;
+      const int32_t id = __builtin_amdgcn_readfirstlane(sm.keys[kj]);
+      const uint16_t* krow = id >= 0 ? ent + (int64_t)id * 512 : raw + (int64_t)(-id - 1) * a.raw_ld;
+      copy_to_lds16(krow + lane * 8,
+                    __builtin_amdgcn_readfirstlane(ring + (uint32_t)((buf * kNK + r) * kKNS * 2)));
     }
-    // partial logits -> LDS: head mt*32 + (r/4)*8 + (lane/32)*4 + r%4, key lane%32
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sm.sred[wave][mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)][lane & 31] = sacc[mt][r];
-    // key slice, transposed: vt[dim][key]
-#pragma unroll
-    for (int s = 0; s < kDW / 16; ++s) {
-      const uint32_t w4[4] = {ku[s].x, ku[s].y, ku[s].z, ku[s].w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        sm.vt[wave][s * 16 + (lane >> 5) * 8 + j][lane & 31] = (uint16_t)(w4[j >> 1] >> ((j & 1) * 16));
-    }
-    // this register set is free again: start gathering the tile three ahead into it
-    if (tile + 3 < ntiles) load_slice(ku, sm.keys, k0 + 3 * kNK + (lane & 31), kend, ent, raw, a.raw_ld, wave, lane);
-    __syncthreads();
+  };
+  // this wave's copies of every tile but the newest `pending` ones have landed
+  auto wait_tiles = [&](bool pending) {
+    if (pending) CSA_WAIT_VMCNT(kRowsPerWave);
+    else CSA_WAIT_VMCNT(0);
+  };
 
-    // ---- online softmax of kHW heads x 32 keys per wave
-    {
-      float sv[4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = sk0 + j;
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < kNW; ++w) v += sm.sred[w][sh][key];
-        v = (k0 + key < kend) ? v * scale : -INFINITY;
-        sv[j] = v;
-        tmax = fmaxf(tmax, v);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 4, 64));
-      // lazy rescaling: the reference max moves only when a logit exceeds it by more than 2^8, so
-      // weights stay below 256 and O is rescaled in few tiles
-      const float m_new = tmax > m_run + kRescaleLog2 ? tmax : m_run;
-      const float al = m_new == m_run ? 1.f : exp2f(m_run - m_new);
-      float psum = 0.f;
-      uint16_t pb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint16_t h16 = f2bf(exp2f(sv[j] - m_new));
-        pb[j] = h16;
-        psum += bf2f(h16);  // the denominator sums the same rounded weights P V uses
-      }
-      psum += __shfl_xor(psum, 1, 64);
-      psum += __shfl_xor(psum, 2, 64);
-      psum += __shfl_xor(psum, 4, 64);
-      l_run = l_run * al + psum;
-      m_run = m_new;
-      *reinterpret_cast<uint2*>(&sm.pl[sh][sk0]) =
-          make_uint2(pb[0] | ((uint32_t)pb[1] << 16), pb[2] | ((uint32_t)pb[3] << 16));
-      if ((lane & 7) == 0) {
-        sm.alpha[sh] = al;
-        sm.lsum[sh] = l_run;
-        sm.mrun[sh] = m_run;
-      }
-      // the flag of this tile's parity was cleared a tile ago; clear the other one for the next tile
-      if (al != 1.f) sm.rescale[tile & 1] = 1;
-      if (threadIdx.x == 0) sm.rescale[(tile + 1) & 1] = 0;
-    }
-    __syncthreads();
-
-    // ---- O = alpha * O + P V over this wave's dims
-    if (sm.rescale[tile & 1]) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float al = sm.alpha[mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
-#pragma unroll
-          for (int nt = 0; nt < kDW / 32; ++nt) o[mt][nt][r] *= al;
-        }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      bf16x8 pf[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        pf[ks] = *reinterpret_cast<const bf16x8*>(&sm.pl[mt * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8]);
-#pragma unroll
-      for (int nt = 0; nt < kDW / 32; ++nt) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sm.vt[wave][nt * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8]);
-          o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[ks], vf, o[mt][nt], 0, 0, 0);
-        }
-      }
-    }
-    };
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (j < ntiles) load_slice(kbuf[j], sm.keys, kbeg + j * kNK + (lane & 31), kend, ent, raw, a.raw_ld, wave, lane);
-  for (int tile = 0; tile < ntiles; tile += 3) {
-    tile_step(kbuf[0], tile);
-    if (tile + 1 < ntiles) tile_step(kbuf[1], tile + 1);
-    if (tile + 2 < ntiles) tile_step(kbuf[2], tile + 2);
-  }
-  if (ntiles == 0 && (lane & 7) == 0) {
-    sm.lsum[sh] = l_run;
-    sm.mrun[sh] = m_run;
-  }
+  // q has landed before the loop, so that no wait for it stays in the loop body
+  __builtin_amdgcn_s_waitcnt(0);
+  if (ntiles > 0) load_tile(0, 0);
+  if (ntiles > 1) load_tile(1, 1);
+  wait_tiles(ntiles > 1);
   __syncthreads();
+  // per-lane LDS byte offsets: S^T A-fragments (row lane%16, dims g*8 ..) and the transposing reads
+  // of V^T (rows 4g + (lane%16)/4 and 16 + 4g + (lane%16)/4, dims 4*(lane%4) ..)
+  const uint32_t qk_off = (uint32_t)(((lane & 15) * kKNS + g * 8) * 2);
+  const uint32_t pv_off = (uint32_t)(((4 * g + ((lane & 15) >> 2)) * kKNS + 4 * (lane & 3)) * 2);
+  int cur = 0;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const uint8_t* kt = reinterpret_cast<const uint8_t*>(&sm.kn[cur][0][0]);
+    if (tile + 2 < ntiles) load_tile(tile + 2, cur == 0 ? 2 : cur - 1);
+    // S^T: rows = keys 16kb + lane%16 of the tile, cols = heads. Fragments in groups of 4, the next
+    // group read while the current one multiplies.
+    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    {
+      bf16x8 kf[2][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kf[0][i] = *reinterpret_cast<const bf16x8*>(kt + qk_off + (i >> 1) * 16 * kKNS * 2 + (i & 1) * 64);
+#pragma unroll
+      for (int sg = 0; sg < 8; ++sg) {
+        if (sg < 7) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            kf[(sg + 1) & 1][i] = *reinterpret_cast<const bf16x8*>(kt + qk_off + (i >> 1) * 16 * kKNS * 2 +
+                                                                    ((sg + 1) * 2 + (i & 1)) * 64);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sacc[i >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[sg & 1][i], qf[sg * 2 + (i & 1)], sacc[i >> 1], 0, 0, 0);
+        asm volatile("" ::"v"(sacc[0]), "v"(sacc[1]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // online softmax: this lane holds head `head`, keys 16kb + 4g + r
+    const int k0 = kbeg + tile * kNK;
+    float v[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = (k0 + kb * 16 + 4 * g + r < kend) ? sacc[kb][r] * scale : -INFINITY;
+        v[kb][r] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // lazy rescaling: the reference max moves only when a logit exceeds it by more than 2^8, so
+    // weights stay below 256 and O is rescaled in few tiles
+    const float m_new = tmax > m_run + kRescaleLog2 ? tmax : m_run;
+    const float al = m_new == m_run ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+    uint32_t pw[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint16_t h0 = f2bf(exp2f(v[m >> 1][(m & 1) * 2] - m_new));
+      const uint16_t h1 = f2bf(exp2f(v[m >> 1][(m & 1) * 2 + 1] - m_new));
+      psum += bf2f(h0) + bf2f(h1);  // the denominator sums the same rounded weights P V uses
+      pw[m] = h0 | ((uint32_t)h1 << 16);
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * al + psum;
+    m_run = m_new;
+    if (__ballot(al != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 32; ++db) o[db] *= al;
+    }
+    // P^T B-fragment: k index j <-> key 4g + j (j < 4) and 16 + 4g + j - 4 (j >= 4)
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    // O^T[dims 16db + lane%16 (rows) x heads] += V^T P^T; each V^T fragment is two transposing
+    // reads: lane 16g + i gets dim 16db + i of keys 4g .. 4g+3, then of keys 16+4g .. 16+4g+3
+    {
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+      const uint32_t vb = ring + (uint32_t)(cur * kNK * kKNS * 2) + pv_off;
+      auto vread = [&](int db, int half) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(uintptr_t)(vb + (uint32_t)(half * 16 * kKNS * 2 + db * 32)));
+      };
+      v4i16 vf[2][4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vf[0][i][0] = vread(i, 0);
+        vf[0][i][1] = vread(i, 1);
+      }
+#pragma unroll
+      for (int dg = 0; dg < 8; ++dg) {
+        if (dg < 7) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vf[(dg + 1) & 1][i][0] = vread((dg + 1) * 4 + i, 0);
+            vf[(dg + 1) & 1][i][1] = vread((dg + 1) * 4 + i, 1);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4i16 lo = vf[dg & 1][i][0], hi = vf[dg & 1][i][1];
+          const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dg * 4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[dg * 4 + i], 0, 0, 0);
+        }
+        asm volatile("" ::"v"(o[dg * 4]), "v"(o[dg * 4 + 1]), "v"(o[dg * 4 + 2]), "v"(o[dg * 4 + 3]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (tile + 1 < ntiles) wait_tiles(tile + 2 < ntiles);  // tile + 1 has landed
+    __syncthreads();
+    cur = cur == kRingA - 1 ? 0 : cur + 1;
+  }
+
+  // ---- output: lane holds head `head`, dims db*16 + 4g + r
   if (sp.n_splits == 1) {
-    // ---- normalise and store: head hg*64 + row index, dim wave*64 + nt*32 + lane%32
-    const int64_t obase = (row * a.H + (int64_t)hg * kHG) * 512 + wave * kDW;
+    const float inv = 1.f / l_run;
+    const int64_t ob = (row * a.H + head) * 512 + 4 * g;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int db = 0; db < 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int h = mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const float inv = 1.f / sm.lsum[h];
-#pragma unroll
-        for (int nt = 0; nt < kDW / 32; ++nt)
-          store_elem<OT>(a.out, obase + (int64_t)h * 512 + nt * 32 + (lane & 31), o[mt][nt][r] * inv);
-      }
+      for (int r = 0; r < 4; ++r) store_elem<OT>(a.out, ob + db * 16 + r, o[db][r] * inv);
   } else {
-    // ---- this split's partial for attn_combine: O / l in bf16, (m, l) in fp32
-    const int64_t pidx = rg * sp.n_splits + split;
-    uint16_t* po = sp.part_o + pidx * (kHG * 512) + wave * kDW;
+    const int64_t pidx = row * sp.n_splits + split;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* po = sp.part_o + (pidx * a.H + head) * 512 + 4 * g;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int h = mt * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const float l = sm.lsum[h];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-        for (int nt = 0; nt < kDW / 32; ++nt) po[h * 512 + nt * 32 + (lane & 31)] = f2bf(o[mt][nt][r] * inv);
-      }
-    if (threadIdx.x < kHG) {
-      sp.part_ml[(pidx * kHG + threadIdx.x) * 2] = sm.mrun[threadIdx.x];
-      sp.part_ml[(pidx * kHG + threadIdx.x) * 2 + 1] = sm.lsum[threadIdx.x];
+    for (int db = 0; db < 32; ++db) {
+      const uint32_t w0 = f2bf(o[db][0] * inv) | ((uint32_t)f2bf(o[db][1] * inv) << 16);
+      const uint32_t w1 = f2bf(o[db][2] * inv) | ((uint32_t)f2bf(o[db][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(po + db * 16) = make_uint2(w0, w1);
+    }
+    if (g == 0) {
+      sp.part_ml[(pidx * a.H + head) * 2] = m_run;
+      sp.part_ml[(pidx * a.H + head) * 2 + 1] = l_run;
     }
   }
 }
 
 // Merges the n_splits partials of every (row, head): M = max m_s, L = sum l_s 2^(m_s - M) (plus the
-// sink), O = sum l_s 2^(m_s - M) (O_s / l_s) / L, splits taken in order. One workgroup per
-// (row, 4 heads).
+// sink), O = sum l_s 2^(m_s - M) (O_s / l_s) / L, splits taken in order. One wave per (row, head),
+// four per workgroup.
 template <int OT>
-__global__ void __launch_bounds__(256) attn_combine(AttnArgs a, int n_groups, AttnSplit sp) {
+__global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   const int64_t R = (int64_t)a.B * a.T;
   const int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
   if (gid >= R * a.H) return;
   const int64_t row = gid / a.H;
   const int h = (int)(gid % a.H);
-  const int hg = h / kHG, hl = h % kHG;
-  const int64_t rg = row * n_groups + hg;
   const int lane = lane_id();
   float M = -INFINITY;
   for (int s = 0; s < sp.n_splits; ++s) {
-    const float* ml = sp.part_ml + ((rg * sp.n_splits + s) * kHG + hl) * 2;
+    const float* ml = sp.part_ml + ((row * sp.n_splits + s) * a.H + h) * 2;
     if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
   }
   float sink2 = -INFINITY;
@@ -388,16 +392,26 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, int n_groups, At
   }
   float L = a.sink ? exp2f(sink2 - M) : 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < sp.n_splits; ++s) {
-    const int64_t pidx = rg * sp.n_splits + s;
-    const float* ml = sp.part_ml + (pidx * kHG + hl) * 2;
-    if (!(ml[1] > 0.f)) continue;
-    const float wgt = ml[1] * exp2f(ml[0] - M);
-    L += wgt;
-    const uint4 u = *reinterpret_cast<const uint4*>(sp.part_o + pidx * (kHG * 512) + hl * 512 + lane * 8);
-    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+  // splits in groups of four, every load of a group issued before any is used; a split without
+  // keys has l = 0 and a zero partial, so it adds nothing
+  for (int s0 = 0; s0 < sp.n_splits; s0 += 4) {
+    uint4 u[4];
+    float wgt[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = fmaf(__uint_as_float((w4[j >> 1] >> ((j & 1) * 16)) << 16), wgt, acc[j]);
+    for (int j = 0; j < 4; ++j) {
+      const int s = s0 + j < sp.n_splits ? s0 + j : sp.n_splits - 1;
+      const int64_t pidx = row * sp.n_splits + s;
+      const float* ml = sp.part_ml + (pidx * a.H + h) * 2;
+      wgt[j] = (s0 + j < sp.n_splits && ml[1] > 0.f) ? ml[1] * exp2f(ml[0] - M) : 0.f;
+      u[j] = *reinterpret_cast<const uint4*>(sp.part_o + (pidx * a.H + h) * 512 + lane * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      L += wgt[j];
+      const uint32_t w4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(__uint_as_float((w4[i >> 1] >> ((i & 1) * 16)) << 16), wgt[j], acc[i]);
+    }
   }
   const float inv = 1.f / L;
   const int64_t ob = (row * a.H + h) * 512 + lane * 8;
@@ -408,13 +422,13 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, int n_groups, At
 int attn_mfma_lds(const AttnArgs& a) { return (int)(sizeof(AttnSmem) + (size_t)(a.k + a.W + 1) * 4); }
 
 bool use_attn_mfma(const AttnArgs& a) {
-  return a.in_dtype == CSA_BF16 && a.D == 512 && a.H % kHG == 0 && a.raw_ld % 8 == 0 && a.q_ld % 8 == 0 &&
-         a.q_seq_stride % 8 == 0 && a.entries_seq_stride % 8 == 0 && a.raw_seq_stride % 8 == 0;
+  return a.in_dtype == CSA_BF16 && a.D == 512 && (a.H == 64 || a.H == 128) && a.raw_ld % 4 == 0 &&
+         a.q_ld % 8 == 0 && a.q_seq_stride % 8 == 0 && a.entries_seq_stride % 4 == 0 && a.raw_seq_stride % 4 == 0 &&
+         attn_mfma_lds(a) <= kMaxLds;
 }
 
-
 constexpr int kDecodeRows = 8;     // fewer query rows per sequence than this: decode regime
-constexpr int kSplitKeys = 256;    // keys per split in the decode regime
+constexpr int kSplitKeys = 128;    // keys per split in the decode regime
 
 AttnSplit plan_split(const AttnArgs& a) {
   AttnSplit sp{1, a.k + a.W, nullptr, nullptr};
@@ -429,13 +443,22 @@ AttnSplit plan_split(const AttnArgs& a) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+template <int NW, int OT>
+hipError_t launch_mfma(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
+  const int lds = attn_mfma_lds(a);
+  hipError_t e;
+  if ((e = allow_lds((const void*)attn_mfma<NW, OT>, lds)) != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_mfma<NW, OT>), dim3((unsigned)(R * sp.n_splits)), dim3(NW * 64), lds, s, a, sp);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t attn_workspace(const AttnArgs& a) {
   const AttnSplit sp = plan_split(a);
   if (sp.n_splits <= 1) return 0;
-  const int64_t parts = (int64_t)a.B * a.T * (a.H / kHG) * sp.n_splits;
-  return align256((size_t)parts * kHG * 512 * 2) + align256((size_t)parts * kHG * 2 * 4);
+  const int64_t parts = (int64_t)a.B * a.T * sp.n_splits;
+  return align256((size_t)parts * a.H * 512 * 2) + align256((size_t)parts * a.H * 2 * 4);
 }
 
 hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -443,30 +466,24 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
   if (R == 0) return hipSuccess;
   hipError_t e;
   if (use_attn_mfma(a)) {
-    const int ng = a.H / kHG;
-    const int lds = attn_mfma_lds(a);
     AttnSplit sp = plan_split(a);
     if (sp.n_splits > 1) {
       if (ws == nullptr || ws_bytes < attn_workspace(a)) return hipErrorInvalidValue;
-      const int64_t parts = R * ng * sp.n_splits;
+      const int64_t parts = R * sp.n_splits;
       sp.part_o = static_cast<uint16_t*>(ws);
-      sp.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256((size_t)parts * kHG * 512 * 2));
+      sp.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256((size_t)parts * a.H * 512 * 2));
     }
-    const dim3 grid((unsigned)(R * ng * sp.n_splits));
-    if (a.out_dtype == CSA_BF16) {
-      if ((e = allow_lds((const void*)attn_mfma<CSA_BF16>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(attn_mfma<CSA_BF16>, grid, dim3(kNW * 64), lds, s, a, ng, sp);
-    } else {
-      if ((e = allow_lds((const void*)attn_mfma<CSA_F32>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(attn_mfma<CSA_F32>, grid, dim3(kNW * 64), lds, s, a, ng, sp);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.H == 128)
+      e = a.out_dtype == CSA_BF16 ? launch_mfma<8, CSA_BF16>(a, sp, R, s) : launch_mfma<8, CSA_F32>(a, sp, R, s);
+    else
+      e = a.out_dtype == CSA_BF16 ? launch_mfma<4, CSA_BF16>(a, sp, R, s) : launch_mfma<4, CSA_F32>(a, sp, R, s);
+    if (e != hipSuccess) return e;
     if (sp.n_splits > 1) {
       const dim3 cg((unsigned)ceil_div(R * a.H, 4));
       if (a.out_dtype == CSA_BF16)
-        hipLaunchKernelGGL(attn_combine<CSA_BF16>, cg, dim3(256), 0, s, a, ng, sp);
+        hipLaunchKernelGGL(attn_combine<CSA_BF16>, cg, dim3(256), 0, s, a, sp);
       else
-        hipLaunchKernelGGL(attn_combine<CSA_F32>, cg, dim3(256), 0, s, a, ng, sp);
+        hipLaunchKernelGGL(attn_combine<CSA_F32>, cg, dim3(256), 0, s, a, sp);
       return hipGetLastError();
     }
     return hipSuccess;

@@ -113,6 +113,33 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// ------------------------------------------------------------------ direct global -> LDS loads
+
+// Global -> LDS copy of 16 bytes per lane: lane p writes LDS bytes [lds + 16p, lds + 16p + 16).
+// Issued as inline asm so that the compiler does not make later LDS reads wait for it; the
+// caller waits on vmcnt before the barrier that publishes the tile. M0 (the LDS base of the
+// load) is saved and restored around it.
+__device__ __forceinline__ void copy_to_lds16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
+}
+
+// s_waitcnt with only vmcnt = n (n < 16), expcnt and lgkmcnt left free
+#define CSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // n_vis(p) = min(floor((p+1)/m), n_cap): entries whose block is complete at position p.

@@ -132,27 +132,6 @@ __device__ __forceinline__ constexpr int key_read_off(int s, int nt) {  // bytes
   return 512 * (s & 1) + 2048 * (s >> 1) + 8192 * nt;
 }
 
-// Global -> LDS copy of 16 bytes per lane: lane p writes LDS bytes [lds + 16p, lds + 16p + 16).
-// Issued as inline asm so that the compiler does not make later LDS reads wait for it; the
-// caller waits on vmcnt before the barrier that publishes the tile. M0 (the LDS base of the
-// load) is saved and restored around it.
-__device__ __forceinline__ void copy_to_lds16(const void* src, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
-}
 
 template <int QW>
 __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int cap, int t_blocks) {
@@ -209,8 +188,8 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
   // waits for this wave's copies of every tile but the newest `pending` ones (2 instructions each)
   auto wait_tiles = [&](int pending) {
     static_assert(16 / QW == 2, "vmcnt immediates assume two copies per wave and tile");
-    if (pending) __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
+    if (pending) CSA_WAIT_VMCNT(2);
+    else CSA_WAIT_VMCNT(0);
   };
 
   // Software pipeline over 32-entry column tiles: while the matrix cores run one column tile, the
@@ -482,7 +461,6 @@ int stream_grid() {
   return 2 * cus;
 }
 
-constexpr int kMaxLds = 160 * 1024;
 
 bool use_prefill_mfma(const IndexArgs& a) {
   return a.idx_dtype == CSA_BF16 && a.H_I == 64 && a.D_I == 128 && a.T >= kPrefillQW &&

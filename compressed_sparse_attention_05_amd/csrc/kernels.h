@@ -96,6 +96,8 @@ hipError_t launch_copy_rows(int B, int rows, int cols, int esize, const void* sr
                             int64_t src_seq, void* dst, int64_t dst_ld, int64_t dst_seq,
                             hipStream_t s);
 
+constexpr int kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
+
 // Sets the dynamic-LDS ceiling of a kernel once (needed above 64 KiB).
 hipError_t allow_lds(const void* kernel, int bytes);
 
