@@ -59,7 +59,8 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         list(ex.map(compile_one, zip(srcs, objs)))
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp,
+          "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"])
     os.replace(tmp, LIB)
     return LIB
 

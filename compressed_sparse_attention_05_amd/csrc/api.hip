@@ -236,8 +236,10 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
       if (op == CSA_OP_FORWARD) {
         const int es = idx_dtype == CSA_F32 ? 4 : 2;
         const size_t at = attn_workspace(sizing_attn(dims, B, T, idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16));
+        size_t scratch = need > at ? need : at;  // index / attention scratch, or the projection's
+        if (idx_dtype == CSA_BF16 && scratch < kGemmWorkspace) scratch = kGemmWorkspace;
         need = align256((size_t)B * T * n_tot_of(dims) * es) + align256((size_t)B * T * dims->top_k * 4) +
-               align256(need > at ? need : at);
+               align256(scratch);
       }
       *bytes = (int64_t)need;
       return CSA_OK;
@@ -410,7 +412,9 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
   const size_t i_bytes = align256((size_t)B * T * k * 4);
   const size_t i_ws = index_topk_workspace(probe);
   const size_t a_ws = attn_workspace(sizing_attn(dims, B, T, dtype));
-  const size_t x_bytes = align256(i_ws > a_ws ? i_ws : a_ws);
+  size_t scratch = i_ws > a_ws ? i_ws : a_ws;  // index / attention scratch, or the projection's
+  if (dtype == CSA_BF16 && scratch < kGemmWorkspace) scratch = kGemmWorkspace;
+  const size_t x_bytes = align256(scratch);
   rc = check_ws(ws, ws_bytes, p_bytes + i_bytes + x_bytes);
   if (rc) return rc;
   if (!aligned(x, 16) || !aligned(w->w_proj, 16)) return fail(CSA_ERR_ARG, "x and w_proj must be 16-byte aligned");
@@ -437,7 +441,9 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
   g.ldb = d_model;
   g.C = P;
   g.ldc = ntot;
-  hipError_t e = launch_gemm(g, s);
+  bool done = false;
+  hipError_t e = launch_gemm_library(g, xws, x_bytes, s, &done);
+  if (e == hipSuccess && !done) e = launch_gemm(g, s);
   if (e != hipSuccess) return hip_status(e, "csa_forward: projection");
 
   rc = csa_compress(B, T, pos0, m, D, dtype, col(c_ca), col(c_za), col(c_cb), col(c_zb), ntot, (int64_t)T * ntot,

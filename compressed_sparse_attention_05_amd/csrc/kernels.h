@@ -33,6 +33,11 @@ struct GemmArgs {
   int64_t ldc;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// bf16 GEMM through hipBLASLt with a caller workspace of kGemmWorkspace bytes; *done is false
+// (and nothing launched) when the library path does not apply, so that launch_gemm runs instead.
+constexpr size_t kGemmWorkspace = 32u << 20;
+bool gemm_library_eligible(const GemmArgs& a);
+hipError_t launch_gemm_library(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s, bool* done);
 
 struct IndexArgs {
   int B, T;
