@@ -104,11 +104,12 @@ constexpr int kNK = 32;               // keys per tile
 constexpr int kKNS = 536;             // LDS row stride (bf16) of a key row, 1072 B: 16 consecutive
                                       // rows start in 16 distinct 16-byte bank groups, and 4
                                       // consecutive rows keep 32-byte reads apart
-constexpr int kRingA = 3;             // key tiles in LDS: the one read and two being loaded
 constexpr float kRescaleLog2 = 8.f;   // reference-max slack before O is rescaled
 
+// RING key tiles in LDS: the one read and RING - 1 being loaded
+template <int RING>
 struct AttnSmem {
-  uint16_t kn[kRingA][kNK][kKNS];   // 3 x 34304 B
+  uint16_t kn[RING][kNK][kKNS];     // RING x 34304 B
   int32_t wcnt[16];                 // per-wave counts while the key list is compacted
   int32_t keys[1];                  // gathered key list (entry ids >= 0, window rows as -(r+1))
 };
@@ -133,11 +134,14 @@ struct AttnSplit {
 //   O_w^T[512 x 16] += V^T[512 x 32] P^T          (V^T read from the same key rows with the
 //                                                   transposing ds_read_b64_tr_b16, P^T in VGPRs)
 // Key rows are gathered by direct global-to-LDS loads (one 1 KiB row per instruction) into a
-// three-deep ring, two tiles ahead of the math; one barrier per tile.
-template <int NW, int OT>
-__global__ void __launch_bounds__(NW * 64) attn_mfma(AttnArgs a, AttnSplit sp) {
+// RING-deep ring, RING - 1 tiles ahead of the math; one barrier per tile. With 64 heads (4 waves)
+// the ring is two deep so that two workgroups (two query rows) share a compute unit and fill each
+// other's stalls.
+template <int NW, int RING, int OT>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) attn_mfma(AttnArgs a, AttnSplit sp) {
+  static_assert(RING == 2 || RING == 3, "one or two tiles in flight");
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
+  AttnSmem<RING>& sm = *reinterpret_cast<AttnSmem<RING>*>(smem_raw);
   constexpr int kThreads = NW * 64;
   constexpr int kRowsPerWave = kNK / NW;  // key rows one wave loads per tile
   const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -233,8 +237,8 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma(AttnArgs a, AttnSplit sp) {
   // q has landed before the loop, so that no wait for it stays in the loop body
   __builtin_amdgcn_s_waitcnt(0);
   if (ntiles > 0) load_tile(0, 0);
-  if (ntiles > 1) load_tile(1, 1);
-  wait_tiles(ntiles > 1);
+  if (RING == 3 && ntiles > 1) load_tile(1, 1);
+  wait_tiles(RING == 3 && ntiles > 1);
   __syncthreads();
   // per-lane LDS byte offsets: S^T A-fragments (row lane%16, dims g*8 ..) and the transposing reads
   // of V^T (rows 4g + (lane%16)/4 and 16 + 4g + (lane%16)/4, dims 4*(lane%4) ..)
@@ -243,7 +247,7 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma(AttnArgs a, AttnSplit sp) {
   int cur = 0;
   for (int tile = 0; tile < ntiles; ++tile) {
     const uint8_t* kt = reinterpret_cast<const uint8_t*>(&sm.kn[cur][0][0]);
-    if (tile + 2 < ntiles) load_tile(tile + 2, cur == 0 ? 2 : cur - 1);
+    if (tile + RING - 1 < ntiles) load_tile(tile + RING - 1, cur == 0 ? RING - 1 : cur - 1);
     // S^T: rows = keys 16kb + lane%16 of the tile, cols = heads. Fragments in groups of 4, the next
     // group read while the current one multiplies.
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
@@ -339,9 +343,9 @@ __global__ void __launch_bounds__(NW * 64) attn_mfma(AttnArgs a, AttnSplit sp) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (tile + 1 < ntiles) wait_tiles(tile + 2 < ntiles);  // tile + 1 has landed
+    if (tile + 1 < ntiles) wait_tiles(RING == 3 && tile + 2 < ntiles);  // tile + 1 has landed
     __syncthreads();
-    cur = cur == kRingA - 1 ? 0 : cur + 1;
+    cur = cur == RING - 1 ? 0 : cur + 1;
   }
 
   // ---- output: lane holds head `head`, dims db*16 + 4g + r
@@ -419,7 +423,12 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   for (int j = 0; j < 8; ++j) store_elem<OT>(a.out, ob + j, acc[j] * inv);
 }
 
-int attn_mfma_lds(const AttnArgs& a) { return (int)(sizeof(AttnSmem) + (size_t)(a.k + a.W + 1) * 4); }
+// 128 heads: 8 waves and a three-deep ring; 64 heads: 4 waves, two-deep ring, two workgroups per CU
+int attn_ring(const AttnArgs& a) { return a.H == 128 ? 3 : 2; }
+int attn_mfma_lds(const AttnArgs& a) {
+  const size_t base = attn_ring(a) == 3 ? sizeof(AttnSmem<3>) : sizeof(AttnSmem<2>);
+  return (int)(base + (size_t)(a.k + a.W + 1) * 4);
+}
 
 bool use_attn_mfma(const AttnArgs& a) {
   return a.in_dtype == CSA_BF16 && a.D == 512 && (a.H == 64 || a.H == 128) && a.raw_ld % 4 == 0 &&
@@ -443,12 +452,12 @@ AttnSplit plan_split(const AttnArgs& a) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-template <int NW, int OT>
+template <int NW, int RING, int OT>
 hipError_t launch_mfma(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
   const int lds = attn_mfma_lds(a);
   hipError_t e;
-  if ((e = allow_lds((const void*)attn_mfma<NW, OT>, lds)) != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_mfma<NW, OT>), dim3((unsigned)(R * sp.n_splits)), dim3(NW * 64), lds, s, a, sp);
+  if ((e = allow_lds((const void*)attn_mfma<NW, RING, OT>, lds)) != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_mfma<NW, RING, OT>), dim3((unsigned)(R * sp.n_splits)), dim3(NW * 64), lds, s, a, sp);
   return hipGetLastError();
 }
 
@@ -474,9 +483,9 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
       sp.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256((size_t)parts * a.H * 512 * 2));
     }
     if (a.H == 128)
-      e = a.out_dtype == CSA_BF16 ? launch_mfma<8, CSA_BF16>(a, sp, R, s) : launch_mfma<8, CSA_F32>(a, sp, R, s);
+      e = a.out_dtype == CSA_BF16 ? launch_mfma<8, 3, CSA_BF16>(a, sp, R, s) : launch_mfma<8, 3, CSA_F32>(a, sp, R, s);
     else
-      e = a.out_dtype == CSA_BF16 ? launch_mfma<4, CSA_BF16>(a, sp, R, s) : launch_mfma<4, CSA_F32>(a, sp, R, s);
+      e = a.out_dtype == CSA_BF16 ? launch_mfma<4, 2, CSA_BF16>(a, sp, R, s) : launch_mfma<4, 2, CSA_F32>(a, sp, R, s);
     if (e != hipSuccess) return e;
     if (sp.n_splits > 1) {
       const dim3 cg((unsigned)ceil_div(R * a.H, 4));
