@@ -125,8 +125,8 @@ struct AttnSplit {
   float* part_ml;    // [R*S, H, 2]: running max (log2 units), running sum
 };
 
-// One workgroup per (query row, split) with all H = 16 * NW heads; wave w owns heads 16w .. 16w+15
-// whole, so logits, softmax and O of a head never leave its wave:
+// One workgroup per (query row, split, group of 16 * NW heads); each wave owns 16 heads whole, so
+// logits, softmax and O of a head never leave its wave:
 //   S^T[32 keys x 16 heads] = K[32 x 512] Q_w^T   (v_mfma_f32_16x16x32_bf16, K rows from LDS, Q in
 //                                                   VGPRs)
 //   online softmax over the keys of each head: lane l holds head l%16 and keys 4g .. 4g+3,
@@ -134,22 +134,34 @@ struct AttnSplit {
 //   O_w^T[512 x 16] += V^T[512 x 32] P^T          (V^T read from the same key rows with the
 //                                                   transposing ds_read_b64_tr_b16, P^T in VGPRs)
 // Key rows are gathered by direct global-to-LDS loads (one 1 KiB row per instruction) into a
-// RING-deep ring, RING - 1 tiles ahead of the math; one barrier per tile. With 64 heads (4 waves)
-// the ring is two deep so that two workgroups (two query rows) share a compute unit and fill each
-// other's stalls.
+// RING-deep ring, RING - 1 tiles ahead of the math; one barrier per tile. With fewer than 8 waves
+// the ring is two deep so that two workgroups share a compute unit and fill each other's stalls.
 template <int NW, int RING, int OT>
-__global__ void __launch_bounds__(NW * 64, 8 / NW) attn_mfma(AttnArgs a, AttnSplit sp) {
+__global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp) {
   static_assert(RING == 2 || RING == 3, "one or two tiles in flight");
   extern __shared__ __align__(16) uint8_t smem_raw[];
   AttnSmem<RING>& sm = *reinterpret_cast<AttnSmem<RING>*>(smem_raw);
   constexpr int kThreads = NW * 64;
   constexpr int kRowsPerWave = kNK / NW;  // key rows one wave loads per tile
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int split = (int)(blockIdx.x % sp.n_splits);
-  const int64_t row = blockIdx.x / sp.n_splits;
+  // block -> (row, split, head group of 16*NW heads)
+  const int n_hg = a.H / (kHPW * NW);
+  const int hg = (int)(blockIdx.x % n_hg);
+  const int split = (int)((blockIdx.x / n_hg) % sp.n_splits);
+  const int64_t row = blockIdx.x / n_hg / sp.n_splits;
   const int b = (int)(row / a.T), t = (int)(row % a.T);
   const int64_t p = a.q_pos0 + t;
   const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
+
+  // ---- Q_w^T as B-fragments: head 16w + lane%16, dims s*32 + (lane/16)*8 .. +7 (issued first, so
+  // that their latency overlaps the key list)
+  const int head = (hg * NW + wave) * kHPW + (lane & 15);
+  const int g = lane >> 4;
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld +
+                         (int64_t)head * 512 + g * 8;
+  bf16x8 qf[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 32);
 
   // ---- key list: valid selected entries, then the window rows. All threads load their indices in
   // one burst (one memory latency, not one per 64 indices) and the waves compact them in order.
@@ -192,14 +204,6 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_mfma(AttnArgs a, AttnSpl
   const int kend = kbeg + sp.split_keys < nkeys ? kbeg + sp.split_keys : nkeys;
   const int ntiles = __builtin_amdgcn_readfirstlane(kend > kbeg ? (kend - kbeg + kNK - 1) / kNK : 0);
 
-  // ---- Q_w^T as B-fragments: head 16w + lane%16, dims s*32 + (lane/16)*8 .. +7
-  const int head = wave * kHPW + (lane & 15);
-  const int g = lane >> 4;
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld +
-                         (int64_t)head * 512 + g * 8;
-  bf16x8 qf[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 32);
 
   f32x4 o[32];
 #pragma unroll
@@ -230,8 +234,12 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_mfma(AttnArgs a, AttnSpl
   };
   // this wave's copies of every tile but the newest `pending` ones have landed
   auto wait_tiles = [&](bool pending) {
-    if (pending) CSA_WAIT_VMCNT(kRowsPerWave);
-    else CSA_WAIT_VMCNT(0);
+    if constexpr (RING == 3) {
+      if (pending) wait_vmcnt<kRowsPerWave>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
   };
 
   // q has landed before the loop, so that no wait for it stays in the loop body
@@ -423,12 +431,9 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   for (int j = 0; j < 8; ++j) store_elem<OT>(a.out, ob + j, acc[j] * inv);
 }
 
-// 128 heads: 8 waves and a three-deep ring; 64 heads: 4 waves, two-deep ring, two workgroups per CU
-int attn_ring(const AttnArgs& a) { return a.H == 128 ? 3 : 2; }
-int attn_mfma_lds(const AttnArgs& a) {
-  const size_t base = attn_ring(a) == 3 ? sizeof(AttnSmem<3>) : sizeof(AttnSmem<2>);
-  return (int)(base + (size_t)(a.k + a.W + 1) * 4);
-}
+// LDS of the deepest variant (8 waves, three-deep ring); the 4-wave variant uses a two-deep ring
+// so that two workgroups share a compute unit
+int attn_mfma_lds(const AttnArgs& a) { return (int)(sizeof(AttnSmem<3>) + (size_t)(a.k + a.W + 1) * 4); }
 
 bool use_attn_mfma(const AttnArgs& a) {
   return a.in_dtype == CSA_BF16 && a.D == 512 && (a.H == 64 || a.H == 128) && a.raw_ld % 4 == 0 &&
@@ -437,7 +442,7 @@ bool use_attn_mfma(const AttnArgs& a) {
 }
 
 constexpr int kDecodeRows = 8;     // fewer query rows per sequence than this: decode regime
-constexpr int kSplitKeys = 128;    // keys per split in the decode regime
+constexpr int kSplitKeys = 288;    // keys per split in the decode regime (9 tiles: 1152 keys in 4)
 
 AttnSplit plan_split(const AttnArgs& a) {
   AttnSplit sp{1, a.k + a.W, nullptr, nullptr};
@@ -454,11 +459,27 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <int NW, int RING, int OT>
 hipError_t launch_mfma(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
-  const int lds = attn_mfma_lds(a);
+  const int lds = (int)(sizeof(AttnSmem<RING>) + (size_t)(a.k + a.W + 1) * 4);
   hipError_t e;
   if ((e = allow_lds((const void*)attn_mfma<NW, RING, OT>, lds)) != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_mfma<NW, RING, OT>), dim3((unsigned)(R * sp.n_splits)), dim3(NW * 64), lds, s, a, sp);
+  const int64_t n_hg = a.H / (kHPW * NW);
+  hipLaunchKernelGGL((attn_mfma<NW, RING, OT>), dim3((unsigned)(R * sp.n_splits * n_hg)), dim3(NW * 64), lds, s, a,
+                     sp);
   return hipGetLastError();
+}
+
+// Waves per workgroup (16 heads each). A query row's 128 heads share one workgroup (8 waves, each
+// key row loaded once) unless there are too few (row, split) units to fill the chip, as in decode
+// with a small batch: then they are spread over two 4-wave workgroups. Heads are independent, so
+// the split of the heads never changes a result.
+int attn_waves(const AttnArgs& a, const AttnSplit& sp) {
+  const int64_t units = (int64_t)a.B * a.T * sp.n_splits;
+  return a.H == 128 && units >= 256 ? 8 : 4;
+}
+
+template <int OT>
+hipError_t launch_mfma_for(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
+  return attn_waves(a, sp) == 8 ? launch_mfma<8, 3, OT>(a, sp, R, s) : launch_mfma<4, 2, OT>(a, sp, R, s);
 }
 
 }  // namespace
@@ -482,10 +503,7 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
       sp.part_o = static_cast<uint16_t*>(ws);
       sp.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256((size_t)parts * a.H * 512 * 2));
     }
-    if (a.H == 128)
-      e = a.out_dtype == CSA_BF16 ? launch_mfma<8, 3, CSA_BF16>(a, sp, R, s) : launch_mfma<8, 3, CSA_F32>(a, sp, R, s);
-    else
-      e = a.out_dtype == CSA_BF16 ? launch_mfma<4, 2, CSA_BF16>(a, sp, R, s) : launch_mfma<4, 2, CSA_F32>(a, sp, R, s);
+    e = a.out_dtype == CSA_BF16 ? launch_mfma_for<CSA_BF16>(a, sp, R, s) : launch_mfma_for<CSA_F32>(a, sp, R, s);
     if (e != hipSuccess) return e;
     if (sp.n_splits > 1) {
       const dim3 cg((unsigned)ceil_div(R * a.H, 4));

@@ -188,8 +188,8 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
   // waits for this wave's copies of every tile but the newest `pending` ones (2 instructions each)
   auto wait_tiles = [&](int pending) {
     static_assert(16 / QW == 2, "vmcnt immediates assume two copies per wave and tile");
-    if (pending) CSA_WAIT_VMCNT(2);
-    else CSA_WAIT_VMCNT(0);
+    if (pending) wait_vmcnt<2>();
+    else wait_vmcnt<0>();
   };
 
   // Software pipeline over 32-entry column tiles: while the matrix cores run one column tile, the
