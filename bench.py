@@ -9,6 +9,13 @@ timed region starts. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload chunk1m] [--no-decode] [--no-cpu-baseline]
     python bench.py --copy-probe      # a plain 1 GiB device copy, for counter calibration
+    python bench.py --pmc-summary DIR # HBM bytes of the indexer kernel from rocprofv3 --pmc runs
+
+Counter runs (repository root; from /tmp with TMPDIR=/tmp), each in a process of its own:
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- python3 bench.py --steps 2 \
+        --warmup 1 --no-decode --no-cpu-baseline
+    (the same with WRITE_SIZE into DIR/write, and both counters of --copy-probe into
+    DIR/copy_fetch and DIR/copy_write), then --pmc-summary DIR writes profiles/*_pmc.json and .md.
 """
 from __future__ import annotations
 
@@ -93,6 +100,70 @@ def load_traffic(name: str):
     if d.get("kernel_sources_sha256_16") != kernel_hash():
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(path, counter):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc csv for one counter."""
+    import csv
+    out = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out.append((row["Kernel_Name"], float(row["Counter_Value"])))
+    return out
+
+
+def pmc_summary(pmc_dir, workload):
+    """HBM traffic of the indexer kernel from four rocprofv3 --pmc runs (see the module docstring):
+    FETCH_SIZE and WRITE_SIZE of the bench, and the same two counters of the 1 GiB copy probe, which
+    gives the factor from counter KiB to bytes. Writes profiles/index_prefill_mfma_<wl>_pmc.json/.md."""
+    def per_dispatch(run, counter, match):
+        vals = [v for n, v in _counter_rows(os.path.join(pmc_dir, run, "run_counter_collection.csv"), counter)
+                if match(n)]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for the kernel in {run}")
+        return float(np.median(vals)), len(vals)
+    is_idx = lambda n: "index_prefill_mfma" in n
+    is_copy = lambda n: "copy" in n.lower()
+    fetch_kib, nf = per_dispatch("fetch", "FETCH_SIZE", is_idx)
+    write_kib, nw = per_dispatch("write", "WRITE_SIZE", is_idx)
+    cf_kib, _ = per_dispatch("copy_fetch", "FETCH_SIZE", is_copy)
+    cw_kib, _ = per_dispatch("copy_write", "WRITE_SIZE", is_copy)
+    copy_bytes = 1 << 30
+    f_scale, w_scale = copy_bytes / cf_kib, copy_bytes / cw_kib  # bytes per counter unit
+    hbm = fetch_kib * f_scale + write_kib * w_scale
+    bench_cmd = ("python3 /root/repo/bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline --workload " + workload)
+    cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o run -- {bench_cmd}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- {bench_cmd}",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/copy_fetch -o run -- python3 /root/repo/bench.py --copy-probe",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/copy_write -o run -- python3 /root/repo/bench.py --copy-probe",
+            f"python3 /root/repo/bench.py --pmc-summary <out> --workload {workload}"]
+    d = {"kernel": "index_prefill_mfma", "workload": workload, "kernel_sources": list(KERNEL_SOURCES),
+         "kernel_sources_sha256_16": kernel_hash(),
+         "fetch_size_kib_per_dispatch": round(fetch_kib, 1), "write_size_kib_per_dispatch": round(write_kib, 1),
+         "dispatches": [nf, nw],
+         "copy_probe": {"bytes_read": copy_bytes, "bytes_written": copy_bytes, "fetch_size_kib": round(cf_kib, 1),
+                        "write_size_kib": round(cw_kib, 1)},
+         "bytes_per_fetch_unit": round(f_scale, 2), "bytes_per_write_unit": round(w_scale, 2),
+         "hbm_bytes_per_launch": int(hbm), "commands": cmds,
+         "note": "run from /tmp with TMPDIR=/tmp; <out> is a scratch directory of the GPU run"}
+    base = os.path.join(ROOT, "profiles", f"index_prefill_mfma_{workload}_pmc")
+    with open(base + ".json", "w") as f:
+        json.dump(d, f, indent=1)
+    with open(base + ".md", "w") as f:
+        f.write(f"# index_prefill_mfma, {workload}: HBM traffic from rocprofv3 counters\n\n")
+        f.write("Commands (repository root, run from /tmp with TMPDIR=/tmp):\n\n```\n" + "\n".join(cmds) + "\n```\n\n")
+        f.write("| quantity | value |\n|---|---|\n")
+        f.write(f"| FETCH_SIZE per dispatch (KiB, median of {nf}) | {fetch_kib:.1f} |\n")
+        f.write(f"| WRITE_SIZE per dispatch (KiB, median of {nw}) | {write_kib:.1f} |\n")
+        f.write(f"| copy probe (1 GiB read + 1 GiB written): FETCH_SIZE / WRITE_SIZE KiB | {cf_kib:.1f} / {cw_kib:.1f} |\n")
+        f.write(f"| bytes per counter KiB (fetch / write) | {f_scale:.1f} / {w_scale:.1f} |\n")
+        f.write(f"| HBM bytes per launch | {hbm:.4g} |\n")
+        f.write(f"| kernel sources sha256[:16] | {kernel_hash()} |\n")
+        f.write("\nFETCH_SIZE counts what the L2 caches fetch from the fabric, Infinity-Cache hits included, "
+                "so it bounds the HBM reads from above. The algorithmic bytes of one launch are the visible "
+                "keys, q_I, the head weights and the selected indices.\n")
+    print(json.dumps(d))
 
 
 def cpu_baseline(wl, inp):
@@ -230,7 +301,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-summary", metavar="DIR", help="summarise four rocprofv3 --pmc runs under DIR")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.workload)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print(f"bench.py runs on one GPU only: the CSA layer here is a single-GPU build (asked for "
