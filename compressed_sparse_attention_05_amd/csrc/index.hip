@@ -194,10 +194,11 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
 
   // Software pipeline over 32-entry column tiles: while the matrix cores run one column tile, the
   // VALU reduces the heads of the previous one. The source order below is the issue order (each
-  // sched_barrier pins it): every MFMA is followed by the ReLU + weighted sums of two accumulator
-  // element pairs of the other column tile, which run while the MFMA is in flight.
-  //   phase A of tile t: MFMA column 0 of t  |  reduce column 1 of t-1
-  //   phase B of tile t: MFMA column 1 of t  |  reduce column 0 of t
+  // sched_barrier pins it): every MFMA is followed by the ReLU + weighted sums of one accumulator
+  // row of both head tiles of the other column tile, which run while the MFMA is in flight.
+  //   phase A of tile t: MFMA column 0 of t  |  reduce column 1 of t-1, read column 1 of t
+  //   barrier: tile t+1 published
+  //   phase B of tile t: MFMA column 1 of t  |  reduce column 0 of t, read column 0 of t+1
   //   then offer the 64 scores of tile t-1 (column 0 from phase B of t-1, column 1 from phase A)
   f32x16 acc0[2], acc1[2];
 #pragma unroll
@@ -218,57 +219,66 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
   if (ntiles > 1) load_tile(1, 1);
   wait_tiles(ntiles > 1);
   __syncthreads();
+  // Column 0 of a tile is read during phase B of the tile before (after the barrier that publishes
+  // it), so phase A starts on fragments already in registers.
+  bf16x8 kf0[8], kf1[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kf0[s] = *reinterpret_cast<const bf16x8*>(smem + lbase + key_read_off(s, 0));
   int cur = 0;  // ring slot of the tile being read
   for (int tile = 0; tile < ntiles; ++tile) {
     const uint8_t* kt = smem + cur * kTileBytes + lbase;
+    const int nxt = cur == kRing - 1 ? 0 : cur + 1;
     if (tile + 2 < ntiles) load_tile(tile + 2, cur == 0 ? 2 : cur - 1);
     float sc;
-    {
-      bf16x8 kf0[8], kf1[8];
+    float p4[4] = {0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) kf0[s] = *reinterpret_cast<const bf16x8*>(kt + key_read_off(s, 0));
-      float p4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 8; ++s) {
+      acc0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf0[s], s ? acc0[0] : f32x16{}, 0, 0, 0);
+      asm volatile("" ::"v"(acc0[0]));
+      reduce_r(p4, acc1, 2 * s);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        acc0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf0[s], s ? acc0[0] : f32x16{}, 0, 0, 0);
-        asm volatile("" ::"v"(acc0[0]));
-        reduce_r(p4, acc1, 2 * s);
-        __builtin_amdgcn_sched_barrier(0);
-        acc0[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf0[s], s ? acc0[1] : f32x16{}, 0, 0, 0);
-        asm volatile("" ::"v"(acc0[1]));
-        kf1[s] = *reinterpret_cast<const bf16x8*>(kt + key_read_off(s, 1));
-        reduce_r(p4, acc1, 2 * s + 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      acc0[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf0[s], s ? acc0[1] : f32x16{}, 0, 0, 0);
+      asm volatile("" ::"v"(acc0[1]));
+      kf1[s] = *reinterpret_cast<const bf16x8*>(kt + key_read_off(s, 1));
+      reduce_r(p4, acc1, 2 * s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
       const float part1 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
       // lanes < 32 end with column 0 of t-1 (both head halves), lanes >= 32 with column 1
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part0), __float_as_uint(part1), false, false);
       sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p4[j] = 0.f;
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        acc1[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf1[s], s ? acc1[0] : f32x16{}, 0, 0, 0);
-        asm volatile("" ::"v"(acc1[0]));
-        reduce_r(p4, acc0, 2 * s);
-        __builtin_amdgcn_sched_barrier(0);
-        acc1[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf1[s], s ? acc1[1] : f32x16{}, 0, 0, 0);
-        asm volatile("" ::"v"(acc1[1]));
-        reduce_r(p4, acc0, 2 * s + 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      part0 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-      asm volatile("" ::"v"(part0));  // keeps the reduction inside phase B
     }
+    // tile + 1 has landed and every wave is past its reads of tile - 1
+    if (tile + 1 < ntiles) {
+      wait_tiles(tile + 2 < ntiles);
+      __syncthreads();
+    }
+    const uint8_t* kn = smem + nxt * kTileBytes + lbase;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p4[j] = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      acc1[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf1[s], s ? acc1[0] : f32x16{}, 0, 0, 0);
+      asm volatile("" ::"v"(acc1[0]));
+      reduce_r(p4, acc0, 2 * s);
+      __builtin_amdgcn_sched_barrier(0);
+      acc1[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf1[s], s ? acc1[1] : f32x16{}, 0, 0, 0);
+      asm volatile("" ::"v"(acc1[1]));
+      // column 0 of tile + 1 (an unused read of the next ring slot after the last tile)
+      kf0[s] = *reinterpret_cast<const bf16x8*>(kn + key_read_off(s, 0));
+      reduce_r(p4, acc0, 2 * s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    part0 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+    asm volatile("" ::"v"(part0));  // keeps the reduction inside phase B
     if (active && tile > 0) {
       const int64_t i = (int64_t)(tile - 1) * kNE + lane;
       tk.offer(make_cand(sc, (uint32_t)i), i < nv);
     }
-    if (tile + 1 < ntiles) wait_tiles(tile + 2 < ntiles);  // tile + 1 has landed
-    __syncthreads();
-    cur = cur == kRing - 1 ? 0 : cur + 1;
+    cur = nxt;
   }
   if (ntiles > 0) {
     float p4[4] = {0.f, 0.f, 0.f, 0.f};
