@@ -330,10 +330,14 @@ constexpr int kUnit = kStreamWaves * 64;
 constexpr int kQLd = 136;  // LDS row stride (bf16) of the staged q_I heads
 
 __global__ void __launch_bounds__(kStreamWaves * 64) score_bf16_stream(IndexArgs a, float* scores, int32_t* n_valid,
-                                                                        int64_t units_per_row) {
+                                                                        int64_t units_per_row, uint32_t* zero,
+                                                                        int64_t zero_words) {
   __shared__ __align__(16) uint16_t qs[64 * kQLd];
   __shared__ float ws[64];
   const int wave = threadIdx.x >> 6, lane = lane_id();
+  // the selection's histogram and counters start at zero (they are read only after this kernel)
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < zero_words; i += (int64_t)gridDim.x * blockDim.x)
+    zero[i] = 0u;
   const int64_t R = (int64_t)a.B * a.T;
   const int64_t total = R * units_per_row;
   int64_t cur_row = -1;
@@ -396,8 +400,12 @@ __global__ void __launch_bounds__(kStreamWaves * 64) score_bf16_stream(IndexArgs
 constexpr int kFp4Waves = 4;
 
 __global__ void __launch_bounds__(kFp4Waves * 64) score_fp4_stream(IndexArgs a, float* scores, int32_t* n_valid,
-                                                                     int64_t tiles_per_row) {
+                                                                     int64_t tiles_per_row, uint32_t* zero,
+                                                                     int64_t zero_words) {
   const int lane = lane_id();
+  // the selection's histogram and counters start at zero (they are read only after this kernel)
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < zero_words; i += (int64_t)gridDim.x * blockDim.x)
+    zero[i] = 0u;
   const int g = lane >> 4, c = lane & 15;
   const int64_t R = (int64_t)a.B * a.T;
   const int64_t total = R * tiles_per_row;
@@ -516,15 +524,17 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
       const int64_t tpr = ceil_div(a.n_cap, 64) > 0 ? ceil_div(a.n_cap, 64) : 1;
       int64_t g = ceil_div(R * tpr, kFp4Waves);
       if (g > 2 * stream_grid()) g = 2 * stream_grid();
-      hipLaunchKernelGGL(score_fp4_stream, dim3((unsigned)g), dim3(kFp4Waves * 64), 0, s, a, scores, nvalid, tpr);
+      hipLaunchKernelGGL(score_fp4_stream, dim3((unsigned)g), dim3(kFp4Waves * 64), 0, s, a, scores, nvalid, tpr,
+                         select_hist(p), select_zero_words((int)R));
     } else {
       const int64_t upr = ceil_div(a.n_cap, kUnit) > 0 ? ceil_div(a.n_cap, kUnit) : 1;
       int64_t g = R * upr;
       if (g > stream_grid()) g = stream_grid();
-      hipLaunchKernelGGL(score_bf16_stream, dim3((unsigned)g), dim3(kStreamWaves * 64), 0, s, a, scores, nvalid, upr);
+      hipLaunchKernelGGL(score_bf16_stream, dim3((unsigned)g), dim3(kStreamWaves * 64), 0, s, a, scores, nvalid, upr,
+                         select_hist(p), select_zero_words((int)R));
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, false, s);
+    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s);
   }
   const int cap = topk_cap_for(a.k, 256);
   const int lds = kGenWaves * (cap * 8 + 256 * 4);

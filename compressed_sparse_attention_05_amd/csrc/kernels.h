@@ -72,9 +72,11 @@ size_t topk_workspace(int R, int64_t n, int k);
 // Multi-workgroup selection over long materialised rows (select.hip).
 size_t select_workspace(int R, int64_t ld, int k);
 uint32_t* select_hist(void* ws);  // the [R, 4096] histogram at the start of the workspace
+// 32-bit words at the start of the workspace that must be zero before launch_select(zeroed=true)
+int64_t select_zero_words(int R);
 hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s);
 hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
-                         float* out_score, void* ws, bool hist_done, hipStream_t s);
+                         float* out_score, void* ws, bool zeroed, hipStream_t s);
 hipError_t launch_topk_from_scores(const TopkArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct AttnArgs {

@@ -12,7 +12,7 @@ __global__ void __launch_bounds__(256) sel_zero(uint32_t* hist, uint32_t* cnt, i
   const int64_t n = (int64_t)R * kSelBins;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) hist[i] = 0u;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 2LL * R; i += stride) cnt[i] = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 4LL * R; i += stride) cnt[i] = 0u;
 }
 
 __device__ __forceinline__ int64_t row_valid(const int32_t* n_valid, int64_t row, int64_t ld) {
@@ -32,7 +32,16 @@ __global__ void __launch_bounds__(kSelThreads) sel_hist(const float* scores, int
   __syncthreads();
   const int64_t end = base + kSelChunk < nv ? base + kSelChunk : nv;
   const float* s = scores + row * ld;
-  for (int64_t i = base + threadIdx.x; i < end; i += kSelThreads) atomicAdd(&lh[score_to_key(s[i]) >> kSelShift], 1u);
+  constexpr int kPer = kSelChunk / kSelThreads;
+  uint32_t dg[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {  // all loads first, then the LDS atomics
+    const int64_t i = base + (int64_t)j * kSelThreads + threadIdx.x;
+    dg[j] = i < end ? score_to_key(s[i]) >> kSelShift : kSelBins;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (dg[j] < (uint32_t)kSelBins) atomicAdd(&lh[dg[j]], 1u);
   __syncthreads();
   sel_flush_hist(lh, hist + row * kSelBins);
 }
@@ -75,7 +84,7 @@ __global__ void __launch_bounds__(kSelThreads) sel_collect(const float* scores, 
     d = sh_d;
   }
   const float* s = scores + row * ld;
-  uint32_t* cnt = w.cnt + row * 2;
+  uint32_t* cnt = w.cnt + row * 4;
   uint64_t* above = w.above + row * k;
   uint64_t* bnd = w.bnd + row * ld;
   // classify this thread's scores, count per wave, then one atomic per list per workgroup
@@ -147,7 +156,7 @@ __global__ void __launch_bounds__(kSelThreads) sel_final(const int32_t* n_valid,
   const int64_t row = blockIdx.x;
   const int64_t nv = row_valid(n_valid, row, ld);
   const int ntake = (int)(nv < k ? nv : k);
-  const uint32_t na = w.cnt[row * 2], nb = w.cnt[row * 2 + 1];
+  const uint32_t na = w.cnt[row * 4], nb = w.cnt[row * 4 + 1];
   const int krem = ntake - (int)na;
   const uint64_t* A = w.above + row * k;
   const uint64_t* Bg = w.bnd + row * ld;
@@ -273,7 +282,7 @@ SelWork carve(void* ws, int R, int64_t ld, int k) {
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += a256((size_t)R * kSelBins * 4);
   w.cnt = reinterpret_cast<uint32_t*>(p);
-  p += a256((size_t)R * 2 * 4);
+  p += a256((size_t)R * 4 * 4);
   w.above = reinterpret_cast<uint64_t*>(p);
   p += a256((size_t)R * k * 8);
   w.bnd = reinterpret_cast<uint64_t*>(p);
@@ -283,10 +292,12 @@ SelWork carve(void* ws, int R, int64_t ld, int k) {
 }  // namespace
 
 size_t select_workspace(int R, int64_t ld, int k) {
-  return a256((size_t)R * kSelBins * 4) + a256((size_t)R * 2 * 4) + a256((size_t)R * k * 8) + a256((size_t)R * ld * 8);
+  return a256((size_t)R * kSelBins * 4) + a256((size_t)R * 4 * 4) + a256((size_t)R * k * 8) + a256((size_t)R * ld * 8);
 }
 
 uint32_t* select_hist(void* ws) { return static_cast<uint32_t*>(ws); }
+
+int64_t select_zero_words(int R) { return (int64_t)((a256((size_t)R * kSelBins * 4) + (size_t)R * 4 * 4) / 4); }
 
 hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s) {
   SelWork w = carve(ws, R, ld, k);
@@ -298,15 +309,13 @@ hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s)
 }
 
 hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
-                         float* out_score, void* ws, bool hist_done, hipStream_t s) {
+                         float* out_score, void* ws, bool zeroed, hipStream_t s) {
   SelWork w = carve(ws, R, ld, k);
   hipError_t e;
   const unsigned nchunks = (unsigned)(ceil_div(ld, kSelChunk) > 0 ? ceil_div(ld, kSelChunk) : 1);
-  if (!hist_done) {
-    if ((e = launch_select_zero(ws, R, ld, k, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(sel_hist, dim3(nchunks, (unsigned)R), dim3(kSelThreads), 0, s, scores, ld, n_valid, w.hist);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if (!zeroed && (e = launch_select_zero(ws, R, ld, k, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(sel_hist, dim3(nchunks, (unsigned)R), dim3(kSelThreads), 0, s, scores, ld, n_valid, w.hist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(sel_collect, dim3(nchunks, (unsigned)R), dim3(kSelThreads), 0, s, scores, ld, n_valid, k, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   int P = 1;

@@ -3,15 +3,15 @@
 //
 // Keys are the same 64-bit keys as the streaming selection (topk_wave.h): order-preserving score
 // bits in the high half, ~index in the low half, so the k largest keys are the layer's top-k.
-//   pass A  (fused into the score kernels, or sel_hist): a 4096-bin histogram of the top 12 bits of
-//           every row's score keys, built in LDS per workgroup and added to the row's global
-//           histogram (integer atomics: the totals are exact and order-independent);
+//   pass A  (sel_hist, many workgroups per row): a 4096-bin histogram of the top 12 bits of every
+//           row's score keys, built in LDS per workgroup and added to the row's global histogram
+//           (integer atomics: the totals are exact and order-independent);
 //   pass B  (sel_collect, many workgroups per row): every workgroup finds the row's boundary digit
 //           d (the 12-bit bin holding the k-th key) from the histogram, then appends its
-//           candidates with digit > d to the row's "above" list (fewer than k of them) and those with
-//           digit == d to the row's "boundary" list;
+//           candidates with digit > d to the row's "above" list (fewer than k of them) and those
+//           with digit == d to the row's "boundary" list;
 //   pass C  (sel_final, one workgroup per row): a block radix select over the boundary list picks
-//           the k - |above| largest, the union is sorted by entry index (bitonic) and written.
+//           the k - |above| largest, and the union is written in entry-index order.
 // List order depends on atomic slot assignment, but the selected set does not, and the output is
 // sorted: results are deterministic.
 #pragma once
@@ -27,7 +27,7 @@ constexpr int kSelThreads = 256;
 
 struct SelWork {
   uint32_t* hist;      // [R, kSelBins]
-  uint32_t* cnt;       // [R, 2]: above, boundary
+  uint32_t* cnt;       // [R, 4]: above count, boundary count (two words unused)
   uint64_t* above;     // [R, k]
   uint64_t* bnd;       // [R, n]
 };
