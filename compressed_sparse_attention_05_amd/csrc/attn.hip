@@ -125,6 +125,21 @@ struct AttnSplit {
   float* part_ml;    // [R*S, H, 2]: running max (log2 units), running sum
 };
 
+// Cross-lane reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the gfx950
+// row-swap permutes, which stay on the VALU.
+__device__ __forceinline__ float group4_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // One workgroup per (query row, split, group of 16 * NW heads); each wave owns 16 heads whole, so
 // logits, softmax and O of a head never leave its wave:
 //   S^T[32 keys x 16 heads] = K[32 x 512] Q_w^T   (v_mfma_f32_16x16x32_bf16, K rows from LDS, Q in
@@ -252,32 +267,54 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
   // of V^T (rows 4g + (lane%16)/4 and 16 + 4g + (lane%16)/4, dims 4*(lane%4) ..)
   const uint32_t qk_off = (uint32_t)(((lane & 15) * kKNS + g * 8) * 2);
   const uint32_t pv_off = (uint32_t)(((4 * g + ((lane & 15) >> 2)) * kKNS + 4 * (lane & 3)) * 2);
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  auto kread = [&](int slot, int i, int sg) {  // K fragment i (key block i/2, k-step 2sg + i%2)
+    const uint8_t* kt = reinterpret_cast<const uint8_t*>(&sm.kn[slot][0][0]);
+    return *reinterpret_cast<const bf16x8*>(kt + qk_off + (i >> 1) * 16 * kKNS * 2 + (sg * 2 + (i & 1)) * 64);
+  };
+  auto vread = [&](int slot, int db, int half) {
+    const uint32_t vb = ring + (uint32_t)(slot * kNK * kKNS * 2) + pv_off;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(uintptr_t)(vb + (uint32_t)(half * 16 * kKNS * 2 + db * 32)));
+  };
+  // With the three-deep ring the barrier sits between the softmax and P V: it publishes tile + 1,
+  // whose first K fragments are then read while P V runs, so the next S^T starts from registers.
+  bf16x8 kf[2][4];
+  if constexpr (RING == 3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kf[0][i] = kread(0, i, 0);
+  }
   int cur = 0;
   for (int tile = 0; tile < ntiles; ++tile) {
-    const uint8_t* kt = reinterpret_cast<const uint8_t*>(&sm.kn[cur][0][0]);
-    if (tile + RING - 1 < ntiles) load_tile(tile + RING - 1, cur == 0 ? RING - 1 : cur - 1);
+    const int nxt = cur == RING - 1 ? 0 : cur + 1;
+    if constexpr (RING == 2) {
+      if (tile + 1 < ntiles) load_tile(tile + 1, nxt);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[0][i] = kread(cur, i, 0);
+    }
     // S^T: rows = keys 16kb + lane%16 of the tile, cols = heads. Fragments in groups of 4, the next
     // group read while the current one multiplies.
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
-    {
-      bf16x8 kf[2][4];
+#pragma unroll
+    for (int sg = 0; sg < 8; ++sg) {
+      if (sg < 7) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[(sg + 1) & 1][i] = kread(cur, i, sg + 1);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        kf[0][i] = *reinterpret_cast<const bf16x8*>(kt + qk_off + (i >> 1) * 16 * kKNS * 2 + (i & 1) * 64);
+        sacc[i >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[sg & 1][i], qf[sg * 2 + (i & 1)], sacc[i >> 1], 0, 0, 0);
+      asm volatile("" ::"v"(sacc[0]), "v"(sacc[1]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the first V^T fragments are read while the softmax runs
+    constexpr int VG = 2;  // dim blocks per group
+    v4i16 vf[2][VG][2];
 #pragma unroll
-      for (int sg = 0; sg < 8; ++sg) {
-        if (sg < 7) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            kf[(sg + 1) & 1][i] = *reinterpret_cast<const bf16x8*>(kt + qk_off + (i >> 1) * 16 * kKNS * 2 +
-                                                                    ((sg + 1) * 2 + (i & 1)) * 64);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sacc[i >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[sg & 1][i], qf[sg * 2 + (i & 1)], sacc[i >> 1], 0, 0, 0);
-        asm volatile("" ::"v"(sacc[0]), "v"(sacc[1]));
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < VG; ++i) {
+      vf[0][i][0] = vread(cur, i, 0);
+      vf[0][i][1] = vread(cur, i, 1);
     }
     // online softmax: this lane holds head `head`, keys 16kb + 4g + r
     const int k0 = kbeg + tile * kNK;
@@ -291,8 +328,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
         v[kb][r] = x;
         tmax = fmaxf(tmax, x);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = group4_max(tmax);
     // lazy rescaling: the reference max moves only when a logit exceeds it by more than 2^8, so
     // weights stay below 256 and O is rescaled in few tiles
     const float m_new = tmax > m_run + kRescaleLog2 ? tmax : m_run;
@@ -306,8 +342,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
       psum += bf2f(h0) + bf2f(h1);  // the denominator sums the same rounded weights P V uses
       pw[m] = h0 | ((uint32_t)h1 << 16);
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = group4_sum(psum);
     l_run = l_run * al + psum;
     m_run = m_new;
     if (__ballot(al != 1.f)) {
@@ -316,44 +351,43 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
     }
     // P^T B-fragment: k index j <-> key 4g + j (j < 4) and 16 + 4g + j - 4 (j >= 4)
     const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    if constexpr (RING == 3) {
+      if (tile + 1 < ntiles) {  // tile + 1 has landed; every wave is past its reads of tile - 1
+        wait_tiles(false);
+        __syncthreads();
+      }
+      if (tile + 2 < ntiles) load_tile(tile + 2, nxt == RING - 1 ? 0 : nxt + 1);
+    }
     // O^T[dims 16db + lane%16 (rows) x heads] += V^T P^T; each V^T fragment is two transposing
     // reads: lane 16g + i gets dim 16db + i of keys 4g .. 4g+3, then of keys 16+4g .. 16+4g+3
-    {
-      typedef short v4i16 __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-      const uint32_t vb = ring + (uint32_t)(cur * kNK * kKNS * 2) + pv_off;
-      auto vread = [&](int db, int half) {
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(uintptr_t)(vb + (uint32_t)(half * 16 * kKNS * 2 + db * 32)));
-      };
-      v4i16 vf[2][4][2];
+    constexpr int NG = 32 / VG;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vf[0][i][0] = vread(i, 0);
-        vf[0][i][1] = vread(i, 1);
+    for (int dg = 0; dg < NG; ++dg) {
+      if (dg < NG - 1) {
+#pragma unroll
+        for (int i = 0; i < VG; ++i) {
+          vf[(dg + 1) & 1][i][0] = vread(cur, (dg + 1) * VG + i, 0);
+          vf[(dg + 1) & 1][i][1] = vread(cur, (dg + 1) * VG + i, 1);
+        }
+      }
+      if constexpr (RING == 3) {
+        if (dg < 4) kf[0][dg] = kread(nxt, dg, 0);  // first K fragments of tile + 1
       }
 #pragma unroll
-      for (int dg = 0; dg < 8; ++dg) {
-        if (dg < 7) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vf[(dg + 1) & 1][i][0] = vread((dg + 1) * 4 + i, 0);
-            vf[(dg + 1) & 1][i][1] = vread((dg + 1) * 4 + i, 1);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v4i16 lo = vf[dg & 1][i][0], hi = vf[dg & 1][i][1];
-          const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[dg * 4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[dg * 4 + i], 0, 0, 0);
-        }
-        asm volatile("" ::"v"(o[dg * 4]), "v"(o[dg * 4 + 1]), "v"(o[dg * 4 + 2]), "v"(o[dg * 4 + 3]));
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < VG; ++i) {
+        const v4i16 lo = vf[dg & 1][i][0], hi = vf[dg & 1][i][1];
+        const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dg * VG + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[dg * VG + i], 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < VG; ++i) asm volatile("" ::"v"(o[dg * VG + i]));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (tile + 1 < ntiles) wait_tiles(RING == 3 && tile + 2 < ntiles);  // tile + 1 has landed
-    __syncthreads();
-    cur = cur == RING - 1 ? 0 : cur + 1;
+    if constexpr (RING == 2) {
+      if (tile + 1 < ntiles) wait_tiles(false);  // tile + 1 has landed
+      __syncthreads();
+    }
+    cur = nxt;
   }
 
   // ---- output: lane holds head `head`, dims db*16 + 4g + r
