@@ -4,16 +4,16 @@
 // layer"; bullet "An attention sink": an extra exp(sink_h) in the denominator).
 //
 // Paths:
-//  * attn_mfma (bf16, D = 512, 64-head groups): one workgroup per (query row, 64-head group); the
-//    four waves split the 512 dims into quarters. For each tile of 32 gathered keys a wave loads its
-//    quarter of every key straight from HBM/L2 into MFMA B-fragments, computes the partial logits of
-//    all 64 heads (QK^T over its 128 dims, q resident in VGPRs), and stores the partials plus a
-//    transposed copy of its key quarter (the V operand) in LDS. After a barrier each wave finishes
-//    the online softmax of 16 heads (sum of the four partials, running max and sum, P in bf16);
-//    after a second barrier each wave accumulates O[64 heads x its 128 dims] += P V with MFMA.
-//    Key bytes cross the L2->CU path once per head group; the entry is both K and V.
+//  * attn_pairs (bf16, D = 512, 128 heads, 8 waves): one workgroup per (query row, key split);
+//    wave pairs own 32 heads and split the 512 dims in halves, meet through LDS for the logits, and
+//    run as two groups half a tile apart so that softmax and MFMA work of a SIMD overlap.
+//  * attn_mfma (bf16, D = 512, 64-head groups of 4 waves or 128 heads in 8): each wave owns 16
+//    heads whole; used for 64-head layers and for small-batch decode, where the heads are spread
+//    over more workgroups.
 //  * attn_generic (any H, D, fp32 or bf16): one wave per (row, head), lanes over dims, one key at
 //    a time with a wave reduction; used for fp32 layers and odd shapes.
+// With fewer than 8 query rows per sequence the key list is cut into fixed splits and
+// attn_combine merges the partial results.
 #include "kernels.h"
 
 namespace csa {
@@ -415,6 +415,314 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
   }
 }
 
+// ---------------------------------------------------------------- MFMA, wave pairs (bf16, D = 512)
+//
+// One workgroup per (query row, split, group of 16 * NW heads). The waves form pairs; a pair owns
+// 32 heads and each of its two waves owns half of the 512 dims, so a wave keeps Q and O of 32 heads
+// x 256 dims in registers and every K or V^T fragment it reads from LDS feeds a 32-head MFMA
+// (twice the reuse of a 16-head wave; LDS bandwidth is what bounds this loop). Per 32-key tile:
+//   S_w^T[32 keys x 32 heads] = K[32 x its 256 dims] Q_w^T   (v_mfma_f32_32x32x16_bf16)
+//   the two partial logit tiles meet through LDS; both waves add them (a + b = b + a, so both
+//   hold the same logits) and run the same online softmax: lane l holds head l%32 and 16 keys,
+//   one v_permlane32_swap per reduction
+//   O_w^T[its 256 dims x 32 heads] += V^T P^T                (V^T by the transposing
+//                                                             ds_read_b64_tr_b16, P^T in VGPRs)
+// The K fragment row of lane l is key pi(l%32), pi = swap of bits 2 and 3, so that the keys of the
+// logit accumulator a lane holds are exactly the keys of the P^T fragment it feeds to P V.
+// Key rows come by direct global-to-LDS loads into a three-deep ring. Two barriers per tile and
+// wave: after the partial logits are written, and after P V (the exchange buffer is free again).
+constexpr int kPairRing = 3;
+
+template <int NW>
+struct PairSmem {
+  uint16_t kn[kPairRing][kNK][kKNS];  // 3 x 34304 B
+  uint4 sx[NW][4][64];                // partial logits, 4 KiB per wave
+  int32_t wcnt[16];
+  int32_t keys[1];
+};
+
+template <int NW, int OT>
+__global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit sp) {
+  static_assert(NW == 2 || NW == 4 || NW == 8, "whole wave pairs, at most 8 waves");
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  PairSmem<NW>& sm = *reinterpret_cast<PairSmem<NW>*>(smem_raw);
+  constexpr int kThreads = NW * 64;
+  constexpr int kRowsPerWave = kNK / NW;
+  constexpr int kHeadsPerBlock = 16 * NW;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int n_hg = a.H / kHeadsPerBlock;
+  const int hg = (int)(blockIdx.x % n_hg);
+  const int split = (int)((blockIdx.x / n_hg) % sp.n_splits);
+  const int64_t row = blockIdx.x / n_hg / sp.n_splits;
+  const int b = (int)(row / a.T), t = (int)(row % a.T);
+  const int64_t p = a.q_pos0 + t;
+  const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
+
+  const int half = wave & 1;                    // dims 256*half .. +255
+  const int hl = lane & 31, hh = lane >> 5;     // head within the pair; k half of a fragment
+  const int head = hg * kHeadsPerBlock + (wave >> 1) * 32 + hl;
+
+  // ---- Q_w^T B-fragments: lane l holds head `head`, dims 256*half + 16s + 8hh .. +7
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld +
+                         (int64_t)head * 512 + 256 * half + 8 * hh;
+  bf16x8 qf[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 16);
+
+  // ---- key list (valid selected entries, then the window rows), compacted in order
+  {
+    const int32_t* idx = a.idx + row * a.k;
+    int nsel = 0;
+    for (int base = 0; base < a.k; base += 4 * kThreads) {
+      int32_t e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = base + r * kThreads + (int)threadIdx.x;
+        e[r] = j < a.k ? idx[j] : -1;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (base + r * kThreads >= a.k) break;
+        const bool ok = e[r] >= 0 && e[r] < a.n_cap;
+        const uint64_t bm = __ballot(ok);
+        if (lane == 0) sm.wcnt[wave] = __popcll(bm);
+        __syncthreads();
+        int off = nsel, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int c = sm.wcnt[w];
+          off += w < wave ? c : 0;
+          tot += c;
+        }
+        if (ok) sm.keys[off + __popcll(bm & lanemask_lt())] = e[r];
+        nsel += tot;
+        __syncthreads();
+      }
+    }
+    const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
+    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
+    if (threadIdx.x == 0) sm.keys[a.k + a.W] = nsel + nwin;
+  }
+  __syncthreads();
+  const int nkeys = sm.keys[a.k + a.W];
+  const int kbeg = split * sp.split_keys;
+  const int kend = kbeg + sp.split_keys < nkeys ? kbeg + sp.split_keys : nkeys;
+  const int ntiles = __builtin_amdgcn_readfirstlane(kend > kbeg ? (kend - kbeg + kNK - 1) / kNK : 0);
+
+  f32x16 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x16{};
+  const float scale = a.scale * 1.4426950408889634f;  // logits in log2 units
+  float m_run = -INFINITY, l_run = 0.f;
+  if (a.sink && sp.n_splits == 1) {
+    m_run = a.sink[head] * 1.4426950408889634f;
+    l_run = 1.f;
+  }
+
+  const uint16_t* ent = static_cast<const uint16_t*>(a.entries) + (int64_t)b * a.entries_seq_stride;
+  const uint16_t* raw = static_cast<const uint16_t*>(a.raw) + (int64_t)b * a.raw_seq_stride;
+  const uint32_t ring = lds_offset(&sm.kn[0][0][0]);
+  // row r of tile `tile` into ring slot `buf`; keys past the split's end repeat its last key
+  // (finite values; their logits are masked). Lane l reads the key id of row l%32 (one LDS round
+  // trip per tile), and the rows of this wave are taken from it with readlane.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto load_tile = [&](int tile, int buf) {
+    int kl = kbeg + tile * kNK + (lane & 31);
+    kl = kl < kend ? kl : kend - 1;
+    const int32_t id = sm.keys[kl];
+    // row address of row l%32, computed on the vector unit without branches
+    const uint64_t ra = id >= 0 ? (uint64_t)(ent + (int64_t)id * 512) : (uint64_t)(raw + (int64_t)(-id - 1) * a.raw_ld);
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int r = j * NW + wave_u;
+      const uint64_t rb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(ra >> 32), r) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ra, r);
+      copy_to_lds16(reinterpret_cast<const uint16_t*>(rb) + lane * 8,
+                    __builtin_amdgcn_readfirstlane(ring + (uint32_t)((buf * kNK + r) * kKNS * 2)));
+    }
+  };
+
+  // per-lane LDS byte offsets within a ring slot:
+  //  K A-fragment s: row pi(l%32), dims 256*half + 16s + 8hh .. +7
+  //  V^T A-fragment (dims 32dt .., keys 16ks ..), read r of two: 16-lane group g = l/16, i = l%16
+  //  addresses row 16ks + 8(g/2) + 4r + i/4, dims 256*half + 32dt + 16(g%2) + 4(i%4) .. +3
+  const int prow = (hl & 0x13) | ((hl & 4) << 1) | ((hl & 8) >> 1);
+  const uint32_t qk_off = (uint32_t)((prow * kKNS + 256 * half + 8 * hh) * 2);
+  const int g = lane >> 4, gi = lane & 15;
+  const uint32_t pv_off = (uint32_t)(((8 * (g >> 1) + (gi >> 2)) * kKNS + 256 * half + 16 * (g & 1) + 4 * (gi & 3)) * 2);
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  auto kread = [&](int slot, int s) {
+    const uint8_t* kt = reinterpret_cast<const uint8_t*>(&sm.kn[slot][0][0]);
+    return *reinterpret_cast<const bf16x8*>(kt + qk_off + s * 32);
+  };
+  auto vread = [&](int slot, int dt, int ks) {
+    const uint32_t vb = ring + (uint32_t)(slot * kNK * kKNS * 2) + pv_off + (uint32_t)(ks * 16 * kKNS * 2 + dt * 64);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)vb);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(vb + 4 * kKNS * 2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // q has landed before the loop, so that no wait for it stays in the loop body
+  __builtin_amdgcn_s_waitcnt(0);
+  if (ntiles > 0) load_tile(0, 0);
+  if (ntiles > 1) load_tile(1, 1);
+  if (ntiles > 1) wait_vmcnt<kRowsPerWave>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+
+  // Two groups of waves, half a tile apart: group 0 (waves 0-3) runs the logits and the exchange
+  // of tile t while group 1 (waves 4-7, the same four SIMDs) runs the softmax and P V of tile t-1,
+  // and the other way round, so that every SIMD has MFMA work while one of its waves is in the
+  // softmax. Barriers count arrivals, not code positions: between consecutive barriers one group
+  // does [logits, exchange write] and the other [exchange read, softmax, P V]. Group 1 opens with
+  // one extra barrier and group 0 closes with one, so both pass 2 * ntiles + 1 barriers (numbered
+  // from 0 after the prologue). Tile t + 1 is published by barrier 2t + 1 (every wave waits for its
+  // own copies of it first); tile t - 1 is read for the last time before barrier 2t, so tile t + 2
+  // is copied into its slot after barrier 2t, three barriers before group 0 reads it.
+  const int grp = NW == 8 ? (wave >> 2) & 1 : 0;
+  // this wave's copies of tile + 1 have landed (those of tile + 2 may still be in flight)
+  auto wait_next = [&](int tile) {
+    if (tile + 1 < ntiles) {
+      if (tile + 2 < ntiles) wait_vmcnt<kRowsPerWave>();
+      else wait_vmcnt<0>();
+    }
+  };
+  if (grp == 1) __syncthreads();
+
+  int cur = 0;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int nxt = cur == kPairRing - 1 ? 0 : cur + 1;
+    const int nxt2 = nxt == kPairRing - 1 ? 0 : nxt + 1;
+    // the slot of tile - 1 is free once group 1 has passed its P V of tile - 1
+    if (grp == 1 && tile + 2 < ntiles) load_tile(tile + 2, nxt2);
+
+    // ---- partial S^T over this wave's 256 dims; fragments read two ahead of the MFMA
+    f32x16 sacc = f32x16{};
+    bf16x8 kf[4];
+    kf[0] = kread(cur, 0);
+    kf[1] = kread(cur, 1);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s + 2 < 16) kf[(s + 2) & 3] = kread(cur, s + 2);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s & 3], qf[s], sacc, 0, 0, 0);
+      asm volatile("" ::"v"(sacc));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- exchange: both waves of the pair end with the same logits
+    uint4* mine = &sm.sx[wave][0][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mine[i * 64] = make_uint4(__float_as_uint(sacc[4 * i]), __float_as_uint(sacc[4 * i + 1]),
+                                __float_as_uint(sacc[4 * i + 2]), __float_as_uint(sacc[4 * i + 3]));
+    if (grp == 1) wait_next(tile);
+    __syncthreads();
+    if (grp == 0 && tile + 2 < ntiles) load_tile(tile + 2, nxt2);
+    const uint4* other = &sm.sx[wave ^ 1][0][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = other[i * 64];
+      sacc[4 * i] += __uint_as_float(u.x);
+      sacc[4 * i + 1] += __uint_as_float(u.y);
+      sacc[4 * i + 2] += __uint_as_float(u.z);
+      sacc[4 * i + 3] += __uint_as_float(u.w);
+    }
+    // ---- online softmax: lane l holds head `head` and keys 16(r/8) + 8hh + r%8 of the tile; the
+    // max is taken on the raw logits (scale > 0) and the scale goes into the exponent's FMA
+    const int k0 = kbeg + tile * kNK;
+    if (k0 + kNK > kend) {  // last tile of the split: keys past its end are masked
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k0 + 16 * (r >> 3) + 8 * hh + (r & 7) >= kend) sacc[r] = -INFINITY;
+    }
+    float tmax = fmaxf(sacc[0], sacc[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(sacc[r], sacc[r + 1]));
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale;
+    }
+    // lazy rescaling: the reference max moves only when a logit exceeds it by more than 2^8
+    const float m_new = tmax > m_run + kRescaleLog2 ? tmax : m_run;
+    const float al = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // weights rounded to bf16 by v_cvt_pk_bf16_f32; the denominator sums the same rounded weights
+    // that P V uses (v_dot2 with ones)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    bf16x2 pp[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * m], scale, -m_new));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[2 * m + 1], scale, -m_new));
+      pp[m] = bf16x2{(__bf16)p0, (__bf16)p1};
+      psum = __builtin_amdgcn_fdot2_f32_bf16(pp[m], ones, psum, false);
+    }
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+      psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    l_run = l_run * al + psum;
+    m_run = m_new;
+    if (__ballot(al != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= al;
+    }
+    // P^T B-fragment of k-step ks: keys 16ks + 8hh + j, j = 0..7
+    const bf16x8 pf0 = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
+                                                         __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3])));
+    const bf16x8 pf1 = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint32_t, pp[4]), __builtin_bit_cast(uint32_t, pp[5]),
+                                                         __builtin_bit_cast(uint32_t, pp[6]), __builtin_bit_cast(uint32_t, pp[7])));
+    // ---- O^T[dims 32dt + .. x heads] += V^T P^T, V^T fragments read one dim tile ahead
+    bf16x8 vf[2][2];
+    vf[0][0] = vread(cur, 0, 0);
+    vf[0][1] = vread(cur, 0, 1);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      if (dt + 1 < 8) {
+        vf[(dt + 1) & 1][0] = vread(cur, dt + 1, 0);
+        vf[(dt + 1) & 1][1] = vread(cur, dt + 1, 1);
+      }
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt & 1][0], pf0, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt & 1][1], pf1, o[dt], 0, 0, 0);
+      asm volatile("" ::"v"(o[dt]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // after this barrier the pair's exchange buffer can be written again
+    if (grp == 0) wait_next(tile);
+    __syncthreads();
+    cur = nxt;
+  }
+  if (grp == 0) __syncthreads();
+
+  // ---- output: lane holds head `head`, dims 256*half + 32dt + 8(r/4) + 4hh + r%4
+  const int dbase = 256 * half + 4 * hh;
+  if (sp.n_splits == 1) {
+    const float inv = 1.f / l_run;
+    const int64_t ob = (row * a.H + head) * 512 + dbase;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) store_elem<OT>(a.out, ob + 32 * dt + 8 * (r >> 2) + (r & 3), o[dt][r] * inv);
+  } else {
+    const int64_t pidx = row * sp.n_splits + split;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* po = sp.part_o + (pidx * a.H + head) * 512 + dbase;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint32_t w0 = f2bf(o[dt][4 * q4] * inv) | ((uint32_t)f2bf(o[dt][4 * q4 + 1] * inv) << 16);
+        const uint32_t w1 = f2bf(o[dt][4 * q4 + 2] * inv) | ((uint32_t)f2bf(o[dt][4 * q4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(po + 32 * dt + 8 * q4) = make_uint2(w0, w1);
+      }
+    if (half == 0 && hh == 0) {
+      sp.part_ml[(pidx * a.H + head) * 2] = m_run;
+      sp.part_ml[(pidx * a.H + head) * 2 + 1] = l_run;
+    }
+  }
+}
+
 // Merges the n_splits partials of every (row, head): M = max m_s, L = sum l_s 2^(m_s - M) (plus the
 // sink), O = sum l_s 2^(m_s - M) (O_s / l_s) / L, splits taken in order. One wave per (row, head),
 // four per workgroup.
@@ -467,7 +775,10 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
 
 // LDS of the deepest variant (8 waves, three-deep ring); the 4-wave variant uses a two-deep ring
 // so that two workgroups share a compute unit
-int attn_mfma_lds(const AttnArgs& a) { return (int)(sizeof(AttnSmem<3>) + (size_t)(a.k + a.W + 1) * 4); }
+int attn_mfma_lds(const AttnArgs& a) {
+  const size_t deepest = sizeof(AttnSmem<3>) > sizeof(PairSmem<8>) ? sizeof(AttnSmem<3>) : sizeof(PairSmem<8>);
+  return (int)(deepest + (size_t)(a.k + a.W + 1) * 4);
+}
 
 bool use_attn_mfma(const AttnArgs& a) {
   return a.in_dtype == CSA_BF16 && a.D == 512 && (a.H == 64 || a.H == 128) && a.raw_ld % 4 == 0 &&
@@ -511,9 +822,19 @@ int attn_waves(const AttnArgs& a, const AttnSplit& sp) {
   return a.H == 128 && units >= 256 ? 8 : 4;
 }
 
+template <int NW, int OT>
+hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
+  const int lds = (int)(sizeof(PairSmem<NW>) + (size_t)(a.k + a.W + 1) * 4);
+  hipError_t e;
+  if ((e = allow_lds((const void*)attn_pairs<NW, OT>, lds)) != hipSuccess) return e;
+  const int64_t n_hg = a.H / (16 * NW);
+  hipLaunchKernelGGL((attn_pairs<NW, OT>), dim3((unsigned)(R * sp.n_splits * n_hg)), dim3(NW * 64), lds, s, a, sp);
+  return hipGetLastError();
+}
+
 template <int OT>
 hipError_t launch_mfma_for(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
-  return attn_waves(a, sp) == 8 ? launch_mfma<8, 3, OT>(a, sp, R, s) : launch_mfma<4, 2, OT>(a, sp, R, s);
+  return attn_waves(a, sp) == 8 ? launch_pairs<8, OT>(a, sp, R, s) : launch_mfma<4, 2, OT>(a, sp, R, s);
 }
 
 }  // namespace
