@@ -441,6 +441,10 @@ struct PairSmem {
   int32_t keys[1];
 };
 
+// Workgroups of one head group per (row, split), several splits: the splits of a row are grouped
+// on one XCD.
+__host__ __device__ inline bool pairs_xcd_grouped(int H, int NW, int n_splits) { return H == 16 * NW && n_splits > 1; }
+
 template <int NW, int OT>
 __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit sp) {
   static_assert(NW == 2 || NW == 4 || NW == 8, "whole wave pairs, at most 8 waves");
@@ -451,9 +455,21 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   constexpr int kHeadsPerBlock = 16 * NW;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int n_hg = a.H / kHeadsPerBlock;
-  const int hg = (int)(blockIdx.x % n_hg);
-  const int split = (int)((blockIdx.x / n_hg) % sp.n_splits);
-  const int64_t row = blockIdx.x / n_hg / sp.n_splits;
+  int hg, split;
+  int64_t row;
+  if (pairs_xcd_grouped(a.H, NW, sp.n_splits)) {
+    // the splits of a row run on one XCD (workgroups are dealt to the 8 XCDs round-robin), so the
+    // row's q is read once into that XCD's L2
+    const int64_t j = blockIdx.x >> 3;
+    hg = 0;
+    split = (int)(j % sp.n_splits);
+    row = (j / sp.n_splits) * 8 + (blockIdx.x & 7);
+    if (row >= (int64_t)a.B * a.T) return;  // padding workgroup of the last row group
+  } else {
+    hg = (int)(blockIdx.x % n_hg);
+    split = (int)((blockIdx.x / n_hg) % sp.n_splits);
+    row = blockIdx.x / n_hg / sp.n_splits;
+  }
   const int b = (int)(row / a.T), t = (int)(row % a.T);
   const int64_t p = a.q_pos0 + t;
   const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
@@ -462,17 +478,22 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   const int hl = lane & 31, hh = lane >> 5;     // head within the pair; k half of a fragment
   const int head = hg * kHeadsPerBlock + (wave >> 1) * 32 + hl;
 
-  // ---- Q_w^T B-fragments: lane l holds head `head`, dims 256*half + 16s + 8hh .. +7
+  // ---- Q_w^T B-fragments: lane l holds head `head`, dims 256*half + 16s + 8hh .. +7. They are
+  // loaded after the first burst of key indices: loads complete in order, so waiting for the
+  // indices does not wait for q as well.
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld +
                          (int64_t)head * 512 + 256 * half + 8 * hh;
   bf16x8 qf[16];
+  auto load_q = [&]() {
 #pragma unroll
-  for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 16);
+    for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 16);
+  };
 
   // ---- key list (valid selected entries, then the window rows), compacted in order
   {
     const int32_t* idx = a.idx + row * a.k;
     int nsel = 0;
+    if (a.k <= 0) load_q();
     for (int base = 0; base < a.k; base += 4 * kThreads) {
       int32_t e[4];
 #pragma unroll
@@ -480,6 +501,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
         const int j = base + r * kThreads + (int)threadIdx.x;
         e[r] = j < a.k ? idx[j] : -1;
       }
+      if (base == 0) load_q();
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (base + r * kThreads >= a.k) break;
@@ -828,7 +850,8 @@ hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipSt
   hipError_t e;
   if ((e = allow_lds((const void*)attn_pairs<NW, OT>, lds)) != hipSuccess) return e;
   const int64_t n_hg = a.H / (16 * NW);
-  hipLaunchKernelGGL((attn_pairs<NW, OT>), dim3((unsigned)(R * sp.n_splits * n_hg)), dim3(NW * 64), lds, s, a, sp);
+  const int64_t blocks = pairs_xcd_grouped(a.H, NW, sp.n_splits) ? ceil_div(R, 8) * 8 * sp.n_splits : R * sp.n_splits * n_hg;
+  hipLaunchKernelGGL((attn_pairs<NW, OT>), dim3((unsigned)blocks), dim3(NW * 64), lds, s, a, sp);
   return hipGetLastError();
 }
 
