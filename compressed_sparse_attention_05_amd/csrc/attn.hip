@@ -857,7 +857,11 @@ hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipSt
 
 template <int OT>
 hipError_t launch_mfma_for(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
-  return attn_waves(a, sp) == 8 ? launch_pairs<8, OT>(a, sp, R, s) : launch_mfma<4, 2, OT>(a, sp, R, s);
+  if (attn_waves(a, sp) == 8) return launch_pairs<8, OT>(a, sp, R, s);
+  // Too few workgroups to share compute units: a three-deep ring keeps two gathers in flight per
+  // workgroup. Otherwise a two-deep ring lets two workgroups share a compute unit.
+  if (R * sp.n_splits * (a.H / (kHPW * 4)) < 256) return launch_mfma<4, 3, OT>(a, sp, R, s);
+  return launch_mfma<4, 2, OT>(a, sp, R, s);
 }
 
 }  // namespace
