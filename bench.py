@@ -10,12 +10,16 @@ timed region starts. Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload chunk1m] [--no-decode] [--no-cpu-baseline]
     python bench.py --copy-probe      # a plain 1 GiB device copy, for counter calibration
     python bench.py --pmc-summary DIR # HBM bytes of the indexer kernel from rocprofv3 --pmc runs
+    python bench.py --mfma-summary DIR  # matrix-core busy share of the prefill kernels (one --pmc run)
 
 Counter runs (repository root; from /tmp with TMPDIR=/tmp), each in a process of its own:
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- python3 bench.py --steps 2 \
         --warmup 1 --no-decode --no-cpu-baseline
     (the same with WRITE_SIZE into DIR/write, and both counters of --copy-probe into
     DIR/copy_fetch and DIR/copy_write), then --pmc-summary DIR writes profiles/*_pmc.json and .md.
+    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d DIR/mfma -o run \
+        -- python3 bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline
+    then --mfma-summary DIR writes profiles/mfma_busy_<workload>.md.
 """
 from __future__ import annotations
 
@@ -166,6 +170,37 @@ def pmc_summary(pmc_dir, workload):
     print(json.dumps(d))
 
 
+def mfma_summary(pmc_dir, workload):
+    """Share of cycles in which the matrix cores were busy, per prefill kernel, from one rocprofv3
+    --pmc run with SQ_VALU_MFMA_BUSY_CYCLES (summed over all SIMDs) and GRBM_GUI_ACTIVE (summed over
+    the 8 XCDs). Writes profiles/mfma_busy_<workload>.md."""
+    path = os.path.join(pmc_dir, "mfma", "run_counter_collection.csv")
+    busy = _counter_rows(path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _counter_rows(path, "GRBM_GUI_ACTIVE")
+    simds, xcds = 256 * 4, 8
+    rows = []
+    for label, key in (("index_prefill_mfma", "index_prefill_mfma"), ("attn_pairs", "attn_pairs"),
+                       ("attn_mfma", "attn_mfma<"), ("projection (hipBLASLt)", "Cijk_")):
+        b = [v for n, v in busy if key in n]
+        g = [v for n, v in gui if key in n]
+        if not b or len(b) != len(g):
+            continue
+        share = [100.0 * bb / (gg / xcds * simds) for bb, gg in zip(b, g)]
+        rows.append((label, len(b), float(np.median(share)), float(np.median(g)) / xcds))
+    bench_cmd = ("python3 /root/repo/bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline --workload " + workload)
+    cmds = [f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d <out>/mfma -o run -- {bench_cmd}",
+            f"python3 /root/repo/bench.py --mfma-summary <out> --workload {workload}"]
+    with open(os.path.join(ROOT, "profiles", f"mfma_busy_{workload}.md"), "w") as f:
+        f.write(f"# Matrix-core busy share of the prefill kernels, {workload}\n\n")
+        f.write("Commands (repository root, run from /tmp with TMPDIR=/tmp):\n\n```\n" + "\n".join(cmds) + "\n```\n\n")
+        f.write("busy share = SQ_VALU_MFMA_BUSY_CYCLES (all SIMDs) / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs), "
+                "median over the dispatches\n\n")
+        f.write("| kernel | dispatches | MFMA busy | GPU cycles per dispatch (one XCD) |\n|---|---|---|---|\n")
+        for label, n, share, cyc in rows:
+            f.write(f"| {label} | {n} | {share:.1f}% | {cyc:.4g} |\n")
+    print(json.dumps({"workload": workload, "mfma_busy_percent": {r[0]: round(r[2], 1) for r in rows}}))
+
+
 def cpu_baseline(wl, inp):
     """The oracle, as it stands, on a bounded sample of the workload: the per-chunk work (projection
     of the compressor and window columns, both compressors) plus 4 and then 12 query rows; per-row
@@ -302,7 +337,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise four rocprofv3 --pmc runs under DIR")
+    ap.add_argument("--mfma-summary", metavar="DIR", help="summarise one rocprofv3 --pmc run of the MFMA busy counter")
     args = ap.parse_args()
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary, args.workload)
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.workload)
         return
