@@ -35,6 +35,10 @@ Readings where the pages are silent (each is listed with its reason in the desig
   scale 1/sqrt(D); top-k ties break toward the smaller entry index; fewer than k visible entries
   means all of them are kept and the index list is padded with -1.
 
+HCA ([ANAT] bullet "Heavily Compressed Attention (HCA)"): hca_compress pools each block of m = 128
+tokens with no overlap (reading: the CSA pooling over the entry's own block); dense_attention
+attends to every visible entry plus the window.
+
 Parity status: every function here is pinned by the CPU tests (closed forms, invariants, a dense
 attention routine, hand-worked examples, the MXFP4 table of the OCP spec). What the pages leave open
 (the readings above) cannot be pinned against DeepSeek's own layer: that part is parity unpinned.
@@ -244,6 +248,50 @@ def sparse_attention(q, entries, idx, raw, raw_pos0: int, q_pos, W: int, scale=N
             den = den + np.exp(np.asarray(sink, dtype=np.float64) - mx)
         out[t] = (ex @ keys) / den[:, None]
     return out
+
+
+def hca_compress(c, z, bias, m: int, first_entry: int = 0):
+    """HCA compressor: one entry per complete block of m tokens (m = 128), without overlap.
+
+    [ANAT] bullet "Heavily Compressed Attention (HCA)": every 128 tokens become one entry, with no
+    overlap between entries. The pages name no other pooling, so the entry pools its own block with
+    the CSA compressor's per-channel softmax over learned position biases (one series):
+        logits  = { z[i*m + r, j] + bias[r, j] : r < m }
+        E[i, j] = sum_r softmax(logits)[r] * c[i*m + r, j]
+    c, z: [T, c] rows of this call, whose first token is the first token of block `first_entry`.
+    Only complete blocks produce entries: floor(T / m) of them. Returns entries [n, c].
+    """
+    c = np.asarray(c, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    T, ch = c.shape
+    n = T // m
+    entries = np.zeros((n, ch))
+    for e in range(n):
+        own = slice(e * m, (e + 1) * m)
+        logits = z[own] + bias                                 # [m, c]
+        ex = np.exp(logits - logits.max(axis=0, keepdims=True))
+        entries[e] = (ex / ex.sum(axis=0, keepdims=True) * c[own]).sum(axis=0)
+    return entries
+
+
+def dense_attention(q, entries, raw, raw_pos0: int, q_pos, m: int, W: int, scale=None, sink=None):
+    """HCA attention: every visible entry plus the raw-token window, one softmax.
+
+    [ANAT] bullet "Heavily Compressed Attention (HCA)": queries attend to all entries densely;
+    bullet "A sliding window in every layer"; bullet "An attention sink". It is sparse_attention
+    with the selection replaced by every entry visible at p: idx[t] = 0 .. n_vis(p_t) - 1 (capped at
+    the entries given).
+    """
+    entries = np.asarray(entries, dtype=np.float64)
+    N = entries.shape[0]
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    nv = np.minimum(n_visible(q_pos, m), N)
+    width = int(max(nv.max(initial=0), 1))
+    idx = np.full((len(q_pos), width), -1, dtype=np.int64)
+    for t, n in enumerate(nv):
+        idx[t, :n] = np.arange(n)
+    return sparse_attention(q, entries, idx, raw, raw_pos0, q_pos, W, scale=scale, sink=sink)
 
 
 # --------------------------------------------------------------------------------------------------

@@ -181,6 +181,55 @@ def test_compress_single_series_special_case():
         np.testing.assert_allclose(e[i], (w * cc[rows]).sum(axis=0), atol=1e-12)
 
 
+def test_hca_compress_closed_forms():
+    # [ANAT] bullet "HCA": one entry per block of m tokens, no overlap
+    rng = np.random.default_rng(40)
+    T, c, m = 3 * 128 + 50, 6, 128
+    cc, zz = _rand(rng, T, c), _rand(rng, T, c) * 4
+    bias = _rand(rng, m, c)
+    e = O.hca_compress(cc, zz, bias, m)
+    assert e.shape == (3, c)                                   # the tail block produces nothing
+    z0 = np.zeros((T, c))
+    np.testing.assert_allclose(O.hca_compress(cc, z0, np.zeros((m, c)), m),
+                               cc[:3 * m].reshape(3, m, c).mean(axis=1), atol=1e-12)
+    hot = np.zeros((m, c))
+    hot[77] = 1e4
+    np.testing.assert_allclose(O.hca_compress(cc, zz, hot, m), cc[77:3 * m:m], atol=1e-9)
+    const = np.tile(np.linspace(-3, 3, c), (T, 1))
+    np.testing.assert_allclose(O.hca_compress(const, zz, bias, m), const[:3], atol=1e-12)
+    # entries are convex combinations of their own block only
+    for i in range(3):
+        blk = cc[i * m:(i + 1) * m]
+        assert np.all(e[i] <= blk.max(axis=0) + 1e-12) and np.all(e[i] >= blk.min(axis=0) - 1e-12)
+
+
+def test_dense_attention_equals_sdpa_with_causal_entries_and_window():
+    rng = np.random.default_rng(41)
+    T, H, D, m, W, p0 = 29, 3, 8, 4, 6, 40
+    N = (p0 + T) // m
+    q = _rand(rng, T, H, D)
+    ent = _rand(rng, N, D)
+    raw = _rand(rng, p0 + T, D)
+    q_pos = p0 + np.arange(T)
+    sink = rng.standard_normal(H)
+    o = O.dense_attention(q, ent, raw, 0, q_pos, m, W, sink=sink)
+    nv = O.n_visible(q_pos, m)
+    keys = torch.from_numpy(np.concatenate([ent, raw, np.zeros((1, D))], axis=0))   # + sink slot
+    L = keys.shape[0]
+    mask = torch.zeros(T, L, dtype=torch.bool)
+    for t in range(T):
+        p = int(q_pos[t])
+        mask[t, :nv[t]] = True
+        mask[t, N + max(0, p - W + 1):N + p + 1] = True
+    mask[:, L - 1] = True
+    scale = 1.0 / np.sqrt(D)
+    logits = torch.einsum("thd,ld->htl", torch.from_numpy(q), keys) * scale
+    logits[:, :, L - 1] = torch.from_numpy(sink)[:, None]           # the sink's logit, value row 0
+    logits = logits.masked_fill(~mask.unsqueeze(0), float("-inf"))
+    ref = torch.softmax(logits, dim=-1) @ keys                          # [H, T, D]
+    np.testing.assert_allclose(o, ref.permute(1, 0, 2).numpy(), atol=1e-12)
+
+
 # ---------------------------------------------------------------------------------- indexer
 
 
