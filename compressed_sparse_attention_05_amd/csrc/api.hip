@@ -89,11 +89,13 @@ using namespace csa;
 
 namespace {
 
-int check_dims(const csa_dims* d) {
+// uses_topk = false: the dense (HCA) attention, which ignores top_k
+int check_dims(const csa_dims* d, bool uses_topk = true) {
   if (!d) return fail(CSA_ERR_ARG, "dims is NULL");
   if (d->m < 1 || d->m > compress_max_m()) return fail(CSA_ERR_ARG, "m=%d out of [1, %d]", d->m, compress_max_m());
   if (d->D < 1 || d->H < 1 || d->H_I < 1 || d->D_I < 1) return fail(CSA_ERR_ARG, "dims must be positive");
-  if (d->top_k < 1 || d->top_k > kMaxTopK) return fail(CSA_ERR_ARG, "top_k=%d out of [1, %d]", d->top_k, kMaxTopK);
+  if (uses_topk && (d->top_k < 1 || d->top_k > kMaxTopK))
+    return fail(CSA_ERR_ARG, "top_k=%d out of [1, %d]", d->top_k, kMaxTopK);
   if (d->window < 1) return fail(CSA_ERR_ARG, "window=%d must be >= 1", d->window);
   if (!(d->sm_scale >= 0.f) || std::isinf(d->sm_scale)) return fail(CSA_ERR_ARG, "sm_scale must be finite and >= 0");
   return CSA_OK;
@@ -199,6 +201,66 @@ int validate_index(const csa_dims* d, int B, int T, int64_t q_pos0, int idx_dtyp
   return CSA_OK;
 }
 
+int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+              const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride,
+              int64_t n_cap, const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+              int64_t raw_pos0, int64_t raw_len, const float* sink, void* out, int out_dtype, void* ws,
+              size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims, !dense);
+  if (rc) return rc;
+  if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
+  if (!is_act_dtype(in_dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
+  if (q_pos0 < 0 || n_cap < 0 || raw_len < 0) return fail(CSA_ERR_ARG, "negative position or size");
+  if (dims->D > 1024) return fail(CSA_ERR_UNSUPPORTED, "D > 1024");
+  if ((int64_t)B * T == 0) return CSA_OK;
+  if (!q || (!dense && !idx) || !kv_raw || !out || (!entries && n_cap > 0))
+    return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  const int64_t H = dims->H, D = dims->D;
+  if (q_ld < H * D) return fail(CSA_ERR_ARG, "q_ld < H*D");
+  if (B > 1 && q_seq_stride < (int64_t)T * q_ld) return fail(CSA_ERR_ARG, "q_seq_stride too small");
+  if (B > 1 && entries_seq_stride < n_cap * D) return fail(CSA_ERR_ARG, "entries_seq_stride too small");
+  if (raw_ld < D) return fail(CSA_ERR_ARG, "raw_ld < D");
+  if (B > 1 && raw_seq_stride < raw_len * raw_ld) return fail(CSA_ERR_ARG, "raw_seq_stride too small");
+  const int64_t need_lo = q_pos0 - dims->window + 1 > 0 ? q_pos0 - dims->window + 1 : 0;
+  const int64_t need_hi = q_pos0 + T - 1;
+  if (raw_pos0 > need_lo || raw_pos0 + raw_len - 1 < need_hi)
+    return fail(CSA_ERR_ARG, "kv_raw rows [%lld, %lld] do not cover the windows [%lld, %lld]", (long long)raw_pos0,
+                (long long)(raw_pos0 + raw_len - 1), (long long)need_lo, (long long)need_hi);
+  const size_t al = esize(in_dtype) == 2 ? 16 : 4;
+  if (!aligned(q, al) || !aligned(kv_raw, al) || (entries && !aligned(entries, al)))
+    return fail(CSA_ERR_ARG, "misaligned q / entries / kv_raw");
+  AttnArgs a{};
+  a.B = B;
+  a.T = T;
+  a.q_pos0 = q_pos0;
+  a.H = dims->H;
+  a.D = dims->D;
+  a.k = dense ? 0 : dims->top_k;
+  a.W = dims->window;
+  a.scale = scale_of(dims);
+  a.dense = dense ? 1 : 0;
+  a.m = dims->m;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.q_ld = q_ld;
+  a.q_seq_stride = q_seq_stride;
+  a.entries = entries;
+  a.entries_seq_stride = entries_seq_stride;
+  a.n_cap = n_cap;
+  a.idx = idx;
+  a.raw = kv_raw;
+  a.raw_ld = raw_ld;
+  a.raw_seq_stride = raw_seq_stride;
+  a.raw_pos0 = raw_pos0;
+  a.raw_len = raw_len;
+  a.sink = sink;
+  a.out = out;
+  rc = check_ws(ws, ws_bytes, attn_workspace(a));
+  if (rc) return rc;
+  return hip_status(launch_attn(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,6 +281,18 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
       int rc = check_dims(dims);
       if (rc) return rc;
       *bytes = (int64_t)attn_workspace(sizing_attn(dims, B, T, idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16));
+      return CSA_OK;
+    }
+    case CSA_OP_DENSE_ATTN: {
+      int rc = check_dims(dims, false);
+      if (rc) return rc;
+      AttnArgs a = sizing_attn(dims, B, T, idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16);
+      a.dense = 1;
+      a.m = dims->m;
+      a.k = 0;
+      a.n_cap = n_cap;
+      a.q_pos0 = n_cap * dims->m;  // every entry visible: the most keys a row can have
+      *bytes = (int64_t)attn_workspace(a);
       return CSA_OK;
     }
     case CSA_OP_TOPK_FROM_SCORES: {
@@ -300,6 +374,50 @@ int csa_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype, const v
   return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)), "csa_compress");
 }
 
+int csa_hca_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype, const void* cv, const void* z,
+                     int64_t ld, int64_t seq_stride, const float* bias, void* entries, int64_t entries_seq_stride,
+                     int64_t n_cap, int out_dtype, void* stream) {
+  if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
+  if (m < 1 || m > compress_max_m()) return fail(CSA_ERR_ARG, "m=%d out of [1, %d]", m, compress_max_m());
+  if (c < 1) return fail(CSA_ERR_ARG, "c must be >= 1");
+  if (!is_act_dtype(in_dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
+  if (pos0 < 0 || pos0 % m) return fail(CSA_ERR_ARG, "pos0=%lld must be a non-negative multiple of m", (long long)pos0);
+  const int n_new = T / m;
+  if (B == 0 || n_new == 0) return CSA_OK;
+  const int64_t first = pos0 / m;
+  if (first + n_new > n_cap) return fail(CSA_ERR_ARG, "entries rows %lld..%lld exceed n_cap=%lld", (long long)first,
+                                         (long long)(first + n_new - 1), (long long)n_cap);
+  if (!cv || !z || !bias || !entries) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  if (ld < c) return fail(CSA_ERR_ARG, "ld=%lld < c=%d", (long long)ld, c);
+  if (B > 1 && seq_stride < (int64_t)T * ld) return fail(CSA_ERR_ARG, "seq_stride too small");
+  if (B > 1 && entries_seq_stride < n_cap * c) return fail(CSA_ERR_ARG, "entries_seq_stride too small");
+  CompressArgs a{};
+  a.B = B;
+  a.n_new = n_new;
+  a.m = m;
+  a.c = c;
+  a.first_entry = first;
+  a.in_dtype = in_dtype;
+  a.out_dtype = out_dtype;
+  a.ca = cv;
+  a.za = z;
+  a.cb = cv;  // series b is not read without overlap
+  a.zb = z;
+  a.ld = ld;
+  a.seq_stride = seq_stride;
+  a.halo_cb = cv;
+  a.halo_zb = z;
+  a.halo_ld = ld;
+  a.halo_seq_stride = seq_stride;
+  a.bias_a = bias;
+  a.bias_b = bias;
+  a.entries = entries;
+  a.entries_seq_stride = entries_seq_stride;
+  a.aligned16 = aligned(cv, 16) && aligned(z, 16) && aligned(entries, 16);
+  a.overlap = false;
+  return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)), "csa_hca_compress");
+}
+
 int csa_index_topk(const csa_dims* dims, int B, int T, int64_t q_pos0, int idx_dtype, const void* q_idx, int64_t q_ld,
                    int64_t q_seq_stride, const void* q_scale, const float* w, int64_t w_ld, const void* keys,
                    int64_t keys_seq_stride, const void* k_scale, int64_t n_cap, int32_t* out_idx, float* out_score,
@@ -328,61 +446,24 @@ int csa_topk_from_scores(const float* scores, int64_t ld, const int32_t* n_valid
   return hip_status(launch_topk_from_scores(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), "csa_topk_from_scores");
 }
 
+
 int csa_sparse_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype, const void* q, int64_t q_ld,
                     int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride, int64_t n_cap,
                     const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
                     int64_t raw_len, const float* sink, void* out, int out_dtype, void* ws, size_t ws_bytes,
                     void* stream) {
-  int rc = check_dims(dims);
-  if (rc) return rc;
-  if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
-  if (!is_act_dtype(in_dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
-  if (q_pos0 < 0 || n_cap < 0 || raw_len < 0) return fail(CSA_ERR_ARG, "negative position or size");
-  if (dims->D > 1024) return fail(CSA_ERR_UNSUPPORTED, "D > 1024");
-  if ((int64_t)B * T == 0) return CSA_OK;
-  if (!q || !idx || !kv_raw || !out || (!entries && n_cap > 0)) return fail(CSA_ERR_ARG, "NULL tensor pointer");
-  const int64_t H = dims->H, D = dims->D;
-  if (q_ld < H * D) return fail(CSA_ERR_ARG, "q_ld < H*D");
-  if (B > 1 && q_seq_stride < (int64_t)T * q_ld) return fail(CSA_ERR_ARG, "q_seq_stride too small");
-  if (B > 1 && entries_seq_stride < n_cap * D) return fail(CSA_ERR_ARG, "entries_seq_stride too small");
-  if (raw_ld < D) return fail(CSA_ERR_ARG, "raw_ld < D");
-  if (B > 1 && raw_seq_stride < raw_len * raw_ld) return fail(CSA_ERR_ARG, "raw_seq_stride too small");
-  const int64_t need_lo = q_pos0 - dims->window + 1 > 0 ? q_pos0 - dims->window + 1 : 0;
-  const int64_t need_hi = q_pos0 + T - 1;
-  if (raw_pos0 > need_lo || raw_pos0 + raw_len - 1 < need_hi)
-    return fail(CSA_ERR_ARG, "kv_raw rows [%lld, %lld] do not cover the windows [%lld, %lld]", (long long)raw_pos0,
-                (long long)(raw_pos0 + raw_len - 1), (long long)need_lo, (long long)need_hi);
-  const size_t al = esize(in_dtype) == 2 ? 16 : 4;
-  if (!aligned(q, al) || !aligned(kv_raw, al) || (entries && !aligned(entries, al)))
-    return fail(CSA_ERR_ARG, "misaligned q / entries / kv_raw");
-  AttnArgs a{};
-  a.B = B;
-  a.T = T;
-  a.q_pos0 = q_pos0;
-  a.H = dims->H;
-  a.D = dims->D;
-  a.k = dims->top_k;
-  a.W = dims->window;
-  a.scale = scale_of(dims);
-  a.in_dtype = in_dtype;
-  a.out_dtype = out_dtype;
-  a.q = q;
-  a.q_ld = q_ld;
-  a.q_seq_stride = q_seq_stride;
-  a.entries = entries;
-  a.entries_seq_stride = entries_seq_stride;
-  a.n_cap = n_cap;
-  a.idx = idx;
-  a.raw = kv_raw;
-  a.raw_ld = raw_ld;
-  a.raw_seq_stride = raw_seq_stride;
-  a.raw_pos0 = raw_pos0;
-  a.raw_len = raw_len;
-  a.sink = sink;
-  a.out = out;
-  rc = check_ws(ws, ws_bytes, attn_workspace(a));
-  if (rc) return rc;
-  return hip_status(launch_attn(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), "csa_sparse_attn");
+  return attn_call("csa_sparse_attn", false, dims, B, T, q_pos0, in_dtype, q, q_ld, q_seq_stride, entries,
+                   entries_seq_stride, n_cap, idx, kv_raw, raw_ld, raw_seq_stride, raw_pos0, raw_len, sink, out,
+                   out_dtype, ws, ws_bytes, stream);
+}
+
+int csa_dense_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype, const void* q, int64_t q_ld,
+                   int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride, int64_t n_cap,
+                   const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0, int64_t raw_len,
+                   const float* sink, void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  return attn_call("csa_dense_attn", true, dims, B, T, q_pos0, in_dtype, q, q_ld, q_seq_stride, entries,
+                   entries_seq_stride, n_cap, nullptr, kv_raw, raw_ld, raw_seq_stride, raw_pos0, raw_len, sink, out,
+                   out_dtype, ws, ws_bytes, stream);
 }
 
 int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_t pos0, int d_model, int dtype,

@@ -31,6 +31,11 @@ __device__ __forceinline__ int64_t window_hi(const AttnArgs& a, int64_t p) {
   if (hi > a.raw_pos0 + a.raw_len - 1) hi = a.raw_pos0 + a.raw_len - 1;
   return hi;
 }
+// dense mode: the entries visible to position p, min(floor((p+1)/m), n_cap)
+__host__ __device__ __forceinline__ int64_t dense_visible(const AttnArgs& a, int64_t p) {
+  const int64_t n = (p + 1) / a.m;
+  return n < a.n_cap ? n : a.n_cap;
+}
 
 // ---------------------------------------------------------------- generic
 
@@ -43,7 +48,7 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
   const int b = (int)(row / a.T), t = (int)(row % a.T);
   const int64_t p = a.q_pos0 + t;
   const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
-  const int32_t* idx = a.idx + row * a.k;
+  const int32_t* idx = a.dense ? nullptr : a.idx + row * a.k;
   constexpr int kMaxPer = 16;  // dims per lane (D <= 1024)
   const int per = (a.D + 63) / 64;
   for (int h = wave; h < a.H; h += kGenWaves) {
@@ -59,13 +64,13 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
       mx = a.sink[h];
       den = 1.f;
     }
-    const int64_t nsel = a.k;
+    const int64_t nsel = a.dense ? dense_visible(a, p) : a.k;
     const int64_t nwin = whi >= wlo ? whi - wlo + 1 : 0;
     for (int64_t j = 0; j < nsel + nwin; ++j) {
       int64_t off;
       const void* src;
       if (j < nsel) {
-        const int32_t e = idx[j];
+        const int32_t e = a.dense ? (int32_t)j : idx[j];
         if (e < 0 || e >= a.n_cap) continue;
         src = a.entries;
         off = (int64_t)b * a.entries_seq_stride + (int64_t)e * a.D;
@@ -179,8 +184,14 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
   for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 32);
 
   // ---- key list: valid selected entries, then the window rows. All threads load their indices in
-  // one burst (one memory latency, not one per 64 indices) and the waves compact them in order.
-  {
+  // one burst (one memory latency, not one per 64 indices) and the waves compact them in order. In
+  // dense mode the list is every visible entry in order, then the window: ids follow from the
+  // position and nothing is stored.
+  const int64_t nvis_d = a.dense ? dense_visible(a, p) : 0;
+  auto key_id = [&](int kj) -> int32_t {
+    return kj < nvis_d ? kj : -(int32_t)(wlo - a.raw_pos0 + (kj - nvis_d)) - 1;
+  };
+  if (!a.dense) {
     const int32_t* idx = a.idx + row * a.k;
     int nsel = 0;
     for (int base = 0; base < a.k; base += 4 * kThreads) {
@@ -212,9 +223,9 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
     for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
     if (threadIdx.x == 0) sm.keys[a.k + a.W] = nsel + nwin;
+    __syncthreads();
   }
-  __syncthreads();
-  const int nkeys = sm.keys[a.k + a.W];
+  const int nkeys = a.dense ? (int)nvis_d + (whi >= wlo ? (int)(whi - wlo + 1) : 0) : sm.keys[a.k + a.W];
   const int kbeg = split * sp.split_keys;
   const int kend = kbeg + sp.split_keys < nkeys ? kbeg + sp.split_keys : nkeys;
   const int ntiles = __builtin_amdgcn_readfirstlane(kend > kbeg ? (kend - kbeg + kNK - 1) / kNK : 0);
@@ -241,7 +252,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
       const int r = j * NW + wave;
       int kj = kbeg + tile * kNK + r;
       kj = kj < kend ? kj : kend - 1;
-      const int32_t id = __builtin_amdgcn_readfirstlane(sm.keys[kj]);
+      const int32_t id = __builtin_amdgcn_readfirstlane(a.dense ? key_id(kj) : sm.keys[kj]);
       const uint16_t* krow = id >= 0 ? ent + (int64_t)id * 512 : raw + (int64_t)(-id - 1) * a.raw_ld;
       copy_to_lds16(krow + lane * 8,
                     __builtin_amdgcn_readfirstlane(ring + (uint32_t)((buf * kNK + r) * kKNS * 2)));
@@ -489,8 +500,14 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 16);
   };
 
-  // ---- key list (valid selected entries, then the window rows), compacted in order
-  {
+  // ---- key list (valid selected entries, then the window rows), compacted in order; in dense
+  // mode every visible entry in order, then the window, with ids from the position
+  const int64_t nvis_d = a.dense ? dense_visible(a, p) : 0;
+  auto key_id = [&](int kj) -> int32_t {
+    return kj < nvis_d ? kj : -(int32_t)(wlo - a.raw_pos0 + (kj - nvis_d)) - 1;
+  };
+  if (a.dense) load_q();
+  else {
     const int32_t* idx = a.idx + row * a.k;
     int nsel = 0;
     if (a.k <= 0) load_q();
@@ -524,9 +541,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
     for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
     if (threadIdx.x == 0) sm.keys[a.k + a.W] = nsel + nwin;
+    __syncthreads();
   }
-  __syncthreads();
-  const int nkeys = sm.keys[a.k + a.W];
+  const int nkeys = a.dense ? (int)nvis_d + (whi >= wlo ? (int)(whi - wlo + 1) : 0) : sm.keys[a.k + a.W];
   const int kbeg = split * sp.split_keys;
   const int kend = kbeg + sp.split_keys < nkeys ? kbeg + sp.split_keys : nkeys;
   const int ntiles = __builtin_amdgcn_readfirstlane(kend > kbeg ? (kend - kbeg + kNK - 1) / kNK : 0);
@@ -551,7 +568,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   auto load_tile = [&](int tile, int buf) {
     int kl = kbeg + tile * kNK + (lane & 31);
     kl = kl < kend ? kl : kend - 1;
-    const int32_t id = sm.keys[kl];
+    const int32_t id = a.dense ? key_id(kl) : sm.keys[kl];
     // row address of row l%32, computed on the vector unit without branches
     const uint64_t ra = id >= 0 ? (uint64_t)(ent + (int64_t)id * 512) : (uint64_t)(raw + (int64_t)(-id - 1) * a.raw_ld);
 #pragma unroll
@@ -797,9 +814,12 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
 
 // LDS of the deepest variant (8 waves, three-deep ring); the 4-wave variant uses a two-deep ring
 // so that two workgroups share a compute unit
+// LDS of the compacted key list (dense mode stores none)
+size_t attn_keys_lds(const AttnArgs& a) { return a.dense ? 4 : (size_t)(a.k + a.W + 1) * 4; }
+
 int attn_mfma_lds(const AttnArgs& a) {
   const size_t deepest = sizeof(AttnSmem<3>) > sizeof(PairSmem<8>) ? sizeof(AttnSmem<3>) : sizeof(PairSmem<8>);
-  return (int)(deepest + (size_t)(a.k + a.W + 1) * 4);
+  return (int)(deepest + attn_keys_lds(a));
 }
 
 bool use_attn_mfma(const AttnArgs& a) {
@@ -810,15 +830,23 @@ bool use_attn_mfma(const AttnArgs& a) {
 
 constexpr int kDecodeRows = 8;     // fewer query rows per sequence than this: decode regime
 constexpr int kSplitKeys = 288;    // keys per split in the decode regime (9 tiles: 1152 keys in 4)
+constexpr int kDenseSplitKeys = 1024;  // dense mode (thousands of keys per row): 32 tiles per split
+
+// most keys any query row of the call can have
+int64_t attn_max_keys(const AttnArgs& a) {
+  if (!a.dense) return (int64_t)a.k + a.W;
+  return dense_visible(a, a.q_pos0 + a.T - 1) + a.W;
+}
 
 AttnSplit plan_split(const AttnArgs& a) {
-  AttnSplit sp{1, a.k + a.W, nullptr, nullptr};
+  const int64_t maxkeys = attn_max_keys(a);
+  AttnSplit sp{1, (int)maxkeys, nullptr, nullptr};
   if (!use_attn_mfma(a) || a.T >= kDecodeRows) return sp;
-  const int maxkeys = a.k + a.W;
-  const int S = (int)ceil_div(maxkeys, kSplitKeys);
+  const int split = a.dense ? kDenseSplitKeys : kSplitKeys;
+  const int S = (int)ceil_div(maxkeys, split);
   if (S <= 1) return sp;
   sp.n_splits = S;
-  sp.split_keys = kSplitKeys;
+  sp.split_keys = split;
   return sp;
 }
 
@@ -826,7 +854,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <int NW, int RING, int OT>
 hipError_t launch_mfma(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
-  const int lds = (int)(sizeof(AttnSmem<RING>) + (size_t)(a.k + a.W + 1) * 4);
+  const int lds = (int)(sizeof(AttnSmem<RING>) + attn_keys_lds(a));
   hipError_t e;
   if ((e = allow_lds((const void*)attn_mfma<NW, RING, OT>, lds)) != hipSuccess) return e;
   const int64_t n_hg = a.H / (kHPW * NW);
@@ -846,7 +874,7 @@ int attn_waves(const AttnArgs& a, const AttnSplit& sp) {
 
 template <int NW, int OT>
 hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
-  const int lds = (int)(sizeof(PairSmem<NW>) + (size_t)(a.k + a.W + 1) * 4);
+  const int lds = (int)(sizeof(PairSmem<NW>) + attn_keys_lds(a));
   hipError_t e;
   if ((e = allow_lds((const void*)attn_pairs<NW, OT>, lds)) != hipSuccess) return e;
   const int64_t n_hg = a.H / (16 * NW);

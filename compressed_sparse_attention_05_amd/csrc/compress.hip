@@ -3,7 +3,9 @@
 // One entry per complete block of m tokens, per channel a softmax over the 2m logits of the
 // entry's own block (series a) and the previous block (series b), then the weighted sum of the
 // matching values ("The Exchange Rates of a Million Tokens", section 3; "Anatomy of a Frontier
-// Model", bullet "Compressed Sparse Attention (CSA)").
+// Model", bullet "Compressed Sparse Attention (CSA)"). The HCA compressor ("Anatomy of a Frontier
+// Model", bullet "Heavily Compressed Attention (HCA)": blocks of 128 tokens, no overlap) is the
+// same pooling over the own block only (overlap = false).
 //
 // The step is HBM-bound and reads every input element exactly once: entry i reads block i of
 // series a and block i-1 of series b, so no row is shared between entries and no LDS staging is
@@ -56,7 +58,7 @@ struct Scalar {
   __device__ static void store(void* p, int64_t off, const float* v) { store_elem<DT>(p, off, v[0]); }
 };
 
-constexpr int kMaxM = 64;
+constexpr int kMaxM = 128;
 
 // Softmax-weighted sum accumulated online per channel: running maximum mx, denominator den and
 // numerator num; each logit rescales the running sums when it raises the maximum.
@@ -105,8 +107,8 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     for (int v = 0; v < V; ++v) bias[v] = a.bias_a[r * a.c + j0 + v];
     accumulate<V>(z, bias, c, mx, den, num);
   }
-  // previous block, series b (entry 0 has none)
-  if (i >= 1) {
+  // previous block, series b (entry 0 has none; HCA pools its own block only)
+  if (a.overlap && i >= 1) {
     for (int r = 0; r < m; ++r) {
       const void* cb;
       const void* zb;

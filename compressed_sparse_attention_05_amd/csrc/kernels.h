@@ -17,6 +17,7 @@ struct CompressArgs {
   void* entries;
   int64_t entries_seq_stride;
   bool aligned16;
+  bool overlap = true;  // pool the previous block too (CSA); false: own block only (HCA)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 int compress_max_m();
@@ -94,6 +95,8 @@ struct AttnArgs {
   int64_t raw_ld, raw_seq_stride, raw_pos0, raw_len;
   const float* sink;
   void* out;
+  int dense = 0;  // attend to every visible entry in order (HCA); idx is not read and k is unused
+  int m = 1;      // tokens per entry (dense only: entry i is visible to p iff (i+1)*m - 1 <= p)
 };
 size_t attn_workspace(const AttnArgs& a);
 hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);

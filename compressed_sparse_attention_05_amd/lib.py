@@ -15,9 +15,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_MXFP4 = 0, 1, 2
-CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD = range(5)
+CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD, CSA_OP_DENSE_ATTN = \
+    range(6)
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
-           "csa_topk_from_scores", "csa_sparse_attn", "csa_forward")
+           "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn")
 
 
 class CsaError(RuntimeError):
@@ -68,8 +69,11 @@ def load() -> ctypes.CDLL:
                                     i64, i64, i64, i64, vp, vp, i32, vp, sz, vp]
     lib.csa_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i32, i64, i32, i32, vp,
                                 ctypes.POINTER(Cache), vp, i32, vp, vp, sz, vp]
+    lib.csa_hca_compress.argtypes = [i32, i32, i64, i32, i32, i32, vp, vp, i64, i64, vp, vp, i64, i64, i32, vp]
+    lib.csa_dense_attn.argtypes = [ctypes.POINTER(Dims), i32, i32, i64, i32, vp, i64, i64, vp, i64, i64, vp,
+                                   i64, i64, i64, i64, vp, vp, i32, vp, sz, vp]
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
-              "csa_forward"):
+              "csa_forward", "csa_hca_compress", "csa_dense_attn"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -219,6 +223,39 @@ def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, ra
                                   _p(entries), entries.stride(0), entries.shape[1], _p(idx), _p(kv_raw),
                                   kv_raw.stride(1), kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out),
                                   _dt(out), wp, wn, _stream()))
+    return out
+
+
+def csa_hca_compress(cv, z, bias, entries, *, pos0: int, m: int):
+    """HCA compressor. cv, z: [B, T, c] views sharing strides; bias float32 [m, c]; entries [B, n_cap, c]."""
+    _require_cuda(cv, z, bias, entries)
+    B, T, c = cv.shape
+    if z.shape != cv.shape or z.stride() != cv.stride():
+        raise ValueError("cv and z must share shape and strides")
+    if cv.stride(2) != 1 or entries.stride(2) != 1 or entries.stride(1) != c:
+        raise ValueError("channel axes must be contiguous")
+    _check(load().csa_hca_compress(B, T, pos0, m, c, _dt(cv), _p(cv), _p(z), cv.stride(1), cv.stride(0), _p(bias),
+                                   _p(entries), entries.stride(0), entries.shape[1], _dt(entries), _stream()))
+    return entries
+
+
+def csa_dense_attn(dims: Dims, q, entries, kv_raw, out, *, q_pos0: int, raw_pos0: int, sink=None, ws=None):
+    """HCA attention over every visible entry plus the window. q [B, T, H, D]; entries [B, n_cap, D];
+    kv_raw [B, R, D] whose row r is position raw_pos0 + r; out [B, T, H, D] (float32 or bfloat16)."""
+    _require_cuda(q, entries, kv_raw, out, sink)
+    B, T = q.shape[0], q.shape[1]
+    if q.stride(3) != 1 or q.stride(2) != dims.D or entries.stride(2) != 1 or entries.stride(1) != dims.D:
+        raise ValueError("q heads and entry rows must be contiguous")
+    if kv_raw.stride(2) != 1 or not out.is_contiguous():
+        raise ValueError("kv_raw rows and out must be contiguous")
+    need = csa_workspace_size(CSA_OP_DENSE_ATTN, dims, B, T, entries.shape[1], 0, _dt(q))
+    if ws is None or ws.numel() < need + 256:
+        ws = _workspace(need, q.device)
+    wp, wn = _aligned_ptr(ws)
+    _check(load().csa_dense_attn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
+                                 _p(entries), entries.stride(0), entries.shape[1], _p(kv_raw), kv_raw.stride(1),
+                                 kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out), _dt(out), wp, wn,
+                                 _stream()))
     return out
 
 

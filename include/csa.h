@@ -57,6 +57,7 @@ extern "C" {
 #define CSA_OP_TOPK_FROM_SCORES 2
 #define CSA_OP_SPARSE_ATTN 3
 #define CSA_OP_FORWARD 4
+#define CSA_OP_DENSE_ATTN 5  /* csa_dense_attn; n_cap bounds the entries a row can see */
 
 /* Layer dimensions. */
 typedef struct csa_dims {
@@ -106,6 +107,23 @@ int csa_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype,
                  const float* bias_a, const float* bias_b,
                  void* entries, int64_t entries_seq_stride, int64_t n_cap, int out_dtype,
                  void* stream);
+
+/*
+ * HCA compressor ("Anatomy of a Frontier Model", section "The attention: compress, then select",
+ * bullet "Heavily Compressed Attention (HCA)": every 128 tokens become one entry, without overlap).
+ * The pages name no other pooling; read as the CSA compressor's pooling over the entry's own block:
+ * for each complete block of this call (entry i = pos0/m + e, e < floor(T/m)) and channel j,
+ *   entries[i, j] = softmax_r(z[i*m+r, j] + bias[r, j]) . c[i*m+r, j]        (r < m)
+ *   c, z      [B, T, c] views: token stride `ld`, sequence stride `seq_stride`, channel stride 1;
+ *             dtype in_dtype (F32 or BF16).
+ *   bias      [m, c] float32.
+ *   entries   [B, n_cap, c] (row stride c, sequence stride entries_seq_stride), dtype out_dtype.
+ * Requires 1 <= m <= 128, pos0 % m == 0 and pos0/m + floor(T/m) <= n_cap; no halo is needed.
+ */
+int csa_hca_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype,
+                     const void* cv, const void* z, int64_t ld, int64_t seq_stride,
+                     const float* bias, void* entries, int64_t entries_seq_stride, int64_t n_cap,
+                     int out_dtype, void* stream);
 
 /*
  * Steps 2+3 — lightning indexer fused with top-k ("Anatomy of a Frontier Model", bullet
@@ -169,6 +187,23 @@ int csa_sparse_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_d
                     const float* sink,
                     void* out, int out_dtype,
                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * HCA attention ("Anatomy of a Frontier Model", bullet "Heavily Compressed Attention (HCA)":
+ * queries attend to all entries densely; bullets "A sliding window in every layer" and "An
+ * attention sink"): csa_sparse_attn with the selection replaced by every entry visible to the
+ * query, in order: S_t = { entries[i] : i < min(floor((p+1)/m), n_cap) } ++ the window rows.
+ * Arguments as csa_sparse_attn, without idx; dims->m is the HCA block (128) and dims->top_k is not
+ * used. Workspace: csa_workspace_size(CSA_OP_DENSE_ATTN, dims, B, T, n_cap, ...).
+ */
+int csa_dense_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+                   const void* q, int64_t q_ld, int64_t q_seq_stride,
+                   const void* entries, int64_t entries_seq_stride, int64_t n_cap,
+                   const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
+                   int64_t raw_len,
+                   const float* sink,
+                   void* out, int out_dtype,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /* Weights of one CSA layer (device pointers). */
 typedef struct csa_weights {
