@@ -327,6 +327,74 @@ def bench_decode(name, steps, warmup):
             "mall": "512 MiB read between steps, outside the timed events"}
 
 
+def bench_hca(steps, warmup):
+    """The HCA steps ("Heavily Compressed Attention": 128-token blocks without overlap, dense attention
+    over every visible entry plus the window) at 1M context: a 4096-token chunk after 1,044,480
+    tokens (compressor of the chunk's 32 blocks, dense attention of its 4096 rows over 8160-8191
+    entries) and decode of 16 sequences at 1,048,576 tokens (8192 entries each)."""
+    import torch
+    from compressed_sparse_attention_05_amd import lib
+    from synth import gen as G
+    from synth.torch_io import to_device
+
+    m, D, H, W = 128, 512, 128, 128
+    dims = lib.make_dims(m, D, H, 64, 128, 0, W)
+    bf = lambda seed, name, shape, std=1.0: to_device(G.f32_to_bf16_bits(G.normal_f32(seed, name, shape, std)), "bf16")
+    out = {}
+    # prefill chunk
+    L, T = 1044480, 4096
+    n_cap = (L + T) // m
+    log("generating hca chunk inputs")
+    q, ent = bf(70, "hca_q", (1, T, H, D)), bf(70, "hca_ent", (1, n_cap, D))
+    raw = bf(70, "hca_raw", (1, T + W - 1, D))
+    cv, z = bf(70, "hca_c", (1, T, D)), bf(70, "hca_z", (1, T, D), 2.0)
+    bias = to_device(G.normal_f32(70, "hca_bias", (m, D), 0.5), "f32")
+    o = torch.empty(1, T, H, D, dtype=torch.bfloat16, device="cuda")
+    ws = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_DENSE_ATTN, dims, 1, T, n_cap, 0, lib.CSA_BF16) + 256)
+    att = lambda: lib.csa_dense_attn(dims, q, ent, raw, o, q_pos0=L, raw_pos0=L - W + 1, ws=ws)
+    cmp = lambda: lib.csa_hca_compress(cv, z, bias, ent, pos0=L, m=m)
+    for _ in range(warmup):
+        cmp()
+        att()
+    torch.cuda.synchronize()
+    a_ms = timed_events(att, steps, torch.cuda.synchronize)
+    c_ms = timed_events(cmp, steps, torch.cuda.synchronize)
+    pos = L + np.arange(T)
+    keys = np.minimum((pos + 1) // m, n_cap) + np.minimum(pos + 1, W)
+    flops = int(keys.sum()) * H * D * 4
+    am = float(np.median(a_ms))
+    out["hca_chunk1m"] = {"attn_ms": round(am, 3), "compress_us": round(float(np.median(c_ms)) * 1e3, 1),
+                          "algorithmic_flops": flops, "tflops": round(flops / (am * 1e-3) / 1e12, 1),
+                          "frac_bf16_peak": round(flops / (am * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "chunk_tokens": T, "context_tokens": L, "entries_visible": [int(keys.min() - W), int(keys.max() - W)]}
+    del q, ent, raw, o, ws
+    # decode
+    B, L = 16, 1048576
+    n_cap = L // m
+    log("generating hca decode inputs")
+    q, ent = bf(71, "hca_q", (B, 1, H, D)), bf(71, "hca_ent", (B, n_cap, D))
+    raw = bf(71, "hca_raw", (B, W, D))
+    o = torch.empty(B, 1, H, D, dtype=torch.bfloat16, device="cuda")
+    ws = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_DENSE_ATTN, dims, B, 1, n_cap, 0, lib.CSA_BF16) + 256)
+    step = lambda: lib.csa_dense_attn(dims, q, ent, raw, o, q_pos0=L - 1, raw_pos0=L - W, ws=ws)
+    flush = torch.ones(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(max(steps, 10)):
+        flush.sum()
+        ms += timed_events(step, 1, torch.cuda.synchronize)
+    nbytes = B * (n_cap + W) * D * 2 + 2 * B * H * D * 2
+    us = float(np.median(ms)) * 1e3
+    out["hca_decode1m"] = {"us_per_step": round(us, 2), "algorithmic_bytes": int(nbytes),
+                           "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                           "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "B": B,
+                           "context_tokens": L, "entries_per_sequence": n_cap,
+                           "mall": "512 MiB read between steps, outside the timed events"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +403,7 @@ def main():
     ap.add_argument("--workload", default="chunk1m")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hca", action="store_true", help="skip the HCA legs")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise four rocprofv3 --pmc runs under DIR")
     ap.add_argument("--mfma-summary", metavar="DIR", help="summarise one rocprofv3 --pmc run of the MFMA busy counter")
@@ -403,6 +472,8 @@ def main():
     }
     if not args.no_decode:
         res["decode"] = {n: bench_decode(n, max(args.steps, 10), 3) for n in ("decode128k", "decode1m_fp4")}
+    if not args.no_hca:
+        res["hca"] = bench_hca(min(args.steps, 5), 2)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, r["inp"])

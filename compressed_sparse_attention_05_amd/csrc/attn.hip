@@ -830,7 +830,7 @@ bool use_attn_mfma(const AttnArgs& a) {
 
 constexpr int kDecodeRows = 8;     // fewer query rows per sequence than this: decode regime
 constexpr int kSplitKeys = 288;    // keys per split in the decode regime (9 tiles: 1152 keys in 4)
-constexpr int kDenseSplitKeys = 1024;  // dense mode (thousands of keys per row): 32 tiles per split
+constexpr int kDenseSplitKeys = 512;  // dense mode (thousands of keys per row): 16 tiles per split
 
 // most keys any query row of the call can have
 int64_t attn_max_keys(const AttnArgs& a) {

@@ -77,15 +77,36 @@ __device__ __forceinline__ void accumulate(const float* z, const float* bias, co
   }
 }
 
+// Merges the online-softmax state of another thread's rows: both maxima are brought to the larger
+// one. Symmetric in its two operands, so every lane of a butterfly ends with the same bits.
+template <int V>
+__device__ __forceinline__ void merge(float* mx, float* den, float* num, const float* mx2, const float* den2,
+                                      const float* num2) {
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const float nm = fmaxf(mx[v], mx2[v]);
+    const float s1 = expf(mx[v] - nm), s2 = expf(mx2[v] - nm);
+    den[v] = den[v] * s1 + den2[v] * s2;
+    num[v] = num[v] * s1 + num2[v] * s2;
+    mx[v] = nm;
+  }
+}
+
+// G consecutive threads share one (entry, channel vector): thread `sub` takes rows sub, sub + G, ...
+// of each block, and the G partial softmax states meet through a shuffle butterfly. G = 1 for short
+// blocks (CSA, m = 4); long blocks (HCA, m = 128) use G = 16 so that a chunk has enough threads.
 template <class VI, class VO>
 __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   constexpr int V = VI::N;
+  const int G = a.group;
   const int cv = a.c / V;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int b = blockIdx.y;
-  if (gid >= (int64_t)a.n_new * cv) return;
-  const int e = (int)(gid / cv);
-  const int j0 = (int)(gid % cv) * V;
+  const int64_t slot = gid / G;
+  const int sub = (int)(gid % G);
+  if (slot >= (int64_t)a.n_new * cv) return;  // whole groups only: G divides the block size
+  const int e = (int)(slot / cv);
+  const int j0 = (int)(slot % cv) * V;
   const int m = a.m;
   const int64_t i = a.first_entry + e;
   const int64_t sbase = (int64_t)b * a.seq_stride;
@@ -97,39 +118,65 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     den[v] = 0.f;
     num[v] = 0.f;
   }
+  // This thread's rows of a block are taken kRows at a time, all loads of a group issued before any
+  // is used (one memory latency per group, not per row); the logits enter the online softmax in
+  // row order.
+  constexpr int kRows = 8;
   // own block, series a
-  for (int r = 0; r < m; ++r) {
-    const int64_t row = sbase + (int64_t)(e * m + r) * a.ld + j0;
-    float z[V], c[V], bias[V];
-    VI::load(a.za, row, z);
-    VI::load(a.ca, row, c);
+  for (int r0 = sub; r0 < m; r0 += kRows * G) {
+    float z[kRows][V], c[kRows][V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) bias[v] = a.bias_a[r * a.c + j0 + v];
-    accumulate<V>(z, bias, c, mx, den, num);
+    for (int q = 0; q < kRows; ++q) {
+      if (r0 + q * G >= m) break;
+      const int64_t row = sbase + (int64_t)(e * m + r0 + q * G) * a.ld + j0;
+      VI::load(a.za, row, z[q]);
+      VI::load(a.ca, row, c[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kRows; ++q) {
+      if (r0 + q * G >= m) break;
+      float bias[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) bias[v] = a.bias_a[(r0 + q * G) * a.c + j0 + v];
+      accumulate<V>(z[q], bias, c[q], mx, den, num);
+    }
   }
   // previous block, series b (entry 0 has none; HCA pools its own block only)
   if (a.overlap && i >= 1) {
-    for (int r = 0; r < m; ++r) {
-      const void* cb;
-      const void* zb;
-      int64_t row;
-      if (e >= 1) {
-        cb = a.cb;
-        zb = a.zb;
-        row = sbase + (int64_t)((e - 1) * m + r) * a.ld + j0;
-      } else {
-        cb = a.halo_cb;
-        zb = a.halo_zb;
-        row = (int64_t)b * a.halo_seq_stride + (int64_t)r * a.halo_ld + j0;
-      }
-      float z[V], c[V], bias[V];
-      VI::load(zb, row, z);
-      VI::load(cb, row, c);
+    const void* cb = e >= 1 ? a.cb : a.halo_cb;
+    const void* zb = e >= 1 ? a.zb : a.halo_zb;
+    for (int r0 = sub; r0 < m; r0 += kRows * G) {
+      float z[kRows][V], c[kRows][V];
 #pragma unroll
-      for (int v = 0; v < V; ++v) bias[v] = a.bias_b[r * a.c + j0 + v];
-      accumulate<V>(z, bias, c, mx, den, num);
+      for (int q = 0; q < kRows; ++q) {
+        if (r0 + q * G >= m) break;
+        const int r = r0 + q * G;
+        const int64_t row = e >= 1 ? sbase + (int64_t)((e - 1) * m + r) * a.ld + j0
+                                   : (int64_t)b * a.halo_seq_stride + (int64_t)r * a.halo_ld + j0;
+        VI::load(zb, row, z[q]);
+        VI::load(cb, row, c[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < kRows; ++q) {
+        if (r0 + q * G >= m) break;
+        float bias[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) bias[v] = a.bias_b[(r0 + q * G) * a.c + j0 + v];
+        accumulate<V>(z[q], bias, c[q], mx, den, num);
+      }
     }
   }
+  for (int off = G >> 1; off > 0; off >>= 1) {
+    float mx2[V], den2[V], num2[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      mx2[v] = __shfl_xor(mx[v], off, 64);
+      den2[v] = __shfl_xor(den[v], off, 64);
+      num2[v] = __shfl_xor(num[v], off, 64);
+    }
+    merge<V>(mx, den, num, mx2, den2, num2);
+  }
+  if (sub != 0) return;
   float out[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) out[v] = num[v] / den[v];
@@ -143,7 +190,7 @@ hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
                       (a.halo_seq_stride % Vec<DI>::N == 0) && (a.entries_seq_stride % Vec<DI>::N == 0) &&
                       Vec<DI>::N == Vec<DO>::N && a.aligned16;
   const int V = vec_ok ? Vec<DI>::N : 1;
-  const int64_t threads = (int64_t)a.n_new * (a.c / V);
+  const int64_t threads = (int64_t)a.n_new * (a.c / V) * a.group;
   dim3 grid((unsigned)ceil_div(threads, 256), (unsigned)a.B);
   if (vec_ok) {
     hipLaunchKernelGGL((compress_kernel<Vec<DI>, Vec<DO>>), grid, dim3(256), 0, s, a);
@@ -155,8 +202,10 @@ hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
-  if (a.n_new <= 0 || a.B <= 0) return hipSuccess;
+hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
+  if (a0.n_new <= 0 || a0.B <= 0) return hipSuccess;
+  CompressArgs a = a0;
+  a.group = a.m >= 64 ? 16 : 1;  // threads per (entry, channel vector); every thread has >= 4 rows
   if (a.in_dtype == CSA_BF16 && a.out_dtype == CSA_BF16) return launch_typed<CSA_BF16, CSA_BF16>(a, s);
   if (a.in_dtype == CSA_F32 && a.out_dtype == CSA_F32) return launch_typed<CSA_F32, CSA_F32>(a, s);
   if (a.in_dtype == CSA_BF16 && a.out_dtype == CSA_F32) {

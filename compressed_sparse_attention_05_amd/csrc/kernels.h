@@ -18,6 +18,7 @@ struct CompressArgs {
   int64_t entries_seq_stride;
   bool aligned16;
   bool overlap = true;  // pool the previous block too (CSA); false: own block only (HCA)
+  int group = 1;        // threads per (entry, channel vector); set by launch_compress
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 int compress_max_m();
