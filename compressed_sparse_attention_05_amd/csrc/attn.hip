@@ -7,9 +7,8 @@
 //  * attn_pairs (bf16, D = 512, 128 heads, 8 waves): one workgroup per (query row, key split);
 //    wave pairs own 32 heads and split the 512 dims in halves, meet through LDS for the logits, and
 //    run as two groups half a tile apart so that softmax and MFMA work of a SIMD overlap.
-//  * attn_mfma (bf16, D = 512, 64-head groups of 4 waves or 128 heads in 8): each wave owns 16
-//    heads whole; used for 64-head layers and for small-batch decode, where the heads are spread
-//    over more workgroups.
+//  * attn_mfma (bf16, D = 512, 64-head groups of 4 waves): each wave owns 16 heads whole; used for
+//    64-head layers.
 //  * attn_generic (any H, D, fp32 or bf16): one wave per (row, head), lanes over dims, one key at
 //    a time with a wave reduction; used for fp32 layers and odd shapes.
 // With fewer than 8 query rows per sequence the key list is cut into fixed splits and
@@ -863,14 +862,11 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStr
   return hipGetLastError();
 }
 
-// Waves per workgroup (16 heads each). A query row's 128 heads share one workgroup (8 waves, each
-// key row loaded once) unless there are too few (row, split) units to fill the chip, as in decode
-// with a small batch: then they are spread over two 4-wave workgroups. Heads are independent, so
-// the split of the heads never changes a result.
-int attn_waves(const AttnArgs& a, const AttnSplit& sp) {
-  const int64_t units = (int64_t)a.B * a.T * sp.n_splits;
-  return a.H == 128 && units >= 256 ? 8 : 4;
-}
+// Waves per workgroup (16 heads each): a query row's 128 heads share one attn_pairs workgroup (8
+// waves, each key row loaded once); 64-head layers use attn_mfma. The choice depends on the layer's
+// shape only, never on the batch or the number of rows: the two kernels round differently, and a
+// sequence's output must not depend on what else is in the batch.
+int attn_waves(const AttnArgs& a) { return a.H == 128 ? 8 : 4; }
 
 template <int NW, int OT>
 hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
@@ -885,7 +881,7 @@ hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipSt
 
 template <int OT>
 hipError_t launch_mfma_for(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
-  if (attn_waves(a, sp) == 8) return launch_pairs<8, OT>(a, sp, R, s);
+  if (attn_waves(a) == 8) return launch_pairs<8, OT>(a, sp, R, s);
   // Too few workgroups to share compute units: a three-deep ring keeps two gathers in flight per
   // workgroup. Otherwise a two-deep ring lets two workgroups share a compute unit.
   if (R * sp.n_splits * (a.H / (kHPW * 4)) < 256) return launch_mfma<4, 3, OT>(a, sp, R, s);
