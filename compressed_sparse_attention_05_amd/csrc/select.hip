@@ -1,4 +1,5 @@
-// Exact top-k over materialised score rows with many workgroups per row (see select_radix.h).
+// Exact top-k over materialised score rows: one workgroup per row for rows that fit its registers
+// (sel_row), many workgroups per row for longer rows (see select_radix.h).
 #include "kernels.h"
 #include "select_radix.h"
 
@@ -276,6 +277,245 @@ __global__ void __launch_bounds__(kSelThreads) sel_final(const int32_t* n_valid,
   }
 }
 
+// Rows of up to kRowMax scores: one workgroup per row does the whole selection with the row held in
+// registers, so nothing is staged in global memory and there is one launch instead of three.
+// Thread t holds the four consecutive scores 4(q*kRowThreads + t) .. +3 for q < P/4 (one 16-byte load
+// per q, coalesced across the workgroup). The k-th largest 32-bit key is found by radix passes over an
+// LDS histogram (12 bits per pass) of the candidate range [lo, lo + span]. The first pass bins only
+// the keys at or above a lower bound of the k-th largest: the smallest of the per-thread maxima when
+// every thread holds a score and k <= kRowThreads (then kRowThreads distinct scores are at least that
+// large), else the row minimum; this keeps most of the row out of the LDS atomics. Selected are the
+// keys above the k-th largest plus the lowest-indexed keys equal to it (ties toward the smaller
+// index). Ranks in index order come from per-wave ballots and one scan of per-chunk counts, a chunk
+// being the 256 consecutive scores one wave holds for one q.
+constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kRowMax = 32 * kRowThreads;
+constexpr int kRowBins = 4096;
+constexpr int kRowChunks = kRowMax / 256;
+
+struct RowSmem {
+  uint32_t hist[kRowBins];
+  uint32_t chunk[kRowChunks];
+  uint32_t wsum[kRowWaves];
+  uint32_t wred[3][kRowWaves];
+  uint32_t sh[3];
+};
+
+// Block-wide exclusive scan of one value per thread over kRowThreads threads.
+__device__ __forceinline__ uint32_t row_excl_scan(uint32_t v, uint32_t* wsum) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t off = 0;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) off += w < wave ? wsum[w] : 0u;
+  __syncthreads();
+  return off + incl - v;
+}
+
+// Ranks in index order among the row's flagged elements (bit 4q+e of `mask` flags score
+// 4(q*kRowThreads + t) + e): base[q] is the rank of this thread's first flagged element of group q,
+// and an element's rank adds the flagged bits below it in its group.
+template <int P>
+__device__ __forceinline__ void row_ranks(uint32_t mask, RowSmem& sm, uint32_t* base) {
+  constexpr int NQ = P / 4, NC = NQ * kRowWaves;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    uint32_t tot = 0, mine = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t b = __ballot((mask >> (4 * q + e)) & 1u);
+      tot += (uint32_t)__popcll(b);
+      mine += (uint32_t)__popcll(b & lt);
+    }
+    base[q] = mine;
+    if (lane == 0) sm.chunk[q * kRowWaves + wave] = tot;
+  }
+  __syncthreads();
+  if (wave == 0) {  // chunks 2l, 2l+1 per lane: exclusive scan over the NC chunk counts
+    const uint32_t c0 = 2 * lane < NC ? sm.chunk[2 * lane] : 0u;
+    const uint32_t c1 = 2 * lane + 1 < NC ? sm.chunk[2 * lane + 1] : 0u;
+    const uint32_t ex = wave_incl_scan(c0 + c1) - c0 - c1;
+    if (2 * lane < NC) sm.chunk[2 * lane] = ex;
+    if (2 * lane + 1 < NC) sm.chunk[2 * lane + 1] = ex + c0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) base[q] += sm.chunk[q * kRowWaves + wave];
+  __syncthreads();
+}
+
+template <int P, bool VEC>
+__global__ void __launch_bounds__(kRowThreads) sel_row(const float* scores, int64_t ld, const int32_t* n_valid,
+                                                       int k, int32_t* out_idx, float* out_score) {
+  static_assert(P % 4 == 0 && 4 * P <= kRowChunks && P <= 32, "row layout");
+  constexpr int NQ = P / 4;
+  __shared__ RowSmem sm;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+  const int64_t row = blockIdx.x;
+  const int64_t nv = row_valid(n_valid, row, ld);
+  const float* s = scores + row * ld;
+  int32_t* oi = out_idx + row * k;
+  float* os = out_score ? out_score + row * k : nullptr;
+  if (nv <= k) {  // every valid entry is selected
+    for (int j = tid; j < k; j += kRowThreads) {
+      oi[j] = j < nv ? j : -1;
+      if (os) os[j] = j < nv ? key_to_score(score_to_key(s[j])) : -INFINITY;
+    }
+    return;
+  }
+  uint32_t key[P];
+  uint32_t valid = 0;  // bit j: key[j] is a score of the row (index < nv)
+  uint32_t tmin = 0xFFFFFFFFu, tmax = 0u;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t i = 4 * ((int64_t)q * kRowThreads + tid);
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (VEC) {
+      if (i + 4 <= ld) {
+        const float4 x = *reinterpret_cast<const float4*>(s + i);
+        v[0] = x.x;
+        v[1] = x.y;
+        v[2] = x.z;
+        v[3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i + e < nv) v[e] = s[i + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = i + e < nv;
+      const uint32_t kk = score_to_key(v[e]);
+      key[4 * q + e] = kk;
+      valid |= (ok ? 1u : 0u) << (4 * q + e);
+      tmin = ok && kk < tmin ? kk : tmin;
+      tmax = ok && kk > tmax ? kk : tmax;
+    }
+  }
+  // block reductions: smallest per-thread maximum (threads holding a score), row maximum, row minimum
+  uint32_t r0 = valid ? tmax : 0xFFFFFFFFu, r1 = tmax, r2 = tmin;
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = __shfl_xor(r0, o, 64), b = __shfl_xor(r1, o, 64), c = __shfl_xor(r2, o, 64);
+    r0 = a < r0 ? a : r0;
+    r1 = b > r1 ? b : r1;
+    r2 = c < r2 ? c : r2;
+  }
+  if (lane == 0) {
+    sm.wred[0][wave] = r0;
+    sm.wred[1][wave] = r1;
+    sm.wred[2][wave] = r2;
+  }
+  __syncthreads();
+  uint32_t bound = 0xFFFFFFFFu, hi = 0u, rmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    bound = sm.wred[0][w] < bound ? sm.wred[0][w] : bound;
+    hi = sm.wred[1][w] > hi ? sm.wred[1][w] : hi;
+    rmin = sm.wred[2][w] < rmin ? sm.wred[2][w] : rmin;
+  }
+  const bool every_thread = nv > 4 * (int64_t)(kRowThreads - 1);
+  uint32_t lo = (every_thread && k <= kRowThreads) ? bound : rmin;
+  uint32_t span = hi - lo;
+  uint32_t need = (uint32_t)k;
+  bool whole;  // true: select every key >= lo; false: keys > lo plus the first `need` keys equal to lo
+  for (;;) {
+    const int bits = span == 0u ? 0 : 32 - __clz(span);
+    const int sh = bits > 12 ? bits - 12 : 0;
+#pragma unroll
+    for (int b = tid; b < kRowBins; b += kRowThreads) sm.hist[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const uint32_t u = key[j] - lo;
+      if (((valid >> j) & 1u) && key[j] >= lo && u <= span) atomicAdd(&sm.hist[u >> sh], 1u);
+    }
+    __syncthreads();
+    // thread t scans bins 4095-4t .. 4092-4t, i.e. from the top digit down
+    constexpr int per = kRowBins / kRowThreads;
+    uint32_t c[per], local = 0;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      c[j] = sm.hist[kRowBins - 1 - per * tid - j];
+      local += c[j];
+    }
+    const uint32_t excl = row_excl_scan(local, sm.wsum);
+    if (excl < need && need <= excl + local) {
+      uint32_t run = excl;
+#pragma unroll
+      for (int j = 0; j < per; ++j) {
+        if (run < need && need <= run + c[j]) {
+          sm.sh[0] = (uint32_t)(kRowBins - 1 - per * tid - j);
+          sm.sh[1] = run;
+          sm.sh[2] = c[j];
+        }
+        run += c[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t d = sm.sh[0], above = sm.sh[1], inbin = sm.sh[2];
+    __syncthreads();
+    need -= above;
+    lo += d << sh;
+    if (inbin == need) {
+      whole = true;
+      break;
+    }
+    if (sh == 0) {  // the bin is the single key value lo
+      whole = false;
+      break;
+    }
+    const uint32_t w = (1u << sh) - 1u;
+    span = span - (d << sh) < w ? span - (d << sh) : w;
+  }
+  uint32_t sel = 0;
+  if (whole) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) sel |= (((valid >> j) & 1u) && key[j] >= lo ? 1u : 0u) << j;
+  } else {
+    uint32_t eq = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      sel |= (((valid >> j) & 1u) && key[j] > lo ? 1u : 0u) << j;
+      eq |= (((valid >> j) & 1u) && key[j] == lo ? 1u : 0u) << j;
+    }
+    uint32_t rb[NQ];
+    row_ranks<P>(eq, sm, rb);
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const uint32_t r = rb[j / 4] + (uint32_t)__popc(eq & (((1u << (j % 4)) - 1u) << (j & ~3)));
+      sel |= (((eq >> j) & 1u) && r < need ? 1u : 0u) << j;
+    }
+  }
+  uint32_t pb[NQ];
+  row_ranks<P>(sel, sm, pb);
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const uint32_t pos = pb[j / 4] + (uint32_t)__popc(sel & (((1u << (j % 4)) - 1u) << (j & ~3)));
+    if (((sel >> j) & 1u) && pos < (uint32_t)k) {  // exactly k are selected; the test only bounds the writes
+      oi[pos] = (int32_t)(4 * ((int64_t)(j / 4) * kRowThreads + tid) + (j % 4));
+      if (os) os[pos] = key_to_score(key[j]);
+    }
+  }
+}
+
+template <int P>
+void launch_row(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
+                float* out_score, hipStream_t s) {
+  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL((sel_row<P, true>), dim3((unsigned)R), dim3(kRowThreads), 0, s, scores, ld, n_valid, k,
+                       out_idx, out_score);
+  else
+    hipLaunchKernelGGL((sel_row<P, false>), dim3((unsigned)R), dim3(kRowThreads), 0, s, scores, ld, n_valid, k,
+                       out_idx, out_score);
+}
+
 SelWork carve(void* ws, int R, int64_t ld, int k) {
   uint8_t* p = static_cast<uint8_t*>(ws);
   SelWork w;
@@ -310,6 +550,13 @@ hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s)
 
 hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
                          float* out_score, void* ws, bool zeroed, hipStream_t s) {
+  if (ld <= kRowMax) {
+    if (ld <= 4 * kRowThreads) launch_row<4>(scores, ld, n_valid, R, k, out_idx, out_score, s);
+    else if (ld <= 8 * kRowThreads) launch_row<8>(scores, ld, n_valid, R, k, out_idx, out_score, s);
+    else if (ld <= 16 * kRowThreads) launch_row<16>(scores, ld, n_valid, R, k, out_idx, out_score, s);
+    else launch_row<32>(scores, ld, n_valid, R, k, out_idx, out_score, s);
+    return hipGetLastError();
+  }
   SelWork w = carve(ws, R, ld, k);
   hipError_t e;
   const unsigned nchunks = (unsigned)(ceil_div(ld, kSelChunk) > 0 ? ceil_div(ld, kSelChunk) : 1);

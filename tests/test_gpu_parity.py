@@ -24,7 +24,9 @@ def _oracle_topk_rows(s32, nv, k):
 
 
 @pytest.mark.parametrize("R,n,k,tie", [(7, 100, 16, False), (5, 3000, 512, True), (3, 5000, 1024, False),
-                                       (2, 40000, 1024, True), (4, 70000, 100, False), (6, 64, 64, True)])
+                                       (2, 40000, 1024, True), (4, 70000, 100, False), (6, 64, 64, True),
+                                       # one workgroup per row (rows of 16K..32K scores), odd and full lengths
+                                       (3, 20001, 1024, True), (7, 32768, 512, False), (5, 24000, 2048, True)])
 def test_topk_from_scores_bit_exact(R, n, k, tie):
     rng = np.random.default_rng(R * 1000 + n)
     s = rng.standard_normal((R, n)).astype(np.float32)
@@ -43,6 +45,21 @@ def test_topk_from_scores_bit_exact(R, n, k, tie):
     for r in range(R):
         v = want[r] >= 0
         np.testing.assert_array_equal(gs[r][v], s[r][want[r][v]])
+
+
+@pytest.mark.parametrize("n", [20000, 32768, 50000])
+def test_topk_from_scores_constant_rows(n):
+    # every score equal: the top-k is the first k entries (ties go to the smaller index)
+    R, k = 3, 1024
+    s = np.full((R, n), 0.75, dtype=np.float32)
+    s[1] = -2.0
+    s[2, : n // 2] = 0.0
+    s[2, n // 2:] = -0.0
+    nv = np.array([n, n - 3, n], dtype=np.int32)
+    idx = torch.empty(R, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk_from_scores(to_device(s, "f32"), to_device(nv, "i32"), k, idx)
+    np.testing.assert_array_equal(idx.cpu().numpy(), _oracle_topk_rows(s, nv, k))
+    np.testing.assert_array_equal(idx.cpu().numpy(), np.tile(np.arange(k, dtype=np.int32), (R, 1)))
 
 
 # ------------------------------------------------------------------------------------ tiny fp32
@@ -237,13 +254,14 @@ def test_decode_mxfp4_small():
     _decode_check(wl, inp, st, range(wl.B))
 
 
-def test_decode_batch_invariance():
-    wl = get("decode128k").with_(B=8, L=4 * 9000)
+@pytest.mark.parametrize("B,L,b", [(8, 4 * 9000, 5), (64, 4 * 2000, 37)])
+def test_decode_batch_invariance(B, L, b):
+    # a sequence decoded alone gives the bits it gets inside a batch, whatever the batch size
+    wl = get("decode128k").with_(B=B, L=L)
     inp = G.make_inputs(wl)
     t = decode_tensors(wl, inp)
     full = run_decode(wl, t)
     o_full, i_full = full.out.clone(), full.idx.clone()
-    b = 5
     one = {k: (v[b:b + 1] if (v is not None and k != "w_head") else v) for k, v in t.items()}
     solo = run_decode(wl.with_(B=1), one)
     assert torch.equal(solo.out[0], o_full[b]) and torch.equal(solo.idx[0], i_full[b])
@@ -312,3 +330,23 @@ def test_decode_sink_split_kv():
         check_idx_rows(gidx[b], r["idx"], r["scores"], r["n_vis"])
         ref = O.sparse_attention(r["q"], r["entries"], gidx[b], r["raw"], wl.L - wl.W + 1, [wl.L], wl.W, sink=sink)
         assert max_err(gout[b], ref) <= TOL["bf16"]
+
+
+def test_sparse_attn_prefill_batch_invariance():
+    # 128 query rows of 128 heads: each sequence of a batch of 2 gives the bits it gets alone
+    B, T, H, D, k, n_cap, q_pos0 = 2, 128, 128, 512, 512, 1500, 4 * 1500 - 128
+    d = dims_of(get("decode128k").with_(k=k))
+    mk = lambda name, shape: to_device(G.f32_to_bf16_bits(G.normal_f32(71, name, shape)), "bf16")
+    q, ent = mk("q", (B, T, H, D)), mk("ent", (B, n_cap, D))
+    raw_pos0 = q_pos0 - 127
+    raw = mk("raw", (B, q_pos0 + T - raw_pos0, D))
+    rng = np.random.default_rng(71)
+    idx = np.stack([np.stack([np.sort(rng.choice(n_cap, k, replace=False)) for _ in range(T)]) for _ in range(B)])
+    idx = to_device(idx.astype(np.int32), "i32")
+    out = torch.empty(B, T, H, D, dtype=torch.float32, device="cuda")
+    lib.csa_sparse_attn(d, q, ent, idx, raw, out, q_pos0=q_pos0, raw_pos0=raw_pos0)
+    for b in range(B):
+        one = torch.empty(1, T, H, D, dtype=torch.float32, device="cuda")
+        lib.csa_sparse_attn(d, q[b:b + 1].contiguous(), ent[b:b + 1].contiguous(), idx[b:b + 1].contiguous(),
+                            raw[b:b + 1].contiguous(), one, q_pos0=q_pos0, raw_pos0=raw_pos0)
+        assert torch.equal(one[0], out[b])
