@@ -35,6 +35,11 @@ Readings where the pages are silent (each is listed with its reason in the desig
   scale 1/sqrt(D); top-k ties break toward the smaller entry index; fewer than k visible entries
   means all of them are kept and the index list is padded with -1.
 
+QK-norm and partial RoPE ([ANAT] bullet "QK-norm and partial RoPE"): rms_norm and rope, applied by
+prefill/decode when their fid argument is given (readings: a per-dim gain, adjacent-pair rotation
+with base theta, entries rotated at the last token of their block, the window's raw KV normalised
+and rotated like an entry at its token's position).
+
 HCA ([ANAT] bullet "Heavily Compressed Attention (HCA)"): hca_compress pools each block of m = 128
 tokens with no overlap (reading: the CSA pooling over the entry's own block); dense_attention
 attends to every visible entry plus the window.
@@ -295,6 +300,53 @@ def dense_attention(q, entries, raw, raw_pos0: int, q_pos, m: int, W: int, scale
 
 
 # --------------------------------------------------------------------------------------------------
+# QK-norm and partial RoPE ([ANAT] bullet "QK-norm and partial RoPE")
+# --------------------------------------------------------------------------------------------------
+
+
+def rms_norm(x, gamma, eps: float):
+    """RMS normalisation of each head vector (the last axis), then the learned per-dim gain:
+        y = x / sqrt(mean(x^2) + eps) * gamma
+    [ANAT] bullet "QK-norm and partial RoPE": queries and compressed entries are RMS-normalised per
+    head. The gain vector and eps are readings (the pages name the norm only)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x / r * np.asarray(gamma, dtype=np.float64)
+
+
+def rope(x, pos, rope_dims: int, theta: float, inverse: bool = False):
+    """Rotary position embedding on the last rope_dims dims of each vector (the last axis).
+
+    [ANAT] bullet "QK-norm and partial RoPE": RoPE rotates only the last 64 of the 512 dims; the
+    output is rotated back by the query's own position. Reading: the rotated slice is taken in
+    adjacent pairs (2i, 2i+1), pair i turns by the angle pos * theta^(-2i/rope_dims), i.e.
+        (a, b) -> (a cos - b sin, a sin + b cos)
+    and inverse=True turns by the negative angle. pos broadcasts against x.shape[:-1] from the left
+    (pos [T] with x [T, H, D] gives every head of row t the position pos[t])."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    if rope_dims == 0:
+        return y
+    D = y.shape[-1]
+    pos = np.asarray(pos, dtype=np.float64)
+    freq = float(theta) ** (-2.0 * np.arange(rope_dims // 2) / rope_dims)
+    ang = pos.reshape(pos.shape + (1,) * (y.ndim - 1 - pos.ndim)) [..., None] * freq
+    if inverse:
+        ang = -ang
+    c, s = np.cos(ang), np.sin(ang)
+    a = y[..., D - rope_dims::2].copy()
+    b = y[..., D - rope_dims + 1::2].copy()
+    y[..., D - rope_dims::2] = a * c - b * s
+    y[..., D - rope_dims + 1::2] = a * s + b * c
+    return y
+
+
+def entry_positions(first_entry: int, n: int, m: int):
+    """Position at which RoPE turns entry i: the last token of its block, (i+1)*m - 1 (reading: the
+    position at which the entry becomes visible; the pages give none)."""
+    return (np.arange(first_entry, first_entry + n) + 1) * m - 1
+
+
+# --------------------------------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------------------------------
 
@@ -323,13 +375,19 @@ def _val(a, bf16: bool):
     return bf16_bits_to_f64(a) if bf16 else np.asarray(a, dtype=np.float64)
 
 
-def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None):
+def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None, fid=None):
     """The CSA layer over a chunk of T tokens whose context holds L earlier tokens (sequence b).
 
     Steps in the pages' order: projections, compressor (entries and indexer keys), indexer scores,
     top-k, sparse attention over entries + window. query_rows selects which query rows to finish
     (all by default); every row still feeds the compressor and the window.
     Returns a dict with the projected parts, new entries/keys, scores, idx and out for query_rows.
+    fid (optional) turns on QK-norm and partial RoPE: a dict with gamma_q, gamma_kv [D], eps,
+    rope_dims, theta. Queries, new entries and the chunk's raw KV are then RMS-normalised and
+    rotated (queries at their positions, raw KV at its token's position, entries at
+    entry_positions) and stored again; the output is rotated back by the query position. Context
+    caches (prefix entries and window rows) are taken as stored, i.e. already normalised and
+    rotated.
     """
     bf = wl.dtype == "bf16"
     m, D, DI, H, HI = wl.m, wl.D, wl.D_I, wl.H, wl.H_I
@@ -347,6 +405,10 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None):
     parts = {n: proj(n) for n in ("ca", "za", "cb", "zb", "ica", "iza", "icb", "izb", "kv")}
     q = proj("q", rows).reshape(len(rows), H, D)
     q_idx = proj("q_idx", rows).reshape(len(rows), HI, DI)
+    if fid is not None:
+        q = _store(rope(rms_norm(q, fid["gamma_q"], fid["eps"]), L + rows, fid["rope_dims"], fid["theta"]), bf)
+        parts["kv"] = _store(rope(rms_norm(parts["kv"], fid["gamma_kv"], fid["eps"]), L + np.arange(T),
+                                  fid["rope_dims"], fid["theta"]), bf)
 
     first = L // m
     halo = _val(inp["halo"][b], bf) if L > 0 else None
@@ -358,6 +420,9 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None):
                             inp["bias_b"], m, first, hcb, hzb), bf)
     new_k = _store(compress(parts["ica"], parts["iza"], parts["icb"], parts["izb"], inp["ibias_a"],
                             inp["ibias_b"], m, first, hicb, hizb), bf)
+    if fid is not None:
+        new_e = _store(rope(rms_norm(new_e, fid["gamma_kv"], fid["eps"]), entry_positions(first, len(new_e), m),
+                            fid["rope_dims"], fid["theta"]), bf)
     if L > 0:
         entries = np.concatenate([_val(inp["entries_prefix"][b], bf), new_e], axis=0)
         keys = np.concatenate([_val(inp["keys_prefix"][b], bf), new_k], axis=0)
@@ -371,14 +436,18 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None):
     scores = index_scores(q_idx, keys, inp["w_head"], nv)
     idx = np.stack([topk_select(scores[i], nv[i], wl.k) for i in range(len(rows))])
     out = sparse_attention(q, entries, idx, raw, raw_pos0, q_pos, wl.W, sink=sink)
+    if fid is not None:
+        out = rope(out, q_pos, fid["rope_dims"], fid["theta"], inverse=True)
     return dict(parts=parts, q=q, q_idx=q_idx, entries_new=new_e, keys_new=new_k,
                 entries=entries, keys=keys, raw=raw, raw_pos0=raw_pos0, rows=rows, q_pos=q_pos,
                 n_vis=nv, scores=scores, idx=idx, out=out)
 
 
-def decode(inp: dict, wl, b: int, sink=None):
+def decode(inp: dict, wl, b: int, sink=None, fid=None):
     """One decode step of sequence b: the new token sits at position L (it opens a new block, so
-    no compression runs), the caches hold L/m entries and the raw KV of positions L-W+1..L."""
+    no compression runs), the caches hold L/m entries and the raw KV of positions L-W+1..L.
+    fid (see prefill): the query is RMS-normalised and rotated at L (then stored), the caches are
+    taken as stored, and the output is rotated back by L."""
     bf = wl.dtype == "bf16"
     L, m = wl.L, wl.m
     entries = _val(inp["entries"][b], bf)
@@ -391,9 +460,13 @@ def decode(inp: dict, wl, b: int, sink=None):
     q = _val(inp["q"][b], bf)
     raw = _val(inp["kv_raw"][b], bf)
     q_pos = np.array([L])
+    if fid is not None:
+        q = _store(rope(rms_norm(q, fid["gamma_q"], fid["eps"]), q_pos, fid["rope_dims"], fid["theta"]), bf)
     nv = n_visible(q_pos, m)
     scores = index_scores(q_idx, keys, inp["w_head"], nv)
     idx = topk_select(scores[0], nv[0], wl.k)[None]
     out = sparse_attention(q, entries, idx, raw, L - (wl.W - 1), q_pos, wl.W, sink=sink)
+    if fid is not None:
+        out = rope(out, q_pos, fid["rope_dims"], fid["theta"], inverse=True)
     return dict(scores=scores, idx=idx, out=out, n_vis=nv, keys=keys, entries=entries, q=q,
                 q_idx=q_idx, raw=raw)

@@ -466,3 +466,123 @@ def test_prefill_invariants_bf16_tiny():
         np.testing.assert_array_equal(O.round_bf16(a), a)
     for t in range(wl.T):
         _check_topk_properties(r["scores"][t], r["n_vis"][t], wl.k, r["idx"][t])
+
+
+# ---------------------------------------------------------------------------------- QK-norm, partial RoPE
+
+
+def test_rms_norm_closed_forms():
+    # hand-worked: x = (3, 4): mean of squares 12.5, so y = x / sqrt(12.5)
+    np.testing.assert_allclose(O.rms_norm([3.0, 4.0], [1.0, 1.0], 0.0), [3 / np.sqrt(12.5), 4 / np.sqrt(12.5)],
+                               rtol=0, atol=1e-15)
+    rng = np.random.default_rng(80)
+    x = rng.standard_normal((5, 3, 64))
+    y = O.rms_norm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, atol=1e-13)        # unit RMS per head vector
+    np.testing.assert_allclose(O.rms_norm(7.5 * x, np.ones(64), 0.0), y, atol=1e-13)   # scale invariance
+    g = rng.uniform(0.5, 2.0, 64)
+    np.testing.assert_allclose(O.rms_norm(x, g, 0.0), y * g, atol=1e-13)        # the gain is per dim
+    assert np.all(O.rms_norm(np.zeros(8), np.ones(8), 1e-6) == 0)               # eps keeps zero finite
+    np.testing.assert_allclose(O.rms_norm([1e-4] * 4, [1.0] * 4, 1e-6), [1e-4 / np.sqrt(1e-8 + 1e-6)] * 4, rtol=1e-14)
+
+
+def test_rope_closed_forms():
+    p = 3.0
+    # pair 0 of the rotated slice turns at frequency 1: (1, 0) -> (cos p, sin p); other dims untouched
+    y = O.rope([5.0, -2.0, 1.0, 0.0], p, 2, 10000.0)
+    np.testing.assert_allclose(y, [5.0, -2.0, np.cos(p), np.sin(p)], atol=1e-15)
+    # pair 1 of a 4-dim slice with theta = 100 turns at 100^(-1/2) = 0.1: (0, 1) -> (-sin, cos)
+    y = O.rope([0.0, 0.0, 0.0, 1.0], p, 4, 100.0)
+    np.testing.assert_allclose(y, [0.0, 0.0, -np.sin(0.1 * p), np.cos(0.1 * p)], atol=1e-15)
+    # the rotation of each pair is the complex product (a + ib) e^{i angle}
+    rng = np.random.default_rng(81)
+    x = rng.standard_normal(512)
+    pos = 123457.0
+    y = O.rope(x, pos, 64, 10000.0)
+    z = (x[448::2] + 1j * x[449::2]) * np.exp(1j * pos * 10000.0 ** (-np.arange(32) / 32.0))
+    np.testing.assert_allclose(y[448::2], z.real, atol=1e-9)
+    np.testing.assert_allclose(y[449::2], z.imag, atol=1e-9)
+    np.testing.assert_array_equal(y[:448], x[:448])
+    # norm preserved, position 0 is the identity, the inverse undoes it
+    np.testing.assert_allclose(np.linalg.norm(y), np.linalg.norm(x), rtol=1e-14)
+    np.testing.assert_array_equal(O.rope(x, 0.0, 64, 10000.0), x)
+    np.testing.assert_allclose(O.rope(y, pos, 64, 10000.0, inverse=True), x, atol=1e-12)
+
+
+def test_rope_logits_depend_on_relative_position_only():
+    rng = np.random.default_rng(82)
+    q, k = rng.standard_normal(512), rng.standard_normal(512)
+    a = O.rope(q, 1000.0, 64, 10000.0) @ O.rope(k, 37.0, 64, 10000.0)
+    b = O.rope(q, 1000.0 + 65536.0, 64, 10000.0) @ O.rope(k, 37.0 + 65536.0, 64, 10000.0)
+    c = O.rope(q, 1001.0, 64, 10000.0) @ O.rope(k, 37.0, 64, 10000.0)
+    assert abs(a - b) < 1e-9 and abs(a - c) > 1e-6
+
+
+def test_rotated_attention_output_is_shift_invariant():
+    # entries and raw KV rotated at their positions, queries at theirs, the output rotated back by the
+    # query position: shifting every position by the same amount leaves the output unchanged, and
+    # leaving out the back-rotation does not
+    rng = np.random.default_rng(83)
+    m, D, H, W, N, T = 4, 64, 3, 8, 40, 5
+    q0, e0 = rng.standard_normal((T, H, D)), rng.standard_normal((N, D))
+    idx = np.stack([np.sort(rng.choice(N, 12, replace=False)) for _ in range(T)])
+
+    def run(shift, back=True):
+        L = 4 * N + shift
+        q_pos = L + np.arange(T)
+        raw_pos0 = L - W + 1
+        raw0 = np.random.default_rng(84).standard_normal((W - 1 + T, D))
+        e = O.rope(e0, O.entry_positions(shift // m, N, m), 16, 10000.0)
+        raw = O.rope(raw0, raw_pos0 + np.arange(len(raw0)), 16, 10000.0)
+        q = O.rope(q0, q_pos, 16, 10000.0)
+        out = O.sparse_attention(q, e, idx, raw, raw_pos0, q_pos, W)
+        return O.rope(out, q_pos, 16, 10000.0, inverse=True) if back else out
+
+    np.testing.assert_allclose(run(4 * 1000), run(0), atol=1e-12)
+    assert np.abs(run(4 * 1000, back=False) - run(0, back=False)).max() > 1e-3
+
+
+def _fid(D, seed=85, rope_dims=16):
+    rng = np.random.default_rng(seed)
+    return {"gamma_q": rng.uniform(0.5, 1.5, D), "gamma_kv": rng.uniform(0.5, 1.5, D), "eps": 1e-6,
+            "rope_dims": rope_dims, "theta": 10000.0}
+
+
+def test_fid_chunked_prefill_equals_one_shot():
+    # positions of queries, raw KV and new entries follow the absolute token positions of the chunk
+    wl_full = _tiny(T=96)
+    fid = _fid(wl_full.D)
+    inp = G.make_inputs(wl_full)
+    full = O.prefill(inp, wl_full, fid=fid)
+    wl, inp2 = _prefix_inputs_from_full(inp, wl_full, full, L=48)
+    part = O.prefill(inp2, wl, fid=fid)
+    np.testing.assert_allclose(part["entries"], full["entries"], atol=1e-12)
+    np.testing.assert_allclose(part["out"], full["out"][48:], atol=1e-12)
+    np.testing.assert_array_equal(part["idx"], full["idx"][48:])
+    # the fid layer is not the plain one
+    assert np.abs(O.prefill(inp, wl_full)["out"] - full["out"]).max() > 1e-3
+
+
+def test_fid_decode_equals_prefill_of_the_last_token():
+    wl_full = _tiny(T=97)
+    fid = _fid(wl_full.D)
+    inp = G.make_inputs(wl_full)
+    full = O.prefill(inp, wl_full, fid=fid)
+    L = 96
+    wl = wl_full.with_(kind="decode", L=L, T=1, d=0, dtype="f32", idx_dtype="f32")
+    cols, _ = O.projection_columns(wl.D, wl.D_I, wl.H, wl.H_I)
+    x = np.asarray(inp["x"][0], dtype=np.float64)
+    lo, hi = cols["q"]
+    q_raw = (x[L:L + 1] @ np.asarray(inp["W"], dtype=np.float64)[lo:hi].T).reshape(1, wl.H, wl.D)
+    dec = {
+        "entries": full["entries"][None, : L // 4],
+        "keys": full["keys"][None, : L // 4],
+        "kv_raw": full["parts"]["kv"][None, L - wl.W + 1:L + 1],
+        "q": q_raw[None],                         # before the norm: decode normalises and rotates it
+        "q_idx": full["q_idx"][None, L:L + 1],
+        "w_head": inp["w_head"],
+    }
+    r = O.decode(dec, wl, 0, fid=fid)
+    np.testing.assert_allclose(r["q"][0], full["q"][L], atol=1e-12)
+    np.testing.assert_array_equal(r["idx"][0], full["idx"][L])
+    np.testing.assert_allclose(r["out"][0], full["out"][L], atol=1e-12)
