@@ -466,6 +466,47 @@ int csa_dense_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dt
                    out_dtype, ws, ws_bytes, stream);
 }
 
+int csa_norm_rope(int B, int R, int H, int D, int dtype, const void* x, int64_t x_ld, int64_t x_seq_stride, void* y,
+                  int64_t y_ld, int64_t y_seq_stride, const float* gamma, float eps, int rope_dims, float rope_theta,
+                  int64_t pos0, int64_t pos_step, int inverse, void* stream) {
+  if (B < 0 || R < 0 || H < 0) return fail(CSA_ERR_ARG, "B, R and H must be >= 0");
+  if (D < 2 || D % 2 || D > norm_rope_max_dim())
+    return fail(CSA_ERR_ARG, "D=%d must be even and in [2, %d]", D, norm_rope_max_dim());
+  if (!is_act_dtype(dtype)) return fail(CSA_ERR_ARG, "dtype must be F32 or BF16");
+  if (rope_dims < 0 || rope_dims > D || rope_dims % 2) return fail(CSA_ERR_ARG, "rope_dims=%d must be even and in [0, D]", rope_dims);
+  if (rope_dims > 0 && !(rope_theta > 0.f)) return fail(CSA_ERR_ARG, "rope_theta must be > 0");
+  if (gamma && inverse) return fail(CSA_ERR_ARG, "the inverse rotation takes no norm");
+  if (!(eps >= 0.f)) return fail(CSA_ERR_ARG, "eps must be >= 0");
+  if ((int64_t)B * R * H == 0) return CSA_OK;
+  if (!x || !y) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  if (x_ld < (int64_t)H * D || y_ld < (int64_t)H * D) return fail(CSA_ERR_ARG, "row stride smaller than H*D");
+  if (B > 1 && (x_seq_stride < (int64_t)R * x_ld || y_seq_stride < (int64_t)R * y_ld))
+    return fail(CSA_ERR_ARG, "sequence stride too small");
+  NormRopeArgs a{};
+  a.B = B;
+  a.R = R;
+  a.H = H;
+  a.D = D;
+  a.dtype = dtype;
+  a.x = x;
+  a.x_ld = x_ld;
+  a.x_seq_stride = x_seq_stride;
+  a.y = y;
+  a.y_ld = y_ld;
+  a.y_seq_stride = y_seq_stride;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.rope_dims = rope_dims;
+  a.theta = rope_theta;
+  a.pos0 = pos0;
+  a.pos_step = pos_step;
+  a.inverse = inverse ? 1 : 0;
+  hipError_t e = launch_norm_rope(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "csa_norm_rope");
+  g_err.clear();
+  return CSA_OK;
+}
+
 int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_t pos0, int d_model, int dtype,
                 const void* x, const csa_cache* cache, void* out, int out_dtype, int32_t* out_idx, void* ws,
                 size_t ws_bytes, void* stream) {
@@ -484,6 +525,10 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
   if ((int64_t)W - 1 + T > cache->win_cap) return fail(CSA_ERR_ARG, "window - 1 + T exceeds win_cap");
   if (pos0 > 0 && !cache->halo) return fail(CSA_ERR_ARG, "pos0 > 0 needs cache->halo");
   if (cache->halo_out && T % m) return fail(CSA_ERR_ARG, "halo_out needs T %% m == 0");
+  const bool fid = w->gamma_q || w->gamma_kv || w->rope_dims != 0;
+  if (fid && (w->rope_dims < 0 || w->rope_dims > D || w->rope_dims % 2 || (w->rope_dims > 0 && !(w->rope_theta > 0.f)) ||
+              !(w->norm_eps >= 0.f)))
+    return fail(CSA_ERR_ARG, "QK-norm / RoPE parameters: rope_dims even in [0, D], rope_theta > 0, norm_eps >= 0");
   const int64_t ntot = n_tot_of(dims);
   const int es = esize(dtype);
   // workspace: P [B*T, ntot] | idx [B*T, k] | index scratch
@@ -540,6 +585,20 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
   e = launch_copy_rows(B, T, D, es, col(c_kv), ntot, (int64_t)T * ntot,
                        static_cast<uint8_t*>(cache->win) + (size_t)(W - 1) * D * es, D, cache->win_cap * D, s);
   if (e != hipSuccess) return hip_status(e, "csa_forward: window copy");
+  if (fid) {
+    // queries (in the projection buffer), the chunk's window rows and the new entries, in place
+    rc = csa_norm_rope(B, T, H, D, dtype, col(c_q), ntot, (int64_t)T * ntot, col(c_q), ntot, (int64_t)T * ntot,
+                       w->gamma_q, w->norm_eps, w->rope_dims, w->rope_theta, pos0, 1, 0, stream);
+    if (rc) return rc;
+    void* wrows = static_cast<uint8_t*>(cache->win) + (size_t)(W - 1) * D * es;
+    rc = csa_norm_rope(B, T, 1, D, dtype, wrows, D, cache->win_cap * D, wrows, D, cache->win_cap * D, w->gamma_kv,
+                       w->norm_eps, w->rope_dims, w->rope_theta, pos0, 1, 0, stream);
+    if (rc) return rc;
+    void* erows = static_cast<uint8_t*>(cache->entries) + (size_t)(pos0 / m) * D * es;
+    rc = csa_norm_rope(B, T / m, 1, D, dtype, erows, D, cache->n_cap * D, erows, D, cache->n_cap * D, w->gamma_kv,
+                       w->norm_eps, w->rope_dims, w->rope_theta, pos0 + m - 1, m, 0, stream);
+    if (rc) return rc;
+  }
   rc = csa_index_topk(dims, B, T, pos0, dtype, col(c_qi), ntot, (int64_t)T * ntot, nullptr, w->w_head, 0, cache->keys,
                       cache->n_cap * DI, nullptr, cache->n_cap, idx, nullptr, xws, x_bytes, stream);
   if (rc) return rc;
@@ -547,6 +606,11 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
                        cache->n_cap, idx, cache->win, D, cache->win_cap * D, pos0 - (W - 1), (int64_t)W - 1 + T,
                        w->sink, out, out_dtype, xws, x_bytes, stream);
   if (rc) return rc;
+  if (fid && w->rope_dims > 0) {
+    rc = csa_norm_rope(B, T, H, D, out_dtype, out, (int64_t)H * D, (int64_t)T * H * D, out, (int64_t)H * D,
+                       (int64_t)T * H * D, nullptr, 0.f, w->rope_dims, w->rope_theta, pos0, 1, 1, stream);
+    if (rc) return rc;
+  }
   if (cache->halo_out) {
     uint8_t* ho = static_cast<uint8_t*>(cache->halo_out);
     e = launch_copy_rows(B, m, 2 * D, es, col(c_cb + (int64_t)(T - m) * ntot), ntot, (int64_t)T * ntot, ho, halo_ld,

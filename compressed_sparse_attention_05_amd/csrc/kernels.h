@@ -21,6 +21,24 @@ struct CompressArgs {
   int group = 1;        // threads per (entry, channel vector); set by launch_compress
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
+// QK-norm and partial RoPE over B x R rows of H head vectors of D dims; row r sits at position
+// pos0 + r * pos_step. gamma == nullptr: no norm; rope_dims == 0: no rotation; inverse: turn back.
+struct NormRopeArgs {
+  int B = 0, R = 0, H = 0, D = 0, dtype = 0;
+  const void* x = nullptr;
+  int64_t x_ld = 0, x_seq_stride = 0;
+  void* y = nullptr;
+  int64_t y_ld = 0, y_seq_stride = 0;
+  const float* gamma = nullptr;
+  float eps = 0.f;
+  int rope_dims = 0;
+  double theta = 10000.0;
+  int64_t pos0 = 0, pos_step = 1;
+  int inverse = 0;
+};
+hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t s);
+int norm_rope_max_dim();
 int compress_max_m();
 
 // C[M, N] (row stride ldc) = A[M, K] (row stride lda) . Bm[N, K]^T (row stride ldb)

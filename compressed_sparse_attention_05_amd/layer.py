@@ -39,11 +39,17 @@ class CSAPrefill:
 
 class CSADecode:
     """One decode step of B sequences at position L (the caches hold L/m entries and the raw KV of
-    positions L-window+1 .. L): indexer + top-k, then sparse attention."""
+    positions L-window+1 .. L): indexer + top-k, then sparse attention.
+
+    fid (optional): QK-norm and partial RoPE, a dict with gamma_q (float32 [D] tensor or None), eps,
+    rope_dims, theta. The query is then normalised and rotated at L into a buffer of its own before
+    the attention and the output is rotated back by L; the caches are read as stored (already
+    normalised and rotated)."""
 
     def __init__(self, d: lib.Dims, B: int, n_cap: int, idx_dtype: int = lib.CSA_BF16, out_dtype=torch.float32,
-                 device="cuda"):
-        self.d, self.B = d, B
+                 device="cuda", fid=None, q_dtype=torch.bfloat16):
+        self.d, self.B, self.fid = d, B, fid
+        self.q_n = torch.empty(B, 1, d.H, d.D, dtype=q_dtype, device=device) if fid else None
         self.idx = torch.empty(B, 1, d.top_k, dtype=torch.int32, device=device)
         self.out = torch.empty(B, 1, d.H, d.D, dtype=out_dtype, device=device)
         self.ws = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, d, B, 1, n_cap, 0, idx_dtype), device)
@@ -51,8 +57,14 @@ class CSADecode:
                                      device)
 
     def __call__(self, L: int, q_idx, w_head, keys, q, entries, kv_raw, q_scale=None, k_scale=None, sink=None):
+        f = self.fid
+        if f:
+            q = lib.csa_norm_rope(q, y=self.q_n, pos0=L, gamma=f.get("gamma_q"), eps=f.get("eps", 0.0),
+                                  rope_dims=f.get("rope_dims", 0), theta=f.get("theta", 10000.0))
         lib.csa_index_topk(self.d, q_idx, w_head, keys, self.idx, q_pos0=L, q_scale=q_scale, k_scale=k_scale,
                            ws=self.ws)
         lib.csa_sparse_attn(self.d, q, entries, self.idx, kv_raw, self.out, q_pos0=L,
                             raw_pos0=L - (self.d.window - 1), sink=sink, ws=self.ws_attn)
+        if f and f.get("rope_dims", 0):
+            lib.csa_norm_rope(self.out, pos0=L, rope_dims=f["rope_dims"], theta=f.get("theta", 10000.0), inverse=True)
         return self.out

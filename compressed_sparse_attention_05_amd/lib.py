@@ -18,7 +18,8 @@ CSA_F32, CSA_BF16, CSA_MXFP4 = 0, 1, 2
 CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD, CSA_OP_DENSE_ATTN = \
     range(6)
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
-           "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn")
+           "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
+           "csa_norm_rope")
 
 
 class CsaError(RuntimeError):
@@ -36,7 +37,8 @@ class Dims(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [("w_proj", ctypes.c_void_p), ("bias_a", ctypes.c_void_p), ("bias_b", ctypes.c_void_p),
                 ("ibias_a", ctypes.c_void_p), ("ibias_b", ctypes.c_void_p), ("w_head", ctypes.c_void_p),
-                ("sink", ctypes.c_void_p)]
+                ("sink", ctypes.c_void_p), ("gamma_q", ctypes.c_void_p), ("gamma_kv", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float), ("rope_dims", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
 
 
 class Cache(ctypes.Structure):
@@ -72,8 +74,10 @@ def load() -> ctypes.CDLL:
     lib.csa_hca_compress.argtypes = [i32, i32, i64, i32, i32, i32, vp, vp, i64, i64, vp, vp, i64, i64, i32, vp]
     lib.csa_dense_attn.argtypes = [ctypes.POINTER(Dims), i32, i32, i64, i32, vp, i64, i64, vp, i64, i64, vp,
                                    i64, i64, i64, i64, vp, vp, i32, vp, sz, vp]
+    lib.csa_norm_rope.argtypes = [i32, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, ctypes.c_float, i32,
+                                  ctypes.c_float, i64, i64, i32, vp]
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
-              "csa_forward", "csa_hca_compress", "csa_dense_attn"):
+              "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -239,6 +243,27 @@ def csa_hca_compress(cv, z, bias, entries, *, pos0: int, m: int):
     return entries
 
 
+def csa_norm_rope(x, *, pos0: int, pos_step: int = 1, gamma=None, eps: float = 0.0, rope_dims: int = 0,
+                  theta: float = 10000.0, inverse: bool = False, y=None):
+    """QK-norm and partial RoPE on x [B, R, H, D] (or [B, R, D]: one head), row r at position
+    pos0 + r * pos_step; into y (same shape and dtype) or in place. gamma float32 [D] or None."""
+    _require_cuda(x, y, gamma)
+    y = x if y is None else y
+    if x.dim() == 3:
+        B, R, D = x.shape
+        H = 1
+    else:
+        B, R, H, D = x.shape
+    for t in (x, y):
+        if t.stride(-1) != 1 or (t.dim() == 4 and t.stride(2) != D):
+            raise ValueError("head vectors must be contiguous")
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("y must match x")
+    _check(load().csa_norm_rope(B, R, H, D, _dt(x), _p(x), x.stride(1), x.stride(0), _p(y), y.stride(1), y.stride(0),
+                                _p(gamma), eps, rope_dims, theta, pos0, pos_step, 1 if inverse else 0, _stream()))
+    return y
+
+
 def csa_dense_attn(dims: Dims, q, entries, kv_raw, out, *, q_pos0: int, raw_pos0: int, sink=None, ws=None):
     """HCA attention over every visible entry plus the window. q [B, T, H, D]; entries [B, n_cap, D];
     kv_raw [B, R, D] whose row r is position raw_pos0 + r; out [B, T, H, D] (float32 or bfloat16)."""
@@ -279,7 +304,9 @@ class Forward:
 
     def __call__(self, weights: dict, x, cache: dict, out, *, pos0: int, out_idx=None):
         w = Weights(_p(weights["w_proj"]), _p(weights["bias_a"]), _p(weights["bias_b"]), _p(weights["ibias_a"]),
-                    _p(weights["ibias_b"]), _p(weights["w_head"]), _p(weights.get("sink")))
+                    _p(weights["ibias_b"]), _p(weights["w_head"]), _p(weights.get("sink")),
+                    _p(weights.get("gamma_q")), _p(weights.get("gamma_kv")), float(weights.get("norm_eps", 0.0)),
+                    int(weights.get("rope_dims", 0)), float(weights.get("rope_theta", 10000.0)))
         c = Cache(_p(cache["entries"]), _p(cache["keys"]), cache["entries"].shape[1], _p(cache["win"]),
                   cache["win"].shape[1], _p(cache.get("halo")), _p(cache.get("halo_out")))
         _check(load().csa_forward(ctypes.byref(self.dims), ctypes.byref(w), self.B, self.T, pos0, self.d_model,

@@ -205,6 +205,28 @@ int csa_dense_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dt
                    void* out, int out_dtype,
                    void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * QK-norm and partial RoPE ("Anatomy of a Frontier Model", bullet "QK-norm and partial RoPE":
+ * queries and compressed entries are RMS-normalised per head, RoPE turns only the last 64 of the 512
+ * dims, and each output is turned back by its own position so that only relative position remains).
+ * For B x R rows of H head vectors of D dims (dtype F32 or BF16, x and y alike), row r of sequence
+ * b at x + b*x_seq_stride + r*x_ld + h*D (elements), at position pos0 + r*pos_step:
+ *   gamma != NULL:  v = v / sqrt(mean(v^2) + eps) * gamma          (gamma [D] fp32, device)
+ *   rope_dims > 0:  the last rope_dims dims, in adjacent pairs (2i, 2i+1) of that slice, turn by
+ *                   the angle pos * rope_theta^(-2i/rope_dims): (a, b) -> (a cos - b sin,
+ *                   a sin + b cos); inverse != 0 turns by the negative angle (no norm then).
+ * y may equal x (in place, same strides); other overlaps are undefined. Norm in fp32, angles and
+ * their sine/cosine in fp64. Errors: CSA_ERR_ARG for negative sizes, odd D, rope_dims odd or
+ * outside [0, D], D > 4096, a missing pointer, rope_theta <= 0 with rope_dims > 0, or gamma with
+ * inverse. Asynchronous on `stream`; allocates nothing.
+ */
+int csa_norm_rope(int B, int R, int H, int D, int dtype,
+                  const void* x, int64_t x_ld, int64_t x_seq_stride,
+                  void* y, int64_t y_ld, int64_t y_seq_stride,
+                  const float* gamma, float eps,
+                  int rope_dims, float rope_theta, int64_t pos0, int64_t pos_step, int inverse,
+                  void* stream);
+
 /* Weights of one CSA layer (device pointers). */
 typedef struct csa_weights {
   /* Fused projection, [n_tot, d_model] row-major (one output column per row), dtype of x, with
@@ -217,6 +239,17 @@ typedef struct csa_weights {
   const float* ibias_b;  /* [m, D_I] */
   const float* w_head;   /* [H_I]    */
   const float* sink;     /* nullable [H] */
+  /* QK-norm and partial RoPE ("Anatomy of a Frontier Model", bullet "QK-norm and partial RoPE"),
+     off when gamma_q, gamma_kv are NULL and rope_dims is 0. When on, the queries (at their
+     positions), the chunk's raw KV (at its token positions) and the new entries (entry i at
+     position (i+1)*m - 1) are RMS-normalised and rotated in place before the attention, and the
+     output is rotated back by the query position (see csa_norm_rope). The caches' context rows are
+     read as stored, i.e. already normalised and rotated. */
+  const float* gamma_q;  /* nullable [D]: norm gain of the query heads (NULL: no query norm)     */
+  const float* gamma_kv; /* nullable [D]: norm gain of entries and raw KV (NULL: no such norm)    */
+  float norm_eps;        /* eps of both norms                                                     */
+  int32_t rope_dims;     /* trailing dims turned by RoPE (64), 0: none; even, <= D                */
+  float rope_theta;      /* RoPE base (10000), > 0 when rope_dims > 0                             */
 } csa_weights;
 
 /* Caches the layer reads and extends (device pointers, all of the activation dtype). */
