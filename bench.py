@@ -277,10 +277,28 @@ def bench_prefill(wl, steps, warmup):
     run_attn()
     torch.cuda.synchronize()
     attn_ms = timed_events(run_attn, steps, torch.cuda.synchronize)
-    return dict(inp=inp, ms_per_step=ms_per_step, step_ms=step_ms, idx_ms=idx_ms, attn_ms=attn_ms)
+
+    # the same step with QK-norm and partial RoPE on (gains from the seeded generator)
+    w_fid = dict(weights, **fid_device(wl.D))
+    for _ in range(warmup):
+        st(w_fid, x, wl.L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    timed_events(lambda: st(w_fid, x, wl.L), steps, torch.cuda.synchronize)
+    fid_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return dict(inp=inp, ms_per_step=ms_per_step, step_ms=step_ms, idx_ms=idx_ms, attn_ms=attn_ms, fid_ms=fid_ms)
 
 
-def bench_decode(name, steps, warmup):
+def fid_device(D):
+    """QK-norm gains (1 + 0.2 N(0,1), seeded) and RoPE on the last 64 dims, base 10000."""
+    from synth import gen as G
+    from synth.torch_io import to_device
+    g = lambda name: to_device((1.0 + 0.2 * G.normal_f32(7, name, (D,))).astype(np.float32), "f32")
+    return {"gamma_q": g("gamma_q"), "gamma_kv": g("gamma_kv"), "norm_eps": 1e-6, "rope_dims": 64,
+            "rope_theta": 10000.0}
+
+
+def bench_decode(name, steps, warmup, fid=False):
     import torch
     from compressed_sparse_attention_05_amd import layer, lib
     from synth import gen as G
@@ -302,7 +320,11 @@ def bench_decode(name, steps, warmup):
     del inp
     d = layer.dims(wl.m, wl.D, wl.H, wl.H_I, wl.D_I, wl.k, wl.W)
     N = wl.L // wl.m
-    st = layer.CSADecode(d, wl.B, N, idx_dtype=lib.CSA_MXFP4 if fp4 else lib.CSA_BF16)
+    f = None
+    if fid:
+        fd = fid_device(wl.D)
+        f = {"gamma_q": fd["gamma_q"], "eps": fd["norm_eps"], "rope_dims": fd["rope_dims"], "theta": fd["rope_theta"]}
+    st = layer.CSADecode(d, wl.B, N, idx_dtype=lib.CSA_MXFP4 if fp4 else lib.CSA_BF16, fid=f)
     flush = torch.ones(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     step = lambda: st(wl.L, t["q_idx"], t["w_head"], t["keys"], t["q"], t["entries"], t["kv_raw"],
                       q_scale=t["q_scale"], k_scale=t["k_scale"])
@@ -470,8 +492,14 @@ def main():
                      "layer_tflops": round((flops_idx + flops_attn + flops_proj) / (ms * 1e-3) / 1e12, 1)},
         },
     }
+    res["fid"] = {"what": "the same step with QK-norm (RMS norm with gains) and RoPE on the last 64 dims, "
+                          "output rotated back",
+                  "ms_per_step": round(r["fid_ms"], 3), "tokens_per_s": round(wl.B * wl.T / (r["fid_ms"] * 1e-3), 1),
+                  "overhead_frac": round(r["fid_ms"] / ms - 1.0, 4)}
     if not args.no_decode:
         res["decode"] = {n: bench_decode(n, max(args.steps, 10), 3) for n in ("decode128k", "decode1m_fp4")}
+        dfid = bench_decode("decode128k", max(args.steps, 10), 3, fid=True)
+        res["fid"]["decode128k_us_per_step"] = dfid["us_per_step"]
     if not args.no_hca:
         res["hca"] = bench_hca(min(args.steps, 5), 2)
     if not args.no_cpu_baseline:

@@ -28,11 +28,14 @@ __global__ void __launch_bounds__(kNormWaves * 64) norm_rope_kernel(NormRopeArgs
   const int64_t r = br % a.R, b = br / a.R;
   const int64_t xo = b * a.x_seq_stride + r * a.x_ld + (int64_t)h * a.D;
   const int64_t yo = b * a.y_seq_stride + r * a.y_ld + (int64_t)h * a.D;
+  // in place without the norm (the output's back-rotation) only the rotated slice is read and written
+  const bool inplace = a.x == a.y && a.x_ld == a.y_ld && a.x_seq_stride == a.y_seq_stride;
+  const int jlo = (a.gamma || !inplace) ? 0 : (a.D - a.rope_dims) / 64;
   float v[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int d = lane + 64 * j;
-    v[j] = d < a.D ? load_elem<DT>(a.x, xo + d) : 0.f;
+    v[j] = (j >= jlo && d < a.D) ? load_elem<DT>(a.x, xo + d) : 0.f;
   }
   if (a.gamma) {
     float ss = 0.f;
@@ -69,7 +72,7 @@ __global__ void __launch_bounds__(kNormWaves * 64) norm_rope_kernel(NormRopeArgs
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int d = lane + 64 * j;
-    if (d < a.D) store_elem<DT>(a.y, yo + d, v[j]);
+    if (j >= jlo && d < a.D) store_elem<DT>(a.y, yo + d, v[j]);
   }
 }
 
