@@ -35,6 +35,11 @@ Readings where the pages are silent (each is listed with its reason in the desig
   scale 1/sqrt(D); top-k ties break toward the smaller entry index; fewer than k visible entries
   means all of them are kept and the index list is padded with -1.
 
+Entry records ([ANAT] "The KV cache, recomputed"): e4m3_encode / e4m3_decode (OCP FP8 E4M3) and
+entry_pack / entry_unpack, the 584-byte record of 448 FP8 dims with 7 UE8M0 scales plus 64 bf16
+RoPE dims (readings: byte order, and the smallest power-of-two scale that keeps a 64-dim group
+within 448).
+
 QK-norm and partial RoPE ([ANAT] bullet "QK-norm and partial RoPE"): rms_norm and rope, applied by
 prefill/decode when their fid argument is given (readings: a per-dim gain, adjacent-pair rotation
 with base theta, entries rotated at the last token of their block, the window's raw KV normalised
@@ -111,6 +116,89 @@ def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     D = vals.shape[-1]
     vals = vals.reshape(vals.shape[:-1] + (D // 32, 32)) * scale[..., None]
     return vals.reshape(vals.shape[:-2] + (D,))
+
+
+# e4m3 (OCP 8-bit Floating Point Specification, E4M3): bit 7 sign, bits 6-3 exponent (bias 7), bits
+# 2-0 mantissa. Normal values 2^(e-7) * (1 + m/8) for e = 1..15, except e = 15, m = 7 (NaN);
+# subnormals (e = 0) 2^-6 * m/8; no infinities; the largest finite magnitude is 448.
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """8-bit e4m3 codes -> float64 (NaN for the two NaN codes)."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float64 -> the nearest e4m3 code, ties to the even code (mantissa bit 0 clear); magnitudes
+    above 448 saturate to 448; the sign bit is the sign of x (so -0.0 gives 0x80)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.isnan(x)):
+        raise ValueError("NaN has no e4m3 code here")
+    mags = e4m3_decode(np.arange(0x7F, dtype=np.uint8))     # codes 0x00..0x7E, ascending magnitudes
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    i = np.clip(np.searchsorted(mags, a), 1, 0x7E)          # mags[i-1] < a <= mags[i] (or a == 0)
+    lo, hi = mags[i - 1], mags[i]
+    up = (hi - a < a - lo) | ((hi - a == a - lo) & (i % 2 == 0))
+    code = np.where(up, i, i - 1).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+# The compressed-entry record ([ANAT] "The KV cache, recomputed" and bullet "QK-norm and partial
+# RoPE"): 512 numbers, the 448 position-free ones in FP8 and the 64 RoPE dims in BF16, with seven
+# one-byte UE8M0 scales and one pad byte, 584 bytes. Byte order (a reading: the pages give the sizes
+# only): e4m3 codes of dims 0..447 | bf16 of dims 448..511, little-endian | 7 scale exponents, one per
+# 64 consecutive FP8 dims | a zero pad byte.
+ENTRY_FP8_DIMS, ENTRY_GROUP, ENTRY_BYTES = 448, 64, 584
+
+
+def entry_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """UE8M0 exponent E (scale 2^(E-127)) of a group: the smallest power of two s with amax / s <=
+    448, so that no element saturates (reading); an all-zero group takes E = 127."""
+    amax = np.asarray(amax, dtype=np.float64)
+    q = np.where(amax > 0, amax, 1.0) / E4M3_MAX
+    f, e = np.frexp(q)                                     # q = f * 2^e, 0.5 <= f < 1
+    k = np.where(f == 0.5, e - 1, e)                       # ceil(log2(q))
+    E = np.where(amax > 0, k + 127, 127)
+    if np.any((E < 0) | (E > 254)):
+        raise ValueError("group magnitude outside the UE8M0 range")
+    return E.astype(np.int64)
+
+
+def entry_pack(e: np.ndarray) -> np.ndarray:
+    """Entries [..., 512] (dims 448..511 on the bf16 grid) -> records [..., 584] uint8."""
+    e = np.asarray(e, dtype=np.float64)
+    if e.shape[-1] != 512:
+        raise ValueError("entry records hold 512 dims")
+    lead = e.shape[:-1]
+    fp = e[..., :ENTRY_FP8_DIMS].reshape(lead + (ENTRY_FP8_DIMS // ENTRY_GROUP, ENTRY_GROUP))
+    E = entry_scale_exponent(np.abs(fp).max(axis=-1))
+    codes = e4m3_encode(fp / np.ldexp(1.0, E - 127)[..., None]).reshape(lead + (ENTRY_FP8_DIMS,))
+    rope = e[..., ENTRY_FP8_DIMS:]
+    if not np.array_equal(round_bf16(rope), rope):
+        raise ValueError("RoPE dims must be bf16 values")
+    bits = (rope.astype(np.float32).view(np.uint32) >> 16).astype("<u2")
+    out = np.zeros(lead + (ENTRY_BYTES,), dtype=np.uint8)
+    out[..., :448] = codes
+    out[..., 448:576] = bits.view(np.uint8).reshape(lead + (128,))
+    out[..., 576:583] = E.astype(np.uint8)
+    return out
+
+
+def entry_unpack(rec: np.ndarray) -> np.ndarray:
+    """Records [..., 584] uint8 -> entries [..., 512] float64 (exact values of the stored format)."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    lead = rec.shape[:-1]
+    E = rec[..., 576:583].astype(np.int64)
+    if np.any(E == 255):
+        raise ValueError("UE8M0 NaN scale")
+    fp = e4m3_decode(rec[..., :448]).reshape(lead + (7, 64)) * np.ldexp(1.0, E - 127)[..., None]
+    bits = np.ascontiguousarray(rec[..., 448:576]).view("<u2").reshape(lead + (64,))
+    return np.concatenate([fp.reshape(lead + (448,)), bf16_bits_to_f64(bits)], axis=-1)
 
 
 # --------------------------------------------------------------------------------------------------
@@ -443,14 +531,18 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None, fid=None):
                 n_vis=nv, scores=scores, idx=idx, out=out)
 
 
-def decode(inp: dict, wl, b: int, sink=None, fid=None):
+def decode(inp: dict, wl, b: int, sink=None, fid=None, fp8_entries=False):
     """One decode step of sequence b: the new token sits at position L (it opens a new block, so
     no compression runs), the caches hold L/m entries and the raw KV of positions L-W+1..L.
     fid (see prefill): the query is RMS-normalised and rotated at L (then stored), the caches are
-    taken as stored, and the output is rotated back by L."""
+    taken as stored, and the output is rotated back by L.
+    fp8_entries: the entry cache holds the 584-byte records of the given entries (entry_pack), so
+    the attention sees their stored values (entry_unpack)."""
     bf = wl.dtype == "bf16"
     L, m = wl.L, wl.m
     entries = _val(inp["entries"][b], bf)
+    if fp8_entries:
+        entries = entry_unpack(entry_pack(entries))
     if wl.idx_dtype == "mxfp4":
         keys = mxfp4_decode(inp["keys_codes"][b], inp["keys_scales"][b])
         q_idx = mxfp4_decode(inp["q_idx_codes"][b], inp["q_idx_scales"][b])

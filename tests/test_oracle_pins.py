@@ -586,3 +586,76 @@ def test_fid_decode_equals_prefill_of_the_last_token():
     np.testing.assert_allclose(r["q"][0], full["q"][L], atol=1e-12)
     np.testing.assert_array_equal(r["idx"][0], full["idx"][L])
     np.testing.assert_allclose(r["out"][0], full["out"][L], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------- FP8 entry records
+
+
+def test_e4m3_table_closed_forms():
+    dec = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    # spot values from the E4M3 definition
+    assert dec[0x00] == 0.0 and dec[0x01] == 2.0 ** -9 and dec[0x07] == 7 * 2.0 ** -9
+    assert dec[0x08] == 2.0 ** -6 and dec[0x38] == 1.0 and dec[0x3C] == 1.5 and dec[0x7E] == 448.0
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF])
+    np.testing.assert_array_equal(dec[0x80:0xFF], -dec[0x00:0x7F])
+    assert np.all(np.diff(dec[:0x7F]) > 0)                  # codes 0x00..0x7E ascend
+    # each binade of a normal exponent holds 8 evenly spaced values
+    for e in range(1, 15):
+        v = dec[8 * e:8 * e + 8]
+        np.testing.assert_allclose(np.diff(v), 2.0 ** (e - 10), rtol=0)
+
+
+def test_e4m3_encode_rounding():
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = O.e4m3_decode(finite)
+    np.testing.assert_array_equal(O.e4m3_encode(vals), finite)           # every value encodes to its code
+    # midpoints go to the even code, the rest to the nearest
+    assert O.e4m3_encode(np.array([1.0625]))[0] == 0x38                  # between 1.0 (0x38) and 1.125
+    assert O.e4m3_encode(np.array([1.1875]))[0] == 0x3A                  # between 1.125 and 1.25 (0x3A)
+    assert O.e4m3_encode(np.array([1.0625 + 1e-9]))[0] == 0x39
+    assert O.e4m3_encode(np.array([2.0 ** -10]))[0] == 0x00              # half the smallest subnormal
+    assert O.e4m3_encode(np.array([3 * 2.0 ** -10]))[0] == 0x02          # 1.5 subnormal steps -> even
+    assert O.e4m3_encode(np.array([500.0, -1e9]))[0] == 0x7E and O.e4m3_encode(np.array([-1e9]))[0] == 0xFE
+    assert O.e4m3_encode(np.array([-0.0]))[0] == 0x80
+    # brute force: the nearest finite value, ties to the even code
+    rng = np.random.default_rng(86)
+    x = np.concatenate([rng.standard_normal(4000) * 50, rng.standard_normal(1000) * 0.01])
+    got = O.e4m3_decode(O.e4m3_encode(x))
+    pos = vals[vals >= 0][:127]
+    for xi, gi in zip(x, got):
+        d = np.abs(pos - min(abs(xi), 448.0))
+        best = pos[d == d.min()]
+        assert abs(gi) in best
+
+
+def test_entry_record_golden():
+    g = _gold("entry_fp8_record.json")
+    e = np.zeros(512)
+    for k, v in g["nonzero_dims"].items():
+        e[int(k)] = v
+    e[448:] = g["rope_dims_value"]
+    r = O.entry_pack(e)
+    assert r.shape == (584,)
+    for k, v in g["expected_bytes"].items():
+        assert r[int(k)] == v, k
+    assert list(r[448:452]) == g["expected_rope_bytes_first4"]
+    assert list(r[576:584]) == g["expected_scales_and_pad"]
+    np.testing.assert_array_equal(O.entry_unpack(r), e)                  # these values are exact in the format
+
+
+def test_entry_record_error_bound_and_scale_choice():
+    rng = np.random.default_rng(87)
+    e = O.round_bf16(O.rms_norm(rng.standard_normal((50, 512)) * rng.uniform(0.01, 100, (50, 1)), np.ones(512), 0))
+    r = O.entry_pack(e)
+    u = O.entry_unpack(r)
+    np.testing.assert_array_equal(u[:, 448:], e[:, 448:])                # RoPE dims kept in bf16
+    E = r[:, 576:583].astype(np.int64)
+    s = np.ldexp(1.0, E - 127)                                           # [50, 7]
+    amax = np.abs(e[:, :448]).reshape(50, 7, 64).max(axis=-1)
+    assert np.all(amax / s <= 448) and np.all(amax / (s / 2) > 448)      # the smallest such power of two
+    x = e[:, :448].reshape(50, 7, 64) / s[..., None]
+    err = np.abs(u[:, :448].reshape(50, 7, 64) / s[..., None] - x)
+    binade = np.floor(np.log2(np.maximum(np.abs(x), 1e-300)))
+    half_ulp = np.where(np.abs(x) >= 2.0 ** -6, 2.0 ** (binade - 4), 2.0 ** -10)
+    assert np.all(err <= half_ulp * (1 + 1e-12))
+    assert np.all(r[:, 583] == 0)
