@@ -205,7 +205,7 @@ int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, 
               const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride,
               int64_t n_cap, const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
               int64_t raw_pos0, int64_t raw_len, const float* sink, void* out, int out_dtype, void* ws,
-              size_t ws_bytes, void* stream) {
+              size_t ws_bytes, void* stream, int entry_fmt = 0) {
   int rc = check_dims(dims, !dense);
   if (rc) return rc;
   if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
@@ -218,7 +218,9 @@ int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, 
   const int64_t H = dims->H, D = dims->D;
   if (q_ld < H * D) return fail(CSA_ERR_ARG, "q_ld < H*D");
   if (B > 1 && q_seq_stride < (int64_t)T * q_ld) return fail(CSA_ERR_ARG, "q_seq_stride too small");
-  if (B > 1 && entries_seq_stride < n_cap * D) return fail(CSA_ERR_ARG, "entries_seq_stride too small");
+  if (entry_fmt && D != 512) return fail(CSA_ERR_ARG, "entry records hold D = 512");
+  if (B > 1 && entries_seq_stride < n_cap * (entry_fmt ? (int64_t)kEntryRecordBytes : D))
+    return fail(CSA_ERR_ARG, "entries_seq_stride too small");
   if (raw_ld < D) return fail(CSA_ERR_ARG, "raw_ld < D");
   if (B > 1 && raw_seq_stride < raw_len * raw_ld) return fail(CSA_ERR_ARG, "raw_seq_stride too small");
   const int64_t need_lo = q_pos0 - dims->window + 1 > 0 ? q_pos0 - dims->window + 1 : 0;
@@ -227,8 +229,9 @@ int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, 
     return fail(CSA_ERR_ARG, "kv_raw rows [%lld, %lld] do not cover the windows [%lld, %lld]", (long long)raw_pos0,
                 (long long)(raw_pos0 + raw_len - 1), (long long)need_lo, (long long)need_hi);
   const size_t al = esize(in_dtype) == 2 ? 16 : 4;
-  if (!aligned(q, al) || !aligned(kv_raw, al) || (entries && !aligned(entries, al)))
+  if (!aligned(q, al) || !aligned(kv_raw, al) || (entries && !aligned(entries, entry_fmt ? 16 : al)))
     return fail(CSA_ERR_ARG, "misaligned q / entries / kv_raw");
+  if (entry_fmt && entries_seq_stride % 8) return fail(CSA_ERR_ARG, "record sequence stride must be a multiple of 8 bytes");
   AttnArgs a{};
   a.B = B;
   a.T = T;
@@ -256,6 +259,7 @@ int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, 
   a.raw_len = raw_len;
   a.sink = sink;
   a.out = out;
+  a.entry_fmt = entry_fmt;
   rc = check_ws(ws, ws_bytes, attn_workspace(a));
   if (rc) return rc;
   return hip_status(launch_attn(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), name);
@@ -455,6 +459,41 @@ int csa_sparse_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_d
   return attn_call("csa_sparse_attn", false, dims, B, T, q_pos0, in_dtype, q, q_ld, q_seq_stride, entries,
                    entries_seq_stride, n_cap, idx, kv_raw, raw_ld, raw_seq_stride, raw_pos0, raw_len, sink, out,
                    out_dtype, ws, ws_bytes, stream);
+}
+
+int csa_sparse_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype, const void* q, int64_t q_ld,
+                        int64_t q_seq_stride, const void* records, int64_t records_seq_stride, int64_t n_cap,
+                        const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+                        int64_t raw_pos0, int64_t raw_len, const float* sink, void* out, int out_dtype, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return attn_call("csa_sparse_attn_fp8", false, dims, B, T, q_pos0, in_dtype, q, q_ld, q_seq_stride, records,
+                   records_seq_stride, n_cap, idx, kv_raw, raw_ld, raw_seq_stride, raw_pos0, raw_len, sink, out,
+                   out_dtype, ws, ws_bytes, stream, 1);
+}
+
+int csa_entry_pack(int B, int N, int in_dtype, const void* entries, int64_t ld, int64_t seq_stride, void* records,
+                   int64_t records_seq_stride, void* stream) {
+  if (B < 0 || N < 0) return fail(CSA_ERR_ARG, "B and N must be >= 0");
+  if (!is_act_dtype(in_dtype)) return fail(CSA_ERR_ARG, "dtype must be F32 or BF16");
+  if ((int64_t)B * N == 0) return CSA_OK;
+  if (!entries || !records) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  if (ld < 512) return fail(CSA_ERR_ARG, "ld < 512");
+  if (B > 1 && (seq_stride < (int64_t)N * ld || records_seq_stride < (int64_t)N * kEntryRecordBytes))
+    return fail(CSA_ERR_ARG, "sequence stride too small");
+  if (!aligned(records, 8) || records_seq_stride % 8) return fail(CSA_ERR_ARG, "records need 8-byte alignment");
+  EntryPackArgs a{};
+  a.B = B;
+  a.N = N;
+  a.dtype = in_dtype;
+  a.entries = entries;
+  a.ld = ld;
+  a.seq_stride = seq_stride;
+  a.records = records;
+  a.rec_seq_stride = records_seq_stride;
+  hipError_t e = launch_entry_pack(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "csa_entry_pack");
+  g_err.clear();
+  return CSA_OK;
 }
 
 int csa_dense_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype, const void* q, int64_t q_ld,

@@ -38,6 +38,21 @@ __host__ __device__ __forceinline__ int64_t dense_visible(const AttnArgs& a, int
 
 // ---------------------------------------------------------------- generic
 
+constexpr int kEntryBytes = 584;  // FP8 entry record: 448 e4m3 codes | 64 bf16 | 7 UE8M0 scales | pad
+
+// Element d of a 584-byte entry record: dims < 448 are e4m3 codes (OCP E4M3: bias 7, subnormals
+// 2^-6 m/8) times 2^(E-127) of their 64-dim group; dims 448..511 are stored bf16.
+__device__ __forceinline__ float record_elem(const uint8_t* rec, int d) {
+  if (d >= 448) {
+    const uint16_t h = *reinterpret_cast<const uint16_t*>(rec + 448 + 2 * (d - 448));
+    return __uint_as_float((uint32_t)h << 16);
+  }
+  const uint32_t c = rec[d], e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  const float v = ldexpf(mag, (int)rec[576 + (d >> 6)] - 127);
+  return (c & 0x80u) ? -v : v;
+}
+
 constexpr int kGenWaves = 4;
 
 template <int DT, int OT>
@@ -68,11 +83,13 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
     for (int64_t j = 0; j < nsel + nwin; ++j) {
       int64_t off;
       const void* src;
+      bool record = false;
       if (j < nsel) {
         const int32_t e = a.dense ? (int32_t)j : idx[j];
         if (e < 0 || e >= a.n_cap) continue;
         src = a.entries;
-        off = (int64_t)b * a.entries_seq_stride + (int64_t)e * a.D;
+        record = a.entry_fmt != 0;
+        off = (int64_t)b * a.entries_seq_stride + (int64_t)e * (record ? kEntryBytes : a.D);
       } else {
         src = a.raw;
         off = (int64_t)b * a.raw_seq_stride + (wlo + (j - nsel) - a.raw_pos0) * a.raw_ld;
@@ -81,7 +98,10 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
       float part = 0.f;
       for (int jj = 0; jj < kMaxPer; ++jj) {
         const int d = lane + 64 * jj;
-        kv[jj] = (jj < per && d < a.D) ? load_elem<DT>(src, off + d) : 0.f;
+        if (record)
+          kv[jj] = (jj < per && d < a.D) ? record_elem(static_cast<const uint8_t*>(src) + off, d) : 0.f;
+        else
+          kv[jj] = (jj < per && d < a.D) ? load_elem<DT>(src, off + d) : 0.f;
         part = fmaf(qv[jj], kv[jj], part);
       }
       const float l = wave_sum(part);
@@ -443,6 +463,12 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
 // wave: after the partial logits are written, and after P V (the exchange buffer is free again).
 constexpr int kPairRing = 3;
 
+constexpr int kStageRow = 592;  // a staged 584-byte record, rounded up to 16 bytes
+size_t attn_keys_lds(const AttnArgs& a);
+// byte offset of the record staging rows (FMT 1) in the pairs kernel's dynamic LDS
+template <int NW>
+__host__ __device__ inline size_t attn_stage_offset(const AttnArgs& a);
+
 template <int NW>
 struct PairSmem {
   uint16_t kn[kPairRing][kNK][kKNS];  // 3 x 34304 B
@@ -455,7 +481,17 @@ struct PairSmem {
 // on one XCD.
 __host__ __device__ inline bool pairs_xcd_grouped(int H, int NW, int n_splits) { return H == 16 * NW && n_splits > 1; }
 
-template <int NW, int OT>
+template <int NW>
+__host__ __device__ inline size_t attn_stage_offset(const AttnArgs& a) {
+  const size_t keys = a.dense ? 4 : (size_t)(a.k + a.W + 1) * 4;
+  return (sizeof(PairSmem<NW>) - sizeof(int32_t) + keys + 15) & ~(size_t)15;
+}
+template <int NW>
+size_t pairs_lds(const AttnArgs& a) {
+  return a.entry_fmt ? attn_stage_offset<NW>(a) + (size_t)kNK * kStageRow : sizeof(PairSmem<NW>) + attn_keys_lds(a);
+}
+
+template <int NW, int OT, int FMT>
 __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit sp) {
   static_assert(NW == 2 || NW == 4 || NW == 8, "whole wave pairs, at most 8 waves");
   extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -557,26 +593,91 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
     l_run = 1.f;
   }
 
-  const uint16_t* ent = static_cast<const uint16_t*>(a.entries) + (int64_t)b * a.entries_seq_stride;
+  // entries: bf16 rows of 512 (FMT 0) or 584-byte FP8 records (FMT 1, sequence stride in bytes)
+  const uint8_t* ent = static_cast<const uint8_t*>(a.entries) +
+                       (FMT ? (int64_t)b * a.entries_seq_stride : (int64_t)b * a.entries_seq_stride * 2);
   const uint16_t* raw = static_cast<const uint16_t*>(a.raw) + (int64_t)b * a.raw_seq_stride;
   const uint32_t ring = lds_offset(&sm.kn[0][0][0]);
+  // FMT 1: record rows go by direct loads into this wave's staging rows (a record per row slot of
+  // kStageRow bytes: 36 lanes x 16 bytes for codes and bf16 dims, 2 lanes x 4 bytes for the scales
+  // and the pad), one tile ahead of the ring, and are converted into the ring slot at the point
+  // where the wave waits for its next tile. Window rows always go straight into the ring.
+  uint8_t* stage = smem_raw + attn_stage_offset<NW>(a) + (size_t)wave * kRowsPerWave * kStageRow;
+  uint32_t stage_mask = 0;  // bit j: row j of this wave's staged tile is a record
   // row r of tile `tile` into ring slot `buf`; keys past the split's end repeat its last key
   // (finite values; their logits are masked). Lane l reads the key id of row l%32 (one LDS round
-  // trip per tile), and the rows of this wave are taken from it with readlane.
+  // trip per tile), and the rows of this wave are taken from it with readlane. With FMT 1 only the
+  // window rows are loaded here, and the count of those loads is returned.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto load_tile = [&](int tile, int buf) {
+  auto row_addr = [&](int tile, int32_t& id) -> uint64_t {
     int kl = kbeg + tile * kNK + (lane & 31);
     kl = kl < kend ? kl : kend - 1;
-    const int32_t id = a.dense ? key_id(kl) : sm.keys[kl];
+    id = a.dense ? key_id(kl) : sm.keys[kl];
     // row address of row l%32, computed on the vector unit without branches
-    const uint64_t ra = id >= 0 ? (uint64_t)(ent + (int64_t)id * 512) : (uint64_t)(raw + (int64_t)(-id - 1) * a.raw_ld);
+    return id >= 0 ? (uint64_t)(ent + (int64_t)id * (FMT ? kEntryBytes : 1024))
+                   : (uint64_t)(raw + (int64_t)(-id - 1) * a.raw_ld);
+  };
+  auto readlane64 = [](uint64_t v, int r) -> uint64_t {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), r) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, r);
+  };
+  auto load_tile = [&](int tile, int buf) -> int {
+    int32_t id;
+    const uint64_t ra = row_addr(tile, id);
+    int n = 0;
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) {
       const int r = j * NW + wave_u;
-      const uint64_t rb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(ra >> 32), r) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ra, r);
-      copy_to_lds16(reinterpret_cast<const uint16_t*>(rb) + lane * 8,
+      if (FMT && __builtin_amdgcn_readlane(id, r) >= 0) continue;  // a record: staged separately
+      copy_to_lds16(reinterpret_cast<const uint16_t*>(readlane64(ra, r)) + lane * 8,
                     __builtin_amdgcn_readfirstlane(ring + (uint32_t)((buf * kNK + r) * kKNS * 2)));
+      ++n;
+    }
+    return n;
+  };
+  auto stage_records = [&](int tile) {
+    int32_t id;
+    const uint64_t ra = row_addr(tile, id);
+    stage_mask = 0;
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      const int r = j * NW + wave_u;
+      if (__builtin_amdgcn_readlane(id, r) < 0) continue;
+      const uint8_t* rec = reinterpret_cast<const uint8_t*>(readlane64(ra, r));
+      const uint32_t dst = lds_offset(stage + j * kStageRow);
+      if (lane < 36) copy_to_lds16(rec + 16 * lane, __builtin_amdgcn_readfirstlane(dst));
+      if (lane < 2) copy_to_lds4(rec + 576 + 4 * lane, __builtin_amdgcn_readfirstlane(dst + 576));
+      stage_mask |= 1u << j;
+    }
+  };
+  // staged records -> bf16 rows of ring slot `buf`. Lane l < 28 turns the 16 e4m3 codes of dims
+  // 16l..16l+15 into bf16 with its group's scale 2^(E-127) (exact: 4 significant bits; the
+  // conversion instruction was checked against the E4M3 table on this part), lanes 28..35 copy the
+  // bf16 dims 448 + 8(l-28)...
+  auto convert = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      if (!((stage_mask >> j) & 1u)) continue;  // wave-uniform
+      const int r = j * NW + wave_u;
+      const uint8_t* srow = stage + j * kStageRow;
+      const uint2 sc = *reinterpret_cast<const uint2*>(srow + 576);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(&sm.kn[buf][r][0]);
+      if (lane < 28) {
+        const int g = lane >> 2;
+        const uint32_t E = (g < 4 ? sc.x >> (8 * g) : sc.y >> (8 * (g - 4))) & 0xFFu;
+        const float scale = __uint_as_float(E << 23);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // 8 codes -> 8 bf16 at a time (fewer live registers)
+          const uint2 u = *reinterpret_cast<const uint2*>(srow + 16 * lane + 8 * h);
+          const uint32_t o0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, scale, false));
+          const uint32_t o1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, scale, true));
+          const uint32_t o2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, scale, false));
+          const uint32_t o3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, scale, true));
+          *reinterpret_cast<uint4*>(dst + 32 * lane + 16 * h) = make_uint4(o0, o1, o2, o3);
+        }
+      } else if (lane < 36) {
+        *reinterpret_cast<uint4*>(dst + 896 + 16 * (lane - 28)) = *reinterpret_cast<const uint4*>(srow + 16 * lane);
+      }
     }
   };
 
@@ -603,10 +704,25 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
 
   // q has landed before the loop, so that no wait for it stays in the loop body
   __builtin_amdgcn_s_waitcnt(0);
-  if (ntiles > 0) load_tile(0, 0);
-  if (ntiles > 1) load_tile(1, 1);
-  if (ntiles > 1) wait_vmcnt<kRowsPerWave>();
-  else wait_vmcnt<0>();
+  if (FMT) {
+    // tile 0 complete before the loop; tile 1's window rows in flight and its records staged
+    if (ntiles > 0) {
+      load_tile(0, 0);
+      stage_records(0);
+      wait_vmcnt<0>();
+      convert(0);
+    }
+    if (ntiles > 1) {
+      load_tile(1, 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the staging rows have been read
+      stage_records(1);
+    }
+  } else {
+    if (ntiles > 0) load_tile(0, 0);
+    if (ntiles > 1) load_tile(1, 1);
+    if (ntiles > 1) wait_vmcnt<kRowsPerWave>();
+    else wait_vmcnt<0>();
+  }
   __syncthreads();
 
   // Two groups of waves, half a tile apart: group 0 (waves 0-3) runs the logits and the exchange
@@ -626,6 +742,22 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
       else wait_vmcnt<0>();
     }
   };
+  // FMT 1: tile + 1 is staged (its records, issued before the window rows of tile + 2, and its own
+  // window rows): wait for all but this wave's n_next2 newest loads, convert it into its slot, then
+  // stage the records of tile + 2 (the staging rows were read by the conversion just before).
+  auto next_ready = [&](int tile, int n_next2, int nxt_slot) {
+    if (!FMT) {
+      wait_next(tile);
+      return;
+    }
+    if (tile + 1 >= ntiles) return;
+    wait_vmcnt_upto16(n_next2);
+    convert(nxt_slot);
+    if (tile + 2 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      stage_records(tile + 2);
+    }
+  };
   if (grp == 1) __syncthreads();
 
   int cur = 0;
@@ -633,7 +765,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
     const int nxt = cur == kPairRing - 1 ? 0 : cur + 1;
     const int nxt2 = nxt == kPairRing - 1 ? 0 : nxt + 1;
     // the slot of tile - 1 is free once group 1 has passed its P V of tile - 1
-    if (grp == 1 && tile + 2 < ntiles) load_tile(tile + 2, nxt2);
+    int n_next2 = 0;  // this wave's loads of tile + 2 issued at its load point (FMT 1: window rows)
+    if (grp == 1 && tile + 2 < ntiles) n_next2 = load_tile(tile + 2, nxt2);
 
     // ---- partial S^T over this wave's 256 dims; fragments read two ahead of the MFMA
     f32x16 sacc = f32x16{};
@@ -653,9 +786,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
     for (int i = 0; i < 4; ++i)
       mine[i * 64] = make_uint4(__float_as_uint(sacc[4 * i]), __float_as_uint(sacc[4 * i + 1]),
                                 __float_as_uint(sacc[4 * i + 2]), __float_as_uint(sacc[4 * i + 3]));
-    if (grp == 1) wait_next(tile);
+    if (grp == 1) next_ready(tile, n_next2, nxt);
     __syncthreads();
-    if (grp == 0 && tile + 2 < ntiles) load_tile(tile + 2, nxt2);
+    if (grp == 0 && tile + 2 < ntiles) n_next2 = load_tile(tile + 2, nxt2);
     const uint4* other = &sm.sx[wave ^ 1][0][lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -727,7 +860,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
       __builtin_amdgcn_sched_barrier(0);
     }
     // after this barrier the pair's exchange buffer can be written again
-    if (grp == 0) wait_next(tile);
+    if (grp == 0) next_ready(tile, n_next2, nxt);
     __syncthreads();
     cur = nxt;
   }
@@ -822,6 +955,8 @@ int attn_mfma_lds(const AttnArgs& a) {
 }
 
 bool use_attn_mfma(const AttnArgs& a) {
+  // records: the pairs kernel (128 heads, staging rows within the LDS) or the generic one
+  if (a.entry_fmt && (a.H != 128 || pairs_lds<8>(a) > (size_t)kMaxLds)) return false;
   return a.in_dtype == CSA_BF16 && a.D == 512 && (a.H == 64 || a.H == 128) && a.raw_ld % 4 == 0 &&
          a.q_ld % 8 == 0 && a.q_seq_stride % 8 == 0 && a.entries_seq_stride % 4 == 0 && a.raw_seq_stride % 4 == 0 &&
          attn_mfma_lds(a) <= kMaxLds;
@@ -868,15 +1003,19 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStr
 // sequence's output must not depend on what else is in the batch.
 int attn_waves(const AttnArgs& a) { return a.H == 128 ? 8 : 4; }
 
-template <int NW, int OT>
-hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
-  const int lds = (int)(sizeof(PairSmem<NW>) + attn_keys_lds(a));
+template <int NW, int OT, int FMT>
+hipError_t launch_pairs_fmt(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
+  const int lds = (int)pairs_lds<NW>(a);
   hipError_t e;
-  if ((e = allow_lds((const void*)attn_pairs<NW, OT>, lds)) != hipSuccess) return e;
+  if ((e = allow_lds((const void*)attn_pairs<NW, OT, FMT>, lds)) != hipSuccess) return e;
   const int64_t n_hg = a.H / (16 * NW);
   const int64_t blocks = pairs_xcd_grouped(a.H, NW, sp.n_splits) ? ceil_div(R, 8) * 8 * sp.n_splits : R * sp.n_splits * n_hg;
-  hipLaunchKernelGGL((attn_pairs<NW, OT>), dim3((unsigned)blocks), dim3(NW * 64), lds, s, a, sp);
+  hipLaunchKernelGGL((attn_pairs<NW, OT, FMT>), dim3((unsigned)blocks), dim3(NW * 64), lds, s, a, sp);
   return hipGetLastError();
+}
+template <int NW, int OT>
+hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
+  return a.entry_fmt ? launch_pairs_fmt<NW, OT, 1>(a, sp, R, s) : launch_pairs_fmt<NW, OT, 0>(a, sp, R, s);
 }
 
 template <int OT>

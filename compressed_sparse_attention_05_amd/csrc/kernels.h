@@ -38,6 +38,17 @@ struct NormRopeArgs {
   int inverse = 0;
 };
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t s);
+
+// 584-byte FP8 entry records of B x N entries of 512 dims (entries at b*seq_stride + n*ld).
+constexpr int kEntryRecordBytes = 584;
+struct EntryPackArgs {
+  int B = 0, N = 0, dtype = 0;
+  const void* entries = nullptr;
+  int64_t ld = 512, seq_stride = 0;
+  void* records = nullptr;
+  int64_t rec_seq_stride = 0;  // bytes
+};
+hipError_t launch_entry_pack(const EntryPackArgs& a, hipStream_t s);
 int norm_rope_max_dim();
 int compress_max_m();
 
@@ -116,6 +127,8 @@ struct AttnArgs {
   void* out;
   int dense = 0;  // attend to every visible entry in order (HCA); idx is not read and k is unused
   int m = 1;      // tokens per entry (dense only: entry i is visible to p iff (i+1)*m - 1 <= p)
+  int entry_fmt = 0;  // 0: entries are in_dtype rows of D; 1: 584-byte FP8 records (D = 512), whose
+                      // entries_seq_stride counts bytes
 };
 size_t attn_workspace(const AttnArgs& a);
 hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);

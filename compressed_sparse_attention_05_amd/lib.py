@@ -15,11 +15,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_MXFP4 = 0, 1, 2
+ENTRY_RECORD_BYTES = 584
 CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD, CSA_OP_DENSE_ATTN = \
     range(6)
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
-           "csa_norm_rope")
+           "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8")
 
 
 class CsaError(RuntimeError):
@@ -76,8 +77,11 @@ def load() -> ctypes.CDLL:
                                    i64, i64, i64, i64, vp, vp, i32, vp, sz, vp]
     lib.csa_norm_rope.argtypes = [i32, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, ctypes.c_float, i32,
                                   ctypes.c_float, i64, i64, i32, vp]
+    lib.csa_entry_pack.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, vp]
+    lib.csa_sparse_attn_fp8.argtypes = lib.csa_sparse_attn.argtypes
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
-              "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope"):
+              "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
+              "csa_sparse_attn_fp8"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -215,7 +219,9 @@ def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, ra
     position raw_pos0 + r; out [B, T, H, D] (float32 or bfloat16)."""
     _require_cuda(q, entries, idx, kv_raw, out, sink)
     B, T = q.shape[0], q.shape[1]
-    if q.stride(3) != 1 or q.stride(2) != dims.D or entries.stride(2) != 1 or entries.stride(1) != dims.D:
+    records = entries.dtype == torch.uint8          # [B, n_cap, 584] FP8 entry records
+    row = ENTRY_RECORD_BYTES if records else dims.D
+    if q.stride(3) != 1 or q.stride(2) != dims.D or entries.stride(2) != 1 or entries.stride(1) != row:
         raise ValueError("q heads and entry rows must be contiguous")
     if kv_raw.stride(2) != 1 or not out.is_contiguous() or not idx.is_contiguous():
         raise ValueError("kv_raw rows, idx and out must be contiguous")
@@ -223,11 +229,27 @@ def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, ra
     if ws is None or ws.numel() < need + 256:
         ws = _workspace(need, q.device)
     wp, wn = _aligned_ptr(ws)
-    _check(load().csa_sparse_attn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
-                                  _p(entries), entries.stride(0), entries.shape[1], _p(idx), _p(kv_raw),
-                                  kv_raw.stride(1), kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out),
-                                  _dt(out), wp, wn, _stream()))
+    fn = load().csa_sparse_attn_fp8 if records else load().csa_sparse_attn
+    _check(fn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
+              _p(entries), entries.stride(0), entries.shape[1], _p(idx), _p(kv_raw),
+              kv_raw.stride(1), kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out),
+              _dt(out), wp, wn, _stream()))
     return out
+
+
+def csa_entry_pack(entries, records=None):
+    """entries [B, N, 512] (float32 or bfloat16) -> 584-byte FP8 records [B, N, 584] (uint8)."""
+    _require_cuda(entries, records)
+    B, N, D = entries.shape
+    if D != 512 or entries.stride(2) != 1:
+        raise ValueError("entries must be [B, N, 512] with contiguous rows")
+    if records is None:
+        records = torch.empty(B, N, ENTRY_RECORD_BYTES, dtype=torch.uint8, device=entries.device)
+    if records.shape != (B, N, ENTRY_RECORD_BYTES) or records.stride(2) != 1 or records.stride(1) != ENTRY_RECORD_BYTES:
+        raise ValueError("records must be [B, N, 584] with contiguous rows")
+    _check(load().csa_entry_pack(B, N, _dt(entries), _p(entries), entries.stride(1), entries.stride(0), _p(records),
+                                 records.stride(0), _stream()))
+    return records
 
 
 def csa_hca_compress(cv, z, bias, entries, *, pos0: int, m: int):

@@ -227,6 +227,38 @@ int csa_norm_rope(int B, int R, int H, int D, int dtype,
                   int rope_dims, float rope_theta, int64_t pos0, int64_t pos_step, int inverse,
                   void* stream);
 
+/*
+ * The pages' compressed-entry record ("Anatomy of a Frontier Model", section "The KV cache,
+ * recomputed": 512 numbers, 448 in FP8 and the 64 RoPE dims in BF16, with seven one-byte UE8M0
+ * scales and a pad byte, 584 bytes; bullet "QK-norm and partial RoPE": the 448 position-free dims
+ * are the FP8 ones). Byte layout: e4m3 codes of dims 0..447 | bf16 of dims 448..511, little-endian |
+ * scale exponents E_0..E_6 | 0. Dims 64g..64g+63 have scale 2^(E_g - 127), the smallest power of two
+ * that keeps the group's largest magnitude within 448 (127 for an all-zero group); codes are OCP
+ * E4M3, rounded to nearest with ties to even, the sign bit from the value's sign.
+ *
+ * csa_entry_pack: entries [B, N, 512] (dtype F32 or BF16; row n of sequence b at
+ * b*seq_stride + n*ld elements, ld >= 512) -> records (row n of sequence b at
+ * b*records_seq_stride + n*584 bytes; 8-byte aligned). F32 RoPE dims are rounded to bf16 (RNE).
+ * CSA_ERR_ARG on negative sizes, a NULL pointer, small strides or misalignment.
+ */
+int csa_entry_pack(int B, int N, int in_dtype, const void* entries, int64_t ld, int64_t seq_stride,
+                   void* records, int64_t records_seq_stride, void* stream);
+
+/*
+ * csa_sparse_attn over an entry cache of 584-byte records (see csa_entry_pack): as
+ * csa_sparse_attn, with `records` [B, n_cap, 584] bytes (16-byte aligned base, sequence stride in
+ * bytes, a multiple of 8) in place of the entries; D must be 512. q and kv_raw keep in_dtype. The
+ * attention sees each entry's stored values exactly (FP8 times its scale, bf16 RoPE dims). The
+ * workspace is the one csa_workspace_size gives for CSA_OP_SPARSE_ATTN.
+ */
+int csa_sparse_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+                        const void* q, int64_t q_ld, int64_t q_seq_stride,
+                        const void* records, int64_t records_seq_stride, int64_t n_cap,
+                        const int32_t* idx,
+                        const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
+                        int64_t raw_len, const float* sink, void* out, int out_dtype,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /* Weights of one CSA layer (device pointers). */
 typedef struct csa_weights {
   /* Fused projection, [n_tot, d_model] row-major (one output column per row), dtype of x, with

@@ -1,0 +1,140 @@
+"""GPU parity of the 584-byte FP8 entry records ("Anatomy of a Frontier Model", section "The KV
+cache, recomputed"): csa_entry_pack bit for bit against the oracle's entry_pack, and attention over
+a record cache (csa_sparse_attn_fp8; pairs kernel for 128 heads, generic kernel otherwise) against
+the oracle's attention over the records' stored values."""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_05_amd import layer, lib
+from synth.torch_io import to_device
+from synth.workloads import get
+from tests.csa_testlib import O, G, TOL, check_idx_rows, decode_tensors, dims_of, max_err, run_decode, tensor_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _entries(seed, B, N, dtype="bf16"):
+    """entries with per-row magnitudes from 1e-3 to 1e3, an all-zero group, values at the 448 edge"""
+    x = G.normal_f32(seed, "fp8_ent", (B, N, 512)).astype(np.float64)
+    x *= np.exp(np.linspace(np.log(1e-3), np.log(1e3), N))[None, :, None]
+    x[:, 1, 64:128] = 0.0                        # an all-zero group
+    x[:, 2, :64] = 0.0
+    x[:, 2, 5] = 448.0 * 2.0 ** -3               # exactly on a scale boundary
+    x[:, 3, 70] = -449.0 * 2.0 ** -5             # just above one
+    if dtype == "bf16":
+        bits = G.f32_to_bf16_bits(x.astype(np.float32))
+        return to_device(bits, "bf16"), O.bf16_bits_to_f64(bits)
+    x32 = x.astype(np.float32)
+    x32[..., 448:] = O.round_bf16(x32[..., 448:].astype(np.float64)).astype(np.float32)  # RoPE dims on the bf16 grid
+    return to_device(x32, "f32"), x32.astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_entry_pack_bit_exact(dtype):
+    B, N = 2, 300
+    dev, host = _entries(100, B, N, dtype)
+    rec = lib.csa_entry_pack(dev)
+    got = rec.cpu().numpy()
+    want = O.entry_pack(host)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_entry_pack_strided_into_a_larger_cache():
+    # rows of a wider buffer into the middle of a record cache; nothing else is written
+    B, N = 3, 40
+    dev, host = _entries(101, B, N)
+    wide = torch.zeros(B, N, 600, dtype=torch.bfloat16, device="cuda")
+    wide[:, :, :512] = dev
+    cache = torch.full((B, N + 10, 584), 0xAB, dtype=torch.uint8, device="cuda")
+    lib.csa_entry_pack(wide[:, :, :512], cache[:, 5:5 + N])
+    c = cache.cpu().numpy()
+    np.testing.assert_array_equal(c[:, 5:5 + N], O.entry_pack(host))
+    assert np.all(c[:, :5] == 0xAB) and np.all(c[:, 5 + N:] == 0xAB)
+
+
+def _attn_case(seed, B, T, H, n_cap, k, q_pos0, q_dtype="bf16"):
+    wl = get("decode128k").with_(H=H, k=k)
+    d = dims_of(wl)
+    ent_dev, ent = _entries(seed, B, n_cap)
+    # entries of unit-scale magnitude for the attention (the ramp above is for the format)
+    bits = G.f32_to_bf16_bits(G.normal_f32(seed, "fp8_attn_ent", (B, n_cap, 512)))
+    ent_dev, ent = to_device(bits, "bf16"), O.bf16_bits_to_f64(bits)
+    rec = lib.csa_entry_pack(ent_dev)
+    qf = G.normal_f32(seed, "fp8_q", (B, T, H, 512))
+    if q_dtype == "bf16":
+        qb = G.f32_to_bf16_bits(qf)
+        q_dev, q = to_device(qb, "bf16"), O.bf16_bits_to_f64(qb)
+    else:
+        q_dev, q = to_device(qf, "f32"), qf.astype(np.float64)
+    raw_pos0 = q_pos0 - 127
+    R = q_pos0 + T - raw_pos0
+    rf = G.normal_f32(seed, "fp8_raw", (B, R, 512))
+    if q_dtype == "bf16":
+        rb = G.f32_to_bf16_bits(rf)
+        raw_dev, raw = to_device(rb, "bf16"), O.bf16_bits_to_f64(rb)
+    else:
+        raw_dev, raw = to_device(rf, "f32"), rf.astype(np.float64)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.stack([np.sort(rng.choice(n_cap, k, replace=False)) for _ in range(T)]) for _ in range(B)])
+    idx[:, :, -3:] = -1                            # padding
+    idx = np.sort(np.where(idx < 0, 1 << 30, idx), axis=-1)
+    idx = np.where(idx >= 1 << 30, -1, idx).astype(np.int32)
+    out = torch.empty(B, T, H, 512, dtype=torch.float32, device="cuda")
+    lib.csa_sparse_attn(d, q_dev, rec, to_device(idx, "i32"), raw_dev, out, q_pos0=q_pos0, raw_pos0=raw_pos0)
+    stored = O.entry_unpack(O.entry_pack(ent))
+    return out, q, stored, idx, raw, raw_pos0
+
+
+@pytest.mark.parametrize("B,T,H,k", [(2, 1, 128, 1024), (1, 72, 128, 512), (2, 5, 64, 256)])
+def test_sparse_attn_over_records(B, T, H, k):
+    # 128 heads: the pairs kernel (decode splits at T = 1, whole rows at T = 72); 64 heads: generic
+    n_cap, q_pos0 = 3000, 4 * 3000 + 7
+    out, q, stored, idx, raw, raw_pos0 = _attn_case(102 + T, B, T, H, n_cap, k, q_pos0)
+    got = tensor_f64(out)
+    for b in range(B):
+        want = O.sparse_attention(q[b], stored[b], idx[b], raw[b], raw_pos0, q_pos0 + np.arange(T), 128)
+        assert max_err(got[b], want) <= TOL["bf16"]
+
+
+def test_sparse_attn_over_records_fp32_queries():
+    # fp32 q and window rows with a record cache take the generic kernel
+    out, q, stored, idx, raw, raw_pos0 = _attn_case(110, 1, 3, 128, 800, 64, 4 * 800, q_dtype="f32")
+    want = O.sparse_attention(q[0], stored[0], idx[0], raw[0], raw_pos0, 4 * 800 + np.arange(3), 128)
+    assert max_err(tensor_f64(out[0]), want) <= 1e-4
+
+
+def _decode_records(wl, t):
+    t = dict(t)
+    t["entries"] = lib.csa_entry_pack(t["entries"])
+    return run_decode(wl, t)
+
+
+def test_decode_over_records_small_and_batch_invariance():
+    wl = get("decode128k").with_(B=64, L=4 * 2500)
+    inp = G.make_inputs(wl)
+    t = decode_tensors(wl, inp)
+    st = _decode_records(wl, t)
+    for b in (0, 37, 63):
+        r = O.decode(inp, wl, b, fp8_entries=True)
+        gidx = st.idx[b].cpu().numpy()
+        check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
+        ref = O.sparse_attention(r["q"], r["entries"], gidx, r["raw"], wl.L - (wl.W - 1), np.array([wl.L]), wl.W)
+        assert max_err(tensor_f64(st.out[b]), ref) <= TOL["bf16"]
+    # a sequence alone gives the bits it gets in the batch
+    one = {k: (v[37:38] if (v is not None and k != "w_head") else v) for k, v in t.items()}
+    solo = _decode_records(wl.with_(B=1), one)
+    assert torch.equal(solo.out[0], st.out[37])
+
+
+def test_full_decode128k_over_records_sampled():
+    wl = get("decode128k")
+    inp = G.make_inputs(wl)
+    t = decode_tensors(wl, inp)
+    st = _decode_records(wl, t)
+    for b in (0, 63):
+        r = O.decode(inp, wl, b, fp8_entries=True)
+        gidx = st.idx[b].cpu().numpy()
+        check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
+        ref = O.sparse_attention(r["q"], r["entries"], gidx, r["raw"], wl.L - (wl.W - 1), np.array([wl.L]), wl.W)
+        assert max_err(tensor_f64(st.out[b]), ref) <= TOL["bf16"]
