@@ -201,6 +201,27 @@ int validate_index(const csa_dims* d, int B, int T, int64_t q_pos0, int idx_dtyp
   return CSA_OK;
 }
 
+// Workspace of csa_decode_step: the contiguous window, the rotated query, one compressed entry
+// per sequence (records), the selected indices, and the index / attention scratch.
+struct DecodeWs {
+  size_t win, q, ent, idx, scratch, total;
+};
+DecodeWs decode_ws(const csa_dims* d, int B, int64_t n_cap, int dtype) {
+  const size_t es = dtype == CSA_F32 ? 4 : 2;
+  DecodeWs w{};
+  w.win = 0;
+  w.q = w.win + align256((size_t)B * d->window * d->D * es);
+  w.ent = w.q + align256((size_t)B * d->H * d->D * es);
+  w.idx = w.ent + align256((size_t)B * d->D * es);
+  w.scratch = w.idx + align256((size_t)B * d->top_k * 4);
+  IndexArgs ia = make_index_args(d, B, 1, 0, dtype, nullptr, 0, 0, nullptr, nullptr, 0, nullptr, 0, nullptr, n_cap,
+                                 nullptr, nullptr);
+  const size_t iw = index_topk_workspace(ia);
+  const size_t aw = attn_workspace(sizing_attn(d, B, 1, dtype));
+  w.total = w.scratch + align256(iw > aw ? iw : aw);
+  return w;
+}
+
 int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
               const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride,
               int64_t n_cap, const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
@@ -297,6 +318,12 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
       a.n_cap = n_cap;
       a.q_pos0 = n_cap * dims->m;  // every entry visible: the most keys a row can have
       *bytes = (int64_t)attn_workspace(a);
+      return CSA_OK;
+    }
+    case CSA_OP_DECODE_STEP: {
+      int rc = check_dims(dims);
+      if (rc) return rc;
+      *bytes = (int64_t)decode_ws(dims, B, n_cap, idx_dtype).total;
       return CSA_OK;
     }
     case CSA_OP_TOPK_FROM_SCORES: {
@@ -542,6 +569,149 @@ int csa_norm_rope(int B, int R, int H, int D, int dtype, const void* x, int64_t 
   a.inverse = inverse ? 1 : 0;
   hipError_t e = launch_norm_rope(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_status(e, "csa_norm_rope");
+  g_err.clear();
+  return CSA_OK;
+}
+
+int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t pos, int dtype, const void* q,
+                    const void* q_idx, const void* kv, const void* comp, const csa_decode_state* st, void* out,
+                    int out_dtype, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!w || !st) return fail(CSA_ERR_ARG, "weights or state is NULL");
+  if (B < 0) return fail(CSA_ERR_ARG, "B must be >= 0");
+  if (!is_act_dtype(dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
+  if (B == 0) return CSA_OK;
+  const int m = dims->m, D = dims->D, DI = dims->D_I, H = dims->H, HI = dims->H_I, W = dims->window;
+  const int64_t n_cap = st->n_cap;
+  if (pos < 0 || (pos + 1) / m > n_cap) return fail(CSA_ERR_ARG, "pos=%lld outside the entry capacity", (long long)pos);
+  if (!q || !q_idx || !kv || !comp || !out || !st->entries || !st->keys || !st->win || !st->block)
+    return fail(CSA_ERR_ARG, "NULL tensor or state pointer");
+  if (!w->bias_a || !w->bias_b || !w->ibias_a || !w->ibias_b || !w->w_head) return fail(CSA_ERR_ARG, "NULL weight pointer");
+  if (st->entry_fmt != 0 && st->entry_fmt != 1) return fail(CSA_ERR_ARG, "entry_fmt must be 0 or 1");
+  if (st->entry_fmt && D != 512) return fail(CSA_ERR_ARG, "entry records hold D = 512");
+  const bool fid = w->gamma_q || w->gamma_kv || w->rope_dims != 0;
+  if (fid && (w->rope_dims < 0 || w->rope_dims > D || w->rope_dims % 2 || (w->rope_dims > 0 && !(w->rope_theta > 0.f)) ||
+              !(w->norm_eps >= 0.f)))
+    return fail(CSA_ERR_ARG, "QK-norm / RoPE parameters: rope_dims even in [0, D], rope_theta > 0, norm_eps >= 0");
+  const DecodeWs L = decode_ws(dims, B, n_cap, dtype);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int es = esize(dtype);
+  const int64_t nc = 4LL * D + 4LL * DI;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* blk = static_cast<uint8_t*>(st->block);
+  uint8_t* cur = blk + (size_t)m * nc * es;  // the current block's rows
+
+  // the token's compressor inputs and raw KV join the state
+  hipError_t e = launch_copy_rows(B, 1, (int)nc, es, comp, nc, nc, cur + (size_t)(pos % m) * nc * es, nc,
+                                  2LL * m * nc, s);
+  uint8_t* wrow = static_cast<uint8_t*>(st->win) + (size_t)(pos % W) * D * es;
+  if (e == hipSuccess) e = launch_copy_rows(B, 1, D, es, kv, D, D, wrow, D, (int64_t)W * D, s);
+  if (e != hipSuccess) return hip_status(e, "csa_decode_step: state rows");
+  if (fid) {
+    rc = csa_norm_rope(B, 1, 1, D, dtype, wrow, D, (int64_t)W * D, wrow, D, (int64_t)W * D, w->gamma_kv, w->norm_eps,
+                       w->rope_dims, w->rope_theta, pos, 1, 0, stream);
+    if (rc) return rc;
+  }
+
+  // a completed block: its entry and indexer key (own block = series a, previous block = series b)
+  if ((pos + 1) % m == 0) {
+    const int64_t i = (pos + 1) / m - 1;
+    CompressArgs a{};
+    a.B = B;
+    a.n_new = 1;
+    a.m = m;
+    a.first_entry = i;
+    a.in_dtype = dtype;
+    a.out_dtype = dtype;
+    a.ld = nc;
+    a.seq_stride = 2LL * m * nc;
+    a.halo_ld = nc;
+    a.halo_seq_stride = 2LL * m * nc;
+    const bool has_prev = i >= 1;
+    auto run = [&](int c, int64_t col, const float* ba, const float* bb, void* dst, int64_t dst_seq,
+                   int64_t out_first) {
+      CompressArgs x = a;
+      x.c = c;
+      x.ca = cur + (size_t)col * es;
+      x.za = cur + (size_t)(col + c) * es;
+      x.cb = cur + (size_t)(col + 2 * c) * es;
+      x.zb = cur + (size_t)(col + 3 * c) * es;
+      x.halo_cb = has_prev ? blk + (size_t)(col + 2 * c) * es : x.ca;
+      x.halo_zb = has_prev ? blk + (size_t)(col + 3 * c) * es : x.za;
+      x.bias_a = ba;
+      x.bias_b = bb;
+      x.entries = dst;
+      x.entries_seq_stride = dst_seq;
+      x.out_first = out_first;
+      x.aligned16 = aligned(x.ca, 16) && aligned(x.za, 16) && aligned(x.cb, 16) && aligned(x.zb, 16) &&
+                    aligned(x.halo_cb, 16) && aligned(x.halo_zb, 16) && aligned(dst, 16) && (nc * es) % 16 == 0;
+      return launch_compress(x, s);
+    };
+    // the entry: into its cache row, or into a scratch row that is then packed into a record
+    void* erow = st->entry_fmt ? (void*)(base + L.ent) : static_cast<uint8_t*>(st->entries) + (size_t)i * D * es;
+    e = run(D, 0, w->bias_a, w->bias_b, st->entry_fmt ? (void*)(base + L.ent) : st->entries,
+            st->entry_fmt ? (int64_t)D : n_cap * D, st->entry_fmt ? 0 : -1);
+    if (e == hipSuccess) e = run(DI, 4LL * D, w->ibias_a, w->ibias_b, st->keys, n_cap * DI, -1);
+    if (e != hipSuccess) return hip_status(e, "csa_decode_step: compress");
+    const int64_t eseq = st->entry_fmt ? (int64_t)D : n_cap * D;
+    if (fid) {
+      rc = csa_norm_rope(B, 1, 1, D, dtype, erow, D, eseq, erow, D, eseq, w->gamma_kv, w->norm_eps, w->rope_dims,
+                         w->rope_theta, pos, 1, 0, stream);
+      if (rc) return rc;
+    }
+    if (st->entry_fmt) {
+      rc = csa_entry_pack(B, 1, dtype, erow, D, D, static_cast<uint8_t*>(st->entries) + (size_t)i * kEntryRecordBytes,
+                          n_cap * kEntryRecordBytes, stream);
+      if (rc) return rc;
+    }
+    // the block becomes the previous one
+    e = launch_copy_rows(B, m, (int)nc, es, cur, nc, 2LL * m * nc, blk, nc, 2LL * m * nc, s);
+    if (e != hipSuccess) return hip_status(e, "csa_decode_step: block shift");
+  }
+
+  // the query, normalised and rotated at pos
+  const void* qq = q;
+  if (fid) {
+    rc = csa_norm_rope(B, 1, H, D, dtype, q, (int64_t)H * D, (int64_t)H * D, base + L.q, (int64_t)H * D,
+                       (int64_t)H * D, w->gamma_q, w->norm_eps, w->rope_dims, w->rope_theta, pos, 1, 0, stream);
+    if (rc) return rc;
+    qq = base + L.q;
+  }
+  int32_t* idx = out_idx ? out_idx : reinterpret_cast<int32_t*>(base + L.idx);
+  void* scratch = base + L.scratch;
+  const size_t scratch_bytes = L.total - L.scratch;
+  rc = csa_index_topk(dims, B, 1, pos, dtype, q_idx, (int64_t)HI * DI, (int64_t)HI * DI, nullptr, w->w_head, 0,
+                      st->keys, n_cap * DI, nullptr, n_cap, idx, nullptr, scratch, scratch_bytes, stream);
+  if (rc) return rc;
+  // the window [pos - raw_len + 1, pos] out of the ring, in position order
+  const int64_t raw_len = pos + 1 < W ? pos + 1 : W;
+  const int64_t raw_pos0 = pos - raw_len + 1;
+  const int r0 = (int)(raw_pos0 % W);
+  const int n1 = (int)(raw_len < W - r0 ? raw_len : W - r0);
+  uint8_t* wt = base + L.win;
+  const uint8_t* ring = static_cast<const uint8_t*>(st->win);
+  e = launch_copy_rows(B, n1, D, es, ring + (size_t)r0 * D * es, D, (int64_t)W * D, wt, D, (int64_t)W * D, s);
+  if (e == hipSuccess && raw_len > n1)
+    e = launch_copy_rows(B, (int)(raw_len - n1), D, es, ring, D, (int64_t)W * D, wt + (size_t)n1 * D * es, D,
+                         (int64_t)W * D, s);
+  if (e != hipSuccess) return hip_status(e, "csa_decode_step: window");
+  if (st->entry_fmt)
+    rc = csa_sparse_attn_fp8(dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries,
+                             n_cap * kEntryRecordBytes, n_cap, idx, wt, D, (int64_t)W * D, raw_pos0, raw_len, w->sink,
+                             out, out_dtype, scratch, scratch_bytes, stream);
+  else
+    rc = csa_sparse_attn(dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries, n_cap * D, n_cap,
+                         idx, wt, D, (int64_t)W * D, raw_pos0, raw_len, w->sink, out, out_dtype, scratch,
+                         scratch_bytes, stream);
+  if (rc) return rc;
+  if (fid && w->rope_dims > 0) {
+    rc = csa_norm_rope(B, 1, H, D, out_dtype, out, (int64_t)H * D, (int64_t)H * D, out, (int64_t)H * D,
+                       (int64_t)H * D, nullptr, 0.f, w->rope_dims, w->rope_theta, pos, 1, 1, stream);
+    if (rc) return rc;
+  }
   g_err.clear();
   return CSA_OK;
 }

@@ -180,7 +180,8 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   float out[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) out[v] = num[v] / den[v];
-  VO::store(a.entries, (int64_t)b * a.entries_seq_stride + i * a.c + j0, out);
+  const int64_t orow = (a.out_first >= 0 ? a.out_first : a.first_entry) + e;
+  VO::store(a.entries, (int64_t)b * a.entries_seq_stride + orow * a.c + j0, out);
 }
 
 template <int DI, int DO>

@@ -19,6 +19,7 @@ struct CompressArgs {
   bool aligned16;
   bool overlap = true;  // pool the previous block too (CSA); false: own block only (HCA)
   int group = 1;        // threads per (entry, channel vector); set by launch_compress
+  int64_t out_first = -1;  // row of `entries` receiving the first new entry (-1: first_entry)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 

@@ -68,3 +68,33 @@ class CSADecode:
         if f and f.get("rope_dims", 0):
             lib.csa_norm_rope(self.out, pos0=L, rope_dims=f["rope_dims"], theta=f.get("theta", 10000.0), inverse=True)
         return self.out
+
+
+class CSADecodeState:
+    """Token-by-token decode of B sequences over a state cache (entries, indexer keys, a ring of the
+    last `window` raw KV rows, the compressor inputs of the previous and current block); when a token
+    completes its block the entry and key are compressed into the caches (csa_decode_step).
+    records=True keeps the entries as 584-byte FP8 records."""
+
+    def __init__(self, d: lib.Dims, B: int, n_cap: int, dtype=torch.bfloat16, out_dtype=torch.float32,
+                 records: bool = False, device="cuda"):
+        self.d, self.B = d, B
+        if records:
+            self.entries = torch.zeros(B, n_cap, lib.ENTRY_RECORD_BYTES, dtype=torch.uint8, device=device)
+        else:
+            self.entries = torch.zeros(B, n_cap, d.D, dtype=dtype, device=device)
+        self.keys = torch.zeros(B, n_cap, d.D_I, dtype=dtype, device=device)
+        self.win = torch.zeros(B, d.window, d.D, dtype=dtype, device=device)
+        self.block = torch.zeros(B, 2 * d.m, 4 * d.D + 4 * d.D_I, dtype=dtype, device=device)
+        self.out = torch.empty(B, d.H, d.D, dtype=out_dtype, device=device)
+        self.idx = torch.empty(B, d.top_k, dtype=torch.int32, device=device)
+        code = lib.CSA_BF16 if dtype == torch.bfloat16 else lib.CSA_F32
+        self.ws = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_DECODE_STEP, d, B, 1, n_cap, 0, code), device)
+
+    def state(self) -> dict:
+        return {"entries": self.entries, "keys": self.keys, "win": self.win, "block": self.block}
+
+    def step(self, weights: dict, pos: int, q, q_idx, kv, comp):
+        return lib.csa_decode_step(self.d, weights, pos, q, q_idx, kv, comp, self.state(), self.out,
+                                   out_idx=self.idx, ws=self.ws)
+

@@ -16,11 +16,11 @@ LIB_PATH = os.path.join(_PKG, "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_MXFP4 = 0, 1, 2
 ENTRY_RECORD_BYTES = 584
-CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD, CSA_OP_DENSE_ATTN = \
-    range(6)
+CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD, CSA_OP_DENSE_ATTN, \
+    CSA_OP_DECODE_STEP = range(7)
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
-           "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8")
+           "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step")
 
 
 class CsaError(RuntimeError):
@@ -46,6 +46,11 @@ class Cache(ctypes.Structure):
     _fields_ = [("entries", ctypes.c_void_p), ("keys", ctypes.c_void_p), ("n_cap", ctypes.c_int64),
                 ("win", ctypes.c_void_p), ("win_cap", ctypes.c_int64), ("halo", ctypes.c_void_p),
                 ("halo_out", ctypes.c_void_p)]
+
+
+class DecodeState(ctypes.Structure):
+    _fields_ = [("entries", ctypes.c_void_p), ("entry_fmt", ctypes.c_int32), ("keys", ctypes.c_void_p),
+                ("n_cap", ctypes.c_int64), ("win", ctypes.c_void_p), ("block", ctypes.c_void_p)]
 
 
 _lib = None
@@ -78,10 +83,12 @@ def load() -> ctypes.CDLL:
     lib.csa_norm_rope.argtypes = [i32, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, ctypes.c_float, i32,
                                   ctypes.c_float, i64, i64, i32, vp]
     lib.csa_entry_pack.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, vp]
+    lib.csa_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i64, i32, vp, vp, vp, vp,
+                                    ctypes.POINTER(DecodeState), vp, i32, vp, vp, sz, vp]
     lib.csa_sparse_attn_fp8.argtypes = lib.csa_sparse_attn.argtypes
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
-              "csa_sparse_attn_fp8"):
+              "csa_sparse_attn_fp8", "csa_decode_step"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -306,6 +313,36 @@ def csa_dense_attn(dims: Dims, q, entries, kv_raw, out, *, q_pos0: int, raw_pos0
     return out
 
 
+def weights_struct(weights: dict) -> Weights:
+    return Weights(_p(weights.get("w_proj")), _p(weights["bias_a"]), _p(weights["bias_b"]), _p(weights["ibias_a"]),
+                   _p(weights["ibias_b"]), _p(weights["w_head"]), _p(weights.get("sink")),
+                   _p(weights.get("gamma_q")), _p(weights.get("gamma_kv")), float(weights.get("norm_eps", 0.0)),
+                   int(weights.get("rope_dims", 0)), float(weights.get("rope_theta", 10000.0)))
+
+
+def csa_decode_step(dims: Dims, weights: dict, pos: int, q, q_idx, kv, comp, state: dict, out, *, out_idx=None,
+                    ws=None):
+    """One decode step of B sequences at position pos over a decode state (see include/csa.h):
+    q [B, H, D], q_idx [B, H_I, D_I], kv [B, D], comp [B, 4D + 4D_I]; state holds entries (rows, or
+    uint8 records [B, n_cap, 584]), keys, win [B, window, D], block [B, 2m, 4D + 4D_I]."""
+    _require_cuda(q, q_idx, kv, comp, out, out_idx)
+    for t in (q, q_idx, kv, comp, out):
+        if not t.is_contiguous():
+            raise ValueError("decode step tensors must be contiguous")
+    B = q.shape[0]
+    ent = state["entries"]
+    st = DecodeState(_p(ent), 1 if ent.dtype == torch.uint8 else 0, _p(state["keys"]), ent.shape[1],
+                     _p(state["win"]), _p(state["block"]))
+    need = csa_workspace_size(CSA_OP_DECODE_STEP, dims, B, 1, ent.shape[1], 0, _dt(q))
+    if ws is None or ws.numel() < need + 256:
+        ws = _workspace(need, q.device)
+    wp, wn = _aligned_ptr(ws)
+    w = weights_struct(weights)
+    _check(load().csa_decode_step(ctypes.byref(dims), ctypes.byref(w), B, pos, _dt(q), _p(q), _p(q_idx), _p(kv),
+                                  _p(comp), ctypes.byref(st), _p(out), _dt(out), _p(out_idx), wp, wn, _stream()))
+    return out
+
+
 class Forward:
     """csa_forward with a reusable workspace (allocated once per shape, outside the timed call)."""
 
@@ -325,10 +362,7 @@ class Forward:
         return raw.view(torch.float32 if es == 4 else torch.bfloat16).view(self.B * self.T, n_tot)
 
     def __call__(self, weights: dict, x, cache: dict, out, *, pos0: int, out_idx=None):
-        w = Weights(_p(weights["w_proj"]), _p(weights["bias_a"]), _p(weights["bias_b"]), _p(weights["ibias_a"]),
-                    _p(weights["ibias_b"]), _p(weights["w_head"]), _p(weights.get("sink")),
-                    _p(weights.get("gamma_q")), _p(weights.get("gamma_kv")), float(weights.get("norm_eps", 0.0)),
-                    int(weights.get("rope_dims", 0)), float(weights.get("rope_theta", 10000.0)))
+        w = weights_struct(weights)
         c = Cache(_p(cache["entries"]), _p(cache["keys"]), cache["entries"].shape[1], _p(cache["win"]),
                   cache["win"].shape[1], _p(cache.get("halo")), _p(cache.get("halo_out")))
         _check(load().csa_forward(ctypes.byref(self.dims), ctypes.byref(w), self.B, self.T, pos0, self.d_model,

@@ -58,6 +58,7 @@ extern "C" {
 #define CSA_OP_SPARSE_ATTN 3
 #define CSA_OP_FORWARD 4
 #define CSA_OP_DENSE_ATTN 5  /* csa_dense_attn; n_cap bounds the entries a row can see */
+#define CSA_OP_DECODE_STEP 6 /* csa_decode_step; T = 1, idx_dtype = the activation dtype */
 
 /* Layer dimensions. */
 typedef struct csa_dims {
@@ -298,6 +299,46 @@ typedef struct csa_cache {
   void* halo_out;        /* nullable [B, m, 2D + 2D_I]: receives this chunk's last block (needs
                             T % m == 0), i.e. the next chunk's halo                               */
 } csa_cache;
+
+/* Decode state of B sequences (device pointers, activation dtype unless stated). */
+typedef struct csa_decode_state {
+  void* entries;         /* [B, n_cap, D] rows, or [B, n_cap, 584] FP8 records when entry_fmt = 1  */
+  int32_t entry_fmt;     /* 0: rows of the activation dtype, 1: FP8 records (see csa_entry_pack)    */
+  void* keys;            /* [B, n_cap, D_I] indexer keys                                             */
+  int64_t n_cap;
+  void* win;             /* [B, window, D] ring of raw KV: position p in row p % window              */
+  void* block;           /* [B, 2m, 4D + 4D_I] compressor inputs ca|za|cb|zb (D each) and the
+                            indexer's ica|iza|icb|izb (D_I each) of the previous complete block (rows
+                            0..m-1) and of the current block (rows m..2m-1, filled as tokens come)    */
+} csa_decode_state;
+
+/*
+ * One decode step of B sequences, all at position pos (the layer of "Anatomy of a Frontier Model",
+ * "The attention: compress, then select", run token by token): the new token's compressor inputs
+ * go to row m + pos % m of state->block and its raw KV to window row pos % window; when the token
+ * completes its block ((pos+1) % m == 0) entry i = (pos+1)/m - 1 and its indexer key are compressed
+ * from the block and the previous one (the CSA pooling over both) and stored (with QK-norm and
+ * RoPE at position (i+1)m - 1 when the weights carry them; packed into a record when entry_fmt = 1),
+ * and the block becomes the previous one. Then the query (normalised and rotated at pos when the
+ * weights carry the options) is indexed against the floor((pos+1)/m) visible entries, the top-k
+ * are selected, and the attention runs over them plus the window [max(0, pos-window+1), pos]; the
+ * output is rotated back by pos when RoPE is on.
+ *   q      [B, H, D], q_idx [B, H_I, D_I], kv [B, D], comp [B, 4D + 4D_I] (columns as in block),
+ *          each sequence contiguous (sequence strides H*D, H_I*D_I, D, 4D + 4D_I).
+ *   w      the layer weights: bias_a/bias_b, ibias_a/ibias_b, w_head, sink, the QK-norm / RoPE
+ *          fields (w_proj is not used: the step takes projected rows).
+ *   out    [B, H, D] (out_dtype); out_idx nullable [B, top_k].
+ * Before the first step the caller fills the state's context: the entries and keys of the
+ * floor(pos/m) complete blocks before pos, the window rows of positions pos-window+1 .. pos-1, and
+ * the block rows of the previous block and of the current block's tokens before pos; the calls then
+ * go pos, pos+1, ... Workspace: csa_workspace_size(
+ * CSA_OP_DECODE_STEP, dims, B, 1, n_cap, 0, dtype). Errors: CSA_ERR_ARG for bad sizes, pointers,
+ * pos outside [0, n_cap*m), an MXFP4 or mismatched dtype.
+ */
+int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t pos, int dtype,
+                    const void* q, const void* q_idx, const void* kv, const void* comp,
+                    const csa_decode_state* state, void* out, int out_dtype, int32_t* out_idx,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The whole layer for a chunk of T tokens per sequence at positions pos0 .. pos0+T-1:
