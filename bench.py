@@ -349,6 +349,66 @@ def bench_decode(name, steps, warmup, fid=False):
             "mall": "512 MiB read between steps, outside the timed events"}
 
 
+def bench_decode_state(steps, warmup):
+    """Token-by-token decode of the decode128k batch over a state cache (csa_decode_step) with the
+    pages' cache format (584-byte FP8 entry records) and QK-norm + RoPE on: four consecutive steps
+    L .. L+3, the last of which completes a block and compresses its entry and key. Reported per
+    step, averaged over the block."""
+    import torch
+    from compressed_sparse_attention_05_amd import layer, lib
+    from synth import gen as G
+    from synth.torch_io import act, to_device
+    from synth.workloads import get
+
+    wl = get("decode128k")
+    log("generating decode-state inputs")
+    inp = G.make_inputs(wl)
+    d = layer.dims(wl.m, wl.D, wl.H, wl.H_I, wl.D_I, wl.k, wl.W)
+    N = wl.L // wl.m
+    st = layer.CSADecodeState(d, wl.B, N + 1, records=True)
+    ent = act(inp["entries"], wl)
+    lib.csa_entry_pack(ent, st.entries[:, :N])
+    del ent
+    st.keys[:, :N] = act(inp["keys"], wl)
+    raw = act(inp["kv_raw"], wl)                      # positions L-127 .. L
+    for r in range(wl.W - 1):
+        st.win[:, (wl.L - wl.W + 1 + r) % wl.W] = raw[:, r]
+    bf = lambda name, shape: to_device(G.f32_to_bf16_bits(G.normal_f32(9, name, shape)), "bf16")
+    st.block.copy_(bf("ds_block", tuple(st.block.shape)))
+    nc = 4 * wl.D + 4 * wl.D_I
+    qs = [bf(f"ds_q{j}", (wl.B, wl.H, wl.D)) for j in range(4)]
+    qis = [bf(f"ds_qi{j}", (wl.B, wl.H_I, wl.D_I)) for j in range(4)]
+    kvs = [bf(f"ds_kv{j}", (wl.B, wl.D)) for j in range(4)]
+    comps = [bf(f"ds_c{j}", (wl.B, nc)) for j in range(4)]
+    # position biases N(0, 0.1) as in the prefill workloads (decode inputs carry none: no block completes there)
+    fb = lambda name, c: to_device(G.normal_f32(9, name, (wl.m, c), float(np.sqrt(0.1))), "f32")
+    w = {"bias_a": fb("ds_bias_a", wl.D), "bias_b": fb("ds_bias_b", wl.D), "ibias_a": fb("ds_ibias_a", wl.D_I),
+         "ibias_b": fb("ds_ibias_b", wl.D_I), "w_head": to_device(inp["w_head"], "f32")}
+    w.update(fid_device(wl.D))
+    del inp
+    # a block of four steps starting at the block boundary L (L % m == 0); the state is restored
+    # between repetitions only in what the steps change (entry row N, block rows), outside the timing
+    flush = torch.ones(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    block0 = st.block.clone()
+
+    def four():
+        for j in range(4):
+            st.step(w, wl.L + j, qs[j], qis[j], kvs[j], comps[j])
+
+    for _ in range(warmup):
+        st.block.copy_(block0)
+        four()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        st.block.copy_(block0)
+        flush.sum()
+        ms += timed_events(four, 1, torch.cuda.synchronize)
+    us = float(np.median(ms)) * 1e3 / 4
+    return {"us_per_step": round(us, 2), "B": wl.B, "context_tokens": wl.L, "entries": "584-byte FP8 records",
+            "qk_norm_rope": True, "what": "4 steps at L..L+3, one block completed (entry + key compressed)"}
+
+
 def bench_hca(steps, warmup):
     """The HCA steps ("Heavily Compressed Attention": 128-token blocks without overlap, dense attention
     over every visible entry plus the window) at 1M context: a 4096-token chunk after 1,044,480
@@ -500,6 +560,7 @@ def main():
         res["decode"] = {n: bench_decode(n, max(args.steps, 10), 3) for n in ("decode128k", "decode1m_fp4")}
         dfid = bench_decode("decode128k", max(args.steps, 10), 3, fid=True)
         res["fid"]["decode128k_us_per_step"] = dfid["us_per_step"]
+        res["decode_state"] = bench_decode_state(max(args.steps, 10), 2)
     if not args.no_hca:
         res["hca"] = bench_hca(min(args.steps, 5), 2)
     if not args.no_cpu_baseline:
