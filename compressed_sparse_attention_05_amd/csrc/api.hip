@@ -201,7 +201,7 @@ int validate_index(const csa_dims* d, int B, int T, int64_t q_pos0, int idx_dtyp
   return CSA_OK;
 }
 
-// Workspace of csa_decode_step: the contiguous window, the rotated query, one compressed entry
+// Workspace of csa_decode_step: the rotated query, one compressed entry
 // per sequence (records), the selected indices, and the index / attention scratch.
 struct DecodeWs {
   size_t win, q, ent, idx, scratch, total;
@@ -209,8 +209,8 @@ struct DecodeWs {
 DecodeWs decode_ws(const csa_dims* d, int B, int64_t n_cap, int dtype) {
   const size_t es = dtype == CSA_F32 ? 4 : 2;
   DecodeWs w{};
-  w.win = 0;
-  w.q = w.win + align256((size_t)B * d->window * d->D * es);
+  w.win = 0;  // the attention reads the window straight from the state's ring
+  w.q = w.win;
   w.ent = w.q + align256((size_t)B * d->H * d->D * es);
   w.idx = w.ent + align256((size_t)B * d->D * es);
   w.scratch = w.idx + align256((size_t)B * d->top_k * 4);
@@ -226,7 +226,7 @@ int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, 
               const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride,
               int64_t n_cap, const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
               int64_t raw_pos0, int64_t raw_len, const float* sink, void* out, int out_dtype, void* ws,
-              size_t ws_bytes, void* stream, int entry_fmt = 0) {
+              size_t ws_bytes, void* stream, int entry_fmt = 0, int64_t raw_ring = 0) {
   int rc = check_dims(dims, !dense);
   if (rc) return rc;
   if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
@@ -246,6 +246,8 @@ int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, 
   if (B > 1 && raw_seq_stride < raw_len * raw_ld) return fail(CSA_ERR_ARG, "raw_seq_stride too small");
   const int64_t need_lo = q_pos0 - dims->window + 1 > 0 ? q_pos0 - dims->window + 1 : 0;
   const int64_t need_hi = q_pos0 + T - 1;
+  if (raw_ring > 0 && (T != 1 || raw_ring < dims->window))
+    return fail(CSA_ERR_ARG, "a raw KV ring serves one query row and holds at least the window");
   if (raw_pos0 > need_lo || raw_pos0 + raw_len - 1 < need_hi)
     return fail(CSA_ERR_ARG, "kv_raw rows [%lld, %lld] do not cover the windows [%lld, %lld]", (long long)raw_pos0,
                 (long long)(raw_pos0 + raw_len - 1), (long long)need_lo, (long long)need_hi);
@@ -281,6 +283,7 @@ int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, 
   a.sink = sink;
   a.out = out;
   a.entry_fmt = entry_fmt;
+  a.raw_ring = raw_ring;
   rc = check_ws(ws, ws_bytes, attn_workspace(a));
   if (rc) return rc;
   return hip_status(launch_attn(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), name);
@@ -607,13 +610,14 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t p
   // the token's compressor inputs and raw KV join the state
   hipError_t e = launch_copy_rows(B, 1, (int)nc, es, comp, nc, nc, cur + (size_t)(pos % m) * nc * es, nc,
                                   2LL * m * nc, s);
+  if (e != hipSuccess) return hip_status(e, "csa_decode_step: block row");
   uint8_t* wrow = static_cast<uint8_t*>(st->win) + (size_t)(pos % W) * D * es;
-  if (e == hipSuccess) e = launch_copy_rows(B, 1, D, es, kv, D, D, wrow, D, (int64_t)W * D, s);
-  if (e != hipSuccess) return hip_status(e, "csa_decode_step: state rows");
-  if (fid) {
-    rc = csa_norm_rope(B, 1, 1, D, dtype, wrow, D, (int64_t)W * D, wrow, D, (int64_t)W * D, w->gamma_kv, w->norm_eps,
-                       w->rope_dims, w->rope_theta, pos, 1, 0, stream);
+  if (fid) {  // normalised and rotated on the way into the ring
+    rc = csa_norm_rope(B, 1, 1, D, dtype, kv, D, D, wrow, D, (int64_t)W * D, w->gamma_kv, w->norm_eps, w->rope_dims,
+                       w->rope_theta, pos, 1, 0, stream);
     if (rc) return rc;
+  } else if ((e = launch_copy_rows(B, 1, D, es, kv, D, D, wrow, D, (int64_t)W * D, s)) != hipSuccess) {
+    return hip_status(e, "csa_decode_step: window row");
   }
 
   // a completed block: its entry and indexer key (own block = series a, previous block = series b)
@@ -686,26 +690,12 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t p
   rc = csa_index_topk(dims, B, 1, pos, dtype, q_idx, (int64_t)HI * DI, (int64_t)HI * DI, nullptr, w->w_head, 0,
                       st->keys, n_cap * DI, nullptr, n_cap, idx, nullptr, scratch, scratch_bytes, stream);
   if (rc) return rc;
-  // the window [pos - raw_len + 1, pos] out of the ring, in position order
+  // the window [pos - raw_len + 1, pos], read by the attention straight from the ring
   const int64_t raw_len = pos + 1 < W ? pos + 1 : W;
   const int64_t raw_pos0 = pos - raw_len + 1;
-  const int r0 = (int)(raw_pos0 % W);
-  const int n1 = (int)(raw_len < W - r0 ? raw_len : W - r0);
-  uint8_t* wt = base + L.win;
-  const uint8_t* ring = static_cast<const uint8_t*>(st->win);
-  e = launch_copy_rows(B, n1, D, es, ring + (size_t)r0 * D * es, D, (int64_t)W * D, wt, D, (int64_t)W * D, s);
-  if (e == hipSuccess && raw_len > n1)
-    e = launch_copy_rows(B, (int)(raw_len - n1), D, es, ring, D, (int64_t)W * D, wt + (size_t)n1 * D * es, D,
-                         (int64_t)W * D, s);
-  if (e != hipSuccess) return hip_status(e, "csa_decode_step: window");
-  if (st->entry_fmt)
-    rc = csa_sparse_attn_fp8(dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries,
-                             n_cap * kEntryRecordBytes, n_cap, idx, wt, D, (int64_t)W * D, raw_pos0, raw_len, w->sink,
-                             out, out_dtype, scratch, scratch_bytes, stream);
-  else
-    rc = csa_sparse_attn(dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries, n_cap * D, n_cap,
-                         idx, wt, D, (int64_t)W * D, raw_pos0, raw_len, w->sink, out, out_dtype, scratch,
-                         scratch_bytes, stream);
+  rc = attn_call("csa_decode_step", false, dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries,
+                 n_cap * (st->entry_fmt ? (int64_t)kEntryRecordBytes : D), n_cap, idx, st->win, D, (int64_t)W * D,
+                 raw_pos0, raw_len, w->sink, out, out_dtype, scratch, scratch_bytes, stream, st->entry_fmt, W);
   if (rc) return rc;
   if (fid && w->rope_dims > 0) {
     rc = csa_norm_rope(B, 1, H, D, out_dtype, out, (int64_t)H * D, (int64_t)H * D, out, (int64_t)H * D,

@@ -30,6 +30,10 @@ __device__ __forceinline__ int64_t window_hi(const AttnArgs& a, int64_t p) {
   if (hi > a.raw_pos0 + a.raw_len - 1) hi = a.raw_pos0 + a.raw_len - 1;
   return hi;
 }
+// row of kv_raw holding raw position u: u - raw_pos0, or u mod raw_ring for a ring buffer
+__device__ __forceinline__ int64_t raw_row(const AttnArgs& a, int64_t u) {
+  return a.raw_ring > 0 ? u % a.raw_ring : u - a.raw_pos0;
+}
 // dense mode: the entries visible to position p, min(floor((p+1)/m), n_cap)
 __host__ __device__ __forceinline__ int64_t dense_visible(const AttnArgs& a, int64_t p) {
   const int64_t n = (p + 1) / a.m;
@@ -92,7 +96,7 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
         off = (int64_t)b * a.entries_seq_stride + (int64_t)e * (record ? kEntryBytes : a.D);
       } else {
         src = a.raw;
-        off = (int64_t)b * a.raw_seq_stride + (wlo + (j - nsel) - a.raw_pos0) * a.raw_ld;
+        off = (int64_t)b * a.raw_seq_stride + raw_row(a, wlo + (j - nsel)) * a.raw_ld;
       }
       float kv[kMaxPer];
       float part = 0.f;
@@ -208,7 +212,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
   // position and nothing is stored.
   const int64_t nvis_d = a.dense ? dense_visible(a, p) : 0;
   auto key_id = [&](int kj) -> int32_t {
-    return kj < nvis_d ? kj : -(int32_t)(wlo - a.raw_pos0 + (kj - nvis_d)) - 1;
+    return kj < nvis_d ? kj : -(int32_t)raw_row(a, wlo + (kj - nvis_d)) - 1;
   };
   if (!a.dense) {
     const int32_t* idx = a.idx + row * a.k;
@@ -240,7 +244,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
       }
     }
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
-    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
+    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)raw_row(a, wlo + j) - 1;
     if (threadIdx.x == 0) sm.keys[a.k + a.W] = nsel + nwin;
     __syncthreads();
   }
@@ -539,7 +543,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   // mode every visible entry in order, then the window, with ids from the position
   const int64_t nvis_d = a.dense ? dense_visible(a, p) : 0;
   auto key_id = [&](int kj) -> int32_t {
-    return kj < nvis_d ? kj : -(int32_t)(wlo - a.raw_pos0 + (kj - nvis_d)) - 1;
+    return kj < nvis_d ? kj : -(int32_t)raw_row(a, wlo + (kj - nvis_d)) - 1;
   };
   if (a.dense) load_q();
   else {
@@ -574,7 +578,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
       }
     }
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
-    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)(wlo - a.raw_pos0 + j) - 1;
+    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)raw_row(a, wlo + j) - 1;
     if (threadIdx.x == 0) sm.keys[a.k + a.W] = nsel + nwin;
     __syncthreads();
   }

@@ -128,6 +128,7 @@ struct AttnArgs {
   void* out;
   int dense = 0;  // attend to every visible entry in order (HCA); idx is not read and k is unused
   int m = 1;      // tokens per entry (dense only: entry i is visible to p iff (i+1)*m - 1 <= p)
+  int64_t raw_ring = 0;  // > 0: kv_raw is a ring of raw_ring rows, position u in row u % raw_ring
   int entry_fmt = 0;  // 0: entries are in_dtype rows of D; 1: 584-byte FP8 records (D = 512), whose
                       // entries_seq_stride counts bytes
 };
