@@ -27,7 +27,8 @@ def _fid(D, seed, rope_dims):
 
 @pytest.mark.parametrize("dtype,D,rope_dims,pos0,step", [("bf16", 512, 64, 1_048_000, 1), ("f32", 512, 64, 131_000, 4),
                                                          ("f32", 32, 16, 5, 1), ("bf16", 192, 0, 0, 1),
-                                                         ("f32", 96, 96, 777_777, 3)])
+                                                         ("f32", 96, 96, 777_777, 3), ("f32", 256, 64, 999_999, 1),
+                                                         ("bf16", 1024, 192, 65_537, 2)])
 def test_norm_rope_matches_oracle(dtype, D, rope_dims, pos0, step):
     B, R, H = 2, 7, 3
     x64 = G.normal_f32(90, "nr_x", (B, R, H, D)).astype(np.float64) * 3.0
