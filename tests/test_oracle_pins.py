@@ -659,3 +659,16 @@ def test_entry_record_error_bound_and_scale_choice():
     half_ulp = np.where(np.abs(x) >= 2.0 ** -6, 2.0 ** (binade - 4), 2.0 ** -10)
     assert np.all(err <= half_ulp * (1 + 1e-12))
     assert np.all(r[:, 583] == 0)
+
+
+def test_entry_rotation_position_is_the_last_token_of_its_block():
+    # reading: entry i turns at the position of its block's last token, (i+1)m - 1, so a query on
+    # that token meets the entry at relative distance 0 (m = 4: entries 0, 1, 2 at 3, 7, 11)
+    assert list(O.entry_positions(0, 3, 4)) == [3, 7, 11]
+    assert list(O.entry_positions(5, 2, 128)) == [767, 895]
+    rng = np.random.default_rng(88)
+    v = rng.standard_normal(64)
+    q = O.rope(v, 7.0, 16, 10000.0)
+    e = O.rope(v, O.entry_positions(1, 1, 4)[0], 16, 10000.0)
+    assert abs(q @ e - v @ v) < 1e-9                       # rotations cancel at distance 0
+    assert abs(q @ O.rope(v, 4.0, 16, 10000.0) - v @ v) > 1e-3
