@@ -349,25 +349,60 @@ __device__ __forceinline__ void row_ranks(uint32_t mask, RowSmem& sm, uint32_t* 
   __syncthreads();
 }
 
+// A workgroup selects within one piece of a row: piece c of row r is scores r*ld + c*chunk .. (at most
+// chunk of them), and its k results go to slots (r*nchunk + c)*k of the outputs. remap (optional)
+// turns a position p of the row into the index remap[r*ld + p]; row_nv (optional) is the row's own
+// count of valid entries when the scores are candidates of another selection: with at most k of
+// them, every entry 0 .. row_nv-1 is selected.
+struct RowSel {
+  const float* scores;
+  int64_t ld, chunk;
+  int nchunk;
+  const int32_t* n_valid;  // nullable: every score of the row is valid
+  int k;
+  int32_t* out_idx;
+  float* out_score;        // nullable
+  const int32_t* remap;    // nullable
+  const int32_t* row_nv;   // nullable
+};
+
 template <int P, bool VEC>
-__global__ void __launch_bounds__(kRowThreads) sel_row(const float* scores, int64_t ld, const int32_t* n_valid,
-                                                       int k, int32_t* out_idx, float* out_score) {
+__global__ void __launch_bounds__(kRowThreads) sel_row(RowSel a) {
   static_assert(P % 4 == 0 && 4 * P <= kRowChunks && P <= 32, "row layout");
   constexpr int NQ = P / 4;
   __shared__ RowSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
-  const int64_t row = blockIdx.x;
-  const int64_t nv = row_valid(n_valid, row, ld);
-  const float* s = scores + row * ld;
-  int32_t* oi = out_idx + row * k;
-  float* os = out_score ? out_score + row * k : nullptr;
+  const int k = a.k;
+  const int64_t row = blockIdx.x / a.nchunk;
+  const int64_t base = (int64_t)(blockIdx.x % a.nchunk) * a.chunk;
+  const int64_t nv_row = a.n_valid ? row_valid(a.n_valid, row, a.ld) : a.ld;
+  const int64_t piece = a.ld - base < a.chunk ? a.ld - base : a.chunk;
+  const int64_t nv = nv_row - base <= 0 ? 0 : (nv_row - base < piece ? nv_row - base : piece);
+  const float* s = a.scores + row * a.ld + base;
+  int32_t* oi = a.out_idx + (int64_t)blockIdx.x * k;
+  float* os = a.out_score ? a.out_score + (int64_t)blockIdx.x * k : nullptr;
+  auto index_of = [&](int64_t p) -> int32_t { return a.remap ? a.remap[row * a.ld + p] : (int32_t)p; };
+  if (a.row_nv) {
+    // candidates of a row with at most k valid entries: all of them, in order. They all lie in the
+    // first piece (valid entries are a prefix of the row), whose candidates lead the list with
+    // positions equal to their indices.
+    const int64_t t = a.row_nv[row] < 0 ? 0 : a.row_nv[row];
+    if (t <= k) {
+      for (int j = tid; j < k; j += kRowThreads) {
+        oi[j] = j < t ? j : -1;
+        if (os) os[j] = j < t ? a.scores[row * a.ld + j] : -INFINITY;
+      }
+      return;
+    }
+  }
   if (nv <= k) {  // every valid entry is selected
     for (int j = tid; j < k; j += kRowThreads) {
-      oi[j] = j < nv ? j : -1;
+      oi[j] = j < nv ? index_of(base + j) : -1;
       if (os) os[j] = j < nv ? key_to_score(score_to_key(s[j])) : -INFINITY;
     }
     return;
   }
+  const int64_t ld = piece;  // bound of this piece's loads
   uint32_t key[P];
   uint32_t valid = 0;  // bit j: key[j] is a score of the row (index < nv)
   uint32_t tmin = 0xFFFFFFFFu, tmax = 0u;
@@ -498,22 +533,26 @@ __global__ void __launch_bounds__(kRowThreads) sel_row(const float* scores, int6
   for (int j = 0; j < P; ++j) {
     const uint32_t pos = pb[j / 4] + (uint32_t)__popc(sel & (((1u << (j % 4)) - 1u) << (j & ~3)));
     if (((sel >> j) & 1u) && pos < (uint32_t)k) {  // exactly k are selected; the test only bounds the writes
-      oi[pos] = (int32_t)(4 * ((int64_t)(j / 4) * kRowThreads + tid) + (j % 4));
+      oi[pos] = index_of(base + 4 * ((int64_t)(j / 4) * kRowThreads + tid) + (j % 4));
       if (os) os[pos] = key_to_score(key[j]);
     }
   }
 }
 
 template <int P>
-void launch_row(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
-                float* out_score, hipStream_t s) {
-  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
-  if (vec)
-    hipLaunchKernelGGL((sel_row<P, true>), dim3((unsigned)R), dim3(kRowThreads), 0, s, scores, ld, n_valid, k,
-                       out_idx, out_score);
-  else
-    hipLaunchKernelGGL((sel_row<P, false>), dim3((unsigned)R), dim3(kRowThreads), 0, s, scores, ld, n_valid, k,
-                       out_idx, out_score);
+void launch_row_p(const RowSel& a, int R, hipStream_t s) {
+  const bool vec = (a.ld % 4 == 0) && (a.chunk % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
+  const dim3 grid((unsigned)(R * a.nchunk));
+  if (vec) hipLaunchKernelGGL((sel_row<P, true>), grid, dim3(kRowThreads), 0, s, a);
+  else hipLaunchKernelGGL((sel_row<P, false>), grid, dim3(kRowThreads), 0, s, a);
+}
+// pieces of at most kRowMax scores
+void launch_row(const RowSel& a, int R, hipStream_t s) {
+  const int64_t n = a.chunk;
+  if (n <= 4 * kRowThreads) launch_row_p<4>(a, R, s);
+  else if (n <= 8 * kRowThreads) launch_row_p<8>(a, R, s);
+  else if (n <= 16 * kRowThreads) launch_row_p<16>(a, R, s);
+  else launch_row_p<32>(a, R, s);
 }
 
 SelWork carve(void* ws, int R, int64_t ld, int k) {
@@ -550,11 +589,48 @@ hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s)
 
 hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
                          float* out_score, void* ws, bool zeroed, hipStream_t s) {
+  RowSel rs{};
+  rs.k = k;
   if (ld <= kRowMax) {
-    if (ld <= 4 * kRowThreads) launch_row<4>(scores, ld, n_valid, R, k, out_idx, out_score, s);
-    else if (ld <= 8 * kRowThreads) launch_row<8>(scores, ld, n_valid, R, k, out_idx, out_score, s);
-    else if (ld <= 16 * kRowThreads) launch_row<16>(scores, ld, n_valid, R, k, out_idx, out_score, s);
-    else launch_row<32>(scores, ld, n_valid, R, k, out_idx, out_score, s);
+    rs.scores = scores;
+    rs.ld = ld;
+    rs.chunk = ld;
+    rs.nchunk = 1;
+    rs.n_valid = n_valid;
+    rs.out_idx = out_idx;
+    rs.out_score = out_score;
+    launch_row(rs, R, s);
+    return hipGetLastError();
+  }
+  // Longer rows, while the candidates fit one workgroup: the k best of every kRowMax-score piece
+  // (the row's k best are among them; each piece's list is in index order, so the concatenation
+  // is too), then the k best of those candidates with positions mapped back to indices. Both
+  // passes use the same key order, so the result is the direct selection's.
+  const int64_t nchunk = ceil_div(ld, kRowMax);
+  if (nchunk * k <= kRowMax && (size_t)R * nchunk * k * 8 + 256 <= select_workspace(R, ld, k)) {
+    int32_t* cand_idx = static_cast<int32_t*>(ws);
+    float* cand_score = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + a256((size_t)R * nchunk * k * 4));
+    rs.scores = scores;
+    rs.ld = ld;
+    rs.chunk = kRowMax;
+    rs.nchunk = (int)nchunk;
+    rs.n_valid = n_valid;
+    rs.out_idx = cand_idx;
+    rs.out_score = cand_score;
+    launch_row(rs, R, s);
+    hipError_t e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    RowSel r2{};
+    r2.scores = cand_score;
+    r2.ld = nchunk * k;
+    r2.chunk = nchunk * k;
+    r2.nchunk = 1;
+    r2.k = k;
+    r2.out_idx = out_idx;
+    r2.out_score = out_score;
+    r2.remap = cand_idx;
+    r2.row_nv = n_valid;
+    launch_row(r2, R, s);
     return hipGetLastError();
   }
   SelWork w = carve(ws, R, ld, k);
