@@ -346,6 +346,8 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
         const size_t at = attn_workspace(sizing_attn(dims, B, T, idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16));
         size_t scratch = need > at ? need : at;  // index / attention scratch, or the projection's
         if (idx_dtype == CSA_BF16 && scratch < kGemmWorkspace) scratch = kGemmWorkspace;
+        const size_t ent_tmp = (size_t)B * (T / dims->m) * dims->D * es;  // new entries before packing
+        if (scratch < ent_tmp) scratch = ent_tmp;
         need = align256((size_t)B * T * n_tot_of(dims) * es) + align256((size_t)B * T * dims->top_k * 4) +
                align256(scratch);
       }
@@ -728,6 +730,9 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
   if (fid && (w->rope_dims < 0 || w->rope_dims > D || w->rope_dims % 2 || (w->rope_dims > 0 && !(w->rope_theta > 0.f)) ||
               !(w->norm_eps >= 0.f)))
     return fail(CSA_ERR_ARG, "QK-norm / RoPE parameters: rope_dims even in [0, D], rope_theta > 0, norm_eps >= 0");
+  const bool records = cache->entry_fmt != 0;
+  if (cache->entry_fmt != 0 && cache->entry_fmt != 1) return fail(CSA_ERR_ARG, "entry_fmt must be 0 or 1");
+  if (records && D != 512) return fail(CSA_ERR_ARG, "entry records hold D = 512");
   const int64_t ntot = n_tot_of(dims);
   const int es = esize(dtype);
   // workspace: P [B*T, ntot] | idx [B*T, k] | index scratch
@@ -739,6 +744,8 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
   const size_t a_ws = attn_workspace(sizing_attn(dims, B, T, dtype));
   size_t scratch = i_ws > a_ws ? i_ws : a_ws;  // index / attention scratch, or the projection's
   if (dtype == CSA_BF16 && scratch < kGemmWorkspace) scratch = kGemmWorkspace;
+  const size_t ent_tmp = (size_t)B * (T / m) * D * es;  // new entries before packing into records
+  if (scratch < ent_tmp) scratch = ent_tmp;
   const size_t x_bytes = align256(scratch);
   rc = check_ws(ws, ws_bytes, p_bytes + i_bytes + x_bytes);
   if (rc) return rc;
@@ -771,10 +778,42 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
   if (e == hipSuccess && !done) e = launch_gemm(g, s);
   if (e != hipSuccess) return hip_status(e, "csa_forward: projection");
 
-  rc = csa_compress(B, T, pos0, m, D, dtype, col(c_ca), col(c_za), col(c_cb), col(c_zb), ntot, (int64_t)T * ntot,
-                    halo ? halo : nullptr, halo ? halo + (size_t)D * es : nullptr, halo_ld, (int64_t)m * halo_ld,
-                    w->bias_a, w->bias_b, cache->entries, cache->n_cap * D, cache->n_cap, dtype, stream);
-  if (rc) return rc;
+  // new entries: into their cache rows, or (records) into the scratch, to be packed below
+  void* ent_dst = records ? xws : cache->entries;
+  const int64_t ent_seq = records ? (int64_t)(T / m) * D : cache->n_cap * D;
+  if (records) {
+    CompressArgs ca{};
+    ca.B = B;
+    ca.n_new = T / m;
+    ca.m = m;
+    ca.c = D;
+    ca.first_entry = pos0 / m;
+    ca.in_dtype = dtype;
+    ca.out_dtype = dtype;
+    ca.ca = col(c_ca);
+    ca.za = col(c_za);
+    ca.cb = col(c_cb);
+    ca.zb = col(c_zb);
+    ca.ld = ntot;
+    ca.seq_stride = (int64_t)T * ntot;
+    ca.halo_cb = halo ? halo : ca.ca;
+    ca.halo_zb = halo ? halo + (size_t)D * es : ca.za;
+    ca.halo_ld = halo ? halo_ld : ntot;
+    ca.halo_seq_stride = halo ? (int64_t)m * halo_ld : (int64_t)T * ntot;
+    ca.bias_a = w->bias_a;
+    ca.bias_b = w->bias_b;
+    ca.entries = xws;
+    ca.entries_seq_stride = ent_seq;
+    ca.out_first = 0;
+    ca.aligned16 = aligned(ca.ca, 16) && aligned(ca.za, 16) && aligned(ca.cb, 16) && aligned(ca.zb, 16) &&
+                   aligned(ca.halo_cb, 16) && aligned(ca.halo_zb, 16) && (ntot * es) % 16 == 0;
+    if (ca.n_new > 0 && (e = launch_compress(ca, s)) != hipSuccess) return hip_status(e, "csa_forward: compress");
+  } else {
+    rc = csa_compress(B, T, pos0, m, D, dtype, col(c_ca), col(c_za), col(c_cb), col(c_zb), ntot, (int64_t)T * ntot,
+                      halo ? halo : nullptr, halo ? halo + (size_t)D * es : nullptr, halo_ld, (int64_t)m * halo_ld,
+                      w->bias_a, w->bias_b, cache->entries, cache->n_cap * D, cache->n_cap, dtype, stream);
+    if (rc) return rc;
+  }
   rc = csa_compress(B, T, pos0, m, DI, dtype, col(c_ica), col(c_iza), col(c_icb), col(c_izb), ntot, (int64_t)T * ntot,
                     halo ? halo + (size_t)2 * D * es : nullptr, halo ? halo + (size_t)(2 * D + DI) * es : nullptr,
                     halo_ld, (int64_t)m * halo_ld, w->ibias_a, w->ibias_b, cache->keys, cache->n_cap * DI,
@@ -793,17 +832,24 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_
     rc = csa_norm_rope(B, T, 1, D, dtype, wrows, D, cache->win_cap * D, wrows, D, cache->win_cap * D, w->gamma_kv,
                        w->norm_eps, w->rope_dims, w->rope_theta, pos0, 1, 0, stream);
     if (rc) return rc;
-    void* erows = static_cast<uint8_t*>(cache->entries) + (size_t)(pos0 / m) * D * es;
-    rc = csa_norm_rope(B, T / m, 1, D, dtype, erows, D, cache->n_cap * D, erows, D, cache->n_cap * D, w->gamma_kv,
-                       w->norm_eps, w->rope_dims, w->rope_theta, pos0 + m - 1, m, 0, stream);
+    void* erows = records ? ent_dst : static_cast<uint8_t*>(cache->entries) + (size_t)(pos0 / m) * D * es;
+    rc = csa_norm_rope(B, T / m, 1, D, dtype, erows, D, ent_seq, erows, D, ent_seq, w->gamma_kv, w->norm_eps,
+                       w->rope_dims, w->rope_theta, pos0 + m - 1, m, 0, stream);
+    if (rc) return rc;
+  }
+  if (records) {
+    rc = csa_entry_pack(B, T / m, dtype, ent_dst, D, ent_seq,
+                        static_cast<uint8_t*>(cache->entries) + (size_t)(pos0 / m) * kEntryRecordBytes,
+                        cache->n_cap * kEntryRecordBytes, stream);
     if (rc) return rc;
   }
   rc = csa_index_topk(dims, B, T, pos0, dtype, col(c_qi), ntot, (int64_t)T * ntot, nullptr, w->w_head, 0, cache->keys,
                       cache->n_cap * DI, nullptr, cache->n_cap, idx, nullptr, xws, x_bytes, stream);
   if (rc) return rc;
-  rc = csa_sparse_attn(dims, B, T, pos0, dtype, col(c_q), ntot, (int64_t)T * ntot, cache->entries, cache->n_cap * D,
-                       cache->n_cap, idx, cache->win, D, cache->win_cap * D, pos0 - (W - 1), (int64_t)W - 1 + T,
-                       w->sink, out, out_dtype, xws, x_bytes, stream);
+  rc = attn_call("csa_forward", false, dims, B, T, pos0, dtype, col(c_q), ntot, (int64_t)T * ntot, cache->entries,
+                 cache->n_cap * (records ? (int64_t)kEntryRecordBytes : D), cache->n_cap, idx, cache->win, D,
+                 cache->win_cap * D, pos0 - (W - 1), (int64_t)W - 1 + T, w->sink, out, out_dtype, xws, x_bytes, stream,
+                 records ? 1 : 0);
   if (rc) return rc;
   if (fid && w->rope_dims > 0) {
     rc = csa_norm_rope(B, T, H, D, out_dtype, out, (int64_t)H * D, (int64_t)T * H * D, out, (int64_t)H * D,

@@ -20,9 +20,12 @@ class CSAPrefill:
     """
 
     def __init__(self, d: lib.Dims, B: int, T: int, d_model: int, n_cap: int, dtype=torch.bfloat16,
-                 out_dtype=torch.float32, device="cuda"):
+                 out_dtype=torch.float32, device="cuda", records: bool = False):
         self.d, self.B, self.T = d, B, T
-        self.entries = torch.zeros(B, n_cap, d.D, dtype=dtype, device=device)
+        if records:  # the entry cache as 584-byte FP8 records
+            self.entries = torch.zeros(B, n_cap, lib.ENTRY_RECORD_BYTES, dtype=torch.uint8, device=device)
+        else:
+            self.entries = torch.zeros(B, n_cap, d.D, dtype=dtype, device=device)
         self.keys = torch.zeros(B, n_cap, d.D_I, dtype=dtype, device=device)
         self.win = torch.zeros(B, d.window - 1 + T, d.D, dtype=dtype, device=device)
         self.halo = torch.zeros(B, d.m, 2 * d.D + 2 * d.D_I, dtype=dtype, device=device)

@@ -45,7 +45,7 @@ class Weights(ctypes.Structure):
 class Cache(ctypes.Structure):
     _fields_ = [("entries", ctypes.c_void_p), ("keys", ctypes.c_void_p), ("n_cap", ctypes.c_int64),
                 ("win", ctypes.c_void_p), ("win_cap", ctypes.c_int64), ("halo", ctypes.c_void_p),
-                ("halo_out", ctypes.c_void_p)]
+                ("halo_out", ctypes.c_void_p), ("entry_fmt", ctypes.c_int32)]
 
 
 class DecodeState(ctypes.Structure):
@@ -364,7 +364,8 @@ class Forward:
     def __call__(self, weights: dict, x, cache: dict, out, *, pos0: int, out_idx=None):
         w = weights_struct(weights)
         c = Cache(_p(cache["entries"]), _p(cache["keys"]), cache["entries"].shape[1], _p(cache["win"]),
-                  cache["win"].shape[1], _p(cache.get("halo")), _p(cache.get("halo_out")))
+                  cache["win"].shape[1], _p(cache.get("halo")), _p(cache.get("halo_out")),
+                  1 if cache["entries"].dtype == torch.uint8 else 0)
         _check(load().csa_forward(ctypes.byref(self.dims), ctypes.byref(w), self.B, self.T, pos0, self.d_model,
                                   self.dtype, _p(x), ctypes.byref(c), _p(out), _dt(out), _p(out_idx), self._wp,
                                   self._wn, _stream()))

@@ -298,6 +298,9 @@ typedef struct csa_cache {
                             pos0 == 0                                                            */
   void* halo_out;        /* nullable [B, m, 2D + 2D_I]: receives this chunk's last block (needs
                             T % m == 0), i.e. the next chunk's halo                               */
+  int32_t entry_fmt;     /* 0: entries are rows of the activation dtype; 1: 584-byte FP8 records
+                            [B, n_cap, 584] (see csa_entry_pack; D = 512): new entries are packed
+                            and the attention reads the records                                   */
 } csa_cache;
 
 /* Decode state of B sequences (device pointers, activation dtype unless stated). */

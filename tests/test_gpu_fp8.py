@@ -138,3 +138,46 @@ def test_full_decode128k_over_records_sampled():
         check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
         ref = O.sparse_attention(r["q"], r["entries"], gidx, r["raw"], wl.L - (wl.W - 1), np.array([wl.L]), wl.W)
         assert max_err(tensor_f64(st.out[b]), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fid", [False, True])
+def test_forward_chunk_with_record_cache(fid):
+    # a chunk after context with the entry cache in records: the new entries are packed (normalised
+    # and rotated first when the options are on) and the attention reads records throughout
+    wl = get("chunk1m").with_(L=2048, T=264, d=512)
+    inp = G.make_inputs(wl)
+    host = dev = None
+    if fid:
+        gq = (1.0 + 0.2 * G.normal_f32(130, "gamma_q", (wl.D,))).astype(np.float32)
+        gk = (1.0 + 0.2 * G.normal_f32(130, "gamma_kv", (wl.D,))).astype(np.float32)
+        host = {"gamma_q": gq.astype(np.float64), "gamma_kv": gk.astype(np.float64), "eps": float(np.float32(1e-6)),
+                "rope_dims": 64, "theta": 10000.0}
+        dev = {"gamma_q": to_device(gq, "f32"), "gamma_kv": to_device(gk, "f32"), "norm_eps": 1e-6, "rope_dims": 64,
+               "rope_theta": 10000.0}
+    r = O.prefill(inp, wl, fid=host)
+    from tests.csa_testlib import weights_to_device
+    from synth.torch_io import act
+    w = weights_to_device(wl, inp)
+    if fid:
+        w.update(dev)
+    st = layer.CSAPrefill(dims_of(wl), 1, wl.T, wl.d, wl.n_cap, records=True)
+    n0 = wl.L // wl.m
+    lib.csa_entry_pack(act(inp["entries_prefix"], wl), st.entries[:, :n0])
+    st.keys[:, :n0] = act(inp["keys_prefix"], wl)
+    st.win[:, : wl.W - 1] = act(inp["win_prefix"], wl)
+    st.halo.copy_(act(inp["halo"], wl))
+    st(w, act(inp["x"], wl), wl.L)
+    torch.cuda.synchronize()
+    n_new = wl.T // wl.m
+    got_rec = st.entries[0, n0:n0 + n_new].cpu().numpy()
+    want_rec = O.entry_pack(r["entries_new"])
+    # the records of the new entries: equal where the bf16 entries agree, within one E4M3 step elsewhere
+    assert np.mean(got_rec == want_rec) >= 0.99
+    np.testing.assert_allclose(O.entry_unpack(got_rec), O.entry_unpack(want_rec), rtol=2 ** -3, atol=1e-2)
+    stored = O.entry_unpack(O.entry_pack(r["entries"]))
+    gidx = st.idx[0].cpu().numpy()
+    differ = check_idx_rows(gidx, r["idx"], r["scores"], r["n_vis"])
+    assert len(differ) <= wl.T // 20
+    o = O.sparse_attention(r["q"], stored, gidx, r["raw"], r["raw_pos0"], r["q_pos"], wl.W)
+    ref = O.rope(o, r["q_pos"], 64, 10000.0, inverse=True) if fid else o
+    assert max_err(tensor_f64(st.out[0]), ref) <= TOL["bf16"]
