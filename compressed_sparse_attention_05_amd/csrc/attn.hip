@@ -640,14 +640,16 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
     return n;
   };
   auto stage_records = [&](int tile) {
-    int32_t id;
-    const uint64_t ra = row_addr(tile, id);
+    int kl = kbeg + tile * kNK + (lane & 31);
+    kl = kl < kend ? kl : kend - 1;
+    const int32_t id = a.dense ? key_id(kl) : sm.keys[kl];
     stage_mask = 0;
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) {
       const int r = j * NW + wave_u;
-      if (__builtin_amdgcn_readlane(id, r) < 0) continue;
-      const uint8_t* rec = reinterpret_cast<const uint8_t*>(readlane64(ra, r));
+      const int32_t idr = __builtin_amdgcn_readlane(id, r);
+      if (idr < 0) continue;
+      const uint8_t* rec = ent + (int64_t)idr * kEntryBytes;  // scalar address
       const uint32_t dst = lds_offset(stage + j * kStageRow);
       if (lane < 36) copy_to_lds16(rec + 16 * lane, __builtin_amdgcn_readfirstlane(dst));
       if (lane < 2) copy_to_lds4(rec + 576 + 4 * lane, __builtin_amdgcn_readfirstlane(dst + 576));
@@ -664,11 +666,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
       if (!((stage_mask >> j) & 1u)) continue;  // wave-uniform
       const int r = j * NW + wave_u;
       const uint8_t* srow = stage + j * kStageRow;
-      const uint2 sc = *reinterpret_cast<const uint2*>(srow + 576);
       uint8_t* dst = reinterpret_cast<uint8_t*>(&sm.kn[buf][r][0]);
       if (lane < 28) {
-        const int g = lane >> 2;
-        const uint32_t E = (g < 4 ? sc.x >> (8 * g) : sc.y >> (8 * (g - 4))) & 0xFFu;
+        const uint32_t E = srow[576 + (lane >> 2)];  // the scale exponent of this lane's 64-dim group
         const float scale = __uint_as_float(E << 23);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {  // 8 codes -> 8 bf16 at a time (fewer live registers)
