@@ -129,3 +129,57 @@ def test_forward_rejects_capacity_overflow():
     rc, msg = _err(L.csa_forward(ctypes.byref(d), ctypes.byref(w), 1, 8192, 0, 4096, lib.CSA_BF16, p, ctypes.byref(c),
                                  p, lib.CSA_F32, None, None, 0, None))
     assert rc == -1 and "n_cap" in msg
+
+
+def test_norm_rope_entry_pack_and_fp8_attention_reject_bad_arguments():
+    L = lib.load()
+    p = ctypes.c_void_p(4096)
+    # odd rope_dims, rope_dims beyond D, a norm on the inverse rotation, D beyond the kernel's limit
+    for args in ((1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, None, 0.0, 3, 10000.0, 0, 1, 0, None),
+                 (1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, None, 0.0, 10, 10000.0, 0, 1, 0, None),
+                 (1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, p, 0.0, 4, 10000.0, 0, 1, 1, None),
+                 (1, 2, 1, 8192, lib.CSA_F32, p, 8192, 16384, p, 8192, 16384, None, 0.0, 0, 10000.0, 0, 1, 0, None),
+                 (1, 2, 3, 8, lib.CSA_F32, p, 8, 48, p, 24, 48, None, 0.0, 4, 10000.0, 0, 1, 0, None)):
+        rc, _ = _err(L.csa_norm_rope(*args))
+        assert rc == -1, args
+    assert L.csa_norm_rope(0, 2, 3, 8, lib.CSA_F32, None, 24, 48, None, 24, 48, None, 0.0, 4, 10000.0, 0, 1, 0,
+                           None) == 0
+    # records: misaligned, short sequence stride, bad dtype
+    rc, msg = _err(L.csa_entry_pack(2, 4, lib.CSA_BF16, p, 512, 2048, ctypes.c_void_p(4100), 4 * 584, None))
+    assert rc == -1 and "align" in msg
+    rc, msg = _err(L.csa_entry_pack(2, 4, lib.CSA_BF16, p, 512, 2048, p, 100, None))
+    assert rc == -1 and "stride" in msg
+    rc, _ = _err(L.csa_entry_pack(2, 4, lib.CSA_MXFP4, p, 512, 2048, p, 4 * 584, None))
+    assert rc == -1
+    # attention over records needs D = 512 and a byte stride of whole records
+    d = _d(D=256)
+    rc, msg = _err(L.csa_sparse_attn_fp8(ctypes.byref(d), 1, 1, 1000, lib.CSA_BF16, p, 64 * 256, 0, p, 0, 256, p,
+                                         p, 256, 0, 873, 128, None, p, lib.CSA_F32, None, 0, None))
+    assert rc == -1 and "512" in msg
+
+
+def test_decode_step_rejects_bad_arguments():
+    L = lib.load()
+    p = ctypes.c_void_p(4096)
+    d = _d(H=128, top_k=1024)
+    w = lib.Weights(None, 4096, 4096, 4096, 4096, 4096, None, None, None, 0.0, 0, 10000.0)
+    st = lib.DecodeState(4096, 0, 4096, 100, 4096, 4096)
+    # position beyond the entry capacity (100 entries of 4 tokens)
+    rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, 404, lib.CSA_BF16, p, p, p, p,
+                                     ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "capacity" in msg
+    # MXFP4 is not an activation dtype
+    rc, _ = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, 10, lib.CSA_MXFP4, p, p, p, p,
+                                   ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1
+    # records need D = 512
+    st2 = lib.DecodeState(4096, 1, 4096, 100, 4096, 4096)
+    d2 = _d(D=256, H=128, top_k=1024)
+    rc, msg = _err(L.csa_decode_step(ctypes.byref(d2), ctypes.byref(w), 2, 10, lib.CSA_BF16, p, p, p, p,
+                                     ctypes.byref(st2), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "512" in msg
+    # no workspace
+    rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, 10, lib.CSA_BF16, p, p, p, p,
+                                     ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -3 and "workspace" in msg
+    assert lib.csa_workspace_size(lib.CSA_OP_DECODE_STEP, d, 2, 1, 100, 0, lib.CSA_BF16) > 0
