@@ -503,6 +503,15 @@ int csa_sparse_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int 
                    out_dtype, ws, ws_bytes, stream, 1);
 }
 
+int csa_dense_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype, const void* q, int64_t q_ld,
+                       int64_t q_seq_stride, const void* records, int64_t records_seq_stride, int64_t n_cap,
+                       const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0, int64_t raw_len,
+                       const float* sink, void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  return attn_call("csa_dense_attn_fp8", true, dims, B, T, q_pos0, in_dtype, q, q_ld, q_seq_stride, records,
+                   records_seq_stride, n_cap, nullptr, kv_raw, raw_ld, raw_seq_stride, raw_pos0, raw_len, sink, out,
+                   out_dtype, ws, ws_bytes, stream, 1);
+}
+
 int csa_entry_pack(int B, int N, int in_dtype, const void* entries, int64_t ld, int64_t seq_stride, void* records,
                    int64_t records_seq_stride, void* stream) {
   if (B < 0 || N < 0) return fail(CSA_ERR_ARG, "B and N must be >= 0");

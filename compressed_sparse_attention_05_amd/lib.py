@@ -20,7 +20,7 @@ CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN,
     CSA_OP_DECODE_STEP = range(7)
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
-           "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step")
+           "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8")
 
 
 class CsaError(RuntimeError):
@@ -86,9 +86,10 @@ def load() -> ctypes.CDLL:
     lib.csa_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i64, i32, vp, vp, vp, vp,
                                     ctypes.POINTER(DecodeState), vp, i32, vp, vp, sz, vp]
     lib.csa_sparse_attn_fp8.argtypes = lib.csa_sparse_attn.argtypes
+    lib.csa_dense_attn_fp8.argtypes = lib.csa_dense_attn.argtypes
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
-              "csa_sparse_attn_fp8", "csa_decode_step"):
+              "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -298,7 +299,9 @@ def csa_dense_attn(dims: Dims, q, entries, kv_raw, out, *, q_pos0: int, raw_pos0
     kv_raw [B, R, D] whose row r is position raw_pos0 + r; out [B, T, H, D] (float32 or bfloat16)."""
     _require_cuda(q, entries, kv_raw, out, sink)
     B, T = q.shape[0], q.shape[1]
-    if q.stride(3) != 1 or q.stride(2) != dims.D or entries.stride(2) != 1 or entries.stride(1) != dims.D:
+    records = entries.dtype == torch.uint8          # [B, n_cap, 584] FP8 entry records
+    row = ENTRY_RECORD_BYTES if records else dims.D
+    if q.stride(3) != 1 or q.stride(2) != dims.D or entries.stride(2) != 1 or entries.stride(1) != row:
         raise ValueError("q heads and entry rows must be contiguous")
     if kv_raw.stride(2) != 1 or not out.is_contiguous():
         raise ValueError("kv_raw rows and out must be contiguous")
@@ -306,10 +309,10 @@ def csa_dense_attn(dims: Dims, q, entries, kv_raw, out, *, q_pos0: int, raw_pos0
     if ws is None or ws.numel() < need + 256:
         ws = _workspace(need, q.device)
     wp, wn = _aligned_ptr(ws)
-    _check(load().csa_dense_attn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
-                                 _p(entries), entries.stride(0), entries.shape[1], _p(kv_raw), kv_raw.stride(1),
-                                 kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out), _dt(out), wp, wn,
-                                 _stream()))
+    fn = load().csa_dense_attn_fp8 if records else load().csa_dense_attn
+    _check(fn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
+              _p(entries), entries.stride(0), entries.shape[1], _p(kv_raw), kv_raw.stride(1),
+              kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out), _dt(out), wp, wn, _stream()))
     return out
 
 

@@ -260,6 +260,19 @@ int csa_sparse_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int 
                         int64_t raw_len, const float* sink, void* out, int out_dtype,
                         void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * csa_dense_attn over a cache of 584-byte records (the HCA layers keep the same entry format as the
+ * CSA layers in "Anatomy of a Frontier Model", section "The KV cache, recomputed"): as
+ * csa_dense_attn with `records` [B, n_cap, 584] bytes in place of the entries (16-byte aligned,
+ * sequence stride in bytes, a multiple of 8); D must be 512. Workspace: CSA_OP_DENSE_ATTN.
+ */
+int csa_dense_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+                       const void* q, int64_t q_ld, int64_t q_seq_stride,
+                       const void* records, int64_t records_seq_stride, int64_t n_cap,
+                       const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
+                       int64_t raw_len, const float* sink, void* out, int out_dtype,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* Weights of one CSA layer (device pointers). */
 typedef struct csa_weights {
   /* Fused projection, [n_tot, d_model] row-major (one output column per row), dtype of x, with

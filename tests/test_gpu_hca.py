@@ -105,3 +105,20 @@ def test_dense_attn_fp32_small():
     want = O.dense_attention(q64[0].astype(np.float32), e64[0].astype(np.float32), r64[0].astype(np.float32), 0,
                              q_pos0 + np.arange(T), m, w)
     assert max_err(tensor_f64(out[0]), want) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("B,T,q_pos0,n_cap", [(2, 1, 128 * 2000 + 5, 2100), (1, 40, 128 * 300 + 11, 320)])
+def test_dense_attn_over_records(B, T, q_pos0, n_cap):
+    # HCA entries in the 584-byte record format: decode splits (T = 1) and whole rows
+    q, q64 = _bf16(64, "q", (B, T, H, D))
+    ent, e64 = _bf16(64, "ent", (B, n_cap, D))
+    raw_pos0 = max(0, q_pos0 - W + 1)
+    raw, r64 = _bf16(64, "raw", (B, q_pos0 + T - raw_pos0, D))
+    rec = lib.csa_entry_pack(ent)
+    out = torch.empty(B, T, H, D, dtype=torch.float32, device="cuda")
+    lib.csa_dense_attn(_dims(), q, rec, raw, out, q_pos0=q_pos0, raw_pos0=raw_pos0)
+    stored = O.entry_unpack(O.entry_pack(e64))
+    got = tensor_f64(out)
+    for b in range(B):
+        want = O.dense_attention(q64[b], stored[b], r64[b], raw_pos0, q_pos0 + np.arange(T), M, W)
+        assert max_err(got[b], want) <= TOL["bf16"]
