@@ -81,7 +81,7 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     spacing = np.ldexp(1.0, e - 8)
     y = np.rint(x / spacing) * spacing           # np.rint rounds half to even
     big = 3.3895313892515355e38                  # largest finite bf16
-    y = np.where(np.abs(y) > big, np.sign(y) * np.inf, y)
+    y = np.where(np.abs(y) > big, np.copysign(np.inf, y), y)
     return y
 
 
