@@ -222,6 +222,26 @@ DecodeWs decode_ws(const csa_dims* d, int B, int64_t n_cap, int dtype) {
   return w;
 }
 
+// Workspace of csa_hca_decode_step: the rotated query, one compressed entry per sequence (records),
+// the dense attention's split partials.
+DecodeWs hca_decode_ws(const csa_dims* d, int B, int64_t n_cap, int dtype) {
+  const size_t es = dtype == CSA_F32 ? 4 : 2;
+  DecodeWs w{};
+  w.win = 0;
+  w.q = 0;
+  w.ent = align256((size_t)B * d->H * d->D * es);
+  w.idx = w.ent + align256((size_t)B * d->D * es);
+  w.scratch = w.idx;
+  AttnArgs a = sizing_attn(d, B, 1, dtype);
+  a.dense = 1;
+  a.m = d->m;
+  a.k = 0;
+  a.n_cap = n_cap;
+  a.q_pos0 = n_cap * d->m;  // every entry visible: the most keys a row can have
+  w.total = w.scratch + align256(attn_workspace(a));
+  return w;
+}
+
 int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
               const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride,
               int64_t n_cap, const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
@@ -327,6 +347,12 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
       int rc = check_dims(dims);
       if (rc) return rc;
       *bytes = (int64_t)decode_ws(dims, B, n_cap, idx_dtype).total;
+      return CSA_OK;
+    }
+    case CSA_OP_HCA_DECODE_STEP: {
+      int rc = check_dims(dims, false);
+      if (rc) return rc;
+      *bytes = (int64_t)hca_decode_ws(dims, B, n_cap, idx_dtype).total;
       return CSA_OK;
     }
     case CSA_OP_TOPK_FROM_SCORES: {
@@ -707,6 +733,110 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t p
   rc = attn_call("csa_decode_step", false, dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries,
                  n_cap * (st->entry_fmt ? (int64_t)kEntryRecordBytes : D), n_cap, idx, st->win, D, (int64_t)W * D,
                  raw_pos0, raw_len, w->sink, out, out_dtype, scratch, scratch_bytes, stream, st->entry_fmt, W);
+  if (rc) return rc;
+  if (fid && w->rope_dims > 0) {
+    rc = csa_norm_rope(B, 1, H, D, out_dtype, out, (int64_t)H * D, (int64_t)H * D, out, (int64_t)H * D,
+                       (int64_t)H * D, nullptr, 0.f, w->rope_dims, w->rope_theta, pos, 1, 1, stream);
+    if (rc) return rc;
+  }
+  g_err.clear();
+  return CSA_OK;
+}
+
+int csa_hca_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t pos, int dtype, const void* q,
+                        const void* kv, const void* comp, const csa_decode_state* st, void* out, int out_dtype,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims, false);
+  if (rc) return rc;
+  if (!w || !st) return fail(CSA_ERR_ARG, "weights or state is NULL");
+  if (B < 0) return fail(CSA_ERR_ARG, "B must be >= 0");
+  if (!is_act_dtype(dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
+  if (B == 0) return CSA_OK;
+  const int m = dims->m, D = dims->D, H = dims->H, W = dims->window;
+  if (m > compress_max_m()) return fail(CSA_ERR_ARG, "m=%d above %d", m, compress_max_m());
+  const int64_t n_cap = st->n_cap;
+  if (pos < 0 || (pos + 1) / m > n_cap) return fail(CSA_ERR_ARG, "pos=%lld outside the entry capacity", (long long)pos);
+  if (!q || !kv || !comp || !out || !st->entries || !st->win || !st->block || !w->bias_a)
+    return fail(CSA_ERR_ARG, "NULL tensor, state or bias pointer");
+  if (st->entry_fmt != 0 && st->entry_fmt != 1) return fail(CSA_ERR_ARG, "entry_fmt must be 0 or 1");
+  if (st->entry_fmt && D != 512) return fail(CSA_ERR_ARG, "entry records hold D = 512");
+  const bool fid = w->gamma_q || w->gamma_kv || w->rope_dims != 0;
+  if (fid && (w->rope_dims < 0 || w->rope_dims > D || w->rope_dims % 2 || (w->rope_dims > 0 && !(w->rope_theta > 0.f)) ||
+              !(w->norm_eps >= 0.f)))
+    return fail(CSA_ERR_ARG, "QK-norm / RoPE parameters: rope_dims even in [0, D], rope_theta > 0, norm_eps >= 0");
+  const DecodeWs L = hca_decode_ws(dims, B, n_cap, dtype);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int es = esize(dtype);
+  const int64_t nc = 2LL * D;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* blk = static_cast<uint8_t*>(st->block);
+  hipError_t e = launch_copy_rows(B, 1, (int)nc, es, comp, nc, nc, blk + (size_t)(pos % m) * nc * es, nc,
+                                  (int64_t)m * nc, s);
+  if (e != hipSuccess) return hip_status(e, "csa_hca_decode_step: block row");
+  uint8_t* wrow = static_cast<uint8_t*>(st->win) + (size_t)(pos % W) * D * es;
+  if (fid) {
+    rc = csa_norm_rope(B, 1, 1, D, dtype, kv, D, D, wrow, D, (int64_t)W * D, w->gamma_kv, w->norm_eps, w->rope_dims,
+                       w->rope_theta, pos, 1, 0, stream);
+    if (rc) return rc;
+  } else if ((e = launch_copy_rows(B, 1, D, es, kv, D, D, wrow, D, (int64_t)W * D, s)) != hipSuccess) {
+    return hip_status(e, "csa_hca_decode_step: window row");
+  }
+  // a completed block: its entry, pooled over the block alone
+  if ((pos + 1) % m == 0) {
+    const int64_t i = (pos + 1) / m - 1;
+    CompressArgs a{};
+    a.B = B;
+    a.n_new = 1;
+    a.m = m;
+    a.c = D;
+    a.first_entry = i;
+    a.in_dtype = dtype;
+    a.out_dtype = dtype;
+    a.ca = blk;
+    a.za = blk + (size_t)D * es;
+    a.cb = a.ca;
+    a.zb = a.za;
+    a.ld = nc;
+    a.seq_stride = (int64_t)m * nc;
+    a.halo_cb = a.ca;
+    a.halo_zb = a.za;
+    a.halo_ld = nc;
+    a.halo_seq_stride = (int64_t)m * nc;
+    a.bias_a = w->bias_a;
+    a.bias_b = w->bias_a;
+    a.overlap = false;
+    void* erow = st->entry_fmt ? (void*)(base + L.ent) : static_cast<uint8_t*>(st->entries) + (size_t)i * D * es;
+    a.entries = st->entry_fmt ? (void*)(base + L.ent) : st->entries;
+    a.entries_seq_stride = st->entry_fmt ? (int64_t)D : n_cap * D;
+    a.out_first = st->entry_fmt ? 0 : -1;
+    a.aligned16 = aligned(a.ca, 16) && aligned(a.za, 16) && aligned(a.entries, 16) && (nc * es) % 16 == 0;
+    if ((e = launch_compress(a, s)) != hipSuccess) return hip_status(e, "csa_hca_decode_step: compress");
+    const int64_t eseq = a.entries_seq_stride;
+    if (fid) {
+      rc = csa_norm_rope(B, 1, 1, D, dtype, erow, D, eseq, erow, D, eseq, w->gamma_kv, w->norm_eps, w->rope_dims,
+                         w->rope_theta, pos, 1, 0, stream);
+      if (rc) return rc;
+    }
+    if (st->entry_fmt) {
+      rc = csa_entry_pack(B, 1, dtype, erow, D, D, static_cast<uint8_t*>(st->entries) + (size_t)i * kEntryRecordBytes,
+                          n_cap * kEntryRecordBytes, stream);
+      if (rc) return rc;
+    }
+  }
+  const void* qq = q;
+  if (fid) {
+    rc = csa_norm_rope(B, 1, H, D, dtype, q, (int64_t)H * D, (int64_t)H * D, base + L.q, (int64_t)H * D,
+                       (int64_t)H * D, w->gamma_q, w->norm_eps, w->rope_dims, w->rope_theta, pos, 1, 0, stream);
+    if (rc) return rc;
+    qq = base + L.q;
+  }
+  const int64_t raw_len = pos + 1 < W ? pos + 1 : W;
+  rc = attn_call("csa_hca_decode_step", true, dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries,
+                 n_cap * (st->entry_fmt ? (int64_t)kEntryRecordBytes : D), n_cap, nullptr, st->win, D, (int64_t)W * D,
+                 pos - raw_len + 1, raw_len, w->sink, out, out_dtype, base + L.scratch, L.total - L.scratch, stream,
+                 st->entry_fmt, W);
   if (rc) return rc;
   if (fid && w->rope_dims > 0) {
     rc = csa_norm_rope(B, 1, H, D, out_dtype, out, (int64_t)H * D, (int64_t)H * D, out, (int64_t)H * D,

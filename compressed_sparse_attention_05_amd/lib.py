@@ -17,10 +17,11 @@ LIB_PATH = os.path.join(_PKG, "libcsa.so")
 CSA_F32, CSA_BF16, CSA_MXFP4 = 0, 1, 2
 ENTRY_RECORD_BYTES = 584
 CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD, CSA_OP_DENSE_ATTN, \
-    CSA_OP_DECODE_STEP = range(7)
+    CSA_OP_DECODE_STEP, CSA_OP_HCA_DECODE_STEP = range(8)
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
-           "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8")
+           "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8",
+           "csa_hca_decode_step")
 
 
 class CsaError(RuntimeError):
@@ -87,9 +88,11 @@ def load() -> ctypes.CDLL:
                                     ctypes.POINTER(DecodeState), vp, i32, vp, vp, sz, vp]
     lib.csa_sparse_attn_fp8.argtypes = lib.csa_sparse_attn.argtypes
     lib.csa_dense_attn_fp8.argtypes = lib.csa_dense_attn.argtypes
+    lib.csa_hca_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i64, i32, vp, vp, vp,
+                                        ctypes.POINTER(DecodeState), vp, i32, vp, sz, vp]
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
-              "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8"):
+              "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8", "csa_hca_decode_step"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -343,6 +346,30 @@ def csa_decode_step(dims: Dims, weights: dict, pos: int, q, q_idx, kv, comp, sta
     w = weights_struct(weights)
     _check(load().csa_decode_step(ctypes.byref(dims), ctypes.byref(w), B, pos, _dt(q), _p(q), _p(q_idx), _p(kv),
                                   _p(comp), ctypes.byref(st), _p(out), _dt(out), _p(out_idx), wp, wn, _stream()))
+    return out
+
+
+def csa_hca_decode_step(dims: Dims, weights: dict, pos: int, q, kv, comp, state: dict, out, *, ws=None):
+    """One HCA decode step (see include/csa.h): q [B, H, D], kv [B, D], comp [B, 2D]; state holds entries
+    (rows, or uint8 records), win [B, window, D], block [B, m, 2D]; weights: bias_a [m, D] (the pooling
+    biases), sink and the QK-norm / RoPE fields."""
+    _require_cuda(q, kv, comp, out)
+    for t in (q, kv, comp, out):
+        if not t.is_contiguous():
+            raise ValueError("decode step tensors must be contiguous")
+    B = q.shape[0]
+    ent = state["entries"]
+    st = DecodeState(_p(ent), 1 if ent.dtype == torch.uint8 else 0, None, ent.shape[1], _p(state["win"]),
+                     _p(state["block"]))
+    need = csa_workspace_size(CSA_OP_HCA_DECODE_STEP, dims, B, 1, ent.shape[1], 0, _dt(q))
+    if ws is None or ws.numel() < need + 256:
+        ws = _workspace(need, q.device)
+    wp, wn = _aligned_ptr(ws)
+    w = Weights(None, _p(weights["bias_a"]), None, None, None, None, _p(weights.get("sink")),
+                _p(weights.get("gamma_q")), _p(weights.get("gamma_kv")), float(weights.get("norm_eps", 0.0)),
+                int(weights.get("rope_dims", 0)), float(weights.get("rope_theta", 10000.0)))
+    _check(load().csa_hca_decode_step(ctypes.byref(dims), ctypes.byref(w), B, pos, _dt(q), _p(q), _p(kv), _p(comp),
+                                      ctypes.byref(st), _p(out), _dt(out), wp, wn, _stream()))
     return out
 
 

@@ -59,6 +59,7 @@ extern "C" {
 #define CSA_OP_FORWARD 4
 #define CSA_OP_DENSE_ATTN 5  /* csa_dense_attn; n_cap bounds the entries a row can see */
 #define CSA_OP_DECODE_STEP 6 /* csa_decode_step; T = 1, idx_dtype = the activation dtype */
+#define CSA_OP_HCA_DECODE_STEP 7 /* csa_hca_decode_step; T = 1, idx_dtype = the activation dtype */
 
 /* Layer dimensions. */
 typedef struct csa_dims {
@@ -355,6 +356,24 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t p
                     const void* q, const void* q_idx, const void* kv, const void* comp,
                     const csa_decode_state* state, void* out, int out_dtype, int32_t* out_idx,
                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step of an HCA layer ("Anatomy of a Frontier Model", bullet "Heavily Compressed
+ * Attention (HCA)": blocks of m = 128 tokens pooled without overlap, attention over every visible
+ * entry plus the window), all B sequences at position pos, over a decode state whose `block` is
+ * [B, m, 2D]: the c | z compressor inputs of the current block's tokens (keys unused). The token's
+ * c|z row goes to block row pos % m and its raw KV to window row pos % window; when it completes
+ * the block, entry (pos+1)/m - 1 is pooled from the block's rows with weights bias_a [m, D]
+ * (normalised and rotated at pos, packed into a record when entry_fmt = 1). Then the query
+ * (normalised and rotated at pos when on) attends to the floor((pos+1)/m) entries and the window;
+ * the output is rotated back by pos when RoPE is on.
+ *   q [B, H, D], kv [B, D], comp [B, 2D]; out [B, H, D] (out_dtype).
+ * Workspace: csa_workspace_size(CSA_OP_HCA_DECODE_STEP, dims, B, 1, n_cap, 0, dtype). dims->top_k
+ * and the indexer sizes are not used. Errors as csa_decode_step.
+ */
+int csa_hca_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t pos, int dtype,
+                        const void* q, const void* kv, const void* comp, const csa_decode_state* state,
+                        void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The whole layer for a chunk of T tokens per sequence at positions pos0 .. pos0+T-1:

@@ -122,3 +122,71 @@ def test_dense_attn_over_records(B, T, q_pos0, n_cap):
     for b in range(B):
         want = O.dense_attention(q64[b], stored[b], r64[b], raw_pos0, q_pos0 + np.arange(T), M, W)
         assert max_err(got[b], want) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant", ["plain", "fid_records"])
+def test_hca_decode_steps(variant):
+    # token-by-token HCA decode over a state: every step equals the oracle's row, and the entry the
+    # step at a block's last token pools equals the oracle's
+    B, L0, T = 2, 2 * M, 3 * M + 40                 # steps at 256 .. 423, the block ending at 383 completes
+    fid = variant != "plain"
+    records = fid
+    cv, c64 = _bf16(70, "hd_c", (B, T, D))
+    z, z64 = _bf16(70, "hd_z", (B, T, D), std=2.0)
+    kvd, kv64 = _bf16(70, "hd_kv", (B, T, D))
+    qd, q64 = _bf16(70, "hd_q", (B, T, H, D))
+    bias = G.normal_f32(70, "hd_bias", (M, D), std=0.5)
+    gq = (1.0 + 0.2 * G.normal_f32(70, "hd_gq", (D,))).astype(np.float32)
+    gk = (1.0 + 0.2 * G.normal_f32(70, "hd_gk", (D,))).astype(np.float32)
+    n_cap = T // M + 1
+    # oracle side: entries, window rows and queries as the layer stores them
+    ent = [O.round_bf16(O.hca_compress(c64[b], z64[b], bias.astype(np.float64), M)) for b in range(B)]
+    raw = [kv64[b] for b in range(B)]
+    qs = [q64[b] for b in range(B)]
+    if fid:
+        g_q, g_k = gq.astype(np.float64), gk.astype(np.float64)
+        ent = [O.round_bf16(O.rope(O.rms_norm(e, g_k, float(np.float32(1e-6))), O.entry_positions(0, len(e), M), 64,
+                                   10000.0)) for e in ent]
+        raw = [O.round_bf16(O.rope(O.rms_norm(r, g_k, float(np.float32(1e-6))), np.arange(T), 64, 10000.0)) for r in raw]
+        qs = [O.round_bf16(O.rope(O.rms_norm(q, g_q, float(np.float32(1e-6))), np.arange(T), 64, 10000.0)) for q in qs]
+    seen = [O.entry_unpack(O.entry_pack(e)) if records else e for e in ent]
+    # GPU state: entries of the two complete blocks, window rows of positions L0-W+1 .. L0-1
+    dims = _dims()
+    bits = lambda a: to_device(G.f32_to_bf16_bits(np.asarray(a, dtype=np.float32)), "bf16")
+    ent_dev = torch.zeros(B, n_cap, D, dtype=torch.bfloat16, device="cuda")
+    ent_dev[:, :2] = bits(np.stack([e[:2] for e in ent]))
+    if records:
+        ent_state = torch.zeros(B, n_cap, lib.ENTRY_RECORD_BYTES, dtype=torch.uint8, device="cuda")
+        lib.csa_entry_pack(ent_dev[:, :2].contiguous(), ent_state[:, :2])
+    else:
+        ent_state = ent_dev
+    win = torch.zeros(B, W, D, dtype=torch.bfloat16, device="cuda")
+    for p in range(L0 - W + 1, L0):
+        win[:, p % W] = bits(np.stack([r[p] for r in raw]))
+    block = torch.zeros(B, M, 2 * D, dtype=torch.bfloat16, device="cuda")
+    state = {"entries": ent_state, "win": win, "block": block}
+    weights = {"bias_a": to_device(bias, "f32")}
+    if fid:
+        weights.update({"gamma_q": to_device(gq, "f32"), "gamma_kv": to_device(gk, "f32"), "norm_eps": 1e-6,
+                        "rope_dims": 64, "rope_theta": 10000.0})
+    out = torch.empty(B, H, D, dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for p in range(L0, T):
+        comp = torch.cat([cv[:, p], z[:, p]], dim=1).contiguous()
+        lib.csa_hca_decode_step(dims, weights, p, qd[:, p].contiguous(), kvd[:, p].contiguous(), comp, state, out)
+        if p % 16 == 0 or p in (L0, 3 * M - 1, 3 * M, T - 1):
+            torch.cuda.synchronize()
+            got = tensor_f64(out)
+            for b in range(B):
+                o = O.dense_attention(qs[b][p:p + 1], seen[b], raw[b], 0, np.array([p]), M, W)
+                if fid:
+                    o = O.rope(o, np.array([p]), 64, 10000.0, inverse=True)
+                worst = max(worst, max_err(got[b], o[0]))
+    assert worst <= TOL["bf16"], worst
+    # the entry of the block that completed at 383
+    torch.cuda.synchronize()
+    if records:
+        np.testing.assert_allclose(O.entry_unpack(ent_state[:, 2].cpu().numpy()), np.stack([s[2] for s in seen]),
+                                   rtol=2 ** -3, atol=1e-2)
+    else:
+        assert max_err(tensor_f64(ent_state[:, 2]), np.stack([e[2] for e in ent])) <= TOL["bf16"]
