@@ -602,17 +602,20 @@ hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid
     launch_row(rs, R, s);
     return hipGetLastError();
   }
-  // Longer rows, while the candidates fit one workgroup: the k best of every kRowMax-score piece
+  // Longer rows, while the candidates fit one workgroup: the k best of every piece
   // (the row's k best are among them; each piece's list is in index order, so the concatenation
   // is too), then the k best of those candidates with positions mapped back to indices. Both
   // passes use the same key order, so the result is the direct selection's.
-  const int64_t nchunk = ceil_div(ld, kRowMax);
+  // pieces of 16K scores when their candidates fit (more workgroups, shorter ones: measured faster
+  // than 32K or 8K pieces for 1M-token rows), else 32K
+  const int64_t piece = ceil_div(ld, kRowMax / 2) * k <= kRowMax ? kRowMax / 2 : kRowMax;
+  const int64_t nchunk = ceil_div(ld, piece);
   if (nchunk * k <= kRowMax && (size_t)R * nchunk * k * 8 + 256 <= select_workspace(R, ld, k)) {
     int32_t* cand_idx = static_cast<int32_t*>(ws);
     float* cand_score = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + a256((size_t)R * nchunk * k * 4));
     rs.scores = scores;
     rs.ld = ld;
-    rs.chunk = kRowMax;
+    rs.chunk = piece;
     rs.nchunk = (int)nchunk;
     rs.n_valid = n_valid;
     rs.out_idx = cand_idx;
