@@ -980,7 +980,14 @@ AttnSplit plan_split(const AttnArgs& a) {
   const int64_t maxkeys = attn_max_keys(a);
   AttnSplit sp{1, (int)maxkeys, nullptr, nullptr};
   if (!use_attn_mfma(a) || a.T >= kDecodeRows) return sp;
-  const int split = a.dense ? kDenseSplitKeys : kSplitKeys;
+  int split = a.dense ? kDenseSplitKeys : kSplitKeys;
+  if (a.dense && maxkeys / kDenseSplitKeys >= 2) {
+    // as many splits as whole 512-key runs, the keys spread evenly over them (rounded up to a
+    // tile): 8192 entries + the window make 16 splits of 544 keys rather than 16 of 512 and a
+    // 17th of 128, which would start a second round of workgroups at 16 sequences
+    const int64_t s0 = maxkeys / kDenseSplitKeys;
+    split = (int)(ceil_div(ceil_div(maxkeys, s0), kNK) * kNK);
+  }
   const int S = (int)ceil_div(maxkeys, split);
   if (S <= 1) return sp;
   sp.n_splits = S;
@@ -1036,7 +1043,9 @@ hipError_t launch_mfma_for(const AttnArgs& a, const AttnSplit& sp, int64_t R, hi
 size_t attn_workspace(const AttnArgs& a) {
   const AttnSplit sp = plan_split(a);
   if (sp.n_splits <= 1) return 0;
-  const int64_t parts = (int64_t)a.B * a.T * sp.n_splits;
+  // a dense plan for fewer keys never has more splits than whole 512-key runs plus one
+  const int64_t S = a.dense ? ceil_div(attn_max_keys(a), kDenseSplitKeys) + 1 : sp.n_splits;
+  const int64_t parts = (int64_t)a.B * a.T * S;
   return align256((size_t)parts * a.H * 512 * 2) + align256((size_t)parts * a.H * 2 * 4);
 }
 
