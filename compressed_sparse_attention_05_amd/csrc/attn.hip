@@ -480,6 +480,10 @@ struct PairSmem {
   int32_t wcnt[16];
   int32_t keys[1];
 };
+// output staging after the loop: 32 rows of 256 bf16 per wave, rows 16 bytes apart in bank terms,
+// laid over the ring and the exchange buffers (which come first in PairSmem)
+constexpr int kOutStageRow = 528;
+static_assert(8 * 32 * kOutStageRow <= sizeof(PairSmem<8>::kn) + sizeof(PairSmem<8>::sx), "output staging fits the ring");
 
 // Workgroups of one head group per (row, split), several splits: the splits of a row are grouped
 // on one XCD.
@@ -872,29 +876,43 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
 
   // ---- output: lane holds head `head`, dims 256*half + 32dt + 8(r/4) + 4hh + r%4
   const int dbase = 256 * half + 4 * hh;
-  if (sp.n_splits == 1) {
-    const float inv = 1.f / l_run;
-    const int64_t ob = (row * a.H + head) * 512 + dbase;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) store_elem<OT>(a.out, ob + 32 * dt + 8 * (r >> 2) + (r & 3), o[dt][r] * inv);
-  } else {
+  const bool part = sp.n_splits > 1;
+  if (part || (OT == CSA_BF16 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0)) {
+    // bf16 rows go out through LDS: the wave writes its 32 heads x 256 dims into its own staging
+    // rows, then each store instruction writes two whole 512-byte half rows (16 bytes a lane)
+    // instead of 16-byte pieces of 32 rows. Every wave has passed its last read of the ring and the
+    // exchange buffers (the last barrier follows the last P V of both groups), so their space is free.
     const int64_t pidx = row * sp.n_splits + split;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* po = sp.part_o + (pidx * a.H + head) * 512 + dbase;
+    const float inv = part ? (l_run > 0.f ? 1.f / l_run : 0.f) : 1.f / l_run;
+    uint8_t* stg = smem_raw + (size_t)wave * 32 * kOutStageRow;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const uint32_t w0 = f2bf(o[dt][4 * q4] * inv) | ((uint32_t)f2bf(o[dt][4 * q4 + 1] * inv) << 16);
         const uint32_t w1 = f2bf(o[dt][4 * q4 + 2] * inv) | ((uint32_t)f2bf(o[dt][4 * q4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(po + 32 * dt + 8 * q4) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(stg + hl * kOutStageRow + (32 * dt + 8 * q4 + 4 * hh) * 2) = make_uint2(w0, w1);
       }
-    if (half == 0 && hh == 0) {
+    __syncthreads();  // lanes read what other lanes wrote (the condition is uniform over the workgroup)
+    uint16_t* dst = part ? sp.part_o + pidx * a.H * 512 : static_cast<uint16_t*>(a.out) + row * a.H * 512;
+    const int head0 = head - hl;  // first head of this wave
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int hr = 2 * i + (lane >> 5);
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + hr * kOutStageRow + (lane & 31) * 16);
+      *reinterpret_cast<uint4*>(dst + (int64_t)(head0 + hr) * 512 + 256 * half + (lane & 31) * 8) = v;
+    }
+    if (part && half == 0 && hh == 0) {
       sp.part_ml[(pidx * a.H + head) * 2] = m_run;
       sp.part_ml[(pidx * a.H + head) * 2 + 1] = l_run;
     }
+  } else {
+    const float inv = 1.f / l_run;
+    const int64_t ob = (row * a.H + head) * 512 + dbase;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) store_elem<OT>(a.out, ob + 32 * dt + 8 * (r >> 2) + (r & 3), o[dt][r] * inv);
   }
 }
 
