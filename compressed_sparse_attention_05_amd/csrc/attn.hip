@@ -134,6 +134,10 @@ constexpr int kKNS = 536;             // LDS row stride (bf16) of a key row, 107
                                       // consecutive rows keep 32-byte reads apart
 constexpr float kRescaleLog2 = 8.f;   // reference-max slack before O is rescaled
 
+// output staging row of the 16-head kernel: 512 bf16 plus 16 bytes, so that the 16 rows of a
+// wave start on different banks
+constexpr int kOutStageRowM = 1040;
+
 // RING key tiles in LDS: the one read and RING - 1 being loaded
 template <int RING>
 struct AttnSmem {
@@ -425,27 +429,40 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
   }
 
   // ---- output: lane holds head `head`, dims db*16 + 4g + r
-  if (sp.n_splits == 1) {
+  const bool part = sp.n_splits > 1;
+  if (part || (OT == CSA_BF16 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0)) {
+    // bf16 rows go out through LDS: the wave writes its 16 heads x 512 dims into its own staging
+    // rows over the ring, then each store instruction writes one whole 1 KiB head row
+    static_assert(NW * 16 * kOutStageRowM <= RING * kNK * kKNS * 2, "output staging fits the ring");
+    const int64_t pidx = row * sp.n_splits + split;
+    const float inv = part ? (l_run > 0.f ? 1.f / l_run : 0.f) : 1.f / l_run;
+    uint8_t* stg = reinterpret_cast<uint8_t*>(&sm.kn[0][0][0]) + (size_t)wave * 16 * kOutStageRowM;
+    __syncthreads();  // every wave is past its last read of the ring (the condition is uniform)
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const uint32_t w0 = f2bf(o[db][0] * inv) | ((uint32_t)f2bf(o[db][1] * inv) << 16);
+      const uint32_t w1 = f2bf(o[db][2] * inv) | ((uint32_t)f2bf(o[db][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(stg + (lane & 15) * kOutStageRowM + (db * 16 + 4 * g) * 2) = make_uint2(w0, w1);
+    }
+    __syncthreads();  // lanes read what other lanes wrote
+    uint16_t* dst = part ? sp.part_o + pidx * a.H * 512 : static_cast<uint16_t*>(a.out) + row * a.H * 512;
+    const int head0 = head - (lane & 15);  // first head of this wave
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + i * kOutStageRowM + lane * 16);
+      *reinterpret_cast<uint4*>(dst + (int64_t)(head0 + i) * 512 + lane * 8) = v;
+    }
+    if (part && g == 0) {
+      sp.part_ml[(pidx * a.H + head) * 2] = m_run;
+      sp.part_ml[(pidx * a.H + head) * 2 + 1] = l_run;
+    }
+  } else {
     const float inv = 1.f / l_run;
     const int64_t ob = (row * a.H + head) * 512 + 4 * g;
 #pragma unroll
     for (int db = 0; db < 32; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) store_elem<OT>(a.out, ob + db * 16 + r, o[db][r] * inv);
-  } else {
-    const int64_t pidx = row * sp.n_splits + split;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* po = sp.part_o + (pidx * a.H + head) * 512 + 4 * g;
-#pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const uint32_t w0 = f2bf(o[db][0] * inv) | ((uint32_t)f2bf(o[db][1] * inv) << 16);
-      const uint32_t w1 = f2bf(o[db][2] * inv) | ((uint32_t)f2bf(o[db][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(po + db * 16) = make_uint2(w0, w1);
-    }
-    if (g == 0) {
-      sp.part_ml[(pidx * a.H + head) * 2] = m_run;
-      sp.part_ml[(pidx * a.H + head) * 2 + 1] = l_run;
-    }
   }
 }
 

@@ -232,8 +232,9 @@ def _decode_check(wl, inp, st, seqs):
         assert max_err(gout[b], ref) <= TOL["bf16"], f"sequence {b}"
 
 
-def test_decode_bf16_small():
-    wl = get("decode128k").with_(B=3, L=4096 + 2048)
+@pytest.mark.parametrize("H", [128, 64])   # 64 heads: the 16-head-per-wave kernel and its split merge
+def test_decode_bf16_small(H):
+    wl = get("decode128k").with_(B=3, L=4096 + 2048, H=H)
     inp = G.make_inputs(wl)
     st = run_decode(wl, decode_tensors(wl, inp))
     _decode_check(wl, inp, st, range(wl.B))
@@ -350,3 +351,27 @@ def test_sparse_attn_prefill_batch_invariance():
         lib.csa_sparse_attn(d, q[b:b + 1].contiguous(), ent[b:b + 1].contiguous(), idx[b:b + 1].contiguous(),
                             raw[b:b + 1].contiguous(), one, q_pos0=q_pos0, raw_pos0=raw_pos0)
         assert torch.equal(one[0], out[b])
+
+
+@pytest.mark.parametrize("H", [128, 64])
+def test_sparse_attn_bf16_output_alignment(H):
+    # a bf16 output that is not 16-byte aligned takes the element-wise store path; both paths give
+    # the same bits as the LDS-staged row stores
+    T, D, k, n_cap, q_pos0 = 64, 512, 512, 1500, 4 * 1500 - 64
+    d = dims_of(get("decode128k").with_(k=k, H=H))
+    mk = lambda name, shape: to_device(G.f32_to_bf16_bits(G.normal_f32(72, name, shape)), "bf16")
+    q, ent = mk("q", (1, T, H, D)), mk("ent", (1, n_cap, D))
+    raw_pos0 = q_pos0 - 127
+    raw = mk("raw", (1, q_pos0 + T - raw_pos0, D))
+    rng = np.random.default_rng(72)
+    idx = to_device(np.stack([np.sort(rng.choice(n_cap, k, replace=False)) for _ in range(T)])[None].astype(np.int32), "i32")
+    out = torch.empty(1, T, H, D, dtype=torch.bfloat16, device="cuda")
+    lib.csa_sparse_attn(d, q, ent, idx, raw, out, q_pos0=q_pos0, raw_pos0=raw_pos0)
+    buf = torch.empty(T * H * D + 8, dtype=torch.bfloat16, device="cuda")
+    odd = buf[1:1 + T * H * D].view(1, T, H, D)
+    assert odd.data_ptr() % 16 != 0
+    lib.csa_sparse_attn(d, q, ent, idx, raw, odd, q_pos0=q_pos0, raw_pos0=raw_pos0)
+    assert torch.equal(odd, out)
+    ref = torch.empty(1, T, H, D, dtype=torch.float32, device="cuda")
+    lib.csa_sparse_attn(d, q, ent, idx, raw, ref, q_pos0=q_pos0, raw_pos0=raw_pos0)
+    assert torch.equal(ref.bfloat16(), out)
