@@ -944,10 +944,31 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   const int64_t row = gid / a.H;
   const int h = (int)(gid % a.H);
   const int lane = lane_id();
+  const int S = sp.n_splits;
+  // splits in groups of four, every load of a group issued before any is used; the first group is
+  // loaded together with the (m, l) pairs, so that the common case (at most four splits) waits for
+  // memory once. A split without keys has l = 0 and a zero partial, so it adds nothing.
+  auto load_group = [&](int s0, uint4 (&u)[4], float (&m)[4], float (&l)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = s0 + j < S ? s0 + j : S - 1;
+      const int64_t pidx = row * S + s;
+      const float2 ml = *reinterpret_cast<const float2*>(sp.part_ml + (pidx * a.H + h) * 2);
+      m[j] = ml.x;
+      l[j] = s0 + j < S ? ml.y : 0.f;
+      u[j] = *reinterpret_cast<const uint4*>(sp.part_o + (pidx * a.H + h) * 512 + lane * 8);
+    }
+  };
+  uint4 u[4];
+  float m[4], l[4];
+  load_group(0, u, m, l);
   float M = -INFINITY;
-  for (int s = 0; s < sp.n_splits; ++s) {
-    const float* ml = sp.part_ml + ((row * sp.n_splits + s) * a.H + h) * 2;
-    if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (l[j] > 0.f) M = fmaxf(M, m[j]);
+  for (int s = 4; s < S; ++s) {
+    const float2 ml = *reinterpret_cast<const float2*>(sp.part_ml + ((row * S + s) * a.H + h) * 2);
+    if (ml.y > 0.f) M = fmaxf(M, ml.x);
   }
   float sink2 = -INFINITY;
   if (a.sink) {
@@ -956,31 +977,28 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   }
   float L = a.sink ? exp2f(sink2 - M) : 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // splits in groups of four, every load of a group issued before any is used; a split without
-  // keys has l = 0 and a zero partial, so it adds nothing
-  for (int s0 = 0; s0 < sp.n_splits; s0 += 4) {
-    uint4 u[4];
-    float wgt[4];
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    if (s0 > 0) load_group(s0, u, m, l);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int s = s0 + j < sp.n_splits ? s0 + j : sp.n_splits - 1;
-      const int64_t pidx = row * sp.n_splits + s;
-      const float* ml = sp.part_ml + (pidx * a.H + h) * 2;
-      wgt[j] = (s0 + j < sp.n_splits && ml[1] > 0.f) ? ml[1] * exp2f(ml[0] - M) : 0.f;
-      u[j] = *reinterpret_cast<const uint4*>(sp.part_o + (pidx * a.H + h) * 512 + lane * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      L += wgt[j];
+      const float wgt = l[j] > 0.f ? l[j] * exp2f(m[j] - M) : 0.f;
+      L += wgt;
       const uint32_t w4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(__uint_as_float((w4[i >> 1] >> ((i & 1) * 16)) << 16), wgt[j], acc[i]);
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(__uint_as_float((w4[i >> 1] >> ((i & 1) * 16)) << 16), wgt, acc[i]);
     }
   }
   const float inv = 1.f / L;
   const int64_t ob = (row * a.H + h) * 512 + lane * 8;
+  if (OT == CSA_BF16 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0) {
+    uint32_t w[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) store_elem<OT>(a.out, ob + j, acc[j] * inv);
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(acc[2 * i] * inv) | ((uint32_t)f2bf(acc[2 * i + 1] * inv) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + ob) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) store_elem<OT>(a.out, ob + j, acc[j] * inv);
+  }
 }
 
 // LDS of the deepest variant (8 waves, three-deep ring); the 4-wave variant uses a two-deep ring
