@@ -936,7 +936,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
 // Merges the n_splits partials of every (row, head): M = max m_s, L = sum l_s 2^(m_s - M) (plus the
 // sink), O = sum l_s 2^(m_s - M) (O_s / l_s) / L, splits taken in order. One wave per (row, head),
 // four per workgroup.
-template <int OT>
+template <int OT, int kG>
 __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   const int64_t R = (int64_t)a.B * a.T;
   const int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
@@ -945,13 +945,14 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   const int h = (int)(gid % a.H);
   const int lane = lane_id();
   const int S = sp.n_splits;
-  // splits in groups of four, every load of a group issued before any is used; the first group is
-  // loaded together with the (m, l) pairs, so that the common case (at most four splits) waits for
-  // memory once. A split without keys has l = 0 and a zero partial, so it adds nothing.
-  auto load_group = [&](int s0, uint4 (&u)[4], float (&m)[4], float (&l)[4]) {
+  // splits in groups of kG (4, 8 or 16: the smallest that holds all splits, up to 16), every load
+  // of a group issued before any is used; the first group is loaded together with the (m, l) pairs,
+  // so that up to sixteen splits wait for memory once. A split without keys has l = 0 and a zero
+  // partial, so it adds nothing.
+  auto load_group = [&](int s0, uint4 (&u)[kG], float (&m)[kG], float (&l)[kG]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = s0 + j < S ? s0 + j : S - 1;
+    for (int j = 0; j < kG; ++j) {
+      const int s = s0 + j < S ? s0 + j : S - 1;  // past the last split: its copy, with l = 0
       const int64_t pidx = row * S + s;
       const float2 ml = *reinterpret_cast<const float2*>(sp.part_ml + (pidx * a.H + h) * 2);
       m[j] = ml.x;
@@ -959,14 +960,14 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
       u[j] = *reinterpret_cast<const uint4*>(sp.part_o + (pidx * a.H + h) * 512 + lane * 8);
     }
   };
-  uint4 u[4];
-  float m[4], l[4];
+  uint4 u[kG];
+  float m[kG], l[kG];
   load_group(0, u, m, l);
   float M = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < kG; ++j)
     if (l[j] > 0.f) M = fmaxf(M, m[j]);
-  for (int s = 4; s < S; ++s) {
+  for (int s = kG; s < S; ++s) {
     const float2 ml = *reinterpret_cast<const float2*>(sp.part_ml + ((row * S + s) * a.H + h) * 2);
     if (ml.y > 0.f) M = fmaxf(M, ml.x);
   }
@@ -977,10 +978,11 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   }
   float L = a.sink ? exp2f(sink2 - M) : 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 4) {
+  for (int s0 = 0; s0 < S; s0 += kG) {
     if (s0 > 0) load_group(s0, u, m, l);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kG; ++j) {
+      // past the last split l = 0, so the weight is 0 and the zero partial adds nothing
       const float wgt = l[j] > 0.f ? l[j] * exp2f(m[j] - M) : 0.f;
       L += wgt;
       const uint32_t w4[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
@@ -1118,10 +1120,17 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t
     if (e != hipSuccess) return e;
     if (sp.n_splits > 1) {
       const dim3 cg((unsigned)ceil_div(R * a.H, 4));
-      if (a.out_dtype == CSA_BF16)
-        hipLaunchKernelGGL(attn_combine<CSA_BF16>, cg, dim3(256), 0, s, a, sp);
-      else
-        hipLaunchKernelGGL(attn_combine<CSA_F32>, cg, dim3(256), 0, s, a, sp);
+      const bool bf = a.out_dtype == CSA_BF16;
+      if (sp.n_splits <= 4) {
+        if (bf) hipLaunchKernelGGL((attn_combine<CSA_BF16, 4>), cg, dim3(256), 0, s, a, sp);
+        else hipLaunchKernelGGL((attn_combine<CSA_F32, 4>), cg, dim3(256), 0, s, a, sp);
+      } else if (sp.n_splits <= 8) {
+        if (bf) hipLaunchKernelGGL((attn_combine<CSA_BF16, 8>), cg, dim3(256), 0, s, a, sp);
+        else hipLaunchKernelGGL((attn_combine<CSA_F32, 8>), cg, dim3(256), 0, s, a, sp);
+      } else {
+        if (bf) hipLaunchKernelGGL((attn_combine<CSA_BF16, 16>), cg, dim3(256), 0, s, a, sp);
+        else hipLaunchKernelGGL((attn_combine<CSA_F32, 16>), cg, dim3(256), 0, s, a, sp);
+      }
       return hipGetLastError();
     }
     return hipSuccess;
