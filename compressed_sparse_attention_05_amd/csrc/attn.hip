@@ -1014,8 +1014,11 @@ int attn_mfma_lds(const AttnArgs& a) {
 }
 
 bool use_attn_mfma(const AttnArgs& a) {
-  // records: the pairs kernel (128 heads, staging rows within the LDS) or the generic one
-  if (a.entry_fmt && (a.H != 128 || pairs_lds<8>(a) > (size_t)kMaxLds)) return false;
+  // records: the pairs kernel (8 waves for 128 heads, 4 for 64; staging rows within the LDS) or
+  // the generic one
+  if (a.entry_fmt && !((a.H == 128 && pairs_lds<8>(a) <= (size_t)kMaxLds) ||
+                       (a.H == 64 && pairs_lds<4>(a) <= (size_t)kMaxLds)))
+    return false;
   return a.in_dtype == CSA_BF16 && a.D == 512 && (a.H == 64 || a.H == 128) && a.raw_ld % 4 == 0 &&
          a.q_ld % 8 == 0 && a.q_seq_stride % 8 == 0 && a.entries_seq_stride % 4 == 0 && a.raw_seq_stride % 4 == 0 &&
          attn_mfma_lds(a) <= kMaxLds;
@@ -1087,6 +1090,9 @@ hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipSt
 template <int OT>
 hipError_t launch_mfma_for(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
   if (attn_waves(a) == 8) return launch_pairs<8, OT>(a, sp, R, s);
+  // 64-head layers over records: the pairs kernel with one wave group (it alone stages and converts
+  // records)
+  if (a.entry_fmt) return launch_pairs_fmt<4, OT, 1>(a, sp, R, s);
   // Too few workgroups to share compute units: a three-deep ring keeps two gathers in flight per
   // workgroup. Otherwise a two-deep ring lets two workgroups share a compute unit.
   if (R * sp.n_splits * (a.H / (kHPW * 4)) < 256) return launch_mfma<4, 3, OT>(a, sp, R, s);

@@ -86,9 +86,10 @@ def _attn_case(seed, B, T, H, n_cap, k, q_pos0, q_dtype="bf16"):
     return out, q, stored, idx, raw, raw_pos0
 
 
-@pytest.mark.parametrize("B,T,H,k", [(2, 1, 128, 1024), (1, 72, 128, 512), (2, 5, 64, 256)])
+@pytest.mark.parametrize("B,T,H,k", [(2, 1, 128, 1024), (1, 72, 128, 512), (2, 5, 64, 256), (3, 1, 64, 1024),
+                                     (1, 40, 64, 512)])
 def test_sparse_attn_over_records(B, T, H, k):
-    # 128 heads: the pairs kernel (decode splits at T = 1, whole rows at T = 72); 64 heads: generic
+    # the pairs kernel: 8 waves for 128 heads, 4 for 64 (decode splits at T <= 5, whole rows at T >= 40)
     n_cap, q_pos0 = 3000, 4 * 3000 + 7
     out, q, stored, idx, raw, raw_pos0 = _attn_case(102 + T, B, T, H, n_cap, k, q_pos0)
     got = tensor_f64(out)
