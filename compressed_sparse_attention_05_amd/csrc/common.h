@@ -187,7 +187,7 @@ __device__ __forceinline__ void wait_vmcnt_upto16(int n) {
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // n_vis(p) = min(floor((p+1)/m), n_cap): entries whose block is complete at position p.
-__device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t n_cap) {
+__host__ __device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t n_cap) {
   int64_t v = (p + 1) / m;
   if (v < 0) v = 0;
   return v < n_cap ? v : n_cap;

@@ -534,7 +534,9 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
                          select_hist(p), select_zero_words((int)R));
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s);
+    // every row's valid count is at most that of the last query position
+    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s,
+                         n_visible(a.q_pos0 + a.T - 1, a.m, a.n_cap));
   }
   const int cap = topk_cap_for(a.k, 256);
   const int lds = kGenWaves * (cap * 8 + 256 * 4);

@@ -107,8 +107,10 @@ uint32_t* select_hist(void* ws);  // the [R, 4096] histogram at the start of the
 // 32-bit words at the start of the workspace that must be zero before launch_select(zeroed=true)
 int64_t select_zero_words(int R);
 hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s);
+// max_valid: a bound, known on the host, of every row's n_valid (-1: none); rows longer than one
+// workgroup's reach whose valid prefix fits it are still selected in one pass
 hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
-                         float* out_score, void* ws, bool zeroed, hipStream_t s);
+                         float* out_score, void* ws, bool zeroed, hipStream_t s, int64_t max_valid = -1);
 hipError_t launch_topk_from_scores(const TopkArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct AttnArgs {

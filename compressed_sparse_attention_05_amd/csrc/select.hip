@@ -588,13 +588,15 @@ hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s)
 }
 
 hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
-                         float* out_score, void* ws, bool zeroed, hipStream_t s) {
+                         float* out_score, void* ws, bool zeroed, hipStream_t s, int64_t max_valid) {
   RowSel rs{};
   rs.k = k;
-  if (ld <= kRowMax) {
+  // the part of a row that can hold valid scores (n_valid never exceeds max_valid when it is given)
+  const int64_t span = max_valid >= 0 && max_valid < ld ? max_valid : ld;
+  if (span <= kRowMax) {
     rs.scores = scores;
     rs.ld = ld;
-    rs.chunk = ld;
+    rs.chunk = span;
     rs.nchunk = 1;
     rs.n_valid = n_valid;
     rs.out_idx = out_idx;
@@ -608,8 +610,8 @@ hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid
   // passes use the same key order, so the result is the direct selection's.
   // pieces of 16K scores when their candidates fit (more workgroups, shorter ones: measured faster
   // than 32K or 8K pieces for 1M-token rows), else 32K
-  const int64_t piece = ceil_div(ld, kRowMax / 2) * k <= kRowMax ? kRowMax / 2 : kRowMax;
-  const int64_t nchunk = ceil_div(ld, piece);
+  const int64_t piece = ceil_div(span, kRowMax / 2) * k <= kRowMax ? kRowMax / 2 : kRowMax;
+  const int64_t nchunk = ceil_div(span, piece);
   if (nchunk * k <= kRowMax && (size_t)R * nchunk * k * 8 + 256 <= select_workspace(R, ld, k)) {
     int32_t* cand_idx = static_cast<int32_t*>(ws);
     float* cand_score = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + a256((size_t)R * nchunk * k * 4));

@@ -375,3 +375,21 @@ def test_sparse_attn_bf16_output_alignment(H):
     ref = torch.empty(1, T, H, D, dtype=torch.float32, device="cuda")
     lib.csa_sparse_attn(d, q, ent, idx, raw, ref, q_pos0=q_pos0, raw_pos0=raw_pos0)
     assert torch.equal(ref.bfloat16(), out)
+
+
+@pytest.mark.parametrize("n_cap,L", [(40001, 4 * 30000), (40000, 4 * 24000), (70001, 4 * 50000)])
+def test_decode_index_capacity_beyond_visible(n_cap, L):
+    # a key cache with more slots than the query sees: the selection covers the visible prefix (one
+    # pass while it fits a workgroup, 16K pieces of it otherwise), whatever the row stride
+    B, H_I, D_I, k = 2, 64, 128, 1024
+    d = dims_of(get("decode128k").with_(k=k))
+    mk = lambda name, shape: G.f32_to_bf16_bits(G.normal_f32(73, name, shape))
+    qb, kb = mk("iq", (B, 1, H_I, D_I)), mk("ik", (B, n_cap, D_I))
+    w = G.normal_f32(73, "iw", (H_I,))
+    out_idx = torch.empty(B, 1, k, dtype=torch.int32, device="cuda")
+    lib.csa_index_topk(d, to_device(qb, "bf16"), to_device(w, "f32"), to_device(kb, "bf16"), out_idx, q_pos0=L)
+    got = out_idx.cpu().numpy()
+    nv = min((L + 1) // 4, n_cap)
+    for b in range(B):
+        s = O.index_scores(O.bf16_bits_to_f64(qb[b, 0])[None], O.bf16_bits_to_f64(kb[b]), w.astype(np.float64), [nv])
+        check_idx_rows(got[b], O.topk_select(s[0], nv, k)[None], s, [nv])
