@@ -107,16 +107,18 @@ def test_dense_attn_fp32_small():
     assert max_err(tensor_f64(out[0]), want) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("h", [H, 64])
 @pytest.mark.parametrize("B,T,q_pos0,n_cap", [(2, 1, 128 * 2000 + 5, 2100), (1, 40, 128 * 300 + 11, 320)])
-def test_dense_attn_over_records(B, T, q_pos0, n_cap):
-    # HCA entries in the 584-byte record format: decode splits (T = 1) and whole rows
-    q, q64 = _bf16(64, "q", (B, T, H, D))
+def test_dense_attn_over_records(B, T, q_pos0, n_cap, h):
+    # HCA entries in the 584-byte record format: decode splits (T = 1) and whole rows; 128 heads in
+    # the 8-wave pairs kernel, 64 in the 4-wave one
+    q, q64 = _bf16(64, "q", (B, T, h, D))
     ent, e64 = _bf16(64, "ent", (B, n_cap, D))
     raw_pos0 = max(0, q_pos0 - W + 1)
     raw, r64 = _bf16(64, "raw", (B, q_pos0 + T - raw_pos0, D))
     rec = lib.csa_entry_pack(ent)
-    out = torch.empty(B, T, H, D, dtype=torch.float32, device="cuda")
-    lib.csa_dense_attn(_dims(), q, rec, raw, out, q_pos0=q_pos0, raw_pos0=raw_pos0)
+    out = torch.empty(B, T, h, D, dtype=torch.float32, device="cuda")
+    lib.csa_dense_attn(_dims(h=h), q, rec, raw, out, q_pos0=q_pos0, raw_pos0=raw_pos0)
     stored = O.entry_unpack(O.entry_pack(e64))
     got = tensor_f64(out)
     for b in range(B):
