@@ -264,7 +264,9 @@ def bench_prefill(wl, steps, warmup):
     q_idx = P[:, c_qi:c_qi + wl.H_I * wl.D_I].view(wl.B, wl.T, wl.H_I, wl.D_I)
     idx = torch.empty_like(st.idx)
     w_head = weights["w_head"]
-    run_idx = lambda: lib.csa_index_topk(d, q_idx, w_head, st.keys, idx, q_pos0=wl.L)
+    qp = lib.positions(wl.B, wl.L)                     # device position arrays, built once
+    rp = lib.positions(wl.B, wl.L - (wl.W - 1))
+    run_idx = lambda: lib.csa_index_topk(d, q_idx, w_head, st.keys, idx, q_pos0=qp)
     run_idx()
     torch.cuda.synchronize()
     idx_ms = timed_events(run_idx, steps, torch.cuda.synchronize)
@@ -272,8 +274,7 @@ def bench_prefill(wl, steps, warmup):
     c_q = 4 * wl.D + 4 * wl.D_I
     q = P[:, c_q:c_q + wl.H * wl.D].view(wl.B, wl.T, wl.H, wl.D)
     out = torch.empty_like(st.out)
-    run_attn = lambda: lib.csa_sparse_attn(d, q, st.entries, st.idx, st.win, out, q_pos0=wl.L,
-                                           raw_pos0=wl.L - (wl.W - 1))
+    run_attn = lambda: lib.csa_sparse_attn(d, q, st.entries, st.idx, st.win, out, q_pos0=qp, raw_pos0=rp)
     run_attn()
     torch.cuda.synchronize()
     attn_ms = timed_events(run_attn, steps, torch.cuda.synchronize)
@@ -451,8 +452,9 @@ def bench_hca(steps, warmup):
     bias = to_device(G.normal_f32(70, "hca_bias", (m, D), 0.5), "f32")
     o = torch.empty(1, T, H, D, dtype=torch.bfloat16, device="cuda")
     ws = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_DENSE_ATTN, dims, 1, T, n_cap, 0, lib.CSA_BF16) + 256)
-    att = lambda: lib.csa_dense_attn(dims, q, ent, raw, o, q_pos0=L, raw_pos0=L - W + 1, ws=ws)
-    cmp = lambda: lib.csa_hca_compress(cv, z, bias, ent, pos0=L, m=m)
+    qp, rp = lib.positions(1, L), lib.positions(1, L - W + 1)
+    att = lambda: lib.csa_dense_attn(dims, q, ent, raw, o, q_pos0=qp, raw_pos0=rp, ws=ws)
+    cmp = lambda: lib.csa_hca_compress(cv, z, bias, ent, pos0=qp, m=m)
     for _ in range(warmup):
         cmp()
         att()
@@ -476,7 +478,8 @@ def bench_hca(steps, warmup):
     raw = bf(71, "hca_raw", (B, W, D))
     o = torch.empty(B, 1, H, D, dtype=torch.bfloat16, device="cuda")
     ws = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_DENSE_ATTN, dims, B, 1, n_cap, 0, lib.CSA_BF16) + 256)
-    step = lambda: lib.csa_dense_attn(dims, q, ent, raw, o, q_pos0=L - 1, raw_pos0=L - W, ws=ws)
+    qp, rp = lib.positions(B, L - 1), lib.positions(B, L - W)
+    step = lambda: lib.csa_dense_attn(dims, q, ent, raw, o, q_pos0=qp, raw_pos0=rp, ws=ws)
     flush = torch.ones(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     for _ in range(warmup):
         step()

@@ -19,20 +19,23 @@ namespace csa {
 
 namespace {
 
-__device__ __forceinline__ int64_t window_lo(const AttnArgs& a, int64_t p) {
+// The window [max(0, p - W + 1), p], cut to the raw rows the caller holds: positions rp .. rp +
+// raw_len - 1 (rp = raw_pos[b]); for a ring only the last raw_ring positions up to p.
+__device__ __forceinline__ int64_t window_lo(const AttnArgs& a, int64_t p, int64_t rp) {
   int64_t lo = p - a.W + 1;
   if (lo < 0) lo = 0;
-  if (lo < a.raw_pos0) lo = a.raw_pos0;
+  if (lo < rp) lo = rp;
+  if (a.raw_ring > 0 && lo < p - a.raw_ring + 1) lo = p - a.raw_ring + 1;
   return lo;
 }
-__device__ __forceinline__ int64_t window_hi(const AttnArgs& a, int64_t p) {
+__device__ __forceinline__ int64_t window_hi(const AttnArgs& a, int64_t p, int64_t rp) {
   int64_t hi = p;
-  if (hi > a.raw_pos0 + a.raw_len - 1) hi = a.raw_pos0 + a.raw_len - 1;
+  if (hi > rp + a.raw_len - 1) hi = rp + a.raw_len - 1;
   return hi;
 }
-// row of kv_raw holding raw position u: u - raw_pos0, or u mod raw_ring for a ring buffer
-__device__ __forceinline__ int64_t raw_row(const AttnArgs& a, int64_t u) {
-  return a.raw_ring > 0 ? u % a.raw_ring : u - a.raw_pos0;
+// row of kv_raw holding raw position u: u - rp, or u mod raw_ring for a ring buffer
+__device__ __forceinline__ int64_t raw_row(const AttnArgs& a, int64_t u, int64_t rp) {
+  return a.raw_ring > 0 ? u % a.raw_ring : u - rp;
 }
 // dense mode: the entries visible to position p, min(floor((p+1)/m), n_cap)
 __host__ __device__ __forceinline__ int64_t dense_visible(const AttnArgs& a, int64_t p) {
@@ -64,8 +67,8 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int64_t row = blockIdx.x;
   const int b = (int)(row / a.T), t = (int)(row % a.T);
-  const int64_t p = a.q_pos0 + t;
-  const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
+  const int64_t p = pos_at(a.q_pos, b) + t, rp = raw_at(a.raw_pos, b) + a.raw_off;
+  const int64_t wlo = window_lo(a, p, rp), whi = window_hi(a, p, rp);
   const int32_t* idx = a.dense ? nullptr : a.idx + row * a.k;
   constexpr int kMaxPer = 16;  // dims per lane (D <= 1024)
   const int per = (a.D + 63) / 64;
@@ -96,7 +99,7 @@ __global__ void __launch_bounds__(kGenWaves * 64) attn_generic(AttnArgs a) {
         off = (int64_t)b * a.entries_seq_stride + (int64_t)e * (record ? kEntryBytes : a.D);
       } else {
         src = a.raw;
-        off = (int64_t)b * a.raw_seq_stride + raw_row(a, wlo + (j - nsel)) * a.raw_ld;
+        off = (int64_t)b * a.raw_seq_stride + raw_row(a, wlo + (j - nsel), rp) * a.raw_ld;
       }
       float kv[kMaxPer];
       float part = 0.f;
@@ -197,8 +200,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
   const int split = (int)((blockIdx.x / n_hg) % sp.n_splits);
   const int64_t row = blockIdx.x / n_hg / sp.n_splits;
   const int b = (int)(row / a.T), t = (int)(row % a.T);
-  const int64_t p = a.q_pos0 + t;
-  const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
+  const int64_t p = pos_at(a.q_pos, b) + t, rp = raw_at(a.raw_pos, b) + a.raw_off;
+  const int64_t wlo = window_lo(a, p, rp), whi = window_hi(a, p, rp);
 
   // ---- Q_w^T as B-fragments: head 16w + lane%16, dims s*32 + (lane/16)*8 .. +7 (issued first, so
   // that their latency overlaps the key list)
@@ -216,7 +219,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
   // position and nothing is stored.
   const int64_t nvis_d = a.dense ? dense_visible(a, p) : 0;
   auto key_id = [&](int kj) -> int32_t {
-    return kj < nvis_d ? kj : -(int32_t)raw_row(a, wlo + (kj - nvis_d)) - 1;
+    return kj < nvis_d ? kj : -(int32_t)raw_row(a, wlo + (kj - nvis_d), rp) - 1;
   };
   if (!a.dense) {
     const int32_t* idx = a.idx + row * a.k;
@@ -248,7 +251,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
       }
     }
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
-    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)raw_row(a, wlo + j) - 1;
+    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)raw_row(a, wlo + j, rp) - 1;
     if (threadIdx.x == 0) sm.keys[a.k + a.W] = nsel + nwin;
     __syncthreads();
   }
@@ -542,8 +545,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
     row = blockIdx.x / n_hg / sp.n_splits;
   }
   const int b = (int)(row / a.T), t = (int)(row % a.T);
-  const int64_t p = a.q_pos0 + t;
-  const int64_t wlo = window_lo(a, p), whi = window_hi(a, p);
+  const int64_t p = pos_at(a.q_pos, b) + t, rp = raw_at(a.raw_pos, b) + a.raw_off;
+  const int64_t wlo = window_lo(a, p, rp), whi = window_hi(a, p, rp);
 
   const int half = wave & 1;                    // dims 256*half .. +255
   const int hl = lane & 31, hh = lane >> 5;     // head within the pair; k half of a fragment
@@ -564,7 +567,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   // mode every visible entry in order, then the window, with ids from the position
   const int64_t nvis_d = a.dense ? dense_visible(a, p) : 0;
   auto key_id = [&](int kj) -> int32_t {
-    return kj < nvis_d ? kj : -(int32_t)raw_row(a, wlo + (kj - nvis_d)) - 1;
+    return kj < nvis_d ? kj : -(int32_t)raw_row(a, wlo + (kj - nvis_d), rp) - 1;
   };
   if (a.dense) load_q();
   else {
@@ -599,7 +602,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
       }
     }
     const int nwin = whi >= wlo ? (int)(whi - wlo + 1) : 0;
-    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)raw_row(a, wlo + j) - 1;
+    for (int j = threadIdx.x; j < nwin; j += kThreads) sm.keys[nsel + j] = -(int32_t)raw_row(a, wlo + j, rp) - 1;
     if (threadIdx.x == 0) sm.keys[a.k + a.W] = nsel + nwin;
     __syncthreads();
   }
@@ -1028,10 +1031,11 @@ constexpr int kDecodeRows = 8;     // fewer query rows per sequence than this: d
 constexpr int kSplitKeys = 288;    // keys per split in the decode regime (9 tiles: 1152 keys in 4)
 constexpr int kDenseSplitKeys = 512;  // dense mode (thousands of keys per row): 16 tiles per split
 
-// most keys any query row of the call can have
+// most keys any query row of the call can have (dense: every entry slot visible; the positions
+// live on the device, so the plan takes the capacity)
 int64_t attn_max_keys(const AttnArgs& a) {
   if (!a.dense) return (int64_t)a.k + a.W;
-  return dense_visible(a, a.q_pos0 + a.T - 1) + a.W;
+  return a.n_cap + a.W;
 }
 
 AttnSplit plan_split(const AttnArgs& a) {

@@ -186,6 +186,17 @@ __device__ __forceinline__ void wait_vmcnt_upto16(int n) {
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Position of sequence b from a device array of per-sequence positions; NULL means every sequence
+// is at 0, and a negative value counts as 0.
+__device__ __forceinline__ int64_t pos_at(const int64_t* pos, int64_t b) {
+  if (!pos) return 0;
+  const int64_t p = pos[b];
+  return p > 0 ? p : 0;
+}
+
+// An offset position from a device array, taken as given (NULL: 0).
+__device__ __forceinline__ int64_t raw_at(const int64_t* pos, int64_t b) { return pos ? pos[b] : 0; }
+
 // n_vis(p) = min(floor((p+1)/m), n_cap): entries whose block is complete at position p.
 __host__ __device__ __forceinline__ int64_t n_visible(int64_t p, int m, int64_t n_cap) {
   int64_t v = (p + 1) / m;

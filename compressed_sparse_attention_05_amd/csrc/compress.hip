@@ -12,85 +12,15 @@
 // needed. A thread owns VEC consecutive channels of one entry and issues 16-byte loads along the
 // channel axis (coalesced across the threads of a row).
 #include "kernels.h"
+#include "pool.h"
+#include "record.h"
+#include "rope.h"
 
 namespace csa {
 
 namespace {
 
-template <int DT>
-struct Vec;
-template <>
-struct Vec<CSA_BF16> {
-  static constexpr int N = 8;
-  __device__ static void load(const void* p, int64_t off, float* v) {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + off);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(w[j] << 16);
-      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-  }
-  __device__ static void store(void* p, int64_t off, const float* v) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f2bf(v[2 * j]) | ((uint32_t)f2bf(v[2 * j + 1]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + off) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-};
-template <>
-struct Vec<CSA_F32> {
-  static constexpr int N = 4;
-  __device__ static void load(const void* p, int64_t off, float* v) {
-    const float4 u = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + off);
-    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-  }
-  __device__ static void store(void* p, int64_t off, const float* v) {
-    *reinterpret_cast<float4*>(static_cast<float*>(p) + off) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-};
-
-// Scalar fallback for channel counts or strides that are not vector aligned.
-template <int DT>
-struct Scalar {
-  static constexpr int N = 1;
-  __device__ static void load(const void* p, int64_t off, float* v) { v[0] = load_elem<DT>(p, off); }
-  __device__ static void store(void* p, int64_t off, const float* v) { store_elem<DT>(p, off, v[0]); }
-};
-
 constexpr int kMaxM = 128;
-
-// Softmax-weighted sum accumulated online per channel: running maximum mx, denominator den and
-// numerator num; each logit rescales the running sums when it raises the maximum.
-template <int V>
-__device__ __forceinline__ void accumulate(const float* z, const float* bias, const float* c,
-                                           float* mx, float* den, float* num) {
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const float l = z[v] + bias[v];
-    const float nm = fmaxf(mx[v], l);
-    const float sc = expf(mx[v] - nm);
-    const float p = expf(l - nm);
-    den[v] = fmaf(den[v], sc, p);
-    num[v] = fmaf(num[v], sc, p * c[v]);
-    mx[v] = nm;
-  }
-}
-
-// Merges the online-softmax state of another thread's rows: both maxima are brought to the larger
-// one. Symmetric in its two operands, so every lane of a butterfly ends with the same bits.
-template <int V>
-__device__ __forceinline__ void merge(float* mx, float* den, float* num, const float* mx2, const float* den2,
-                                      const float* num2) {
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const float nm = fmaxf(mx[v], mx2[v]);
-    const float s1 = expf(mx[v] - nm), s2 = expf(mx2[v] - nm);
-    den[v] = den[v] * s1 + den2[v] * s2;
-    num[v] = num[v] * s1 + num2[v] * s2;
-    mx[v] = nm;
-  }
-}
 
 // G consecutive threads share one (entry, channel vector): thread `sub` takes rows sub, sub + G, ...
 // of each block, and the G partial softmax states meet through a shuffle butterfly. G = 1 for short
@@ -108,7 +38,11 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   const int e = (int)(slot / cv);
   const int j0 = (int)(slot % cv) * V;
   const int m = a.m;
-  const int64_t i = a.first_entry + e;
+  const int64_t first = pos_at(a.pos0, b) / m;  // entry of the chunk's first block
+  const int64_t i = first + e;
+  // the entry's row: rows past the capacity are not written (and their inputs not read)
+  const int64_t orow = (a.out_first >= 0 ? a.out_first : first) + e;
+  if (a.out_first < 0 && orow >= a.n_cap) return;
   const int64_t sbase = (int64_t)b * a.seq_stride;
 
   float mx[V], den[V], num[V];
@@ -180,7 +114,55 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   float out[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) out[v] = num[v] / den[v];
-  const int64_t orow = (a.out_first >= 0 ? a.out_first : a.first_entry) + e;
+  if (a.epilogue) {
+    // The cv = c / V threads of one entry are consecutive lanes of one wave (G = 1, cv a power of two
+    // <= 64). The entry is rounded to its storage type, RMS-normalised (gain gamma) and turned by RoPE
+    // at its block's last token, (i + 1) m - 1, as a separate pass over the stored entry would; then
+    // stored, or packed into its 584-byte record (cv = 64: lane l holds dims 8l .. 8l + 7).
+    const bool bf = a.out_dtype == CSA_BF16;
+    if (bf) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[v] = bf2f(f2bf(out[v]));
+    }
+    if (a.gamma) {
+      float ss = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) ss = fmaf(out[v], out[v], ss);
+      for (int o = cv >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+      const float inv = 1.f / sqrtf(ss / (float)a.c + a.eps);
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[v] = out[v] * inv * a.gamma[j0 + v];
+    }
+    if (a.rope_dims > 0) {
+      const int rs = a.c - a.rope_dims;
+      const double pos = (double)((i + 1) * m - 1), lt = log2(a.theta);
+      if (V >= 2) {  // pairs (2t, 2t + 1) inside the vector (j0 is even)
+#pragma unroll
+        for (int v = 0; v + 1 < V; v += 2) {
+          if (j0 + v < rs) continue;
+          float cs, sn;
+          rope_cos_sin(pos, (j0 + v - rs) >> 1, a.rope_dims, lt, false, cs, sn);
+          const float x0 = out[v], x1 = out[v + 1];
+          out[v] = x0 * cs - x1 * sn;
+          out[v + 1] = x0 * sn + x1 * cs;
+        }
+      } else {  // one channel per lane: the partner is the neighbouring lane
+        const float other = __shfl_xor(out[0], 1, 64);
+        if (j0 >= rs) {
+          float cs, sn;
+          rope_cos_sin(pos, (j0 - rs) >> 1, a.rope_dims, lt, false, cs, sn);
+          out[0] = ((j0 - rs) & 1) == 0 ? out[0] * cs - other * sn : other * sn + out[0] * cs;
+        }
+      }
+    }
+    if (a.records) {
+      if constexpr (V == 8) {
+        pack_record_wave(out, static_cast<uint8_t*>(a.entries) + (int64_t)b * a.entries_seq_stride +
+                                  orow * kEntryRecordBytes);
+      }
+      return;
+    }
+  }
   VO::store(a.entries, (int64_t)b * a.entries_seq_stride + orow * a.c + j0, out);
 }
 
@@ -191,6 +173,9 @@ hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
                       (a.halo_seq_stride % Vec<DI>::N == 0) && (a.entries_seq_stride % Vec<DI>::N == 0) &&
                       Vec<DI>::N == Vec<DO>::N && a.aligned16;
   const int V = vec_ok ? Vec<DI>::N : 1;
+  const int cv = a.c / V;
+  // the epilogue's reductions need an entry's threads inside one wave
+  if (a.epilogue && (cv > 64 || (cv & (cv - 1)) || (a.records && V != 8))) return hipErrorInvalidValue;
   const int64_t threads = (int64_t)a.n_new * (a.c / V) * a.group;
   dim3 grid((unsigned)ceil_div(threads, 256), (unsigned)a.B);
   if (vec_ok) {
@@ -203,10 +188,20 @@ hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
 
 }  // namespace
 
+bool compress_epilogue_ok(const CompressArgs& a) {
+  // one entry's channel vectors on consecutive lanes of one wave; records need one wave of 8 dims
+  const int V = a.in_dtype == CSA_BF16 && a.out_dtype == CSA_BF16 ? 8 : (a.in_dtype == CSA_F32 && a.out_dtype == CSA_F32 ? 4 : 1);
+  const int cv = a.c / V;
+  if (a.m >= 64 || a.c % V || cv > 64 || (cv & (cv - 1))) return false;
+  if (a.records && (a.c != 512 || V != 8 || a.out_dtype != CSA_BF16)) return false;
+  return true;
+}
+
 hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
   if (a0.n_new <= 0 || a0.B <= 0) return hipSuccess;
   CompressArgs a = a0;
   a.group = a.m >= 64 ? 16 : 1;  // threads per (entry, channel vector); every thread has >= 4 rows
+  if (a.epilogue && (!compress_epilogue_ok(a) || a.group != 1)) return hipErrorInvalidValue;
   if (a.in_dtype == CSA_BF16 && a.out_dtype == CSA_BF16) return launch_typed<CSA_BF16, CSA_BF16>(a, s);
   if (a.in_dtype == CSA_F32 && a.out_dtype == CSA_F32) return launch_typed<CSA_F32, CSA_F32>(a, s);
   if (a.in_dtype == CSA_BF16 && a.out_dtype == CSA_F32) {

@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(kGenWaves * 64) index_generic(IndexArgs a, int
   const int b = (int)(row / a.T), t = (int)(row % a.T);
   uint64_t* buf = reinterpret_cast<uint64_t*>(smem) + (int64_t)wave * cap;
   uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<uint64_t*>(smem) + kGenWaves * cap) + wave * 256;
-  const int64_t nv = n_visible(a.q_pos0 + t, a.m, a.n_cap);
+  const int64_t nv = n_visible(pos_at(a.q_pos, b) + t, a.m, a.n_cap);
   const int64_t ru = row_units<DT>(a.D_I);
   const int nsb = a.D_I / 32;
   const void* q = advance<DT>(a.q, (int64_t)b * a.q_seq_stride + (int64_t)t * a.q_ld);
@@ -147,9 +147,10 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
   const bool active = t < a.T;
   const int tq = active ? t : t0;
   const int64_t row = (int64_t)b * a.T + tq;
-  const int64_t nv = active ? n_visible(a.q_pos0 + t, a.m, a.n_cap) : 0;
+  const int64_t qp0 = pos_at(a.q_pos, b);
+  const int64_t nv = active ? n_visible(qp0 + t, a.m, a.n_cap) : 0;
   const int t_last = (t0 + QW < a.T ? t0 + QW : a.T) - 1;
-  const int64_t nv_max = n_visible(a.q_pos0 + t_last, a.m, a.n_cap);
+  const int64_t nv_max = n_visible(qp0 + t_last, a.m, a.n_cap);
 
   // q_I of this wave's row as A-fragments: heads mt*32 + lane%32, dims s*16 + (lane/32)*8 .. +7
   const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)tq * a.q_ld;
@@ -345,7 +346,7 @@ __global__ void __launch_bounds__(kStreamWaves * 64) score_bf16_stream(IndexArgs
     const int64_t row = u / units_per_row;
     const int64_t base = (u % units_per_row) * kUnit + wave * 64;
     const int b = (int)(row / a.T), tq = (int)(row % a.T);
-    const int64_t nv = n_visible(a.q_pos0 + tq, a.m, a.n_cap);
+    const int64_t nv = n_visible(pos_at(a.q_pos, b) + tq, a.m, a.n_cap);
     if (row != cur_row) {  // uniform across the workgroup
       __syncthreads();
       cur_row = row;
@@ -418,7 +419,7 @@ __global__ void __launch_bounds__(kFp4Waves * 64) score_fp4_stream(IndexArgs a, 
     const int64_t row = t / tiles_per_row;
     const int64_t base = (t % tiles_per_row) * 64;
     const int b = (int)(row / a.T), tq = (int)(row % a.T);
-    const int64_t nv = n_visible(a.q_pos0 + tq, a.m, a.n_cap);
+    const int64_t nv = n_visible(pos_at(a.q_pos, b) + tq, a.m, a.n_cap);
     if (base == 0 && lane == 0) n_valid[row] = (int32_t)nv;
     if (base >= nv) continue;
     if (row != cur_row) {
@@ -534,9 +535,7 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
                          select_hist(p), select_zero_words((int)R));
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // every row's valid count is at most that of the last query position
-    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s,
-                         n_visible(a.q_pos0 + a.T - 1, a.m, a.n_cap));
+    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s);
   }
   const int cap = topk_cap_for(a.k, 256);
   const int lds = kGenWaves * (cap * 8 + 256 * 4);

@@ -7,7 +7,7 @@ namespace csa {
 
 struct CompressArgs {
   int B, n_new, m, c;
-  int64_t first_entry;
+  const int64_t* pos0;  // device [B] (nullable: all 0): entry rows start at pos0[b] / m
   int in_dtype, out_dtype;
   const void *ca, *za, *cb, *zb;
   int64_t ld, seq_stride;
@@ -16,15 +16,27 @@ struct CompressArgs {
   const float *bias_a, *bias_b;
   void* entries;
   int64_t entries_seq_stride;
+  int64_t n_cap;        // rows of `entries` per sequence (rows at or past it are not written)
   bool aligned16;
   bool overlap = true;  // pool the previous block too (CSA); false: own block only (HCA)
   int group = 1;        // threads per (entry, channel vector); set by launch_compress
-  int64_t out_first = -1;  // row of `entries` receiving the first new entry (-1: first_entry)
+  int64_t out_first = -1;  // row of `entries` receiving the first new entry (-1: pos0[b] / m)
+  // Epilogue (CSA entries, compress_epilogue_ok): after rounding to the storage type, RMS norm with
+  // gain gamma (nullable) and RoPE of the last rope_dims dims at the entry's last token; records: the
+  // entry is packed into a 584-byte record (entries_seq_stride then counts bytes).
+  bool epilogue = false;
+  const float* gamma = nullptr;
+  float eps = 0.f;
+  int rope_dims = 0;
+  double theta = 10000.0;
+  bool records = false;
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+bool compress_epilogue_ok(const CompressArgs& a);
 
-// QK-norm and partial RoPE over B x R rows of H head vectors of D dims; row r sits at position
-// pos0 + r * pos_step. gamma == nullptr: no norm; rope_dims == 0: no rotation; inverse: turn back.
+// QK-norm and partial RoPE over B x R rows of H head vectors of D dims; row r of sequence b sits at
+// position pos[b] + pos_off + r * pos_step (pos nullable: 0). gamma == nullptr: no norm;
+// rope_dims == 0: no rotation; inverse: turn back.
 struct NormRopeArgs {
   int B = 0, R = 0, H = 0, D = 0, dtype = 0;
   const void* x = nullptr;
@@ -35,10 +47,36 @@ struct NormRopeArgs {
   float eps = 0.f;
   int rope_dims = 0;
   double theta = 10000.0;
-  int64_t pos0 = 0, pos_step = 1;
+  const int64_t* pos = nullptr;
+  int64_t pos_off = 0, pos_step = 1;
   int inverse = 0;
 };
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t s);
+
+// The decode state's append for B sequences, each at its own position (decode.hip).
+struct AppendArgs {
+  int B = 0, m = 0, D = 0, D_I = 0, H = 0, W = 0, dtype = 0;
+  bool hca = false;              // HCA state: one block of m rows [c | z], no indexer keys
+  const int64_t* pos = nullptr;  // device [B]
+  const void* comp = nullptr;    // [B, nc]: nc = 4D + 4D_I (CSA) or 2D (HCA)
+  const void* kv = nullptr;      // [B, D]
+  const void* q = nullptr;       // [B, H, D]
+  void* qn = nullptr;            // [B, H, D] normalised / rotated query (nullptr: no query pass)
+  void* block = nullptr;         // CSA [B, 2m, nc] (block i in rows (i % 2) * m ..), HCA [B, m, nc]
+  void* win = nullptr;           // [B, W, D] ring: position p in row p % W
+  void* entries = nullptr;       // [B, n_cap, D] rows or [B, n_cap, 584] records
+  void* keys = nullptr;          // [B, n_cap, D_I] (CSA)
+  int64_t n_cap = 0;
+  int entry_fmt = 0;
+  const float *bias_a = nullptr, *bias_b = nullptr, *ibias_a = nullptr, *ibias_b = nullptr;
+  const float *gamma_q = nullptr, *gamma_kv = nullptr;
+  float eps = 0.f;
+  int rope_dims = 0;
+  double theta = 10000.0;
+  bool aligned16 = false;        // comp, block, entries, keys 16-byte aligned
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+int append_max_dim();
 
 // 584-byte FP8 entry records of B x N entries of 512 dims (entries at b*seq_stride + n*ld).
 constexpr int kEntryRecordBytes = 584;
@@ -73,7 +111,7 @@ hipError_t launch_gemm_library(const GemmArgs& a, void* ws, size_t ws_bytes, hip
 
 struct IndexArgs {
   int B, T;
-  int64_t q_pos0;
+  const int64_t* q_pos;        // device [B] (nullable: all 0): row t of sequence b at q_pos[b] + t
   int m, H_I, D_I, k;
   int idx_dtype;
   const void* q;
@@ -115,7 +153,7 @@ hipError_t launch_topk_from_scores(const TopkArgs& a, void* ws, size_t ws_bytes,
 
 struct AttnArgs {
   int B, T;
-  int64_t q_pos0;
+  const int64_t* q_pos;    // device [B] (nullable: all 0): row t of sequence b at q_pos[b] + t
   int H, D, k, W;
   float scale;
   int in_dtype, out_dtype;
@@ -125,7 +163,10 @@ struct AttnArgs {
   int64_t entries_seq_stride, n_cap;
   const int32_t* idx;
   const void* raw;
-  int64_t raw_ld, raw_seq_stride, raw_pos0, raw_len;
+  int64_t raw_ld, raw_seq_stride;
+  const int64_t* raw_pos;  // device [B] (nullable: all 0): kv_raw row r of sequence b is position
+  int64_t raw_off = 0;     // raw_pos[b] + raw_off + r (any sign; rows of negative positions are not read)
+  int64_t raw_len;
   const float* sink;
   void* out;
   int dense = 0;  // attend to every visible entry in order (HCA); idx is not read and k is unused

@@ -9,6 +9,7 @@
 // The angle is formed and its sine and cosine taken in fp64: at positions near 2^20 an fp32 angle
 // would be off by up to ~0.06 rad.
 #include "kernels.h"
+#include "rope.h"
 
 namespace csa {
 
@@ -16,9 +17,6 @@ namespace {
 
 constexpr int kNormWaves = 4;
 constexpr int kNormMaxPer = 64;  // D <= 4096
-
-__device__ __forceinline__ void rope_cos_sin(double pos, int i, int rope_dims, double lt, bool inverse, float& c,
-                                             float& s);
 
 // PER: dims per lane, a compile-time bound (D <= 64 * PER) so that v[] stays in registers
 template <int DT, int PER>
@@ -54,7 +52,7 @@ __global__ void __launch_bounds__(kNormWaves * 64) norm_rope_kernel(NormRopeArgs
   }
   if (a.rope_dims > 0) {
     const int rs = a.D - a.rope_dims;
-    const double pos = (double)(a.pos0 + r * a.pos_step);
+    const double pos = (double)(pos_at(a.pos, b) + a.pos_off + r * a.pos_step);
     const double lt = log2(a.theta);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -74,17 +72,6 @@ __global__ void __launch_bounds__(kNormWaves * 64) norm_rope_kernel(NormRopeArgs
     const int d = lane + 64 * j;
     if (j >= jlo && d < a.D) store_elem<DT>(a.y, yo + d, v[j]);
   }
-}
-
-// cos and sin of pos * theta^(-2i/rope_dims): the angle is formed and reduced to [-pi, pi] in fp64,
-// then its sine and cosine are taken in fp32 (the reduced angle is exact to ~1e-7 rad)
-__device__ __forceinline__ void rope_cos_sin(double pos, int i, int rope_dims, double lt, bool inverse, float& c,
-                                             float& s) {
-  const double ang = pos * exp2(-(2.0 * i / rope_dims) * lt);
-  const double k = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
-  const float red = (float)fma(-k, 6.283185307179586, ang);
-  sincosf(red, &s, &c);
-  if (inverse) s = -s;
 }
 
 // Contiguous layout (D = 64 * PER, PER a multiple of the 16-byte vector, 16-byte aligned rows): lane
@@ -112,7 +99,7 @@ __global__ void __launch_bounds__(kNormWaves * 64) norm_rope_contig(NormRopeArgs
   const bool mine = a.gamma || !inplace || rot;
   float cs[PER / 2], sn[PER / 2];
   if (rot) {
-    const double pos = (double)(a.pos0 + r * a.pos_step);
+    const double pos = (double)(pos_at(a.pos, b) + a.pos_off + r * a.pos_step);
     const double lt = log2(a.theta);
 #pragma unroll
     for (int t = 0; t < PER / 2; ++t) {

@@ -9,6 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -69,26 +70,26 @@ def load() -> ctypes.CDLL:
     lib.csa_version.restype = i32
     lib.csa_last_error.restype = ctypes.c_char_p
     lib.csa_workspace_size.argtypes = [i32, ctypes.POINTER(Dims), i32, i32, i64, i32, i32, ctypes.POINTER(i64)]
-    lib.csa_compress.argtypes = [i32, i32, i64, i32, i32, i32, vp, vp, vp, vp, i64, i64, vp, vp, i64, i64, vp, vp,
+    lib.csa_compress.argtypes = [i32, i32, vp, i32, i32, i32, vp, vp, vp, vp, i64, i64, vp, vp, i64, i64, vp, vp,
                                  vp, i64, i64, i32, vp]
-    lib.csa_index_topk.argtypes = [ctypes.POINTER(Dims), i32, i32, i64, i32, vp, i64, i64, vp, vp, i64, vp, i64, vp,
+    lib.csa_index_topk.argtypes = [ctypes.POINTER(Dims), i32, i32, vp, i32, vp, i64, i64, vp, vp, i64, vp, i64, vp,
                                    i64, vp, vp, vp, sz, vp]
     lib.csa_topk_from_scores.argtypes = [vp, i64, vp, i32, i32, vp, vp, vp, sz, vp]
-    lib.csa_sparse_attn.argtypes = [ctypes.POINTER(Dims), i32, i32, i64, i32, vp, i64, i64, vp, i64, i64, vp, vp,
-                                    i64, i64, i64, i64, vp, vp, i32, vp, sz, vp]
-    lib.csa_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i32, i64, i32, i32, vp,
+    lib.csa_sparse_attn.argtypes = [ctypes.POINTER(Dims), i32, i32, vp, i32, vp, i64, i64, vp, i64, i64, vp, vp,
+                                    i64, i64, vp, i64, vp, vp, i32, vp, sz, vp]
+    lib.csa_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i32, vp, i32, i32, vp,
                                 ctypes.POINTER(Cache), vp, i32, vp, vp, sz, vp]
-    lib.csa_hca_compress.argtypes = [i32, i32, i64, i32, i32, i32, vp, vp, i64, i64, vp, vp, i64, i64, i32, vp]
-    lib.csa_dense_attn.argtypes = [ctypes.POINTER(Dims), i32, i32, i64, i32, vp, i64, i64, vp, i64, i64, vp,
-                                   i64, i64, i64, i64, vp, vp, i32, vp, sz, vp]
+    lib.csa_hca_compress.argtypes = [i32, i32, vp, i32, i32, i32, vp, vp, i64, i64, vp, vp, i64, i64, i32, vp]
+    lib.csa_dense_attn.argtypes = [ctypes.POINTER(Dims), i32, i32, vp, i32, vp, i64, i64, vp, i64, i64, vp,
+                                   i64, i64, vp, i64, vp, vp, i32, vp, sz, vp]
     lib.csa_norm_rope.argtypes = [i32, i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, vp, ctypes.c_float, i32,
-                                  ctypes.c_float, i64, i64, i32, vp]
+                                  ctypes.c_float, vp, i64, i64, i32, vp]
     lib.csa_entry_pack.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, vp]
-    lib.csa_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i64, i32, vp, vp, vp, vp,
+    lib.csa_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, vp, i32, vp, vp, vp, vp,
                                     ctypes.POINTER(DecodeState), vp, i32, vp, vp, sz, vp]
     lib.csa_sparse_attn_fp8.argtypes = lib.csa_sparse_attn.argtypes
     lib.csa_dense_attn_fp8.argtypes = lib.csa_dense_attn.argtypes
-    lib.csa_hca_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i64, i32, vp, vp, vp,
+    lib.csa_hca_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, vp, i32, vp, vp, vp,
                                         ctypes.POINTER(DecodeState), vp, i32, vp, sz, vp]
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
@@ -142,6 +143,26 @@ def _workspace(nbytes: int, device) -> torch.Tensor | None:
     return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
 
 
+def positions(B: int, v, device="cuda", null_if_zero: bool = True):
+    """Per-sequence positions as the device int64 [B] array the C ABI takes: an int gives every
+    sequence that position (None when it is 0 and null_if_zero: the ABI reads NULL as all zeros), a
+    sequence gives one per sequence, a tensor is passed as is (int64, [B], contiguous, on the GPU)."""
+    if v is None:
+        return None
+    if isinstance(v, torch.Tensor):
+        if v.dtype != torch.int64 or v.numel() != B or not v.is_cuda or not v.is_contiguous():
+            raise ValueError("positions must be a contiguous int64 [B] tensor on the GPU")
+        return v
+    if isinstance(v, (int, np.integer)):
+        if v == 0 and null_if_zero:
+            return None
+        return torch.full((B,), int(v), dtype=torch.int64, device=device)
+    t = torch.as_tensor(np.asarray(v, dtype=np.int64), device=device)
+    if t.numel() != B:
+        raise ValueError(f"{t.numel()} positions for {B} sequences")
+    return t.contiguous()
+
+
 def _aligned_ptr(ws):
     if ws is None:
         return None, 0
@@ -161,8 +182,9 @@ def csa_workspace_size(op: int, dims: Dims, B: int, T: int, n_cap: int, d_model:
     return out.value
 
 
-def csa_compress(ca, za, cb, zb, bias_a, bias_b, entries, *, pos0: int, m: int, halo_cb=None, halo_zb=None):
-    """Step 1. ca/za/cb/zb: [B, T, c] views sharing strides; entries: [B, n_cap, c] (rows contiguous)."""
+def csa_compress(ca, za, cb, zb, bias_a, bias_b, entries, *, pos0, m: int, halo_cb=None, halo_zb=None):
+    """Step 1. ca/za/cb/zb: [B, T, c] views sharing strides; entries: [B, n_cap, c] (rows contiguous);
+    pos0: an int or per-sequence positions (see positions())."""
     _require_cuda(ca, za, cb, zb, bias_a, bias_b, entries, halo_cb, halo_zb)
     B, T, c = ca.shape
     for v in (za, cb, zb):
@@ -175,13 +197,14 @@ def csa_compress(ca, za, cb, zb, bias_a, bias_b, entries, *, pos0: int, m: int, 
         if halo_cb.stride() != halo_zb.stride() or halo_cb.stride(2) != 1:
             raise ValueError("halo views must share strides with unit channel stride")
         hl, hs = halo_cb.stride(1), halo_cb.stride(0)
-    _check(load().csa_compress(B, T, pos0, m, c, _dt(ca), _p(ca), _p(za), _p(cb), _p(zb), ca.stride(1), ca.stride(0),
+    pos = positions(B, pos0, ca.device)
+    _check(load().csa_compress(B, T, _p(pos), m, c, _dt(ca), _p(ca), _p(za), _p(cb), _p(zb), ca.stride(1), ca.stride(0),
                                _p(halo_cb), _p(halo_zb), hl, hs, _p(bias_a), _p(bias_b), _p(entries),
                                entries.stride(0), entries.shape[1], _dt(entries), _stream()))
     return entries
 
 
-def csa_index_topk(dims: Dims, q_idx, w, keys, out_idx, *, q_pos0: int, q_scale=None, k_scale=None,
+def csa_index_topk(dims: Dims, q_idx, w, keys, out_idx, *, q_pos0, q_scale=None, k_scale=None,
                    out_score=None, ws=None):
     """Steps 2+3. q_idx [B, T, H_I, D_I] (MXFP4: uint8 codes [B, T, H_I, D_I/2] + q_scale);
     keys [B, n_cap, D_I] (MXFP4: uint8 [B, n_cap, D_I/2] + k_scale); w [H_I] or per row [B, T, H_I];
@@ -204,7 +227,8 @@ def csa_index_topk(dims: Dims, q_idx, w, keys, out_idx, *, q_pos0: int, q_scale=
     if ws is None or ws.numel() < need + 256:
         ws = _workspace(need, q_idx.device)
     wp, wn = _aligned_ptr(ws)
-    _check(load().csa_index_topk(ctypes.byref(dims), B, T, q_pos0, dt, _p(q_idx), q_ld, q_ss, _p(q_scale), _p(w),
+    qp = positions(B, q_pos0, q_idx.device)
+    _check(load().csa_index_topk(ctypes.byref(dims), B, T, _p(qp), dt, _p(q_idx), q_ld, q_ss, _p(q_scale), _p(w),
                                  w_ld, _p(keys), k_ss, _p(k_scale), n_cap, _p(out_idx), _p(out_score), wp, wn,
                                  _stream()))
     return out_idx
@@ -225,9 +249,10 @@ def csa_topk_from_scores(scores, n_valid, k: int, out_idx, out_score=None):
     return out_idx
 
 
-def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, raw_pos0: int, sink=None, ws=None):
-    """Step 4. q [B, T, H, D]; entries [B, n_cap, D]; idx int32 [B, T, k]; kv_raw [B, R, D] whose row r is
-    position raw_pos0 + r; out [B, T, H, D] (float32 or bfloat16)."""
+def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0, raw_pos0, sink=None, ws=None):
+    """Step 4. q [B, T, H, D]; entries [B, n_cap, D]; idx int32 [B, T, k]; kv_raw [B, R, D] whose row r of
+    sequence b is position raw_pos0[b] + r; out [B, T, H, D] (float32 or bfloat16). Positions: ints or
+    per-sequence (see positions())."""
     _require_cuda(q, entries, idx, kv_raw, out, sink)
     B, T = q.shape[0], q.shape[1]
     records = entries.dtype == torch.uint8          # [B, n_cap, 584] FP8 entry records
@@ -241,9 +266,10 @@ def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0: int, ra
         ws = _workspace(need, q.device)
     wp, wn = _aligned_ptr(ws)
     fn = load().csa_sparse_attn_fp8 if records else load().csa_sparse_attn
-    _check(fn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
+    qp, rp = positions(B, q_pos0, q.device), positions(B, raw_pos0, q.device)
+    _check(fn(ctypes.byref(dims), B, T, _p(qp), _dt(q), _p(q), q.stride(1), q.stride(0),
               _p(entries), entries.stride(0), entries.shape[1], _p(idx), _p(kv_raw),
-              kv_raw.stride(1), kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out),
+              kv_raw.stride(1), kv_raw.stride(0), _p(rp), kv_raw.shape[1], _p(sink), _p(out),
               _dt(out), wp, wn, _stream()))
     return out
 
@@ -263,7 +289,7 @@ def csa_entry_pack(entries, records=None):
     return records
 
 
-def csa_hca_compress(cv, z, bias, entries, *, pos0: int, m: int):
+def csa_hca_compress(cv, z, bias, entries, *, pos0, m: int):
     """HCA compressor. cv, z: [B, T, c] views sharing strides; bias float32 [m, c]; entries [B, n_cap, c]."""
     _require_cuda(cv, z, bias, entries)
     B, T, c = cv.shape
@@ -271,15 +297,17 @@ def csa_hca_compress(cv, z, bias, entries, *, pos0: int, m: int):
         raise ValueError("cv and z must share shape and strides")
     if cv.stride(2) != 1 or entries.stride(2) != 1 or entries.stride(1) != c:
         raise ValueError("channel axes must be contiguous")
-    _check(load().csa_hca_compress(B, T, pos0, m, c, _dt(cv), _p(cv), _p(z), cv.stride(1), cv.stride(0), _p(bias),
+    pos = positions(B, pos0, cv.device)
+    _check(load().csa_hca_compress(B, T, _p(pos), m, c, _dt(cv), _p(cv), _p(z), cv.stride(1), cv.stride(0), _p(bias),
                                    _p(entries), entries.stride(0), entries.shape[1], _dt(entries), _stream()))
     return entries
 
 
-def csa_norm_rope(x, *, pos0: int, pos_step: int = 1, gamma=None, eps: float = 0.0, rope_dims: int = 0,
-                  theta: float = 10000.0, inverse: bool = False, y=None):
-    """QK-norm and partial RoPE on x [B, R, H, D] (or [B, R, D]: one head), row r at position
-    pos0 + r * pos_step; into y (same shape and dtype) or in place. gamma float32 [D] or None."""
+def csa_norm_rope(x, *, pos0, pos_step: int = 1, pos_off: int = 0, gamma=None, eps: float = 0.0,
+                  rope_dims: int = 0, theta: float = 10000.0, inverse: bool = False, y=None):
+    """QK-norm and partial RoPE on x [B, R, H, D] (or [B, R, D]: one head), row r of sequence b at position
+    pos0[b] + pos_off + r * pos_step (pos0: an int or per-sequence positions); into y (same shape and
+    dtype) or in place. gamma float32 [D] or None."""
     _require_cuda(x, y, gamma)
     y = x if y is None else y
     if x.dim() == 3:
@@ -292,12 +320,16 @@ def csa_norm_rope(x, *, pos0: int, pos_step: int = 1, gamma=None, eps: float = 0
             raise ValueError("head vectors must be contiguous")
     if y.shape != x.shape or y.dtype != x.dtype:
         raise ValueError("y must match x")
+    if isinstance(pos0, (int, np.integer)):  # a common position goes in pos_off (no device array)
+        pos_off, pos0 = pos_off + int(pos0), None
+    pos = positions(B, pos0, x.device)
     _check(load().csa_norm_rope(B, R, H, D, _dt(x), _p(x), x.stride(1), x.stride(0), _p(y), y.stride(1), y.stride(0),
-                                _p(gamma), eps, rope_dims, theta, pos0, pos_step, 1 if inverse else 0, _stream()))
+                                _p(gamma), eps, rope_dims, theta, _p(pos), pos_off, pos_step, 1 if inverse else 0,
+                                _stream()))
     return y
 
 
-def csa_dense_attn(dims: Dims, q, entries, kv_raw, out, *, q_pos0: int, raw_pos0: int, sink=None, ws=None):
+def csa_dense_attn(dims: Dims, q, entries, kv_raw, out, *, q_pos0, raw_pos0, sink=None, ws=None):
     """HCA attention over every visible entry plus the window. q [B, T, H, D]; entries [B, n_cap, D];
     kv_raw [B, R, D] whose row r is position raw_pos0 + r; out [B, T, H, D] (float32 or bfloat16)."""
     _require_cuda(q, entries, kv_raw, out, sink)
@@ -313,9 +345,10 @@ def csa_dense_attn(dims: Dims, q, entries, kv_raw, out, *, q_pos0: int, raw_pos0
         ws = _workspace(need, q.device)
     wp, wn = _aligned_ptr(ws)
     fn = load().csa_dense_attn_fp8 if records else load().csa_dense_attn
-    _check(fn(ctypes.byref(dims), B, T, q_pos0, _dt(q), _p(q), q.stride(1), q.stride(0),
+    qp, rp = positions(B, q_pos0, q.device), positions(B, raw_pos0, q.device)
+    _check(fn(ctypes.byref(dims), B, T, _p(qp), _dt(q), _p(q), q.stride(1), q.stride(0),
               _p(entries), entries.stride(0), entries.shape[1], _p(kv_raw), kv_raw.stride(1),
-              kv_raw.stride(0), raw_pos0, kv_raw.shape[1], _p(sink), _p(out), _dt(out), wp, wn, _stream()))
+              kv_raw.stride(0), _p(rp), kv_raw.shape[1], _p(sink), _p(out), _dt(out), wp, wn, _stream()))
     return out
 
 
@@ -326,9 +359,10 @@ def weights_struct(weights: dict) -> Weights:
                    int(weights.get("rope_dims", 0)), float(weights.get("rope_theta", 10000.0)))
 
 
-def csa_decode_step(dims: Dims, weights: dict, pos: int, q, q_idx, kv, comp, state: dict, out, *, out_idx=None,
+def csa_decode_step(dims: Dims, weights: dict, pos, q, q_idx, kv, comp, state: dict, out, *, out_idx=None,
                     ws=None):
-    """One decode step of B sequences at position pos over a decode state (see include/csa.h):
+    """One decode step of B sequences, sequence b at position pos[b] (an int: all at pos), over a decode
+    state (see include/csa.h):
     q [B, H, D], q_idx [B, H_I, D_I], kv [B, D], comp [B, 4D + 4D_I]; state holds entries (rows, or
     uint8 records [B, n_cap, 584]), keys, win [B, window, D], block [B, 2m, 4D + 4D_I]."""
     _require_cuda(q, q_idx, kv, comp, out, out_idx)
@@ -344,12 +378,13 @@ def csa_decode_step(dims: Dims, weights: dict, pos: int, q, q_idx, kv, comp, sta
         ws = _workspace(need, q.device)
     wp, wn = _aligned_ptr(ws)
     w = weights_struct(weights)
-    _check(load().csa_decode_step(ctypes.byref(dims), ctypes.byref(w), B, pos, _dt(q), _p(q), _p(q_idx), _p(kv),
+    pt = positions(B, pos, q.device, null_if_zero=False)
+    _check(load().csa_decode_step(ctypes.byref(dims), ctypes.byref(w), B, _p(pt), _dt(q), _p(q), _p(q_idx), _p(kv),
                                   _p(comp), ctypes.byref(st), _p(out), _dt(out), _p(out_idx), wp, wn, _stream()))
     return out
 
 
-def csa_hca_decode_step(dims: Dims, weights: dict, pos: int, q, kv, comp, state: dict, out, *, ws=None):
+def csa_hca_decode_step(dims: Dims, weights: dict, pos, q, kv, comp, state: dict, out, *, ws=None):
     """One HCA decode step (see include/csa.h): q [B, H, D], kv [B, D], comp [B, 2D]; state holds entries
     (rows, or uint8 records), win [B, window, D], block [B, m, 2D]; weights: bias_a [m, D] (the pooling
     biases), sink and the QK-norm / RoPE fields."""
@@ -368,7 +403,8 @@ def csa_hca_decode_step(dims: Dims, weights: dict, pos: int, q, kv, comp, state:
     w = Weights(None, _p(weights["bias_a"]), None, None, None, None, _p(weights.get("sink")),
                 _p(weights.get("gamma_q")), _p(weights.get("gamma_kv")), float(weights.get("norm_eps", 0.0)),
                 int(weights.get("rope_dims", 0)), float(weights.get("rope_theta", 10000.0)))
-    _check(load().csa_hca_decode_step(ctypes.byref(dims), ctypes.byref(w), B, pos, _dt(q), _p(q), _p(kv), _p(comp),
+    pt = positions(B, pos, q.device, null_if_zero=False)
+    _check(load().csa_hca_decode_step(ctypes.byref(dims), ctypes.byref(w), B, _p(pt), _dt(q), _p(q), _p(kv), _p(comp),
                                       ctypes.byref(st), _p(out), _dt(out), wp, wn, _stream()))
     return out
 
@@ -391,18 +427,20 @@ class Forward:
         raw = self._ws[off:off + self.B * self.T * n_tot * es]
         return raw.view(torch.float32 if es == 4 else torch.bfloat16).view(self.B * self.T, n_tot)
 
-    def __call__(self, weights: dict, x, cache: dict, out, *, pos0: int, out_idx=None):
+    def __call__(self, weights: dict, x, cache: dict, out, *, pos0, out_idx=None):
+        """pos0: an int (every sequence) or per-sequence positions (see positions())."""
         w = weights_struct(weights)
+        pos = positions(self.B, pos0, x.device)
         c = Cache(_p(cache["entries"]), _p(cache["keys"]), cache["entries"].shape[1], _p(cache["win"]),
                   cache["win"].shape[1], _p(cache.get("halo")), _p(cache.get("halo_out")),
                   1 if cache["entries"].dtype == torch.uint8 else 0)
-        _check(load().csa_forward(ctypes.byref(self.dims), ctypes.byref(w), self.B, self.T, pos0, self.d_model,
+        _check(load().csa_forward(ctypes.byref(self.dims), ctypes.byref(w), self.B, self.T, _p(pos), self.d_model,
                                   self.dtype, _p(x), ctypes.byref(c), _p(out), _dt(out), _p(out_idx), self._wp,
                                   self._wn, _stream()))
         return out
 
 
-def csa_forward(dims: Dims, weights: dict, x, cache: dict, out, *, pos0: int, out_idx=None):
+def csa_forward(dims: Dims, weights: dict, x, cache: dict, out, *, pos0, out_idx=None):
     """The whole layer on x [B, T, d_model]; see include/csa.h for the cache layout."""
     _require_cuda(x, out)
     B, T, d = x.shape

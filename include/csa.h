@@ -23,11 +23,19 @@
  *   - No device memory is allocated by a compute call: scratch comes from the caller's workspace
  *     `ws` of `ws_bytes` bytes (256-byte aligned), sized by csa_workspace_size().
  *   - Results are deterministic: no floating-point atomics, fixed reduction orders, and top-k ties
- *     broken toward the smaller entry index.
- *   - Positions: a batch shares one absolute position for its first query (`q_pos0`); query row t
- *     of every sequence sits at position q_pos0 + t.
- *   - Visibility: entry i (tokens [i*m, (i+1)*m)) is visible to position p iff its block is
- *     complete, (i+1)*m - 1 <= p; so n_vis(p) = min(floor((p+1)/m), n_cap).
+ *     broken toward the smaller entry index. A sequence's results do not depend on the other
+ *     sequences of its batch, nor on the batch size.
+ *   - Positions are per sequence: a DEVICE array `const int64_t*` of B values (8-byte aligned),
+ *     read by the kernels, so the sequences of one batch may sit at different lengths and a decode
+ *     loop can advance them without a host round trip. Query row t of sequence b sits at absolute
+ *     position pos[b] + t. NULL means every sequence is at 0; a negative query position counts as
+ *     0. The host cannot see these values: calls check what they can (pointers, strides, sizes)
+ *     and the kernels clamp every row they derive from a position to the buffers they were given,
+ *     so a position outside an entry point's stated contract gives unspecified results, never an
+ *     access outside the caller's tensors.
+ *   - Visibility ("Anatomy of a Frontier Model", bullet "A sliding window in every layer": an entry
+ *     is formed once its block is complete): entry i (tokens [i*m, (i+1)*m)) is visible to position
+ *     p iff (i+1)*m - 1 <= p, so n_vis(p) = min(floor((p+1)/m), n_cap).
  */
 #ifndef CSA_H
 #define CSA_H
@@ -73,7 +81,9 @@ typedef struct csa_dims {
   float sm_scale;   /* softmax scale; 0 selects 1/sqrt(D)                                       */
 } csa_dims;
 
+/* The ABI revision (2: per-sequence device position arrays). */
 int csa_version(void);
+/* The message of this thread's last failed call ("" after a successful one). */
 const char* csa_last_error(void);
 
 /*
@@ -87,22 +97,30 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
                        int idx_dtype, int64_t* bytes);
 
 /*
- * Step 1 — compressor ("The Exchange Rates of a Million Tokens", section 3; "Anatomy of a
- * Frontier Model", bullet "Compressed Sparse Attention (CSA)").
- * For each complete block of this call (entry i = pos0/m + e, e < floor(T/m)) and channel j:
+ * Step 1 — compressor ("The Exchange Rates of a Million Tokens", section 3: two overlapping
+ * series under one joint softmax; "Anatomy of a Frontier Model", bullet "Compressed Sparse
+ * Attention (CSA)": per-channel softmax pooling with learned position biases over the entry's own
+ * block and the one before).
+ * For each sequence b, complete block of this call (entry i = pos0[b]/m + e, e < floor(T/m)) and
+ * channel j:
  *   logits = { za[i*m+r, j] + bias_a[r, j] }_{r<m}  U  { zb[(i-1)*m+r, j] + bias_b[r, j] }_{r<m}
  *   entries[i, j] = softmax(logits) . [ca[i*m+r, j] ; cb[(i-1)*m+r, j]]
  * Entry 0 pools its own block only. Tokens of an incomplete trailing block produce nothing.
  *   ca, za, cb, zb  [B, T, c] views: token stride `ld`, sequence stride `seq_stride` (elements,
  *                   shared by the four), channel stride 1; dtype `in_dtype` (F32 or BF16).
+ *   pos0            device int64 [B]: the chunk's first position per sequence, a multiple of m
+ *                   with pos0[b]/m + floor(T/m) <= n_cap (rows at or past n_cap are not written).
+ *                   NULL: every sequence starts at 0.
  *   halo_cb/zb      the previous block's cb/zb rows [B, m, c] (stride halo_ld / halo_seq_stride),
- *                   required iff pos0 > 0, ignored (may be NULL) when pos0 == 0.
+ *                   required when pos0 is given (the rows of sequences at 0 are not read); may be
+ *                   NULL when pos0 is NULL.
  *   bias_a/b        [m, c] float32.
  *   entries         [B, n_cap, c] (row stride c, sequence stride entries_seq_stride), dtype
- *                   out_dtype; rows pos0/m .. pos0/m + floor(T/m) - 1 are written.
- * Requires pos0 % m == 0 and pos0/m + floor(T/m) <= n_cap. B == 0 or T < m is a no-op.
+ *                   out_dtype; rows pos0[b]/m .. pos0[b]/m + floor(T/m) - 1 are written.
+ * B == 0 or T < m is a no-op. Errors: CSA_ERR_ARG for bad sizes, strides or dtypes, a NULL tensor,
+ * a missing halo with pos0 given, or (pos0 NULL) floor(T/m) > n_cap.
  */
-int csa_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype,
+int csa_compress(int B, int T, const int64_t* pos0, int m, int c, int in_dtype,
                  const void* ca, const void* za, const void* cb, const void* zb,
                  int64_t ld, int64_t seq_stride,
                  const void* halo_cb, const void* halo_zb, int64_t halo_ld, int64_t halo_seq_stride,
@@ -114,15 +132,17 @@ int csa_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype,
  * HCA compressor ("Anatomy of a Frontier Model", section "The attention: compress, then select",
  * bullet "Heavily Compressed Attention (HCA)": every 128 tokens become one entry, without overlap).
  * The pages name no other pooling; read as the CSA compressor's pooling over the entry's own block:
- * for each complete block of this call (entry i = pos0/m + e, e < floor(T/m)) and channel j,
+ * for each sequence b, complete block of this call (entry i = pos0[b]/m + e, e < floor(T/m)) and
+ * channel j,
  *   entries[i, j] = softmax_r(z[i*m+r, j] + bias[r, j]) . c[i*m+r, j]        (r < m)
  *   c, z      [B, T, c] views: token stride `ld`, sequence stride `seq_stride`, channel stride 1;
  *             dtype in_dtype (F32 or BF16).
+ *   pos0      device int64 [B] (NULL: all 0): multiples of m with pos0[b]/m + floor(T/m) <= n_cap.
  *   bias      [m, c] float32.
  *   entries   [B, n_cap, c] (row stride c, sequence stride entries_seq_stride), dtype out_dtype.
- * Requires 1 <= m <= 128, pos0 % m == 0 and pos0/m + floor(T/m) <= n_cap; no halo is needed.
+ * Requires 1 <= m <= 128; no halo is needed. Errors as csa_compress.
  */
-int csa_hca_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype,
+int csa_hca_compress(int B, int T, const int64_t* pos0, int m, int c, int in_dtype,
                      const void* cv, const void* z, int64_t ld, int64_t seq_stride,
                      const float* bias, void* entries, int64_t entries_seq_stride, int64_t n_cap,
                      int out_dtype, void* stream);
@@ -131,9 +151,10 @@ int csa_hca_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype,
  * Steps 2+3 — lightning indexer fused with top-k ("Anatomy of a Frontier Model", bullet
  * "Compressed Sparse Attention (CSA)": 64 heads x 128 dims, top 1,024 / 512; "The Exchange Rates
  * of a Million Tokens", section 3: ReLU-gated dot products, top-k).
- *   s[t, i] = sum_h w[h] * max(0, q_idx[t, h, :] . keys[i, :])   for i < n_vis(q_pos0 + t)
+ *   s[t, i] = sum_h w[h] * max(0, q_idx[t, h, :] . keys[i, :])   for i < n_vis(q_pos[b] + t)
  *   out_idx[t] = the top_k entries by (s descending, i ascending), stored ascending and padded
  *   with -1 when fewer than top_k are visible.
+ *   q_pos    device int64 [B] (NULL: all 0): row t of sequence b sits at q_pos[b] + t.
  *   q_idx    [B, T, H_I, D_I]: token stride q_ld, sequence stride q_seq_stride, heads D_I apart.
  *            MXFP4: codes [B, T, H_I, D_I/2] bytes and q_scale [B, T, H_I, D_I/32], both
  *            contiguous (q_ld / q_seq_stride must be 0).
@@ -141,10 +162,11 @@ int csa_hca_compress(int B, int T, int64_t pos0, int m, int c, int in_dtype,
  *   keys     [B, n_cap, D_I] (row stride D_I, sequence stride keys_seq_stride); MXFP4: codes
  *            [B, n_cap, D_I/2] contiguous plus k_scale [B, n_cap, D_I/32].
  *   out_idx  [B, T, top_k] int32.  out_score (nullable) [B, T, top_k] the scores of out_idx.
- * The T x n_cap score matrix is not stored for large T (fused streaming selection); for few
- * query rows the scores go through the workspace.
+ * The T x n_cap score matrix is not stored for many query rows (fused streaming selection); for
+ * few query rows (decode) the scores of every visible entry pass through the workspace.
+ * Errors: CSA_ERR_ARG for bad sizes, strides, alignment or a NULL tensor; CSA_ERR_WORKSPACE.
  */
-int csa_index_topk(const csa_dims* dims, int B, int T, int64_t q_pos0, int idx_dtype,
+int csa_index_topk(const csa_dims* dims, int B, int T, const int64_t* q_pos, int idx_dtype,
                    const void* q_idx, int64_t q_ld, int64_t q_seq_stride, const void* q_scale,
                    const float* w, int64_t w_ld,
                    const void* keys, int64_t keys_seq_stride, const void* k_scale, int64_t n_cap,
@@ -152,12 +174,15 @@ int csa_index_topk(const csa_dims* dims, int B, int T, int64_t q_pos0, int idx_d
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Step 3 on its own, on caller-provided float32 scores (the selection routine of
- * csa_index_topk, exposed so that it can be checked bit for bit).
+ * Step 3 on its own ("Anatomy of a Frontier Model", bullet "Compressed Sparse Attention (CSA)":
+ * each query keeps the 1,024 (512) compressed entries the indexer ranks highest), on caller-provided
+ * float32 scores: the selection routine of csa_index_topk, exposed so that it can be checked bit
+ * for bit.
  *   scores   [R, ld] float32; row r's candidates are columns 0 .. n_valid[r]-1 (clamped to ld).
  *   n_valid  device int32 [R].
  *   out_idx  [R, k] int32, ascending, -1 padded; out_score (nullable) [R, k].
  * Order: score descending (-0 == +0), then column ascending. NaN scores are not supported.
+ * Errors: CSA_ERR_ARG for k outside [1, 4096], negative sizes or a NULL tensor; CSA_ERR_WORKSPACE.
  */
 int csa_topk_from_scores(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k,
                          int32_t* out_idx, float* out_score,
@@ -167,25 +192,30 @@ int csa_topk_from_scores(const float* scores, int64_t ld, const int32_t* n_valid
  * Step 4 — sparse single-KV-head attention ("Anatomy of a Frontier Model", sections "The
  * skeleton, and what's kept" and "The attention: compress, then select", bullets "A sliding
  * window in every layer" and "An attention sink").
- * For query row t at p = q_pos0 + t and head h, over the key set
+ * For query row t of sequence b at p = q_pos[b] + t and head h, over the key set
  *   S_t = { entries[idx[t, j]] : idx[t, j] >= 0 }  ++  { raw row of position u : u in
  *         [max(0, p - window + 1), p] }
  *   o[t, h] = sum_{v in S_t} exp(l_v - mu) v / (sum_v exp(l_v - mu) [+ exp(sink[h] - mu)]),
  *   l_v = sm_scale * q[t, h] . v,  mu = the largest logit (and sink[h] when given).
+ *   q_pos    device int64 [B] (NULL: all 0).
  *   q        [B, T, H, D]: token stride q_ld, sequence stride q_seq_stride, heads D apart.
  *   entries  [B, n_cap, D] (row stride D); idx [B, T, top_k] int32 (values outside [0, n_cap)
  *            are skipped).
- *   kv_raw   [B, raw_len, D]: row stride raw_ld, sequence stride raw_seq_stride; row r holds
- *            position raw_pos0 + r and must cover every query's window.
+ *   kv_raw   [B, raw_len, D]: row stride raw_ld, sequence stride raw_seq_stride; row r of sequence
+ *            b holds position raw_pos[b] + r (raw_pos: device int64 [B], NULL: all 0; values may
+ *            be negative). The rows must cover every query's window: window positions outside
+ *            [raw_pos[b], raw_pos[b] + raw_len) are not read and drop out of the key set.
  *   sink     nullable float32 [H].
  *   out      [B, T, H, D] contiguous, out_dtype F32 or BF16.
+ * Errors: CSA_ERR_ARG for bad sizes, strides, alignment or a NULL tensor; CSA_ERR_UNSUPPORTED for
+ * D > 1024; CSA_ERR_WORKSPACE.
  */
-int csa_sparse_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+int csa_sparse_attn(const csa_dims* dims, int B, int T, const int64_t* q_pos, int in_dtype,
                     const void* q, int64_t q_ld, int64_t q_seq_stride,
                     const void* entries, int64_t entries_seq_stride, int64_t n_cap,
                     const int32_t* idx,
-                    const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
-                    int64_t raw_len,
+                    const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+                    const int64_t* raw_pos, int64_t raw_len,
                     const float* sink,
                     void* out, int out_dtype,
                     void* ws, size_t ws_bytes, void* stream);
@@ -198,11 +228,11 @@ int csa_sparse_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_d
  * Arguments as csa_sparse_attn, without idx; dims->m is the HCA block (128) and dims->top_k is not
  * used. Workspace: csa_workspace_size(CSA_OP_DENSE_ATTN, dims, B, T, n_cap, ...).
  */
-int csa_dense_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+int csa_dense_attn(const csa_dims* dims, int B, int T, const int64_t* q_pos, int in_dtype,
                    const void* q, int64_t q_ld, int64_t q_seq_stride,
                    const void* entries, int64_t entries_seq_stride, int64_t n_cap,
-                   const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
-                   int64_t raw_len,
+                   const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+                   const int64_t* raw_pos, int64_t raw_len,
                    const float* sink,
                    void* out, int out_dtype,
                    void* ws, size_t ws_bytes, void* stream);
@@ -212,7 +242,8 @@ int csa_dense_attn(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dt
  * queries and compressed entries are RMS-normalised per head, RoPE turns only the last 64 of the 512
  * dims, and each output is turned back by its own position so that only relative position remains).
  * For B x R rows of H head vectors of D dims (dtype F32 or BF16, x and y alike), row r of sequence
- * b at x + b*x_seq_stride + r*x_ld + h*D (elements), at position pos0 + r*pos_step:
+ * b at x + b*x_seq_stride + r*x_ld + h*D (elements), at position pos0[b] + pos_off + r*pos_step
+ * (pos0: device int64 [B], NULL: all 0; pos_off, pos_step: host values):
  *   gamma != NULL:  v = v / sqrt(mean(v^2) + eps) * gamma          (gamma [D] fp32, device)
  *   rope_dims > 0:  the last rope_dims dims, in adjacent pairs (2i, 2i+1) of that slice, turn by
  *                   the angle pos * rope_theta^(-2i/rope_dims): (a, b) -> (a cos - b sin,
@@ -226,8 +257,8 @@ int csa_norm_rope(int B, int R, int H, int D, int dtype,
                   const void* x, int64_t x_ld, int64_t x_seq_stride,
                   void* y, int64_t y_ld, int64_t y_seq_stride,
                   const float* gamma, float eps,
-                  int rope_dims, float rope_theta, int64_t pos0, int64_t pos_step, int inverse,
-                  void* stream);
+                  int rope_dims, float rope_theta, const int64_t* pos0, int64_t pos_off,
+                  int64_t pos_step, int inverse, void* stream);
 
 /*
  * The pages' compressed-entry record ("Anatomy of a Frontier Model", section "The KV cache,
@@ -253,13 +284,13 @@ int csa_entry_pack(int B, int N, int in_dtype, const void* entries, int64_t ld, 
  * attention sees each entry's stored values exactly (FP8 times its scale, bf16 RoPE dims). The
  * workspace is the one csa_workspace_size gives for CSA_OP_SPARSE_ATTN.
  */
-int csa_sparse_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+int csa_sparse_attn_fp8(const csa_dims* dims, int B, int T, const int64_t* q_pos, int in_dtype,
                         const void* q, int64_t q_ld, int64_t q_seq_stride,
                         const void* records, int64_t records_seq_stride, int64_t n_cap,
                         const int32_t* idx,
-                        const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
-                        int64_t raw_len, const float* sink, void* out, int out_dtype,
-                        void* ws, size_t ws_bytes, void* stream);
+                        const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+                        const int64_t* raw_pos, int64_t raw_len, const float* sink, void* out,
+                        int out_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa_dense_attn over a cache of 584-byte records (the HCA layers keep the same entry format as the
@@ -267,12 +298,12 @@ int csa_sparse_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int 
  * csa_dense_attn with `records` [B, n_cap, 584] bytes in place of the entries (16-byte aligned,
  * sequence stride in bytes, a multiple of 8); D must be 512. Workspace: CSA_OP_DENSE_ATTN.
  */
-int csa_dense_attn_fp8(const csa_dims* dims, int B, int T, int64_t q_pos0, int in_dtype,
+int csa_dense_attn_fp8(const csa_dims* dims, int B, int T, const int64_t* q_pos, int in_dtype,
                        const void* q, int64_t q_ld, int64_t q_seq_stride,
                        const void* records, int64_t records_seq_stride, int64_t n_cap,
-                       const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride, int64_t raw_pos0,
-                       int64_t raw_len, const float* sink, void* out, int out_dtype,
-                       void* ws, size_t ws_bytes, void* stream);
+                       const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+                       const int64_t* raw_pos, int64_t raw_len, const float* sink, void* out,
+                       int out_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* Weights of one CSA layer (device pointers). */
 typedef struct csa_weights {
@@ -289,9 +320,9 @@ typedef struct csa_weights {
   /* QK-norm and partial RoPE ("Anatomy of a Frontier Model", bullet "QK-norm and partial RoPE"),
      off when gamma_q, gamma_kv are NULL and rope_dims is 0. When on, the queries (at their
      positions), the chunk's raw KV (at its token positions) and the new entries (entry i at
-     position (i+1)*m - 1) are RMS-normalised and rotated in place before the attention, and the
-     output is rotated back by the query position (see csa_norm_rope). The caches' context rows are
-     read as stored, i.e. already normalised and rotated. */
+     position (i+1)*m - 1) are RMS-normalised and rotated before the attention, and the output is
+     rotated back by the query position (see csa_norm_rope). The caches' context rows are read as
+     stored, i.e. already normalised and rotated. */
   const float* gamma_q;  /* nullable [D]: norm gain of the query heads (NULL: no query norm)     */
   const float* gamma_kv; /* nullable [D]: norm gain of entries and raw KV (NULL: no such norm)    */
   float norm_eps;        /* eps of both norms                                                     */
@@ -299,60 +330,64 @@ typedef struct csa_weights {
   float rope_theta;      /* RoPE base (10000), > 0 when rope_dims > 0                             */
 } csa_weights;
 
-/* Caches the layer reads and extends (device pointers, all of the activation dtype). */
+/* Caches the layer reads and extends (device pointers, all of the activation dtype). Sequence b's
+   chunk starts at position pos0[b] (see csa_forward). */
 typedef struct csa_cache {
-  void* entries;         /* [B, n_cap, D]: rows < pos0/m are the context; new rows appended     */
+  void* entries;         /* [B, n_cap, D]: rows < pos0[b]/m are the context; new rows appended   */
   void* keys;            /* [B, n_cap, D_I] indexer keys, same row numbering                     */
   int64_t n_cap;
-  void* win;             /* [B, win_cap, D] raw KV: row r = position pos0 - (window-1) + r. Rows
-                            [0, window-1) hold the context's last raw tokens (only those at
-                            positions >= 0 are read); rows [window-1, window-1+T) are written.  */
+  void* win;             /* [B, win_cap, D] raw KV: row r of sequence b = position
+                            pos0[b] - (window-1) + r. Rows [0, window-1) hold the context's last raw
+                            tokens (only those at positions >= 0 are read); rows
+                            [window-1, window-1+T) are written.                                   */
   int64_t win_cap;
-  const void* halo;      /* [B, m, 2D + 2D_I] cb | zb | icb | izb of block pos0/m - 1; NULL iff
-                            pos0 == 0                                                            */
+  const void* halo;      /* [B, m, 2D + 2D_I] cb | zb | icb | izb of block pos0[b]/m - 1; required
+                            when pos0 is given (rows of sequences at 0 are not read), may be NULL
+                            when pos0 is NULL                                                     */
   void* halo_out;        /* nullable [B, m, 2D + 2D_I]: receives this chunk's last block (needs
                             T % m == 0), i.e. the next chunk's halo                               */
   int32_t entry_fmt;     /* 0: entries are rows of the activation dtype; 1: 584-byte FP8 records
-                            [B, n_cap, 584] (see csa_entry_pack; D = 512): new entries are packed
-                            and the attention reads the records                                   */
+                            [B, n_cap, 584] (see csa_entry_pack; D = 512, bf16 layer): new entries
+                            are packed and the attention reads the records                        */
 } csa_cache;
 
 /* Decode state of B sequences (device pointers, activation dtype unless stated). */
 typedef struct csa_decode_state {
   void* entries;         /* [B, n_cap, D] rows, or [B, n_cap, 584] FP8 records when entry_fmt = 1  */
   int32_t entry_fmt;     /* 0: rows of the activation dtype, 1: FP8 records (see csa_entry_pack)    */
-  void* keys;            /* [B, n_cap, D_I] indexer keys                                             */
+  void* keys;            /* [B, n_cap, D_I] indexer keys (CSA only)                                  */
   int64_t n_cap;
   void* win;             /* [B, window, D] ring of raw KV: position p in row p % window              */
-  void* block;           /* [B, 2m, 4D + 4D_I] compressor inputs ca|za|cb|zb (D each) and the
-                            indexer's ica|iza|icb|izb (D_I each) of the previous complete block (rows
-                            0..m-1) and of the current block (rows m..2m-1, filled as tokens come)    */
+  void* block;           /* CSA: [B, 2m, 4D + 4D_I] compressor inputs ca|za|cb|zb (D each) and the
+                            indexer's ica|iza|icb|izb (D_I each); token r of block i sits in row
+                            (i % 2)*m + r, so the previous block's rows stay in the other half.
+                            HCA: [B, m, 2D], c | z of the current block's tokens (row p % m).       */
 } csa_decode_state;
 
 /*
- * One decode step of B sequences, all at position pos (the layer of "Anatomy of a Frontier Model",
- * "The attention: compress, then select", run token by token): the new token's compressor inputs
- * go to row m + pos % m of state->block and its raw KV to window row pos % window; when the token
- * completes its block ((pos+1) % m == 0) entry i = (pos+1)/m - 1 and its indexer key are compressed
- * from the block and the previous one (the CSA pooling over both) and stored (with QK-norm and
- * RoPE at position (i+1)m - 1 when the weights carry them; packed into a record when entry_fmt = 1),
- * and the block becomes the previous one. Then the query (normalised and rotated at pos when the
- * weights carry the options) is indexed against the floor((pos+1)/m) visible entries, the top-k
- * are selected, and the attention runs over them plus the window [max(0, pos-window+1), pos]; the
- * output is rotated back by pos when RoPE is on.
+ * One decode step of B sequences, sequence b at its own position pos[b] (the layer of "Anatomy of a
+ * Frontier Model", "The attention: compress, then select", run token by token). One launch appends
+ * every sequence's token: its compressor inputs go to block row ((pos/m) % 2)*m + pos % m and its
+ * raw KV (normalised and rotated at pos when the weights carry QK-norm / RoPE) to window row
+ * pos % window; when the token completes its block ((pos+1) % m == 0) entry i = (pos+1)/m - 1 and
+ * its indexer key are pooled from the block and the previous one (the CSA pooling over both),
+ * normalised and rotated at pos when on, and stored (packed into a record when entry_fmt = 1).
+ * Then the query (normalised and rotated at pos when on) is indexed against the floor((pos+1)/m)
+ * visible entries, the top-k are selected, and the attention runs over them plus the window
+ * [max(0, pos-window+1), pos]; the output is rotated back by pos when RoPE is on.
+ *   pos    device int64 [B] (required): pos[b] >= 0 with (pos[b]+1)/m <= n_cap.
  *   q      [B, H, D], q_idx [B, H_I, D_I], kv [B, D], comp [B, 4D + 4D_I] (columns as in block),
  *          each sequence contiguous (sequence strides H*D, H_I*D_I, D, 4D + 4D_I).
  *   w      the layer weights: bias_a/bias_b, ibias_a/ibias_b, w_head, sink, the QK-norm / RoPE
  *          fields (w_proj is not used: the step takes projected rows).
  *   out    [B, H, D] (out_dtype); out_idx nullable [B, top_k].
- * Before the first step the caller fills the state's context: the entries and keys of the
+ * Before a sequence's first step the caller fills its state's context: the entries and keys of the
  * floor(pos/m) complete blocks before pos, the window rows of positions pos-window+1 .. pos-1, and
  * the block rows of the previous block and of the current block's tokens before pos; the calls then
- * go pos, pos+1, ... Workspace: csa_workspace_size(
- * CSA_OP_DECODE_STEP, dims, B, 1, n_cap, 0, dtype). Errors: CSA_ERR_ARG for bad sizes, pointers,
- * pos outside [0, n_cap*m), an MXFP4 or mismatched dtype.
+ * go pos, pos+1, ... Workspace: csa_workspace_size(CSA_OP_DECODE_STEP, dims, B, 1, n_cap, 0, dtype).
+ * Errors: CSA_ERR_ARG for bad sizes, pointers, a NULL pos, records with D != 512 or fp32 entries.
  */
-int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t pos, int dtype,
+int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, const int64_t* pos, int dtype,
                     const void* q, const void* q_idx, const void* kv, const void* comp,
                     const csa_decode_state* state, void* out, int out_dtype, int32_t* out_idx,
                     void* ws, size_t ws_bytes, void* stream);
@@ -360,30 +395,39 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t p
 /*
  * One decode step of an HCA layer ("Anatomy of a Frontier Model", bullet "Heavily Compressed
  * Attention (HCA)": blocks of m = 128 tokens pooled without overlap, attention over every visible
- * entry plus the window), all B sequences at position pos, over a decode state whose `block` is
- * [B, m, 2D]: the c | z compressor inputs of the current block's tokens (keys unused). The token's
- * c|z row goes to block row pos % m and its raw KV to window row pos % window; when it completes
- * the block, entry (pos+1)/m - 1 is pooled from the block's rows with weights bias_a [m, D]
- * (normalised and rotated at pos, packed into a record when entry_fmt = 1). Then the query
- * (normalised and rotated at pos when on) attends to the floor((pos+1)/m) entries and the window;
- * the output is rotated back by pos when RoPE is on.
- *   q [B, H, D], kv [B, D], comp [B, 2D]; out [B, H, D] (out_dtype).
+ * entry plus the window), sequence b at pos[b], over a decode state whose `block` is [B, m, 2D]:
+ * the c | z compressor inputs of the current block's tokens (keys unused). The token's c|z row goes
+ * to block row pos % m and its raw KV to window row pos % window; when it completes the block,
+ * entry (pos+1)/m - 1 is pooled from the block's rows with weights bias_a [m, D] (normalised and
+ * rotated at pos, packed into a record when entry_fmt = 1). Then the query (normalised and rotated
+ * at pos when on) attends to the floor((pos+1)/m) entries and the window; the output is rotated
+ * back by pos when RoPE is on.
+ *   pos [B] device int64 (required); q [B, H, D], kv [B, D], comp [B, 2D]; out [B, H, D].
  * Workspace: csa_workspace_size(CSA_OP_HCA_DECODE_STEP, dims, B, 1, n_cap, 0, dtype). dims->top_k
  * and the indexer sizes are not used. Errors as csa_decode_step.
  */
-int csa_hca_decode_step(const csa_dims* dims, const csa_weights* w, int B, int64_t pos, int dtype,
-                        const void* q, const void* kv, const void* comp, const csa_decode_state* state,
-                        void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream);
+int csa_hca_decode_step(const csa_dims* dims, const csa_weights* w, int B, const int64_t* pos,
+                        int dtype, const void* q, const void* kv, const void* comp,
+                        const csa_decode_state* state, void* out, int out_dtype, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /*
- * The whole layer for a chunk of T tokens per sequence at positions pos0 .. pos0+T-1:
- * projection (x @ w_proj^T), both compressors, indexer + top-k, sparse attention.
+ * The whole layer ("Anatomy of a Frontier Model", section "The attention: compress, then select":
+ * compress, then select, then attend; "The Exchange Rates of a Million Tokens", section 3) for a
+ * chunk of T tokens per sequence, sequence b at positions pos0[b] .. pos0[b]+T-1: projection
+ * (x @ w_proj^T), both compressors (entries and indexer keys, appended at rows pos0[b]/m ..),
+ * indexer + top-k, sparse attention over the selected entries and the window.
+ *   pos0     device int64 [B] (NULL: every sequence starts at 0): multiples of m with
+ *            (pos0[b] + T)/m <= n_cap.
  *   x        [B, T, d_model] contiguous, dtype F32 or BF16 (also the cache/projection dtype).
+ *   cache    see csa_cache; window - 1 + T <= win_cap.
  *   out      [B, T, H, D] contiguous, out_dtype F32 or BF16.
  *   out_idx  nullable [B, T, top_k]: receives the selected entries.
- * Requires pos0 % m == 0 and (pos0 + T)/m <= n_cap, window - 1 + T <= win_cap.
+ * Errors: CSA_ERR_ARG for bad sizes, pointers, a missing halo with pos0 given; CSA_ERR_UNSUPPORTED
+ * for QK-norm / RoPE or records where one entry's channel vectors do not fit one wave
+ * (D / 8 > 64 in bf16); CSA_ERR_WORKSPACE.
  */
-int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, int64_t pos0,
+int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, const int64_t* pos0,
                 int d_model, int dtype, const void* x, const csa_cache* cache,
                 void* out, int out_dtype, int32_t* out_idx,
                 void* ws, size_t ws_bytes, void* stream);

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(lib.EXPORTS) == set(_declared())
-    assert lib.csa_version() == 1
+    assert lib.csa_version() == 2
 
 
 def _d(**kw):
@@ -59,24 +59,25 @@ def _err(rc):
 def test_compress_rejects_bad_arguments():
     L = lib.load()
     p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
-    # pos0 not a multiple of m
-    rc, msg = _err(L.csa_compress(1, 8, 2, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p,
-                                  64, 8, lib.CSA_BF16, None))
-    assert rc == -1 and "multiple of m" in msg
-    # pos0 > 0 without the previous block
-    rc, msg = _err(L.csa_compress(1, 8, 4, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p,
+    pos = ctypes.c_void_p(4096)  # a device position array (8-byte aligned)
+    # per-sequence positions without the previous block
+    rc, msg = _err(L.csa_compress(1, 8, pos, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p,
                                   64, 8, lib.CSA_BF16, None))
     assert rc == -1 and "halo" in msg
-    # entries beyond capacity
-    rc, msg = _err(L.csa_compress(1, 64, 0, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 1024, None, None, 0, 0, p, p, p,
+    # a misaligned position array
+    rc, msg = _err(L.csa_compress(1, 8, ctypes.c_void_p(4100), 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, p, p, 16,
+                                  64, p, p, p, 64, 8, lib.CSA_BF16, None))
+    assert rc == -1 and "aligned" in msg
+    # entries beyond capacity (every sequence at 0)
+    rc, msg = _err(L.csa_compress(1, 64, None, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 1024, None, None, 0, 0, p, p, p,
                                   64, 8, lib.CSA_BF16, None))
     assert rc == -1 and "n_cap" in msg
     # bad dtype
-    rc, _ = _err(L.csa_compress(1, 8, 0, 4, 16, 7, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p, 64, 8,
+    rc, _ = _err(L.csa_compress(1, 8, None, 4, 16, 7, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p, 64, 8,
                                 lib.CSA_BF16, None))
     assert rc == -1
     # nothing to do is fine
-    assert L.csa_compress(1, 3, 0, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p, 64, 8,
+    assert L.csa_compress(1, 3, None, 4, 16, lib.CSA_BF16, p, p, p, p, 16, 128, None, None, 0, 0, p, p, p, 64, 8,
                           lib.CSA_BF16, None) == 0
 
 
@@ -84,30 +85,38 @@ def test_index_topk_rejects_bad_arguments():
     L = lib.load()
     p = ctypes.c_void_p(256)
     d = _d()
-    rc, msg = _err(L.csa_index_topk(ctypes.byref(_d(top_k=0)), 1, 8, 0, lib.CSA_BF16, p, 8192, 65536, None, p, 0,
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(_d(top_k=0)), 1, 8, None, lib.CSA_BF16, p, 8192, 65536, None, p, 0,
                                     p, 262144, None, 2048, p, None, None, 0, None))
     assert rc == -1 and "top_k" in msg
-    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, 0, lib.CSA_MXFP4, p, 0, 0, None, p, 0, p, 0, None,
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, None, lib.CSA_MXFP4, p, 0, 0, None, p, 0, p, 0, None,
                                     2048, p, None, None, 0, None))
     assert rc == -1 and "scale" in msg
-    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, 0, lib.CSA_BF16, p, 100, 800, None, p, 0, p, 262144,
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, None, lib.CSA_BF16, p, 100, 800, None, p, 0, p, 262144,
                                     None, 2048, p, None, None, 0, None))
     assert rc == -1 and "q_ld" in msg
     # decode shape needs a workspace
-    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 64, 1, 131072, lib.CSA_BF16, ctypes.c_void_p(4096), 8192,
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 64, 1, ctypes.c_void_p(4096), lib.CSA_BF16, ctypes.c_void_p(4096), 8192,
                                     8192, None, p, 0, ctypes.c_void_p(4096), 32768 * 128, None, 32768, p, None,
                                     None, 0, None))
     assert rc == -3 and "workspace" in msg
 
 
-def test_sparse_attn_checks_window_coverage():
+def test_sparse_attn_rejects_bad_arguments():
     L = lib.load()
     p = ctypes.c_void_p(4096)
     d = _d()
-    # raw rows start after the first query's window start
-    rc, msg = _err(L.csa_sparse_attn(ctypes.byref(d), 1, 16, 1000, lib.CSA_BF16, p, 32768, 0, p, 0, 256, p, p, 512,
-                                     0, 900, 200, None, p, lib.CSA_F32, None, 0, None))
-    assert rc == -1 and "cover" in msg
+    # no raw row at all (the window always holds the query's own token)
+    rc, msg = _err(L.csa_sparse_attn(ctypes.byref(d), 1, 16, p, lib.CSA_BF16, p, 32768, 0, p, 0, 256, p, p, 512,
+                                     0, p, 0, None, p, lib.CSA_F32, None, 0, None))
+    assert rc == -1 and "row" in msg
+    # misaligned position arrays
+    rc, msg = _err(L.csa_sparse_attn(ctypes.byref(d), 1, 16, ctypes.c_void_p(4100), lib.CSA_BF16, p, 32768, 0, p, 0,
+                                     256, p, p, 512, 0, p, 200, None, p, lib.CSA_F32, None, 0, None))
+    assert rc == -1 and "aligned" in msg
+    # q rows shorter than H*D
+    rc, msg = _err(L.csa_sparse_attn(ctypes.byref(d), 1, 16, p, lib.CSA_BF16, p, 100, 0, p, 0, 256, p, p, 512,
+                                     0, p, 200, None, p, lib.CSA_F32, None, 0, None))
+    assert rc == -1 and "q_ld" in msg
 
 
 def test_topk_from_scores_rejects_bad_k():
@@ -120,30 +129,44 @@ def test_topk_from_scores_rejects_bad_k():
     assert L.csa_topk_from_scores(p, 100, p, 0, 4, p, None, None, 0, None) == 0
 
 
-def test_forward_rejects_capacity_overflow():
+def test_forward_rejects_bad_arguments():
     L = lib.load()
     p = ctypes.c_void_p(4096)
     d = _d()
     w = lib.Weights(4096, 4096, 4096, 4096, 4096, 4096, None)
-    c = lib.Cache(4096, 4096, 100, 4096, 1000, None, None)
-    rc, msg = _err(L.csa_forward(ctypes.byref(d), ctypes.byref(w), 1, 8192, 0, 4096, lib.CSA_BF16, p, ctypes.byref(c),
-                                 p, lib.CSA_F32, None, None, 0, None))
+    # every sequence at 0 and more blocks than entry slots
+    c = lib.Cache(4096, 4096, 100, 4096, 9000, None, None)
+    rc, msg = _err(L.csa_forward(ctypes.byref(d), ctypes.byref(w), 1, 8192, None, 4096, lib.CSA_BF16, p,
+                                 ctypes.byref(c), p, lib.CSA_F32, None, None, 0, None))
     assert rc == -1 and "n_cap" in msg
+    # per-sequence positions without the previous block
+    c = lib.Cache(4096, 4096, 4000, 4096, 9000, None, None)
+    rc, msg = _err(L.csa_forward(ctypes.byref(d), ctypes.byref(w), 1, 8192, p, 4096, lib.CSA_BF16, p,
+                                 ctypes.byref(c), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "halo" in msg
+    # the window rows do not fit
+    c = lib.Cache(4096, 4096, 4000, 4096, 1000, None, None)
+    rc, msg = _err(L.csa_forward(ctypes.byref(d), ctypes.byref(w), 1, 8192, None, 4096, lib.CSA_BF16, p,
+                                 ctypes.byref(c), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "win_cap" in msg
 
 
 def test_norm_rope_entry_pack_and_fp8_attention_reject_bad_arguments():
     L = lib.load()
     p = ctypes.c_void_p(4096)
     # odd rope_dims, rope_dims beyond D, a norm on the inverse rotation, D beyond the kernel's limit
-    for args in ((1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, None, 0.0, 3, 10000.0, 0, 1, 0, None),
-                 (1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, None, 0.0, 10, 10000.0, 0, 1, 0, None),
-                 (1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, p, 0.0, 4, 10000.0, 0, 1, 1, None),
-                 (1, 2, 1, 8192, lib.CSA_F32, p, 8192, 16384, p, 8192, 16384, None, 0.0, 0, 10000.0, 0, 1, 0, None),
-                 (1, 2, 3, 8, lib.CSA_F32, p, 8, 48, p, 24, 48, None, 0.0, 4, 10000.0, 0, 1, 0, None)):
+    for args in ((1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, None, 0.0, 3, 10000.0, None, 0, 1, 0, None),
+                 (1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, None, 0.0, 10, 10000.0, None, 0, 1, 0, None),
+                 (1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, p, 0.0, 4, 10000.0, None, 0, 1, 1, None),
+                 (1, 2, 1, 8192, lib.CSA_F32, p, 8192, 16384, p, 8192, 16384, None, 0.0, 0, 10000.0, None, 0, 1, 0,
+                  None),
+                 (1, 2, 3, 8, lib.CSA_F32, p, 8, 48, p, 24, 48, None, 0.0, 4, 10000.0, None, 0, 1, 0, None),
+                 (1, 2, 3, 8, lib.CSA_F32, p, 24, 48, p, 24, 48, None, 0.0, 4, 10000.0, ctypes.c_void_p(4100), 0, 1, 0,
+                  None)):
         rc, _ = _err(L.csa_norm_rope(*args))
         assert rc == -1, args
-    assert L.csa_norm_rope(0, 2, 3, 8, lib.CSA_F32, None, 24, 48, None, 24, 48, None, 0.0, 4, 10000.0, 0, 1, 0,
-                           None) == 0
+    assert L.csa_norm_rope(0, 2, 3, 8, lib.CSA_F32, None, 24, 48, None, 24, 48, None, 0.0, 4, 10000.0, None, 0, 1,
+                           0, None) == 0
     # records: misaligned, short sequence stride, bad dtype
     rc, msg = _err(L.csa_entry_pack(2, 4, lib.CSA_BF16, p, 512, 2048, ctypes.c_void_p(4100), 4 * 584, None))
     assert rc == -1 and "align" in msg
@@ -153,8 +176,8 @@ def test_norm_rope_entry_pack_and_fp8_attention_reject_bad_arguments():
     assert rc == -1
     # attention over records needs D = 512 and a byte stride of whole records
     d = _d(D=256)
-    rc, msg = _err(L.csa_sparse_attn_fp8(ctypes.byref(d), 1, 1, 1000, lib.CSA_BF16, p, 64 * 256, 0, p, 0, 256, p,
-                                         p, 256, 0, 873, 128, None, p, lib.CSA_F32, None, 0, None))
+    rc, msg = _err(L.csa_sparse_attn_fp8(ctypes.byref(d), 1, 1, p, lib.CSA_BF16, p, 64 * 256, 0, p, 0, 256, p,
+                                         p, 256, 0, p, 128, None, p, lib.CSA_F32, None, 0, None))
     assert rc == -1 and "512" in msg
 
 
@@ -164,22 +187,22 @@ def test_decode_step_rejects_bad_arguments():
     d = _d(H=128, top_k=1024)
     w = lib.Weights(None, 4096, 4096, 4096, 4096, 4096, None, None, None, 0.0, 0, 10000.0)
     st = lib.DecodeState(4096, 0, 4096, 100, 4096, 4096)
-    # position beyond the entry capacity (100 entries of 4 tokens)
-    rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, 404, lib.CSA_BF16, p, p, p, p,
+    # the positions are required (each sequence decodes at its own)
+    rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, None, lib.CSA_BF16, p, p, p, p,
                                      ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
-    assert rc == -1 and "capacity" in msg
+    assert rc == -1 and "pos" in msg
     # MXFP4 is not an activation dtype
-    rc, _ = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, 10, lib.CSA_MXFP4, p, p, p, p,
+    rc, _ = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, p, lib.CSA_MXFP4, p, p, p, p,
                                    ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
     assert rc == -1
     # records need D = 512
     st2 = lib.DecodeState(4096, 1, 4096, 100, 4096, 4096)
     d2 = _d(D=256, H=128, top_k=1024)
-    rc, msg = _err(L.csa_decode_step(ctypes.byref(d2), ctypes.byref(w), 2, 10, lib.CSA_BF16, p, p, p, p,
+    rc, msg = _err(L.csa_decode_step(ctypes.byref(d2), ctypes.byref(w), 2, p, lib.CSA_BF16, p, p, p, p,
                                      ctypes.byref(st2), p, lib.CSA_F32, None, None, 0, None))
     assert rc == -1 and "512" in msg
     # no workspace
-    rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, 10, lib.CSA_BF16, p, p, p, p,
+    rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(w), 2, p, lib.CSA_BF16, p, p, p, p,
                                      ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
     assert rc == -3 and "workspace" in msg
     assert lib.csa_workspace_size(lib.CSA_OP_DECODE_STEP, d, 2, 1, 100, 0, lib.CSA_BF16) > 0

@@ -55,7 +55,7 @@ def test_decode_steps_equal_prefill_rows(variant):
     st.keys[:, :n0] = _bf(np.stack([r["keys"][:n0] for r in refs]))
     for p in range(L0 - W + 1, L0):
         st.win[:, p % W] = _bf(np.stack([r["raw"][p] for r in refs]))
-    st.block[:, :m] = _bf(np.stack([c[L0 - m:L0] for c in comp]))
+    st.block[:, st.block_rows(L0 // m - 1)] = _bf(np.stack([c[L0 - m:L0] for c in comp]))   # the previous block
     # the projected query and raw KV rows (before any norm: the step applies it), computed as the
     # oracle computes its projections
     pc = O.projection_columns(wl.D, wl.D_I, wl.H, wl.H_I)[0]
