@@ -155,6 +155,10 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
         }
       }
     }
+    if (bf) {  // stored values: what the record is packed from
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[v] = bf2f(f2bf(out[v]));
+    }
     if (a.records) {
       if constexpr (V == 8) {
         pack_record_wave(out, static_cast<uint8_t*>(a.entries) + (int64_t)b * a.entries_seq_stride +
