@@ -83,6 +83,34 @@ hipError_t allow_lds(const void* kernel, int bytes) {
   return e;
 }
 
+// The scratch of csa_decode_step_noalloc: one array per GPU the library runs on, held until the
+// process ends. Host code never uses the name itself (on the host it is a stand-in, not a device
+// address): its device address is looked up once per device and kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[CSA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of this device's scratch array (the current device); nullptr and an error on failure.
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace csa
 
 using namespace csa;
@@ -703,6 +731,27 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, const int
   }
   g_err.clear();
   return CSA_OK;
+}
+
+int csa_decode_step_noalloc(const csa_dims* dims, const csa_weights* w, int B, const int64_t* pos, int dtype,
+                            const void* q, const void* q_idx, const void* kv, const void* comp,
+                            const csa_decode_state* st, void* out, int out_dtype, int32_t* out_idx, void* stream) {
+  // every host-side check of csa_decode_step first, then the size of what the step needs
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  rc = check_decode_state(dims, w, B, pos, dtype, out_dtype, st, false);
+  if (rc || B == 0) return rc;
+  if (!q || !q_idx || !kv || !comp || !out) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  const size_t need = decode_ws(dims, B, st->n_cap, dtype).total;
+  if (need > (size_t)CSA_STATIC_SCRATCH_BYTES)
+    return fail(CSA_ERR_WORKSPACE, "csa_decode_step_noalloc: the step needs %zu bytes of scratch, above the %zu "
+                "bytes the library holds per GPU (use csa_decode_step with a workspace)", need,
+                (size_t)CSA_STATIC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  hipError_t e = static_scratch(&ptr);
+  if (e != hipSuccess) return hip_status(e, "csa_decode_step_noalloc: scratch address");
+  return csa_decode_step(dims, w, B, pos, dtype, q, q_idx, kv, comp, st, out, out_dtype, out_idx, ptr,
+                         (size_t)CSA_STATIC_SCRATCH_BYTES, stream);
 }
 
 int csa_hca_decode_step(const csa_dims* dims, const csa_weights* w, int B, const int64_t* pos, int dtype,

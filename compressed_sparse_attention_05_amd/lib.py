@@ -22,7 +22,8 @@ CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN,
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
            "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8",
-           "csa_hca_decode_step")
+           "csa_hca_decode_step", "csa_decode_step_noalloc")
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class CsaError(RuntimeError):
@@ -91,9 +92,12 @@ def load() -> ctypes.CDLL:
     lib.csa_dense_attn_fp8.argtypes = lib.csa_dense_attn.argtypes
     lib.csa_hca_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, vp, i32, vp, vp, vp,
                                         ctypes.POINTER(DecodeState), vp, i32, vp, sz, vp]
+    lib.csa_decode_step_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, vp, i32, vp, vp, vp,
+                                            vp, ctypes.POINTER(DecodeState), vp, i32, vp, vp]
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
-              "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8", "csa_hca_decode_step"):
+              "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8", "csa_hca_decode_step",
+              "csa_decode_step_noalloc"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -381,6 +385,27 @@ def csa_decode_step(dims: Dims, weights: dict, pos, q, q_idx, kv, comp, state: d
     pt = positions(B, pos, q.device, null_if_zero=False)
     _check(load().csa_decode_step(ctypes.byref(dims), ctypes.byref(w), B, _p(pt), _dt(q), _p(q), _p(q_idx), _p(kv),
                                   _p(comp), ctypes.byref(st), _p(out), _dt(out), _p(out_idx), wp, wn, _stream()))
+    return out
+
+
+def csa_decode_step_noalloc(dims: Dims, weights: dict, pos, q, q_idx, kv, comp, state: dict, out, *, out_idx=None):
+    """csa_decode_step with the scratch the library holds on the GPU (no workspace; see include/csa.h).
+    pos must be a device int64 [B] tensor: building one here would allocate."""
+    _require_cuda(q, q_idx, kv, comp, out, out_idx)
+    for t in (q, q_idx, kv, comp, out):
+        if not t.is_contiguous():
+            raise ValueError("decode step tensors must be contiguous")
+    if not isinstance(pos, torch.Tensor):
+        raise TypeError("pos must be a device int64 [B] tensor")
+    B = q.shape[0]
+    pt = positions(B, pos, q.device)
+    ent = state["entries"]
+    st = DecodeState(_p(ent), 1 if ent.dtype == torch.uint8 else 0, _p(state["keys"]), ent.shape[1],
+                     _p(state["win"]), _p(state["block"]))
+    w = weights_struct(weights)
+    _check(load().csa_decode_step_noalloc(ctypes.byref(dims), ctypes.byref(w), B, _p(pt), _dt(q), _p(q), _p(q_idx),
+                                          _p(kv), _p(comp), ctypes.byref(st), _p(out), _dt(out), _p(out_idx),
+                                          _stream()))
     return out
 
 

@@ -393,6 +393,24 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, const int
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_decode_step for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Arguments and results are those of
+ * csa_decode_step, without the workspace: the step's scratch is an array of
+ * CSA_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on (from the first call on
+ * that device until the process ends). The call allocates nothing. Every call on a GPU shares that
+ * GPU's array, so calls that overlap on one GPU (other streams, other threads) race; calls in order
+ * on one stream are safe (each step writes before it reads whatever of the scratch it uses).
+ * Errors: those of csa_decode_step; CSA_ERR_WORKSPACE when the step needs more scratch than
+ * CSA_STATIC_SCRATCH_BYTES (csa_workspace_size(CSA_OP_DECODE_STEP, ...) gives the need);
+ * CSA_ERR_HIP when the array's device address cannot be taken.
+ */
+#define CSA_STATIC_SCRATCH_BYTES (64u << 20)
+int csa_decode_step_noalloc(const csa_dims* dims, const csa_weights* w, int B, const int64_t* pos,
+                            int dtype, const void* q, const void* q_idx, const void* kv,
+                            const void* comp, const csa_decode_state* state, void* out, int out_dtype,
+                            int32_t* out_idx, void* stream);
+
+/*
  * One decode step of an HCA layer ("Anatomy of a Frontier Model", bullet "Heavily Compressed
  * Attention (HCA)": blocks of m = 128 tokens pooled without overlap, attention over every visible
  * entry plus the window), sequence b at pos[b], over a decode state whose `block` is [B, m, 2D]:

@@ -206,3 +206,20 @@ def test_decode_step_rejects_bad_arguments():
                                      ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
     assert rc == -3 and "workspace" in msg
     assert lib.csa_workspace_size(lib.CSA_OP_DECODE_STEP, d, 2, 1, 100, 0, lib.CSA_BF16) > 0
+
+
+def test_decode_step_noalloc_rejects_a_step_beyond_its_scratch():
+    # checked on the host before any HIP call: 64 sequences over 2M entry slots need more scratch than
+    # the library holds (their scores alone are 512 MiB)
+    L = lib.load()
+    p = ctypes.c_void_p(4096)
+    d = _d(H=128, top_k=1024)
+    w = lib.Weights(None, 4096, 4096, 4096, 4096, 4096, None, None, None, 0.0, 0, 10000.0)
+    st = lib.DecodeState(4096, 0, 4096, 1 << 21, 4096, 4096)
+    need = lib.csa_workspace_size(lib.CSA_OP_DECODE_STEP, d, 64, 1, 1 << 21, 0, lib.CSA_BF16)
+    assert need > lib.STATIC_SCRATCH_BYTES
+    rc, msg = _err(L.csa_decode_step_noalloc(ctypes.byref(d), ctypes.byref(w), 64, p, lib.CSA_BF16, p, p, p, p,
+                                             ctypes.byref(st), p, lib.CSA_F32, None, None))
+    assert rc == -3 and "scratch" in msg
+    # the decode128k batch fits
+    assert lib.csa_workspace_size(lib.CSA_OP_DECODE_STEP, d, 64, 1, 32768, 0, lib.CSA_BF16) <= lib.STATIC_SCRATCH_BYTES
