@@ -42,7 +42,6 @@ int esize(int dt) { return dt == CSA_F32 ? 4 : 2; }
 
 bool is_act_dtype(int dt) { return dt == CSA_F32 || dt == CSA_BF16; }
 
-constexpr int kMaxTopK = 4096;
 
 __global__ void copy_rows_kernel(int rows, int cols, int esz, const uint8_t* src, int64_t src_ld, int64_t src_seq,
                                  uint8_t* dst, int64_t dst_ld, int64_t dst_seq) {

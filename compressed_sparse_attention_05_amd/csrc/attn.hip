@@ -1073,7 +1073,9 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStr
 // Waves per workgroup (16 heads each): a query row's 128 heads share one attn_pairs workgroup (8
 // waves, each key row loaded once); 64-head layers use attn_mfma. The choice depends on the layer's
 // shape only, never on the batch or the number of rows: the two kernels round differently, and a
-// sequence's output must not depend on what else is in the batch.
+// sequence's output must not depend on what else is in the batch. (Dealing a row's 128 heads to
+// more workgroups of fewer wave pairs for small-batch decode was measured slower: one pair per
+// compute unit leaves two of its four SIMDs idle and nothing hides a pair's own latency chain.)
 int attn_waves(const AttnArgs& a) { return a.H == 128 ? 8 : 4; }
 
 template <int NW, int OT, int FMT>

@@ -20,7 +20,6 @@
 //  * index_generic (any dims, fp32 / bf16 / MXFP4): one wave per query row, scalar FMA scores,
 //    same streaming selection.
 #include "kernels.h"
-#include "select_radix.h"
 #include "topk_wave.h"
 
 namespace csa {
@@ -318,7 +317,22 @@ __device__ __forceinline__ void load_keys16(uint4 (&kb)[16], const uint16_t* kse
 
 // ---------------------------------------------------------------- decode scores, streamed
 
-// scores[row, i] for i < n_vis(row); n_valid[row] = n_vis(row).
+// Decode writes scores[row, i] for i < n_vis(row), n_valid[row] = n_vis(row), and the maxima of every
+// g0 consecutive scores (gmax[row, i / g0]) that the selection's lower bound starts from. A row's
+// visible count is formed where its q_I is loaded.
+// score of entry base + lane (valid: i < nv) to the row and its g0-group maximum (-inf for lanes past nv)
+__device__ __forceinline__ void store_scores(float* scores, float* gmax, int64_t row, int64_t n_cap, int64_t gstride,
+                                             int g0, int64_t base, int64_t nv, float mine) {
+  const int lane = lane_id();
+  const int64_t i = base + lane;
+  const bool valid = i < nv;
+  if (valid) scores[row * n_cap + i] = mine;
+  if (g0 == 0) return;  // short rows: the selection needs no group maxima
+  float v = valid ? mine : -INFINITY;
+  for (int o = 1; o < g0; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((lane & (g0 - 1)) == 0 && valid) gmax[row * gstride + i / g0] = v;
+}
+
 // The (row, 512-entry unit) space is walked grid-stride by workgroups of 8 waves, so at every step
 // the whole chip reads adjacent 128 KiB units of the key arrays. The unit's row has its q_I staged
 // in LDS once (A-fragments are read from there), which keeps a wave at ~128 VGPRs and four waves
@@ -330,33 +344,37 @@ constexpr int kStreamWaves = 8;
 constexpr int kUnit = kStreamWaves * 64;
 constexpr int kQLd = 136;  // LDS row stride (bf16) of the staged q_I heads
 
-__global__ void __launch_bounds__(kStreamWaves * 64) score_bf16_stream(IndexArgs a, float* scores, int32_t* n_valid,
+// (at most 128 VGPRs: two workgroups of eight waves per compute unit)
+__global__ void __launch_bounds__(kStreamWaves * 64, 4) score_bf16_stream(IndexArgs a, float* scores, int32_t* n_valid,
                                                                         int64_t units_per_row, uint32_t* zero,
-                                                                        int64_t zero_words) {
+                                                                        int64_t zero_words, float* gmax, int g0,
+                                                                        int64_t gstride) {
   __shared__ __align__(16) uint16_t qs[64 * kQLd];
   __shared__ float ws[64];
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  // the selection's histogram and counters start at zero (they are read only after this kernel)
+  // the selection's counters start at zero (they are read only after this kernel)
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < zero_words; i += (int64_t)gridDim.x * blockDim.x)
     zero[i] = 0u;
   const int64_t R = (int64_t)a.B * a.T;
   const int64_t total = R * units_per_row;
   int64_t cur_row = -1;
+  int64_t nv_cur = 0;
   for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
     const int64_t row = u / units_per_row;
     const int64_t base = (u % units_per_row) * kUnit + wave * 64;
     const int b = (int)(row / a.T), tq = (int)(row % a.T);
-    const int64_t nv = n_visible(pos_at(a.q_pos, b) + tq, a.m, a.n_cap);
     if (row != cur_row) {  // uniform across the workgroup
       __syncthreads();
       cur_row = row;
+      nv_cur = n_visible(pos_at(a.q_pos, b) + tq, a.m, a.n_cap);
       const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)tq * a.q_ld;
       for (int c = threadIdx.x; c < 64 * 16; c += kStreamWaves * 64)
         *reinterpret_cast<uint4*>(&qs[(c >> 4) * kQLd + (c & 15) * 8]) = *reinterpret_cast<const uint4*>(qrow + c * 8);
       if (threadIdx.x < 64) ws[threadIdx.x] = head_weights(a, row)[threadIdx.x];
-      if (threadIdx.x == 0 && u % units_per_row == 0) n_valid[row] = (int32_t)nv;
+      if (threadIdx.x == 0 && u % units_per_row == 0) n_valid[row] = (int32_t)nv_cur;
       __syncthreads();
     }
+    const int64_t nv = nv_cur;
     if (base >= nv) continue;
     const uint16_t* kseq = static_cast<const uint16_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
     uint4 kb[16];
@@ -392,26 +410,30 @@ __global__ void __launch_bounds__(kStreamWaves * 64) score_bf16_stream(IndexArgs
       p += __shfl_xor(p, 32, 64);
       if ((lane >> 4) == g) mine = p;  // lane l keeps entry base + l
     }
-    const int64_t i = base + lane;
-    if (i < nv) scores[row * a.n_cap + i] = mine;
+    store_scores(scores, gmax, row, a.n_cap, gstride, g0, base, nv, mine);
   }
 }
 
-// MXFP4 variant: a tile is 64 entries x (64 code bytes + 4 scale bytes).
+// MXFP4 variant: a tile is 64 entries x (64 code bytes + 4 scale bytes); each key group of 16 entries
+// is one B operand of v_mfma_scale_f32_16x16x128_f8f6f4 (lane l: entry l%16, codes 16(l/16) .. +15,
+// the e8m0 scale of those 32 dims), so no dequantisation pass exists. Waves take one tile per step,
+// grid-stride, so that at every step the chip reads one contiguous stretch of the key arrays (measured
+// faster than giving each wave a run of consecutive tiles, or issuing several tiles' loads at once).
 constexpr int kFp4Waves = 4;
 
-__global__ void __launch_bounds__(kFp4Waves * 64) score_fp4_stream(IndexArgs a, float* scores, int32_t* n_valid,
+__global__ void __launch_bounds__(kFp4Waves * 64, 4) score_fp4_stream(IndexArgs a, float* scores, int32_t* n_valid,
                                                                      int64_t tiles_per_row, uint32_t* zero,
-                                                                     int64_t zero_words) {
+                                                                     int64_t zero_words, float* gmax, int g0,
+                                                                     int64_t gstride) {
   const int lane = lane_id();
-  // the selection's histogram and counters start at zero (they are read only after this kernel)
+  // the selection's counters start at zero (they are read only after this kernel)
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < zero_words; i += (int64_t)gridDim.x * blockDim.x)
     zero[i] = 0u;
   const int g = lane >> 4, c = lane & 15;
   const int64_t R = (int64_t)a.B * a.T;
   const int64_t total = R * tiles_per_row;
   const int64_t nwaves = (int64_t)gridDim.x * kFp4Waves;
-  int64_t cur_row = -1;
+  int64_t cur_row = -1, nv = 0;
   i32x8 qa[4];
   int qs[4];
   float wr[4][4];
@@ -419,11 +441,9 @@ __global__ void __launch_bounds__(kFp4Waves * 64) score_fp4_stream(IndexArgs a, 
     const int64_t row = t / tiles_per_row;
     const int64_t base = (t % tiles_per_row) * 64;
     const int b = (int)(row / a.T), tq = (int)(row % a.T);
-    const int64_t nv = n_visible(pos_at(a.q_pos, b) + tq, a.m, a.n_cap);
-    if (base == 0 && lane == 0) n_valid[row] = (int32_t)nv;
-    if (base >= nv) continue;
     if (row != cur_row) {
       cur_row = row;
+      nv = n_visible(pos_at(a.q_pos, b) + tq, a.m, a.n_cap);
       const uint8_t* qcodes = static_cast<const uint8_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)tq * a.q_ld;
       const uint8_t* qsc = a.q_scale + row * (64 * 4);
 #pragma unroll
@@ -438,6 +458,8 @@ __global__ void __launch_bounds__(kFp4Waves * 64) score_fp4_stream(IndexArgs a, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) wr[mt][r] = w[mt * 16 + g * 4 + r];
     }
+    if (base == 0 && lane == 0) n_valid[row] = (int32_t)nv;
+    if (base >= nv) continue;
     const uint8_t* kcodes = static_cast<const uint8_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
     const uint8_t* ksc = a.k_scale + (int64_t)b * a.n_cap * 4;
     i32x4 kv[4];
@@ -464,8 +486,7 @@ __global__ void __launch_bounds__(kFp4Waves * 64) score_fp4_stream(IndexArgs a, 
       p += __shfl_xor(p, 32, 64);
       if (g == grp) mine = p;
     }
-    const int64_t i = base + lane;
-    if (i < nv) scores[row * a.n_cap + i] = mine;
+    store_scores(scores, gmax, row, a.n_cap, gstride, g0, base, nv, mine);
   }
 }
 
@@ -521,18 +542,21 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
     p += align256((size_t)R * a.n_cap * 4);
     int32_t* nvalid = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)R * 4);
+    const SelPlan pl = select_plan(a.n_cap, a.k);
+    float* gm = select_gmax(p, (int)R);
+    const int g0 = select_needs_gmax(a.n_cap) ? pl.g0 : 0;
     if (a.idx_dtype == CSA_MXFP4) {
       const int64_t tpr = ceil_div(a.n_cap, 64) > 0 ? ceil_div(a.n_cap, 64) : 1;
       int64_t g = ceil_div(R * tpr, kFp4Waves);
       if (g > 2 * stream_grid()) g = 2 * stream_grid();
       hipLaunchKernelGGL(score_fp4_stream, dim3((unsigned)g), dim3(kFp4Waves * 64), 0, s, a, scores, nvalid, tpr,
-                         select_hist(p), select_zero_words((int)R));
+                         select_counters(p), R, gm, g0, pl.gstride);
     } else {
       const int64_t upr = ceil_div(a.n_cap, kUnit) > 0 ? ceil_div(a.n_cap, kUnit) : 1;
       int64_t g = R * upr;
       if (g > stream_grid()) g = stream_grid();
       hipLaunchKernelGGL(score_bf16_stream, dim3((unsigned)g), dim3(kStreamWaves * 64), 0, s, a, scores, nvalid, upr,
-                         select_hist(p), select_zero_words((int)R));
+                         select_counters(p), R, gm, g0, pl.gstride);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s);

@@ -139,16 +139,22 @@ struct TopkArgs {
 };
 size_t topk_workspace(int R, int64_t n, int k);
 
-// Multi-workgroup selection over long materialised rows (select.hip).
+// Selection over long materialised score rows (select.hip): a lower bound T0 of each row's k-th
+// largest score from the maxima of G ~ 2k groups of gs consecutive scores, the entries >= T0 as
+// candidates, then the exact top-k among them. g0 = min(gs, 64): the granularity at which the
+// maxima are stored (gstride per row).
+struct SelPlan {
+  int gs, g0;
+  int64_t gstride;
+};
+SelPlan select_plan(int64_t ld, int k);
+bool select_needs_gmax(int64_t ld);       // false: rows short enough to take their bound from themselves
 size_t select_workspace(int R, int64_t ld, int k);
-uint32_t* select_hist(void* ws);  // the [R, 4096] histogram at the start of the workspace
-// 32-bit words at the start of the workspace that must be zero before launch_select(zeroed=true)
-int64_t select_zero_words(int R);
-hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s);
-// max_valid: a bound, known on the host, of every row's n_valid (-1: none); rows longer than one
-// workgroup's reach whose valid prefix fits it are still selected in one pass
+uint32_t* select_counters(void* ws);      // [R] words that must be zero before launch_select(have_gmax)
+float* select_gmax(void* ws, int R);      // [R, gstride] group maxima
+// have_gmax: the caller has written the maxima and zeroed the counters (the decode indexer does both)
 hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
-                         float* out_score, void* ws, bool zeroed, hipStream_t s, int64_t max_valid = -1);
+                         float* out_score, void* ws, bool have_gmax, hipStream_t s);
 hipError_t launch_topk_from_scores(const TopkArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct AttnArgs {
@@ -184,6 +190,7 @@ hipError_t launch_copy_rows(int B, int rows, int cols, int esize, const void* sr
                             hipStream_t s);
 
 constexpr int kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
+constexpr int kMaxTopK = 4096;       // largest top_k the kernels take
 
 // Sets the dynamic-LDS ceiling of a kernel once (needed above 64 KiB).
 hipError_t allow_lds(const void* kernel, int bytes);

@@ -1,7 +1,30 @@
-// Exact top-k over materialised score rows: one workgroup per row for rows that fit its registers
-// (sel_row), many workgroups per row for longer rows (see select_radix.h).
+// Exact top-k of long materialised score rows (decode: few rows, up to millions of entries each;
+// "Anatomy of a Frontier Model", bullet "Compressed Sparse Attention (CSA)": each query keeps the
+// 1,024 entries the indexer ranks highest).
+//
+// Keys are the 64-bit keys of the streaming selection (topk_wave.h): order-preserving score bits in
+// the high half, ~index in the low half, so the k largest keys are the layer's top-k (ties toward the
+// smaller index) and all keys of a row are distinct.
+//
+// A lower bound first: split the row into G groups of gs consecutive entries. If G >= k, the k-th
+// largest group maximum T0 is at most the k-th largest score (k distinct groups each hold an entry
+// >= T0), so every entry of the top-k has a score >= T0. With G ~ 2k groups few entries clear T0
+// (about 1.4 k for independent scores), so the exact selection runs over a short list.
+//   sel_gmax     (csa_topk_from_scores only: the decode indexer writes the maxima with its scores)
+//                the maxima of every g0 consecutive entries (g0 = min(gs, 64): one wave's lanes)
+//   sel_collect  (many workgroups per row) T0 from the row's group maxima (the lower bound of the
+//                bin, in one histogram pass over their range, that holds the k-th largest), then
+//                every entry of its piece with a score key >= T0 is appended to the row's candidate
+//                list (one atomic per workgroup; the list order varies, the set does not)
+//   sel_final    (one workgroup per row) the exact k-th largest key of the candidates (12-bit
+//                histogram passes over the range that holds it, from LDS when the candidates fit,
+//                else from the global list), then the k selected entries in index order (ranks from
+//                a bitmap of the selected indices; a bitonic sort for rows beyond the bitmap).
+//   sel_row      (rows of up to 32K scores, which need no group maxima: one workgroup per row, one
+//                launch) the row held in registers, radix passes over its key range.
+// Rows with at most k valid entries keep them all.
 #include "kernels.h"
-#include "select_radix.h"
+#include "topk_wave.h"
 
 namespace csa {
 
@@ -9,272 +32,376 @@ namespace {
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-__global__ void __launch_bounds__(256) sel_zero(uint32_t* hist, uint32_t* cnt, int R) {
-  const int64_t n = (int64_t)R * kSelBins;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) hist[i] = 0u;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < 4LL * R; i += stride) cnt[i] = 0u;
-}
+constexpr int kCollectThreads = 256;
+constexpr int kCollectPer = 16;                                  // scores per thread
+constexpr int kCollectPiece = kCollectThreads * kCollectPer;     // scores per workgroup
+constexpr int kFinalThreads = 1024;
+constexpr int kFinalCap = 8192;                                  // candidates held in LDS
 
 __device__ __forceinline__ int64_t row_valid(const int32_t* n_valid, int64_t row, int64_t ld) {
   int64_t nv = n_valid[row];
   return nv < 0 ? 0 : (nv > ld ? ld : nv);
 }
 
-// Pass A on caller scores: histogram of the top 12 key bits per row.
-__global__ void __launch_bounds__(kSelThreads) sel_hist(const float* scores, int64_t ld, const int32_t* n_valid,
-                                                        uint32_t* hist) {
-  __shared__ uint32_t lh[kSelBins];
-  const int64_t row = blockIdx.y;
-  const int64_t nv = row_valid(n_valid, row, ld);
-  const int64_t base = (int64_t)blockIdx.x * kSelChunk;
-  if (base >= nv) return;
-  sel_zero_lds_hist(lh);
+// Block-wide exclusive scan of one value per thread; wsum holds one word per wave.
+template <int BT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) {
+  constexpr int NW = BT / 64;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  const int64_t end = base + kSelChunk < nv ? base + kSelChunk : nv;
-  const float* s = scores + row * ld;
-  constexpr int kPer = kSelChunk / kSelThreads;
-  uint32_t dg[kPer];
+  uint32_t off = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {  // all loads first, then the LDS atomics
-    const int64_t i = base + (int64_t)j * kSelThreads + threadIdx.x;
-    dg[j] = i < end ? score_to_key(s[i]) >> kSelShift : kSelBins;
-  }
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (dg[j] < (uint32_t)kSelBins) atomicAdd(&lh[dg[j]], 1u);
+  for (int w = 0; w < NW; ++w) off += w < wave ? wsum[w] : 0u;
   __syncthreads();
-  sel_flush_hist(lh, hist + row * kSelBins);
+  return off + incl - v;
 }
 
-// Pass B: boundary digit of the row, then classify this workgroup's chunk.
-__global__ void __launch_bounds__(kSelThreads) sel_collect(const float* scores, int64_t ld, const int32_t* n_valid,
-                                                           int k, SelWork w) {
-  __shared__ uint32_t scan4[4];
-  __shared__ uint32_t sh_d;
-  const int64_t row = blockIdx.y;
-  const int64_t nv = row_valid(n_valid, row, ld);
-  const int64_t base = (int64_t)blockIdx.x * kSelChunk;
-  if (base >= nv) return;
+// Four consecutive scores of a row from i on, loaded without a branch so that a thread's loads all go
+// out together: indices are clamped into the row (ld entries; entries past the valid count are masked
+// by the caller). vec: rows of a multiple of 4 floats at a 16-byte aligned base.
+__device__ __forceinline__ void load4(const float* srow, int64_t ld, int64_t i, bool vec, float* v) {
+  if (vec) {
+    const int64_t ic = i + 4 <= ld ? i : ld - 4;
+    const float4 f = *reinterpret_cast<const float4*>(srow + ic);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = srow[i + e < ld ? i + e : ld - 1];
+  }
+}
+
+constexpr int kBins = 4096;  // 12-bit digits of the radix passes
+
+// Block-wide minimum and maximum of keys (KT = uint32_t or uint64_t); red: 2 * (BT / 64) words.
+template <int BT, class KT>
+__device__ __forceinline__ void block_minmax(KT& mn, KT& mx, KT* red) {
+  constexpr int NW = BT / 64;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  for (int o = 32; o > 0; o >>= 1) {
+    KT a, b;
+    if constexpr (sizeof(KT) == 8) {
+      a = shfl_u64(mn, lane ^ o);
+      b = shfl_u64(mx, lane ^ o);
+    } else {
+      a = (KT)__shfl_xor((uint32_t)mn, o, 64);
+      b = (KT)__shfl_xor((uint32_t)mx, o, 64);
+    }
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (lane == 0) {
+    red[wave] = mn;
+    red[NW + wave] = mx;
+  }
+  __syncthreads();
+  mn = red[0];
+  mx = red[NW];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    mn = red[w] < mn ? red[w] : mn;
+    mx = red[NW + w] > mx ? red[NW + w] : mx;
+  }
+  __syncthreads();
+}
+
+// One histogram pass over the keys in [lo, lo + span] (key_at(i), i < n): kBins bins of width 2^sh,
+// sh = max(0, bits(span) - 12), so keys that share their high bits still spread over the bins. Finds
+// the bin holding the krem-th largest of those keys: returns its index d; above = keys in higher
+// bins, inbin = keys in it. sh: the shift used. hist: kBins words, wsum: BT / 64 words, out: 3 words.
+template <int BT, class KT, class KeyAt>
+__device__ uint32_t range_pass(int64_t n, KeyAt key_at, KT lo, KT span, uint32_t krem, int& sh, uint32_t& above,
+                               uint32_t& inbin, uint32_t* hist, uint32_t* wsum, uint32_t* out) {
+  constexpr int KB = 8 * (int)sizeof(KT);
+  constexpr int PER = kBins / BT;  // bins per thread, scanned from the top down
   const int tid = threadIdx.x;
-  const bool all = nv <= k;
-  uint32_t d = 0;
-  if (!all) {
-    const uint32_t* h = w.hist + row * kSelBins;
-    constexpr int per = kSelBins / kSelThreads;  // 16 bins per thread, scanned from the top digit down
-    uint32_t c[per];
-    uint32_t local = 0;
-#pragma unroll
-    for (int j = 0; j < per; ++j) {
-      c[j] = h[kSelBins - 1 - per * tid - j];
-      local += c[j];
-    }
-    const uint32_t incl = block_incl_scan(local, scan4);
-    const uint32_t excl = incl - local;
-    if (excl < (uint32_t)k && (uint32_t)k <= incl) {
-      uint32_t run = excl;
-      for (int j = 0; j < per; ++j) {
-        if (run + c[j] >= (uint32_t)k) {
-          sh_d = kSelBins - 1 - per * tid - j;
-          break;
-        }
-        run += c[j];
-      }
-    }
-    __syncthreads();
-    d = sh_d;
-  }
-  const float* s = scores + row * ld;
-  uint32_t* cnt = w.cnt + row * 4;
-  uint64_t* above = w.above + row * k;
-  uint64_t* bnd = w.bnd + row * ld;
-  // classify this thread's scores, count per wave, then one atomic per list per workgroup
-  constexpr int kPer = kSelChunk / kSelThreads;
-  uint64_t keyv[kPer];
-  uint32_t cls = 0;  // bit 2j: above, bit 2j+1: boundary
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t i = base + (int64_t)j * kSelThreads + tid;
-    const bool valid = i < nv;
-    const float v = valid ? s[i] : 0.f;
-    const uint32_t key = score_to_key(v);
-    const uint32_t dig = key >> kSelShift;
-    const bool isA = valid && (all || dig > d);
-    const bool isB = valid && !all && dig == d;
-    keyv[j] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)i);
-    cls |= (isA ? 1u : 0u) << (2 * j);
-    cls |= (isB ? 1u : 0u) << (2 * j + 1);
-  }
-  uint32_t nA = 0, nB = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    nA += (cls >> (2 * j)) & 1u;
-    nB += (cls >> (2 * j + 1)) & 1u;
-  }
-  // block-exclusive offsets of this thread's A and B candidates
-  const uint32_t packed = nA | (nB << 16);  // at most 16 each per thread, 4096 per block: fits 16 bits
-  const uint32_t incl = block_incl_scan(packed, scan4);
-  __shared__ uint32_t base_ab[2];
-  if (tid == kSelThreads - 1) {
-    const uint32_t totA = incl & 0xFFFFu, totB = incl >> 16;
-    base_ab[0] = totA ? atomicAdd(&cnt[0], totA) : 0u;
-    base_ab[1] = totB ? atomicAdd(&cnt[1], totB) : 0u;
+  const int bits = span == 0 ? 0 : KB - (sizeof(KT) == 8 ? __clzll((long long)span) : __clz((int)span));
+  sh = bits > 12 ? bits - 12 : 0;
+  for (int b = tid; b < kBins; b += BT) hist[b] = 0u;
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += BT) {
+    const KT v = key_at(i);
+    const KT u = v - lo;
+    if (v >= lo && u <= span) atomicAdd(&hist[(uint32_t)(u >> sh)], 1u);
   }
   __syncthreads();
-  uint32_t offA = base_ab[0] + ((incl - packed) & 0xFFFFu);
-  uint32_t offB = base_ab[1] + ((incl - packed) >> 16);
+  uint32_t cnt[PER], local = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if ((cls >> (2 * j)) & 1u) above[offA++] = keyv[j];
-    if ((cls >> (2 * j + 1)) & 1u) bnd[offB++] = keyv[j];
+  for (int j = 0; j < PER; ++j) {
+    cnt[j] = hist[kBins - 1 - PER * tid - j];
+    local += cnt[j];
+  }
+  const uint32_t excl = block_excl_scan<BT>(local, wsum);
+  if (excl < krem && krem <= excl + local) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (run < krem && krem <= run + cnt[j]) {
+        out[0] = (uint32_t)(kBins - 1 - PER * tid - j);
+        out[1] = run;
+        out[2] = cnt[j];
+      }
+      run += cnt[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t d = out[0];
+  above = out[1];
+  inbin = out[2];
+  __syncthreads();
+  return d;
+}
+
+// The g0-maxima of rows of scores (csa_topk_from_scores); zeroes the candidate counters.
+__global__ void __launch_bounds__(256) sel_gmax(const float* scores, int64_t ld, const int32_t* n_valid, int g0,
+                                               int64_t gstride, float* gmax, uint32_t* cnt) {
+  const int64_t row = blockIdx.y;
+  if (blockIdx.x == 0 && threadIdx.x == 0) cnt[row] = 0u;
+  const int64_t nv = row_valid(n_valid, row, ld);
+  const int lane = lane_id();
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  for (int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64; base < nv; base += waves * 64) {
+    const int64_t i = base + lane;
+    float v = i < nv ? scores[row * ld + i] : -INFINITY;
+    for (int o = 1; o < g0; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    if ((lane & (g0 - 1)) == 0 && i < nv) gmax[row * gstride + i / g0] = v;
   }
 }
 
-// Pass C: exact selection among the boundary candidates, then the selected entries in index order.
-// The boundary list is staged in LDS when it fits. Ordering: rows of up to kBitmapMax entries mark
-// the selected indices in an LDS bitmap, and each entry's output slot is the number of marked
-// indices below it (word prefix counts + popcount), so no sort is needed; longer rows fall back to
-// a bitonic sort.
-constexpr int kBndCache = 4096;        // boundary keys staged in LDS
-constexpr int kBitmapMax = 262144;     // entries per row ordered through the bitmap
+// Scratch of the selection between its kernels.
+struct SelBufs {
+  uint32_t* cnt;   // [R] candidates appended per row (zero before sel_collect)
+  float* gmax;     // [R, gstride] maxima of g0 consecutive scores
+  uint64_t* cand;  // [R, ld] candidate keys
+};
 
+__global__ void __launch_bounds__(kCollectThreads) sel_collect(const float* scores, int64_t ld,
+                                                                const int32_t* n_valid, int k, SelPlan pl,
+                                                                SelBufs w) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t red[2 * (kCollectThreads / 64)];
+  __shared__ uint32_t sh3[kCollectThreads / 64 + 4];
+  const int64_t row = blockIdx.y;
+  const int64_t nv = row_valid(n_valid, row, ld);
+  const int64_t p0 = (int64_t)blockIdx.x * kCollectPiece;
+  if (nv <= k || p0 >= nv) return;  // uniform
+  const int tid = threadIdx.x;
+  // the row's score loads of this piece go out first; the threshold is formed while they fly
+  float s[kCollectPer];
+  const float* srow = scores + row * ld;
+  const bool vec = (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
+#pragma unroll
+  for (int j = 0; j < kCollectPer / 4; ++j) load4(srow, ld, p0 + (int64_t)(j * kCollectThreads + tid) * 4, vec, s + 4 * j);
+  // T0: the lower bound of the bin (one histogram pass over the range of the keys) that holds the
+  // k-th largest maximum of the row's groups of gs entries; at most that maximum, so at most the
+  // k-th largest score
+  const int r = pl.gs / pl.g0;  // stored maxima per group
+  const int64_t G = (nv + pl.gs - 1) / pl.gs;
+  const int64_t G0 = (nv + pl.g0 - 1) / pl.g0;
+  const float* gm = w.gmax + row * pl.gstride;
+  auto group_key = [&](int64_t g) -> uint32_t {
+    float v = -INFINITY;
+    for (int j = 0; j < r; ++j) {
+      const int64_t q = g * r + j;
+      if (q < G0) v = fmaxf(v, gm[q]);
+    }
+    return score_to_key(v);
+  };
+  uint32_t T0 = 0;
+  if (G >= k) {
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int64_t g = tid; g < G; g += kCollectThreads) {
+      const uint32_t v = group_key(g);
+      mn = v < mn ? v : mn;
+      mx = v > mx ? v : mx;
+    }
+    block_minmax<kCollectThreads, uint32_t>(mn, mx, red);
+    int shv;
+    uint32_t above, inbin;
+    const uint32_t d = range_pass<kCollectThreads, uint32_t>(G, group_key, mn, mx - mn, (uint32_t)k, shv, above,
+                                                             inbin, hist, sh3, sh3 + kCollectThreads / 64);
+    T0 = mn + (d << shv);
+  }
+  // append this piece's entries with a key >= T0: the workgroup's count is added to the row's
+  // counter by one atomic, and each thread writes its entries after those of the threads before it
+  uint32_t take = 0;
+#pragma unroll
+  for (int j = 0; j < kCollectPer; ++j) {
+    const int64_t i = p0 + (int64_t)((j >> 2) * kCollectThreads + tid) * 4 + (j & 3);
+    take |= (i < nv && score_to_key(s[j]) >= T0 ? 1u : 0u) << j;
+  }
+  const uint32_t mine = (uint32_t)__popc(take);
+  uint32_t off = block_excl_scan<kCollectThreads>(mine, sh3);
+  if (tid == kCollectThreads - 1) hist[0] = off + mine ? atomicAdd(w.cnt + row, off + mine) : 0u;
+  __syncthreads();
+  off += hist[0];
+  uint64_t* cand = w.cand + row * ld;
+#pragma unroll
+  for (int j = 0; j < kCollectPer; ++j) {
+    if ((take >> j) & 1u) {
+      const uint32_t i = (uint32_t)(p0 + (int64_t)((j >> 2) * kCollectThreads + tid) * 4 + (j & 3));
+      cand[off++] = ((uint64_t)score_to_key(s[j]) << 32) | (uint32_t)(~i);
+    }
+  }
+}
+
+// LDS of sel_final: candidate keys | bins | (bitmap of selected indices and per-word ranks, or the
+// selected keys for the bitonic sort of rows longer than the bitmap) | small scratch
+constexpr int kBitmapMax = 262144;  // row length ordered through the bitmap
 struct FinalSmem {
-  uint64_t bc[kBndCache];              // boundary keys
-  uint32_t bm[kBitmapMax / 32];        // selected-index bitmap
-  uint16_t wc[kBitmapMax / 32];        // exclusive popcount per bitmap word
-  uint32_t hist[256];
-  uint32_t scan4[4];
-  uint32_t sh[3];
+  uint64_t keys[kFinalCap];
+  uint32_t hist[kBins];
+  union {
+    struct {
+      uint32_t bm[kBitmapMax / 32];
+      uint16_t wc[kBitmapMax / 32];
+    } b;
+    uint64_t sel[kMaxTopK];
+  } u;
+  uint64_t red[2 * (kFinalThreads / 64)];
+  uint32_t sh[kFinalThreads / 64 + 4];
   uint32_t nsel;
 };
 
-__global__ void __launch_bounds__(kSelThreads) sel_final(const int32_t* n_valid, int64_t ld, int k, SelWork w,
-                                                         int32_t* out_idx, float* out_score) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  FinalSmem& sm = *reinterpret_cast<FinalSmem*>(smem_raw);
-  uint64_t* sel = reinterpret_cast<uint64_t*>(smem_raw + sizeof(FinalSmem));  // next_pow2(k) keys
+// The exact top-k among c candidate keys (all distinct; c >= k) given by key_at, written to
+// oi / os in index order; entries of a row of nv. mn, mx: the smallest and largest candidate key.
+template <class KeyAt>
+__device__ void select_candidates(uint32_t c, KeyAt key_at, uint64_t mn, uint64_t mx, int64_t nv, int k,
+                                  FinalSmem& sm, int32_t* oi, float* os) {
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int64_t nv = row_valid(n_valid, row, ld);
-  const int ntake = (int)(nv < k ? nv : k);
-  const uint32_t na = w.cnt[row * 4], nb = w.cnt[row * 4 + 1];
-  const int krem = ntake - (int)na;
-  const uint64_t* A = w.above + row * k;
-  const uint64_t* Bg = w.bnd + row * ld;
-  for (uint32_t i = tid; i < na; i += kSelThreads) sel[i] = A[i];
-  const bool cached = nb <= (uint32_t)kBndCache;
-  if (krem > 0 && cached)
-    for (uint32_t i = tid; i < nb; i += kSelThreads) sm.bc[i] = Bg[i];
-  __syncthreads();
-  const uint64_t* Bl = cached ? sm.bc : Bg;
-  uint64_t T = 0;
-  if (krem > 0 && (uint32_t)krem < nb) {
-    // every boundary key shares the top 12 bits (the boundary digit): start below them
-    const uint64_t known = ~0ull << (32 + kSelShift);
-    uint64_t prefix = Bl[0] & known, pmask = known;
-    uint32_t kr = (uint32_t)krem;
-    for (int shift = 32 + kSelShift - 8; shift >= 0; shift = shift >= 8 ? shift - 8 : (shift > 0 ? 0 : -1)) {
-      sm.hist[tid] = 0u;
-      __syncthreads();
-      for (uint32_t i = tid; i < nb; i += kSelThreads) {
-        const uint64_t key = Bl[i];
-        if ((key & pmask) == prefix) atomicAdd(&sm.hist[(uint32_t)(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      const uint32_t c = sm.hist[255 - tid];
-      const uint32_t incl = block_incl_scan(c, sm.scan4);
-      const uint32_t excl = incl - c;
-      if (excl < kr && kr <= incl) {
-        sm.sh[0] = 255 - tid;
-        sm.sh[1] = excl;
-        sm.sh[2] = c;
-      }
-      __syncthreads();
-      const uint32_t digit = sm.sh[0], ab = sm.sh[1], inbin = sm.sh[2];
-      __syncthreads();
-      prefix |= (uint64_t)digit << shift;
-      pmask |= 255ull << shift;
-      kr -= ab;
-      if (inbin == kr) break;
+  // the exact k-th largest key: passes over the range that holds it
+  uint64_t lo = mn, span = mx - mn;
+  uint32_t krem = (uint32_t)k;
+  uint64_t T1;
+  while (true) {
+    int shv;
+    uint32_t above, inbin;
+    const uint32_t d = range_pass<kFinalThreads, uint64_t>((int64_t)c, key_at, lo, span, krem, shv, above, inbin,
+                                                           sm.hist, sm.sh, sm.sh + kFinalThreads / 64);
+    krem -= above;
+    lo += (uint64_t)d << shv;
+    // keys >= lo are the ones above the range, above the bin, and the whole bin
+    if (inbin == krem || shv == 0) {
+      T1 = lo;
+      break;
     }
-    T = prefix;
-  }
-  if (tid == 0) sm.nsel = na;
-  __syncthreads();
-  if (krem > 0) {
-    for (uint32_t i = tid; i < nb; i += kSelThreads) {
-      const uint64_t key = Bl[i];
-      if (key >= T) sel[atomicAdd(&sm.nsel, 1u)] = key;
-    }
-  }
-  __syncthreads();
-  const int have = (int)sm.nsel;  // == ntake
-  int32_t* oi = out_idx + row * k;
-  float* os = out_score ? out_score + row * k : nullptr;
-  for (int j = have + tid; j < k; j += kSelThreads) {
-    oi[j] = -1;
-    if (os) os[j] = -INFINITY;
+    const uint64_t wdt = ((uint64_t)1 << shv) - 1;
+    span = span - ((uint64_t)d << shv) < wdt ? span - ((uint64_t)d << shv) : wdt;
   }
   if (nv <= kBitmapMax) {
+    // ranks in index order from a bitmap of the selected indices
     const int nw = (int)((nv + 31) / 32);
-    for (int i = tid; i < nw; i += kSelThreads) sm.bm[i] = 0u;
+    for (int i = tid; i < nw; i += kFinalThreads) sm.u.b.bm[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < have; i += kSelThreads) {
-      const uint32_t idx = ~(uint32_t)sel[i];
-      atomicOr(&sm.bm[idx >> 5], 1u << (idx & 31));
+    for (uint32_t i = tid; i < c; i += kFinalThreads) {
+      const uint64_t v = key_at(i);
+      if (v >= T1) {
+        const uint32_t idx = ~(uint32_t)v;
+        atomicOr(&sm.u.b.bm[idx >> 5], 1u << (idx & 31));
+      }
     }
     __syncthreads();
-    const int wpt = (nw + kSelThreads - 1) / kSelThreads;
+    const int wpt = (nw + kFinalThreads - 1) / kFinalThreads;
     const int w0 = tid * wpt, w1 = w0 + wpt < nw ? w0 + wpt : nw;
-    uint32_t local = 0;
-    for (int i = w0; i < w1; ++i) local += __popc(sm.bm[i]);
-    uint32_t run = block_incl_scan(local, sm.scan4) - local;
+    uint32_t local_cnt = 0;
+    for (int i = w0; i < w1; ++i) local_cnt += __popc(sm.u.b.bm[i]);
+    uint32_t run = block_excl_scan<kFinalThreads>(local_cnt, sm.sh);
     for (int i = w0; i < w1; ++i) {
-      sm.wc[i] = (uint16_t)run;
-      run += __popc(sm.bm[i]);
+      sm.u.b.wc[i] = (uint16_t)run;
+      run += __popc(sm.u.b.bm[i]);
     }
     __syncthreads();
-    for (int i = tid; i < have; i += kSelThreads) {
-      const uint64_t key = sel[i];
-      const uint32_t idx = ~(uint32_t)key;
-      const uint32_t wd = idx >> 5;
-      const int rank = sm.wc[wd] + __popc(sm.bm[wd] & ((1u << (idx & 31)) - 1u));
-      oi[rank] = (int32_t)idx;
-      if (os) os[rank] = key_to_score((uint32_t)(key >> 32));
+    for (uint32_t i = tid; i < c; i += kFinalThreads) {
+      const uint64_t v = key_at(i);
+      if (v >= T1) {
+        const uint32_t idx = ~(uint32_t)v;
+        const uint32_t wd = idx >> 5;
+        const uint32_t rank = sm.u.b.wc[wd] + __popc(sm.u.b.bm[wd] & ((1u << (idx & 31)) - 1u));
+        if (rank < (uint32_t)k) {
+          oi[rank] = (int32_t)idx;
+          if (os) os[rank] = key_to_score((uint32_t)(v >> 32));
+        }
+      }
     }
     return;
   }
+  // longer rows: the k selected keys re-keyed as (index, score key) and sorted by a bitonic network
+  if (tid == 0) sm.nsel = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < c; i += kFinalThreads) {
+    const uint64_t v = key_at(i);
+    if (v >= T1) {
+      const uint32_t slot = atomicAdd(&sm.nsel, 1u);
+      if (slot < (uint32_t)k) sm.u.sel[slot] = ((uint64_t)(~(uint32_t)v) << 32) | (v >> 32);
+    }
+  }
   int P = 1;
   while (P < k) P <<= 1;
-  for (int i = tid; i < P; i += kSelThreads) {
-    uint64_t v = ~0ull;
-    if (i < have) {
-      const uint64_t key = sel[i];
-      v = ((uint64_t)(~(uint32_t)key) << 32) | (key >> 32);
-    }
-    sel[i] = v;
-  }
+  __syncthreads();
+  for (int i = k + tid; i < P; i += kFinalThreads) sm.u.sel[i] = ~0ull;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (P >> 1); t += kSelThreads) {
+      for (int t = tid; t < (P >> 1); t += kFinalThreads) {
         const int i = (t / stride) * stride * 2 + (t % stride);
         const int j = i + stride;
         const bool up = (i & size) == 0;
-        const uint64_t a = sel[i], b = sel[j];
+        const uint64_t a = sm.u.sel[i], b = sm.u.sel[j];
         if ((a > b) == up) {
-          sel[i] = b;
-          sel[j] = a;
+          sm.u.sel[i] = b;
+          sm.u.sel[j] = a;
         }
       }
       __syncthreads();
     }
   }
-  for (int j = tid; j < have; j += kSelThreads) {
-    const uint64_t v = sel[j];
+  for (int j = tid; j < k; j += kFinalThreads) {
+    const uint64_t v = sm.u.sel[j];
     oi[j] = (int32_t)(uint32_t)(v >> 32);
     if (os) os[j] = key_to_score((uint32_t)v);
   }
+}
+
+// Rows with at most k valid entries keep them all, in order (returns true then).
+__device__ __forceinline__ bool keep_all(const float* scores, int64_t ld, int64_t row, int64_t nv, int k,
+                                         int32_t* oi, float* os) {
+  if (nv > k) return false;
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    oi[j] = j < nv ? j : -1;
+    if (os) os[j] = j < nv ? key_to_score(score_to_key(scores[row * ld + j])) : -INFINITY;
+  }
+  return true;
+}
+
+__global__ void __launch_bounds__(kFinalThreads) sel_final(const float* scores, int64_t ld, const int32_t* n_valid,
+                                                            int k, SelBufs w, int32_t* out_idx, float* out_score) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  FinalSmem& sm = *reinterpret_cast<FinalSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t nv = row_valid(n_valid, row, ld);
+  int32_t* oi = out_idx + row * k;
+  float* os = out_score ? out_score + row * k : nullptr;
+  if (keep_all(scores, ld, row, nv, k, oi, os)) return;
+  const uint32_t c = w.cnt[row];  // >= k: at least k entries clear T0
+  const uint64_t* gc = w.cand + row * ld;
+  const bool local = c <= (uint32_t)kFinalCap;
+  uint64_t mn = ~0ull, mx = 0ull;
+  for (uint32_t i = tid; i < c; i += kFinalThreads) {
+    const uint64_t v = gc[i];
+    if (local) sm.keys[i] = v;
+    mn = v < mn ? v : mn;
+    mx = v > mx ? v : mx;
+  }
+  block_minmax<kFinalThreads, uint64_t>(mn, mx, sm.red);  // its barrier also publishes the keys
+  if (local)
+    select_candidates(c, [&](int64_t i) { return sm.keys[i]; }, mn, mx, nv, k, sm, oi, os);
+  else
+    select_candidates(c, [&](int64_t i) { return gc[i]; }, mn, mx, nv, k, sm, oi, os);
 }
 
 // Rows of up to kRowMax scores: one workgroup per row does the whole selection with the row held in
@@ -555,102 +682,77 @@ void launch_row(const RowSel& a, int R, hipStream_t s) {
   else launch_row_p<32>(a, R, s);
 }
 
-SelWork carve(void* ws, int R, int64_t ld, int k) {
+SelBufs carve(void* ws, int R, int64_t ld, int k) {
+  const SelPlan pl = select_plan(ld, k);
   uint8_t* p = static_cast<uint8_t*>(ws);
-  SelWork w;
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += a256((size_t)R * kSelBins * 4);
+  SelBufs w;
   w.cnt = reinterpret_cast<uint32_t*>(p);
-  p += a256((size_t)R * 4 * 4);
-  w.above = reinterpret_cast<uint64_t*>(p);
-  p += a256((size_t)R * k * 8);
-  w.bnd = reinterpret_cast<uint64_t*>(p);
+  p += a256((size_t)R * 4);
+  w.gmax = reinterpret_cast<float*>(p);
+  p += a256((size_t)R * pl.gstride * 4);
+  w.cand = reinterpret_cast<uint64_t*>(p);
   return w;
 }
 
 }  // namespace
 
+bool select_needs_gmax(int64_t ld) { return ld > kRowMax; }
+
+SelPlan select_plan(int64_t ld, int k) {
+  // gs: the largest power of two with ld / gs >= 2k groups (at least 16 entries per group)
+  SelPlan pl{};
+  int64_t gs = 16;
+  while (gs * 2 * 2 * (int64_t)k <= ld) gs *= 2;
+  pl.gs = (int)gs;
+  pl.g0 = gs < 64 ? (int)gs : 64;
+  pl.gstride = (ld + pl.g0 - 1) / pl.g0;
+  return pl;
+}
+
 size_t select_workspace(int R, int64_t ld, int k) {
-  return a256((size_t)R * kSelBins * 4) + a256((size_t)R * 4 * 4) + a256((size_t)R * k * 8) + a256((size_t)R * ld * 8);
+  const SelPlan pl = select_plan(ld, k);
+  return a256((size_t)R * 4) + a256((size_t)R * pl.gstride * 4) + a256((size_t)R * ld * 8);
 }
 
-uint32_t* select_hist(void* ws) { return static_cast<uint32_t*>(ws); }
+uint32_t* select_counters(void* ws) { return static_cast<uint32_t*>(ws); }
 
-int64_t select_zero_words(int R) { return (int64_t)((a256((size_t)R * kSelBins * 4) + (size_t)R * 4 * 4) / 4); }
-
-hipError_t launch_select_zero(void* ws, int R, int64_t ld, int k, hipStream_t s) {
-  SelWork w = carve(ws, R, ld, k);
-  const int64_t n = (int64_t)R * kSelBins;
-  unsigned g = (unsigned)ceil_div(n, 256);
-  if (g > 1024) g = 1024;
-  hipLaunchKernelGGL(sel_zero, dim3(g), dim3(256), 0, s, w.hist, w.cnt, R);
-  return hipGetLastError();
-}
+float* select_gmax(void* ws, int R) { return reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + a256((size_t)R * 4)); }
 
 hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid, int R, int k, int32_t* out_idx,
-                         float* out_score, void* ws, bool zeroed, hipStream_t s, int64_t max_valid) {
-  RowSel rs{};
-  rs.k = k;
-  // the part of a row that can hold valid scores (n_valid never exceeds max_valid when it is given)
-  const int64_t span = max_valid >= 0 && max_valid < ld ? max_valid : ld;
-  if (span <= kRowMax) {
+                         float* out_score, void* ws, bool have_gmax, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  const SelPlan pl = select_plan(ld, k);
+  const SelBufs w = carve(ws, R, ld, k);
+  hipError_t e;
+  const int lds = (int)sizeof(FinalSmem);
+  if (ld <= kRowMax) {  // one workgroup per row, the row in registers, one launch
+    RowSel rs{};
     rs.scores = scores;
     rs.ld = ld;
-    rs.chunk = span;
+    rs.chunk = ld;
     rs.nchunk = 1;
     rs.n_valid = n_valid;
+    rs.k = k;
     rs.out_idx = out_idx;
     rs.out_score = out_score;
     launch_row(rs, R, s);
     return hipGetLastError();
   }
-  // Longer rows, while the candidates fit one workgroup: the k best of every piece
-  // (the row's k best are among them; each piece's list is in index order, so the concatenation
-  // is too), then the k best of those candidates with positions mapped back to indices. Both
-  // passes use the same key order, so the result is the direct selection's.
-  // pieces of 16K scores when their candidates fit (more workgroups, shorter ones: measured faster
-  // than 32K or 8K pieces for 1M-token rows), else 32K
-  const int64_t piece = ceil_div(span, kRowMax / 2) * k <= kRowMax ? kRowMax / 2 : kRowMax;
-  const int64_t nchunk = ceil_div(span, piece);
-  if (nchunk * k <= kRowMax && (size_t)R * nchunk * k * 8 + 256 <= select_workspace(R, ld, k)) {
-    int32_t* cand_idx = static_cast<int32_t*>(ws);
-    float* cand_score = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + a256((size_t)R * nchunk * k * 4));
-    rs.scores = scores;
-    rs.ld = ld;
-    rs.chunk = piece;
-    rs.nchunk = (int)nchunk;
-    rs.n_valid = n_valid;
-    rs.out_idx = cand_idx;
-    rs.out_score = cand_score;
-    launch_row(rs, R, s);
-    hipError_t e;
+  if (!have_gmax) {
+    int64_t gx = ceil_div(ld, 256 * 4);
+    if (gx > 1024) gx = 1024;
+    if (gx < 1) gx = 1;
+    hipLaunchKernelGGL(sel_gmax, dim3((unsigned)gx, (unsigned)R), dim3(256), 0, s, scores, ld, n_valid, pl.g0,
+                       pl.gstride, w.gmax, w.cnt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    RowSel r2{};
-    r2.scores = cand_score;
-    r2.ld = nchunk * k;
-    r2.chunk = nchunk * k;
-    r2.nchunk = 1;
-    r2.k = k;
-    r2.out_idx = out_idx;
-    r2.out_score = out_score;
-    r2.remap = cand_idx;
-    r2.row_nv = n_valid;
-    launch_row(r2, R, s);
-    return hipGetLastError();
   }
-  SelWork w = carve(ws, R, ld, k);
-  hipError_t e;
-  const unsigned nchunks = (unsigned)(ceil_div(ld, kSelChunk) > 0 ? ceil_div(ld, kSelChunk) : 1);
-  if (!zeroed && (e = launch_select_zero(ws, R, ld, k, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_hist, dim3(nchunks, (unsigned)R), dim3(kSelThreads), 0, s, scores, ld, n_valid, w.hist);
+  const unsigned pieces = (unsigned)(ceil_div(ld, kCollectPiece) > 0 ? ceil_div(ld, kCollectPiece) : 1);
+  hipLaunchKernelGGL(sel_collect, dim3(pieces, (unsigned)R), dim3(kCollectThreads), 0, s, scores, ld, n_valid, k, pl,
+                     w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_collect, dim3(nchunks, (unsigned)R), dim3(kSelThreads), 0, s, scores, ld, n_valid, k, w);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  int P = 1;
-  while (P < k) P <<= 1;
-  const int lds = (int)sizeof(FinalSmem) + P * 8;
   if ((e = allow_lds((const void*)sel_final, lds)) != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_final, dim3((unsigned)R), dim3(kSelThreads), lds, s, n_valid, ld, k, w, out_idx, out_score);
+  hipLaunchKernelGGL(sel_final, dim3((unsigned)R), dim3(kFinalThreads), lds, s, scores, ld, n_valid, k, w, out_idx,
+                     out_score);
   return hipGetLastError();
 }
 

@@ -1,8 +1,8 @@
 // Step 3 on materialised scores: exact top-k of each row, ties toward the smaller column.
 //
 // Short rows: one wave per row runs the streaming selection (topk_wave.h) straight to the output.
-// Long rows: select.hip (one workgroup per row with the row in registers up to 32K scores, the
-// multi-workgroup radix selection beyond). All use the same exact key order.
+// Long rows: select.hip (group-maximum lower bound, candidates, exact selection among them). All use
+// the same exact key order.
 #include "kernels.h"
 #include "topk_wave.h"
 
