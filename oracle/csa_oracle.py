@@ -45,12 +45,17 @@ prefill/decode when their fid argument is given (readings: a per-dim gain, adjac
 with base theta, entries rotated at the last token of their block, the window's raw KV normalised
 and rotated like an entry at its token's position).
 
+FP4 indexer ([ANAT] "The KV cache, recomputed" and "Precision: FP8 everywhere, FP4 experts"):
+mxfp4_quantize / mxfp4_decode (OCP MXFP4: e2m1 elements, one e8m0 scale per 32); prefill quantises
+the chunk's new keys and its indexer queries when the workload's indexer storage is MXFP4 (reading:
+quantise the stored bf16 values, the sign bit copies the input's sign).
+
 HCA ([ANAT] bullet "Heavily Compressed Attention (HCA)"): hca_compress pools each block of m = 128
 tokens with no overlap (reading: the CSA pooling over the entry's own block); dense_attention
 attends to every visible entry plus the window.
 
 Parity status: every function here is pinned by the CPU tests (closed forms, invariants, a dense
-attention routine, hand-worked examples, the MXFP4 table of the OCP spec). What the pages leave open
+attention routine, hand-worked examples, the MXFP4 table and conversion rule of the OCP spec). What the pages leave open
 (the readings above) cannot be pinned against DeepSeek's own layer: that part is parity unpinned.
 """
 from __future__ import annotations
@@ -116,6 +121,46 @@ def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     D = vals.shape[-1]
     vals = vals.reshape(vals.shape[:-1] + (D // 32, 32)) * scale[..., None]
     return vals.reshape(vals.shape[:-2] + (D,))
+
+
+def mxfp4_quantize(x: np.ndarray):
+    """float values [..., D] (D % 32 == 0) -> MXFP4 (codes [..., D/2], scales [..., D/32]), the layout
+    of mxfp4_decode.
+
+    The conversion of a block of 32 values in the OCP Microscaling Formats v1.0 spec: the shared scale
+    is 2**X with X = floor(log2(max |x|)) - 2, 2 being the largest exponent an e2m1 element has, kept
+    inside the e8m0 range [-127, 127] (a block of zeros takes X = -127); every element x / 2**X goes to
+    the nearest e2m1 value, ties to the one whose mantissa bit is 0, and magnitudes past 6 saturate to
+    6. The pages keep indexer keys as 128 FP4 numbers plus one scale byte per 32 ([ANAT] "The KV cache,
+    recomputed") and run the indexer's query-key product in FP4 ([ANAT] "Precision: FP8 everywhere,
+    FP4 experts").
+    Readings: the sign bit is the sign of x, so a negative value that rounds to zero is stored as -0
+    (code 8); the values quantised are those of the storage type (bf16-rounded where the layer stores
+    bf16), as a separate pass over the stored keys would see them.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    if D % 32:
+        raise ValueError("MXFP4 blocks need D % 32 == 0")
+    blocks = x.reshape(x.shape[:-1] + (D // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(amax)                     # amax = f * 2**e, f in [0.5, 1): floor(log2 amax) = e - 1
+    X = np.where(amax > 0, e.astype(np.int64) - 1 - 2, -127)
+    X = np.clip(X, -127, 127)
+    v = blocks / np.ldexp(1.0, X)[..., None]  # exact: a power of two
+    dist = np.abs(np.abs(v)[..., None] - E2M1_MAGNITUDE)       # [..., 32, 8]
+    nearest = dist == dist.min(axis=-1, keepdims=True)
+    even = nearest & (np.arange(8) % 2 == 0)
+    code = np.where(even.any(axis=-1), even.argmax(axis=-1), nearest.argmax(axis=-1)).astype(np.uint8)
+    code |= np.where(np.signbit(blocks), 8, 0).astype(np.uint8)
+    code = code.reshape(x.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
+
+
+def mxfp4_round(x: np.ndarray) -> np.ndarray:
+    """The values x takes once stored as MXFP4 (mxfp4_quantize, then mxfp4_decode)."""
+    return mxfp4_decode(*mxfp4_quantize(x))
 
 
 # e4m3 (OCP 8-bit Floating Point Specification, E4M3): bit 7 sign, bits 6-3 exponent (bias 7), bits
@@ -470,6 +515,10 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None, fid=None):
     top-k, sparse attention over entries + window. query_rows selects which query rows to finish
     (all by default); every row still feeds the compressor and the window.
     Returns a dict with the projected parts, new entries/keys, scores, idx and out for query_rows.
+    With an MXFP4 indexer (wl.idx_dtype == "mxfp4") the key cache holds the MXFP4 form of every key
+    (the context's as generated, the chunk's new keys quantised from their stored values) and the
+    indexer queries are quantised the same way before the scores; keys_new stays the unquantised
+    stored key and keys_new_fp4 holds its (codes, scales).
     fid (optional) turns on QK-norm and partial RoPE: a dict with gamma_q, gamma_kv [D], eps,
     rope_dims, theta. Queries, new entries and the chunk's raw KV are then RMS-normalised and
     rotated (queries at their positions, raw KV at its token's position, entries at
@@ -511,13 +560,20 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None, fid=None):
     if fid is not None:
         new_e = _store(rope(rms_norm(new_e, fid["gamma_kv"], fid["eps"]), entry_positions(first, len(new_e), m),
                             fid["rope_dims"], fid["theta"]), bf)
+    fp4 = wl.idx_dtype == "mxfp4"
+    new_k_fp4 = mxfp4_quantize(new_k) if fp4 else None
+    keys_new = mxfp4_decode(*new_k_fp4) if fp4 else new_k   # what the key cache holds
+    if fp4:
+        q_idx = mxfp4_round(q_idx)
     if L > 0:
         entries = np.concatenate([_val(inp["entries_prefix"][b], bf), new_e], axis=0)
-        keys = np.concatenate([_val(inp["keys_prefix"][b], bf), new_k], axis=0)
+        kp = (mxfp4_decode(inp["keys_prefix_codes"][b], inp["keys_prefix_scales"][b]) if fp4
+              else _val(inp["keys_prefix"][b], bf))
+        keys = np.concatenate([kp, keys_new], axis=0)
         raw = np.concatenate([_val(inp["win_prefix"][b], bf), parts["kv"]], axis=0)
         raw_pos0 = L - (wl.W - 1)
     else:
-        entries, keys, raw, raw_pos0 = new_e, new_k, parts["kv"], 0
+        entries, keys, raw, raw_pos0 = new_e, keys_new, parts["kv"], 0
 
     q_pos = L + rows
     nv = n_visible(q_pos, m)
@@ -526,7 +582,7 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None, fid=None):
     out = sparse_attention(q, entries, idx, raw, raw_pos0, q_pos, wl.W, sink=sink)
     if fid is not None:
         out = rope(out, q_pos, fid["rope_dims"], fid["theta"], inverse=True)
-    return dict(parts=parts, q=q, q_idx=q_idx, entries_new=new_e, keys_new=new_k,
+    return dict(parts=parts, q=q, q_idx=q_idx, entries_new=new_e, keys_new=new_k, keys_new_fp4=new_k_fp4,
                 entries=entries, keys=keys, raw=raw, raw_pos0=raw_pos0, rows=rows, q_pos=q_pos,
                 n_vis=nv, scores=scores, idx=idx, out=out)
 

@@ -128,7 +128,11 @@ def make_inputs(wl: Workload) -> dict:
             assert wl.L % m == 0
             n0 = wl.L // m
             out["entries_prefix"] = _act(s, "entries_prefix", (B, n0, D), wl)
-            out["keys_prefix"] = _act(s, "keys_prefix", (B, n0, DI), wl)
+            if wl.idx_dtype == "mxfp4":
+                out["keys_prefix_codes"], out["keys_prefix_scales"] = mxfp4_encode(
+                    normal_f32(s, "keys_prefix", (B, n0, DI)))
+            else:
+                out["keys_prefix"] = _act(s, "keys_prefix", (B, n0, DI), wl)
             out["win_prefix"] = _act(s, "win_prefix", (B, wl.W - 1, D), wl)
             out["halo"] = _act(s, "halo", (B, m, 2 * D + 2 * DI), wl)
     else:

@@ -86,6 +86,83 @@ def test_mxfp4_encoder_roundtrip_error_bound():
     assert np.all(err[np.abs(x) <= 6 * scale] <= 1.0)
 
 
+def _unpack_codes(packed):
+    packed = np.asarray(packed, dtype=np.uint8)
+    return np.stack([packed & 15, packed >> 4], axis=-1).reshape(packed.shape[:-1] + (2 * packed.shape[-1],))
+
+
+def test_mxfp4_quantize_hand_blocks():
+    # blocks worked by hand from the OCP conversion rule: scale choice, ties to even, saturation,
+    # signed zero, clamping of the shared exponent at both ends of the e8m0 range
+    g = _gold("mxfp4_quantize_hand.json")
+    for i, blk in enumerate(g["blocks"]):
+        codes, scales = O.mxfp4_quantize(np.array(blk["x"], dtype=np.float64)[None])
+        assert scales[0, 0] == blk["scale"], (i, scales[0, 0])
+        np.testing.assert_array_equal(_unpack_codes(codes)[0], blk["codes"], err_msg=f"block {i}")
+
+
+def test_mxfp4_quantize_fixed_points():
+    # every MXFP4 value is its own quantisation: a block holding all 16 codes (its largest magnitude
+    # 6 * 2**X puts the shared exponent back at X) comes back unchanged, for every finite scale byte
+    codes = np.tile(np.arange(16, dtype=np.uint8), 2)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    for s in range(0, 254):
+        x = O.mxfp4_decode(packed[None], np.array([[s]], dtype=np.uint8))
+        c2, s2 = O.mxfp4_quantize(x)
+        assert s2[0, 0] == s
+        np.testing.assert_array_equal(c2[0], packed)
+
+
+def test_mxfp4_quantize_is_a_nearest_rounding_brute_force():
+    # each element goes to a nearest value among all 16 codes under the block's scale; on an exact
+    # tie the chosen code has mantissa bit 0; past 6 * scale it saturates to 6 * scale
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((400, 64)) * np.exp2(rng.integers(-20, 20, size=(400, 1)))
+    # exact halfway points and saturating values, placed inside blocks whose max sets a known scale
+    x[:50, :8] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]) * np.exp2(rng.integers(-5, 5, size=(50, 1)))
+    x[:50, 8:32] = 0.0
+    codes, scales = O.mxfp4_quantize(x)
+    got = O.mxfp4_decode(codes, scales)
+    scale = np.repeat(np.ldexp(1.0, scales.astype(int) - 127), 32, axis=-1)
+    allv = O.e2m1_decode(np.arange(16))                          # [16]
+    cand = allv[None, None, :] * scale[..., None]                # [R, D, 16]
+    d = np.abs(cand - x[..., None])
+    best = d.min(axis=-1)
+    np.testing.assert_array_equal(np.abs(got - x), best)
+    c = _unpack_codes(codes)
+    n_near = ((d == best[..., None]) & (np.abs(cand) != 0)).sum(axis=-1)   # +-0 count once
+    tie = n_near >= 2
+    assert tie.sum() > 50
+    assert np.all((c[tie] & 1) == 0)
+    # the scale is the one the rule fixes: max |x| / 2**X in [4, 8)
+    amax = np.abs(x.reshape(400, 2, 32)).max(axis=-1)
+    ratio = amax / np.ldexp(1.0, scales.astype(int) - 127)
+    assert np.all((ratio >= 4) & (ratio < 8))
+
+
+def test_mxfp4_quantize_sign_and_scale_symmetry():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((64, 128))
+    c, s = O.mxfp4_quantize(x)
+    cn, sn = O.mxfp4_quantize(-x)
+    np.testing.assert_array_equal(sn, s)
+    np.testing.assert_array_equal(cn, c ^ 0x88)
+    for j in (-9, -1, 1, 7):
+        cj, sj = O.mxfp4_quantize(x * 2.0 ** j)
+        np.testing.assert_array_equal(cj, c)
+        np.testing.assert_array_equal(sj.astype(int), s.astype(int) + j)
+
+
+def test_mxfp4_quantize_agrees_with_the_generator_encoder_on_values():
+    # the generator's encoder is a separate implementation (edge comparisons instead of a nearest
+    # search); they may differ only in the sign of a zero
+    x = G.normal_f32(13, "k", (256, 128)).astype(np.float64)
+    co, so = O.mxfp4_quantize(x)
+    cg, sg = G.mxfp4_encode(x.astype(np.float32))
+    np.testing.assert_array_equal(so, sg)
+    np.testing.assert_array_equal(O.mxfp4_decode(co, so), O.mxfp4_decode(cg, sg))
+
+
 # ---------------------------------------------------------------------------------- compressor
 
 
