@@ -38,6 +38,11 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA prefill tok/s & decode step µs at 128K/1M ctx; % of HBM/MFMA roofline"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
+# The FP4 indexer's ceiling set by its vector ALU work: w_h * ReLU(s) is one max and one fma per (query,
+# entry, head), 2 * 64 = 128 lane operations per pair; 256 CUs x 64 lanes x 2.4 GHz of fp32 VALU
+# (non-packed) give 39.3 T lane-ops/s, i.e. 307 G pairs/s, against 16384 algorithmic flops per pair.
+VALU_BOUND_FP4_INDEX_TFLOPS = 256 * 64 * 2.4e9 / 128 * 16384 / 1e12
 MALL_FLUSH_BYTES = 512 << 20  # larger than the 256 MB Infinity Cache
 KERNEL_SOURCES = ("csrc/index.hip", "csrc/topk_wave.h", "csrc/common.h")
 
@@ -203,7 +208,7 @@ def mfma_summary(pmc_dir, workload):
 
 def cpu_baseline(wl, inp):
     """The oracle, as it stands, on a bounded sample of the workload: the per-chunk work (projection
-    of the compressor and window columns, both compressors) plus 4 and then 12 query rows; per-row
+    of the compressor and window columns, both compressors) plus 48 and then 160 query rows; per-row
     and per-chunk times are separated from the two runs and scaled to the whole chunk."""
     from oracle import csa_oracle as O
     try:
@@ -211,8 +216,8 @@ def cpu_baseline(wl, inp):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count()
-    rows_a = np.linspace(0, wl.T - 1, 4).astype(int)
-    rows_b = np.linspace(0, wl.T - 1, 12).astype(int)
+    rows_a = np.linspace(0, wl.T - 1, 48).astype(int)
+    rows_b = np.linspace(0, wl.T - 1, 160).astype(int)
     t0 = time.perf_counter()
     O.prefill(inp, wl, query_rows=rows_a)
     t1 = time.perf_counter()
@@ -222,12 +227,15 @@ def cpu_baseline(wl, inp):
     fixed = max((t1 - t0) - len(rows_a) * per_row, 0.0)
     est = fixed + wl.T * per_row
     return {"value": wl.B * wl.T / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{wl.name}: oracle prefill with 4 and with 12 of the {wl.T} query rows "
+            "sample": f"{wl.name}: oracle prefill with {len(rows_a)} and with {len(rows_b)} of the {wl.T} query rows "
                       f"({t1 - t0:.1f} s + {t2 - t1:.1f} s); per-row {per_row * 1e3:.1f} ms and per-chunk "
                       f"{fixed:.1f} s scaled to all {wl.T} rows = {est:.0f} s per chunk"}
 
 
-def bench_prefill(wl, steps, warmup):
+def bench_prefill(wl, steps, warmup, extra_legs=True):
+    """The layer's step on wl's chunk, the indexer and the attention kernels alone (same arguments and
+    launch configuration as inside the step); with extra_legs also the step with QK-norm + RoPE, over
+    584-byte FP8 entry records, and with the MXFP4 indexer key cache."""
     import torch
     from compressed_sparse_attention_05_amd import layer, lib
     from synth import gen as G
@@ -278,6 +286,39 @@ def bench_prefill(wl, steps, warmup):
     run_attn()
     torch.cuda.synchronize()
     attn_ms = timed_events(run_attn, steps, torch.cuda.synchronize)
+    if not extra_legs:
+        return dict(inp=inp, ms_per_step=ms_per_step, step_ms=step_ms, idx_ms=idx_ms, attn_ms=attn_ms)
+
+    # the same step with the MXFP4 indexer: keys cached as e2m1 codes + e8m0 scales, the queries
+    # quantised in the step, the fused FP4 indexer; the context keys are the bf16 keys quantised
+    st4 = layer.CSAPrefill(d, wl.B, wl.T, wl.d, wl.n_cap, dtype=torch.bfloat16, out_dtype=torch.float32,
+                           fp4_keys=True)
+    if wl.L > 0:
+        n0 = wl.L // wl.m
+        for b in range(wl.B):
+            lib.csa_mxfp4_quantize(st.keys[b, :n0], st4.keys[b, :n0], st4.key_scales[b, :n0])
+        st4.entries[:, :n0] = st.entries[:, :n0]
+        st4.win[:, : wl.W - 1] = act(inp["win_prefix"], wl)
+        st4.halo.copy_(st.halo)
+    for _ in range(warmup):
+        st4(weights, x, wl.L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    timed_events(lambda: st4(weights, x, wl.L), steps, torch.cuda.synchronize)
+    fp4_ms = (time.perf_counter() - t0) * 1e3 / steps
+    P4 = st4.fwd.projection()
+    qi4 = P4[:, c_qi:c_qi + wl.H_I * wl.D_I]
+    qc, qsc = lib.csa_mxfp4_quantize(qi4)
+    qc = qc.view(wl.B, wl.T, wl.H_I, wl.D_I // 2)
+    qsc = qsc.view(wl.B, wl.T, wl.H_I, wl.D_I // 32)
+    idx4 = torch.empty_like(st4.idx)
+    run_idx4 = lambda: lib.csa_index_topk(d, qc, w_head, st4.keys, idx4, q_pos0=qp, q_scale=qsc, k_scale=st4.key_scales)
+    run_idx4()
+    torch.cuda.synchronize()
+    idx4_ms = timed_events(run_idx4, steps, torch.cuda.synchronize)
+    assert torch.equal(idx4, st4.idx), "FP4 index kernel alone disagrees with the step"
+    del st4, P4, qi4, qc, qsc, idx4
+    torch.cuda.empty_cache()
 
     # the same step with QK-norm and partial RoPE on (gains from the seeded generator)
     w_fid = dict(weights, **fid_device(wl.D))
@@ -305,7 +346,7 @@ def bench_prefill(wl, steps, warmup):
     timed_events(lambda: sr(w_fid, x, wl.L), steps, torch.cuda.synchronize)
     rec_ms = (time.perf_counter() - t0) * 1e3 / steps
     return dict(inp=inp, ms_per_step=ms_per_step, step_ms=step_ms, idx_ms=idx_ms, attn_ms=attn_ms, fid_ms=fid_ms,
-                rec_ms=rec_ms)
+                rec_ms=rec_ms, fp4_ms=fp4_ms, idx4_ms=idx4_ms)
 
 
 def fid_device(D):
@@ -366,6 +407,46 @@ def bench_decode(name, steps, warmup, fid=False):
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "B": wl.B, "context_tokens": wl.L, "top_k": wl.k, "indexer": "mxfp4" if fp4 else "bf16",
             "mall": "512 MiB read between steps, outside the timed events"}
+
+
+def host_info():
+    """Host cores, CPU model and the BLAS NumPy calls (for the oracle baselines)."""
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 1))
+    except Exception:
+        pass
+    return info
+
+
+def cpu_baseline_decode(name):
+    """The oracle's decode step (float64, as it stands) on one sequence of the batch, scaled by the batch
+    size: every sequence of a decode batch is the same work."""
+    from oracle import csa_oracle as O
+    from synth import gen as G
+    from synth.workloads import get
+    wl = get(name)
+    wl1 = wl.with_(B=1)
+    inp = G.make_inputs(wl1)
+    t0 = time.perf_counter()
+    O.decode(inp, wl1, 0)
+    dt = time.perf_counter() - t0
+    hi = host_info()
+    return {"value": round(dt * wl.B * 1e6, 1), "unit": "µs/step", "cores": hi.get("blas_threads", hi["os_cpu_count"]),
+            "kind": "oracle", "sample": f"{name}: the oracle's decode of 1 of the {wl.B} sequences "
+                                        f"({dt:.2f} s) x {wl.B}", "host": hi}
 
 
 def bench_decode_state(steps, warmup):
@@ -498,6 +579,20 @@ def bench_hca(steps, warmup):
     return out
 
 
+def prefill_record(wl, steps, warmup):
+    """Step time and the indexer / attention kernels' roofline fractions of a prefill workload."""
+    r = bench_prefill(wl, steps, warmup, extra_legs=False)
+    ms = r["ms_per_step"]
+    flops_idx = index_pairs(wl) * wl.H_I * wl.D_I * 2
+    flops_attn = attn_pairs(wl) * wl.H * wl.D * 4
+    idx_ms, attn_ms = float(np.mean(r["idx_ms"])), float(np.mean(r["attn_ms"]))
+    kern = lambda f, t: {"avg_launch_ms": round(t, 3), "algorithmic_flops": f, "tflops": round(f / (t * 1e-3) / 1e12, 1),
+                         "frac_bf16_peak": round(f / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return {"workload": f"{wl.name}: {wl.T} tokens from position 0, H={wl.H}, k={wl.k}",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(wl.B * wl.T / (ms * 1e-3), 1),
+            "index_prefill_mfma": kern(flops_idx, idx_ms), "sparse_attn_mfma": kern(flops_attn, attn_ms)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -507,6 +602,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hca", action="store_true", help="skip the HCA legs")
+    ap.add_argument("--no-prefill8k", action="store_true", help="skip the prefill8k sub-record")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise four rocprofv3 --pmc runs under DIR")
     ap.add_argument("--mfma-summary", metavar="DIR", help="summarise one rocprofv3 --pmc run of the MFMA busy counter")
@@ -534,7 +630,7 @@ def main():
     wl = get(args.workload)
     if wl.kind != "prefill":
         raise SystemExit("--workload must be a prefill workload (tiny, prefill8k, chunk1m)")
-    r = bench_prefill(wl, args.steps, args.warmup)
+    r = bench_prefill(wl, args.steps, args.warmup, extra_legs=wl.name != "tiny")
     ms = r["ms_per_step"]
     flops_idx = index_pairs(wl) * wl.H_I * wl.D_I * 2
     flops_attn = attn_pairs(wl) * wl.H * wl.D * 4
@@ -573,12 +669,24 @@ def main():
                      "layer_tflops": round((flops_idx + flops_attn + flops_proj) / (ms * 1e-3) / 1e12, 1)},
         },
     }
+    idx4_ms = float(np.mean(r["idx4_ms"]))
+    ach4 = flops_idx / (idx4_ms * 1e-3) / 1e12
+    res["fp4_indexer"] = {
+        "what": "the same step with the MXFP4 indexer (keys cached as e2m1 codes + e8m0 scales, queries "
+                "quantised in the step, fused index_prefill_fp4)",
+        "ms_per_step": round(r["fp4_ms"], 3), "tokens_per_s": round(wl.B * wl.T / (r["fp4_ms"] * 1e-3), 1),
+        "index_kernel": {"name": "index_prefill_fp4", "avg_launch_ms": round(idx4_ms, 3),
+                         "algorithmic_flops": flops_idx, "tflops": round(ach4, 1),
+                         "frac_fp4_peak": round(ach4 / PEAK_FP4_TFLOPS, 4),
+                         "frac_valu_bound": round(ach4 / VALU_BOUND_FP4_INDEX_TFLOPS, 4)}}
     res["fid"] = {"what": "the same step with QK-norm (RMS norm with gains) and RoPE on the last 64 dims, "
                           "output rotated back",
                   "ms_per_step": round(r["fid_ms"], 3), "tokens_per_s": round(wl.B * wl.T / (r["fid_ms"] * 1e-3), 1),
                   "overhead_frac": round(r["fid_ms"] / ms - 1.0, 4),
                   "fp8_records_ms_per_step": round(r["rec_ms"], 3),
                   "fp8_records_tokens_per_s": round(wl.B * wl.T / (r["rec_ms"] * 1e-3), 1)}
+    if not args.no_prefill8k and wl.name != "prefill8k":
+        res["prefill8k"] = prefill_record(get("prefill8k"), args.steps, args.warmup)
     if not args.no_decode:
         res["decode"] = {n: bench_decode(n, max(args.steps, 10), 3) for n in ("decode128k", "decode1m_fp4")}
         dfid = bench_decode("decode128k", max(args.steps, 10), 3, fid=True)
@@ -589,6 +697,11 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, r["inp"])
+        res["cpu_baseline"]["host"] = host_info()
+        if not args.no_decode:
+            for n in ("decode128k", "decode1m_fp4"):
+                log(f"cpu baseline (oracle) {n}")
+                res["decode"][n]["cpu_baseline"] = cpu_baseline_decode(n)
     print(json.dumps(res), flush=True)
 
 

@@ -245,14 +245,18 @@ int validate_index(const csa_dims* d, int B, int T, const int64_t* q_pos, int id
 // Workspace of csa_decode_step: the normalised / rotated query, the selected indices, and the index
 // / attention scratch.
 struct DecodeWs {
-  size_t q, idx, scratch, total;
+  size_t q, idx, qi, qis, scratch, total;
 };
+// q | idx | the indexer query in MXFP4 (codes, scales; used by MXFP4 key states) | scratch
 DecodeWs decode_ws(const csa_dims* d, int B, int64_t n_cap, int dtype) {
   const size_t es = dtype == CSA_F32 ? 4 : 2;
+  const size_t nqi = (size_t)B * d->H_I * d->D_I;
   DecodeWs w{};
   w.q = 0;
   w.idx = w.q + align256((size_t)B * d->H * d->D * es);
-  w.scratch = w.idx + align256((size_t)B * d->top_k * 4);
+  w.qi = w.idx + align256((size_t)B * d->top_k * 4);
+  w.qis = w.qi + align256(nqi / 2);
+  w.scratch = w.qis + align256(nqi / 32);
   IndexArgs ia = make_index_args(d, B, 1, nullptr, dtype, nullptr, 0, 0, nullptr, nullptr, 0, nullptr, 0, nullptr,
                                  n_cap, nullptr, nullptr);
   const size_t iw = index_topk_workspace(ia);
@@ -268,6 +272,7 @@ DecodeWs hca_decode_ws(const csa_dims* d, int B, int64_t n_cap, int dtype) {
   DecodeWs w{};
   w.q = 0;
   w.idx = align256((size_t)B * d->H * d->D * es);
+  w.qi = w.qis = w.idx;
   w.scratch = w.idx;
   AttnArgs a = sizing_attn(d, B, 1, dtype);
   a.dense = 1;
@@ -366,7 +371,8 @@ int compress_call(const char* name, bool overlap, int B, int T, const int64_t* p
   if (ld < c) return fail(CSA_ERR_ARG, "ld=%lld < c=%d", (long long)ld, c);
   if (B > 1 && seq_stride < (int64_t)T * ld) return fail(CSA_ERR_ARG, "seq_stride too small");
   const bool records = epi && epi->records;
-  if (B > 1 && entries_seq_stride < n_cap * (records ? (int64_t)kEntryRecordBytes : c))
+  const bool fp4 = epi && epi->fp4_codes;  // MXFP4 rows [B, n_cap, c/2] + scales, contiguous
+  if (!fp4 && B > 1 && entries_seq_stride < n_cap * (records ? (int64_t)kEntryRecordBytes : c))
     return fail(CSA_ERR_ARG, "entries_seq_stride too small");
   if (overlap && pos0) {
     if (!halo_cb || !halo_zb)
@@ -403,7 +409,8 @@ int compress_call(const char* name, bool overlap, int B, int T, const int64_t* p
   a.aligned16 = aligned(ca, 16) && aligned(za, 16) && aligned(cb, 16) && aligned(zb, 16) && aligned(a.halo_cb, 16) &&
                 aligned(a.halo_zb, 16) && aligned(entries, 16);
   if (a.epilogue && !compress_epilogue_ok(a))
-    return fail(CSA_ERR_UNSUPPORTED, "%s: entry norm / RoPE / records need one entry per wave (c / vector <= 64)", name);
+    return fail(CSA_ERR_UNSUPPORTED, "%s: entry norm / RoPE / records / MXFP4 keys need one entry per wave "
+                "(c / vector <= 64, 16-byte aligned rows)", name);
   return hip_status(launch_compress(a, static_cast<hipStream_t>(stream)), name);
 }
 
@@ -450,7 +457,8 @@ int norm_rope_call(int B, int R, int H, int D, int dtype, const void* x, int64_t
 // Shared by csa_decode_step and csa_hca_decode_step: checks and the append launch.
 int decode_append(const char* name, const csa_dims* dims, const csa_weights* w, int B, const int64_t* pos, int dtype,
                   const void* q, const void* kv, const void* comp, const csa_decode_state* st, bool hca, void* qn,
-                  hipStream_t s) {
+                  hipStream_t s, const void* q_idx = nullptr, uint8_t* qi_codes = nullptr,
+                  uint8_t* qi_scales = nullptr) {
   AppendArgs a{};
   a.B = B;
   a.m = dims->m;
@@ -482,6 +490,15 @@ int decode_append(const char* name, const csa_dims* dims, const csa_weights* w, 
   a.theta = w->rope_theta;
   a.aligned16 = aligned(comp, 16) && aligned(st->block, 16) && aligned(st->entries, 16) &&
                 (hca || aligned(st->keys, 16));
+  if (!hca && st->key_fmt) {
+    a.key_fmt = 1;
+    a.key_scales = static_cast<uint8_t*>(st->key_scales);
+    a.q_idx = q_idx;
+    a.H_I = dims->H_I;
+    a.qi_codes = qi_codes;
+    a.qi_scales = qi_scales;
+    a.aligned16 = a.aligned16 && aligned(q_idx, 16);
+  }
   return hip_status(launch_append(a, s), name);
 }
 
@@ -495,6 +512,12 @@ int check_decode_state(const csa_dims* dims, const csa_weights* w, int B, const 
   if (st->n_cap < 1 || st->n_cap > 0x7FFFFFFFLL) return fail(CSA_ERR_ARG, "state n_cap out of range");
   if (!st->entries || !st->win || !st->block || (!hca && !st->keys)) return fail(CSA_ERR_ARG, "NULL state pointer");
   if (st->entry_fmt != 0 && st->entry_fmt != 1) return fail(CSA_ERR_ARG, "entry_fmt must be 0 or 1");
+  if (!hca && st->key_fmt != 0) {
+    if (st->key_fmt != 1) return fail(CSA_ERR_ARG, "key_fmt must be 0 or 1");
+    if (!st->key_scales) return fail(CSA_ERR_ARG, "MXFP4 keys need key_scales");
+    if (dims->D_I % 32 || dims->D_I > append_max_dim()) return fail(CSA_ERR_ARG, "MXFP4 keys need D_I %% 32 == 0");
+    if (!aligned(st->keys, 16)) return fail(CSA_ERR_ARG, "MXFP4 key codes must be 16-byte aligned");
+  }
   if (st->entry_fmt && (dims->D != 512 || dtype != CSA_BF16))
     return fail(CSA_ERR_ARG, "entry records hold D = 512 and take bf16 entries");
   if (dims->D > append_max_dim() || dims->D % 2) return fail(CSA_ERR_UNSUPPORTED, "D must be even and <= %d", append_max_dim());
@@ -507,7 +530,7 @@ int check_decode_state(const csa_dims* dims, const csa_weights* w, int B, const 
 
 extern "C" {
 
-int csa_version(void) { return 2; }
+int csa_version(void) { return 3; }
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
@@ -565,8 +588,9 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
         const size_t at = attn_workspace(sizing_attn(dims, B, T, idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16));
         size_t scratch = need > at ? need : at;  // index / attention scratch, or the projection's
         if (idx_dtype == CSA_BF16 && scratch < kGemmWorkspace) scratch = kGemmWorkspace;
+        const size_t nqi = (size_t)B * T * dims->H_I * dims->D_I;
         need = align256((size_t)B * T * n_tot_of(dims) * es) + align256((size_t)B * T * dims->top_k * 4) +
-               align256(scratch);
+               align256(nqi / 2) + align256(nqi / 32) + align256(scratch);
       }
       *bytes = (int64_t)need;
       return CSA_OK;
@@ -684,6 +708,25 @@ int csa_entry_pack(int B, int N, int in_dtype, const void* entries, int64_t ld, 
   return hip_status(launch_entry_pack(a, static_cast<hipStream_t>(stream)), "csa_entry_pack");
 }
 
+int csa_mxfp4_quantize(int64_t R, int D, int dtype, const void* x, int64_t ld, void* codes, void* scales,
+                       void* stream) {
+  if (R < 0 || D < 1 || D % 32) return fail(CSA_ERR_ARG, "need R >= 0 and D a positive multiple of 32");
+  if (!is_act_dtype(dtype)) return fail(CSA_ERR_ARG, "dtype must be F32 or BF16");
+  if (ld < D) return fail(CSA_ERR_ARG, "ld < D");
+  if (R == 0) return CSA_OK;
+  if (!x || !codes || !scales) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  if (!aligned(codes, 4) || !aligned(x, esize(dtype))) return fail(CSA_ERR_ARG, "misaligned x or codes");
+  QuantArgs a{};
+  a.R = R;
+  a.D = D;
+  a.dtype = dtype;
+  a.x = x;
+  a.ld = ld;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.scales = static_cast<uint8_t*>(scales);
+  return hip_status(launch_mxfp4_quant(a, static_cast<hipStream_t>(stream)), "csa_mxfp4_quantize");
+}
+
 int csa_norm_rope(int B, int R, int H, int D, int dtype, const void* x, int64_t x_ld, int64_t x_seq_stride, void* y,
                   int64_t y_ld, int64_t y_seq_stride, const float* gamma, float eps, int rope_dims, float rope_theta,
                   const int64_t* pos0, int64_t pos_off, int64_t pos_step, int inverse, void* stream) {
@@ -709,14 +752,21 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, const int
   const bool qfid = w->gamma_q || w->rope_dims > 0;
   // the token joins the state; a completed block's entry and key are pooled; the query is
   // normalised and rotated at its position
-  rc = decode_append("csa_decode_step", dims, w, B, pos, dtype, q, kv, comp, st, false, qfid ? base + L.q : nullptr, s);
+  // (and, for MXFP4 keys, the indexer query is quantised)
+  const bool kfp4 = st->key_fmt != 0;
+  rc = decode_append("csa_decode_step", dims, w, B, pos, dtype, q, kv, comp, st, false, qfid ? base + L.q : nullptr, s,
+                     q_idx, base + L.qi, base + L.qis);
   if (rc) return rc;
   const void* qq = qfid ? base + L.q : q;
   int32_t* idx = out_idx ? out_idx : reinterpret_cast<int32_t*>(base + L.idx);
   void* scratch = base + L.scratch;
   const size_t scratch_bytes = L.total - L.scratch;
-  rc = csa_index_topk(dims, B, 1, pos, dtype, q_idx, (int64_t)HI * DI, (int64_t)HI * DI, nullptr, w->w_head, 0,
-                      st->keys, n_cap * DI, nullptr, n_cap, idx, nullptr, scratch, scratch_bytes, stream);
+  if (kfp4)
+    rc = csa_index_topk(dims, B, 1, pos, CSA_MXFP4, base + L.qi, 0, 0, base + L.qis, w->w_head, 0, st->keys, 0,
+                        st->key_scales, n_cap, idx, nullptr, scratch, scratch_bytes, stream);
+  else
+    rc = csa_index_topk(dims, B, 1, pos, dtype, q_idx, (int64_t)HI * DI, (int64_t)HI * DI, nullptr, w->w_head, 0,
+                        st->keys, n_cap * DI, nullptr, n_cap, idx, nullptr, scratch, scratch_bytes, stream);
   if (rc) return rc;
   // the window, read by the attention straight from the ring
   rc = attn_call("csa_decode_step", false, dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries,
@@ -810,15 +860,21 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, const 
   if (rc) return rc;
   const bool fid = fid_on(w);
   const bool records = cache->entry_fmt != 0;
+  const bool kfp4 = cache->key_fmt != 0;
   if (cache->entry_fmt != 0 && cache->entry_fmt != 1) return fail(CSA_ERR_ARG, "entry_fmt must be 0 or 1");
+  if (cache->key_fmt != 0 && cache->key_fmt != 1) return fail(CSA_ERR_ARG, "key_fmt must be 0 or 1");
+  if (kfp4 && (!cache->key_scales || DI % 32 || !aligned(cache->keys, 16)))
+    return fail(CSA_ERR_ARG, "MXFP4 keys need key_scales, D_I %% 32 == 0 and 16-byte aligned codes");
   if (records && (D != 512 || dtype != CSA_BF16)) return fail(CSA_ERR_ARG, "entry records hold D = 512 bf16 entries");
   const int64_t ntot = n_tot_of(dims);
   const int es = esize(dtype);
-  // workspace: P [B*T, ntot] | idx [B*T, k] | index / attention / projection scratch
-  IndexArgs probe = make_index_args(dims, B, T, pos0, dtype, nullptr, 0, 0, nullptr, nullptr, 0, nullptr, 0, nullptr,
-                                    cache->n_cap, nullptr, nullptr);
+  // workspace: P [B*T, ntot] | idx [B*T, k] | q_I in MXFP4 (codes, scales) | index / attention /
+  // projection scratch
+  IndexArgs probe = make_index_args(dims, B, T, pos0, kfp4 ? CSA_MXFP4 : dtype, nullptr, 0, 0, nullptr, nullptr, 0,
+                                    nullptr, 0, nullptr, cache->n_cap, nullptr, nullptr);
   const size_t p_bytes = align256((size_t)B * T * ntot * es);
-  const size_t i_bytes = align256((size_t)B * T * k * 4);
+  const size_t nqi = (size_t)B * T * HI * DI;
+  const size_t i_bytes = align256((size_t)B * T * k * 4) + align256(nqi / 2) + align256(nqi / 32);
   const size_t i_ws = index_topk_workspace(probe);
   const size_t a_ws = attn_workspace(sizing_attn(dims, B, T, dtype));
   size_t scratch = i_ws > a_ws ? i_ws : a_ws;
@@ -830,6 +886,8 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* P = static_cast<uint8_t*>(ws);
   int32_t* idx = out_idx ? out_idx : reinterpret_cast<int32_t*>(P + p_bytes);
+  uint8_t* qi_codes = P + p_bytes + align256((size_t)B * T * k * 4);
+  uint8_t* qi_scales = qi_codes + align256(nqi / 2);
   void* xws = P + p_bytes + i_bytes;
   auto col = [&](int64_t c) { return static_cast<void*>(P + c * es); };
   const int64_t c_ca = 0, c_za = D, c_cb = 2LL * D, c_zb = 3LL * D;
@@ -869,10 +927,15 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, const 
                      w->bias_a, w->bias_b, cache->entries,
                      cache->n_cap * (records ? (int64_t)kEntryRecordBytes : D), cache->n_cap, dtype, stream, &epi);
   if (rc) return rc;
+  // new indexer keys: rows of the activation dtype, or quantised to MXFP4 in the epilogue
+  CompressArgs kepi{};
+  kepi.epilogue = kfp4;
+  kepi.fp4_codes = kfp4 ? static_cast<uint8_t*>(cache->keys) : nullptr;
+  kepi.fp4_scales = kfp4 ? static_cast<uint8_t*>(cache->key_scales) : nullptr;
   rc = compress_call("csa_forward", true, B, T, pos0, m, DI, dtype, col(c_ica), col(c_iza), col(c_icb), col(c_izb),
                      ntot, (int64_t)T * ntot, halo ? halo + (size_t)2 * D * es : nullptr,
                      halo ? halo + (size_t)(2 * D + DI) * es : nullptr, halo_ld, (int64_t)m * halo_ld, w->ibias_a,
-                     w->ibias_b, cache->keys, cache->n_cap * DI, cache->n_cap, dtype, stream);
+                     w->ibias_b, cache->keys, cache->n_cap * DI, cache->n_cap, dtype, stream, &kepi);
   if (rc) return rc;
   // the chunk's raw KV goes to window rows [W-1, W-1+T) (normalised and rotated on the way when on)
   void* wrows = static_cast<uint8_t*>(cache->win) + (size_t)(W - 1) * D * es;
@@ -889,8 +952,23 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, const 
                         w->gamma_q, w->norm_eps, w->rope_dims, w->rope_theta, pos0, 0, 1, 0, stream);
     if (rc) return rc;
   }
-  rc = csa_index_topk(dims, B, T, pos0, dtype, col(c_qi), ntot, (int64_t)T * ntot, nullptr, w->w_head, 0, cache->keys,
-                      cache->n_cap * DI, nullptr, cache->n_cap, idx, nullptr, xws, x_bytes, stream);
+  if (kfp4) {  // the indexer queries to MXFP4, then the FP4 indexer
+    QuantArgs qa{};
+    qa.R = (int64_t)B * T;
+    qa.D = HI * DI;
+    qa.dtype = dtype;
+    qa.x = col(c_qi);
+    qa.ld = ntot;
+    qa.codes = qi_codes;
+    qa.scales = qi_scales;
+    e = launch_mxfp4_quant(qa, s);
+    if (e != hipSuccess) return hip_status(e, "csa_forward: q_I quantisation");
+    rc = csa_index_topk(dims, B, T, pos0, CSA_MXFP4, qi_codes, 0, 0, qi_scales, w->w_head, 0, cache->keys, 0,
+                        cache->key_scales, cache->n_cap, idx, nullptr, xws, x_bytes, stream);
+  } else {
+    rc = csa_index_topk(dims, B, T, pos0, dtype, col(c_qi), ntot, (int64_t)T * ntot, nullptr, w->w_head, 0,
+                        cache->keys, cache->n_cap * DI, nullptr, cache->n_cap, idx, nullptr, xws, x_bytes, stream);
+  }
   if (rc) return rc;
   // window row r of sequence b holds position pos0[b] - (W - 1) + r
   rc = attn_call("csa_forward", false, dims, B, T, pos0, dtype, col(c_q), ntot, (int64_t)T * ntot, cache->entries,

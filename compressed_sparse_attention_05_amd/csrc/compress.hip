@@ -12,6 +12,7 @@
 // needed. A thread owns VEC consecutive channels of one entry and issues 16-byte loads along the
 // channel axis (coalesced across the threads of a row).
 #include "kernels.h"
+#include "mx.h"
 #include "pool.h"
 #include "record.h"
 #include "rope.h"
@@ -118,7 +119,8 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     // The cv = c / V threads of one entry are consecutive lanes of one wave (G = 1, cv a power of two
     // <= 64). The entry is rounded to its storage type, RMS-normalised (gain gamma) and turned by RoPE
     // at its block's last token, (i + 1) m - 1, as a separate pass over the stored entry would; then
-    // stored, or packed into its 584-byte record (cv = 64: lane l holds dims 8l .. 8l + 7).
+    // stored, packed into its 584-byte record (cv = 64: lane l holds dims 8l .. 8l + 7), or (indexer
+    // keys) quantised to MXFP4.
     const bool bf = a.out_dtype == CSA_BF16;
     if (bf) {
 #pragma unroll
@@ -159,6 +161,15 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
 #pragma unroll
       for (int v = 0; v < V; ++v) out[v] = bf2f(f2bf(out[v]));
     }
+    if (a.fp4_codes) {  // MXFP4 key: the 32 / V lanes of each block meet for its maximum
+      if constexpr (V == 4 || V == 8) {
+        int X;
+        const uint32_t pk = mxfp4_quant_lanes<V>(out, X);
+        const int64_t r = (int64_t)b * a.n_cap + orow;
+        mxfp4_store_lanes<V>(a.fp4_codes + r * (a.c / 2), a.fp4_scales + r * (a.c / 32), j0, pk, X);
+      }
+      return;
+    }
     if (a.records) {
       if constexpr (V == 8) {
         pack_record_wave(out, static_cast<uint8_t*>(a.entries) + (int64_t)b * a.entries_seq_stride +
@@ -180,6 +191,7 @@ hipError_t launch_typed(const CompressArgs& a, hipStream_t s) {
   const int cv = a.c / V;
   // the epilogue's reductions need an entry's threads inside one wave
   if (a.epilogue && (cv > 64 || (cv & (cv - 1)) || (a.records && V != 8))) return hipErrorInvalidValue;
+  if (a.fp4_codes && (!a.epilogue || (V != 4 && V != 8) || a.c % 32)) return hipErrorInvalidValue;
   const int64_t threads = (int64_t)a.n_new * (a.c / V) * a.group;
   dim3 grid((unsigned)ceil_div(threads, 256), (unsigned)a.B);
   if (vec_ok) {
@@ -198,6 +210,7 @@ bool compress_epilogue_ok(const CompressArgs& a) {
   const int cv = a.c / V;
   if (a.m >= 64 || a.c % V || cv > 64 || (cv & (cv - 1))) return false;
   if (a.records && (a.c != 512 || V != 8 || a.out_dtype != CSA_BF16)) return false;
+  if (a.fp4_codes && (a.c % 32 || V == 1 || a.records)) return false;
   return true;
 }
 

@@ -16,10 +16,13 @@
 //        type, normalised and rotated at p (its block's last token) when on, and stored as a row
 //        or packed into a 584-byte record; the CSA indexer key is pooled the same way;
 //  * workgroups (1 .., b), when the query is normalised or rotated: four query heads each, one per
-//    wave, normalised and rotated at p into the caller's buffer.
+//    wave, normalised and rotated at p into the caller's buffer;
+//  * with an MXFP4 indexer, the pooled key is quantised (mx.h) into the key cache, and the last
+//    workgroups of each sequence quantise its indexer query, 2048 values each.
 // The pooling takes the rows in the order of the prefill compressor (compress.hip), so an entry
 // pooled here has the bits the chunked prefill gives it.
 #include "kernels.h"
+#include "mx.h"
 #include "pool.h"
 #include "record.h"
 #include "rope.h"
@@ -158,6 +161,19 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   const int m = a.m, D = a.D, DI = a.D_I;
   const double lt = a.rope_dims > 0 ? log2(a.theta) : 0.0;
 
+  const int nq = a.qn ? (a.H + kAppendThreads / 64 - 1) / (kAppendThreads / 64) : 0;
+  if ((int)blockIdx.x > nq) {  // the indexer query to MXFP4: 8 values per thread, 4 lanes per block
+    const int64_t n = (int64_t)a.H_I * DI;
+    const int64_t j0 = ((int64_t)(blockIdx.x - 1 - nq) * kAppendThreads + tid) * 8;
+    if (j0 >= n) return;  // whole blocks of 32: n is a multiple of 32
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i += VI::N) VI::load(a.q_idx, b * n + j0 + i, v + i);
+    int X;
+    const uint32_t pk = mxfp4_quant_lanes<8>(v, X);
+    mxfp4_store_lanes<8>(a.qi_codes + b * (n / 2), a.qi_scales + b * (n / 32), (int)j0, pk, X);
+    return;
+  }
   if (blockIdx.x > 0) {  // query heads, normalised and rotated at p
     const int h = (blockIdx.x - 1) * (kAppendThreads / 64) + wave;
     if (h >= a.H) return;
@@ -170,6 +186,7 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   }
 
   __shared__ float ent[1024];  // the pooled entry (D <= 1024)
+  __shared__ float kent[1024];  // the pooled indexer key when it is quantised (D_I <= 1024)
   const int64_t blk = p / m;
   const int r = (int)(p % m);
   const int64_t nc = a.hca ? 2LL * D : 4LL * D + 4LL * DI;
@@ -204,6 +221,7 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   const void* own = block + own_row0 * nc * es;
   const void* prev = (!a.hca && blk >= 1) ? block + (int64_t)((blk + 1) & 1) * m * nc * es : nullptr;
   const bool finish = a.entry_fmt != 0 || a.gamma_kv || a.rope_dims > 0;  // the entry passes through LDS
+  const bool kfp4 = !a.hca && a.key_fmt != 0;                              // so does an MXFP4 key
   for (int slot = tid / G; slot < nve + nvk; slot += kAppendThreads / G) {
     const int sub = tid % G;
     float out[V];
@@ -226,12 +244,32 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
       const int64_t c0 = 4LL * D;
       pool_entry<VI>(own, prev, nc, m, DI, c0, c0 + DI, c0 + 2LL * DI, c0 + 3LL * DI, a.ibias_a, a.ibias_b, j0, sub,
                      G, out);
-      if (sub == 0) VI::store(a.keys, ((int64_t)b * a.n_cap + blk) * DI + j0, out);
+      if (sub == 0) {
+        if (kfp4) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) kent[j0 + v] = DT == CSA_BF16 ? bf2f(f2bf(out[v])) : out[v];
+        } else {
+          VI::store(a.keys, ((int64_t)b * a.n_cap + blk) * DI + j0, out);
+        }
+      }
     }
   }
-  if (!finish) return;
+  if (!finish && !kfp4) return;
   __syncthreads();
-  if (wave != 0) return;
+  if (kfp4 && wave == 1) {  // the stored key to MXFP4: 4 dims per lane, 8 lanes per block of 32
+    const int64_t row = (int64_t)b * a.n_cap + blk;
+    for (int base = 0; base < DI; base += 256) {
+      const int j0 = base + 4 * lane;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = j0 + i < DI ? kent[j0 + i] : 0.f;
+      int X;
+      const uint32_t pk = mxfp4_quant_lanes<4>(v, X);
+      if (j0 < DI)
+        mxfp4_store_lanes<4>(static_cast<uint8_t*>(a.keys) + row * (DI / 2), a.key_scales + row * (DI / 32), j0, pk, X);
+    }
+  }
+  if (!finish || wave != 0) return;
   // wave 0: normalise and rotate the entry at p (its block's last token), then store or pack it
   float v[kMaxPer];
 #pragma unroll
@@ -260,7 +298,9 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
 template <int DT>
 hipError_t launch_typed(const AppendArgs& a, hipStream_t s) {
   const int nq = a.qn ? (int)ceil_div(a.H, kAppendThreads / 64) : 0;
-  const dim3 grid((unsigned)(1 + nq), (unsigned)a.B), block(kAppendThreads);
+  const int nqi = a.qi_codes ? (int)ceil_div((int64_t)a.H_I * a.D_I, kAppendThreads * 8) : 0;
+  if ((a.key_fmt != 0 && (a.hca || a.D_I % 32)) || (a.qi_codes && (a.H_I * a.D_I) % 32)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(1 + nq + nqi), (unsigned)a.B), block(kAppendThreads);
   constexpr int V = Vec<DT>::N;
   const bool vec = a.aligned16 && a.D % V == 0 && (a.hca || a.D_I % V == 0);
   if (vec) hipLaunchKernelGGL((append_kernel<DT, Vec<DT>>), grid, block, 0, s, a);

@@ -14,6 +14,9 @@
 //    reduces w_h * ReLU over the 32 heads it holds in registers plus one cross-half shuffle, and
 //    offers the 64 scores to its query's streaming top-k buffer in LDS. The T x N score matrix is
 //    never written.
+//  * index_prefill_fp4 (MXFP4, same shapes): the same fused structure with the scaled
+//    v_mfma_scale_f32_16x16x128_f8f6f4 on e2m1 codes and e8m0 block scales, one MFMA per 16 entries
+//    and 16 heads covering all 128 dims.
 //  * decode (few query rows, long contexts): scores of every (row, entry) are written to the
 //    workspace by a key-streaming MFMA kernel (bf16, or MXFP4 through the scaled
 //    v_mfma_scale_f32_16x16x128_f8f6f4 with e8m0 block scales), then selected by the top-k pass.
@@ -299,6 +302,135 @@ constexpr int kPrefillQW = 8;
 
 int prefill_lds(int cap) { return kRing * kTileBytes + kPrefillQW * (cap * 8 + 256 * 4); }
 
+// ---------------------------------------------------------------- fused MXFP4 prefill path
+
+// The MXFP4 form of index_prefill_mfma: QW = 8 consecutive query rows of one sequence, one per wave,
+// each wave's q_I (64 heads x 128 dims: 4 KiB of codes and 256 scale bytes) held as the A operands of
+// v_mfma_scale_f32_16x16x128_f8f6f4 (head mt*16 + lane%16, code bytes 16(lane/16) .. +15 = dims
+// 32(lane/16) .. +31, with that block's e8m0 scale). Key tiles of 128 entries (8 KiB of codes and
+// 512 scale bytes) stream through a three-deep LDS ring by direct global-to-LDS loads, shared by
+// the 8 waves: wave w loads column group w (16 entries, stored so that lane l's B operand, entry
+// l%16 and code bytes 16(l/16) .. +15, is LDS bytes 16l .. 16l + 15 of the group: one conflict-free
+// 16-byte read), waves 0 and 1 load the scales. One MFMA per (column group, head tile) forms all 128
+// dims of the dot products with the block scales applied; w_h * ReLU is summed over the 16 heads a
+// lane holds, and three lane swaps (two 32-lane, one 16-lane) turn the 4 column groups' partial sums
+// into one score per lane, entry base + lane, offered to the wave's streaming top-k. The T x N score
+// matrix is never written.
+constexpr int kF4NE = 128;                             // entries per key tile
+constexpr int kF4CodeBytes = kF4NE * 64;               // 128 dims at 4 bits
+constexpr int kF4TileBytes = kF4CodeBytes + kF4NE * 4;  // + 4 scale bytes per entry
+constexpr int kF4Ring = 3;
+constexpr int kF4QW = 8;
+
+__global__ void __launch_bounds__(kF4QW * 64) index_prefill_fp4(IndexArgs a, int cap, int t_blocks) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint64_t* bufs = reinterpret_cast<uint64_t*>(smem + kF4Ring * kF4TileBytes);
+  uint32_t* hists = reinterpret_cast<uint32_t*>(bufs + (int64_t)kF4QW * cap);
+
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int b = blockIdx.x / t_blocks;
+  const int tb = t_blocks - 1 - (int)(blockIdx.x % t_blocks);  // heaviest (latest) rows first
+  const int t0 = tb * kF4QW;
+  const int t = t0 + wave;
+  const bool active = t < a.T;
+  const int tq = active ? t : t0;
+  const int64_t row = (int64_t)b * a.T + tq;
+  const int64_t qp0 = pos_at(a.q_pos, b);
+  const int64_t nv = active ? n_visible(qp0 + t, a.m, a.n_cap) : 0;
+  const int t_last = (t0 + kF4QW < a.T ? t0 + kF4QW : a.T) - 1;
+  const int64_t nv_max = n_visible(qp0 + t_last, a.m, a.n_cap);
+
+  const int g = lane >> 4, c = lane & 15;
+  const uint8_t* qcodes = static_cast<const uint8_t*>(a.q) + (int64_t)b * a.q_seq_stride + (int64_t)tq * a.q_ld;
+  const uint8_t* qsc = a.q_scale + row * (64 * 4);
+  i32x8 qa[4];
+  int qs[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(qcodes + (mt * 16 + c) * 64 + g * 16);
+    qa[mt] = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    qs[mt] = qsc[(mt * 16 + c) * 4 + g];
+  }
+  // head weights of the accumulator rows this lane holds: head mt*16 + 4(lane/16) + r
+  const float* w = head_weights(a, row);
+  float wr[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wr[mt][r] = w[mt * 16 + g * 4 + r];
+
+  WaveTopK tk;
+  tk.init(bufs + (int64_t)wave * cap, hists + wave * 256, cap, a.k);
+
+  const uint8_t* kcodes = static_cast<const uint8_t*>(a.keys) + (int64_t)b * a.keys_seq_stride;
+  const uint8_t* kscale = a.k_scale + (int64_t)b * a.n_cap * 4;
+  const int ntiles = __builtin_amdgcn_readfirstlane((int)ceil_div(nv_max, kF4NE));  // uniform
+  const uint32_t ring_lds = lds_offset(smem);
+  // rows past the last visible entry are loaded as that entry (in bounds) and never offered
+  auto load_tile = [&](int tile, int slot) {
+    const uint32_t base = ring_lds + slot * kF4TileBytes;
+    int64_t e = (int64_t)tile * kF4NE + wave * 16 + c;
+    e = e < nv_max ? e : nv_max - 1;
+    copy_to_lds16(kcodes + e * 64 + g * 16, __builtin_amdgcn_readfirstlane(base + wave * 1024));
+    if (wave < 2) {
+      int64_t es = (int64_t)tile * kF4NE + wave * 64 + lane;
+      es = es < nv_max ? es : nv_max - 1;
+      copy_to_lds4(kscale + es * 4, __builtin_amdgcn_readfirstlane(base + kF4CodeBytes + wave * 256));
+    }
+  };
+  // waits until this wave's copies of every tile but the newest `pending` one have landed
+  auto wait_tiles = [&](bool pending) {
+    if (!pending) wait_vmcnt<0>();
+    else if (wave < 2) wait_vmcnt<2>();
+    else wait_vmcnt<1>();
+  };
+
+  // the q_I and w loads land before the loop, so no wait for them is left inside it
+  __builtin_amdgcn_s_waitcnt(0);
+  if (ntiles > 0) load_tile(0, 0);
+  if (ntiles > 1) load_tile(1, 1);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int slot = tile % kF4Ring;
+    wait_tiles(tile + 1 < ntiles);
+    __syncthreads();  // tile published; every wave is past its reads of tile - 1
+    if (tile + 2 < ntiles) load_tile(tile + 2, (tile + 2) % kF4Ring);
+    const uint8_t* tp = smem + slot * kF4TileBytes;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float p[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int grp = half * 4 + q;
+        const i32x4 kv = *reinterpret_cast<const i32x4*>(tp + grp * 1024 + lane * 16);
+        const int ks = tp[kF4CodeBytes + (grp * 16 + c) * 4 + g];
+        const i32x8 kb = i32x8{kv[0], kv[1], kv[2], kv[3], 0, 0, 0, 0};
+        float sp = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 acc = {};
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb, acc, 4, 4, 0, qs[mt], 0, ks);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sp = fmaf(wr[mt][r], relu(acc[r]), sp);
+        }
+        p[q] = sp;
+      }
+      // p[q] at lane l: column group q, entry l%16, the heads of lane group l/16. After the swaps lane l
+      // holds the sum over the four lane groups of column group l/16, entry l%16: entry 64 half + l.
+      const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+      const float h02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+      const float h13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h02), __float_as_uint(h13), false, false);
+      const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const int64_t i = (int64_t)tile * kF4NE + half * 64 + lane;
+      if (active) tk.offer(make_cand(sc, (uint32_t)i), i < nv);
+    }
+  }
+  if (active) tk.finish(a.out_idx + row * a.k, a.out_score ? a.out_score + row * a.k : nullptr);
+}
+
+int prefill_fp4_lds(int cap) { return kF4Ring * kF4TileBytes + kF4QW * (cap * 8 + 256 * 4); }
+
 // ---------------------------------------------------------------- decode scores
 
 // Loads one 64-entry tile of bf16 keys as B-fragments of v_mfma_f32_16x16x32_bf16: for column
@@ -506,15 +638,22 @@ bool use_prefill_mfma(const IndexArgs& a) {
   return a.idx_dtype == CSA_BF16 && a.H_I == 64 && a.D_I == 128 && a.T >= kPrefillQW &&
          prefill_lds(topk_cap_for(a.k, 512)) <= kMaxLds;
 }
+bool use_prefill_fp4(const IndexArgs& a) {
+  return a.idx_dtype == CSA_MXFP4 && a.H_I == 64 && a.D_I == 128 && a.T >= kF4QW &&
+         prefill_fp4_lds(topk_cap_for(a.k, 512)) <= kMaxLds;
+}
+// Few query rows per sequence (decode): every visible score passes through the workspace. Many
+// rows always take a fused path (the MFMA kernels, else index_generic), so no T x N matrix exists.
 bool use_decode_scores(const IndexArgs& a) {
   if (a.H_I != 64 || a.D_I != 128) return false;
-  if (a.idx_dtype == CSA_MXFP4) return true;
-  return a.idx_dtype == CSA_BF16 && a.T < kPrefillQW;
+  return (a.idx_dtype == CSA_BF16 || a.idx_dtype == CSA_MXFP4) && a.T < kPrefillQW;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
+
+bool index_fused_fp4(const IndexArgs& a) { return use_prefill_fp4(a); }
 
 size_t index_topk_workspace(const IndexArgs& a) {
   if (!use_decode_scores(a)) return 0;
@@ -533,6 +672,15 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
     const int t_blocks = (int)ceil_div(a.T, kPrefillQW);
     hipLaunchKernelGGL(index_prefill_mfma<kPrefillQW>, dim3((unsigned)(a.B * t_blocks)), dim3(kPrefillQW * 64),
                        lds, s, a, cap, t_blocks);
+    return hipGetLastError();
+  }
+  if (use_prefill_fp4(a)) {
+    const int cap = topk_cap_for(a.k, 512);
+    const int lds = prefill_fp4_lds(cap);
+    if ((e = allow_lds((const void*)index_prefill_fp4, lds)) != hipSuccess) return e;
+    const int t_blocks = (int)ceil_div(a.T, kF4QW);
+    hipLaunchKernelGGL(index_prefill_fp4, dim3((unsigned)(a.B * t_blocks)), dim3(kF4QW * 64), lds, s, a, cap,
+                       t_blocks);
     return hipGetLastError();
   }
   if (use_decode_scores(a)) {

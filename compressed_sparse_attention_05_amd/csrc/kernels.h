@@ -30,6 +30,10 @@ struct CompressArgs {
   int rope_dims = 0;
   double theta = 10000.0;
   bool records = false;
+  // MXFP4 output (indexer keys): the entry, rounded to out_dtype, is quantised into fp4_codes
+  // [B, n_cap, c/2] and fp4_scales [B, n_cap, c/32] instead of being stored (needs c % 32 == 0).
+  uint8_t* fp4_codes = nullptr;
+  uint8_t* fp4_scales = nullptr;
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 bool compress_epilogue_ok(const CompressArgs& a);
@@ -74,6 +78,14 @@ struct AppendArgs {
   int rope_dims = 0;
   double theta = 10000.0;
   bool aligned16 = false;        // comp, block, entries, keys 16-byte aligned
+  // MXFP4 indexer (CSA): the pooled key is quantised into keys (codes [B, n_cap, D_I/2]) and
+  // key_scales [B, n_cap, D_I/32]; q_idx [B, H_I*D_I] is quantised into qi_codes / qi_scales.
+  int key_fmt = 0;
+  uint8_t* key_scales = nullptr;
+  const void* q_idx = nullptr;
+  int H_I = 0;
+  uint8_t* qi_codes = nullptr;
+  uint8_t* qi_scales = nullptr;
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 int append_max_dim();
@@ -109,6 +121,18 @@ constexpr size_t kGemmWorkspace = 32u << 20;
 bool gemm_library_eligible(const GemmArgs& a);
 hipError_t launch_gemm_library(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s, bool* done);
 
+// MXFP4 quantisation of R rows of D values (D % 32 == 0; row r at x + r * ld elements) into
+// codes [R, D/2] and scales [R, D/32], both contiguous.
+struct QuantArgs {
+  int64_t R = 0;
+  int D = 0, dtype = 0;
+  const void* x = nullptr;
+  int64_t ld = 0;
+  uint8_t* codes = nullptr;
+  uint8_t* scales = nullptr;
+};
+hipError_t launch_mxfp4_quant(const QuantArgs& a, hipStream_t s);
+
 struct IndexArgs {
   int B, T;
   const int64_t* q_pos;        // device [B] (nullable: all 0): row t of sequence b at q_pos[b] + t
@@ -127,6 +151,7 @@ struct IndexArgs {
   float* out_score;
 };
 size_t index_topk_workspace(const IndexArgs& a);
+bool index_fused_fp4(const IndexArgs& a);  // MXFP4 query rows take the fused streaming path
 hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct TopkArgs {

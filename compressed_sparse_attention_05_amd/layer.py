@@ -11,6 +11,14 @@ def dims(m: int, D: int, H: int, H_I: int, D_I: int, top_k: int, window: int, sm
     return lib.make_dims(m, D, H, H_I, D_I, top_k, window, sm_scale)
 
 
+def _key_cache(d: lib.Dims, B: int, n_cap: int, dtype, device, fp4: bool):
+    """Indexer key cache: rows of the activation dtype, or MXFP4 codes and scales."""
+    if fp4:
+        return (torch.zeros(B, n_cap, d.D_I // 2, dtype=torch.uint8, device=device),
+                torch.zeros(B, n_cap, d.D_I // 32, dtype=torch.uint8, device=device))
+    return torch.zeros(B, n_cap, d.D_I, dtype=dtype, device=device), None
+
+
 class CSAPrefill:
     """Chunked prefill of B sequences: x [B, T, d_model], sequence b at positions pos0[b] .. pos0[b]+T-1.
 
@@ -20,10 +28,13 @@ class CSAPrefill:
     pos0 > 0, or let chain=True carry them from one call to the next: each call then also writes the
     next chunk's halo (halo_out) and the next chunk's window prefix is moved to the front of win, so
     consecutive calls at pos0, pos0 + T, ... prefill one long sequence chunk by chunk.
+    fp4_keys=True keeps the indexer keys in MXFP4 (keys: uint8 codes [B, n_cap, D_I/2], key_scales
+    [B, n_cap, D_I/32]) and runs the indexer on MXFP4 queries and keys.
     """
 
     def __init__(self, d: lib.Dims, B: int, T: int, d_model: int, n_cap: int, dtype=torch.bfloat16,
-                 out_dtype=torch.float32, device="cuda", records: bool = False, chain: bool = False):
+                 out_dtype=torch.float32, device="cuda", records: bool = False, chain: bool = False,
+                 fp4_keys: bool = False):
         self.d, self.B, self.T, self.chain = d, B, T, chain
         if chain and T % d.m:
             raise ValueError("chained chunks need T % m == 0")
@@ -31,7 +42,7 @@ class CSAPrefill:
             self.entries = torch.zeros(B, n_cap, lib.ENTRY_RECORD_BYTES, dtype=torch.uint8, device=device)
         else:
             self.entries = torch.zeros(B, n_cap, d.D, dtype=dtype, device=device)
-        self.keys = torch.zeros(B, n_cap, d.D_I, dtype=dtype, device=device)
+        self.keys, self.key_scales = _key_cache(d, B, n_cap, dtype, device, fp4_keys)
         self.win = torch.zeros(B, d.window - 1 + T, d.D, dtype=dtype, device=device)
         self.halo = torch.zeros(B, d.m, 2 * d.D + 2 * d.D_I, dtype=dtype, device=device)
         self.halo_next = torch.zeros_like(self.halo) if chain else None
@@ -51,7 +62,7 @@ class CSAPrefill:
 
     def __call__(self, weights: dict, x: torch.Tensor, pos0) -> torch.Tensor:
         pos = self.positions(pos0)
-        cache = {"entries": self.entries, "keys": self.keys, "win": self.win,
+        cache = {"entries": self.entries, "keys": self.keys, "key_scales": self.key_scales, "win": self.win,
                  "halo": self.halo if pos is not None else None,
                  "halo_out": self.halo_next if self.chain else None}
         self.fwd(weights, x, cache, self.out, pos0=pos, out_idx=self.idx)
@@ -116,17 +127,18 @@ class CSADecodeState:
     last `window` raw KV rows, the compressor inputs of the previous and current block, block i in
     rows (i % 2) * m ..); when a token completes its block the entry and key are compressed into the
     caches (csa_decode_step). Each sequence advances at its own position. records=True keeps the
-    entries as 584-byte FP8 records."""
+    entries as 584-byte FP8 records; fp4_keys=True keeps the indexer keys in MXFP4 (the step quantises
+    its q_idx)."""
 
     def __init__(self, d: lib.Dims, B: int, n_cap: int, dtype=torch.bfloat16, out_dtype=torch.float32,
-                 records: bool = False, device="cuda"):
+                 records: bool = False, device="cuda", fp4_keys: bool = False):
         self.d, self.B = d, B
         self.device = device
         if records:
             self.entries = torch.zeros(B, n_cap, lib.ENTRY_RECORD_BYTES, dtype=torch.uint8, device=device)
         else:
             self.entries = torch.zeros(B, n_cap, d.D, dtype=dtype, device=device)
-        self.keys = torch.zeros(B, n_cap, d.D_I, dtype=dtype, device=device)
+        self.keys, self.key_scales = _key_cache(d, B, n_cap, dtype, device, fp4_keys)
         self.win = torch.zeros(B, d.window, d.D, dtype=dtype, device=device)
         self.block = torch.zeros(B, 2 * d.m, 4 * d.D + 4 * d.D_I, dtype=dtype, device=device)
         self.out = torch.empty(B, d.H, d.D, dtype=out_dtype, device=device)
@@ -136,7 +148,8 @@ class CSADecodeState:
         self._pos = {}
 
     def state(self) -> dict:
-        return {"entries": self.entries, "keys": self.keys, "win": self.win, "block": self.block}
+        return {"entries": self.entries, "keys": self.keys, "key_scales": self.key_scales, "win": self.win,
+                "block": self.block}
 
     def block_rows(self, blk: int) -> slice:
         """The rows of the state's block that hold block `blk`."""

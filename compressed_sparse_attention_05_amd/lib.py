@@ -22,7 +22,7 @@ CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN,
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
            "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8",
-           "csa_hca_decode_step", "csa_decode_step_noalloc")
+           "csa_hca_decode_step", "csa_decode_step_noalloc", "csa_mxfp4_quantize")
 STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -48,12 +48,14 @@ class Weights(ctypes.Structure):
 class Cache(ctypes.Structure):
     _fields_ = [("entries", ctypes.c_void_p), ("keys", ctypes.c_void_p), ("n_cap", ctypes.c_int64),
                 ("win", ctypes.c_void_p), ("win_cap", ctypes.c_int64), ("halo", ctypes.c_void_p),
-                ("halo_out", ctypes.c_void_p), ("entry_fmt", ctypes.c_int32)]
+                ("halo_out", ctypes.c_void_p), ("entry_fmt", ctypes.c_int32), ("key_fmt", ctypes.c_int32),
+                ("key_scales", ctypes.c_void_p)]
 
 
 class DecodeState(ctypes.Structure):
     _fields_ = [("entries", ctypes.c_void_p), ("entry_fmt", ctypes.c_int32), ("keys", ctypes.c_void_p),
-                ("n_cap", ctypes.c_int64), ("win", ctypes.c_void_p), ("block", ctypes.c_void_p)]
+                ("n_cap", ctypes.c_int64), ("win", ctypes.c_void_p), ("block", ctypes.c_void_p),
+                ("key_fmt", ctypes.c_int32), ("key_scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -94,10 +96,11 @@ def load() -> ctypes.CDLL:
                                         ctypes.POINTER(DecodeState), vp, i32, vp, sz, vp]
     lib.csa_decode_step_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, vp, i32, vp, vp, vp,
                                             vp, ctypes.POINTER(DecodeState), vp, i32, vp, vp]
+    lib.csa_mxfp4_quantize.argtypes = [i64, i32, i32, vp, i64, vp, vp, vp]
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
               "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8", "csa_hca_decode_step",
-              "csa_decode_step_noalloc"):
+              "csa_decode_step_noalloc", "csa_mxfp4_quantize"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -293,6 +296,24 @@ def csa_entry_pack(entries, records=None):
     return records
 
 
+def csa_mxfp4_quantize(x, codes=None, scales=None):
+    """x [R, D] (float32 or bfloat16, unit stride along D, D % 32 == 0) -> MXFP4 codes uint8 [R, D/2] and
+    scales uint8 [R, D/32] (see include/csa.h). Returns (codes, scales)."""
+    _require_cuda(x, codes, scales)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [R, D] with unit stride along D")
+    R, D = x.shape
+    if codes is None:
+        codes = torch.empty(R, D // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(R, D // 32, dtype=torch.uint8, device=x.device)
+    if not (codes.is_contiguous() and scales.is_contiguous()) or codes.numel() != R * (D // 2) or \
+            scales.numel() != R * (D // 32):
+        raise ValueError("codes / scales must be contiguous [R, D/2] / [R, D/32]")
+    _check(load().csa_mxfp4_quantize(R, D, _dt(x), _p(x), x.stride(0), _p(codes), _p(scales), _stream()))
+    return codes, scales
+
+
 def csa_hca_compress(cv, z, bias, entries, *, pos0, m: int):
     """HCA compressor. cv, z: [B, T, c] views sharing strides; bias float32 [m, c]; entries [B, n_cap, c]."""
     _require_cuda(cv, z, bias, entries)
@@ -363,20 +384,29 @@ def weights_struct(weights: dict) -> Weights:
                    int(weights.get("rope_dims", 0)), float(weights.get("rope_theta", 10000.0)))
 
 
+def _state_struct(state: dict, keys: bool = True) -> DecodeState:
+    """The C decode state of a dict of tensors: entries (rows, or uint8 records), keys (rows, or uint8
+    MXFP4 codes when key_scales is given), win, block."""
+    ent = state["entries"]
+    ks = state.get("key_scales") if keys else None
+    return DecodeState(_p(ent), 1 if ent.dtype == torch.uint8 else 0, _p(state["keys"]) if keys else None,
+                       ent.shape[1], _p(state["win"]), _p(state["block"]), 1 if ks is not None else 0, _p(ks))
+
+
 def csa_decode_step(dims: Dims, weights: dict, pos, q, q_idx, kv, comp, state: dict, out, *, out_idx=None,
                     ws=None):
     """One decode step of B sequences, sequence b at position pos[b] (an int: all at pos), over a decode
     state (see include/csa.h):
     q [B, H, D], q_idx [B, H_I, D_I], kv [B, D], comp [B, 4D + 4D_I]; state holds entries (rows, or
-    uint8 records [B, n_cap, 584]), keys, win [B, window, D], block [B, 2m, 4D + 4D_I]."""
+    uint8 records [B, n_cap, 584]), keys (rows, or uint8 MXFP4 codes [B, n_cap, D_I/2] with key_scales
+    [B, n_cap, D_I/32]), win [B, window, D], block [B, 2m, 4D + 4D_I]."""
     _require_cuda(q, q_idx, kv, comp, out, out_idx)
     for t in (q, q_idx, kv, comp, out):
         if not t.is_contiguous():
             raise ValueError("decode step tensors must be contiguous")
     B = q.shape[0]
     ent = state["entries"]
-    st = DecodeState(_p(ent), 1 if ent.dtype == torch.uint8 else 0, _p(state["keys"]), ent.shape[1],
-                     _p(state["win"]), _p(state["block"]))
+    st = _state_struct(state)
     need = csa_workspace_size(CSA_OP_DECODE_STEP, dims, B, 1, ent.shape[1], 0, _dt(q))
     if ws is None or ws.numel() < need + 256:
         ws = _workspace(need, q.device)
@@ -399,9 +429,7 @@ def csa_decode_step_noalloc(dims: Dims, weights: dict, pos, q, q_idx, kv, comp, 
         raise TypeError("pos must be a device int64 [B] tensor")
     B = q.shape[0]
     pt = positions(B, pos, q.device)
-    ent = state["entries"]
-    st = DecodeState(_p(ent), 1 if ent.dtype == torch.uint8 else 0, _p(state["keys"]), ent.shape[1],
-                     _p(state["win"]), _p(state["block"]))
+    st = _state_struct(state)
     w = weights_struct(weights)
     _check(load().csa_decode_step_noalloc(ctypes.byref(dims), ctypes.byref(w), B, _p(pt), _dt(q), _p(q), _p(q_idx),
                                           _p(kv), _p(comp), ctypes.byref(st), _p(out), _dt(out), _p(out_idx),
@@ -419,8 +447,7 @@ def csa_hca_decode_step(dims: Dims, weights: dict, pos, q, kv, comp, state: dict
             raise ValueError("decode step tensors must be contiguous")
     B = q.shape[0]
     ent = state["entries"]
-    st = DecodeState(_p(ent), 1 if ent.dtype == torch.uint8 else 0, None, ent.shape[1], _p(state["win"]),
-                     _p(state["block"]))
+    st = _state_struct(state, keys=False)
     need = csa_workspace_size(CSA_OP_HCA_DECODE_STEP, dims, B, 1, ent.shape[1], 0, _dt(q))
     if ws is None or ws.numel() < need + 256:
         ws = _workspace(need, q.device)
@@ -456,9 +483,10 @@ class Forward:
         """pos0: an int (every sequence) or per-sequence positions (see positions())."""
         w = weights_struct(weights)
         pos = positions(self.B, pos0, x.device)
+        ks = cache.get("key_scales")
         c = Cache(_p(cache["entries"]), _p(cache["keys"]), cache["entries"].shape[1], _p(cache["win"]),
                   cache["win"].shape[1], _p(cache.get("halo")), _p(cache.get("halo_out")),
-                  1 if cache["entries"].dtype == torch.uint8 else 0)
+                  1 if cache["entries"].dtype == torch.uint8 else 0, 1 if ks is not None else 0, _p(ks))
         _check(load().csa_forward(ctypes.byref(self.dims), ctypes.byref(w), self.B, self.T, _p(pos), self.d_model,
                                   self.dtype, _p(x), ctypes.byref(c), _p(out), _dt(out), _p(out_idx), self._wp,
                                   self._wn, _stream()))

@@ -81,7 +81,7 @@ typedef struct csa_dims {
   float sm_scale;   /* softmax scale; 0 selects 1/sqrt(D)                                       */
 } csa_dims;
 
-/* The ABI revision (2: per-sequence device position arrays). */
+/* The ABI revision (3: per-sequence device position arrays, MXFP4 key caches). */
 int csa_version(void);
 /* The message of this thread's last failed call ("" after a successful one). */
 const char* csa_last_error(void);
@@ -278,6 +278,20 @@ int csa_entry_pack(int B, int N, int in_dtype, const void* entries, int64_t ld, 
                    void* records, int64_t records_seq_stride, void* stream);
 
 /*
+ * MXFP4 quantisation (OCP Microscaling Formats v1.0) of R rows of D values, the storage of the FP4
+ * indexer's keys and queries ("Anatomy of a Frontier Model", sections "The KV cache, recomputed" and
+ * "Precision: FP8 everywhere, FP4 experts"). Per block of 32 consecutive values: shared exponent
+ * X = floor(log2(max |x|)) - 2 clamped to [-127, 127], stored as the byte X + 127; each value
+ * x / 2^X rounded to the nearest e2m1 value (ties to the even code, magnitudes past 6 saturate to 6),
+ * sign bit = sign of x; codes hold two values per byte, the even-indexed one in the low nibble.
+ *   x       [R, D] of dtype (F32 or BF16), row stride ld elements (ld >= D); D % 32 == 0.
+ *   codes   [R, D/2] bytes, contiguous, 4-byte aligned.  scales [R, D/32] bytes, contiguous.
+ * Inf / NaN inputs are not supported. Errors: CSA_ERR_ARG for bad sizes, a NULL or misaligned tensor.
+ */
+int csa_mxfp4_quantize(int64_t R, int D, int dtype, const void* x, int64_t ld, void* codes, void* scales,
+                       void* stream);
+
+/*
  * csa_sparse_attn over an entry cache of 584-byte records (see csa_entry_pack): as
  * csa_sparse_attn, with `records` [B, n_cap, 584] bytes (16-byte aligned base, sequence stride in
  * bytes, a multiple of 8) in place of the entries; D must be 512. q and kv_raw keep in_dtype. The
@@ -349,6 +363,15 @@ typedef struct csa_cache {
   int32_t entry_fmt;     /* 0: entries are rows of the activation dtype; 1: 584-byte FP8 records
                             [B, n_cap, 584] (see csa_entry_pack; D = 512, bf16 layer): new entries
                             are packed and the attention reads the records                        */
+  int32_t key_fmt;       /* 0: keys are rows of the activation dtype; 1: MXFP4 indexer ("Anatomy of a
+                            Frontier Model", "The KV cache, recomputed": 128 FP4 values and a scale
+                            byte per 32; "Precision: FP8 everywhere, FP4 experts": the indexer's
+                            query-key product in FP4): keys holds the e2m1 codes [B, n_cap, D_I/2]
+                            (16-byte aligned, contiguous) and key_scales the e8m0 scales
+                            [B, n_cap, D_I/32]; new keys are quantised from their stored values (see
+                            csa_mxfp4_quantize), the chunk's indexer queries likewise, and the
+                            indexer runs on the MXFP4 operands                                      */
+  void* key_scales;      /* [B, n_cap, D_I/32] when key_fmt = 1, else unused                       */
 } csa_cache;
 
 /* Decode state of B sequences (device pointers, activation dtype unless stated). */
@@ -362,6 +385,11 @@ typedef struct csa_decode_state {
                             indexer's ica|iza|icb|izb (D_I each); token r of block i sits in row
                             (i % 2)*m + r, so the previous block's rows stay in the other half.
                             HCA: [B, m, 2D], c | z of the current block's tokens (row p % m).       */
+  int32_t key_fmt;       /* 0: keys of the activation dtype; 1: MXFP4 (see csa_cache.key_fmt): keys
+                            = codes [B, n_cap, D_I/2], key_scales [B, n_cap, D_I/32]; a completed
+                            block's key is quantised from its stored value, and each step's q_idx
+                            (given in the activation dtype) is quantised before the indexer         */
+  void* key_scales;
 } csa_decode_state;
 
 /*

@@ -518,7 +518,8 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None, fid=None):
     With an MXFP4 indexer (wl.idx_dtype == "mxfp4") the key cache holds the MXFP4 form of every key
     (the context's as generated, the chunk's new keys quantised from their stored values) and the
     indexer queries are quantised the same way before the scores; keys_new stays the unquantised
-    stored key and keys_new_fp4 holds its (codes, scales).
+    stored key and keys_new_fp4 holds its (codes, scales); q_idx is what the indexer multiplies and
+    q_idx_stored the query before quantisation.
     fid (optional) turns on QK-norm and partial RoPE: a dict with gamma_q, gamma_kv [D], eps,
     rope_dims, theta. Queries, new entries and the chunk's raw KV are then RMS-normalised and
     rotated (queries at their positions, raw KV at its token's position, entries at
@@ -563,6 +564,7 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None, fid=None):
     fp4 = wl.idx_dtype == "mxfp4"
     new_k_fp4 = mxfp4_quantize(new_k) if fp4 else None
     keys_new = mxfp4_decode(*new_k_fp4) if fp4 else new_k   # what the key cache holds
+    q_idx_stored = q_idx
     if fp4:
         q_idx = mxfp4_round(q_idx)
     if L > 0:
@@ -582,7 +584,8 @@ def prefill(inp: dict, wl, b: int = 0, query_rows=None, sink=None, fid=None):
     out = sparse_attention(q, entries, idx, raw, raw_pos0, q_pos, wl.W, sink=sink)
     if fid is not None:
         out = rope(out, q_pos, fid["rope_dims"], fid["theta"], inverse=True)
-    return dict(parts=parts, q=q, q_idx=q_idx, entries_new=new_e, keys_new=new_k, keys_new_fp4=new_k_fp4,
+    return dict(parts=parts, q=q, q_idx=q_idx, q_idx_stored=q_idx_stored, entries_new=new_e, keys_new=new_k,
+                keys_new_fp4=new_k_fp4,
                 entries=entries, keys=keys, raw=raw, raw_pos0=raw_pos0, rows=rows, q_pos=q_pos,
                 n_vis=nv, scores=scores, idx=idx, out=out)
 

@@ -150,3 +150,19 @@ def make_inputs(wl: Workload) -> dict:
             out["keys"] = _act(s, "keys", (B, N, DI), wl)
             out["q_idx"] = _act(s, "q_idx", (B, 1, wl.H_I, DI), wl)
     return out
+
+
+def dyadic_projection(inp: dict, wl: Workload) -> dict:
+    """The inputs with x and W moved to coarse power-of-two grids (x in multiples of 1/4 within [-2, 2],
+    W in multiples of 1/128 within [-1/16, 1/16]), so that every projected value is exact in float32
+    whatever the summation order: products are multiples of 2**-9 below 2**-3 in magnitude, and d_model
+    of them need at most 24 significant bits. Used where a quantiser decides codes from the projected
+    values, so that both sides quantise the same numbers."""
+    out = dict(inp)
+    x = np.clip(np.rint(normal_f32(wl.seed, "x", (wl.B, wl.T, wl.d)) * 4), -8, 8) / 4
+    W = np.clip(np.rint(normal_f32(wl.seed, "W", (wl.n_tot, wl.d), std=1.0 / np.sqrt(wl.d)) * 128), -8, 8) / 128
+    assert wl.d * 2 ** -3 < 2 ** 15, "projection sums must stay exact in float32"
+    conv = f32_to_bf16_bits if wl.dtype == "bf16" else (lambda a: a)
+    out["x"] = conv(x.astype(np.float32))
+    out["W"] = conv(W.astype(np.float32))
+    return out

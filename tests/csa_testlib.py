@@ -44,11 +44,16 @@ def run_prefill(wl, inp, weights=None, out_dtype=torch.float32):
     """csa_forward over the workload's chunk; returns the CSAPrefill holding out/idx/caches."""
     d = dims_of(wl)
     w = weights or weights_to_device(wl, inp)
-    st = layer.CSAPrefill(d, wl.B, wl.T, wl.d, wl.n_cap, dtype=torch_dtype(wl), out_dtype=out_dtype)
+    fp4 = wl.idx_dtype == "mxfp4"
+    st = layer.CSAPrefill(d, wl.B, wl.T, wl.d, wl.n_cap, dtype=torch_dtype(wl), out_dtype=out_dtype, fp4_keys=fp4)
     if wl.L > 0:
         n0 = wl.L // wl.m
         st.entries[:, :n0] = act(inp["entries_prefix"], wl)
-        st.keys[:, :n0] = act(inp["keys_prefix"], wl)
+        if fp4:
+            st.keys[:, :n0] = to_device(inp["keys_prefix_codes"], "u8")
+            st.key_scales[:, :n0] = to_device(inp["keys_prefix_scales"], "u8")
+        else:
+            st.keys[:, :n0] = act(inp["keys_prefix"], wl)
         st.win[:, : wl.W - 1] = act(inp["win_prefix"], wl)
         st.halo.copy_(act(inp["halo"], wl))
     x = act(inp["x"], wl)

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in _declared():
         assert hasattr(L, n), n
     assert set(lib.EXPORTS) == set(_declared())
-    assert lib.csa_version() == 2
+    assert lib.csa_version() == 3
 
 
 def _d(**kw):
@@ -47,6 +47,10 @@ def test_workspace_sizes():
     # decode: scores of every (row, entry) pass through the workspace
     nb = lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, _d(top_k=1024), 64, 1, 32768)
     assert nb >= 64 * 32768 * 4
+    # MXFP4 prefill is fused too; MXFP4 decode rows pass their scores through the workspace
+    assert lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, d, 1, 8192, 2048, 0, lib.CSA_MXFP4) == 0
+    assert lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, _d(top_k=1024), 4, 1, 262144, 0,
+                                  lib.CSA_MXFP4) >= 4 * 262144 * 4
     fw = lib.csa_workspace_size(lib.CSA_OP_FORWARD, d, 1, 8192, 2048, 4096)
     n_tot = 4 * 512 + 4 * 128 + 64 * 512 + 64 * 128 + 512
     assert fw >= 8192 * n_tot * 2 + 8192 * 512 * 4
@@ -223,3 +227,41 @@ def test_decode_step_noalloc_rejects_a_step_beyond_its_scratch():
     assert rc == -3 and "scratch" in msg
     # the decode128k batch fits
     assert lib.csa_workspace_size(lib.CSA_OP_DECODE_STEP, d, 64, 1, 32768, 0, lib.CSA_BF16) <= lib.STATIC_SCRATCH_BYTES
+
+
+def test_mxfp4_quantize_rejects_bad_arguments():
+    L = lib.load()
+    p = ctypes.c_void_p(4096)
+    for args, what in (((4, 48, lib.CSA_BF16, p, 48, p, p, None), "multiple of 32"),
+                       ((4, 64, lib.CSA_BF16, p, 32, p, p, None), "ld"),
+                       ((4, 64, lib.CSA_MXFP4, p, 64, p, p, None), "dtype"),
+                       ((4, 64, lib.CSA_BF16, p, 64, ctypes.c_void_p(4098), p, None), "align"),
+                       ((4, 64, lib.CSA_BF16, None, 64, p, p, None), "NULL")):
+        rc, msg = _err(L.csa_mxfp4_quantize(*args))
+        assert rc == -1 and what in msg, (args, msg)
+    assert L.csa_mxfp4_quantize(0, 64, lib.CSA_BF16, None, 64, None, None, None) == 0
+
+
+def test_mxfp4_key_caches_need_their_scales():
+    L = lib.load()
+    p = ctypes.c_void_p(4096)
+    d = _d()
+    w = lib.Weights(4096, 4096, 4096, 4096, 4096, 4096, None)
+    c = lib.Cache(4096, 4096, 4000, 4096, 9000, None, None, 0, 1, None)
+    rc, msg = _err(L.csa_forward(ctypes.byref(d), ctypes.byref(w), 1, 8192, None, 4096, lib.CSA_BF16, p,
+                                 ctypes.byref(c), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "key_scales" in msg
+    c = lib.Cache(4096, 4096, 4000, 4096, 9000, None, None, 0, 2, p)
+    rc, msg = _err(L.csa_forward(ctypes.byref(d), ctypes.byref(w), 1, 8192, None, 4096, lib.CSA_BF16, p,
+                                 ctypes.byref(c), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "key_fmt" in msg
+    d = _d(H=128, top_k=1024)
+    wd = lib.Weights(None, 4096, 4096, 4096, 4096, 4096, None, None, None, 0.0, 0, 10000.0)
+    st = lib.DecodeState(4096, 0, 4096, 100, 4096, 4096, 1, None)
+    rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(wd), 2, p, lib.CSA_BF16, p, p, p, p,
+                                     ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "key_scales" in msg
+    st = lib.DecodeState(4096, 0, ctypes.c_void_p(4104), 100, 4096, 4096, 1, p)
+    rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(wd), 2, p, lib.CSA_BF16, p, p, p, p,
+                                     ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
+    assert rc == -1 and "aligned" in msg
