@@ -9,17 +9,17 @@ timed region starts. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload chunk1m] [--no-decode] [--no-cpu-baseline]
     python bench.py --copy-probe      # a plain 1 GiB device copy, for counter calibration
-    python bench.py --pmc-summary DIR # HBM bytes of the indexer kernel from rocprofv3 --pmc runs
+    python bench.py --pmc-summary DIR # HBM bytes per kernel from rocprofv3 --pmc runs
     python bench.py --mfma-summary DIR  # matrix-core busy share of the prefill kernels (one --pmc run)
+    python bench.py --attn-summary DIR  # LDS / wait counters of the 128-head attention (two --pmc runs)
 
-Counter runs (repository root; from /tmp with TMPDIR=/tmp), each in a process of its own:
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- python3 bench.py --steps 2 \
-        --warmup 1 --no-decode --no-cpu-baseline
-    (the same with WRITE_SIZE into DIR/write, and both counters of --copy-probe into
-    DIR/copy_fetch and DIR/copy_write), then --pmc-summary DIR writes profiles/*_pmc.json and .md.
-    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d DIR/mfma -o run \
-        -- python3 bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline
-    then --mfma-summary DIR writes profiles/mfma_busy_<workload>.md.
+Counter runs (repository root; from /tmp with TMPDIR=/tmp), each in a process of its own, over
+    python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-hca --no-prefill8k --workload chunk1m
+    (COUNTER_BENCH below): FETCH_SIZE into DIR/fetch, WRITE_SIZE into DIR/write, both counters of
+    --copy-probe into DIR/copy_fetch and DIR/copy_write, then --pmc-summary DIR writes
+    profiles/*_pmc.json / .md and profiles/hbm_traffic_<workload>_bench.md; with --no-decode added,
+    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE into DIR/mfma (--mfma-summary) and the two counter sets of
+    attn_summary into DIR/attn1, DIR/attn2 (--attn-summary). Each summary names its exact commands.
 """
 from __future__ import annotations
 
@@ -96,6 +96,44 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
 
 
+def peak_probes():
+    """Measured ceilings on this part (include/csa_probe.h), to report fractions against beside the
+    vendor peaks: HBM read bandwidth of 16-byte loads streaming 4 GiB (far beyond the 256 MB Infinity
+    Cache), the bf16 MFMA rate of independent 32x32x16 chains on every compute unit, and for context a
+    large bf16 GEMM through torch (hipBLASLt) and a 4 GiB device copy."""
+    import torch
+    from compressed_sparse_attention_05_amd import lib
+    sink = lib.probe_sink()
+    n = 4 << 30
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    lib.probe_hbm_read(buf, sink)
+    torch.cuda.synchronize()
+    rd = float(np.median(timed_events(lambda: lib.probe_hbm_read(buf, sink), 5, torch.cuda.synchronize)))
+    y = torch.empty_like(buf)
+    y.copy_(buf)
+    torch.cuda.synchronize()
+    cp = float(np.median(timed_events(lambda: y.copy_(buf), 5, torch.cuda.synchronize)))
+    del buf, y
+    iters = 40000
+    flops = lib.probe_mfma_bf16(iters, sink)
+    torch.cuda.synchronize()
+    mf = float(np.median(timed_events(lambda: lib.probe_mfma_bf16(iters, sink), 5, torch.cuda.synchronize)))
+    M = 8192
+    a = torch.randn(M, M, device="cuda").to(torch.bfloat16)
+    b = torch.randn(M, M, device="cuda").to(torch.bfloat16)
+    c = a @ b
+    torch.cuda.synchronize()
+    mm = float(np.median(timed_events(lambda: torch.matmul(a, b, out=c), 5, torch.cuda.synchronize)))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round(n / (rd * 1e-3) / 1e9, 1),
+            "mfma_bf16_tflops": round(flops / (mf * 1e-3) / 1e12, 1),
+            "hbm_copy_gbs": round(2 * n / (cp * 1e-3) / 1e9, 1),
+            "bf16_gemm_tflops_hipblaslt": round(2 * M ** 3 / (mm * 1e-3) / 1e12, 1),
+            "what": "csa_probe_hbm_read over 4 GiB; csa_probe_mfma_bf16 (4 independent 32x32x16 chains per "
+                    "wave, 8 waves per CU); torch copy of 4 GiB; 8192^3 bf16 torch.matmul; median of 5, HIP events"}
+
+
 def load_traffic(name: str):
     """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
     path = os.path.join(ROOT, "profiles", name)
@@ -122,57 +160,137 @@ def _counter_rows(path, counter):
     return out
 
 
+COUNTER_BENCH = "python3 /root/repo/bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-hca --no-prefill8k --workload "
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"(\w+)(<[^()]*>)?\(", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name[:40]
+
+
 def pmc_summary(pmc_dir, workload):
-    """HBM traffic of the indexer kernel from four rocprofv3 --pmc runs (see the module docstring):
-    FETCH_SIZE and WRITE_SIZE of the bench, and the same two counters of the 1 GiB copy probe, which
-    gives the factor from counter KiB to bytes. Writes profiles/index_prefill_mfma_<wl>_pmc.json/.md."""
-    def per_dispatch(run, counter, match):
-        vals = [v for n, v in _counter_rows(os.path.join(pmc_dir, run, "run_counter_collection.csv"), counter)
-                if match(n)]
-        if not vals:
-            raise SystemExit(f"no {counter} rows for the kernel in {run}")
-        return float(np.median(vals)), len(vals)
-    is_idx = lambda n: "index_prefill_mfma" in n
-    is_copy = lambda n: "copy" in n.lower()
-    fetch_kib, nf = per_dispatch("fetch", "FETCH_SIZE", is_idx)
-    write_kib, nw = per_dispatch("write", "WRITE_SIZE", is_idx)
-    cf_kib, _ = per_dispatch("copy_fetch", "FETCH_SIZE", is_copy)
-    cw_kib, _ = per_dispatch("copy_write", "WRITE_SIZE", is_copy)
+    """HBM traffic from four rocprofv3 --pmc runs (see the module docstring): FETCH_SIZE and WRITE_SIZE
+    of the bench, and the same two counters of the 1 GiB copy probe, which gives the factor from
+    counter KiB to bytes. Writes profiles/<indexer kernel>_<wl>_pmc.json/.md for both prefill indexer
+    kernels and profiles/hbm_traffic_<wl>_bench.md with every library kernel of the run."""
+    def rows(run, counter):
+        return _counter_rows(os.path.join(pmc_dir, run, "run_counter_collection.csv"), counter)
+    def median_of(rs, match):
+        vals = [v for n, v in rs if match(n)]
+        return (float(np.median(vals)), len(vals)) if vals else (None, 0)
+    fetch, write = rows("fetch", "FETCH_SIZE"), rows("write", "WRITE_SIZE")
+    cf_kib, _ = median_of(rows("copy_fetch", "FETCH_SIZE"), lambda n: "copy" in n.lower())
+    cw_kib, _ = median_of(rows("copy_write", "WRITE_SIZE"), lambda n: "copy" in n.lower())
     copy_bytes = 1 << 30
     f_scale, w_scale = copy_bytes / cf_kib, copy_bytes / cw_kib  # bytes per counter unit
-    hbm = fetch_kib * f_scale + write_kib * w_scale
-    bench_cmd = ("python3 /root/repo/bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline --workload " + workload)
+    bench_cmd = COUNTER_BENCH + workload
     cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o run -- {bench_cmd}",
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- {bench_cmd}",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/copy_fetch -o run -- python3 /root/repo/bench.py --copy-probe",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/copy_write -o run -- python3 /root/repo/bench.py --copy-probe",
             f"python3 /root/repo/bench.py --pmc-summary <out> --workload {workload}"]
-    d = {"kernel": "index_prefill_mfma", "workload": workload, "kernel_sources": list(KERNEL_SOURCES),
-         "kernel_sources_sha256_16": kernel_hash(),
-         "fetch_size_kib_per_dispatch": round(fetch_kib, 1), "write_size_kib_per_dispatch": round(write_kib, 1),
-         "dispatches": [nf, nw],
-         "copy_probe": {"bytes_read": copy_bytes, "bytes_written": copy_bytes, "fetch_size_kib": round(cf_kib, 1),
-                        "write_size_kib": round(cw_kib, 1)},
-         "bytes_per_fetch_unit": round(f_scale, 2), "bytes_per_write_unit": round(w_scale, 2),
-         "hbm_bytes_per_launch": int(hbm), "commands": cmds,
-         "note": "run from /tmp with TMPDIR=/tmp; <out> is a scratch directory of the GPU run"}
-    base = os.path.join(ROOT, "profiles", f"index_prefill_mfma_{workload}_pmc")
-    with open(base + ".json", "w") as f:
-        json.dump(d, f, indent=1)
-    with open(base + ".md", "w") as f:
-        f.write(f"# index_prefill_mfma, {workload}: HBM traffic from rocprofv3 counters\n\n")
+    out = {}
+    for kern in ("index_prefill_mfma", "index_prefill_fp4"):
+        match = lambda n, k=kern: k in n
+        fetch_kib, nf = median_of(fetch, match)
+        write_kib, nw = median_of(write, match)
+        if fetch_kib is None or write_kib is None:
+            continue
+        hbm = fetch_kib * f_scale + write_kib * w_scale
+        d = {"kernel": kern, "workload": workload, "kernel_sources": list(KERNEL_SOURCES),
+             "kernel_sources_sha256_16": kernel_hash(),
+             "fetch_size_kib_per_dispatch": round(fetch_kib, 1), "write_size_kib_per_dispatch": round(write_kib, 1),
+             "dispatches": [nf, nw],
+             "copy_probe": {"bytes_read": copy_bytes, "bytes_written": copy_bytes, "fetch_size_kib": round(cf_kib, 1),
+                            "write_size_kib": round(cw_kib, 1)},
+             "bytes_per_fetch_unit": round(f_scale, 2), "bytes_per_write_unit": round(w_scale, 2),
+             "hbm_bytes_per_launch": int(hbm), "commands": cmds,
+             "note": "run from /tmp with TMPDIR=/tmp; <out> is a scratch directory of the GPU run"}
+        out[kern] = d
+        base = os.path.join(ROOT, "profiles", f"{kern}_{workload}_pmc")
+        with open(base + ".json", "w") as f:
+            json.dump(d, f, indent=1)
+        with open(base + ".md", "w") as f:
+            f.write(f"# {kern}, {workload}: HBM traffic from rocprofv3 counters\n\n")
+            f.write("Commands (repository root, run from /tmp with TMPDIR=/tmp):\n\n```\n" + "\n".join(cmds) + "\n```\n\n")
+            f.write("| quantity | value |\n|---|---|\n")
+            f.write(f"| FETCH_SIZE per dispatch (KiB, median of {nf}) | {fetch_kib:.1f} |\n")
+            f.write(f"| WRITE_SIZE per dispatch (KiB, median of {nw}) | {write_kib:.1f} |\n")
+            f.write(f"| copy probe (1 GiB read + 1 GiB written): FETCH_SIZE / WRITE_SIZE KiB | {cf_kib:.1f} / {cw_kib:.1f} |\n")
+            f.write(f"| bytes per counter KiB (fetch / write) | {f_scale:.1f} / {w_scale:.1f} |\n")
+            f.write(f"| HBM bytes per launch | {hbm:.4g} |\n")
+            f.write(f"| kernel sources sha256[:16] | {kernel_hash()} |\n")
+            f.write("\nFETCH_SIZE counts what the L2 caches fetch from the fabric, Infinity-Cache hits included, "
+                    "so it bounds the HBM reads from above. The algorithmic bytes of one launch are the visible "
+                    "keys, q_I, the head weights and the selected indices.\n")
+    # every library kernel of the run
+    names = sorted({_short_kernel(n) for n, _ in fetch if "csa::" in n})
+    with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_bench.md"), "w") as f:
+        f.write(f"# HBM traffic per dispatch of every library kernel in the bench run ({workload} prefill legs "
+                "and the decode legs)\n\n")
         f.write("Commands (repository root, run from /tmp with TMPDIR=/tmp):\n\n```\n" + "\n".join(cmds) + "\n```\n\n")
-        f.write("| quantity | value |\n|---|---|\n")
-        f.write(f"| FETCH_SIZE per dispatch (KiB, median of {nf}) | {fetch_kib:.1f} |\n")
-        f.write(f"| WRITE_SIZE per dispatch (KiB, median of {nw}) | {write_kib:.1f} |\n")
-        f.write(f"| copy probe (1 GiB read + 1 GiB written): FETCH_SIZE / WRITE_SIZE KiB | {cf_kib:.1f} / {cw_kib:.1f} |\n")
-        f.write(f"| bytes per counter KiB (fetch / write) | {f_scale:.1f} / {w_scale:.1f} |\n")
-        f.write(f"| HBM bytes per launch | {hbm:.4g} |\n")
-        f.write(f"| kernel sources sha256[:16] | {kernel_hash()} |\n")
-        f.write("\nFETCH_SIZE counts what the L2 caches fetch from the fabric, Infinity-Cache hits included, "
-                "so it bounds the HBM reads from above. The algorithmic bytes of one launch are the visible "
-                "keys, q_I, the head weights and the selected indices.\n")
-    print(json.dumps(d))
+        f.write(f"Counter units scaled by the copy probe: FETCH_SIZE x {f_scale:.1f}, WRITE_SIZE x {w_scale:.1f} "
+                "bytes per unit. Median over the kernel's dispatches (every workload of the run mixed: read "
+                "with the dispatch count).\n\n")
+        f.write("| kernel | dispatches | fetched MB | written MB |\n|---|---|---|---|\n")
+        for nm in names:
+            fk, nf = median_of(fetch, lambda n, nm=nm: "csa::" in n and _short_kernel(n) == nm)
+            wk, _ = median_of(write, lambda n, nm=nm: "csa::" in n and _short_kernel(n) == nm)
+            if fk is None:
+                continue
+            f.write(f"| {nm} | {nf} | {fk * f_scale / 1e6:.2f} | {(wk or 0) * w_scale / 1e6:.2f} |\n")
+    print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in out.items()}))
+
+
+def attn_summary(pmc_dir, workload):
+    """Counters of the 128-head attention kernel (attn_pairs, bf16 rows) from two rocprofv3 --pmc passes:
+    matrix-core busy, LDS bank-conflict cycles against LDS active cycles, LDS wait and VALU / MFMA /
+    LDS instruction counts. Writes profiles/attn_pairs_counters_<workload>.md."""
+    c1 = "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_INSTS_LDS GRBM_GUI_ACTIVE"
+    c2 = "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE"
+    bench_cmd = COUNTER_BENCH + workload + " --no-decode"
+    cmds = [f"rocprofv3 --pmc {c1} --output-format csv -d <out>/attn1 -o run -- {bench_cmd}",
+            f"rocprofv3 --pmc {c2} --output-format csv -d <out>/attn2 -o run -- {bench_cmd}",
+            f"python3 /root/repo/bench.py --attn-summary <out> --workload {workload}"]
+    vals = {}
+    for run in ("attn1", "attn2"):
+        import csv
+        per = {}
+        with open(os.path.join(pmc_dir, run, "run_counter_collection.csv"), newline="") as f:
+            for row in csv.DictReader(f):
+                if "attn_pairs<8, 0, 0>" not in row["Kernel_Name"] and "attn_pairs<8, 1, 0>" not in row["Kernel_Name"]:
+                    continue
+                key = (row["Dispatch_Id"], row["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+        disp = sorted({k[0] for k in per}, key=int)
+        # the largest dispatches: the chunk's attention (the step's and the kernel timed alone)
+        big = sorted(disp, key=lambda d_: -per.get((d_, "SQ_WAVES"), per.get((d_, "SQ_INSTS_MFMA"), 0)))[:4]
+        for cname in {k[1] for k in per}:
+            vals[cname] = float(np.median([per[(d_, cname)] for d_ in big if (d_, cname) in per]))
+    simds = 256 * 4
+    gui = vals["GRBM_GUI_ACTIVE"] / 8
+    rows = [("MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs))",
+             f"{100 * vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.1f}%"),
+            ("LDS bank-conflict cycles / LDS active cycles", f"{100 * vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_LDS_IDX_ACTIVE']:.1f}%"),
+            ("LDS active cycles per CU / GPU cycles", f"{100 * vals['SQ_LDS_IDX_ACTIVE'] / 256 / gui:.1f}%"),
+            ("waves", f"{vals['SQ_WAVES']:.0f}"),
+            ("MFMA instructions", f"{vals['SQ_INSTS_MFMA']:.4g}"),
+            ("VALU instructions (MFMA included) per MFMA", f"{vals['SQ_INSTS_VALU'] / vals['SQ_INSTS_MFMA']:.2f}"),
+            ("LDS instructions per MFMA", f"{vals['SQ_INSTS_LDS'] / vals['SQ_INSTS_MFMA']:.2f}"),
+            ("wave-cycles waiting (any) / wave-cycles", f"{100 * vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.1f}%"),
+            ("wave-cycles waiting to issue (any) / wave-cycles", f"{100 * vals['SQ_WAIT_INST_ANY'] / vals['SQ_WAVE_CYCLES']:.1f}%"),
+            ("wave-cycles waiting to issue LDS / wave-cycles", f"{100 * vals['SQ_WAIT_INST_LDS'] / vals['SQ_WAVE_CYCLES']:.1f}%"),
+            ("LDS address conflicts", f"{vals['SQ_LDS_ADDR_CONFLICT']:.0f}"),
+            ("GPU cycles per dispatch (one XCD)", f"{gui:.4g}")]
+    with open(os.path.join(ROOT, "profiles", f"attn_pairs_counters_{workload}.md"), "w") as f:
+        f.write(f"# attn_pairs (128 heads, bf16 rows), {workload}: matrix-core, LDS and wait counters\n\n")
+        f.write("Commands (repository root, run from /tmp with TMPDIR=/tmp):\n\n```\n" + "\n".join(cmds) + "\n```\n\n")
+        f.write("Median over the four largest attn_pairs dispatches of the run (the chunk's attention in the step "
+                "and timed alone).\n\n| quantity | value |\n|---|---|\n")
+        for k, v in rows:
+            f.write(f"| {k} | {v} |\n")
+    print(json.dumps(dict(rows)))
 
 
 def mfma_summary(pmc_dir, workload):
@@ -184,7 +302,8 @@ def mfma_summary(pmc_dir, workload):
     gui = _counter_rows(path, "GRBM_GUI_ACTIVE")
     simds, xcds = 256 * 4, 8
     rows = []
-    for label, key in (("index_prefill_mfma", "index_prefill_mfma"), ("attn_pairs", "attn_pairs"),
+    for label, key in (("index_prefill_mfma", "index_prefill_mfma"), ("index_prefill_fp4", "index_prefill_fp4"),
+                       ("attn_pairs", "attn_pairs"),
                        ("attn_mfma", "attn_mfma<"), ("projection (hipBLASLt)", "Cijk_")):
         b = [v for n, v in busy if key in n]
         g = [v for n, v in gui if key in n]
@@ -192,7 +311,7 @@ def mfma_summary(pmc_dir, workload):
             continue
         share = [100.0 * bb / (gg / xcds * simds) for bb, gg in zip(b, g)]
         rows.append((label, len(b), float(np.median(share)), float(np.median(g)) / xcds))
-    bench_cmd = ("python3 /root/repo/bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline --workload " + workload)
+    bench_cmd = COUNTER_BENCH + workload + " --no-decode"
     cmds = [f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d <out>/mfma -o run -- {bench_cmd}",
             f"python3 /root/repo/bench.py --mfma-summary <out> --workload {workload}"]
     with open(os.path.join(ROOT, "profiles", f"mfma_busy_{workload}.md"), "w") as f:
@@ -606,7 +725,12 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise four rocprofv3 --pmc runs under DIR")
     ap.add_argument("--mfma-summary", metavar="DIR", help="summarise one rocprofv3 --pmc run of the MFMA busy counter")
+    ap.add_argument("--attn-summary", metavar="DIR", help="summarise two rocprofv3 --pmc runs of attention counters")
+    ap.add_argument("--no-peak-probes", action="store_true", help="skip the measured HBM / GEMM ceilings")
     args = ap.parse_args()
+    if args.attn_summary:
+        attn_summary(args.attn_summary, args.workload)
+        return
     if args.mfma_summary:
         mfma_summary(args.mfma_summary, args.workload)
         return
@@ -694,6 +818,14 @@ def main():
         res["decode_state"] = bench_decode_state(max(args.steps, 10), 2)
     if not args.no_hca:
         res["hca"] = bench_hca(min(args.steps, 5), 2)
+    if not args.no_peak_probes:
+        log("peak probes")
+        pk = peak_probes()
+        res["measured_peaks"] = pk
+        res["roofline"]["frac_measured_peak"] = round(ach / pk["mfma_bf16_tflops"], 4)
+        res["roofline"]["measured_peak"] = pk["mfma_bf16_tflops"]
+        for v in res.get("decode", {}).values():
+            v["hbm_frac_measured_read"] = round(v["hbm_gbs"] / pk["hbm_read_gbs"], 4)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, r["inp"])

@@ -56,6 +56,10 @@ __global__ void copy_rows_kernel(int rows, int cols, int esz, const uint8_t* src
 
 }  // namespace
 
+// error reporting for the probe entry points (csa_probe.h), through this thread's message
+int probe_fail(const char* msg) { return fail(CSA_ERR_ARG, "%s", msg); }
+int probe_status(hipError_t e, const char* what) { return hip_status(e, what); }
+
 hipError_t launch_copy_rows(int B, int rows, int cols, int esz, const void* src, int64_t src_ld, int64_t src_seq,
                             void* dst, int64_t dst_ld, int64_t dst_seq, hipStream_t s) {
   if (B == 0 || rows == 0 || cols == 0) return hipSuccess;

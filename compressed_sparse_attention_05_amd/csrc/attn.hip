@@ -505,9 +505,8 @@ struct PairSmem {
 constexpr int kOutStageRow = 528;
 static_assert(8 * 32 * kOutStageRow <= sizeof(PairSmem<8>::kn) + sizeof(PairSmem<8>::sx), "output staging fits the ring");
 
-// Workgroups of one head group per (row, split), several splits: the splits of a row are grouped
-// on one XCD.
-__host__ __device__ inline bool pairs_xcd_grouped(int H, int NW, int n_splits) { return H == 16 * NW && n_splits > 1; }
+// Several splits: the workgroups of a row (its splits and head groups) are grouped on one XCD.
+__host__ __device__ inline bool pairs_xcd_grouped(int H, int NW, int n_splits) { return n_splits > 1; }
 
 template <int NW>
 __host__ __device__ inline size_t attn_stage_offset(const AttnArgs& a) {
@@ -532,12 +531,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   int hg, split;
   int64_t row;
   if (pairs_xcd_grouped(a.H, NW, sp.n_splits)) {
-    // the splits of a row run on one XCD (workgroups are dealt to the 8 XCDs round-robin), so the
-    // row's q is read once into that XCD's L2
+    // the splits and head groups of a row run on one XCD (workgroups are dealt to the 8 XCDs
+    // round-robin), so the row's q and its gathered keys are read once into that XCD's L2
     const int64_t j = blockIdx.x >> 3;
-    hg = 0;
-    split = (int)(j % sp.n_splits);
-    row = (j / sp.n_splits) * 8 + (blockIdx.x & 7);
+    hg = (int)(j % n_hg);
+    split = (int)((j / n_hg) % sp.n_splits);
+    row = (j / n_hg / sp.n_splits) * 8 + (blockIdx.x & 7);
     if (row >= (int64_t)a.B * a.T) return;  // padding workgroup of the last row group
   } else {
     hg = (int)(blockIdx.x % n_hg);
@@ -1028,7 +1027,10 @@ bool use_attn_mfma(const AttnArgs& a) {
 }
 
 constexpr int kDecodeRows = 8;     // fewer query rows per sequence than this: decode regime
-constexpr int kSplitKeys = 288;    // keys per split in the decode regime (9 tiles: 1152 keys in 4)
+#ifndef CSA_DECODE_SPLIT_KEYS
+#define CSA_DECODE_SPLIT_KEYS 288
+#endif
+constexpr int kSplitKeys = CSA_DECODE_SPLIT_KEYS;  // keys per split in the decode regime (a multiple of 32)
 constexpr int kDenseSplitKeys = 512;  // dense mode (thousands of keys per row): 16 tiles per split
 
 // most keys any query row of the call can have (dense: every entry slot visible; the positions
@@ -1076,7 +1078,13 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStr
 // sequence's output must not depend on what else is in the batch. (Dealing a row's 128 heads to
 // more workgroups of fewer wave pairs for small-batch decode was measured slower: one pair per
 // compute unit leaves two of its four SIMDs idle and nothing hides a pair's own latency chain.)
-int attn_waves(const AttnArgs& a) { return a.H == 128 ? 8 : 4; }
+#ifndef CSA_DECODE_NW
+#define CSA_DECODE_NW 8
+#endif
+int attn_waves(const AttnArgs& a) {
+  if (a.H != 128) return 4;
+  return a.T < kDecodeRows && !a.dense ? CSA_DECODE_NW : 8;
+}
 
 template <int NW, int OT, int FMT>
 hipError_t launch_pairs_fmt(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
@@ -1084,7 +1092,8 @@ hipError_t launch_pairs_fmt(const AttnArgs& a, const AttnSplit& sp, int64_t R, h
   hipError_t e;
   if ((e = allow_lds((const void*)attn_pairs<NW, OT, FMT>, lds)) != hipSuccess) return e;
   const int64_t n_hg = a.H / (16 * NW);
-  const int64_t blocks = pairs_xcd_grouped(a.H, NW, sp.n_splits) ? ceil_div(R, 8) * 8 * sp.n_splits : R * sp.n_splits * n_hg;
+  const int64_t blocks = pairs_xcd_grouped(a.H, NW, sp.n_splits) ? ceil_div(R, 8) * 8 * sp.n_splits * n_hg
+                                                                   : R * sp.n_splits * n_hg;
   hipLaunchKernelGGL((attn_pairs<NW, OT, FMT>), dim3((unsigned)blocks), dim3(NW * 64), lds, s, a, sp);
   return hipGetLastError();
 }
@@ -1096,6 +1105,7 @@ hipError_t launch_pairs(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipSt
 template <int OT>
 hipError_t launch_mfma_for(const AttnArgs& a, const AttnSplit& sp, int64_t R, hipStream_t s) {
   if (attn_waves(a) == 8) return launch_pairs<8, OT>(a, sp, R, s);
+  if (a.H == 128) return launch_pairs<4, OT>(a, sp, R, s);  // decode: two 64-head groups per row
   // 64-head layers over records: the pairs kernel with one wave group (it alone stages and converts
   // records)
   if (a.entry_fmt) return launch_pairs_fmt<4, OT, 1>(a, sp, R, s);

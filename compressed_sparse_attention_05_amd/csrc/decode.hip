@@ -65,17 +65,23 @@ __device__ __forceinline__ void norm_rope_strided(float (&v)[kMaxPer], int D, co
     }
   }
   if (rope_dims > 0) {
+    // only the 64-dim chunks that hold rotated dims, in a loop that is not unrolled (one copy of the
+    // angle code); chunk j's value is picked from and put back into v by selects on the uniform j
     const int rs = D - rope_dims;
+#pragma unroll 1
+    for (int j = rs / 64; j < (D + 63) / 64; ++j) {
+      float x = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      if (64 * j >= D || 64 * j + 63 < rs) continue;  // uniform: the whole wave takes part in the swap
+      for (int t = 0; t < kMaxPer; ++t) x = t == j ? v[t] : x;
       const int d = lane + 64 * j;
-      const float other = __shfl_xor(v[j], 1, 64);
+      const float other = __shfl_xor(x, 1, 64);
       if (d >= rs && d < D) {
         float c, s;
         rope_cos_sin((double)pos, (d - rs) >> 1, rope_dims, lt, false, c, s);
-        v[j] = ((d - rs) & 1) == 0 ? v[j] * c - other * s : other * s + v[j] * c;
+        x = ((d - rs) & 1) == 0 ? x * c - other * s : other * s + x * c;
       }
+#pragma unroll
+      for (int t = 0; t < kMaxPer; ++t) v[t] = t == j ? x : v[t];
     }
   }
   if (DT == CSA_BF16) {

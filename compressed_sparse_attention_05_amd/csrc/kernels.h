@@ -214,6 +214,9 @@ hipError_t launch_copy_rows(int B, int rows, int cols, int esize, const void* sr
                             int64_t src_seq, void* dst, int64_t dst_ld, int64_t dst_seq,
                             hipStream_t s);
 
+int probe_fail(const char* msg);
+int probe_status(hipError_t e, const char* what);
+
 constexpr int kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
 constexpr int kMaxTopK = 4096;       // largest top_k the kernels take
 

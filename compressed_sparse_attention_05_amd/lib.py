@@ -23,6 +23,7 @@ EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress"
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
            "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8",
            "csa_hca_decode_step", "csa_decode_step_noalloc", "csa_mxfp4_quantize")
+PROBE_EXPORTS = ("csa_probe_hbm_read", "csa_probe_mfma_bf16", "csa_probe_sink_words")
 STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -97,6 +98,12 @@ def load() -> ctypes.CDLL:
     lib.csa_decode_step_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, vp, i32, vp, vp, vp,
                                             vp, ctypes.POINTER(DecodeState), vp, i32, vp, vp]
     lib.csa_mxfp4_quantize.argtypes = [i64, i32, i32, vp, i64, vp, vp, vp]
+    lib.csa_probe_hbm_read.argtypes = [vp, sz, vp, vp]
+    lib.csa_probe_hbm_read.restype = i32
+    lib.csa_probe_mfma_bf16.argtypes = [i32, vp, vp]
+    lib.csa_probe_mfma_bf16.restype = i32
+    lib.csa_probe_sink_words.argtypes = []
+    lib.csa_probe_sink_words.restype = sz
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
               "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8", "csa_hca_decode_step",
@@ -312,6 +319,22 @@ def csa_mxfp4_quantize(x, codes=None, scales=None):
         raise ValueError("codes / scales must be contiguous [R, D/2] / [R, D/32]")
     _check(load().csa_mxfp4_quantize(R, D, _dt(x), _p(x), x.stride(0), _p(codes), _p(scales), _stream()))
     return codes, scales
+
+
+def probe_sink(device="cuda") -> torch.Tensor:
+    """A sink buffer for the ceiling probes (include/csa_probe.h)."""
+    return torch.empty(load().csa_probe_sink_words(), dtype=torch.int32, device=device)
+
+
+def probe_hbm_read(buf: torch.Tensor, sink: torch.Tensor):
+    """Reads all of buf (a contiguous device tensor, 16-byte aligned, nbytes % 16 == 0) once."""
+    _check(load().csa_probe_hbm_read(_p(buf), buf.numel() * buf.element_size(), _p(sink), _stream()))
+
+
+def probe_mfma_bf16(iters: int, sink: torch.Tensor) -> int:
+    """Runs the MFMA probe; returns its FLOP count."""
+    _check(load().csa_probe_mfma_bf16(iters, _p(sink), _stream()))
+    return (load().csa_probe_sink_words() // 64) * 4 * 32768 * iters
 
 
 def csa_hca_compress(cv, z, bias, entries, *, pos0, m: int):

@@ -11,8 +11,8 @@ from compressed_sparse_attention_05_amd import lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "csa.h")).read()
+def _declared(header="csa.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(csa_[a-z0-9_]+)\s*\(", src)))
 
@@ -30,6 +30,12 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
     assert set(lib.EXPORTS) == set(_declared())
     assert lib.csa_version() == 3
+    # the ceiling probes of include/csa_probe.h
+    for n in _declared("csa_probe.h"):
+        assert hasattr(L, n), n
+    assert set(lib.PROBE_EXPORTS) == set(_declared("csa_probe.h"))
+    assert os.listdir(os.path.join(ROOT, "include")) and \
+        sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == ["csa.h", "csa_probe.h"]
 
 
 def _d(**kw):
@@ -265,3 +271,11 @@ def test_mxfp4_key_caches_need_their_scales():
     rc, msg = _err(L.csa_decode_step(ctypes.byref(d), ctypes.byref(wd), 2, p, lib.CSA_BF16, p, p, p, p,
                                      ctypes.byref(st), p, lib.CSA_F32, None, None, 0, None))
     assert rc == -1 and "aligned" in msg
+
+
+def test_probes_reject_bad_arguments():
+    L = lib.load()
+    rc, msg = _err(L.csa_probe_hbm_read(ctypes.c_void_p(4100), 4096, ctypes.c_void_p(4096), None))
+    assert rc == -1 and "aligned" in msg
+    rc, msg = _err(L.csa_probe_mfma_bf16(0, ctypes.c_void_p(4096), None))
+    assert rc == -1 and "iters" in msg
