@@ -568,11 +568,11 @@ def cpu_baseline_decode(name):
                                         f"({dt:.2f} s) x {wl.B}", "host": hi}
 
 
-def bench_decode_state(steps, warmup):
-    """Token-by-token decode of the decode128k batch over a state cache (csa_decode_step) with the
-    pages' cache format (584-byte FP8 entry records) and QK-norm + RoPE on: four consecutive steps
-    L .. L+3, the last of which completes a block and compresses its entry and key. Reported per
-    step, averaged over the block."""
+def bench_decode_state(steps, warmup, records=True):
+    """Token-by-token decode of the decode128k batch over a state cache (csa_decode_step) with
+    QK-norm + RoPE on, over the pages' cache format (584-byte FP8 entry records) or bf16 entry rows:
+    four consecutive steps L .. L+3, the last of which completes a block and compresses its entry and
+    key. Reported per step, averaged over the block."""
     import torch
     from compressed_sparse_attention_05_amd import layer, lib
     from synth import gen as G
@@ -584,9 +584,12 @@ def bench_decode_state(steps, warmup):
     inp = G.make_inputs(wl)
     d = layer.dims(wl.m, wl.D, wl.H, wl.H_I, wl.D_I, wl.k, wl.W)
     N = wl.L // wl.m
-    st = layer.CSADecodeState(d, wl.B, N + 1, records=True)
+    st = layer.CSADecodeState(d, wl.B, N + 1, records=records)
     ent = act(inp["entries"], wl)
-    lib.csa_entry_pack(ent, st.entries[:, :N])
+    if records:
+        lib.csa_entry_pack(ent, st.entries[:, :N])
+    else:
+        st.entries[:, :N] = ent
     del ent
     st.keys[:, :N] = act(inp["keys"], wl)
     raw = act(inp["kv_raw"], wl)                      # positions L-127 .. L
@@ -624,7 +627,8 @@ def bench_decode_state(steps, warmup):
         flush.sum()
         ms += timed_events(four, 1, torch.cuda.synchronize)
     us = float(np.median(ms)) * 1e3 / 4
-    return {"us_per_step": round(us, 2), "B": wl.B, "context_tokens": wl.L, "entries": "584-byte FP8 records",
+    return {"us_per_step": round(us, 2), "B": wl.B, "context_tokens": wl.L,
+            "entries": "584-byte FP8 records" if records else "bf16 rows",
             "qk_norm_rope": True, "what": "4 steps at L..L+3, one block completed (entry + key compressed)"}
 
 
@@ -816,6 +820,7 @@ def main():
         dfid = bench_decode("decode128k", max(args.steps, 10), 3, fid=True)
         res["fid"]["decode128k_us_per_step"] = dfid["us_per_step"]
         res["decode_state"] = bench_decode_state(max(args.steps, 10), 2)
+        res["decode_state_bf16_entries"] = bench_decode_state(max(args.steps, 10), 2, records=False)
     if not args.no_hca:
         res["hca"] = bench_hca(min(args.steps, 5), 2)
     if not args.no_peak_probes:

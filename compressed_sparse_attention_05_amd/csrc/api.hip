@@ -289,11 +289,12 @@ DecodeWs hca_decode_ws(const csa_dims* d, int B, int64_t n_cap, int dtype) {
 
 // raw_ring > 0: kv_raw is a ring of raw_ring rows (position u in row u % raw_ring) holding at least
 // each query's window; raw_pos and raw_len are then not used.
-int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, const int64_t* q_pos, int in_dtype,
-              const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride,
-              int64_t n_cap, const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
-              const int64_t* raw_pos, int64_t raw_len, const float* sink, void* out, int out_dtype, void* ws,
-              size_t ws_bytes, void* stream, int entry_fmt = 0, int64_t raw_ring = 0, int64_t raw_off = 0) {
+// Validates the attention's arguments and fills *out (nothing is launched).
+int attn_prepare(bool dense, const csa_dims* dims, int B, int T, const int64_t* q_pos, int in_dtype,
+                 const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride,
+                 int64_t n_cap, const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+                 const int64_t* raw_pos, int64_t raw_len, const float* sink, void* out, int out_dtype,
+                 int entry_fmt, int64_t raw_ring, int64_t raw_off, AttnArgs* res) {
   int rc = check_dims(dims, !dense);
   if (rc) return rc;
   if (B < 0 || T < 0) return fail(CSA_ERR_ARG, "B and T must be >= 0");
@@ -350,9 +351,46 @@ int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, 
   a.out = out;
   a.entry_fmt = entry_fmt;
   a.raw_ring = raw_ring;
-  rc = check_ws(ws, ws_bytes, attn_workspace(a));
+  *res = a;
+  return CSA_OK;
+}
+
+int attn_run(const char* name, const AttnArgs& a, void* ws, size_t ws_bytes, void* stream) {
+  if ((int64_t)a.B * a.T == 0) return CSA_OK;
+  int rc = check_ws(ws, ws_bytes, attn_workspace(a));
   if (rc) return rc;
   return hip_status(launch_attn(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), name);
+}
+
+// The query's QK-norm / RoPE and the output's back-rotation folded into the attention, where its
+// kernels take them ("Anatomy of a Frontier Model", bullet "QK-norm and partial RoPE"); false: the
+// caller runs the separate passes.
+bool attn_try_fuse(AttnArgs& a, const csa_weights* w) {
+  if (!w || (!w->gamma_q && w->rope_dims == 0)) return false;
+  if (w->gamma_q && !aligned(w->gamma_q, 16)) return false;  // staged as 16-byte vectors
+  a.fuse_fid = true;
+  a.gamma_q = w->gamma_q;
+  a.q_eps = w->norm_eps;
+  a.rope_dims = w->rope_dims;
+  a.rope_lt = w->rope_dims > 0 ? std::log2((double)w->rope_theta) : 0.0;
+  if (attn_fuses_fid(a)) return true;
+  a.fuse_fid = false;
+  a.gamma_q = nullptr;
+  a.rope_dims = 0;
+  return false;
+}
+
+int attn_call(const char* name, bool dense, const csa_dims* dims, int B, int T, const int64_t* q_pos, int in_dtype,
+              const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries, int64_t entries_seq_stride,
+              int64_t n_cap, const int32_t* idx, const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+              const int64_t* raw_pos, int64_t raw_len, const float* sink, void* out, int out_dtype, void* ws,
+              size_t ws_bytes, void* stream, int entry_fmt = 0, int64_t raw_ring = 0, int64_t raw_off = 0) {
+  AttnArgs a{};
+  int rc = attn_prepare(dense, dims, B, T, q_pos, in_dtype, q, q_ld, q_seq_stride, entries, entries_seq_stride, n_cap,
+                        idx, kv_raw, raw_ld, raw_seq_stride, raw_pos, raw_len, sink, out, out_dtype, entry_fmt,
+                        raw_ring, raw_off, &a);
+  if (rc || (int64_t)B * T == 0) return rc;
+  return attn_run(name, a, ws, ws_bytes, stream);
 }
 
 // Compressor arguments common to csa_compress, csa_hca_compress and csa_forward.
@@ -754,17 +792,26 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, const int
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
   const bool qfid = w->gamma_q || w->rope_dims > 0;
-  // the token joins the state; a completed block's entry and key are pooled; the query is
-  // normalised and rotated at its position
-  // (and, for MXFP4 keys, the indexer query is quantised)
-  const bool kfp4 = st->key_fmt != 0;
-  rc = decode_append("csa_decode_step", dims, w, B, pos, dtype, q, kv, comp, st, false, qfid ? base + L.q : nullptr, s,
-                     q_idx, base + L.qi, base + L.qis);
-  if (rc) return rc;
-  const void* qq = qfid ? base + L.q : q;
   int32_t* idx = out_idx ? out_idx : reinterpret_cast<int32_t*>(base + L.idx);
   void* scratch = base + L.scratch;
   const size_t scratch_bytes = L.total - L.scratch;
+  // the attention reads the window straight from the ring; where it takes the query's norm and
+  // rotation itself (and turns the output back), the append leaves the query alone
+  AttnArgs at{};
+  rc = attn_prepare(false, dims, B, 1, pos, dtype, q, (int64_t)H * D, (int64_t)H * D, st->entries,
+                    n_cap * (st->entry_fmt ? (int64_t)kEntryRecordBytes : D), n_cap, idx, st->win, D, (int64_t)W * D,
+                    nullptr, 0, w->sink, out, out_dtype, st->entry_fmt, W, 0, &at);
+  if (rc) return rc;
+  const bool fused = attn_try_fuse(at, w);
+  const bool qpass = qfid && !fused;
+  // the token joins the state; a completed block's entry and key are pooled; the query is
+  // normalised and rotated at its position unless the attention does it (and, for MXFP4 keys, the
+  // indexer query is quantised)
+  const bool kfp4 = st->key_fmt != 0;
+  rc = decode_append("csa_decode_step", dims, w, B, pos, dtype, q, kv, comp, st, false, qpass ? base + L.q : nullptr, s,
+                     q_idx, base + L.qi, base + L.qis);
+  if (rc) return rc;
+  if (qpass) at.q = base + L.q;
   if (kfp4)
     rc = csa_index_topk(dims, B, 1, pos, CSA_MXFP4, base + L.qi, 0, 0, base + L.qis, w->w_head, 0, st->keys, 0,
                         st->key_scales, n_cap, idx, nullptr, scratch, scratch_bytes, stream);
@@ -772,12 +819,9 @@ int csa_decode_step(const csa_dims* dims, const csa_weights* w, int B, const int
     rc = csa_index_topk(dims, B, 1, pos, dtype, q_idx, (int64_t)HI * DI, (int64_t)HI * DI, nullptr, w->w_head, 0,
                         st->keys, n_cap * DI, nullptr, n_cap, idx, nullptr, scratch, scratch_bytes, stream);
   if (rc) return rc;
-  // the window, read by the attention straight from the ring
-  rc = attn_call("csa_decode_step", false, dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D, st->entries,
-                 n_cap * (st->entry_fmt ? (int64_t)kEntryRecordBytes : D), n_cap, idx, st->win, D, (int64_t)W * D,
-                 nullptr, 0, w->sink, out, out_dtype, scratch, scratch_bytes, stream, st->entry_fmt, W);
+  rc = attn_run("csa_decode_step", at, scratch, scratch_bytes, stream);
   if (rc) return rc;
-  if (w->rope_dims > 0) {
+  if (w->rope_dims > 0 && !fused) {
     rc = norm_rope_call(B, 1, H, D, out_dtype, out, (int64_t)H * D, (int64_t)H * D, out, (int64_t)H * D,
                         (int64_t)H * D, nullptr, 0.f, w->rope_dims, w->rope_theta, pos, 0, 1, 1, stream);
     if (rc) return rc;
@@ -823,16 +867,20 @@ int csa_hca_decode_step(const csa_dims* dims, const csa_weights* w, int B, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* base = static_cast<uint8_t*>(ws);
   const bool qfid = w->gamma_q || w->rope_dims > 0;
+  AttnArgs at{};
+  rc = attn_prepare(true, dims, B, 1, pos, dtype, q, (int64_t)H * D, (int64_t)H * D, st->entries,
+                    n_cap * (st->entry_fmt ? (int64_t)kEntryRecordBytes : D), n_cap, nullptr, st->win, D,
+                    (int64_t)W * D, nullptr, 0, w->sink, out, out_dtype, st->entry_fmt, W, 0, &at);
+  if (rc) return rc;
+  const bool fused = attn_try_fuse(at, w);
+  const bool qpass = qfid && !fused;
   rc = decode_append("csa_hca_decode_step", dims, w, B, pos, dtype, q, kv, comp, st, true,
-                     qfid ? base + L.q : nullptr, s);
+                     qpass ? base + L.q : nullptr, s);
   if (rc) return rc;
-  const void* qq = qfid ? base + L.q : q;
-  rc = attn_call("csa_hca_decode_step", true, dims, B, 1, pos, dtype, qq, (int64_t)H * D, (int64_t)H * D,
-                 st->entries, n_cap * (st->entry_fmt ? (int64_t)kEntryRecordBytes : D), n_cap, nullptr, st->win, D,
-                 (int64_t)W * D, nullptr, 0, w->sink, out, out_dtype, base + L.scratch, L.total - L.scratch, stream,
-                 st->entry_fmt, W);
+  if (qpass) at.q = base + L.q;
+  rc = attn_run("csa_hca_decode_step", at, base + L.scratch, L.total - L.scratch, stream);
   if (rc) return rc;
-  if (w->rope_dims > 0) {
+  if (w->rope_dims > 0 && !fused) {
     rc = norm_rope_call(B, 1, H, D, out_dtype, out, (int64_t)H * D, (int64_t)H * D, out, (int64_t)H * D,
                         (int64_t)H * D, nullptr, 0.f, w->rope_dims, w->rope_theta, pos, 0, 1, 1, stream);
     if (rc) return rc;
@@ -951,7 +999,17 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, const 
     e = launch_copy_rows(B, T, D, es, col(c_kv), ntot, (int64_t)T * ntot, wrows, D, cache->win_cap * D, s);
     if (e != hipSuccess) return hip_status(e, "csa_forward: window copy");
   }
-  if (w->gamma_q || w->rope_dims > 0) {  // the queries, in place in the projection buffer
+  // window row r of sequence b holds position pos0[b] - (W - 1) + r; the attention takes the queries'
+  // norm and rotation (and turns the output back) where its kernels can, else the queries are
+  // normalised in place in the projection buffer
+  AttnArgs at{};
+  rc = attn_prepare(false, dims, B, T, pos0, dtype, col(c_q), ntot, (int64_t)T * ntot, cache->entries,
+                    cache->n_cap * (records ? (int64_t)kEntryRecordBytes : D), cache->n_cap, idx, cache->win, D,
+                    cache->win_cap * D, pos0, (int64_t)W - 1 + T, w->sink, out, out_dtype, records ? 1 : 0, 0,
+                    -(int64_t)(W - 1), &at);
+  if (rc) return rc;
+  const bool fused = attn_try_fuse(at, w);
+  if ((w->gamma_q || w->rope_dims > 0) && !fused) {
     rc = norm_rope_call(B, T, H, D, dtype, col(c_q), ntot, (int64_t)T * ntot, col(c_q), ntot, (int64_t)T * ntot,
                         w->gamma_q, w->norm_eps, w->rope_dims, w->rope_theta, pos0, 0, 1, 0, stream);
     if (rc) return rc;
@@ -974,13 +1032,9 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, const 
                         cache->keys, cache->n_cap * DI, nullptr, cache->n_cap, idx, nullptr, xws, x_bytes, stream);
   }
   if (rc) return rc;
-  // window row r of sequence b holds position pos0[b] - (W - 1) + r
-  rc = attn_call("csa_forward", false, dims, B, T, pos0, dtype, col(c_q), ntot, (int64_t)T * ntot, cache->entries,
-                 cache->n_cap * (records ? (int64_t)kEntryRecordBytes : D), cache->n_cap, idx, cache->win, D,
-                 cache->win_cap * D, pos0, (int64_t)W - 1 + T, w->sink, out, out_dtype, xws, x_bytes, stream,
-                 records ? 1 : 0, 0, -(int64_t)(W - 1));
+  rc = attn_run("csa_forward", at, xws, x_bytes, stream);
   if (rc) return rc;
-  if (w->rope_dims > 0) {
+  if (w->rope_dims > 0 && !fused) {
     rc = norm_rope_call(B, T, H, D, out_dtype, out, (int64_t)H * D, (int64_t)T * H * D, out, (int64_t)H * D,
                         (int64_t)T * H * D, nullptr, 0.f, w->rope_dims, w->rope_theta, pos0, 0, 1, 1, stream);
     if (rc) return rc;

@@ -14,6 +14,7 @@
 // With fewer than 8 query rows per sequence the key list is cut into fixed splits and
 // attn_combine merges the partial results.
 #include "kernels.h"
+#include "rope.h"
 
 namespace csa {
 
@@ -513,9 +514,21 @@ __host__ __device__ inline size_t attn_stage_offset(const AttnArgs& a) {
   const size_t keys = a.dense ? 4 : (size_t)(a.k + a.W + 1) * 4;
   return (sizeof(PairSmem<NW>) - sizeof(int32_t) + keys + 15) & ~(size_t)15;
 }
+// the fused QK-norm / RoPE's LDS follows everything else: the cos / sin table of the row's position
+// (rope_dims / 2 pairs), then the query gain gamma_q (512 floats)
+template <int NW>
+__host__ __device__ inline size_t pairs_rope_offset(const AttnArgs& a) {
+  const size_t keys = a.dense ? 4 : (size_t)(a.k + a.W + 1) * 4;  // attn_keys_lds
+  const size_t end = a.entry_fmt ? attn_stage_offset<NW>(a) + (size_t)kNK * kStageRow : sizeof(PairSmem<NW>) + keys;
+  return (end + 15) & ~(size_t)15;
+}
+__host__ __device__ inline size_t rope_tab_bytes(const AttnArgs& a) {
+  return a.fuse_fid && a.rope_dims > 0 ? (size_t)(a.rope_dims / 2) * 8 : 0;
+}
 template <int NW>
 size_t pairs_lds(const AttnArgs& a) {
-  return a.entry_fmt ? attn_stage_offset<NW>(a) + (size_t)kNK * kStageRow : sizeof(PairSmem<NW>) + attn_keys_lds(a);
+  const size_t g = a.fuse_fid && a.gamma_q ? 512 * sizeof(float) : 0;
+  return pairs_rope_offset<NW>(a) + rope_tab_bytes(a) + g;
 }
 
 template <int NW, int OT, int FMT>
@@ -550,6 +563,21 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   const int half = wave & 1;                    // dims 256*half .. +255
   const int hl = lane & 31, hh = lane >> 5;     // head within the pair; k half of a fragment
   const int head = hg * kHeadsPerBlock + (wave >> 1) * 32 + hl;
+
+  // fused QK-norm / RoPE: cos / sin of the row's position for every rotated pair, once per
+  // workgroup, and the query gain, both in LDS (published by barriers before they are read)
+  const bool rot = a.fuse_fid && a.rope_dims > 0;
+  float2* rope_tab = reinterpret_cast<float2*>(smem_raw + pairs_rope_offset<NW>(a));
+  float* gam = reinterpret_cast<float*>(smem_raw + pairs_rope_offset<NW>(a) + rope_tab_bytes(a));
+  if (a.fuse_fid && a.gamma_q && threadIdx.x < 128)
+    reinterpret_cast<float4*>(gam)[threadIdx.x] = reinterpret_cast<const float4*>(a.gamma_q)[threadIdx.x];
+  if (rot) {
+    for (int i = threadIdx.x; i < a.rope_dims / 2; i += kThreads) {
+      float c, sn;
+      rope_cos_sin((double)p, i, a.rope_dims, a.rope_lt, false, c, sn);
+      rope_tab[i] = make_float2(c, sn);
+    }
+  }
 
   // ---- Q_w^T B-fragments: lane l holds head `head`, dims 256*half + 16s + 8hh .. +7. They are
   // loaded after the first burst of key indices: loads complete in order, so waiting for the
@@ -747,6 +775,64 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   } else {
     if (ntiles > 0) load_tile(0, 0);
     if (ntiles > 1) load_tile(1, 1);
+  }
+  // fused QK-norm / RoPE of the query (the values a separate pass would store): the lane's 128 dims
+  // of head `head`, the other 128 of its half in lane ^ 32 and the other half in the partner wave
+  // meet for the sum of squares (through the exchange buffer, free until the first tile); then
+  // x * inv * gamma, the rotation of the pairs past 512 - rope_dims, and rounding to bf16. It runs
+  // while the first tiles' gathers are in flight and issues no memory loads of its own.
+  if (a.fuse_fid) {
+    float inv = 1.f;
+    if (a.gamma_q) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint4 u = __builtin_bit_cast(uint4, qf[s]);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+          ss = fmaf(x, x, ss);
+        }
+      }
+      ss += __shfl_xor(ss, 32, 64);
+      float* xs = reinterpret_cast<float*>(&sm.sx[0][0][0]);
+      xs[wave * 64 + lane] = ss;
+      __syncthreads();  // also publishes the rotation table and the gain
+      ss += xs[(wave ^ 1) * 64 + lane];
+      inv = 1.f / sqrtf(ss / 512.f + a.q_eps);
+    } else {
+      __syncthreads();  // the rotation table is complete
+    }
+    const int rs = 512 - a.rope_dims;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const uint4 u = __builtin_bit_cast(uint4, qf[s]);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      const int d0 = 256 * half + 16 * s + 8 * hh;  // dims d0 .. d0 + 7
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+        y[e] = a.gamma_q ? x * inv * gam[d0 + e] : x;
+      }
+      if (rot && d0 + 8 > rs) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          if (d0 + e < rs) continue;
+          const float2 cs = rope_tab[(d0 + e - rs) >> 1];
+          const float y0 = y[e], y1 = y[e + 1];
+          y[e] = y0 * cs.x - y1 * cs.y;
+          y[e + 1] = y0 * cs.y + y1 * cs.x;
+        }
+      }
+      uint32_t o4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o4[j] = (uint32_t)f2bf(y[2 * j]) | ((uint32_t)f2bf(y[2 * j + 1]) << 16);
+      qf[s] = __builtin_bit_cast(bf16x8, make_uint4(o4[0], o4[1], o4[2], o4[3]));
+    }
+  }
+  if (!FMT) {
     if (ntiles > 1) wait_vmcnt<kRowsPerWave>();
     else wait_vmcnt<0>();
   }
@@ -896,6 +982,24 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   // ---- output: lane holds head `head`, dims 256*half + 32dt + 8(r/4) + 4hh + r%4
   const int dbase = 256 * half + 4 * hh;
   const bool part = sp.n_splits > 1;
+  if (rot && !part) {
+    // the fused back-rotation by the row's position (split rows turn back in the merge); the rotation
+    // is linear, so it is applied before the division by the softmax sum
+    const int rs = 512 - a.rope_dims;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      if (256 * half + 32 * dt + 32 <= rs) continue;  // uniform: no rotated dims in this tile
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int d = dbase + 32 * dt + 8 * (r >> 2) + (r & 3);
+        if (d < rs) continue;
+        const float2 cs = rope_tab[(d - rs) >> 1];
+        const float y0 = o[dt][r], y1 = o[dt][r + 1], sn = -cs.y;
+        o[dt][r] = y0 * cs.x - y1 * sn;
+        o[dt][r + 1] = y0 * sn + y1 * cs.x;
+      }
+    }
+  }
   if (part || (OT == CSA_BF16 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0)) {
     // bf16 rows go out through LDS: the wave writes its 32 heads x 256 dims into its own staging
     // rows, then each store instruction writes two whole 512-byte half rows (16 bytes a lane)
@@ -992,8 +1096,33 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
       for (int i = 0; i < 8; ++i) acc[i] = fmaf(__uint_as_float((w4[i >> 1] >> ((i & 1) * 16)) << 16), wgt, acc[i]);
     }
   }
-  const float inv = 1.f / L;
+  float inv = 1.f / L;
   const int64_t ob = (row * a.H + h) * 512 + lane * 8;
+  if (a.fuse_fid && a.rope_dims > 0) {
+    // the fused back-rotation by the row's position, on O / L (the division is the one the store
+    // would make); lane i of a round forms pair i's angle, the lanes holding rotated dims fetch theirs
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    inv = 1.f;
+    const int rs = 512 - a.rope_dims, npair = a.rope_dims / 2;
+    const int64_t b = row / a.T, t = row % a.T;
+    const double p = (double)(pos_at(a.q_pos, b) + t);
+    for (int i0 = 0; i0 < npair; i0 += 64) {  // uniform
+      float c = 1.f, sn = 0.f;
+      if (i0 + lane < npair) rope_cos_sin(p, i0 + lane, a.rope_dims, a.rope_lt, true, c, sn);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int d = lane * 8 + e;
+        const int src = ((d - rs) >> 1) - i0;  // the lane holding this pair's angle
+        const float cc = __shfl(c, src & 63, 64), ss = __shfl(sn, src & 63, 64);
+        if (d >= rs && src >= 0 && src < 64) {
+          const float y0 = acc[e], y1 = acc[e + 1];
+          acc[e] = y0 * cc - y1 * ss;
+          acc[e + 1] = y0 * ss + y1 * cc;
+        }
+      }
+    }
+  }
   if (OT == CSA_BF16 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0) {
     uint32_t w[4];
 #pragma unroll
@@ -1116,6 +1245,14 @@ hipError_t launch_mfma_for(const AttnArgs& a, const AttnSplit& sp, int64_t R, hi
 }
 
 }  // namespace
+
+bool attn_fuses_fid(const AttnArgs& a) {
+  if (!use_attn_mfma(a) || a.rope_dims < 0 || a.rope_dims > 512 || (a.rope_dims & 1)) return false;
+  // the launches that run attn_pairs, with the rotation table and the gain inside the LDS
+  if (attn_waves(a) == 8) return pairs_lds<8>(a) <= (size_t)kMaxLds;
+  if (a.H == 128 || a.entry_fmt) return pairs_lds<4>(a) <= (size_t)kMaxLds;
+  return false;
+}
 
 size_t attn_workspace(const AttnArgs& a) {
   const AttnSplit sp = plan_split(a);

@@ -205,8 +205,18 @@ struct AttnArgs {
   int64_t raw_ring = 0;  // > 0: kv_raw is a ring of raw_ring rows, position u in row u % raw_ring
   int entry_fmt = 0;  // 0: entries are in_dtype rows of D; 1: 584-byte FP8 records (D = 512), whose
                       // entries_seq_stride counts bytes
+  // QK-norm / partial RoPE folded into the attention (fuse_fid, where attn_fuses_fid): each query
+  // head is RMS-normalised with gain gamma_q (nullable: no norm, eps q_eps) and its last rope_dims dims
+  // turned by its position as it is loaded (then rounded to bf16, as a stored query would be), and the
+  // output's last rope_dims dims are turned back by the position before it is stored.
+  bool fuse_fid = false;
+  const float* gamma_q = nullptr;
+  float q_eps = 0.f;
+  int rope_dims = 0;
+  double rope_lt = 0.0;  // log2(theta)
 };
 size_t attn_workspace(const AttnArgs& a);
+bool attn_fuses_fid(const AttnArgs& a);  // the kernels this call runs take the fused QK-norm / RoPE
 hipError_t launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Copies rows: dst[b, r, :] = src[b, r, :] for r < rows, `cols` elements of `esize` bytes.
