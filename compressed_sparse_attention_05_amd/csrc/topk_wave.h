@@ -12,8 +12,9 @@
 // overflow the buffer, a radix select (8-bit digits, most significant first, histogram in LDS)
 // finds a key at or below the k-th largest that keeps at most cap - 64 keys, the buffer is
 // compacted to the keys at or above it, and the smallest kept key becomes the new threshold. The
-// final selection resolves the exact k-th largest key. At the end the kept entries are sorted ascending by entry index with
-// a bitonic network and written out, padded with -1.
+// final selection resolves the exact k-th largest key. Candidates are offered in ascending entry
+// order and every step keeps the buffer's order, so the kept entries come out in index order,
+// padded with -1.
 //
 // Every function must be called by all 64 lanes of the wave with uniform arguments.
 #pragma once
@@ -188,42 +189,18 @@ struct WaveTopK {
     wave_sync();
   }
 
-  // Final top-k, sorted by entry index ascending; out_idx[j] (and out_score[j]) for j < k.
+  // Final top-k, in entry index order; out_idx[j] (and out_score[j]) for j < k, -1 padded.
+  // Every caller offers its candidates in ascending entry order, appends keep the lane (= entry)
+  // order, and compaction is stable, so the buffer is always sorted by entry index: the exact
+  // k-th-key compaction leaves the answer in order and nothing is sorted.
   __device__ void finish(int32_t* out_idx, float* out_score) {
     const int lane = lane_id();
     if (cnt > k) compact_to(kth_threshold(k));
-    // re-key as (index << 32 | score key) so that sorting orders by entry index
-    int P = 1;
-    while (P < k) P <<= 1;
-    for (int i = lane; i < P; i += 64) {
-      uint64_t v = ~0ull;
-      if (i < cnt) {
-        const uint64_t key = buf[i];
-        v = ((uint64_t)(~(uint32_t)key) << 32) | (key >> 32);
-      }
-      buf[i] = v;  // each lane rewrites only slots it read itself
-    }
-    wave_sync();
-    for (int size = 2; size <= P; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int t = lane; t < (P >> 1); t += 64) {
-          const int i = (t / stride) * stride * 2 + (t % stride);
-          const int j = i + stride;
-          const bool up = (i & size) == 0;
-          const uint64_t a = buf[i], b = buf[j];
-          if ((a > b) == up) {
-            buf[i] = b;
-            buf[j] = a;
-          }
-        }
-        wave_sync();
-      }
-    }
     for (int j = lane; j < k; j += 64) {
-      const uint64_t v = buf[j];
-      const uint32_t idx = (uint32_t)(v >> 32);
-      out_idx[j] = idx == 0xFFFFFFFFu ? -1 : (int32_t)idx;
-      if (out_score) out_score[j] = idx == 0xFFFFFFFFu ? -INFINITY : key_to_score((uint32_t)v);
+      const bool have = j < cnt;
+      const uint64_t v = have ? buf[j] : 0ull;
+      out_idx[j] = have ? (int32_t)(~(uint32_t)v) : -1;
+      if (out_score) out_score[j] = have ? key_to_score((uint32_t)(v >> 32)) : -INFINITY;
     }
     wave_sync();
   }
