@@ -397,21 +397,37 @@ __global__ void __launch_bounds__(kF4QW * 64) index_prefill_fp4(IndexArgs a, int
     const uint8_t* tp = smem + slot * kF4TileBytes;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      float p[4];
+      // the 16 MFMAs of the half (four column groups x four head tiles) are issued first, each into an
+      // accumulator of its own (pinned in place by empty asm uses), then the ReLU and weighted sums
+      // read them: no sum waits for the MFMA just issued, and the other wave of the SIMD fills the gap
+      // (issuing all 32 of the tile first was measured slower)
+      i32x4 kv[4];
+      int ks[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int grp = half * 4 + q;
-        const i32x4 kv = *reinterpret_cast<const i32x4*>(tp + grp * 1024 + lane * 16);
-        const int ks = tp[kF4CodeBytes + (grp * 16 + c) * 4 + g];
-        const i32x8 kb = i32x8{kv[0], kv[1], kv[2], kv[3], 0, 0, 0, 0};
-        float sp = 0.f;
+        kv[q] = *reinterpret_cast<const i32x4*>(tp + grp * 1024 + lane * 16);
+        ks[q] = tp[kF4CodeBytes + (grp * 16 + c) * 4 + g];
+      }
+      f32x4 acc[4][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const i32x8 kb = i32x8{kv[q][0], kv[q][1], kv[q][2], kv[q][3], 0, 0, 0, 0};
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          f32x4 acc = {};
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb, acc, 4, 4, 0, qs[mt], 0, ks);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sp = fmaf(wr[mt][r], relu(acc[r]), sp);
+          acc[q][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb, f32x4{}, 4, 4, 0, qs[mt], 0, ks[q]);
+          asm volatile("" ::"v"(acc[q][mt]));
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float p[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float sp = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sp = fmaf(wr[mt][r], relu(acc[q][mt][r]), sp);
         p[q] = sp;
       }
       // p[q] at lane l: column group q, entry l%16, the heads of lane group l/16. After the swaps lane l
