@@ -488,6 +488,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
 // wave: after the partial logits are written, and after P V (the exchange buffer is free again).
 constexpr int kPairRing = 3;
 
+// Row order of a key tile in the pairs kernel's ring: each group of 16 rows is stored transposed as a
+// 4 x 4 grid (logical row q at 4(q % 4) + q / 4). With rows 1072 bytes (12 banks mod 64) apart, the 16
+// rows a K-fragment read spans cover 16 distinct 4-bank groups, and the 4 rows of a transposing V^T
+// read pass (lanes 0-31: rows q .. q + 3, 64 bytes each) land 48 banks apart: both without conflicts
+// (in logical order the V^T rows were 12 banks apart and overlapped).
+__host__ __device__ constexpr int pair_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
 constexpr int kStageRow = 592;  // a staged 584-byte record, rounded up to 16 bytes
 size_t attn_keys_lds(const AttnArgs& a);
 // byte offset of the record staging rows (FMT 1) in the pairs kernel's dynamic LDS
@@ -685,7 +692,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
       const int r = j * NW + wave_u;
       if (FMT && __builtin_amdgcn_readlane(id, r) >= 0) continue;  // a record: staged separately
       copy_to_lds16(reinterpret_cast<const uint16_t*>(readlane64(ra, r)) + lane * 8,
-                    __builtin_amdgcn_readfirstlane(ring + (uint32_t)((buf * kNK + r) * kKNS * 2)));
+                    __builtin_amdgcn_readfirstlane(ring + (uint32_t)((buf * kNK + pair_row(r)) * kKNS * 2)));
       ++n;
     }
     return n;
@@ -717,7 +724,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
       if (!((stage_mask >> j) & 1u)) continue;  // wave-uniform
       const int r = j * NW + wave_u;
       const uint8_t* srow = stage + j * kStageRow;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(&sm.kn[buf][r][0]);
+      uint8_t* dst = reinterpret_cast<uint8_t*>(&sm.kn[buf][pair_row(r)][0]);
       if (lane < 28) {
         const uint32_t E = srow[576 + (lane >> 2)];  // the scale exponent of this lane's 64-dim group
         const float scale = __uint_as_float(E << 23);
@@ -741,9 +748,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   //  V^T A-fragment (dims 32dt .., keys 16ks ..), read r of two: 16-lane group g = l/16, i = l%16
   //  addresses row 16ks + 8(g/2) + 4r + i/4, dims 256*half + 32dt + 16(g%2) + 4(i%4) .. +3
   const int prow = (hl & 0x13) | ((hl & 4) << 1) | ((hl & 8) >> 1);
-  const uint32_t qk_off = (uint32_t)((prow * kKNS + 256 * half + 8 * hh) * 2);
+  const uint32_t qk_off = (uint32_t)((pair_row(prow) * kKNS + 256 * half + 8 * hh) * 2);
   const int g = lane >> 4, gi = lane & 15;
-  const uint32_t pv_off = (uint32_t)(((8 * (g >> 1) + (gi >> 2)) * kKNS + 256 * half + 16 * (g & 1) + 4 * (gi & 3)) * 2);
+  // (rows in the ring's order: logical row 8(g/2) + 4r + i/4 sits at 4(i/4) + 2(g/2) + r)
+  const uint32_t pv_off = (uint32_t)(((4 * (gi >> 2) + 2 * (g >> 1)) * kKNS + 256 * half + 16 * (g & 1) + 4 * (gi & 3)) * 2);
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
   auto kread = [&](int slot, int s) {
@@ -753,7 +761,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   auto vread = [&](int slot, int dt, int ks) {
     const uint32_t vb = ring + (uint32_t)(slot * kNK * kKNS * 2) + pv_off + (uint32_t)(ks * 16 * kKNS * 2 + dt * 64);
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)vb);
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(vb + 4 * kKNS * 2));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(vb + kKNS * 2));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
