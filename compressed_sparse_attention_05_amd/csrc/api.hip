@@ -590,6 +590,14 @@ int csa_workspace_size(int op, const csa_dims* dims, int B, int T, int64_t n_cap
       *bytes = (int64_t)attn_workspace(sizing_attn(dims, B, T, idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16));
       return CSA_OK;
     }
+    case CSA_OP_SPARSE_ATTN_QK: {
+      int rc = check_dims(dims);
+      if (rc) return rc;
+      const int dt = idx_dtype == CSA_F32 ? CSA_F32 : CSA_BF16;
+      *bytes = (int64_t)(align256((size_t)B * T * dims->H * dims->D * esize(dt)) +
+                         attn_workspace(sizing_attn(dims, B, T, dt)));
+      return CSA_OK;
+    }
     case CSA_OP_DENSE_ATTN: {
       int rc = check_dims(dims, false);
       if (rc) return rc;
@@ -696,6 +704,47 @@ int csa_sparse_attn(const csa_dims* dims, int B, int T, const int64_t* q_pos, in
   return attn_call("csa_sparse_attn", false, dims, B, T, q_pos, in_dtype, q, q_ld, q_seq_stride, entries,
                    entries_seq_stride, n_cap, idx, kv_raw, raw_ld, raw_seq_stride, raw_pos, raw_len, sink, out,
                    out_dtype, ws, ws_bytes, stream);
+}
+
+int csa_sparse_attn_qk(const csa_dims* dims, const csa_weights* w, int B, int T, const int64_t* q_pos, int in_dtype,
+                       const void* q, int64_t q_ld, int64_t q_seq_stride, const void* entries,
+                       int64_t entries_seq_stride, int64_t n_cap, const int32_t* idx, const void* kv_raw,
+                       int64_t raw_ld, int64_t raw_seq_stride, const int64_t* raw_pos, int64_t raw_len, void* out,
+                       int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  if (!w) return fail(CSA_ERR_ARG, "weights NULL");
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  rc = check_fid(w, dims->D);
+  if (rc) return rc;
+  AttnArgs at{};
+  rc = attn_prepare(false, dims, B, T, q_pos, in_dtype, q, q_ld, q_seq_stride, entries, entries_seq_stride, n_cap, idx,
+                    kv_raw, raw_ld, raw_seq_stride, raw_pos, raw_len, w->sink, out, out_dtype, 0, 0, 0, &at);
+  if (rc || (int64_t)B * T == 0) return rc;
+  const int H = dims->H, D = dims->D;
+  const bool fused = attn_try_fuse(at, w);
+  const bool qpass = (w->gamma_q || w->rope_dims > 0) && !fused;
+  // workspace: the normalised query (when the attention does not take the options) | attention scratch
+  const size_t qbytes = align256((size_t)B * T * H * D * esize(in_dtype));
+  rc = check_ws(ws, ws_bytes, qbytes + attn_workspace(at));
+  if (rc) return rc;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  if (qpass) {
+    rc = norm_rope_call(B, T, H, D, in_dtype, q, q_ld, q_seq_stride, base, (int64_t)H * D, (int64_t)T * H * D,
+                        w->gamma_q, w->norm_eps, w->rope_dims, w->rope_theta, q_pos, 0, 1, 0, stream);
+    if (rc) return rc;
+    at.q = base;
+    at.q_ld = (int64_t)H * D;
+    at.q_seq_stride = (int64_t)T * H * D;
+  }
+  rc = attn_run("csa_sparse_attn_qk", at, base + qbytes, ws_bytes - qbytes, stream);
+  if (rc) return rc;
+  if (w->rope_dims > 0 && !fused) {
+    rc = norm_rope_call(B, T, H, D, out_dtype, out, (int64_t)H * D, (int64_t)T * H * D, out, (int64_t)H * D,
+                        (int64_t)T * H * D, nullptr, 0.f, w->rope_dims, w->rope_theta, q_pos, 0, 1, 1, stream);
+    if (rc) return rc;
+  }
+  g_err.clear();
+  return CSA_OK;
 }
 
 int csa_sparse_attn_fp8(const csa_dims* dims, int B, int T, const int64_t* q_pos, int in_dtype, const void* q,

@@ -91,8 +91,8 @@ class CSADecode:
         self.idx = torch.empty(B, 1, d.top_k, dtype=torch.int32, device=device)
         self.out = torch.empty(B, 1, d.H, d.D, dtype=out_dtype, device=device)
         self.ws = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, d, B, 1, n_cap, 0, idx_dtype), device)
-        self.ws_attn = lib.workspace(lib.csa_workspace_size(lib.CSA_OP_SPARSE_ATTN, d, B, 1, n_cap, 0, lib.CSA_BF16),
-                                     device)
+        op = lib.CSA_OP_SPARSE_ATTN_QK if fid else lib.CSA_OP_SPARSE_ATTN
+        self.ws_attn = lib.workspace(lib.csa_workspace_size(op, d, B, 1, n_cap, 0, lib.CSA_BF16), device)
         self._pos = {}
 
     def _positions(self, L):
@@ -109,11 +109,16 @@ class CSADecode:
     def __call__(self, L, q_idx, w_head, keys, q, entries, kv_raw, q_scale=None, k_scale=None, sink=None):
         f = self.fid
         qp, rp = self._positions(L)
+        lib.csa_index_topk(self.d, q_idx, w_head, keys, self.idx, q_pos0=qp, q_scale=q_scale, k_scale=k_scale,
+                           ws=self.ws)
+        if f and entries.dtype != torch.uint8:
+            # the query's norm and rotation and the output's back-rotation inside the attention call
+            lib.csa_sparse_attn_qk(self.d, f, q, entries, self.idx, kv_raw, self.out, q_pos0=qp, raw_pos0=rp,
+                                   sink=sink, ws=self.ws_attn)
+            return self.out
         if f:
             q = lib.csa_norm_rope(q, y=self.q_n, pos0=qp, gamma=f.get("gamma_q"), eps=f.get("eps", 0.0),
                                   rope_dims=f.get("rope_dims", 0), theta=f.get("theta", 10000.0))
-        lib.csa_index_topk(self.d, q_idx, w_head, keys, self.idx, q_pos0=qp, q_scale=q_scale, k_scale=k_scale,
-                           ws=self.ws)
         lib.csa_sparse_attn(self.d, q, entries, self.idx, kv_raw, self.out, q_pos0=qp, raw_pos0=rp, sink=sink,
                             ws=self.ws_attn)
         if f and f.get("rope_dims", 0):

@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_PKG, "libcsa.so")
 CSA_F32, CSA_BF16, CSA_MXFP4 = 0, 1, 2
 ENTRY_RECORD_BYTES = 584
 CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN, CSA_OP_FORWARD, CSA_OP_DENSE_ATTN, \
-    CSA_OP_DECODE_STEP, CSA_OP_HCA_DECODE_STEP = range(8)
+    CSA_OP_DECODE_STEP, CSA_OP_HCA_DECODE_STEP, CSA_OP_SPARSE_ATTN_QK = range(9)
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
            "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8",
-           "csa_hca_decode_step", "csa_decode_step_noalloc", "csa_mxfp4_quantize")
+           "csa_hca_decode_step", "csa_decode_step_noalloc", "csa_mxfp4_quantize", "csa_sparse_attn_qk")
 PROBE_EXPORTS = ("csa_probe_hbm_read", "csa_probe_mfma_bf16", "csa_probe_sink_words")
 STATIC_SCRATCH_BYTES = 64 << 20
 
@@ -98,6 +98,8 @@ def load() -> ctypes.CDLL:
     lib.csa_decode_step_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, vp, i32, vp, vp, vp,
                                             vp, ctypes.POINTER(DecodeState), vp, i32, vp, vp]
     lib.csa_mxfp4_quantize.argtypes = [i64, i32, i32, vp, i64, vp, vp, vp]
+    lib.csa_sparse_attn_qk.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i32, vp, i32, vp, i64, i64, vp,
+                                       i64, i64, vp, vp, i64, i64, vp, i64, vp, i32, vp, sz, vp]
     lib.csa_probe_hbm_read.argtypes = [vp, sz, vp, vp]
     lib.csa_probe_hbm_read.restype = i32
     lib.csa_probe_mfma_bf16.argtypes = [i32, vp, vp]
@@ -107,7 +109,7 @@ def load() -> ctypes.CDLL:
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
               "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8", "csa_hca_decode_step",
-              "csa_decode_step_noalloc", "csa_mxfp4_quantize"):
+              "csa_decode_step_noalloc", "csa_mxfp4_quantize", "csa_sparse_attn_qk"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -285,6 +287,30 @@ def csa_sparse_attn(dims: Dims, q, entries, idx, kv_raw, out, *, q_pos0, raw_pos
               _p(entries), entries.stride(0), entries.shape[1], _p(idx), _p(kv_raw),
               kv_raw.stride(1), kv_raw.stride(0), _p(rp), kv_raw.shape[1], _p(sink), _p(out),
               _dt(out), wp, wn, _stream()))
+    return out
+
+
+def csa_sparse_attn_qk(dims: Dims, fid: dict, q, entries, idx, kv_raw, out, *, q_pos0, raw_pos0, sink=None,
+                       ws=None):
+    """csa_sparse_attn with QK-norm and partial RoPE of the query and the output's back-rotation (see
+    include/csa.h); fid: gamma_q (float32 [D] tensor or None), eps, rope_dims, theta. Entries are rows."""
+    _require_cuda(q, entries, idx, kv_raw, out, sink, fid.get("gamma_q"))
+    B, T = q.shape[0], q.shape[1]
+    if q.stride(3) != 1 or q.stride(2) != dims.D or entries.stride(2) != 1 or entries.stride(1) != dims.D:
+        raise ValueError("q heads and entry rows must be contiguous")
+    if kv_raw.stride(2) != 1 or not out.is_contiguous() or not idx.is_contiguous():
+        raise ValueError("kv_raw rows, idx and out must be contiguous")
+    need = csa_workspace_size(CSA_OP_SPARSE_ATTN_QK, dims, B, T, entries.shape[1], 0, _dt(q))
+    if ws is None or ws.numel() < need + 256:
+        ws = _workspace(need, q.device)
+    wp, wn = _aligned_ptr(ws)
+    w = Weights(None, None, None, None, None, None, _p(sink), _p(fid.get("gamma_q")), None,
+                float(fid.get("eps", 0.0)), int(fid.get("rope_dims", 0)), float(fid.get("theta", 10000.0)))
+    qp, rp = positions(B, q_pos0, q.device), positions(B, raw_pos0, q.device)
+    _check(load().csa_sparse_attn_qk(ctypes.byref(dims), ctypes.byref(w), B, T, _p(qp), _dt(q), _p(q), q.stride(1),
+                                     q.stride(0), _p(entries), entries.stride(0), entries.shape[1], _p(idx),
+                                     _p(kv_raw), kv_raw.stride(1), kv_raw.stride(0), _p(rp), kv_raw.shape[1],
+                                     _p(out), _dt(out), wp, wn, _stream()))
     return out
 
 

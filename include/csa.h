@@ -68,6 +68,7 @@ extern "C" {
 #define CSA_OP_DENSE_ATTN 5  /* csa_dense_attn; n_cap bounds the entries a row can see */
 #define CSA_OP_DECODE_STEP 6 /* csa_decode_step; T = 1, idx_dtype = the activation dtype */
 #define CSA_OP_HCA_DECODE_STEP 7 /* csa_hca_decode_step; T = 1, idx_dtype = the activation dtype */
+#define CSA_OP_SPARSE_ATTN_QK 8  /* csa_sparse_attn_qk; idx_dtype = the query dtype */
 
 /* Layer dimensions. */
 typedef struct csa_dims {
@@ -343,6 +344,26 @@ typedef struct csa_weights {
   int32_t rope_dims;     /* trailing dims turned by RoPE (64), 0: none; even, <= D                */
   float rope_theta;      /* RoPE base (10000), > 0 when rope_dims > 0                             */
 } csa_weights;
+
+/*
+ * csa_sparse_attn with the layer's QK-norm and partial RoPE ("Anatomy of a Frontier Model", bullet
+ * "QK-norm and partial RoPE"; the forms of csa_norm_rope): the query heads are RMS-normalised with
+ * gain w->gamma_q (NULL: no norm, eps w->norm_eps) and their last w->rope_dims dims turned by RoPE at
+ * the row's position before the logits, and each head's output is turned back by that position; the
+ * entries and raw KV are read as stored (already normalised and rotated). For a decode over caches the
+ * caller keeps itself. w->sink is the attention sink (nullable); the other fields of w are not read.
+ * Where the attention kernel takes the options (bf16 queries on its matrix-core path, a 16-byte aligned
+ * gain, and the rotation table and gain fit its LDS) they cost no pass of their own; otherwise the query
+ * is normalised into the workspace and the output turned back in place. Arguments otherwise as csa_sparse_attn. Workspace:
+ * csa_workspace_size(CSA_OP_SPARSE_ATTN_QK, dims, B, T, n_cap, 0, in_dtype). Errors as csa_sparse_attn,
+ * and those of csa_norm_rope for the options.
+ */
+int csa_sparse_attn_qk(const csa_dims* dims, const csa_weights* w, int B, int T, const int64_t* q_pos,
+                       int in_dtype, const void* q, int64_t q_ld, int64_t q_seq_stride,
+                       const void* entries, int64_t entries_seq_stride, int64_t n_cap, const int32_t* idx,
+                       const void* kv_raw, int64_t raw_ld, int64_t raw_seq_stride,
+                       const int64_t* raw_pos, int64_t raw_len, void* out, int out_dtype,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* Caches the layer reads and extends (device pointers, all of the activation dtype). Sequence b's
    chunk starts at position pos0[b] (see csa_forward). */

@@ -125,3 +125,41 @@ def test_fid_decode_bf16():
             o = O.sparse_attention(r["q"], r["entries"], gidx, r["raw"], wl.L - (wl.W - 1), np.array([wl.L]), wl.W)
             ref = O.rope(o, np.array([wl.L]), 64, 10000.0, inverse=True)
         assert max_err(tensor_f64(st.out[b]), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", ["fused_sink", "gamma_unaligned", "rope_only", "f32"])
+def test_sparse_attn_qk_matches_oracle(case):
+    """csa_sparse_attn_qk over the oracle's selection: the query normalised and rotated inside the attention
+    (bf16, 128 heads) or by a pass of its own (a gain that is not 16-byte aligned, float32 queries), with no
+    norm (rotation only), and with a sink."""
+    wl = get("decode128k").with_(B=2, L=4 * 2500, **({"dtype": "f32"} if case == "f32" else {}))
+    bf = wl.dtype == "bf16"
+    host, dev = _fid(wl.D, 95, 64)
+    inp = G.make_inputs(wl)
+    t = decode_tensors(wl, inp)
+    sink_h = G.normal_f32(96, "qk_sink", (wl.H,)) if case == "fused_sink" else None
+    fid = {"gamma_q": dev["gamma_q"], "eps": 1e-6, "rope_dims": 64, "theta": 10000.0}
+    if case == "gamma_unaligned":
+        buf = torch.empty(wl.D + 1, dtype=torch.float32, device="cuda")
+        buf[1:] = dev["gamma_q"]
+        fid["gamma_q"] = buf[1:]
+    elif case == "rope_only":
+        fid["gamma_q"] = None
+    refs = [O.decode(inp, wl, b, sink=None if sink_h is None else sink_h.astype(np.float64), fid=host)
+            for b in range(wl.B)]
+    idx = to_device(np.stack([r["idx"] for r in refs]).astype(np.int32), "i32").view(wl.B, 1, wl.k)
+    out = torch.empty(wl.B, 1, wl.H, wl.D, dtype=torch.float32, device="cuda")
+    from tests.csa_testlib import dims_of
+    lib.csa_sparse_attn_qk(dims_of(wl), fid, t["q"], t["entries"], idx, t["kv_raw"], out, q_pos0=wl.L,
+                           raw_pos0=wl.L - (wl.W - 1),
+                           sink=None if sink_h is None else to_device(sink_h.astype(np.float32), "f32"))
+    torch.cuda.synchronize()
+    for b, r in enumerate(refs):
+        ref = r["out"]
+        if case == "rope_only":
+            qpos = np.array([wl.L])
+            q = O.rope(O._val(inp["q"][b], bf), qpos, 64, 10000.0)
+            q = O.round_bf16(q) if bf else q
+            o = O.sparse_attention(q, r["entries"], r["idx"], r["raw"], wl.L - (wl.W - 1), qpos, wl.W)
+            ref = O.rope(o, qpos, 64, 10000.0, inverse=True)
+        assert max_err(tensor_f64(out[b]), ref) <= TOL[wl.dtype], (case, b)
