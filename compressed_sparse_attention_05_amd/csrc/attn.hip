@@ -375,14 +375,18 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
     // weights stay below 256 and O is rescaled in few tiles
     const float m_new = tmax > m_run + kRescaleLog2 ? tmax : m_run;
     const float al = m_new == m_run ? 1.f : exp2f(m_run - m_new);
+    // weights rounded to bf16 by v_cvt_pk_bf16_f32; the denominator sums the same rounded weights
+    // that P V uses (v_dot2 with ones)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
     float psum = 0.f;
     uint32_t pw[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint16_t h0 = f2bf(exp2f(v[m >> 1][(m & 1) * 2] - m_new));
-      const uint16_t h1 = f2bf(exp2f(v[m >> 1][(m & 1) * 2 + 1] - m_new));
-      psum += bf2f(h0) + bf2f(h1);  // the denominator sums the same rounded weights P V uses
-      pw[m] = h0 | ((uint32_t)h1 << 16);
+      const bf16x2 pp = {(__bf16)__builtin_amdgcn_exp2f(v[m >> 1][(m & 1) * 2] - m_new),
+                         (__bf16)__builtin_amdgcn_exp2f(v[m >> 1][(m & 1) * 2 + 1] - m_new)};
+      psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+      pw[m] = __builtin_bit_cast(uint32_t, pp);
     }
     psum = group4_sum(psum);
     l_run = l_run * al + psum;
@@ -444,8 +448,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_mfma(AttnArgs a, AttnSplit sp
     __syncthreads();  // every wave is past its last read of the ring (the condition is uniform)
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
-      const uint32_t w0 = f2bf(o[db][0] * inv) | ((uint32_t)f2bf(o[db][1] * inv) << 16);
-      const uint32_t w1 = f2bf(o[db][2] * inv) | ((uint32_t)f2bf(o[db][3] * inv) << 16);
+      const uint32_t w0 = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
       *reinterpret_cast<uint2*>(stg + (lane & 15) * kOutStageRowM + (db * 16 + 4 * g) * 2) = make_uint2(w0, w1);
     }
     __syncthreads();  // lanes read what other lanes wrote
@@ -522,7 +526,8 @@ __host__ __device__ inline size_t attn_stage_offset(const AttnArgs& a) {
   return (sizeof(PairSmem<NW>) - sizeof(int32_t) + keys + 15) & ~(size_t)15;
 }
 // the fused QK-norm / RoPE's LDS follows everything else: the cos / sin table of the row's position
-// (rope_dims / 2 pairs), then the query gain gamma_q (512 floats)
+// (rope_dims / 2 pairs), then the query gain gamma_q (512 floats; ones when there is no norm, so
+// that the per-value code has no branch)
 template <int NW>
 __host__ __device__ inline size_t pairs_rope_offset(const AttnArgs& a) {
   const size_t keys = a.dense ? 4 : (size_t)(a.k + a.W + 1) * 4;  // attn_keys_lds
@@ -534,7 +539,7 @@ __host__ __device__ inline size_t rope_tab_bytes(const AttnArgs& a) {
 }
 template <int NW>
 size_t pairs_lds(const AttnArgs& a) {
-  const size_t g = a.fuse_fid && a.gamma_q ? 512 * sizeof(float) : 0;
+  const size_t g = a.fuse_fid ? 512 * sizeof(float) : 0;
   return pairs_rope_offset<NW>(a) + rope_tab_bytes(a) + g;
 }
 
@@ -571,20 +576,15 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   const int hl = lane & 31, hh = lane >> 5;     // head within the pair; k half of a fragment
   const int head = hg * kHeadsPerBlock + (wave >> 1) * 32 + hl;
 
-  // fused QK-norm / RoPE: cos / sin of the row's position for every rotated pair, once per
-  // workgroup, and the query gain, both in LDS (published by barriers before they are read)
+  // fused QK-norm / RoPE: the query gain and the cos / sin of the row's position for every rotated
+  // pair go to LDS once per workgroup, in the block that normalises q (after the first tiles'
+  // loads are issued, so neither the gain's load nor the angles hold up the gathers); the gain is
+  // loaded here, into registers
   const bool rot = a.fuse_fid && a.rope_dims > 0;
   float2* rope_tab = reinterpret_cast<float2*>(smem_raw + pairs_rope_offset<NW>(a));
   float* gam = reinterpret_cast<float*>(smem_raw + pairs_rope_offset<NW>(a) + rope_tab_bytes(a));
-  if (a.fuse_fid && a.gamma_q && threadIdx.x < 128)
-    reinterpret_cast<float4*>(gam)[threadIdx.x] = reinterpret_cast<const float4*>(a.gamma_q)[threadIdx.x];
-  if (rot) {
-    for (int i = threadIdx.x; i < a.rope_dims / 2; i += kThreads) {
-      float c, sn;
-      rope_cos_sin((double)p, i, a.rope_dims, a.rope_lt, false, c, sn);
-      rope_tab[i] = make_float2(c, sn);
-    }
-  }
+  float4 gq4 = make_float4(1.f, 1.f, 1.f, 1.f);
+  if (a.fuse_fid && a.gamma_q && threadIdx.x < 128) gq4 = reinterpret_cast<const float4*>(a.gamma_q)[threadIdx.x];
 
   // ---- Q_w^T B-fragments: lane l holds head `head`, dims 256*half + 16s + 8hh .. +7. They are
   // loaded after the first burst of key indices: loads complete in order, so waiting for the
@@ -788,21 +788,31 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
   // of head `head`, the other 128 of its half in lane ^ 32 and the other half in the partner wave
   // meet for the sum of squares (through the exchange buffer, free until the first tile); then
   // x * inv * gamma, the rotation of the pairs past 512 - rope_dims, and rounding to bf16. It runs
-  // while the first tiles' gathers are in flight and issues no memory loads of its own.
+  // while the first tiles' gathers are in flight and issues no memory loads of its own. A workgroup
+  // turns 128 x 512 values, so the vector work per value is kept short: squares summed two at a
+  // time by v_dot2 (bf16 products are exact in fp32) and the rounding by v_cvt_pk_bf16_f32.
   if (a.fuse_fid) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    if (threadIdx.x < 128) reinterpret_cast<float4*>(gam)[threadIdx.x] = gq4;
+    if (rot) {
+      for (int i = threadIdx.x; i < a.rope_dims / 2; i += kThreads) {
+        float c, sn;
+        rope_cos_sin((double)p, i, a.rope_dims, a.rope_lt, false, c, sn);
+        rope_tab[i] = make_float2(c, sn);
+      }
+    }
     float inv = 1.f;
     if (a.gamma_q) {
-      float ss = 0.f;
+      float ss = 0.f, ss2 = 0.f;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const uint4 u = __builtin_bit_cast(uint4, qf[s]);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
-          ss = fmaf(x, x, ss);
-        }
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.x), __builtin_bit_cast(bf16x2, u.x), ss, false);
+        ss2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.y), __builtin_bit_cast(bf16x2, u.y), ss2, false);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.z), __builtin_bit_cast(bf16x2, u.z), ss, false);
+        ss2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u.w), __builtin_bit_cast(bf16x2, u.w), ss2, false);
       }
+      ss += ss2;
       ss += __shfl_xor(ss, 32, 64);
       float* xs = reinterpret_cast<float*>(&sm.sx[0][0][0]);
       xs[wave * 64 + lane] = ss;
@@ -818,25 +828,34 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
       const uint4 u = __builtin_bit_cast(uint4, qf[s]);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
       const int d0 = 256 * half + 16 * s + 8 * hh;  // dims d0 .. d0 + 7
+      // the gain and the angles as whole vectors, read before any is used (one LDS wait)
+      const float4 g0 = *reinterpret_cast<const float4*>(gam + d0);
+      const float4 g1 = *reinterpret_cast<const float4*>(gam + d0 + 4);
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
-        y[e] = a.gamma_q ? x * inv * gam[d0 + e] : x;
+        y[e] = x * inv * gv[e];
       }
       if (rot && d0 + 8 > rs) {
+        float2 cs[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          if (d0 + e < rs) continue;
-          const float2 cs = rope_tab[(d0 + e - rs) >> 1];
-          const float y0 = y[e], y1 = y[e + 1];
-          y[e] = y0 * cs.x - y1 * cs.y;
-          y[e + 1] = y0 * cs.y + y1 * cs.x;
+        for (int j = 0; j < 4; ++j) {
+          const int i = (d0 + 2 * j - rs) >> 1;
+          cs[j] = rope_tab[i < 0 ? 0 : i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float y0 = y[2 * j], y1 = y[2 * j + 1];
+          const bool on = d0 + 2 * j >= rs;
+          y[2 * j] = on ? y0 * cs[j].x - y1 * cs[j].y : y0;
+          y[2 * j + 1] = on ? y0 * cs[j].y + y1 * cs[j].x : y1;
         }
       }
       uint32_t o4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o4[j] = (uint32_t)f2bf(y[2 * j]) | ((uint32_t)f2bf(y[2 * j + 1]) << 16);
+      for (int j = 0; j < 4; ++j) o4[j] = pack_bf16x2(y[2 * j], y[2 * j + 1]);
       qf[s] = __builtin_bit_cast(bf16x8, make_uint4(o4[0], o4[1], o4[2], o4[3]));
     }
   }
@@ -997,14 +1016,18 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       if (256 * half + 32 * dt + 32 <= rs) continue;  // uniform: no rotated dims in this tile
+      float2 cs[8];  // the tile's angles, all read before any is used (one LDS wait)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const int d = dbase + 32 * dt + 8 * (r >> 2) + (r & 3);
-        if (d < rs) continue;
-        const float2 cs = rope_tab[(d - rs) >> 1];
-        const float y0 = o[dt][r], y1 = o[dt][r + 1], sn = -cs.y;
-        o[dt][r] = y0 * cs.x - y1 * sn;
-        o[dt][r + 1] = y0 * sn + y1 * cs.x;
+        const int i = (dbase + 32 * dt + 8 * (r >> 2) + (r & 3) - rs) >> 1;
+        cs[r >> 1] = rope_tab[i < 0 ? 0 : i];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const bool on = dbase + 32 * dt + 8 * (r >> 2) + (r & 3) >= rs;
+        const float y0 = o[dt][r], y1 = o[dt][r + 1], c = cs[r >> 1].x, sn = -cs[r >> 1].y;
+        o[dt][r] = on ? y0 * c - y1 * sn : y0;
+        o[dt][r + 1] = on ? y0 * sn + y1 * c : y1;
       }
     }
   }
@@ -1020,8 +1043,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_pairs(AttnArgs a, AttnSplit s
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const uint32_t w0 = f2bf(o[dt][4 * q4] * inv) | ((uint32_t)f2bf(o[dt][4 * q4 + 1] * inv) << 16);
-        const uint32_t w1 = f2bf(o[dt][4 * q4 + 2] * inv) | ((uint32_t)f2bf(o[dt][4 * q4 + 3] * inv) << 16);
+        const uint32_t w0 = pack_bf16x2(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
         *reinterpret_cast<uint2*>(stg + hl * kOutStageRow + (32 * dt + 8 * q4 + 4 * hh) * 2) = make_uint2(w0, w1);
       }
     __syncthreads();  // lanes read what other lanes wrote (the condition is uniform over the workgroup)
@@ -1074,9 +1097,16 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
       u[j] = *reinterpret_cast<const uint4*>(sp.part_o + (pidx * a.H + h) * 512 + lane * 8);
     }
   };
+  // the fused back-rotation: the row's position is loaded before the partials and the first 64
+  // pairs' angles (lane i: pair i) are formed while the partials are in flight
+  const bool rot = a.fuse_fid && a.rope_dims > 0;
+  double pq = 0.0;
+  if (rot) pq = (double)(pos_at(a.q_pos, row / a.T) + row % a.T);
   uint4 u[kG];
   float m[kG], l[kG];
   load_group(0, u, m, l);
+  float rc = 1.f, rsn = 0.f;
+  if (rot && lane < a.rope_dims / 2) rope_cos_sin(pq, lane, a.rope_dims, a.rope_lt, true, rc, rsn);
   float M = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kG; ++j)
@@ -1106,18 +1136,20 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   }
   float inv = 1.f / L;
   const int64_t ob = (row * a.H + h) * 512 + lane * 8;
-  if (a.fuse_fid && a.rope_dims > 0) {
-    // the fused back-rotation by the row's position, on O / L (the division is the one the store
-    // would make); lane i of a round forms pair i's angle, the lanes holding rotated dims fetch theirs
+  if (rot) {
+    // the back-rotation by the row's position, on O / L (the division is the one the store would
+    // make); lane i of a round holds pair i's angle, the lanes holding rotated dims fetch theirs
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= inv;
     inv = 1.f;
     const int rs = 512 - a.rope_dims, npair = a.rope_dims / 2;
-    const int64_t b = row / a.T, t = row % a.T;
-    const double p = (double)(pos_at(a.q_pos, b) + t);
     for (int i0 = 0; i0 < npair; i0 += 64) {  // uniform
-      float c = 1.f, sn = 0.f;
-      if (i0 + lane < npair) rope_cos_sin(p, i0 + lane, a.rope_dims, a.rope_lt, true, c, sn);
+      float c = rc, sn = rsn;
+      if (i0 > 0) {
+        c = 1.f;
+        sn = 0.f;
+        if (i0 + lane < npair) rope_cos_sin(pq, i0 + lane, a.rope_dims, a.rope_lt, true, c, sn);
+      }
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const int d = lane * 8 + e;
@@ -1134,7 +1166,7 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, AttnSplit sp) {
   if (OT == CSA_BF16 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(acc[2 * i] * inv) | ((uint32_t)f2bf(acc[2 * i + 1] * inv) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + ob) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
 #pragma unroll

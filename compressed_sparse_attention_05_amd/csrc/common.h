@@ -27,6 +27,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// two floats to bf16 (round to nearest even, as f2bf) in one v_cvt_pk_bf16_f32; a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
+}
+
 template <int DT>
 __device__ __forceinline__ float load_elem(const void* p, int64_t i);
 template <>
