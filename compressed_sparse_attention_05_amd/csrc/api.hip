@@ -818,6 +818,28 @@ int csa_mxfp4_quantize(int64_t R, int D, int dtype, const void* x, int64_t ld, v
   return hip_status(launch_mxfp4_quant(a, static_cast<hipStream_t>(stream)), "csa_mxfp4_quantize");
 }
 
+int csa_projection_gemm(int M, int N, int K, int in_dtype, const void* A, int64_t lda, const void* Wt, int64_t ldb,
+                        void* C, int64_t ldc, int out_dtype, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(CSA_ERR_ARG, "M, N, K must be >= 0");
+  if (!is_act_dtype(in_dtype) || !is_act_dtype(out_dtype)) return fail(CSA_ERR_ARG, "dtypes must be F32 or BF16");
+  if (lda < K || ldb < K || ldc < N) return fail(CSA_ERR_ARG, "strides below the row lengths");
+  if ((int64_t)M * N == 0) return CSA_OK;
+  if (!A || !Wt || !C) return fail(CSA_ERR_ARG, "NULL tensor pointer");
+  GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.dtype = in_dtype;
+  g.out_dtype = out_dtype;
+  g.A = A;
+  g.lda = lda;
+  g.Bm = Wt;
+  g.ldb = ldb;
+  g.C = C;
+  g.ldc = ldc;
+  return hip_status(launch_gemm(g, static_cast<hipStream_t>(stream)), "csa_projection_gemm");
+}
+
 int csa_norm_rope(int B, int R, int H, int D, int dtype, const void* x, int64_t x_ld, int64_t x_seq_stride, void* y,
                   int64_t y_ld, int64_t y_seq_stride, const float* gamma, float eps, int rope_dims, float rope_theta,
                   const int64_t* pos0, int64_t pos_off, int64_t pos_step, int inverse, void* stream) {

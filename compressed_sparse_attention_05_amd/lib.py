@@ -22,7 +22,8 @@ CSA_OP_COMPRESS, CSA_OP_INDEX_TOPK, CSA_OP_TOPK_FROM_SCORES, CSA_OP_SPARSE_ATTN,
 EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress", "csa_index_topk",
            "csa_topk_from_scores", "csa_sparse_attn", "csa_forward", "csa_hca_compress", "csa_dense_attn",
            "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8",
-           "csa_hca_decode_step", "csa_decode_step_noalloc", "csa_mxfp4_quantize", "csa_sparse_attn_qk")
+           "csa_hca_decode_step", "csa_decode_step_noalloc", "csa_mxfp4_quantize", "csa_sparse_attn_qk",
+           "csa_projection_gemm")
 PROBE_EXPORTS = ("csa_probe_hbm_read", "csa_probe_mfma_bf16", "csa_probe_sink_words")
 STATIC_SCRATCH_BYTES = 64 << 20
 
@@ -98,6 +99,7 @@ def load() -> ctypes.CDLL:
     lib.csa_decode_step_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, vp, i32, vp, vp, vp,
                                             vp, ctypes.POINTER(DecodeState), vp, i32, vp, vp]
     lib.csa_mxfp4_quantize.argtypes = [i64, i32, i32, vp, i64, vp, vp, vp]
+    lib.csa_projection_gemm.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, i32, vp]
     lib.csa_sparse_attn_qk.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), i32, i32, vp, i32, vp, i64, i64, vp,
                                        i64, i64, vp, vp, i64, i64, vp, i64, vp, i32, vp, sz, vp]
     lib.csa_probe_hbm_read.argtypes = [vp, sz, vp, vp]
@@ -109,7 +111,8 @@ def load() -> ctypes.CDLL:
     for f in ("csa_workspace_size", "csa_compress", "csa_index_topk", "csa_topk_from_scores", "csa_sparse_attn",
               "csa_forward", "csa_hca_compress", "csa_dense_attn", "csa_norm_rope", "csa_entry_pack",
               "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8", "csa_hca_decode_step",
-              "csa_decode_step_noalloc", "csa_mxfp4_quantize", "csa_sparse_attn_qk"):
+              "csa_decode_step_noalloc", "csa_mxfp4_quantize", "csa_sparse_attn_qk",
+           "csa_projection_gemm"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -345,6 +348,21 @@ def csa_mxfp4_quantize(x, codes=None, scales=None):
         raise ValueError("codes / scales must be contiguous [R, D/2] / [R, D/32]")
     _check(load().csa_mxfp4_quantize(R, D, _dt(x), _p(x), x.stride(0), _p(codes), _p(scales), _stream()))
     return codes, scales
+
+
+def csa_projection_gemm(a, wt, c):
+    """c [M, N] = a [M, K] @ wt [N, K]^T on the library's own GEMM kernels (see include/csa.h); rows of
+    each operand must have unit stride."""
+    _require_cuda(a, wt, c)
+    if a.stride(1) != 1 or wt.stride(1) != 1 or c.stride(1) != 1 or a.dtype != wt.dtype:
+        raise ValueError("operands need unit stride along rows and one input dtype")
+    M, K = a.shape
+    N = wt.shape[0]
+    if wt.shape[1] != K or tuple(c.shape) != (M, N):
+        raise ValueError("shapes do not match")
+    _check(load().csa_projection_gemm(M, N, K, _dt(a), _p(a), a.stride(0), _p(wt), wt.stride(0), _p(c), c.stride(0),
+                                      _dt(c), _stream()))
+    return c
 
 
 def probe_sink(device="cuda") -> torch.Tensor:

@@ -479,6 +479,21 @@ int csa_hca_decode_step(const csa_dims* dims, const csa_weights* w, int B, const
                         size_t ws_bytes, void* stream);
 
 /*
+ * The layer's fused input projection C = A W^T on the library's own kernels: the GEMM csa_forward
+ * falls back to when hipBLASLt declines a shape (the pages give no projection; one dense product over
+ * the concatenated weights makes every per-token vector the layer reads, see csa_weights.w_proj).
+ *   A  [M, K] of in_dtype (F32 or BF16), row stride lda >= K elements.
+ *   Wt [N, K] of in_dtype, row stride ldb >= K (one output column per row).
+ *   C  [M, N] of out_dtype (F32 or BF16), row stride ldc >= N; fp32 accumulation, bf16 out rounded
+ *      to nearest even.
+ * BF16 inputs with K % 64 == 0, lda, ldb multiples of 8 and 16-byte aligned A, Wt run the matrix-core
+ * kernel (128 x 128 tiles); everything else a one-output-per-thread kernel. Device pointers,
+ * asynchronous on `stream`. Errors: CSA_ERR_ARG for negative sizes, small strides or NULL pointers.
+ */
+int csa_projection_gemm(int M, int N, int K, int in_dtype, const void* A, int64_t lda, const void* Wt, int64_t ldb,
+                        void* C, int64_t ldc, int out_dtype, void* stream);
+
+/*
  * The whole layer ("Anatomy of a Frontier Model", section "The attention: compress, then select":
  * compress, then select, then attend; "The Exchange Rates of a Million Tokens", section 3) for a
  * chunk of T tokens per sequence, sequence b at positions pos0[b] .. pos0[b]+T-1: projection

@@ -279,3 +279,17 @@ def test_probes_reject_bad_arguments():
     assert rc == -1 and "aligned" in msg
     rc, msg = _err(L.csa_probe_mfma_bf16(0, ctypes.c_void_p(4096), None))
     assert rc == -1 and "iters" in msg
+
+
+def test_projection_gemm_rejects_bad_arguments():
+    L = lib.load()
+    p = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    rc, msg = _err(L.csa_projection_gemm(-1, 8, 64, lib.CSA_BF16, p, 64, p, 64, p, 8, lib.CSA_BF16, None))
+    assert rc == -1 and ">= 0" in msg
+    rc, msg = _err(L.csa_projection_gemm(4, 8, 64, lib.CSA_MXFP4, p, 64, p, 64, p, 8, lib.CSA_BF16, None))
+    assert rc == -1 and "dtype" in msg
+    rc, msg = _err(L.csa_projection_gemm(4, 8, 64, lib.CSA_BF16, p, 64, p, 63, p, 8, lib.CSA_BF16, None))
+    assert rc == -1 and "stride" in msg
+    rc, msg = _err(L.csa_projection_gemm(4, 8, 64, lib.CSA_BF16, None, 64, p, 64, p, 8, lib.CSA_F32, None))
+    assert rc == -1 and "NULL" in msg
+    assert L.csa_projection_gemm(0, 8, 64, lib.CSA_BF16, None, 64, None, 64, None, 8, lib.CSA_F32, None) == 0
