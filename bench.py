@@ -9,6 +9,9 @@ timed region starts. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload chunk1m] [--no-decode] [--no-cpu-baseline]
     python bench.py --copy-probe      # a plain 1 GiB device copy, for counter calibration
+    python bench.py --gather-probe    # 1 KiB rows gathered by index (the attention's pattern), likewise
+    python bench.py --decode-leg decode128k   # one decode leg alone (for its counters)
+    python bench.py --decode-pmc-summary DIR --decode-leg decode128k  # its per-kernel HBM traffic
     python bench.py --pmc-summary DIR # HBM bytes per kernel from rocprofv3 --pmc runs
     python bench.py --mfma-summary DIR  # matrix-core busy share of the prefill kernels (one --pmc run)
     python bench.py --attn-summary DIR  # LDS / wait counters of the 128-head attention (two --pmc runs)
@@ -16,7 +19,8 @@ timed region starts. Prints one JSON line.
 Counter runs (repository root; from /tmp with TMPDIR=/tmp), each in a process of its own, over
     python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-hca --no-prefill8k --workload chunk1m
     (COUNTER_BENCH below): FETCH_SIZE into DIR/fetch, WRITE_SIZE into DIR/write, both counters of
-    --copy-probe into DIR/copy_fetch and DIR/copy_write, then --pmc-summary DIR writes
+    --copy-probe into DIR/copy_fetch and DIR/copy_write, FETCH_SIZE of --gather-probe into
+    DIR/gather_fetch, then --pmc-summary DIR writes
     profiles/*_pmc.json / .md and profiles/hbm_traffic_<workload>_bench.md; with --no-decode added,
     SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE into DIR/mfma (--mfma-summary) and the two counter sets of
     attn_summary into DIR/attn1, DIR/attn2 (--attn-summary). Each summary names its exact commands.
@@ -94,6 +98,32 @@ def copy_probe():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+
+
+GATHER_PROBE_ROWS = 64 * 1152  # the decode128k attention's gathered rows: 64 rows x (1024 selected + 128 window)
+
+
+def gather_probe():
+    """1 KiB rows gathered by index from a 2 GiB buffer (the attention's access pattern), for counter
+    calibration: GATHER_PROBE_ROWS distinct rows in ascending order, read once per launch, three
+    launches, each after a 512 MiB read that evicts the caches; prints the bytes and the rate."""
+    import torch
+    from compressed_sparse_attention_05_amd import lib
+    n, row = 2 << 30, 1024
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    rng = np.random.default_rng(11)
+    idx = torch.from_numpy(np.sort(rng.choice(n // row, GATHER_PROBE_ROWS, replace=False)).astype(np.int32)).cuda()
+    sink = lib.probe_sink()
+    flush = torch.ones(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    ms = []
+    for _ in range(3):
+        flush.sum()
+        ms += timed_events(lambda: lib.probe_gather_read(buf, row, idx, sink), 1, torch.cuda.synchronize)
+    nbytes = GATHER_PROBE_ROWS * row
+    print(json.dumps({"gather_probe_rows": GATHER_PROBE_ROWS, "row_bytes": row, "bytes_per_launch": nbytes,
+                      "launches": 3, "us_per_launch": round(float(np.median(ms)) * 1e3, 2),
+                      "gbs": round(nbytes / (float(np.median(ms)) * 1e-3) / 1e9, 1)}))
 
 
 def peak_probes():
@@ -181,6 +211,11 @@ def pmc_summary(pmc_dir, workload):
         return (float(np.median(vals)), len(vals)) if vals else (None, 0)
     fetch, write = rows("fetch", "FETCH_SIZE"), rows("write", "WRITE_SIZE")
     cf_kib, _ = median_of(rows("copy_fetch", "FETCH_SIZE"), lambda n: "copy" in n.lower())
+    # gathered 1 KiB rows (the attention's pattern) may count differently from a streamed copy
+    gpath = os.path.join(pmc_dir, "gather_fetch", "run_counter_collection.csv")
+    gf_kib = median_of(rows("gather_fetch", "FETCH_SIZE"), lambda n: "probe_gather" in n)[0] \
+        if os.path.exists(gpath) else None
+    g_scale = GATHER_PROBE_ROWS * 1024 / gf_kib if gf_kib else None
     cw_kib, _ = median_of(rows("copy_write", "WRITE_SIZE"), lambda n: "copy" in n.lower())
     copy_bytes = 1 << 30
     f_scale, w_scale = copy_bytes / cf_kib, copy_bytes / cw_kib  # bytes per counter unit
@@ -189,6 +224,7 @@ def pmc_summary(pmc_dir, workload):
             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- {bench_cmd}",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/copy_fetch -o run -- python3 /root/repo/bench.py --copy-probe",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/copy_write -o run -- python3 /root/repo/bench.py --copy-probe",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/gather_fetch -o run -- python3 /root/repo/bench.py --gather-probe",
             f"python3 /root/repo/bench.py --pmc-summary <out> --workload {workload}"]
     out = {}
     for kern in ("index_prefill_mfma", "index_prefill_fp4"):
@@ -233,14 +269,83 @@ def pmc_summary(pmc_dir, workload):
         f.write(f"Counter units scaled by the copy probe: FETCH_SIZE x {f_scale:.1f}, WRITE_SIZE x {w_scale:.1f} "
                 "bytes per unit. Median over the kernel's dispatches (every workload of the run mixed: read "
                 "with the dispatch count).\n\n")
-        f.write("| kernel | dispatches | fetched MB | written MB |\n|---|---|---|---|\n")
+        if g_scale:
+            f.write(f"Gather probe ({GATHER_PROBE_ROWS} distinct 1 KiB rows read by index, caches evicted "
+                    f"before each launch): FETCH_SIZE {gf_kib:.1f} KiB per launch, so {g_scale:.1f} bytes per "
+                    f"unit for gathered rows against {f_scale:.1f} for the streamed copy; the last column "
+                    "scales the fetch of the gathering kernels (the attention) by it.\n\n")
+        f.write("| kernel | dispatches | fetched MB | written MB | fetched MB, gather factor |\n|---|---|---|---|---|\n")
         for nm in names:
             fk, nf = median_of(fetch, lambda n, nm=nm: "csa::" in n and _short_kernel(n) == nm)
             wk, _ = median_of(write, lambda n, nm=nm: "csa::" in n and _short_kernel(n) == nm)
             if fk is None:
                 continue
-            f.write(f"| {nm} | {nf} | {fk * f_scale / 1e6:.2f} | {(wk or 0) * w_scale / 1e6:.2f} |\n")
+            gcol = f"{fk * g_scale / 1e6:.2f}" if g_scale and "attn" in nm else "-"
+            f.write(f"| {nm} | {nf} | {fk * f_scale / 1e6:.2f} | {(wk or 0) * w_scale / 1e6:.2f} | {gcol} |\n")
     print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in out.items()}))
+
+
+def decode_pmc_summary(pmc_dir, name):
+    """Per-kernel HBM traffic of one decode leg alone (decode128k or decode1m_fp4), from FETCH_SIZE and
+    WRITE_SIZE runs of `bench.py --decode-leg NAME` and the probes' runs (copy for both counters, gather
+    for the attention's gathered rows), against each kernel's compulsory bytes. Writes
+    profiles/decode_traffic_<name>.md."""
+    from synth.workloads import get
+    wl = get(name)
+    def rows(run, counter):
+        return _counter_rows(os.path.join(pmc_dir, run, "run_counter_collection.csv"), counter)
+    def med(rs, match):
+        v = [x for n, x in rs if match(n)]
+        return (float(np.median(v)), len(v)) if v else (None, 0)
+    cf = med(rows("copy_fetch", "FETCH_SIZE"), lambda n: "copy" in n.lower())[0]
+    cw = med(rows("copy_write", "WRITE_SIZE"), lambda n: "copy" in n.lower())[0]
+    gf = med(rows("gather_fetch", "FETCH_SIZE"), lambda n: "probe_gather" in n)[0]
+    f_scale, w_scale, g_scale = (1 << 30) / cf, (1 << 30) / cw, GATHER_PROBE_ROWS * 1024 / gf
+    fetch, write = rows(f"dfetch_{name}", "FETCH_SIZE"), rows(f"dwrite_{name}", "WRITE_SIZE")
+    fp4 = wl.idx_dtype == "mxfp4"
+    N, S = wl.L // wl.m, -(-(wl.k + wl.W) // 288)
+    key_row = wl.D_I // 2 + wl.D_I // 32 if fp4 else wl.D_I * 2
+    qi_row = wl.H_I * key_row
+    scores = wl.B * N * 4
+    q = wl.B * wl.H * wl.D * 2
+    parts = wl.B * S * wl.H * (wl.D * 2 + 8)
+    # compulsory reads / writes of each kernel: what it must read from HBM once and write
+    comp = {"score": (wl.B * N * key_row + wl.B * qi_row, scores),
+            "sel": (scores, wl.B * wl.k * 4),
+            "attn_pairs": (wl.B * (wl.k + wl.W) * wl.D * 2 + q + wl.B * wl.k * 4, parts),
+            "attn_combine": (parts, wl.B * wl.H * wl.D * 4)}
+    cmd = f"python3 /root/repo/bench.py --decode-leg {name} --steps 3 --warmup 1"
+    cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/dfetch_{name} -o run -- {cmd}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/dwrite_{name} -o run -- {cmd}",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/copy_fetch -o run -- python3 /root/repo/bench.py --copy-probe",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/copy_write -o run -- python3 /root/repo/bench.py --copy-probe",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/gather_fetch -o run -- python3 /root/repo/bench.py --gather-probe",
+            f"python3 /root/repo/bench.py --decode-pmc-summary <out> --decode-leg {name}"]
+    names = sorted({_short_kernel(n) for n, _ in fetch if "csa::" in n})
+    with open(os.path.join(ROOT, "profiles", f"decode_traffic_{name}.md"), "w") as f:
+        f.write(f"# {name}: HBM traffic per kernel of one decode step (the leg run alone)\n\n")
+        f.write("Commands (repository root, run from /tmp with TMPDIR=/tmp):\n\n```\n" + "\n".join(cmds) + "\n```\n\n")
+        f.write(f"Bytes per counter unit: FETCH_SIZE {f_scale:.1f} (1 GiB copy), {g_scale:.1f} (gather probe: "
+                f"{GATHER_PROBE_ROWS} distinct 1 KiB rows by index), WRITE_SIZE {w_scale:.1f} (copy). The attention's "
+                "fetch is scaled by the gather figure, the rest by the copy's. Median over the leg's dispatches "
+                "(warm-up included; the caches are evicted before each timed step). Compulsory: what the kernel "
+                "must read once (keys and q_I; scores; gathered rows, window rows, q and indices; split partials) "
+                f"and write (scores; indices; {S} split partials per row; the output).\n\n")
+        f.write("| kernel | dispatches | fetched MB | compulsory read MB | written MB | compulsory write MB |\n"
+                "|---|---|---|---|---|---|\n")
+        for nm in names:
+            fk, nd = med(fetch, lambda n, nm=nm: "csa::" in n and _short_kernel(n) == nm)
+            wk = med(write, lambda n, nm=nm: "csa::" in n and _short_kernel(n) == nm)[0] or 0.0
+            key = next((k for k in ("score", "sel", "attn_pairs", "attn_combine") if nm.startswith(k)), None)
+            cr, cwb = comp.get(key, (None, None)) if key else (None, None)
+            if nm.startswith("sel_collect"):  # the long-row selection: scores in, candidates out
+                cwb = None
+            elif nm.startswith("sel_final"):  # candidates in, indices out
+                cr = None
+            fb = fk * (g_scale if key == "attn_pairs" else f_scale)
+            f.write(f"| {nm} | {nd} | {fb / 1e6:.2f} | {'-' if cr is None else f'{cr / 1e6:.2f}'} | "
+                    f"{wk * w_scale / 1e6:.2f} | {'-' if cwb is None else f'{cwb / 1e6:.2f}'} |\n")
+    print(json.dumps({"decode_traffic": name, "kernels": names}))
 
 
 def attn_summary(pmc_dir, workload):
@@ -727,6 +832,9 @@ def main():
     ap.add_argument("--no-hca", action="store_true", help="skip the HCA legs")
     ap.add_argument("--no-prefill8k", action="store_true", help="skip the prefill8k sub-record")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--gather-probe", action="store_true")
+    ap.add_argument("--decode-leg", metavar="NAME", help="run one decode leg alone (decode128k, decode1m_fp4)")
+    ap.add_argument("--decode-pmc-summary", metavar="DIR", help="summarise the --pmc runs of one --decode-leg")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise four rocprofv3 --pmc runs under DIR")
     ap.add_argument("--mfma-summary", metavar="DIR", help="summarise one rocprofv3 --pmc run of the MFMA busy counter")
     ap.add_argument("--attn-summary", metavar="DIR", help="summarise two rocprofv3 --pmc runs of attention counters")
@@ -741,6 +849,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.workload)
         return
+    if args.decode_pmc_summary:
+        decode_pmc_summary(args.decode_pmc_summary, args.decode_leg)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print(f"bench.py runs on one GPU only: the CSA layer here is a single-GPU build (asked for "
@@ -753,6 +864,12 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.gather_probe:
+        gather_probe()
+        return
+    if args.decode_leg:
+        print(json.dumps({args.decode_leg: bench_decode(args.decode_leg, args.steps, args.warmup)}))
         return
     from synth.workloads import get
     wl = get(args.workload)

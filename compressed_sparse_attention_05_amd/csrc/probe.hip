@@ -1,5 +1,6 @@
-// Ceiling probes (include/csa_probe.h): HBM read bandwidth with 16-byte loads, and the bf16 MFMA
-// rate of four independent 32x32x16 chains per wave at eight waves per compute unit.
+// Ceiling probes (include/csa_probe.h): HBM read bandwidth with 16-byte loads, the read of rows
+// gathered by index (the attention's access pattern), and the bf16 MFMA rate of four independent
+// 32x32x16 chains per wave at eight waves per compute unit.
 #include "csa_probe.h"
 
 #include <hip/hip_runtime.h>
@@ -33,6 +34,36 @@ __global__ void __launch_bounds__(kProbeThreads) probe_read(const uint4* buf, in
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   sink[tid] = acc;
+}
+
+// one wave per gathered row, four rows in flight per wave; row numbers are clamped into the buffer
+__global__ void __launch_bounds__(kProbeThreads) probe_gather(const uint8_t* buf, int64_t buf_rows, int row16,
+                                                              const int32_t* idx, int64_t n_rows, uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+  auto row_ptr = [&](int64_t r) {
+    int64_t i = idx[r];
+    i = i < 0 ? 0 : (i >= buf_rows ? buf_rows - 1 : i);
+    return reinterpret_cast<const uint4*>(buf + i * (int64_t)row16 * 16);
+  };
+  uint32_t acc = 0;
+  int64_t r = wave;
+  for (; r + 3 * nw < n_rows; r += 4 * nw) {
+    const uint4 *p0 = row_ptr(r), *p1 = row_ptr(r + nw), *p2 = row_ptr(r + 2 * nw), *p3 = row_ptr(r + 3 * nw);
+    for (int j = lane; j < row16; j += 64) {
+      const uint4 a = p0[j], b = p1[j], c = p2[j], d = p3[j];
+      acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+  }
+  for (; r < n_rows; r += nw) {
+    const uint4* p0 = row_ptr(r);
+    for (int j = lane; j < row16; j += 64) {
+      const uint4 a = p0[j];
+      acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+  }
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 __global__ void __launch_bounds__(kProbeThreads) probe_mfma(int iters, float* sink) {
@@ -69,6 +100,19 @@ int csa_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stre
   hipLaunchKernelGGL(csa::probe_read, dim3((unsigned)csa::probe_grid()), dim3(csa::kProbeThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf), (int64_t)(bytes / 16), sink);
   return csa::probe_status(hipGetLastError(), "csa_probe_hbm_read");
+}
+
+int csa_probe_gather_read(const void* buf, size_t buf_bytes, size_t row_bytes, const int32_t* idx, int64_t n_rows,
+                          uint32_t* sink, void* stream) {
+  if (!buf || !sink || !idx || n_rows < 0 || row_bytes < 16 || row_bytes % 16 || row_bytes > (1u << 20) ||
+      buf_bytes < row_bytes || reinterpret_cast<uintptr_t>(buf) % 16 || reinterpret_cast<uintptr_t>(idx) % 4)
+    return csa::probe_fail("csa_probe_gather_read: buf 16-byte aligned with at least one row, row_bytes a multiple of "
+                           "16 (<= 1 MiB), idx 4-byte aligned, n_rows >= 0 and a sink are required");
+  if (n_rows == 0) return 0;
+  hipLaunchKernelGGL(csa::probe_gather, dim3((unsigned)csa::probe_grid()), dim3(csa::kProbeThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(buf),
+                     (int64_t)(buf_bytes / row_bytes), (int)(row_bytes / 16), idx, n_rows, sink);
+  return csa::probe_status(hipGetLastError(), "csa_probe_gather_read");
 }
 
 int csa_probe_mfma_bf16(int iters, float* sink, void* stream) {

@@ -24,7 +24,7 @@ EXPORTS = ("csa_version", "csa_last_error", "csa_workspace_size", "csa_compress"
            "csa_norm_rope", "csa_entry_pack", "csa_sparse_attn_fp8", "csa_decode_step", "csa_dense_attn_fp8",
            "csa_hca_decode_step", "csa_decode_step_noalloc", "csa_mxfp4_quantize", "csa_sparse_attn_qk",
            "csa_projection_gemm")
-PROBE_EXPORTS = ("csa_probe_hbm_read", "csa_probe_mfma_bf16", "csa_probe_sink_words")
+PROBE_EXPORTS = ("csa_probe_hbm_read", "csa_probe_gather_read", "csa_probe_mfma_bf16", "csa_probe_sink_words")
 STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -104,6 +104,8 @@ def load() -> ctypes.CDLL:
                                        i64, i64, vp, vp, i64, i64, vp, i64, vp, i32, vp, sz, vp]
     lib.csa_probe_hbm_read.argtypes = [vp, sz, vp, vp]
     lib.csa_probe_hbm_read.restype = i32
+    lib.csa_probe_gather_read.argtypes = [vp, sz, sz, vp, i64, vp, vp]
+    lib.csa_probe_gather_read.restype = i32
     lib.csa_probe_mfma_bf16.argtypes = [i32, vp, vp]
     lib.csa_probe_mfma_bf16.restype = i32
     lib.csa_probe_sink_words.argtypes = []
@@ -373,6 +375,12 @@ def probe_sink(device="cuda") -> torch.Tensor:
 def probe_hbm_read(buf: torch.Tensor, sink: torch.Tensor):
     """Reads all of buf (a contiguous device tensor, 16-byte aligned, nbytes % 16 == 0) once."""
     _check(load().csa_probe_hbm_read(_p(buf), buf.numel() * buf.element_size(), _p(sink), _stream()))
+
+
+def probe_gather_read(buf: torch.Tensor, row_bytes: int, idx: torch.Tensor, sink: torch.Tensor):
+    """Reads the rows idx (int32 device tensor) of buf, each row_bytes long, once (see include/csa_probe.h)."""
+    _check(load().csa_probe_gather_read(_p(buf), buf.numel() * buf.element_size(), row_bytes, _p(idx), idx.numel(),
+                                        _p(sink), _stream()))
 
 
 def probe_mfma_bf16(iters: int, sink: torch.Tensor) -> int:

@@ -279,6 +279,12 @@ def test_probes_reject_bad_arguments():
     assert rc == -1 and "aligned" in msg
     rc, msg = _err(L.csa_probe_mfma_bf16(0, ctypes.c_void_p(4096), None))
     assert rc == -1 and "iters" in msg
+    p = ctypes.c_void_p(4096)
+    for args in ((p, 1 << 20, 1000, p, 8, p), (p, 512, 1024, p, 8, p), (ctypes.c_void_p(4104), 1 << 20, 1024, p, 8, p),
+                 (p, 1 << 20, 1024, ctypes.c_void_p(4098), 8, p), (p, 1 << 20, 1024, p, -1, p)):
+        rc, msg = _err(L.csa_probe_gather_read(*args, None))
+        assert rc == -1 and "gather" in msg, args
+    assert L.csa_probe_gather_read(p, 1 << 20, 1024, p, 0, p, None) == 0  # nothing to read: no launch
 
 
 def test_projection_gemm_rejects_bad_arguments():

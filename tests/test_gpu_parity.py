@@ -26,7 +26,10 @@ def _oracle_topk_rows(s32, nv, k):
 @pytest.mark.parametrize("R,n,k,tie", [(7, 100, 16, False), (5, 3000, 512, True), (3, 5000, 1024, False),
                                        (2, 40000, 1024, True), (4, 70000, 100, False), (6, 64, 64, True),
                                        # one workgroup per row (rows of 16K..32K scores), odd and full lengths
-                                       (3, 20001, 1024, True), (7, 32768, 512, False), (5, 24000, 2048, True)])
+                                       (3, 20001, 1024, True), (7, 32768, 512, False), (5, 24000, 2048, True),
+                                       # rows past 32K scores (the three-launch path) with many rows
+                                       (40, 32769, 1024, True), (33, 49152, 512, False), (32, 40001, 2048, True),
+                                       (31, 40000, 1024, False), (32, 49153, 1024, False)])
 def test_topk_from_scores_bit_exact(R, n, k, tie):
     rng = np.random.default_rng(R * 1000 + n)
     s = rng.standard_normal((R, n)).astype(np.float32)
@@ -34,7 +37,7 @@ def test_topk_from_scores_bit_exact(R, n, k, tie):
         s = (np.round(s * 4) / 4).astype(np.float32)
         s[:, ::3] = 0.0
         s[:, 1::7] = -0.0
-    nv = np.array([n, n // 2, 0, 1, min(n, k - 1), n - 1, 5][:R], dtype=np.int32)
+    nv = np.resize(np.array([n, n // 2, 0, 1, min(n, k - 1), n - 1, 5], dtype=np.int32), R)
     idx = torch.empty(R, k, dtype=torch.int32, device="cuda")
     sc = torch.empty(R, k, dtype=torch.float32, device="cuda")
     lib.csa_topk_from_scores(to_device(s, "f32"), to_device(nv, "i32"), k, idx, out_score=sc)
@@ -290,18 +293,20 @@ def _sampled_prefill(name, rows):
 
 
 def test_full_prefill8k_sampled():
-    _sampled_prefill("prefill8k", np.array([0, 3, 4, 127, 128, 1000, 4095, 4096, 6001, 8190, 8191]))
+    # rows at the 8-row workgroup and 64-entry key-tile seams as well as the ends
+    _sampled_prefill("prefill8k", np.array([0, 3, 4, 7, 8, 63, 64, 127, 128, 1000, 1023, 1024, 3071, 3072, 4095, 4096,
+                                            6001, 8190, 8191]))
 
 
 def test_full_chunk1m_sampled():
-    _sampled_prefill("chunk1m", np.array([0, 1, 2, 3, 777, 2048, 4094, 4095]))
+    _sampled_prefill("chunk1m", np.array([0, 1, 2, 3, 7, 8, 63, 64, 777, 1023, 1024, 2048, 3071, 3072, 4094, 4095]))
 
 
 def test_full_decode128k_sampled():
     wl = get("decode128k")
     inp = G.make_inputs(wl)
     st = run_decode(wl, decode_tensors(wl, inp))
-    _decode_check(wl, inp, st, [0, 17, 63])
+    _decode_check(wl, inp, st, [0, 7, 8, 17, 31, 32, 63])
 
 
 def test_full_decode1m_fp4():
