@@ -129,8 +129,9 @@ def gather_probe():
 def peak_probes():
     """Measured ceilings on this part (include/csa_probe.h), to report fractions against beside the
     vendor peaks: HBM read bandwidth of 16-byte loads streaming 4 GiB (far beyond the 256 MB Infinity
-    Cache), the bf16 MFMA rate of independent 32x32x16 chains on every compute unit, and for context a
-    large bf16 GEMM through torch (hipBLASLt) and a 4 GiB device copy."""
+    Cache), the read rate of distinct 1 KiB rows gathered by index (the attention's pattern), the bf16
+    MFMA rate of independent 32x32x16 chains on every compute unit, and for context a large bf16 GEMM
+    through torch (hipBLASLt) and a 4 GiB device copy."""
     import torch
     from compressed_sparse_attention_05_amd import lib
     sink = lib.probe_sink()
@@ -143,7 +144,18 @@ def peak_probes():
     y.copy_(buf)
     torch.cuda.synchronize()
     cp = float(np.median(timed_events(lambda: y.copy_(buf), 5, torch.cuda.synchronize)))
-    del buf, y
+    del y
+    # gathered rows: 1/8 of the 4 GiB buffer's 1 KiB rows, distinct, ascending, the caches evicted first
+    rows = n // 1024
+    rng = np.random.default_rng(12)
+    gidx = torch.from_numpy(np.sort(rng.choice(rows, rows // 8, replace=False)).astype(np.int32)).cuda()
+    flush = torch.ones(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    gms = []
+    for _ in range(5):
+        flush.sum()
+        gms += timed_events(lambda: lib.probe_gather_read(buf, 1024, gidx, sink), 1, torch.cuda.synchronize)
+    gt = float(np.median(gms))
+    del buf, flush
     iters = 40000
     flops = lib.probe_mfma_bf16(iters, sink)
     torch.cuda.synchronize()
@@ -157,10 +169,12 @@ def peak_probes():
     del a, b, c
     torch.cuda.empty_cache()
     return {"hbm_read_gbs": round(n / (rd * 1e-3) / 1e9, 1),
+            "gather_read_gbs": round(gidx.numel() * 1024 / (gt * 1e-3) / 1e9, 1),
             "mfma_bf16_tflops": round(flops / (mf * 1e-3) / 1e12, 1),
             "hbm_copy_gbs": round(2 * n / (cp * 1e-3) / 1e9, 1),
             "bf16_gemm_tflops_hipblaslt": round(2 * M ** 3 / (mm * 1e-3) / 1e12, 1),
-            "what": "csa_probe_hbm_read over 4 GiB; csa_probe_mfma_bf16 (4 independent 32x32x16 chains per "
+            "what": "csa_probe_hbm_read over 4 GiB; csa_probe_gather_read of 524288 distinct 1 KiB rows of that "
+                    "buffer after a 512 MiB cache eviction; csa_probe_mfma_bf16 (4 independent 32x32x16 chains per "
                     "wave, 8 waves per CU); torch copy of 4 GiB; 8192^3 bf16 torch.matmul; median of 5, HIP events"}
 
 
@@ -879,6 +893,7 @@ def main():
     ms = r["ms_per_step"]
     flops_idx = index_pairs(wl) * wl.H_I * wl.D_I * 2
     flops_attn = attn_pairs(wl) * wl.H * wl.D * 4
+    attn_gather = attn_pairs(wl) * wl.D * 2
     flops_proj = 2 * wl.B * wl.T * wl.d * wl.n_tot
     idx_ms = float(np.mean(r["idx_ms"]))
     attn_ms = float(np.mean(r["attn_ms"]))
@@ -908,7 +923,13 @@ def main():
         "kernels": {
             "sparse_attn_mfma": {"avg_launch_ms": round(attn_ms, 3), "algorithmic_flops": flops_attn,
                                  "tflops": round(flops_attn / (attn_ms * 1e-3) / 1e12, 1),
-                                 "frac_bf16_peak": round(flops_attn / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                                 "frac_bf16_peak": round(flops_attn / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                 # every (row, key) pair gathers one 1 KiB row: selected entries from a
+                                 # 268 MB cache and window rows
+                                 "gathered_bytes": attn_gather, "flop_per_byte": round(flops_attn / attn_gather, 1),
+                                 "gather_gbs": round(attn_gather / (attn_ms * 1e-3) / 1e9, 1),
+                                 "frac_hbm_peak": round(attn_gather / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                 "bound": "hbm (gathered rows): below the bf16 ridge of 312 FLOP/B"},
             "step": {"ms_events_median": round(float(np.median(r["step_ms"])), 3),
                      "layer_flops": flops_idx + flops_attn + flops_proj,
                      "layer_tflops": round((flops_idx + flops_attn + flops_proj) / (ms * 1e-3) / 1e12, 1)},
@@ -946,6 +967,8 @@ def main():
         res["measured_peaks"] = pk
         res["roofline"]["frac_measured_peak"] = round(ach / pk["mfma_bf16_tflops"], 4)
         res["roofline"]["measured_peak"] = pk["mfma_bf16_tflops"]
+        sa = res["kernels"]["sparse_attn_mfma"]
+        sa["frac_measured_gather_ceiling"] = round(sa["gather_gbs"] / pk["gather_read_gbs"], 4)
         for v in res.get("decode", {}).values():
             v["hbm_frac_measured_read"] = round(v["hbm_gbs"] / pk["hbm_read_gbs"], 4)
     if not args.no_cpu_baseline:

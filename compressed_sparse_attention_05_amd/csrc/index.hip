@@ -496,7 +496,7 @@ constexpr int kQLd = 136;  // LDS row stride (bf16) of the staged q_I heads
 __global__ void __launch_bounds__(kStreamWaves * 64, 4) score_bf16_stream(IndexArgs a, float* scores, int32_t* n_valid,
                                                                         int64_t units_per_row, uint32_t* zero,
                                                                         int64_t zero_words, float* gmax, int g0,
-                                                                        int64_t gstride) {
+                                                                        int64_t gstride, int64_t sld) {
   __shared__ __align__(16) uint16_t qs[64 * kQLd];
   __shared__ float ws[64];
   const int wave = threadIdx.x >> 6, lane = lane_id();
@@ -505,11 +505,15 @@ __global__ void __launch_bounds__(kStreamWaves * 64, 4) score_bf16_stream(IndexA
     zero[i] = 0u;
   const int64_t R = (int64_t)a.B * a.T;
   const int64_t total = R * units_per_row;
+  // every row's whole units first, then each row's last partial unit (when n_cap is not a multiple of
+  // the unit): the partial units then share the walk's last step instead of adding a step of their own
+  const int64_t upr_full = a.n_cap / kUnit, full = R * upr_full;
   int64_t cur_row = -1;
   int64_t nv_cur = 0;
   for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
-    const int64_t row = u / units_per_row;
-    const int64_t base = (u % units_per_row) * kUnit + wave * 64;
+    const int64_t row = u < full ? u / upr_full : u - full;
+    const int64_t unit = u < full ? u % upr_full : upr_full;
+    const int64_t base = unit * kUnit + wave * 64;
     const int b = (int)(row / a.T), tq = (int)(row % a.T);
     if (row != cur_row) {  // uniform across the workgroup
       __syncthreads();
@@ -519,7 +523,7 @@ __global__ void __launch_bounds__(kStreamWaves * 64, 4) score_bf16_stream(IndexA
       for (int c = threadIdx.x; c < 64 * 16; c += kStreamWaves * 64)
         *reinterpret_cast<uint4*>(&qs[(c >> 4) * kQLd + (c & 15) * 8]) = *reinterpret_cast<const uint4*>(qrow + c * 8);
       if (threadIdx.x < 64) ws[threadIdx.x] = head_weights(a, row)[threadIdx.x];
-      if (threadIdx.x == 0 && u % units_per_row == 0) n_valid[row] = (int32_t)nv_cur;
+      if (threadIdx.x == 0 && unit == 0) n_valid[row] = (int32_t)nv_cur;
       __syncthreads();
     }
     const int64_t nv = nv_cur;
@@ -558,7 +562,7 @@ __global__ void __launch_bounds__(kStreamWaves * 64, 4) score_bf16_stream(IndexA
       p += __shfl_xor(p, 32, 64);
       if ((lane >> 4) == g) mine = p;  // lane l keeps entry base + l
     }
-    store_scores(scores, gmax, row, a.n_cap, gstride, g0, base, nv, mine);
+    store_scores(scores, gmax, row, sld, gstride, g0, base, nv, mine);
   }
 }
 
@@ -572,7 +576,7 @@ constexpr int kFp4Waves = 4;
 __global__ void __launch_bounds__(kFp4Waves * 64, 4) score_fp4_stream(IndexArgs a, float* scores, int32_t* n_valid,
                                                                      int64_t tiles_per_row, uint32_t* zero,
                                                                      int64_t zero_words, float* gmax, int g0,
-                                                                     int64_t gstride) {
+                                                                     int64_t gstride, int64_t sld) {
   const int lane = lane_id();
   // the selection's counters start at zero (they are read only after this kernel)
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < zero_words; i += (int64_t)gridDim.x * blockDim.x)
@@ -585,9 +589,10 @@ __global__ void __launch_bounds__(kFp4Waves * 64, 4) score_fp4_stream(IndexArgs 
   i32x8 qa[4];
   int qs[4];
   float wr[4][4];
+  const int64_t tpr_full = a.n_cap / 64, full = R * tpr_full;  // whole tiles first, as in the bf16 walk
   for (int64_t t = (int64_t)blockIdx.x * kFp4Waves + (threadIdx.x >> 6); t < total; t += nwaves) {
-    const int64_t row = t / tiles_per_row;
-    const int64_t base = (t % tiles_per_row) * 64;
+    const int64_t row = t < full ? t / tpr_full : t - full;
+    const int64_t base = (t < full ? t % tpr_full : tpr_full) * 64;
     const int b = (int)(row / a.T), tq = (int)(row % a.T);
     if (row != cur_row) {
       cur_row = row;
@@ -634,7 +639,7 @@ __global__ void __launch_bounds__(kFp4Waves * 64, 4) score_fp4_stream(IndexArgs 
       p += __shfl_xor(p, 32, 64);
       if (g == grp) mine = p;
     }
-    store_scores(scores, gmax, row, a.n_cap, gstride, g0, base, nv, mine);
+    store_scores(scores, gmax, row, sld, gstride, g0, base, nv, mine);
   }
 }
 
@@ -667,6 +672,10 @@ bool use_decode_scores(const IndexArgs& a) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// row stride of the decode score matrix: n_cap rounded up to 64 scores, so that every row starts
+// 256-byte aligned (up to 32768 entries this keeps the one-launch selection: 32768 is a multiple)
+int64_t score_ld(int64_t n_cap) { return (n_cap + 63) / 64 * 64; }
+
 }  // namespace
 
 bool index_fused_fp4(const IndexArgs& a) { return use_prefill_fp4(a); }
@@ -674,7 +683,8 @@ bool index_fused_fp4(const IndexArgs& a) { return use_prefill_fp4(a); }
 size_t index_topk_workspace(const IndexArgs& a) {
   if (!use_decode_scores(a)) return 0;
   const int64_t R = (int64_t)a.B * a.T;
-  return align256((size_t)R * a.n_cap * 4) + align256((size_t)R * 4) + select_workspace((int)R, a.n_cap, a.k);
+  const int64_t sld = score_ld(a.n_cap);
+  return align256((size_t)R * sld * 4) + align256((size_t)R * 4) + select_workspace((int)R, sld, a.k);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -703,27 +713,28 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
     if (ws == nullptr || ws_bytes < index_topk_workspace(a)) return hipErrorInvalidValue;
     uint8_t* p = static_cast<uint8_t*>(ws);
     float* scores = reinterpret_cast<float*>(p);
-    p += align256((size_t)R * a.n_cap * 4);
+    const int64_t sld = score_ld(a.n_cap);  // rows of the score matrix start 256-byte aligned
+    p += align256((size_t)R * sld * 4);
     int32_t* nvalid = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)R * 4);
-    const SelPlan pl = select_plan(a.n_cap, a.k);
+    const SelPlan pl = select_plan(sld, a.k);
     float* gm = select_gmax(p, (int)R);
-    const int g0 = select_needs_gmax(a.n_cap) ? pl.g0 : 0;
+    const int g0 = select_needs_gmax(sld) ? pl.g0 : 0;
     if (a.idx_dtype == CSA_MXFP4) {
       const int64_t tpr = ceil_div(a.n_cap, 64) > 0 ? ceil_div(a.n_cap, 64) : 1;
       int64_t g = ceil_div(R * tpr, kFp4Waves);
       if (g > 2 * stream_grid()) g = 2 * stream_grid();
       hipLaunchKernelGGL(score_fp4_stream, dim3((unsigned)g), dim3(kFp4Waves * 64), 0, s, a, scores, nvalid, tpr,
-                         select_counters(p), R, gm, g0, pl.gstride);
+                         select_counters(p), R, gm, g0, pl.gstride, sld);
     } else {
       const int64_t upr = ceil_div(a.n_cap, kUnit) > 0 ? ceil_div(a.n_cap, kUnit) : 1;
       int64_t g = R * upr;
       if (g > stream_grid()) g = stream_grid();
       hipLaunchKernelGGL(score_bf16_stream, dim3((unsigned)g), dim3(kStreamWaves * 64), 0, s, a, scores, nvalid, upr,
-                         select_counters(p), R, gm, g0, pl.gstride);
+                         select_counters(p), R, gm, g0, pl.gstride, sld);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_select(scores, a.n_cap, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s);
+    return launch_select(scores, sld, nvalid, (int)R, a.k, a.out_idx, a.out_score, p, true, s);
   }
   const int cap = topk_cap_for(a.k, 256);
   const int lds = kGenWaves * (cap * 8 + 256 * 4);
