@@ -202,7 +202,8 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
   //   phase A of tile t: MFMA column 0 of t  |  reduce column 1 of t-1, read column 1 of t
   //   barrier: tile t+1 published
   //   phase B of tile t: MFMA column 1 of t  |  reduce column 0 of t, read column 0 of t+1
-  //   then offer the 64 scores of tile t-1 (column 0 from phase B of t-1, column 1 from phase A)
+  //   and, within phase B, offer the 64 scores of tile t-1 (column 0 from phase B of t-1, column 1
+  //   from phase A of t)
   f32x16 acc0[2], acc1[2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) acc1[mt] = f32x16{};
@@ -273,14 +274,15 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
       // column 0 of tile + 1 (an unused read of the next ring slot after the last tile)
       kf0[s] = *reinterpret_cast<const bf16x8*>(kn + key_read_off(s, 0));
       reduce_r(p4, acc0, 2 * s + 1);
+      // the 64 scores of tile - 1 go to the streaming top-k while this phase's MFMAs are in flight
+      if (s == 1 && active && tile > 0) {
+        const int64_t i = (int64_t)(tile - 1) * kNE + lane;
+        tk.offer(make_cand(sc, (uint32_t)i), i < nv);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     part0 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
     asm volatile("" ::"v"(part0));  // keeps the reduction inside phase B
-    if (active && tile > 0) {
-      const int64_t i = (int64_t)(tile - 1) * kNE + lane;
-      tk.offer(make_cand(sc, (uint32_t)i), i < nv);
-    }
     cur = nxt;
   }
   if (ntiles > 0) {
