@@ -12,6 +12,7 @@ timed region starts. Prints one JSON line.
     python bench.py --gather-probe    # 1 KiB rows gathered by index (the attention's pattern), likewise
     python bench.py --decode-leg decode128k   # one decode leg alone (for its counters)
     python bench.py --decode-pmc-summary DIR --decode-leg decode128k  # its per-kernel HBM traffic
+    python bench.py --trace-summary DIR     # per-kernel durations of a rocprofv3 --kernel-trace --stats run
     python bench.py --pmc-summary DIR # HBM bytes per kernel from rocprofv3 --pmc runs
     python bench.py --mfma-summary DIR  # matrix-core busy share of the prefill kernels (one --pmc run)
     python bench.py --attn-summary DIR  # LDS / wait counters of the 128-head attention (two --pmc runs)
@@ -297,6 +298,57 @@ def pmc_summary(pmc_dir, workload):
             gcol = f"{fk * g_scale / 1e6:.2f}" if g_scale and "attn" in nm else "-"
             f.write(f"| {nm} | {nf} | {fk * f_scale / 1e6:.2f} | {(wk or 0) * w_scale / 1e6:.2f} | {gcol} |\n")
     print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in out.items()}))
+
+
+def trace_summary(trace_dir, workload, bench_log=None):
+    """Per-kernel durations of one `rocprofv3 --kernel-trace --stats` run of the bench, and for the
+    prefill indexer and the 128-head attention the dispatches split by launch shape (the same kernel
+    serves several legs), from the run's kernel_trace.csv. Writes profiles/kernel_trace_bench_<wl>.md."""
+    import csv
+    import re
+
+    def short(n):
+        n = re.sub(r"\(anonymous namespace\)::", "", n).replace("void ", "").replace("csa::", "")
+        m = re.match(r"([\w:]+(<[^()]*>)?)", n)
+        t = re.sub(r"at::native::", "", m.group(1) if m else n)
+        return ("hipBLASLt " + t[:40]) if t.startswith("Cijk_") else t[:90]
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    tot = sum(float(r["TotalDurationNs"]) for r in stats)
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace -o run -- python3 /root/repo/bench.py "
+           f"--steps 3 --warmup 1 --no-cpu-baseline --workload {workload}")
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_bench_{workload}.md"), "w") as f:
+        f.write(f"# Kernel trace of bench.py ({workload} headline and every extra leg: MXFP4 indexer, QK-norm/RoPE, "
+                "FP8 records, prefill8k, decode, decode state, HCA, ceiling probes)\n\n")
+        f.write("Commands (repository root, run from /tmp with TMPDIR=/tmp; the profiled run's output in <out>/trace.log):"
+                "\n\n```\n" + cmd + f" > <out>/trace.log\npython3 /root/repo/bench.py --trace-summary <out>/trace "
+                f"--bench-log <out>/trace.log --workload {workload}\n```\n\n")
+        if bench_log and os.path.exists(bench_log):
+            lines = [ln for ln in open(bench_log, errors="replace") if ln.startswith("{")]
+            if lines:
+                r = json.loads(lines[-1])
+                f.write(f"The bench line this profiled run printed (its own HIP-event timing): step {r['ms_per_step']} ms, "
+                        f"index_prefill_mfma {r['roofline']['avg_launch_ms']} ms per launch, the chunk's attention "
+                        f"{r['kernels']['sparse_attn_mfma']['avg_launch_ms']} ms. Profiling slows the run; compare "
+                        "these with the chunk-shaped rows of the by-shape table below.\n\n")
+        f.write("Per-kernel durations from the run's `kernel_stats.csv`.\n\n")
+        f.write("| kernel | calls | avg us | min us | max us | share of kernel time |\n|---|---|---|---|---|---|\n")
+        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:32]:
+            f.write(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                    f"{100 * float(r['TotalDurationNs']) / tot:.1f}% |\n")
+        f.write("\nThe same kernels by launch shape (`kernel_trace.csv`; grid in threads): each shape is one leg.\n\n")
+        f.write("| kernel | grid x | workgroup | dispatches | avg us | min us | max us |\n|---|---|---|---|---|---|---|\n")
+        groups = {}
+        for r in trace:
+            nm = short(r["Kernel_Name"])
+            if not (nm.startswith("index_prefill") or nm.startswith("attn_pairs") or nm.startswith("attn_mfma")):
+                continue
+            key = (nm, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for (nm, gx, wg), d in sorted(groups.items(), key=lambda kv: (kv[0][0], -np.mean(kv[1]))):
+            f.write(f"| {nm} | {gx} | {wg} | {len(d)} | {np.mean(d):.1f} | {min(d):.1f} | {max(d):.1f} |\n")
+    print(json.dumps({"trace_summary": workload, "kernels": len(stats)}))
 
 
 def decode_pmc_summary(pmc_dir, name):
@@ -848,6 +900,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--gather-probe", action="store_true")
     ap.add_argument("--decode-leg", metavar="NAME", help="run one decode leg alone (decode128k, decode1m_fp4)")
+    ap.add_argument("--trace-summary", metavar="DIR", help="summarise a rocprofv3 --kernel-trace --stats run in DIR")
+    ap.add_argument("--bench-log", metavar="FILE", help="with --trace-summary: the profiled run's output")
     ap.add_argument("--decode-pmc-summary", metavar="DIR", help="summarise the --pmc runs of one --decode-leg")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise four rocprofv3 --pmc runs under DIR")
     ap.add_argument("--mfma-summary", metavar="DIR", help="summarise one rocprofv3 --pmc run of the MFMA busy counter")
@@ -862,6 +916,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.workload)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.workload, args.bench_log)
         return
     if args.decode_pmc_summary:
         decode_pmc_summary(args.decode_pmc_summary, args.decode_leg)
