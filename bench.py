@@ -986,7 +986,9 @@ def main():
                                  "gathered_bytes": attn_gather, "flop_per_byte": round(flops_attn / attn_gather, 1),
                                  "gather_gbs": round(attn_gather / (attn_ms * 1e-3) / 1e9, 1),
                                  "frac_hbm_peak": round(attn_gather / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                 "bound": "hbm (gathered rows): below the bf16 ridge of 312 FLOP/B"},
+                                 "roofline_bound": "hbm by intensity (256 FLOP per gathered byte, below the bf16 "
+                                                   "ridge of 312); measured, the kernel's own loop limits it (a "
+                                                   "gather-free build is 12 % faster)"},
             "step": {"ms_events_median": round(float(np.median(r["step_ms"])), 3),
                      "layer_flops": flops_idx + flops_attn + flops_proj,
                      "layer_tflops": round((flops_idx + flops_attn + flops_proj) / (ms * 1e-3) / 1e12, 1)},
