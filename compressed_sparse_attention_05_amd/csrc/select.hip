@@ -420,6 +420,7 @@ constexpr int kRowWaves = kRowThreads / 64;
 constexpr int kRowMax = 32 * kRowThreads;
 constexpr int kRowBins = 4096;
 constexpr int kRowChunks = kRowMax / 256;
+constexpr int kFillRows = 256;  // one-workgroup selections that fill the chip (one per compute unit)
 
 struct RowSmem {
   uint32_t hist[kRowBins];
@@ -491,6 +492,7 @@ struct RowSel {
   float* out_score;        // nullable
   const int32_t* remap;    // nullable
   const int32_t* row_nv;   // nullable
+  bool cand_pads;          // pad slots get the smallest key (score bits 0xFFFFFFFF), below any score's
 };
 
 template <int P, bool VEC>
@@ -525,7 +527,7 @@ __global__ void __launch_bounds__(kRowThreads) sel_row(RowSel a) {
   if (nv <= k) {  // every valid entry is selected
     for (int j = tid; j < k; j += kRowThreads) {
       oi[j] = j < nv ? index_of(base + j) : -1;
-      if (os) os[j] = j < nv ? key_to_score(score_to_key(s[j])) : -INFINITY;
+      if (os) os[j] = j < nv ? key_to_score(score_to_key(s[j])) : (a.cand_pads ? __uint_as_float(0xFFFFFFFFu) : -INFINITY);
     }
     return;
   }
@@ -725,7 +727,7 @@ hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid
   const SelBufs w = carve(ws, R, ld, k);
   hipError_t e;
   const int lds = (int)sizeof(FinalSmem);
-  if (ld <= kRowMax) {  // one workgroup per row, the row in registers, one launch
+  if (ld <= kRowMax) {  // one workgroup per row (or per piece of a row), the scores in registers
     RowSel rs{};
     rs.scores = scores;
     rs.ld = ld;
@@ -735,7 +737,45 @@ hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid
     rs.k = k;
     rs.out_idx = out_idx;
     rs.out_score = out_score;
+    // Too few rows to fill the chip: the k best of each of several pieces of a row (at least 2k
+    // scores each), then the k best of those candidates with positions mapped back to indices. The
+    // row's k best are among its pieces' k best, every list is in index order and both passes use
+    // the same key order, so the result is the one-pass selection's.
+    int64_t chunk = ld;
+    if (R < kFillRows) {
+      // a launch's cost grows with the scores a workgroup holds, on top of a fixed part, so about
+      // sqrt(ld / k) pieces balance the two passes
+      const int64_t want = ceil_div(kFillRows, R), most = ld / (2 * (int64_t)k);
+      const int64_t bal = (int64_t)ceil(sqrt((double)ld / k));
+      int64_t pieces = want < most ? want : most;
+      pieces = pieces < bal ? pieces : bal;
+      if (pieces > 1) chunk = ceil_div(ceil_div(ld, pieces), 1024) * 1024;
+    }
+    const int64_t nchunk = ceil_div(ld, chunk);
+    if (nchunk <= 1) {
+      launch_row(rs, R, s);
+      return hipGetLastError();
+    }
+    int32_t* cand_idx = reinterpret_cast<int32_t*>(w.cand);
+    float* cand_score = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(w.cand) + a256((size_t)R * nchunk * k * 4));
+    rs.chunk = chunk;
+    rs.nchunk = (int)nchunk;
+    rs.out_idx = cand_idx;
+    rs.out_score = cand_score;
+    rs.cand_pads = true;  // a piece with fewer than k entries pads below every real candidate
     launch_row(rs, R, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    RowSel r2{};
+    r2.scores = cand_score;
+    r2.ld = nchunk * k;
+    r2.chunk = nchunk * k;
+    r2.nchunk = 1;
+    r2.k = k;
+    r2.out_idx = out_idx;
+    r2.out_score = out_score;
+    r2.remap = cand_idx;
+    r2.row_nv = n_valid;
+    launch_row(r2, R, s);
     return hipGetLastError();
   }
   if (!have_gmax) {

@@ -50,6 +50,21 @@ def test_topk_from_scores_bit_exact(R, n, k, tie):
         np.testing.assert_array_equal(gs[r][v], s[r][want[r][v]])
 
 
+def test_topk_from_scores_negative_infinity_scores():
+    # valid entries scored -inf rank below every finite score and among themselves by index; rows split
+    # into pieces (few rows) must not let a short piece's padding outrank them
+    R, n, k = 4, 12288, 1024
+    rng = np.random.default_rng(77)
+    s = rng.standard_normal((R, n)).astype(np.float32)
+    s[:, 300:] = -np.inf                       # 300 finite scores, then -inf
+    s[1, :] = -np.inf                          # every score -inf
+    s[2, 5000:5100] = 1.0                      # finite scores in a later piece
+    nv = np.array([n, n, n - 7, 2500], dtype=np.int32)
+    idx = torch.empty(R, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk_from_scores(to_device(s, "f32"), to_device(nv, "i32"), k, idx)
+    np.testing.assert_array_equal(idx.cpu().numpy(), _oracle_topk_rows(s, nv, k))
+
+
 @pytest.mark.parametrize("n", [20000, 32768, 50000])
 def test_topk_from_scores_constant_rows(n):
     # every score equal: the top-k is the first k entries (ties go to the smaller index)
