@@ -404,10 +404,17 @@ def decode_pmc_summary(pmc_dir, name):
             wk = med(write, lambda n, nm=nm: "csa::" in n and _short_kernel(n) == nm)[0] or 0.0
             key = next((k for k in ("score", "sel", "attn_pairs", "attn_combine") if nm.startswith(k)), None)
             cr, cwb = comp.get(key, (None, None)) if key else (None, None)
+            rows_sel = sorted(n for n in names if n.startswith("sel_row"))
             if nm.startswith("sel_collect"):  # the long-row selection: scores in, candidates out
                 cwb = None
             elif nm.startswith("sel_final"):  # candidates in, indices out
                 cr = None
+            elif nm.startswith("sel_row") and len(rows_sel) > 1:  # two passes: pieces, then candidates
+                first = max(rows_sel, key=lambda n: int(n.split("<")[1].split(",")[0]))
+                if nm == first:
+                    cwb = None
+                else:
+                    cr = None
             fb = fk * (g_scale if key == "attn_pairs" else f_scale)
             f.write(f"| {nm} | {nd} | {fb / 1e6:.2f} | {'-' if cr is None else f'{cr / 1e6:.2f}'} | "
                     f"{wk * w_scale / 1e6:.2f} | {'-' if cwb is None else f'{cwb / 1e6:.2f}'} |\n")
