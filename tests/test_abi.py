@@ -6,7 +6,7 @@ import re
 
 import pytest
 
-from compressed_sparse_attention_05_amd import lib
+from compressed_sparse_attention_05_amd import layer, lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -299,3 +299,19 @@ def test_projection_gemm_rejects_bad_arguments():
     rc, msg = _err(L.csa_projection_gemm(4, 8, 64, lib.CSA_BF16, None, 64, p, 64, p, 8, lib.CSA_F32, None))
     assert rc == -1 and "NULL" in msg
     assert L.csa_projection_gemm(0, 8, 64, lib.CSA_BF16, None, 64, None, 64, None, 8, lib.CSA_F32, None) == 0
+
+
+def test_sparse_attn_qk_rejects_bad_arguments():
+    L = lib.load()
+    d = layer.dims(4, 512, 128, 64, 128, 1024, 128)
+    p = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    args = lambda w: (ctypes.byref(d), w, 1, 1, p, lib.CSA_BF16, p, 128 * 512, 128 * 512, p, 1024 * 512, 1024, p, p,
+                      512, 128 * 512, p, 128, p, lib.CSA_F32, None, 0, None)
+    rc, msg = _err(L.csa_sparse_attn_qk(*args(None)))
+    assert rc == -1 and "weights" in msg
+    w = lib.Weights(None, None, None, None, None, None, None, None, None, 1e-6, 63, 10000.0)
+    rc, msg = _err(L.csa_sparse_attn_qk(*args(ctypes.byref(w))))
+    assert rc == -1 and "rope_dims" in msg
+    w = lib.Weights(None, None, None, None, None, None, None, None, None, 1e-6, 64, 0.0)
+    rc, msg = _err(L.csa_sparse_attn_qk(*args(ctypes.byref(w))))
+    assert rc == -1 and "rope_theta" in msg
