@@ -427,12 +427,15 @@ def attn_summary(pmc_dir, workload):
     LDS instruction counts. Writes profiles/attn_pairs_counters_<workload>.md."""
     c1 = "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_INSTS_LDS GRBM_GUI_ACTIVE"
     c2 = "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE"
+    c3 = "SQ_VALU_MFMA_COEXEC_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_MISC SQ_ACTIVE_INST_SCA SQ_INST_CYCLES_SALU SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL GRBM_GUI_ACTIVE"
     bench_cmd = COUNTER_BENCH + workload + " --no-decode"
     cmds = [f"rocprofv3 --pmc {c1} --output-format csv -d <out>/attn1 -o run -- {bench_cmd}",
             f"rocprofv3 --pmc {c2} --output-format csv -d <out>/attn2 -o run -- {bench_cmd}",
+            f"rocprofv3 --pmc {c3} --output-format csv -d <out>/attn3 -o run -- {bench_cmd}",
             f"python3 /root/repo/bench.py --attn-summary <out> --workload {workload}"]
     vals = {}
-    for run in ("attn1", "attn2"):
+    runs = [r for r in ("attn1", "attn2", "attn3") if os.path.exists(os.path.join(pmc_dir, r, "run_counter_collection.csv"))]
+    for run in runs:
         import csv
         per = {}
         with open(os.path.join(pmc_dir, run, "run_counter_collection.csv"), newline="") as f:
@@ -461,6 +464,15 @@ def attn_summary(pmc_dir, workload):
             ("wave-cycles waiting to issue LDS / wave-cycles", f"{100 * vals['SQ_WAIT_INST_LDS'] / vals['SQ_WAVE_CYCLES']:.1f}%"),
             ("LDS address conflicts", f"{vals['SQ_LDS_ADDR_CONFLICT']:.0f}"),
             ("GPU cycles per dispatch (one XCD)", f"{gui:.4g}")]
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in vals:
+        rows += [("cycles with VALU and MFMA co-executing / MFMA busy cycles",
+                  f"{100 * vals['SQ_VALU_MFMA_COEXEC_CYCLES'] / vals['SQ_VALU_MFMA_BUSY_CYCLES']:.1f}%"),
+                 ("scalar-ALU instruction cycles / wave-cycles",
+                  f"{100 * vals['SQ_INST_CYCLES_SALU'] / vals['SQ_WAVE_CYCLES']:.1f}%"),
+                 ("LDS data FIFO full, cycles per CU / GPU cycles",
+                  f"{100 * vals['SQ_LDS_DATA_FIFO_FULL'] / 256 / gui:.1f}%"),
+                 ("LDS command FIFO full, cycles per CU / GPU cycles",
+                  f"{100 * vals['SQ_LDS_CMD_FIFO_FULL'] / 256 / gui:.2f}%")]
     with open(os.path.join(ROOT, "profiles", f"attn_pairs_counters_{workload}.md"), "w") as f:
         f.write(f"# attn_pairs (128 heads, bf16 rows), {workload}: matrix-core, LDS and wait counters\n\n")
         f.write("Commands (repository root, run from /tmp with TMPDIR=/tmp):\n\n```\n" + "\n".join(cmds) + "\n```\n\n")
