@@ -67,3 +67,39 @@ def test_noalloc_decode_step_matches_workspace_step(first):
         assert torch.equal(idx, a.idx), f"call {c}: selections differ"
         for name in ("entries", "keys", "win", "block"):
             assert torch.equal(getattr(a, name), getattr(b, name)), f"call {c}: state {name} differs"
+
+
+def test_noalloc_decode_step_replays_in_a_captured_graph():
+    # the caller this entry point is for: a serving loop that captures the step once (nothing may
+    # allocate under capture) and replays it. Replaying the same step rewrites the same state rows with
+    # the same values, so every replay, with eager work between replays, equals the eager call.
+    B, n_cap, seed = 4, 3000, 210
+    d = lib.make_dims(M, D, H, H_I, D_I, K, W)
+    st = _state(seed, B, n_cap, True)
+    w = _weights(seed, True)
+    q, qi = _bf(seed, "q", (B, H, D)), _bf(seed, "qi", (B, H_I, D_I))
+    kv, comp = _bf(seed, "kv", (B, D)), _bf(seed, "comp", (B, 4 * D + 4 * D_I))
+    pos = torch.tensor([4 * 2500 - 1, 4 * 2000 + 1, 4 * 2900 + 3, 700], dtype=torch.int64, device="cuda")
+    out, idx = torch.empty_like(st.out), torch.empty_like(st.idx)
+    state = st.state()
+    step = lambda: lib.csa_decode_step_noalloc(d, w, pos, q, qi, kv, comp, state, out, out_idx=idx)
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_idx = out.clone(), idx.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {r}: outputs differ"
+        assert torch.equal(idx, ref_idx), f"replay {r}: selections differ"
