@@ -721,7 +721,7 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, size_t ws_bytes, hipS
     p += align256((size_t)R * 4);
     const SelPlan pl = select_plan(sld, a.k);
     float* gm = select_gmax(p, (int)R);
-    const int g0 = select_needs_gmax(sld) ? pl.g0 : 0;
+    const int g0 = select_needs_gmax(sld, a.k) ? pl.g0 : 0;
     if (a.idx_dtype == CSA_MXFP4) {
       const int64_t tpr = ceil_div(a.n_cap, 64) > 0 ? ceil_div(a.n_cap, 64) : 1;
       int64_t g = ceil_div(R * tpr, kFp4Waves);

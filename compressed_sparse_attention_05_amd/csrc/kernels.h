@@ -173,7 +173,7 @@ struct SelPlan {
   int64_t gstride;
 };
 SelPlan select_plan(int64_t ld, int k);
-bool select_needs_gmax(int64_t ld);       // false: rows short enough to take their bound from themselves
+bool select_needs_gmax(int64_t ld, int k);       // false: rows short enough to take their bound from themselves
 size_t select_workspace(int R, int64_t ld, int k);
 uint32_t* select_counters(void* ws);      // [R] words that must be zero before launch_select(have_gmax)
 float* select_gmax(void* ws, int R);      // [R, gstride] group maxima

@@ -698,7 +698,13 @@ SelBufs carve(void* ws, int R, int64_t ld, int k) {
 
 }  // namespace
 
-bool select_needs_gmax(int64_t ld) { return ld > kRowMax; }
+// Rows of up to 4 x 32K scores whose pieces' candidates fit one workgroup go in two passes of the
+// one-workgroup kernel; longer rows take the group-maximum path.
+bool select_two_pass(int64_t ld, int k) {
+  return ld <= kRowMax || (ld <= 4 * (int64_t)kRowMax && ceil_div(ld, kRowMax) * k <= kRowMax);
+}
+
+bool select_needs_gmax(int64_t ld, int k) { return !select_two_pass(ld, k); }
 
 SelPlan select_plan(int64_t ld, int k) {
   // gs: the largest power of two with ld / gs >= 2k groups (at least 16 entries per group)
@@ -727,7 +733,7 @@ hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid
   const SelBufs w = carve(ws, R, ld, k);
   hipError_t e;
   const int lds = (int)sizeof(FinalSmem);
-  if (ld <= kRowMax) {  // one workgroup per row (or per piece of a row), the scores in registers
+  if (select_two_pass(ld, k)) {  // one workgroup per row (or per piece of a row), the scores in registers
     RowSel rs{};
     rs.scores = scores;
     rs.ld = ld;
@@ -737,20 +743,23 @@ hipError_t launch_select(const float* scores, int64_t ld, const int32_t* n_valid
     rs.k = k;
     rs.out_idx = out_idx;
     rs.out_score = out_score;
-    // Too few rows to fill the chip: the k best of each of several pieces of a row (at least 2k
-    // scores each), then the k best of those candidates with positions mapped back to indices. The
-    // row's k best are among its pieces' k best, every list is in index order and both passes use
-    // the same key order, so the result is the one-pass selection's.
-    int64_t chunk = ld;
+    // Rows longer than one workgroup holds, or too few rows to fill the chip: the k best of each of
+    // several pieces of a row (at most 32K and, by choice, at least 2k scores each), then the k best
+    // of those candidates with positions mapped back to indices. The row's k best are among its
+    // pieces' k best, every list is in index order and both passes use the same key order, so the
+    // result is the one-pass selection's.
+    int64_t pieces = ceil_div(ld, kRowMax);
     if (R < kFillRows) {
       // a launch's cost grows with the scores a workgroup holds, on top of a fixed part, so about
       // sqrt(ld / k) pieces balance the two passes
       const int64_t want = ceil_div(kFillRows, R), most = ld / (2 * (int64_t)k);
       const int64_t bal = (int64_t)ceil(sqrt((double)ld / k));
-      int64_t pieces = want < most ? want : most;
-      pieces = pieces < bal ? pieces : bal;
-      if (pieces > 1) chunk = ceil_div(ceil_div(ld, pieces), 1024) * 1024;
+      int64_t p = want < most ? want : most;
+      p = p < bal ? p : bal;
+      p = p < kRowMax / k ? p : kRowMax / k;  // the candidates fit one workgroup
+      pieces = p > pieces ? p : pieces;
     }
+    const int64_t chunk = pieces > 1 ? ceil_div(ceil_div(ld, pieces), 1024) * 1024 : ld;
     const int64_t nchunk = ceil_div(ld, chunk);
     if (nchunk <= 1) {
       launch_row(rs, R, s);
