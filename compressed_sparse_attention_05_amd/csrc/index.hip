@@ -478,8 +478,25 @@ __device__ __forceinline__ void store_scores(float* scores, float* gmax, int64_t
   const bool valid = i < nv;
   if (valid) scores[row * n_cap + i] = mine;
   if (g0 == 0) return;  // short rows: the selection needs no group maxima
+  // maximum over aligned groups of g0 (16, 32 or 64) lanes by lane permutations on the vector unit:
+  // two quad permutations and the half-row and row mirrors (groups of 4, 8, 16), then the 16- and
+  // 32-lane swaps
   float v = valid ? mine : -INFINITY;
-  for (int o = 1; o < g0; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  auto dpp_max = [](float x, auto ctrl) {
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false)));
+  };
+  v = dpp_max(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  v = dpp_max(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  v = dpp_max(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  v = dpp_max(v, std::integral_constant<int, 0x140>{});  // row_mirror
+  if (g0 >= 32) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  if (g0 >= 64) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
   if ((lane & (g0 - 1)) == 0 && valid) gmax[row * gstride + i / g0] = v;
 }
 

@@ -29,7 +29,9 @@ def _oracle_topk_rows(s32, nv, k):
                                        (3, 20001, 1024, True), (7, 32768, 512, False), (5, 24000, 2048, True),
                                        # rows past 32K scores (the three-launch path) with many rows
                                        (40, 32769, 1024, True), (33, 49152, 512, False), (32, 40001, 2048, True),
-                                       (31, 40000, 1024, False), (32, 49153, 1024, False)])
+                                       (31, 40000, 1024, False), (32, 49153, 1024, False),
+                                       # rows past 4 x 32K scores: group maxima, candidates, final selection
+                                       (3, 200000, 1024, True), (5, 140000, 512, False)])
 def test_topk_from_scores_bit_exact(R, n, k, tie):
     rng = np.random.default_rng(R * 1000 + n)
     s = rng.standard_normal((R, n)).astype(np.float32)
