@@ -758,11 +758,12 @@ def cpu_baseline_decode(name):
                                         f"({dt:.2f} s) x {wl.B}", "host": hi}
 
 
-def bench_decode_state(steps, warmup, records=True):
+def bench_decode_state(steps, warmup, records=True, fp4_keys=False):
     """Token-by-token decode of the decode128k batch over a state cache (csa_decode_step) with
-    QK-norm + RoPE on, over the pages' cache format (584-byte FP8 entry records) or bf16 entry rows:
-    four consecutive steps L .. L+3, the last of which completes a block and compresses its entry and
-    key. Reported per step, averaged over the block."""
+    QK-norm + RoPE on, over 584-byte FP8 entry records or bf16 entry rows, and bf16 or MXFP4 indexer
+    keys (records + MXFP4 keys: the pages' cache format): four consecutive steps L .. L+3, the last of
+    which completes a block and compresses its entry and key. Reported per step, averaged over the
+    block."""
     import torch
     from compressed_sparse_attention_05_amd import layer, lib
     from synth import gen as G
@@ -774,14 +775,22 @@ def bench_decode_state(steps, warmup, records=True):
     inp = G.make_inputs(wl)
     d = layer.dims(wl.m, wl.D, wl.H, wl.H_I, wl.D_I, wl.k, wl.W)
     N = wl.L // wl.m
-    st = layer.CSADecodeState(d, wl.B, N + 1, records=records)
+    st = layer.CSADecodeState(d, wl.B, N + 1, records=records, fp4_keys=fp4_keys)
     ent = act(inp["entries"], wl)
     if records:
         lib.csa_entry_pack(ent, st.entries[:, :N])
     else:
         st.entries[:, :N] = ent
     del ent
-    st.keys[:, :N] = act(inp["keys"], wl)
+    if fp4_keys:  # the generated bf16 keys in MXFP4, as the compressor's epilogue stores them
+        kb = act(inp["keys"], wl)
+        for b in range(wl.B):
+            c, sc = lib.csa_mxfp4_quantize(kb[b])
+            st.keys[b, :N] = c
+            st.key_scales[b, :N] = sc
+        del kb
+    else:
+        st.keys[:, :N] = act(inp["keys"], wl)
     raw = act(inp["kv_raw"], wl)                      # positions L-127 .. L
     for r in range(wl.W - 1):
         st.win[:, (wl.L - wl.W + 1 + r) % wl.W] = raw[:, r]
@@ -819,6 +828,7 @@ def bench_decode_state(steps, warmup, records=True):
     us = float(np.median(ms)) * 1e3 / 4
     return {"us_per_step": round(us, 2), "B": wl.B, "context_tokens": wl.L,
             "entries": "584-byte FP8 records" if records else "bf16 rows",
+            "indexer_keys": "MXFP4 (64 B codes + 4 B scales)" if fp4_keys else "bf16",
             "qk_norm_rope": True, "what": "4 steps at L..L+3, one block completed (entry + key compressed)"}
 
 
@@ -1037,6 +1047,7 @@ def main():
         res["fid"]["decode128k_us_per_step"] = dfid["us_per_step"]
         res["decode_state"] = bench_decode_state(max(args.steps, 10), 2)
         res["decode_state_bf16_entries"] = bench_decode_state(max(args.steps, 10), 2, records=False)
+        res["decode_state_pages_format"] = bench_decode_state(max(args.steps, 10), 2, records=True, fp4_keys=True)
     if not args.no_hca:
         res["hca"] = bench_hca(min(args.steps, 5), 2)
     if not args.no_peak_probes:
