@@ -163,3 +163,48 @@ def test_sparse_attn_qk_matches_oracle(case):
             o = O.sparse_attention(q, r["entries"], r["idx"], r["raw"], wl.L - (wl.W - 1), qpos, wl.W)
             ref = O.rope(o, qpos, 64, 10000.0, inverse=True)
         assert max_err(tensor_f64(out[b]), ref) <= TOL[wl.dtype], (case, b)
+
+
+@pytest.mark.parametrize("dtype,T", [("bf16", 40), ("bf16", 7), ("f32", 12)])
+def test_sparse_attn_qk_chunk_rows(dtype, T):
+    """csa_sparse_attn_qk over a chunk of T query rows (8 or more: the prefill plan, the norm and rotation
+    inside the 128-head kernel for bf16; fewer: the split plan, turned back in the merge; float32: the
+    separate passes), two sequences at different positions, on seeded selections."""
+    B, H, D, k, W, m = 2, 128, 512, 64, 128, 4
+    n_cap = 600
+    rng = np.random.default_rng(T)
+    host, dev = _fid(D, 97, 64)
+    pos0 = np.array([2000, 1555])
+    bf = dtype == "bf16"
+
+    def make(name, shape, scale=1.0):
+        x = G.normal_f32(98, name, shape) * np.float32(scale)
+        if bf:
+            bits = G.f32_to_bf16_bits(x)
+            return to_device(bits, "bf16"), O.bf16_bits_to_f64(bits)
+        return to_device(x, "f32"), x.astype(np.float64)
+    q_d, q_h = make(f"qk_q{T}", (B, T, H, D))
+    ent_d, ent_h = make(f"qk_e{T}", (B, n_cap, D))
+    R = T + W - 1
+    raw_d, raw_h = make(f"qk_r{T}", (B, R, D))
+    idx = np.full((B, T, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            nv = min(n_cap, (int(pos0[b]) + t + 1) // m)
+            sel = np.sort(rng.choice(nv, size=min(k - 3 * (t % 3), nv), replace=False))
+            idx[b, t, :sel.size] = sel
+    out = torch.empty(B, T, H, D, dtype=torch.float32, device="cuda")
+    d = lib.make_dims(m, D, H, 64, 128, k, W)
+    fid = {"gamma_q": dev["gamma_q"], "eps": 1e-6, "rope_dims": 64, "theta": 10000.0}
+    lib.csa_sparse_attn_qk(d, fid, q_d, ent_d, to_device(idx, "i32"), raw_d, out,
+                           q_pos0=torch.tensor(pos0, dtype=torch.int64, device="cuda"),
+                           raw_pos0=torch.tensor(pos0 - (W - 1), dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    got = tensor_f64(out)
+    for b in range(B):
+        qp = pos0[b] + np.arange(T)
+        qn = O.rope(O.rms_norm(q_h[b], host["gamma_q"], host["eps"]), qp, 64, 10000.0)
+        qn = O.round_bf16(qn) if bf else qn
+        o = O.sparse_attention(qn, ent_h[b], idx[b], raw_h[b], int(pos0[b]) - (W - 1), qp, W)
+        ref = O.rope(o, qp, 64, 10000.0, inverse=True)
+        assert max_err(got[b], ref) <= TOL[dtype], (dtype, T, b)
