@@ -139,6 +139,21 @@ __device__ __forceinline__ void copy_to_lds16(const void* src, uint32_t lds) {
       : "memory");
 }
 
+// The same copy from a wave-uniform base address plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void copy_to_lds16_sbase(const void* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
 // Four bytes per lane (global_load_lds_dword): LDS destination M0 + 4 * lane.
 __device__ __forceinline__ void copy_to_lds4(const void* src, uint32_t lds) {
   uint32_t saved;
@@ -151,6 +166,21 @@ __device__ __forceinline__ void copy_to_lds4(const void* src, uint32_t lds) {
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// The same copy from a wave-uniform base address plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void copy_to_lds4_sbase(const void* base, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds)
       : "memory");
 }
 

@@ -177,15 +177,27 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
   const int ntiles = __builtin_amdgcn_readfirstlane((int)ceil_div(nv_max, kNE));  // uniform
   static_assert(16 % QW == 0, "each wave loads 16 / QW blocks of a key tile");
   const uint32_t ring_lds = lds_offset(smem);
-  // the 16 / QW blocks this wave loads of each tile: q = j*QW + wave
+  // The 16 / QW blocks this wave loads of each tile are q = j*QW + wave. Block j + 1 sits 32 key
+  // rows (8 KB) past block j, so in a tile whose rows are all visible both are one per-lane byte
+  // offset from a wave-uniform address; the last tile clamps its rows to the last visible entry.
+  static_assert(QW == 8, "blocks wave and wave + 8 are 32 key rows apart");
+  const uint32_t lane_off = (uint32_t)(key_block_row(wave, lane) * 256 + key_block_chunk(wave, lane) * 16);
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(ring_lds + wave * 1024);
+  const int full_tiles = __builtin_amdgcn_readfirstlane((int)(nv_max / kNE));  // tiles with every row visible
   auto load_tile = [&](int tile, int buf) {
+    const uint32_t dst = wave_lds + buf * kTileBytes;
+    if (tile < full_tiles) {
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(kseq) + (int64_t)tile * kTileBytes;
 #pragma unroll
-    for (int j = 0; j < 16 / QW; ++j) {
-      const int q = j * QW + wave;
-      int64_t e = (int64_t)tile * kNE + key_block_row(q, lane);
-      e = e < nv_max ? e : nv_max - 1;  // rows past the last visible entry are never offered
-      copy_to_lds16(kseq + e * 128 + key_block_chunk(q, lane) * 8,
-                    __builtin_amdgcn_readfirstlane(ring_lds + buf * kTileBytes + q * 1024));
+      for (int j = 0; j < 16 / QW; ++j) copy_to_lds16_sbase(base + j * 8192, lane_off, dst + j * QW * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16 / QW; ++j) {
+        const int q = j * QW + wave;
+        int64_t e = (int64_t)tile * kNE + key_block_row(q, lane);
+        e = e < nv_max ? e : nv_max - 1;  // rows past the last visible entry are never offered
+        copy_to_lds16(kseq + e * 128 + key_block_chunk(q, lane) * 8, dst + j * QW * 1024);
+      }
     }
   };
   // waits for this wave's copies of every tile but the newest `pending` ones (2 instructions each)
@@ -276,8 +288,8 @@ __global__ void __launch_bounds__(QW * 64) index_prefill_mfma(IndexArgs a, int c
       reduce_r(p4, acc0, 2 * s + 1);
       // the 64 scores of tile - 1 go to the streaming top-k while this phase's MFMAs are in flight
       if (s == 1 && active && tile > 0) {
-        const int64_t i = (int64_t)(tile - 1) * kNE + lane;
-        tk.offer(make_cand(sc, (uint32_t)i), i < nv);
+        const uint32_t i = (uint32_t)(tile - 1) * kNE + lane;
+        tk.offer(make_cand(sc, i), i < (uint32_t)nv);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -368,16 +380,28 @@ __global__ void __launch_bounds__(kF4QW * 64) index_prefill_fp4(IndexArgs a, int
   const uint8_t* kscale = a.k_scale + (int64_t)b * a.n_cap * 4;
   const int ntiles = __builtin_amdgcn_readfirstlane((int)ceil_div(nv_max, kF4NE));  // uniform
   const uint32_t ring_lds = lds_offset(smem);
-  // rows past the last visible entry are loaded as that entry (in bounds) and never offered
+  // A tile whose rows are all visible is loaded from wave-uniform addresses plus per-lane byte
+  // offsets; in the last tile, rows past the last visible entry are loaded as that entry (in bounds)
+  // and never offered.
+  const uint32_t code_off = (uint32_t)((wave * 16 + c) * 64 + g * 16);
+  const uint32_t scale_off = (uint32_t)((wave * 64 + lane) * 4);  // waves 0 and 1
+  const uint32_t code_lds = __builtin_amdgcn_readfirstlane(ring_lds + wave * 1024);
+  const uint32_t scale_lds = __builtin_amdgcn_readfirstlane(ring_lds + kF4CodeBytes + wave * 256);
+  const int full_tiles = __builtin_amdgcn_readfirstlane((int)(nv_max / kF4NE));
   auto load_tile = [&](int tile, int slot) {
-    const uint32_t base = ring_lds + slot * kF4TileBytes;
-    int64_t e = (int64_t)tile * kF4NE + wave * 16 + c;
-    e = e < nv_max ? e : nv_max - 1;
-    copy_to_lds16(kcodes + e * 64 + g * 16, __builtin_amdgcn_readfirstlane(base + wave * 1024));
-    if (wave < 2) {
-      int64_t es = (int64_t)tile * kF4NE + wave * 64 + lane;
-      es = es < nv_max ? es : nv_max - 1;
-      copy_to_lds4(kscale + es * 4, __builtin_amdgcn_readfirstlane(base + kF4CodeBytes + wave * 256));
+    const uint32_t sb = slot * kF4TileBytes;
+    if (tile < full_tiles) {
+      copy_to_lds16_sbase(kcodes + (int64_t)tile * kF4CodeBytes, code_off, code_lds + sb);
+      if (wave < 2) copy_to_lds4_sbase(kscale + (int64_t)tile * kF4NE * 4, scale_off, scale_lds + sb);
+    } else {
+      int64_t e = (int64_t)tile * kF4NE + wave * 16 + c;
+      e = e < nv_max ? e : nv_max - 1;
+      copy_to_lds16(kcodes + e * 64 + g * 16, code_lds + sb);
+      if (wave < 2) {
+        int64_t es = (int64_t)tile * kF4NE + wave * 64 + lane;
+        es = es < nv_max ? es : nv_max - 1;
+        copy_to_lds4(kscale + es * 4, scale_lds + sb);
+      }
     }
   };
   // waits until this wave's copies of every tile but the newest `pending` one have landed
@@ -440,8 +464,8 @@ __global__ void __launch_bounds__(kF4QW * 64) index_prefill_fp4(IndexArgs a, int
       const float h13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
       const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h02), __float_as_uint(h13), false, false);
       const float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      const int64_t i = (int64_t)tile * kF4NE + half * 64 + lane;
-      if (active) tk.offer(make_cand(sc, (uint32_t)i), i < nv);
+      const uint32_t i = (uint32_t)tile * kF4NE + half * 64 + lane;
+      if (active) tk.offer(make_cand(sc, i), i < (uint32_t)nv);
     }
   }
   if (active) tk.finish(a.out_idx + row * a.k, a.out_score ? a.out_score + row * a.k : nullptr);
