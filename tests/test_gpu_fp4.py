@@ -95,10 +95,13 @@ def _fp4_index_case(T, n_cap, k, seed, q_pos0):
     return idx[0].cpu().numpy(), ora, scores, nv
 
 
-@pytest.mark.parametrize("T,n_cap,k,q_pos0", [(44, 3000, 256, 11000), (20, 700, 512, 500), (9, 130, 64, 0)])
+@pytest.mark.parametrize("T,n_cap,k,q_pos0", [(44, 3000, 256, 11000), (20, 700, 512, 500), (9, 130, 64, 0),
+                                               (16, 5000, 64, 512 * 5 - 16), (16, 5000, 64, 512 * 5 - 12),
+                                               (16, 640, 64, 4000), (16, 641, 64, 4000)])
 def test_fused_fp4_prefill_index(T, n_cap, k, q_pos0):
     # T >= 8 rows per sequence take the fused MXFP4 kernel: several 128-entry tiles, a ragged last tile,
-    # a ragged last workgroup of rows, and (second case) rows that see fewer than k entries
+    # a ragged last workgroup of rows, (second case) rows that see fewer than k entries, and (the last
+    # four) a last workgroup that sees exactly 5 whole tiles or one entry more, by position or capacity
     assert lib.csa_workspace_size(lib.CSA_OP_INDEX_TOPK, layer.dims(4, 512, 128, 64, 128, k, 128), 1, T, n_cap,
                                   0, lib.CSA_MXFP4) == 0
     gidx, ora, scores, nv = _fp4_index_case(T, n_cap, k, 40 + T, q_pos0)

@@ -415,3 +415,28 @@ def test_decode_index_capacity_beyond_visible(n_cap, L):
     for b in range(B):
         s = O.index_scores(O.bf16_bits_to_f64(qb[b, 0])[None], O.bf16_bits_to_f64(kb[b]), w.astype(np.float64), [nv])
         check_idx_rows(got[b], O.topk_select(s[0], nv, k)[None], s, [nv])
+
+
+@pytest.mark.parametrize("T,n_cap,q_pos0", [
+    (16, 2000, 256 * 5 - 16),   # the last workgroup sees exactly 5 whole 64-entry tiles
+    (16, 2000, 256 * 5 - 12),   # ... and one entry of a sixth
+    (16, 2000, 256 * 6 - 20),   # ... and 63 entries of a sixth
+    (16, 320, 4000),            # every row capped at n_cap = 5 whole tiles
+    (24, 321, 4000),            # every row capped one entry past them
+])
+def test_fused_bf16_prefill_index_tile_edges(T, n_cap, q_pos0):
+    # the fused bf16 indexer loads whole key tiles from one base address and clamps the rows of the
+    # last, partial tile: rows at and around the 64-entry tile edges, by position and by capacity
+    H_I, D_I, k = 64, 128, 64
+    d = dims_of(get("chunk1m").with_(k=k))
+    mk = lambda name, shape: G.f32_to_bf16_bits(G.normal_f32(91, name, shape))
+    qb, kb = mk("eq", (1, T, H_I, D_I)), mk("ek", (1, n_cap, D_I))
+    w = G.normal_f32(91, "ew", (H_I,))
+    idx = torch.empty(1, T, k, dtype=torch.int32, device="cuda")
+    lib.csa_index_topk(d, to_device(qb, "bf16"), to_device(w, "f32"), to_device(kb, "bf16"), idx, q_pos0=q_pos0)
+    got = idx[0].cpu().numpy()
+    nv = np.minimum(O.n_visible(q_pos0 + np.arange(T), 4), n_cap)
+    s = O.index_scores(O.bf16_bits_to_f64(qb[0]), O.bf16_bits_to_f64(kb[0]), w.astype(np.float64), nv)
+    ora = np.stack([O.topk_select(s[t], nv[t], k) for t in range(T)])
+    differ = check_idx_rows(got, ora, s, nv)
+    assert len(differ) <= 1, differ
