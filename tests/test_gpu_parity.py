@@ -423,6 +423,8 @@ def test_decode_index_capacity_beyond_visible(n_cap, L):
     (16, 2000, 256 * 6 - 20),   # ... and 63 entries of a sixth
     (16, 320, 4000),            # every row capped at n_cap = 5 whole tiles
     (24, 321, 4000),            # every row capped one entry past them
+    (16, 2000, 150),            # rows that see fewer than k entries keep them all
+    (16, 100, 0),               # rows from position 0: no entries, then one or two
 ])
 def test_fused_bf16_prefill_index_tile_edges(T, n_cap, q_pos0):
     # the fused bf16 indexer loads whole key tiles from one base address and clamps the rows of the
