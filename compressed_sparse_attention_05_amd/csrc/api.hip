@@ -233,6 +233,7 @@ int validate_index(const csa_dims* d, int B, int T, const int64_t* q_pos, int id
     if (keys_seq_stride != 0 && keys_seq_stride != n_cap * d->D_I / 2)
       return fail(CSA_ERR_ARG, "MXFP4 keys must be contiguous");
     if (!aligned(q_idx, 16) || (keys && !aligned(keys, 16))) return fail(CSA_ERR_ARG, "MXFP4 codes must be 16-byte aligned");
+    if (k_scale && !aligned(k_scale, 4)) return fail(CSA_ERR_ARG, "MXFP4 key scales must be 4-byte aligned");
   } else {
     if (q_ld < (int64_t)d->H_I * d->D_I) return fail(CSA_ERR_ARG, "q_ld < H_I*D_I");
     if (B > 1 && q_seq_stride < (int64_t)T * q_ld) return fail(CSA_ERR_ARG, "q_seq_stride too small");
@@ -986,8 +987,8 @@ int csa_forward(const csa_dims* dims, const csa_weights* w, int B, int T, const 
   const bool kfp4 = cache->key_fmt != 0;
   if (cache->entry_fmt != 0 && cache->entry_fmt != 1) return fail(CSA_ERR_ARG, "entry_fmt must be 0 or 1");
   if (cache->key_fmt != 0 && cache->key_fmt != 1) return fail(CSA_ERR_ARG, "key_fmt must be 0 or 1");
-  if (kfp4 && (!cache->key_scales || DI % 32 || !aligned(cache->keys, 16)))
-    return fail(CSA_ERR_ARG, "MXFP4 keys need key_scales, D_I %% 32 == 0 and 16-byte aligned codes");
+  if (kfp4 && (!cache->key_scales || DI % 32 || !aligned(cache->keys, 16) || !aligned(cache->key_scales, 4)))
+    return fail(CSA_ERR_ARG, "MXFP4 keys need key_scales (4-byte aligned), D_I %% 32 == 0 and 16-byte aligned codes");
   if (records && (D != 512 || dtype != CSA_BF16)) return fail(CSA_ERR_ARG, "entry records hold D = 512 bf16 entries");
   const int64_t ntot = n_tot_of(dims);
   const int es = esize(dtype);

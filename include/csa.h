@@ -161,7 +161,8 @@ int csa_hca_compress(int B, int T, const int64_t* pos0, int m, int c, int in_dty
  *            contiguous (q_ld / q_seq_stride must be 0).
  *   w        float32 head weights: [H_I] shared when w_ld == 0, else row (b*T + t) at w + row*w_ld.
  *   keys     [B, n_cap, D_I] (row stride D_I, sequence stride keys_seq_stride); MXFP4: codes
- *            [B, n_cap, D_I/2] contiguous plus k_scale [B, n_cap, D_I/32].
+ *            [B, n_cap, D_I/2] contiguous (16-byte aligned) plus k_scale [B, n_cap, D_I/32]
+ *            (4-byte aligned).
  *   out_idx  [B, T, top_k] int32.  out_score (nullable) [B, T, top_k] the scores of out_idx.
  * The T x n_cap score matrix is not stored for many query rows (fused streaming selection); for
  * few query rows (decode) the scores of every visible entry pass through the workspace.
@@ -389,7 +390,7 @@ typedef struct csa_cache {
                             byte per 32; "Precision: FP8 everywhere, FP4 experts": the indexer's
                             query-key product in FP4): keys holds the e2m1 codes [B, n_cap, D_I/2]
                             (16-byte aligned, contiguous) and key_scales the e8m0 scales
-                            [B, n_cap, D_I/32]; new keys are quantised from their stored values (see
+                            [B, n_cap, D_I/32] (4-byte aligned); new keys are quantised from their stored values (see
                             csa_mxfp4_quantize), the chunk's indexer queries likewise, and the
                             indexer runs on the MXFP4 operands                                      */
   void* key_scales;      /* [B, n_cap, D_I/32] when key_fmt = 1, else unused                       */

@@ -101,6 +101,10 @@ def test_index_topk_rejects_bad_arguments():
     rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, None, lib.CSA_MXFP4, p, 0, 0, None, p, 0, p, 0, None,
                                     2048, p, None, None, 0, None))
     assert rc == -1 and "scale" in msg
+    # MXFP4 key scales are read four bytes at a time
+    rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, None, lib.CSA_MXFP4, p, 0, 0, p, p, 0, p, 0,
+                                    ctypes.c_void_p(258), 2048, p, None, None, 0, None))
+    assert rc == -1 and "4-byte aligned" in msg
     rc, msg = _err(L.csa_index_topk(ctypes.byref(d), 1, 8, None, lib.CSA_BF16, p, 100, 800, None, p, 0, p, 262144,
                                     None, 2048, p, None, None, 0, None))
     assert rc == -1 and "q_ld" in msg
